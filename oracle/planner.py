@@ -1,0 +1,456 @@
+"""Oracle for the execution plan: mode orders, node descriptors, launch
+groups and arena offsets, which the GPU library's planner must reproduce
+bit-exactly.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Mode orders follow the reverse-tree "lifetime ordering" of the source page
+("Parallelizing Large-Scale Tensor Network Contraction on Multiple GPUs",
+section 1.4): the root takes the requested output order; walking the steps
+from last to first, an operand's order is the order of its product with the
+modes the product does not carry dropped, followed by the modes reduced at
+that step.  The reduced modes are appended in ascending label order (the page
+only says they are appended together; one common order for both operands is
+what makes them a GEMM's K axis).
+
+``death_sort_orders`` is an independent formulation used to pin the reverse
+pass: every tensor's order is its modes sorted by the step at which each mode
+is reduced, latest first (open modes count as never reduced and keep the
+output order among themselves; modes reduced at the same step are in
+ascending label order).  The page describes this as the emergent property of
+the reverse pass (section 1.4, the paragraph after the algorithm).
+
+Everything else (node classes, operand orientation, output runs, split-K,
+grouping and first-fit arena) is this project's own execution design; the
+rules are restated here from their definitions.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+INF = float("inf")
+
+LIFETIME = 0
+NAIVE = 1
+
+CLASS_TINY = 0
+CLASS_SKINNY = 1
+CLASS_GEMM = 2
+
+SKINNY_MAX_SIDE = 16        # skinny when the smaller of m, n is at most this
+GEMM_NOMINAL_TILE = 128     # nominal tile edge used only by the split-K rule
+NONE = (1 << 64) - 1        # "not in the arena"
+
+
+def _prod(ext, modes) -> int:
+    p = 1
+    for x in modes:
+        p *= int(ext[x])
+    return p
+
+
+def _pow2_floor(v: int) -> int:
+    p = 1
+    while p * 2 <= v:
+        p *= 2
+    return p
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class PlanError(Exception):
+    def __init__(self, code: str, msg: str = ""):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+# ----------------------------------------------------------------------------
+# validation and SSA bookkeeping
+
+
+def validate(extents, leaves, out_modes, lhs, rhs, sliced=()):
+    nm = len(extents)
+    for e in extents:
+        if int(e) < 1:
+            raise PlanError("INVALID_NETWORK", "extent < 1")
+    L = len(leaves)
+    if L < 1:
+        raise PlanError("INVALID_ARG", "no leaves")
+    count = [0] * nm
+    for l in leaves:
+        if len(set(l)) != len(l):
+            raise PlanError("UNSUPPORTED", "mode repeated within one leaf")
+        for x in l:
+            if not (0 <= x < nm):
+                raise PlanError("INVALID_NETWORK", "mode label out of range")
+            count[x] += 1
+    if len(set(out_modes)) != len(out_modes):
+        raise PlanError("INVALID_NETWORK", "repeated output mode")
+    in_out = [False] * nm
+    for x in out_modes:
+        if not (0 <= x < nm):
+            raise PlanError("INVALID_NETWORK", "output mode out of range")
+        in_out[x] = True
+    for x in range(nm):
+        c = count[x] + (1 if in_out[x] else 0)
+        if c > 2:
+            raise PlanError("UNSUPPORTED", "mode in more than two tensors")
+        if c == 1:
+            raise PlanError("INVALID_NETWORK", "dangling mode")
+        if in_out[x] and count[x] != 1:
+            raise PlanError("INVALID_NETWORK", "open mode not on exactly one leaf")
+    S = len(lhs)
+    if S != L - 1 or len(rhs) != S:
+        raise PlanError("INVALID_TREE", "number of steps must be leaves - 1")
+    used = [False] * (L + S)
+    for s in range(S):
+        a, b = int(lhs[s]), int(rhs[s])
+        for t in (a, b):
+            if not (0 <= t < L + s) or used[t]:
+                raise PlanError("INVALID_TREE", "bad or reused operand")
+            used[t] = True
+        if a == b:
+            raise PlanError("INVALID_TREE", "operand used twice")
+    sl = list(sliced)
+    if len(set(sl)) != len(sl):
+        raise PlanError("INVALID_ARG", "repeated sliced mode")
+    for x in sl:
+        if not (0 <= x < nm) or count[x] != 2:
+            raise PlanError("INVALID_ARG", "sliced mode must be a closed mode")
+
+
+def ssa_modes(leaves, lhs, rhs, sliced):
+    """Mode sets of every SSA tensor (sliced modes removed), and per-step
+    (K, M, N) sets."""
+    sl = set(sliced)
+    sets = [frozenset(x for x in l if x not in sl) for l in leaves]
+    steps = []
+    for a, b in zip(lhs, rhs):
+        A, B = sets[a], sets[b]
+        K = A & B
+        steps.append((K, A - K, B - K))
+        sets.append((A | B) - K)
+    return sets, steps
+
+
+def death_steps(leaves, lhs, rhs, sliced) -> Dict[int, float]:
+    """Step index at which each (non-sliced) mode is reduced; open = inf."""
+    _, steps = ssa_modes(leaves, lhs, rhs, sliced)
+    d: Dict[int, float] = {}
+    for l in leaves:
+        for x in l:
+            d[x] = INF
+    for s, (K, _, _) in enumerate(steps):
+        for x in K:
+            d[x] = s
+    return d
+
+
+# ----------------------------------------------------------------------------
+# orders
+
+
+def lifetime_orders(leaves, out_modes, lhs, rhs, sliced=()) -> List[List[int]]:
+    """Reverse pass over the tree: the product's order fixes each operand's
+    retained modes, and the reduced modes (ascending label) go last."""
+    L, S = len(leaves), len(lhs)
+    sets, steps = ssa_modes(leaves, lhs, rhs, sliced)
+    order: List[Optional[List[int]]] = [None] * (L + S)
+    order[L + S - 1] = list(out_modes)
+    for s in range(S - 1, -1, -1):
+        K, _, _ = steps[s]
+        c_order = order[L + s]
+        reduced = sorted(K)
+        for operand in (lhs[s], rhs[s]):
+            kept = [x for x in c_order if x in sets[operand]]
+            order[operand] = kept + reduced
+    return order  # type: ignore[return-value]
+
+
+def death_sort_orders(leaves, out_modes, lhs, rhs, sliced=()) -> List[List[int]]:
+    """Independent formulation: sort each tensor's modes by death step,
+    latest first; open modes first, in output order; equal deaths by label."""
+    sets, _ = ssa_modes(leaves, lhs, rhs, sliced)
+    death = death_steps(leaves, lhs, rhs, sliced)
+    pos = {x: i for i, x in enumerate(out_modes)}
+
+    def key(x):
+        if death[x] == INF:
+            return (0, pos[x])
+        return (1, -death[x], x)
+
+    return [sorted(ms, key=key) for ms in sets]
+
+
+def naive_orders(leaves, lhs, rhs, sliced=()):
+    """Forward order policy used for the ablation: intermediates keep
+    [A's retained modes in A's order | B's retained modes in B's order];
+    operands are re-laid as [retained | K ascending] whenever they differ."""
+    L, S = len(leaves), len(lhs)
+    sl = set(sliced)
+    sets, steps = ssa_modes(leaves, lhs, rhs, sliced)
+    order = [[x for x in l if x not in sl] for l in leaves] + [None] * S
+    gemm_a, gemm_b = [], []
+    for s in range(S):
+        K, _, _ = steps[s]
+        a, b = lhs[s], rhs[s]
+        ra = [x for x in order[a] if x not in K]
+        rb = [x for x in order[b] if x not in K]
+        gemm_a.append(ra + sorted(K))
+        gemm_b.append(rb + sorted(K))
+        order[L + s] = ra + rb
+    return order, gemm_a, gemm_b
+
+
+# ----------------------------------------------------------------------------
+# the plan
+
+
+@dataclass
+class Node:
+    step: int
+    lhs: int
+    rhs: int
+    out: int
+    m: int
+    n: int
+    k: int
+    cls: int
+    swap: int
+    splits: int
+    group: int = -1
+    row_runs: List[tuple] = field(default_factory=list)   # (size, stride), outermost first
+    col_runs: List[tuple] = field(default_factory=list)
+    inner_run: int = 1
+    interleaved: int = 0
+    copy_a: int = 0          # operand A is re-laid into the arena before the step
+    copy_b: int = 0
+    a_off: int = NONE        # arena offset of the GEMM's A operand (copy or intermediate)
+    b_off: int = NONE
+    c_off: int = NONE        # NONE = written to the output buffer
+    scratch_off: int = NONE
+    scratch_bytes: int = 0
+
+
+@dataclass
+class Plan:
+    order: List[List[int]]
+    gemm_a: List[List[int]]
+    gemm_b: List[List[int]]
+    nodes: List[Node]
+    groups: List[List[int]]
+    arena_bytes: int
+    tensor_off: List[int]
+    root_permute: int
+    root_off: int
+    staged_leaf: List[int]
+    flops: int
+    flops_unsliced: int
+    bytes: int
+    max_elems: int
+    num_slices: int
+
+
+def _runs(c_order, ext, row_set):
+    """Maximal runs of same-side modes along c_order (extent-1 modes skipped).
+    Returns (row_runs, col_runs, inner_run, n_runs) with (size, stride) per
+    run, stride = stride in C of the run's innermost mode."""
+    eff = [x for x in c_order if int(ext[x]) > 1]
+    stride = {}
+    s = 1
+    for x in reversed(eff):
+        stride[x] = s
+        s *= int(ext[x])
+    runs = []  # (is_row, size, stride)
+    for x in eff:
+        side = x in row_set
+        if runs and runs[-1][0] == side:
+            r = runs[-1]
+            runs[-1] = (side, r[1] * int(ext[x]), stride[x])
+        else:
+            runs.append((side, int(ext[x]), stride[x]))
+    row_runs = [(sz, st) for side, sz, st in runs if side]
+    col_runs = [(sz, st) for side, sz, st in runs if not side]
+    inner = runs[-1][1] if runs else 1
+    return row_runs, col_runs, inner, len(runs)
+
+
+def _split_rule(cls, R, S, k):
+    if cls == CLASS_GEMM:
+        tiles = _ceil_div(R, GEMM_NOMINAL_TILE) * _ceil_div(S, GEMM_NOMINAL_TILE)
+        if tiles >= 128 or k < 4096:
+            return 1
+        return max(1, min(_pow2_floor(256 // tiles), _pow2_floor(k // 2048)))
+    if cls == CLASS_SKINNY:
+        blocks = _ceil_div(R, 256)
+        if blocks >= 512 or k < 4096:
+            return 1
+        return max(1, min(_pow2_floor(1024 // blocks), _pow2_floor(k // 2048)))
+    return 1
+
+
+class _Arena:
+    """First-fit over a free list of [start, end) holes; the last hole is
+    unbounded.  Frees coalesce with neighbours."""
+
+    def __init__(self):
+        self.free = [[0, None]]
+        self.peak = 0
+
+    def alloc(self, size: int) -> int:
+        for h in self.free:
+            start, end = h
+            if end is None or end - start >= size:
+                off = start
+                h[0] = start + size
+                if end is not None and h[0] == end:
+                    self.free.remove(h)
+                self.peak = max(self.peak, off + size)
+                return off
+        raise AssertionError("unreachable")
+
+    def release(self, off: int, size: int):
+        self.free.append([off, off + size])
+        self.free.sort(key=lambda h: h[0])
+        merged = []
+        for h in self.free:
+            if merged and merged[-1][1] is not None and merged[-1][1] == h[0]:
+                merged[-1][1] = h[1]
+            else:
+                merged.append(list(h))
+        self.free = merged
+
+
+def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), align=256,
+              tiny_mnk=1 << 15, max_group=256) -> Plan:
+    validate(extents, leaves, out_modes, lhs, rhs, sliced)
+    L, S = len(leaves), len(lhs)
+    sl = set(sliced)
+    ext = [1 if x in sl else int(e) for x, e in enumerate(extents)]
+    sets, steps = ssa_modes(leaves, lhs, rhs, sliced)
+    declared = [[x for x in l if x not in sl] for l in leaves]
+    has_sliced = [any(x in sl for x in l) for l in leaves]
+
+    if policy == LIFETIME:
+        order = lifetime_orders(leaves, out_modes, lhs, rhs, sliced)
+        gemm_a = [order[a] for a in lhs]
+        gemm_b = [order[b] for b in rhs]
+        root_permute = 0
+    else:
+        order, gemm_a, gemm_b = naive_orders(leaves, lhs, rhs, sliced)
+        root_permute = int(S > 0 and order[L + S - 1] != list(out_modes))
+
+    staged_leaf = [0] * L
+    nodes: List[Node] = []
+    flops = flops_u = nbytes = 0
+    max_elems = 0
+    for s in range(S):
+        K, M, N = steps[s]
+        a, b = lhs[s], rhs[s]
+        m, n, k = _prod(ext, M), _prod(ext, N), _prod(ext, K)
+        mu = _prod(extents, M); nu = _prod(extents, N); ku = _prod(extents, K)
+        flops += 8 * m * n * k
+        flops_u += 8 * mu * nu * ku
+        nbytes += 8 * (m * k + n * k + m * n)
+        max_elems = max(max_elems, m * n)
+        if m * n * k <= tiny_mnk:
+            cls = CLASS_TINY
+        elif min(m, n) <= SKINNY_MAX_SIDE:
+            cls = CLASS_SKINNY
+        else:
+            cls = CLASS_GEMM
+        # C's order as the GEMM writes it
+        c_order = order[L + s] if not (policy == NAIVE) else order[L + s]
+        eff = [x for x in c_order if ext[x] > 1]
+        if cls == CLASS_SKINNY:
+            swap = int(n > m)
+        else:
+            swap = int(bool(eff) and eff[-1] in M)
+        row_set = N if swap else M
+        row_runs, col_runs, inner, nruns = _runs(c_order, ext, row_set)
+        R, Sx = (n, m) if swap else (m, n)
+        splits = _split_rule(cls, R, Sx, k)
+        node = Node(step=s, lhs=a, rhs=b, out=L + s, m=m, n=n, k=k, cls=cls, swap=swap, splits=splits,
+                    row_runs=row_runs, col_runs=col_runs, inner_run=inner, interleaved=int(nruns > 2))
+        # operand copies
+        for which, t, want in (("a", a, gemm_a[s]), ("b", b, gemm_b[s])):
+            if t < L:
+                need = has_sliced[t] or declared[t] != want
+                if need:
+                    staged_leaf[t] = 1
+            else:
+                need = order[t] != want
+            setattr(node, "copy_" + which, int(need))
+        if splits > 1:
+            node.scratch_bytes = splits * R * Sx * 8
+        nodes.append(node)
+
+    # launch groups
+    groups: List[List[int]] = []
+    open_tiny = False
+    produced_in_group = set()
+    for s, nd in enumerate(nodes):
+        if nd.cls == CLASS_TINY:
+            if (open_tiny and len(groups[-1]) < max_group and nd.lhs not in produced_in_group
+                    and nd.rhs not in produced_in_group):
+                groups[-1].append(s)
+            else:
+                groups.append([s])
+                open_tiny = True
+                produced_in_group = set()
+            produced_in_group.add(nd.out)
+        else:
+            groups.append([s])
+            open_tiny = False
+            produced_in_group = set()
+    for g, members in enumerate(groups):
+        for s in members:
+            nodes[s].group = g
+
+    # arena
+    def rbytes(elems):
+        return _ceil_div(elems * 8, align) * align
+
+    arena = _Arena()
+    tensor_off = [NONE] * (L + S)
+    elems_of = [_prod(ext, st) for st in sets]
+    root = L + S - 1
+    root_off = NONE
+    live_size = {}
+    for members in groups:
+        to_free = []
+        for s in members:
+            nd = nodes[s]
+            for which, t in (("a", nd.lhs), ("b", nd.rhs)):
+                if getattr(nd, "copy_" + which):
+                    off = arena.alloc(rbytes(elems_of[t]))
+                    to_free.append((off, rbytes(elems_of[t])))
+                    if t < L and policy == LIFETIME:
+                        tensor_off[t] = off
+                    setattr(nd, which + "_off", off)
+                elif t >= L:
+                    setattr(nd, which + "_off", tensor_off[t])
+                    to_free.append((tensor_off[t], rbytes(elems_of[t])))
+            if nd.out == root and not root_permute:
+                nd.c_off = NONE
+            else:
+                nd.c_off = arena.alloc(rbytes(elems_of[nd.out]))
+                tensor_off[nd.out] = nd.c_off
+                if nd.out == root:
+                    root_off = nd.c_off
+            if nd.splits > 1:
+                nd.scratch_off = arena.alloc(_ceil_div(nd.scratch_bytes, align) * align)
+                to_free.append((nd.scratch_off, _ceil_div(nd.scratch_bytes, align) * align))
+        for off, sz in to_free:
+            arena.release(off, sz)
+    if S == 0:
+        staged_leaf = [0] * L
+    return Plan(order=order, gemm_a=gemm_a, gemm_b=gemm_b, nodes=nodes, groups=groups,
+                arena_bytes=arena.peak, tensor_off=tensor_off, root_permute=root_permute,
+                root_off=root_off, staged_leaf=staged_leaf, flops=flops, flops_unsliced=flops_u,
+                bytes=nbytes, max_elems=max_elems,
+                num_slices=_prod(extents, sliced) if sliced else 1)
