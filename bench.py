@@ -1,0 +1,268 @@
+"""Benchmark: contraction TFLOP/s (complex64 on FP32 arithmetic), % of the
+MI355X FP32 MFMA peak and wall time per result, on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload sweep|peps|brickwork12|brickwork30]
+
+Default workload: the isolated pairwise-contraction sweep (m, n, k each in
+{2^6, 2^10, 2^14, 2^18}, k <= 2^14, all modes of extent 2, i.i.d. CN(0,1)
+entries, GEMM-aligned declarations; the three m = n = 2^18 cases do not fit
+one GPU and are left out).  One step runs every feasible case once through
+tnc_execute.  Inputs are resident in HBM before timing.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense FP32 matrix
+PEAK_HBM = 8000.0        # GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fill_gaussian(t, seed):
+    """CN(0,1) complex64 in place, chunked, from a seeded device generator."""
+    import torch
+    g = torch.Generator(device=t.device)
+    g.manual_seed(seed)
+    flat = t.view(-1)
+    chunk = 1 << 28
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        flat[s:e] = torch.randn(e - s, dtype=torch.complex64, device=t.device, generator=g)
+
+
+class SweepWorkload:
+    name = "pairwise sweep m,n,k in {2^6,2^10,2^14,2^18}, k<=2^14, 45 feasible cases, aligned"
+
+    def __init__(self, cases=None):
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import sweep
+        self.cases = [c for c in sweep.cases() if c["feasible"]] if cases is None else cases
+        self.plans = []
+        maxa = maxb = maxc = maxws = 0
+        for c in self.cases:
+            m, n, k = 1 << c["logm"], 1 << c["logn"], 1 << c["logk"]
+            net, tree = sweep.network(c["logm"], c["logn"], c["logk"])
+            plan = qa.Plan.from_network(net, tree)
+            self.plans.append((c, plan, m, n, k))
+            maxa, maxb, maxc = max(maxa, m * k), max(maxb, n * k), max(maxc, m * n)
+            maxws = max(maxws, plan.workspace_bytes)
+        dev = "cuda"
+        self.A = torch.empty(maxa, dtype=torch.complex64, device=dev)
+        self.B = torch.empty(maxb, dtype=torch.complex64, device=dev)
+        self.C = torch.empty(maxc, dtype=torch.complex64, device=dev)
+        fill_gaussian(self.A, 200)
+        fill_gaussian(self.B, 201)
+        self.ws = torch.empty(max(256, maxws), dtype=torch.uint8, device=dev)
+        self.flops = sum(8.0 * m * n * k for _, _, m, n, k in self.plans)
+        self.config = {"workload": "pairwise-sweep", "cases": len(self.plans),
+                       "m_n_k": "each in {2^6,2^10,2^14,2^18}, k<=2^14, m=n=2^18 excluded",
+                       "layout": "GEMM-aligned (lifetime order)", "flop_per_step": self.flops}
+
+    def step(self, events=None):
+        for idx, (c, plan, m, n, k) in enumerate(self.plans):
+            if events is not None:
+                events[idx][0].record()
+            plan.execute([self.A[: m * k], self.B[: n * k]], self.C[: m * n], self.ws)
+            if events is not None:
+                events[idx][1].record()
+
+    def kernel_of(self, idx):
+        c, plan, m, n, k = self.plans[idx]
+        return "k_cgemm<128,128>" if n > 64 else ("k_cgemm<256,64>" if n > 32 else "k_cgemm<256,32>")
+
+    def launch_flops(self, idx):
+        _, _, m, n, k = self.plans[idx]
+        return 8.0 * m * n * k
+
+    def cpu_baseline(self, budget_s=12.0):
+        """Oracle on the host: exact complex128 entries of the largest case,
+        on a sub-grid of gathered rows, for about `budget_s` seconds."""
+        import oracle
+        c, plan, m, n, k = max(self.plans, key=lambda p: p[2] * p[3] * p[4])
+        rng = np.random.default_rng(7)
+        rows = np.sort(rng.choice(m, size=64, replace=False))
+        cols = np.sort(rng.choice(n, size=64, replace=False))
+        a = self.A[: m * k].view(m, k)[rows].cpu().numpy()
+        b = self.B[: n * k].view(n, k)[cols].cpu().numpy()
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        done = 0
+        ni = 8
+        while True:
+            oracle.pair_block(a[:ni], b, threads=threads)
+            done += ni * len(cols)
+            el = time.perf_counter() - t0
+            if el > budget_s:
+                break
+            ni = min(64, ni * 2)
+        flops = 8.0 * done * k
+        return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} exact complex128 output entries of the (m,n,k)=(2^{c['logm']},2^{c['logn']},"
+                          f"2^{c['logk']}) case ({flops:.3g} flop in {el:.1f} s)"}
+
+
+class TreeWorkload:
+    def __init__(self, which):
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import circuits, lattice, trees
+        if which == "peps":
+            net = lattice.peps(8, 8, 404)
+            tree = lattice.row_major_tree(8)
+            self.config = {"workload": "peps-8x8-D8", "seed": 404, "tree": "row-major caterpillar"}
+        elif which == "brickwork12":
+            net = circuits.brickwork(12, 8, 101).to_network()
+            tree = trees.greedy_tree(net)
+            self.config = {"workload": "brickwork-12q-d8-amplitude", "seed": 101, "tree": "greedy"}
+        elif which == "brickwork30":
+            net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
+            tree = trees.greedy_tree(net)
+            self.config = {"workload": "brickwork-30q-d14-batch64", "seed": 303, "tree": "greedy"}
+        else:
+            raise ValueError(which)
+        self.name = self.config["workload"]
+        self.net, self.tree = net, tree
+        self.plan = qa.Plan.from_network(net, tree)
+        st = self.plan.stats()
+        self.flops = st["flops"]
+        self.config.update({"flop_per_step": self.flops, "max_intermediate": st["max_intermediate"],
+                            "steps_in_tree": st["num_steps"], "launch_groups": st["num_groups"]})
+        self.leaves = [torch.from_numpy(d).to("cuda") for d in net.data]
+        size = int(np.prod(self.plan.out_shape, dtype=np.int64)) if self.plan.out_shape else 1
+        self.out = torch.empty(size, dtype=torch.complex64, device="cuda")
+        self.ws = qa.alloc_workspace(self.plan)
+
+    def step(self, events=None):
+        if events is not None:
+            events[0][0].record()
+        self.plan.execute(self.leaves, self.out, self.ws)
+        if events is not None:
+            events[0][1].record()
+
+    def kernel_of(self, idx):
+        return "whole tree"
+
+    def launch_flops(self, idx):
+        return self.flops
+
+    def cpu_baseline(self, budget_s=12.0):
+        import oracle
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        oracle.contract_network(self.net, self.tree, threads=threads)
+        el = time.perf_counter() - t0
+        return {"value": self.flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"full contraction ({self.flops:.3g} flop in {el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "peps", "brickwork12", "brickwork30"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cases", default="", help="comma-separated sweep case indices (default: all feasible)")
+    ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this executor contracts on a single MI355X "
+              "(multi-GPU distribution is not part of it); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "needs a GPU"
+
+    t0 = time.time()
+    if args.workload == "sweep":
+        cases = None
+        if args.cases:
+            from workloads import sweep
+            allc = sweep.cases()
+            cases = [allc[int(i)] for i in args.cases.split(",")]
+        wl = SweepWorkload(cases)
+        nlaunch = len(wl.plans)
+    else:
+        wl = TreeWorkload(args.workload)
+        nlaunch = 1
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s; flop/step {wl.flops:.4g}")
+
+    for w in range(args.warmup):
+        wl.step()
+        torch.cuda.synchronize()
+        log(f"warmup {w} done")
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlaunch)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        wl.step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    value = wl.flops / (ms_per_step / 1e3) / 1e12
+
+    # per-launch durations (HIP events on the stream the library enqueues on)
+    per = {}
+    for s in range(args.steps):
+        for i in range(nlaunch):
+            d = evs[s][i][0].elapsed_time(evs[s][i][1])
+            key = wl.kernel_of(i)
+            f = wl.launch_flops(i)
+            acc = per.setdefault(key, [0.0, 0.0, 0])
+            acc[0] += f
+            acc[1] += d
+            acc[2] += 1
+    dom = max(per.items(), key=lambda kv: kv[1][1])
+    achieved = dom[1][0] / (dom[1][1] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": None,
+                "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
+    if args.report:
+        rep = {"per_kernel": {k: {"flop": v[0], "ms": v[1], "launches": v[2]} for k, v in per.items()},
+               "cases": []}
+        if args.workload == "sweep":
+            for i, (c, plan, m, n, k) in enumerate(wl.plans):
+                ms = np.median([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])
+                rep["cases"].append({"logm": c["logm"], "logn": c["logn"], "logk": c["logk"], "ms": float(ms),
+                                     "tflops": 8.0 * m * n * k / (ms / 1e3) / 1e12})
+        os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
+        json.dump(rep, open(args.report, "w"), indent=1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = wl.cpu_baseline()
+    line = {"metric": "contraction-tree TFLOP/s (complex64) + % FP32 MFMA peak; wall time per result",
+            "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2),
+            "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
+            "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
+            "host_wall_s": round(wall, 3)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * tnc.h - exact tensor-network contraction along a fixed tree, on one
+ * MI355X (gfx950) GPU.  C ABI of libtnc.so.
+ *
+ * The operation (page "Parallelizing Large-Scale Tensor Network Contraction
+ * on Multiple GPUs", section 1.1): a network of leaf tensors joined by
+ * shared modes is reduced by a binary tree of pairwise steps.  Each step
+ * forms C[M, N] = sum over K of A[M, K] * B[N, K], where K are the modes
+ * shared by the two operands (summed away) and M, N the modes each keeps.
+ * The result is the network's full sum laid out in a caller-given order of
+ * the open modes.
+ *
+ * How it runs: tnc_plan fixes, on the host, the memory order of every tensor
+ * by the reverse-tree "lifetime ordering" of section 1.4 (the root takes the
+ * requested output order; each operand's order is its product's order
+ * restricted to the operand, followed by the reduced modes).  With those
+ * orders both operands of every step are stored K-innermost, so every step
+ * is a GEMM with no runtime transpose of intermediates.  tnc_plan also
+ * decides each step's kernel, groups the many small steps into shared
+ * launches, and lays all intermediates out in one arena.  tnc_execute then
+ * only enqueues kernels on the caller's stream.
+ *
+ * Conventions common to all calls:
+ *   - Tensors are dense, row-major in their mode order (first mode slowest),
+ *     complex64 entries stored as interleaved (float re, float im).
+ *   - Mode labels are 0 .. num_modes-1.  Every mode appears in exactly two
+ *     tensors counting the output: two leaves (closed mode, summed) or one
+ *     leaf and the output (open mode).
+ *   - No function throws; every failure is a tnc_status.  Functions that
+ *     return an error leave their outputs untouched.
+ *   - The library never allocates device memory.  The caller owns every
+ *     device buffer.
+ */
+#ifndef TNC_H
+#define TNC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TNC_OK = 0,
+  TNC_ERR_INVALID_ARG = 1,        /* NULL pointer, bad option, bad sliced mode, bad id */
+  TNC_ERR_INVALID_NETWORK = 2,    /* extent < 1, label out of range, dangling mode,
+                                     open mode not on exactly one leaf */
+  TNC_ERR_INVALID_TREE = 3,       /* steps != leaves - 1, operand id out of range or reused */
+  TNC_ERR_UNSUPPORTED = 4,        /* mode in more than two tensors (hyperedge / batch mode),
+                                     a mode repeated inside one leaf, rank > 64,
+                                     complex128 data, a size that overflows 64 bits */
+  TNC_ERR_OUT_OF_MEMORY = 5,      /* planned workspace exceeds options.capacity_bytes */
+  TNC_ERR_WORKSPACE_TOO_SMALL = 6,/* tnc_execute got less workspace than planned */
+  TNC_ERR_HIP = 7                 /* a HIP runtime call or kernel launch failed */
+} tnc_status;
+
+typedef enum { TNC_C64 = 0, TNC_C128 = 1 } tnc_dtype;
+
+/* Mode-order policy.  LIFETIME: the page's reverse-tree ordering (section
+ * 1.4); intermediates are never re-laid.  NAIVE: the ablation baseline of
+ * section 1.3 - each product keeps [A's kept modes | B's kept modes] and
+ * every operand that is not already [kept | K] is permuted before its GEMM;
+ * the root is permuted into the output order at the end. */
+typedef enum { TNC_ORDER_LIFETIME = 0, TNC_ORDER_NAIVE = 1 } tnc_order_policy;
+
+/* Kernel class of a step. */
+typedef enum { TNC_CLASS_TINY = 0, TNC_CLASS_SKINNY = 1, TNC_CLASS_GEMM = 2 } tnc_kernel_class;
+
+typedef struct tnc_plan_s *tnc_plan_t;
+
+/* The network.  Arrays are read during tnc_plan only (the plan copies them). */
+typedef struct {
+  int32_t num_modes;
+  const int64_t *extents;     /* [num_modes], each >= 1 */
+  int32_t num_leaves;         /* >= 1 */
+  const int32_t *leaf_rank;   /* [num_leaves] */
+  const int32_t *leaf_modes;  /* concatenated mode lists, each in its buffer's row-major order */
+  int32_t out_rank;
+  const int32_t *out_modes;   /* [out_rank]: the result's mode order */
+  tnc_dtype dtype;            /* TNC_C64 */
+} tnc_network;
+
+/* The tree, in SSA form: leaves are ids 0 .. L-1, step s creates id L + s
+ * from operands lhs[s] and rhs[s]; each id is consumed once; the last step
+ * creates the root.  Steps execute in list order. */
+typedef struct {
+  int32_t num_steps;          /* = num_leaves - 1 */
+  const int32_t *lhs;
+  const int32_t *rhs;
+} tnc_tree;
+
+/* Plan options; pass NULL for the defaults shown. */
+typedef struct {
+  tnc_order_policy order;     /* TNC_ORDER_LIFETIME */
+  int32_t num_sliced;         /* 0: number of closed modes fixed per slice */
+  const int32_t *sliced_modes;/* NULL: closed modes to slice over; tnc_execute sums the
+                                 prod(extents) slices into `out` (page section 1.1) */
+  uint64_t align;             /* 256: arena alignment in bytes (power of two, >= 256) */
+  uint64_t capacity_bytes;    /* 0: no limit; else fail with OUT_OF_MEMORY above it */
+  uint64_t tiny_mnk;          /* 32768: steps with m*n*k <= this share grouped launches */
+  int32_t max_group;          /* 256: most steps in one grouped launch */
+} tnc_plan_options;
+
+/* Fill `opts` with the defaults. */
+void tnc_plan_options_default(tnc_plan_options *opts);
+
+/*
+ * Build a plan.  Host only: no HIP call is made.  On success *plan owns a
+ * copy of everything it needs.
+ * Errors: INVALID_ARG, INVALID_NETWORK, INVALID_TREE, UNSUPPORTED,
+ * OUT_OF_MEMORY (see tnc_status).
+ */
+tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
+                    tnc_plan_t *plan);
+
+void tnc_plan_destroy(tnc_plan_t plan);
+
+/* Device workspace the plan needs, in bytes (header + arena). */
+tnc_status tnc_plan_workspace_bytes(tnc_plan_t plan, uint64_t *bytes);
+
+typedef struct {
+  int32_t num_leaves, num_steps, num_groups;
+  int32_t nodes_tiny, nodes_skinny, nodes_gemm, nodes_split;
+  int32_t nodes_interleaved;     /* steps whose output interleaves A- and B-modes */
+  int32_t min_inner_run;         /* shortest innermost output run, in entries */
+  int32_t staged_leaves;         /* leaves copied into the arena before use */
+  int32_t relayouts;             /* operand re-layouts of intermediates (NAIVE only) */
+  int32_t root_permute;          /* 1 if the root is permuted into `out` (NAIVE) */
+  int64_t num_slices;            /* product of sliced extents (1 if unsliced) */
+  double flops;                  /* sum of 8 m n k over steps of one slice */
+  double flops_unsliced;         /* same for the tree with nothing sliced */
+  double bytes;                  /* sum of 8 (m k + n k + m n) over steps of one slice */
+  uint64_t max_intermediate;     /* largest step output, in entries */
+  uint64_t header_bytes;         /* workspace prefix holding kernel descriptors */
+  uint64_t arena_bytes;          /* arena high-water mark */
+  uint64_t workspace_bytes;      /* header_bytes + arena_bytes */
+} tnc_plan_stats;
+
+tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats);
+
+/* Planned mode order of SSA tensor `id` (0 .. L+S-1).  `modes` must hold 64
+ * entries; *rank receives the order's length. */
+tnc_status tnc_plan_tensor_order(tnc_plan_t plan, int32_t id, int32_t *modes, int32_t *rank);
+
+/* Arena offset (bytes, from the arena start) of SSA tensor `id`: a staged
+ * leaf copy or an intermediate.  UINT64_MAX: read in place (leaf) or written
+ * to `out` (root). */
+tnc_status tnc_plan_tensor_offset(tnc_plan_t plan, int32_t id, uint64_t *offset);
+
+typedef struct {
+  int32_t lhs, rhs, out;         /* SSA ids */
+  int32_t kernel_class;          /* tnc_kernel_class */
+  int32_t swap;                  /* 1: the kernel's row operand is B (C is produced transposed) */
+  int32_t group;                 /* launch group */
+  int32_t splits;                /* K split count (> 1: partial sums in scratch, then a reduce) */
+  int32_t row_runs, col_runs;    /* number of output runs per side */
+  int32_t inner_run;             /* entries in the innermost output run */
+  int32_t interleaved;
+  int32_t copy_a, copy_b;        /* operand copied/permuted into the arena before the step */
+  int64_t m, n, k;
+  uint64_t a_off, b_off, c_off;  /* arena offsets of the GEMM operands / product
+                                    (UINT64_MAX: leaf in place or `out`) */
+  uint64_t scratch_off, scratch_bytes;
+} tnc_node_info;
+
+tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
+
+/*
+ * Run the plan.
+ *   leaves[L]   device pointers to the leaf buffers (declared orders)
+ *   out         device pointer, prod(out extents) complex64 entries, overwritten
+ *   workspace   device pointer, >= tnc_plan_workspace_bytes, 256-byte aligned
+ *   stream      hipStream_t to enqueue on (NULL = the default stream)
+ * Asynchronous: returns once the work is enqueued; no host synchronisation,
+ * no allocation.  The caller keeps the plan, leaves, out and workspace alive
+ * until the stream has finished.  One plan may run concurrently on different
+ * streams given distinct workspaces and outputs.  A sliced plan loops over all
+ * slices and leaves their sum in `out`.
+ * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP (launch failure; faults
+ * surface at the caller's next synchronisation).
+ */
+tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                       uint64_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *tnc_status_string(tnc_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TNC_H */

@@ -54,6 +54,9 @@ def _load():
     lib.oracle_dot_rows.restype = None
     lib.oracle_dot_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, P(ctypes.c_float), P(ctypes.c_float),
                                     P(ctypes.c_double), ctypes.c_int32]
+    lib.oracle_pair_block.restype = None
+    lib.oracle_pair_block.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P(ctypes.c_float),
+                                      P(ctypes.c_float), P(ctypes.c_double), ctypes.c_int32]
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -123,6 +126,21 @@ def dot_rows(a: np.ndarray, b: np.ndarray, threads: Optional[int] = None) -> np.
                             _ptr(b.view(np.float32), ctypes.c_float), _ptr(out, ctypes.c_double),
                             threads if threads else max_threads())
     return out.view(np.complex128)
+
+
+def pair_block(a: np.ndarray, b: np.ndarray, threads: Optional[int] = None) -> np.ndarray:
+    """a: complex64 [ni, k] rows of A, b: complex64 [nj, k] rows of B (K
+    innermost, same K order).  Returns complex128 [ni, nj] = a @ b^T."""
+    a = np.ascontiguousarray(a, dtype=np.complex64)
+    b = np.ascontiguousarray(b, dtype=np.complex64)
+    assert a.ndim == 2 and b.ndim == 2 and a.shape[1] == b.shape[1]
+    ni, k = a.shape
+    nj = b.shape[0]
+    out = np.zeros(2 * ni * nj, dtype=np.float64)
+    _load().oracle_pair_block(ni, nj, k, _ptr(a.view(np.float32), ctypes.c_float),
+                              _ptr(b.view(np.float32), ctypes.c_float), _ptr(out, ctypes.c_double),
+                              threads if threads else max_threads())
+    return out.view(np.complex128).reshape(ni, nj)
 
 
 def row_major_strides(extents, modes):

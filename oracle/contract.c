@@ -270,6 +270,31 @@ void oracle_dot_rows(int64_t count, int64_t k, const float *a, const float *b, d
   }
 }
 
+/*
+ * A block of one pairwise contraction: out[i*nj + j] = sum_l a[i*k + l] * b[j*k + l]
+ * for the ni gathered rows of A and nj gathered rows of B (both complex64,
+ * K innermost), in complex128.  This is C = sum_K A[M, K] B[N, K] restricted
+ * to a sub-grid of output entries.
+ */
+void oracle_pair_block(int64_t ni, int64_t nj, int64_t k, const float *a, const float *b, double *out,
+                       int32_t nthreads) {
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) collapse(2)
+  for (int64_t i = 0; i < ni; ++i) {
+    for (int64_t j = 0; j < nj; ++j) {
+      double re = 0.0, im = 0.0;
+      for (int64_t l = 0; l < k; ++l) {
+        double ar = a[2 * (i * k + l)], ai = a[2 * (i * k + l) + 1];
+        double br = b[2 * (j * k + l)], bi = b[2 * (j * k + l) + 1];
+        re += ar * br - ai * bi;
+        im += ar * bi + ai * br;
+      }
+      out[2 * (i * nj + j)] = re;
+      out[2 * (i * nj + j) + 1] = im;
+    }
+  }
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

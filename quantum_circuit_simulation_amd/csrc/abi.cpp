@@ -1,0 +1,235 @@
+// extern "C" entry points of libtnc.so (declared in include/tnc.h) and the
+// executor that turns a plan's launch program into kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+struct tnc_plan_s {
+  tnc::PlanImpl impl;
+};
+
+namespace {
+
+bool debug_sync() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = std::getenv("TNC_DEBUG_SYNC");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+tnc_status check(hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return TNC_ERR_HIP;
+  if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return TNC_ERR_HIP;
+  return TNC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void tnc_plan_options_default(tnc_plan_options *o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->order = TNC_ORDER_LIFETIME;
+  o->num_sliced = 0;
+  o->sliced_modes = nullptr;
+  o->align = 256;
+  o->capacity_bytes = 0;
+  o->tiny_mnk = 32768;
+  o->max_group = 256;
+}
+
+tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
+                    tnc_plan_t *plan) {
+  if (!plan) return TNC_ERR_INVALID_ARG;
+  tnc_plan_s *p = new (std::nothrow) tnc_plan_s();
+  if (!p) return TNC_ERR_OUT_OF_MEMORY;
+  tnc_status st;
+  try {
+    st = tnc::build_plan(net, tree, opts, &p->impl);
+  } catch (const std::bad_alloc &) {
+    st = TNC_ERR_OUT_OF_MEMORY;
+  } catch (...) {
+    st = TNC_ERR_INVALID_ARG;
+  }
+  if (st != TNC_OK) {
+    delete p;
+    return st;
+  }
+  // the plan keeps no pointer into the caller's arrays
+  p->impl.opts.sliced_modes = nullptr;
+  *plan = p;
+  return TNC_OK;
+}
+
+void tnc_plan_destroy(tnc_plan_t plan) { delete plan; }
+
+tnc_status tnc_plan_workspace_bytes(tnc_plan_t plan, uint64_t *bytes) {
+  if (!plan || !bytes) return TNC_ERR_INVALID_ARG;
+  *bytes = plan->impl.stats.workspace_bytes;
+  return TNC_OK;
+}
+
+tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats) {
+  if (!plan || !stats) return TNC_ERR_INVALID_ARG;
+  *stats = plan->impl.stats;
+  return TNC_OK;
+}
+
+tnc_status tnc_plan_tensor_order(tnc_plan_t plan, int32_t id, int32_t *modes, int32_t *rank) {
+  if (!plan || !modes || !rank) return TNC_ERR_INVALID_ARG;
+  const auto &p = plan->impl;
+  if (id < 0 || id >= p.L + p.S) return TNC_ERR_INVALID_ARG;
+  const auto &o = p.order[id];
+  if ((int)o.size() > tnc::kMaxRank) return TNC_ERR_UNSUPPORTED;
+  for (size_t i = 0; i < o.size(); ++i) modes[i] = o[i];
+  *rank = (int32_t)o.size();
+  return TNC_OK;
+}
+
+tnc_status tnc_plan_tensor_offset(tnc_plan_t plan, int32_t id, uint64_t *offset) {
+  if (!plan || !offset) return TNC_ERR_INVALID_ARG;
+  const auto &p = plan->impl;
+  if (id < 0 || id >= p.L + p.S) return TNC_ERR_INVALID_ARG;
+  *offset = p.tensor_off[id];
+  return TNC_OK;
+}
+
+tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
+  if (!plan || !info) return TNC_ERR_INVALID_ARG;
+  const auto &p = plan->impl;
+  if (step < 0 || step >= p.S) return TNC_ERR_INVALID_ARG;
+  const tnc::Node &n = p.nodes[step];
+  std::memset(info, 0, sizeof(*info));
+  info->lhs = n.lhs;
+  info->rhs = n.rhs;
+  info->out = n.out;
+  info->kernel_class = n.cls;
+  info->swap = n.swap;
+  info->group = n.group;
+  info->splits = n.splits;
+  info->row_runs = (int32_t)n.row_runs.size();
+  info->col_runs = (int32_t)n.col_runs.size();
+  info->inner_run = (int32_t)(n.inner_run > INT32_MAX ? INT32_MAX : n.inner_run);
+  info->interleaved = n.interleaved;
+  info->copy_a = n.copy_a;
+  info->copy_b = n.copy_b;
+  info->m = n.m;
+  info->n = n.n;
+  info->k = n.k;
+  info->a_off = n.a_off;
+  info->b_off = n.b_off;
+  info->c_off = n.c_off;
+  info->scratch_off = n.scratch_off;
+  info->scratch_bytes = n.scratch_bytes;
+  return TNC_OK;
+}
+
+tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                       uint64_t workspace_bytes, void *stream_ptr) {
+  if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
+  const tnc::PlanImpl &p = plan->impl;
+  for (int32_t l = 0; l < p.L; ++l)
+    if (!leaves[l]) return TNC_ERR_INVALID_ARG;
+  if (workspace_bytes < p.stats.workspace_bytes) return TNC_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return TNC_ERR_INVALID_ARG;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+
+  char *ws = static_cast<char *>(workspace);
+  void **ptab = reinterpret_cast<void **>(ws);
+  char *blob = ws + p.ptab_bytes;
+  char *arena = ws + p.header_bytes;
+
+  tnc_status st = check(tnc::launch_write_ptrs(ptab, arena, out, leaves, p.L, stream), stream);
+  if (st != TNC_OK) return st;
+  if (hipMemcpyAsync(blob, p.blob.data(), p.blob.size(), hipMemcpyHostToDevice, stream) != hipSuccess)
+    return TNC_ERR_HIP;
+
+  const auto *runs = reinterpret_cast<const tnc::RunDev *>(blob + p.blob_runs);
+  const auto *cdesc = reinterpret_cast<const tnc::CopyDesc *>(blob + p.blob_copies);
+  const auto *tdesc = reinterpret_cast<const tnc::TinyDesc *>(blob + p.blob_tiny);
+  const auto *ints = reinterpret_cast<const int64_t *>(blob + p.blob_ints);
+
+  auto resolve = [&](int32_t buf, uint64_t off_bytes) -> char * {
+    if (buf == tnc::kBufArena) return arena + off_bytes;
+    if (buf == tnc::kBufOut) return static_cast<char *>(out) + off_bytes;
+    return const_cast<char *>(static_cast<const char *>(leaves[buf - tnc::kBufLeaf0])) + off_bytes;
+  };
+  auto operand = [&](const tnc::Node &nd, int w) -> const float2 * {
+    int32_t t = w == 0 ? nd.lhs : nd.rhs;
+    int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
+    uint64_t off = w == 0 ? nd.a_off : nd.b_off;
+    if (copy || t >= p.L) return reinterpret_cast<const float2 *>(arena + off);
+    return static_cast<const float2 *>(leaves[t]);
+  };
+
+  int64_t num_slices = p.stats.num_slices;
+  tnc::SliceDigits sd{};
+  sd.n = (int32_t)p.slice_extents.size();
+  for (int64_t sigma = 0; sigma < num_slices; ++sigma) {
+    // digits of sigma over the sliced extents, first sliced mode most significant
+    int64_t r = sigma;
+    for (int t = sd.n - 1; t >= 0; --t) {
+      sd.digit[t] = (int32_t)(r % p.slice_extents[t]);
+      r /= p.slice_extents[t];
+    }
+    const int32_t beta = sigma > 0 ? 1 : 0;
+    for (const tnc::Op &op : p.program) {
+      hipError_t e = hipSuccess;
+      switch (op.kind) {
+        case tnc::OP_COPY:
+          e = tnc::launch_copy(cdesc + op.first, op.count, op.max_count, ptab, ints, sd, beta, stream);
+          break;
+        case tnc::OP_TINY_GROUP:
+          e = tnc::launch_tiny(tdesc + op.first, op.count, ptab, runs, beta, stream);
+          break;
+        case tnc::OP_SKINNY:
+        case tnc::OP_GEMM: {
+          const tnc::Node &nd = p.nodes[op.first];
+          tnc::StepArgs a{};
+          a.X = operand(nd, nd.swap ? 1 : 0);
+          a.Y = operand(nd, nd.swap ? 0 : 1);
+          a.C = reinterpret_cast<float2 *>(nd.c_off == tnc::kNone ? resolve(tnc::kBufOut, 0)
+                                                                   : resolve(tnc::kBufArena, nd.c_off));
+          a.R = nd.swap ? nd.n : nd.m;
+          a.S = nd.swap ? nd.m : nd.n;
+          a.K = nd.k;
+          a.runs = runs + nd.runs_index;
+          a.nrr = (int32_t)nd.row_runs.size();
+          a.ncr = (int32_t)nd.col_runs.size();
+          a.beta = (nd.is_root && !p.root_permute) ? beta : 0;
+          a.splits = nd.splits;
+          a.scratch = nd.splits > 1 ? reinterpret_cast<float2 *>(arena + nd.scratch_off) : nullptr;
+          e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm(a, stream) : tnc::launch_skinny(a, stream);
+          break;
+        }
+      }
+      st = check(e, stream);
+      if (st != TNC_OK) return st;
+    }
+  }
+  return TNC_OK;
+}
+
+const char *tnc_status_string(tnc_status s) {
+  switch (s) {
+    case TNC_OK: return "TNC_OK";
+    case TNC_ERR_INVALID_ARG: return "TNC_ERR_INVALID_ARG";
+    case TNC_ERR_INVALID_NETWORK: return "TNC_ERR_INVALID_NETWORK";
+    case TNC_ERR_INVALID_TREE: return "TNC_ERR_INVALID_TREE";
+    case TNC_ERR_UNSUPPORTED: return "TNC_ERR_UNSUPPORTED";
+    case TNC_ERR_OUT_OF_MEMORY: return "TNC_ERR_OUT_OF_MEMORY";
+    case TNC_ERR_WORKSPACE_TOO_SMALL: return "TNC_ERR_WORKSPACE_TOO_SMALL";
+    case TNC_ERR_HIP: return "TNC_ERR_HIP";
+  }
+  return "TNC_ERR_UNKNOWN";
+}
+
+}  // extern "C"

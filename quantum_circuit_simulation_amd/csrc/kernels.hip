@@ -1,0 +1,439 @@
+// gfx950 kernels for tree contraction (complex64 data, FP32 arithmetic).
+//
+// Every pairwise step of the page "Parallelizing Large-Scale Tensor Network
+// Contraction on Multiple GPUs" (section 1.1) is, after lifetime ordering
+// (section 1.4), C[i, j] = sum_l X[i, l] * Y[j, l] with both operands stored
+// K-innermost.  Three kernels cover the step shapes:
+//   k_cgemm   - MFMA tiles (v_mfma_f32_32x32x2_f32) for steps with both
+//               sides > 16; the complex product is a real GEMM of shape
+//               (R, 2S, 2K) whose second operand is expanded on the fly;
+//   k_skinny  - VALU streaming for steps with one side <= 16 (HBM-bound);
+//   k_tiny    - one workgroup per step for the many small early-tree steps,
+//               a whole launch group per launch.
+// Outputs are stored through "runs": rowoff(i) + coloff(j), so a product
+// whose order interleaves the two operands' modes is written in place with
+// no separate permute.  k_copy is a generic strided permute used only for
+// leaf staging and for the naive-order ablation.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace tnc {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void cmac(float2 &acc, float2 a, float2 b) {
+  acc.x = fmaf(a.x, b.x, acc.x);
+  acc.x = fmaf(-a.y, b.y, acc.x);
+  acc.y = fmaf(a.x, b.y, acc.y);
+  acc.y = fmaf(a.y, b.x, acc.y);
+}
+
+// Offset in C (entries) of index `idx` along one side, runs outermost first.
+__device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int n) {
+  int64_t off = 0;
+  for (int q = n - 1; q >= 0; --q) {
+    const int64_t sz = r[q].size;
+    const int64_t d = idx % sz;
+    idx /= sz;
+    off += d * r[q].stride;
+  }
+  return off;
+}
+
+__device__ __forceinline__ void store_c(float2 *p, float2 v, int beta) {
+  if (beta) {
+    float2 o = *p;
+    v.x += o.x;
+    v.y += o.y;
+  }
+  *p = v;
+}
+
+// ---------------------------------------------------------------------------
+// device pointer table
+
+constexpr int kPtrsPerLaunch = 250;
+struct PtrChunk {
+  void *p[kPtrsPerLaunch];
+  int32_t count;
+  int32_t first;
+};
+
+__global__ void k_write_ptrs(void **dst, PtrChunk c) {
+  int t = threadIdx.x;
+  for (int i = t; i < c.count; i += blockDim.x) dst[c.first + i] = c.p[i];
+}
+
+// ---------------------------------------------------------------------------
+// permuting copy (leaf staging, naive-order re-layout, root permute)
+
+__global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int64_t *ints, SliceDigits sd,
+                       int32_t beta) {
+  const CopyDesc d = descs[blockIdx.y];
+  const int64_t *dims = ints + d.ints_index;
+  const int64_t *sst = dims + d.rank;
+  const int64_t *slc = sst + d.rank;
+  int64_t base = d.src_off;
+  for (int t = 0; t < sd.n; ++t) base += (int64_t)sd.digit[t] * slc[t];
+  const float2 *src = (const float2 *)ptab[d.src_buf] + base;
+  float2 *dst = (float2 *)ptab[d.dst_buf] + d.dst_off;
+  const int b = beta && d.is_root;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < d.count; e += step) {
+    int64_t r = e, so = 0;
+    for (int p = d.rank - 1; p >= 0; --p) {
+      const int64_t dm = dims[p];
+      so += (r % dm) * sst[p];
+      r /= dm;
+    }
+    store_c(dst + e, src[so], b);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grouped tiny steps: one workgroup per step
+
+__global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
+                                              int32_t beta) {
+  const TinyDesc d = descs[blockIdx.x];
+  const float2 *X = (const float2 *)ptab[d.x_buf] + d.x_off;
+  const float2 *Y = (const float2 *)ptab[d.y_buf] + d.y_off;
+  float2 *C = (float2 *)ptab[d.c_buf] + d.c_off;
+  const RunDev *rr = runs + d.runs_index;
+  const RunDev *cr = rr + d.nrr;
+  const int R = d.R, S = d.S, K = d.K;
+  const int outputs = R * S;
+  // lanes per output: a power of two <= 64 that keeps the workgroup busy
+  int G = 1;
+  while (G < 64 && G * 2 <= K && outputs * G * 2 <= 256) G *= 2;
+  const int per_pass = 256 / G;
+  const int lane = threadIdx.x % G;
+  const int grp = threadIdx.x / G;
+  const int b = beta && d.is_root;
+  for (int o0 = 0; o0 < outputs; o0 += per_pass) {
+    const int o = o0 + grp;
+    float2 acc = make_float2(0.f, 0.f);
+    if (o < outputs) {
+      const int i = o / S, j = o - (o / S) * S;
+      const float2 *xr = X + (int64_t)i * K;
+      const float2 *yr = Y + (int64_t)j * K;
+      for (int l = lane; l < K; l += G) cmac(acc, xr[l], yr[l]);
+    }
+    for (int w = 1; w < G; w *= 2) {
+      acc.x += __shfl_xor(acc.x, w, 64);
+      acc.y += __shfl_xor(acc.y, w, 64);
+    }
+    if (o < outputs && lane == 0) {
+      const int i = o / S, j = o - (o / S) * S;
+      store_c(C + run_offset(i, rr, d.nrr) + run_offset(j, cr, d.ncr), acc, b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// skinny steps: S <= 16 columns, rows streamed from HBM
+
+constexpr int kSkinnyMax = 16;
+
+__global__ __launch_bounds__(256) void k_skinny(StepArgs a, int64_t kchunk, int G) {
+  const int rows_per_block = 256 / G;
+  const int lane = threadIdx.x % G;
+  const int64_t i = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / G;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  const int S = (int)a.S;
+  float2 acc[kSkinnyMax];
+#pragma unroll
+  for (int s = 0; s < kSkinnyMax; ++s) acc[s] = make_float2(0.f, 0.f);
+  if (i < a.R) {
+    const float2 *xr = a.X + i * a.K;
+    for (int64_t l = k0 + lane; l < k1; l += G) {
+      const float2 x = xr[l];
+#pragma unroll
+      for (int s = 0; s < kSkinnyMax; ++s)
+        if (s < S) cmac(acc[s], x, a.Y[(int64_t)s * a.K + l]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kSkinnyMax; ++s) {
+    for (int w = 1; w < G; w *= 2) {
+      acc[s].x += __shfl_xor(acc[s].x, w, 64);
+      acc[s].y += __shfl_xor(acc[s].y, w, 64);
+    }
+  }
+  if (i < a.R && lane == 0) {
+    if (a.splits > 1) {
+      float2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
+#pragma unroll
+      for (int s = 0; s < kSkinnyMax; ++s)
+        if (s < S) p[s] = acc[s];
+    } else {
+      const int64_t ro = run_offset(i, a.runs, a.nrr);
+#pragma unroll
+      for (int s = 0; s < kSkinnyMax; ++s)
+        if (s < S) store_c(a.C + ro + run_offset(s, a.runs + a.nrr, a.ncr), acc[s], a.beta);
+    }
+  }
+}
+
+// sum split-K partials [splits, R, S] into C through the runs
+__global__ void k_split_reduce(StepArgs a) {
+  const int64_t total = a.R * a.S;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
+    float2 acc = make_float2(0.f, 0.f);
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float2 v = a.scratch[(int64_t)sp * total + e];
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    const int64_t i = e / a.S, j = e - (e / a.S) * a.S;
+    store_c(a.C + run_offset(i, a.runs, a.nrr) + run_offset(j, a.runs + a.nrr, a.ncr), acc, a.beta);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// complex GEMM on FP32 MFMA.
+//
+// Real view: with x = (xr, xi) and y = (yr, yi),
+//   Cr = sum_l xr*yr + xi*(-yi),   Ci = sum_l xr*yi + xi*yr.
+// v_mfma_f32_32x32x2_f32 multiplies a 32x2 block by a 2x32 block.  Its
+// 2-long reduction axis is used for (re, im) of one complex l: lanes 0-31
+// supply xr of rows 0-31 and lanes 32-63 supply xi.  For the real-part
+// product the second operand carries (yr, -yi); for the imaginary part
+// (yi, yr).  So one complex l costs two MFMAs per 32x32 complex block and
+// the operation count is exactly 8 R S K.
+//
+// LDS holds the X tile de-interleaved as two planes (re, im) and the Y tile
+// as three planes (yr, -yi, yi), each [rows][BK + pad]; a lane reads four
+// consecutive l of its plane with one 16-byte load.  Two LDS stages overlap
+// the global loads of the next K tile with the MFMAs of the current one.
+
+template <int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, int64_t tiles_c) {
+  constexpr int PAD = 4;
+  constexpr int LDK = BK + PAD;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int WAVES_C = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert(BK % 4 == 0, "BK");
+  constexpr int A_PER = BM * BK / 256;
+  constexpr int B_PER = BN * BK / 256;
+  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for 256 threads");
+
+  __shared__ float As[2][2][BM][LDK];
+  __shared__ float Bs[2][3][BN][LDK];
+  __shared__ int64_t rowoff[BM];
+  __shared__ int64_t coloff[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WAVES_C, wc = wave % WAVES_C;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t tile = blockIdx.x;
+  const int64_t r0 = (tile / tiles_c) * BM, c0 = (tile % tiles_c) * BN;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  const int64_t nkt = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+  const int64_t R = a.R, S = a.S, K = a.K;
+
+  f32x16 accR[MB][NB], accI[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accR[mb][nb][r] = 0.f;
+        accI[mb][nb][r] = 0.f;
+      }
+    }
+
+  float2 ra[A_PER], rb[B_PER];
+  auto gload = [&](int64_t kt) {
+    const int64_t kb = k0 + kt * BK;
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      const int64_t gi = r0 + row, gl = kb + l;
+      ra[q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      const int64_t gj = c0 + col, gl = kb + l;
+      rb[q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : make_float2(0.f, 0.f);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      As[st][0][row][l] = ra[q].x;
+      As[st][1][row][l] = ra[q].y;
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      Bs[st][0][col][l] = rb[q].x;
+      Bs[st][1][col][l] = -rb[q].y;
+      Bs[st][2][col][l] = rb[q].y;
+    }
+  };
+
+  const int arow = wr * WM + l32;
+  const int bcol = wc * WN + l32;
+  const int pbr = h ? 1 : 0;  // plane feeding the real-part MFMA: yr (lanes 0-31), -yi (32-63)
+  const int pbi = h ? 0 : 2;  // imaginary part: yi (lanes 0-31), yr (32-63)
+
+  if (nkt > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    const int st = (int)(kt & 1);
+    if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+    for (int l4 = 0; l4 < BK; l4 += 4) {
+      f32x4 av[MB], brv[NB], biv[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[mb] = *(const f32x4 *)&As[st][h][arow + mb * 32][l4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        brv[nb] = *(const f32x4 *)&Bs[st][pbr][bcol + nb * 32][l4];
+        biv[nb] = *(const f32x4 *)&Bs[st][pbi][bcol + nb * 32][l4];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            accR[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb][kk], brv[nb][kk], accR[mb][nb], 0, 0, 0);
+            accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb][kk], biv[nb][kk], accI[mb][nb], 0, 0, 0);
+          }
+    }
+    if (kt + 1 < nkt) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: output offsets of this tile's rows and columns
+  const bool partial = a.splits > 1;
+  if (!partial) {
+    for (int t = tid; t < BM; t += 256) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += 256) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wc * WN + nb * 32 + l32;
+      const int64_t gj = c0 + col;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * WM + mb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+        const int64_t gi = r0 + row;
+        if (gi < R && gj < S) {
+          const float2 v = make_float2(accR[mb][nb][r], accI[mb][nb][r]);
+          if (partial) a.scratch[((int64_t)split * R + gi) * S + gj] = v;
+          else store_c(a.C + rowoff[row] + coloff[col], v, a.beta);
+        }
+      }
+    }
+}
+
+int pow2_floor_i(int64_t v) {
+  int p = 1;
+  while ((int64_t)p * 2 <= v && p < (1 << 30)) p *= 2;
+  return p;
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
+  const int64_t tiles_r = (a.R + BM - 1) / BM, tiles_c = (a.S + BN - 1) / BN;
+  int64_t kchunk = a.K;
+  if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  dim3 grid((unsigned)(tiles_r * tiles_c), (unsigned)a.splits);
+  hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, kchunk, tiles_c);
+  return hipGetLastError();
+}
+
+hipError_t run_split_reduce(const StepArgs &a, hipStream_t stream) {
+  const int64_t total = a.R * a.S;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *const *leaves, int32_t num_leaves,
+                             hipStream_t stream) {
+  const int32_t total = num_leaves + 2;
+  for (int32_t first = 0; first < total; first += kPtrsPerLaunch) {
+    PtrChunk c;
+    c.first = first;
+    c.count = total - first < kPtrsPerLaunch ? total - first : kPtrsPerLaunch;
+    for (int i = 0; i < c.count; ++i) {
+      int32_t id = first + i;
+      c.p[i] = id == 0 ? arena : id == 1 ? out : const_cast<void *>(leaves[id - 2]);
+    }
+    hipLaunchKernelGGL(k_write_ptrs, dim3(1), dim3(64), 0, stream, dst, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, const void *const *ptab,
+                       const int64_t *ints, const SliceDigits &digits, int32_t beta, hipStream_t stream) {
+  int64_t blocks = (max_count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, descs, ptab, ints,
+                     digits, beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
+                       int32_t beta, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tiny, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
+  int64_t kchunk = a.K;
+  if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
+  int G = pow2_floor_i(kchunk / 8);
+  if (G > 64) G = 64;
+  if (G < 1) G = 1;
+  const int rows_per_block = 256 / G;
+  dim3 grid((unsigned)((a.R + rows_per_block - 1) / rows_per_block), (unsigned)a.splits);
+  hipLaunchKernelGGL(k_skinny, grid, dim3(256), 0, stream, a, kchunk, G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return run_split_reduce(a, stream);
+}
+
+hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
+  hipError_t e;
+  if (a.S > 64) e = run_cgemm<128, 128, 8, 64, 64>(a, stream);
+  else if (a.S > 32) e = run_cgemm<256, 64, 8, 64, 64>(a, stream);
+  else e = run_cgemm<256, 32, 8, 64, 32>(a, stream);
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return run_split_reduce(a, stream);
+}
+
+}  // namespace tnc

@@ -1,0 +1,620 @@
+// Host planner: validation, lifetime ordering, step descriptors, launch
+// groups, first-fit arena and the device descriptor blob.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <list>
+#include <set>
+
+namespace tnc {
+namespace {
+
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+int64_t pow2_floor(int64_t v) {
+  int64_t p = 1;
+  while (p * 2 <= v) p *= 2;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// product of extents of `modes`; returns false on int64 overflow
+bool checked_prod(const std::vector<int64_t> &ext, const std::vector<int32_t> &modes, int64_t *out) {
+  __int128 p = 1;
+  for (int32_t x : modes) {
+    p *= ext[x];
+    if (p > (__int128)(INT64_MAX / 8)) return false;
+  }
+  *out = (int64_t)p;
+  return true;
+}
+
+int64_t prod(const std::vector<int64_t> &ext, const std::vector<int32_t> &modes) {
+  int64_t p = 1;
+  for (int32_t x : modes) p *= ext[x];
+  return p;
+}
+
+bool contains(const std::vector<int32_t> &v, int32_t x) { return std::find(v.begin(), v.end(), x) != v.end(); }
+
+// First-fit arena over a sorted free list of holes; the last hole is unbounded.
+class Arena {
+ public:
+  uint64_t alloc(uint64_t size) {
+    for (auto it = holes_.begin(); it != holes_.end(); ++it) {
+      if (it->second == kNone || it->second - it->first >= size) {
+        uint64_t off = it->first;
+        it->first += size;
+        if (it->second != kNone && it->first == it->second) holes_.erase(it);
+        peak_ = std::max(peak_, off + size);
+        return off;
+      }
+    }
+    return kNone;  // unreachable: the last hole is unbounded
+  }
+  void release(uint64_t off, uint64_t size) {
+    auto it = holes_.begin();
+    while (it != holes_.end() && it->first < off) ++it;
+    it = holes_.insert(it, {off, off + size});
+    // merge with the next hole
+    auto nx = std::next(it);
+    if (nx != holes_.end() && it->second == nx->first) {
+      it->second = nx->second;
+      holes_.erase(nx);
+    }
+    // merge with the previous hole
+    if (it != holes_.begin()) {
+      auto pv = std::prev(it);
+      if (pv->second == it->first) {
+        pv->second = it->second;
+        holes_.erase(it);
+      }
+    }
+  }
+  uint64_t peak() const { return peak_; }
+
+ private:
+  std::list<std::pair<uint64_t, uint64_t>> holes_{{0, kNone}};
+  uint64_t peak_ = 0;
+};
+
+int32_t split_rule(int32_t cls, int64_t R, int64_t S, int64_t k) {
+  if (cls == TNC_CLASS_GEMM) {
+    int64_t tiles = ceil_div(R, kGemmNominalTile) * ceil_div(S, kGemmNominalTile);
+    if (tiles >= 128 || k < 4096) return 1;
+    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(256 / tiles), pow2_floor(k / 2048)));
+  }
+  if (cls == TNC_CLASS_SKINNY) {
+    int64_t blocks = ceil_div(R, 256);
+    if (blocks >= 512 || k < 4096) return 1;
+    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(1024 / blocks), pow2_floor(k / 2048)));
+  }
+  return 1;
+}
+
+// Output runs of C along `c_order` (extent-1 modes skipped).
+void make_runs(const std::vector<int32_t> &c_order, const std::vector<int64_t> &ext,
+               const std::vector<int32_t> &row_modes, Node *nd) {
+  std::vector<int32_t> eff;
+  for (int32_t x : c_order)
+    if (ext[x] > 1) eff.push_back(x);
+  std::vector<int64_t> stride(eff.size());
+  int64_t s = 1;
+  for (int p = (int)eff.size() - 1; p >= 0; --p) {
+    stride[p] = s;
+    s *= ext[eff[p]];
+  }
+  struct R3 { bool row; int64_t size, stride; };
+  std::vector<R3> runs;
+  for (size_t p = 0; p < eff.size(); ++p) {
+    bool side = contains(row_modes, eff[p]);
+    if (!runs.empty() && runs.back().row == side) {
+      runs.back().size *= ext[eff[p]];
+      runs.back().stride = stride[p];
+    } else {
+      runs.push_back({side, ext[eff[p]], stride[p]});
+    }
+  }
+  nd->row_runs.clear();
+  nd->col_runs.clear();
+  for (auto &r : runs) (r.row ? nd->row_runs : nd->col_runs).push_back({r.size, r.stride});
+  nd->inner_run = runs.empty() ? 1 : runs.back().size;
+  nd->interleaved = runs.size() > 2 ? 1 : 0;
+}
+
+tnc_status validate(PlanImpl *p, const tnc_network *net, const tnc_tree *tree) {
+  const int32_t nm = net->num_modes;
+  if (nm < 0) return TNC_ERR_INVALID_NETWORK;
+  if (nm > 0 && !net->extents) return TNC_ERR_INVALID_ARG;
+  for (int32_t x = 0; x < nm; ++x)
+    if (net->extents[x] < 1) return TNC_ERR_INVALID_NETWORK;
+  if (net->num_leaves < 1) return TNC_ERR_INVALID_ARG;
+  if (!net->leaf_rank) return TNC_ERR_INVALID_ARG;
+  const int32_t L = net->num_leaves;
+  std::vector<int> count(nm, 0);
+  int64_t pos = 0;
+  p->leaves.resize(L);
+  for (int32_t l = 0; l < L; ++l) {
+    int32_t r = net->leaf_rank[l];
+    if (r < 0) return TNC_ERR_INVALID_NETWORK;
+    if (r > 0 && !net->leaf_modes) return TNC_ERR_INVALID_ARG;
+    std::vector<int32_t> ms(net->leaf_modes + pos, net->leaf_modes + pos + r);
+    pos += r;
+    std::vector<int32_t> sorted_ms = ms;
+    std::sort(sorted_ms.begin(), sorted_ms.end());
+    if (std::adjacent_find(sorted_ms.begin(), sorted_ms.end()) != sorted_ms.end()) return TNC_ERR_UNSUPPORTED;
+    for (int32_t x : ms) {
+      if (x < 0 || x >= nm) return TNC_ERR_INVALID_NETWORK;
+      count[x]++;
+    }
+    p->leaves[l] = std::move(ms);
+  }
+  if (net->out_rank < 0 || (net->out_rank > 0 && !net->out_modes)) return TNC_ERR_INVALID_ARG;
+  std::vector<int32_t> out(net->out_modes, net->out_modes + net->out_rank);
+  {
+    std::vector<int32_t> so = out;
+    std::sort(so.begin(), so.end());
+    if (std::adjacent_find(so.begin(), so.end()) != so.end()) return TNC_ERR_INVALID_NETWORK;
+  }
+  std::vector<char> in_out(nm, 0);
+  for (int32_t x : out) {
+    if (x < 0 || x >= nm) return TNC_ERR_INVALID_NETWORK;
+    in_out[x] = 1;
+  }
+  for (int32_t x = 0; x < nm; ++x) {
+    int c = count[x] + (in_out[x] ? 1 : 0);
+    if (c > 2) return TNC_ERR_UNSUPPORTED;
+    if (c == 1) return TNC_ERR_INVALID_NETWORK;
+    if (in_out[x] && count[x] != 1) return TNC_ERR_INVALID_NETWORK;
+  }
+  const int32_t S = tree->num_steps;
+  if (S != L - 1) return TNC_ERR_INVALID_TREE;
+  if (S > 0 && (!tree->lhs || !tree->rhs)) return TNC_ERR_INVALID_ARG;
+  std::vector<char> used(L + S, 0);
+  for (int32_t s = 0; s < S; ++s) {
+    int32_t a = tree->lhs[s], b = tree->rhs[s];
+    for (int32_t t : {a, b}) {
+      if (t < 0 || t >= L + s || used[t]) return TNC_ERR_INVALID_TREE;
+      used[t] = 1;
+    }
+    if (a == b) return TNC_ERR_INVALID_TREE;
+  }
+  // sliced modes
+  const tnc_plan_options &o = p->opts;
+  if (o.num_sliced < 0 || (o.num_sliced > 0 && !o.sliced_modes)) return TNC_ERR_INVALID_ARG;
+  if (o.num_sliced > kMaxSliced) return TNC_ERR_UNSUPPORTED;
+  std::vector<int32_t> sl(o.sliced_modes, o.sliced_modes + o.num_sliced);
+  {
+    std::vector<int32_t> ss = sl;
+    std::sort(ss.begin(), ss.end());
+    if (std::adjacent_find(ss.begin(), ss.end()) != ss.end()) return TNC_ERR_INVALID_ARG;
+  }
+  for (int32_t x : sl)
+    if (x < 0 || x >= nm || count[x] != 2) return TNC_ERR_INVALID_ARG;
+
+  p->num_modes = nm;
+  p->extents.assign(net->extents, net->extents + nm);
+  p->out_modes = out;
+  p->lhs.assign(tree->lhs, tree->lhs + S);
+  p->rhs.assign(tree->rhs, tree->rhs + S);
+  p->sliced = sl;
+  p->L = L;
+  p->S = S;
+  return TNC_OK;
+}
+
+}  // namespace
+
+tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
+                      PlanImpl *p) {
+  if (!net || !tree || !p) return TNC_ERR_INVALID_ARG;
+  if (opts) p->opts = *opts;
+  else tnc_plan_options_default(&p->opts);
+  const tnc_plan_options &o = p->opts;
+  if (o.align < 256 || (o.align & (o.align - 1)) != 0) return TNC_ERR_INVALID_ARG;
+  if (o.max_group < 1) return TNC_ERR_INVALID_ARG;
+  if (o.order != TNC_ORDER_LIFETIME && o.order != TNC_ORDER_NAIVE) return TNC_ERR_INVALID_ARG;
+  if (net->dtype != TNC_C64) return TNC_ERR_UNSUPPORTED;
+  tnc_status st = validate(p, net, tree);
+  if (st != TNC_OK) return st;
+
+  const int32_t L = p->L, S = p->S, T = L + S;
+  p->ext = p->extents;
+  for (int32_t x : p->sliced) p->ext[x] = 1;
+  const std::vector<int64_t> &ext = p->ext;
+
+  // ---- SSA mode sets (sliced modes removed), per-step K/M/N
+  std::vector<std::vector<int32_t>> sets(T);  // sorted mode lists
+  std::vector<std::vector<int32_t>> declared(L);
+  std::vector<char> has_sliced(L, 0);
+  for (int32_t l = 0; l < L; ++l) {
+    for (int32_t x : p->leaves[l]) {
+      if (contains(p->sliced, x)) has_sliced[l] = 1;
+      else declared[l].push_back(x);
+    }
+    if ((int)declared[l].size() > kMaxRank) return TNC_ERR_UNSUPPORTED;
+    sets[l] = declared[l];
+    std::sort(sets[l].begin(), sets[l].end());
+    int64_t tmp;
+    if (!checked_prod(p->extents, p->leaves[l], &tmp)) return TNC_ERR_UNSUPPORTED;
+  }
+  std::vector<std::vector<int32_t>> K(S), M(S), N(S);
+  for (int32_t s = 0; s < S; ++s) {
+    const auto &A = sets[p->lhs[s]], &B = sets[p->rhs[s]];
+    std::set_intersection(A.begin(), A.end(), B.begin(), B.end(), std::back_inserter(K[s]));
+    std::set_difference(A.begin(), A.end(), K[s].begin(), K[s].end(), std::back_inserter(M[s]));
+    std::set_difference(B.begin(), B.end(), K[s].begin(), K[s].end(), std::back_inserter(N[s]));
+    std::vector<int32_t> C;
+    std::set_union(M[s].begin(), M[s].end(), N[s].begin(), N[s].end(), std::back_inserter(C));
+    if ((int)C.size() > kMaxRank) return TNC_ERR_UNSUPPORTED;
+    int64_t tmp;
+    if (!checked_prod(p->extents, C, &tmp)) return TNC_ERR_UNSUPPORTED;
+    sets[L + s] = std::move(C);
+  }
+
+  // ---- orders
+  p->order.assign(T, {});
+  p->gemm_a.assign(S, {});
+  p->gemm_b.assign(S, {});
+  const bool naive = o.order == TNC_ORDER_NAIVE;
+  if (!naive) {
+    // Reverse pass (page section 1.4): the root takes the output order; each
+    // operand keeps its product's order restricted to its own modes and gets
+    // the reduced modes (ascending label) appended.
+    p->order[T - 1] = p->out_modes;
+    for (int32_t s = S - 1; s >= 0; --s) {
+      const auto &c_order = p->order[L + s];
+      for (int32_t operand : {p->lhs[s], p->rhs[s]}) {
+        std::vector<int32_t> o2;
+        for (int32_t x : c_order)
+          if (std::binary_search(sets[operand].begin(), sets[operand].end(), x)) o2.push_back(x);
+        o2.insert(o2.end(), K[s].begin(), K[s].end());
+        p->order[operand] = std::move(o2);
+      }
+    }
+    for (int32_t s = 0; s < S; ++s) {
+      p->gemm_a[s] = p->order[p->lhs[s]];
+      p->gemm_b[s] = p->order[p->rhs[s]];
+    }
+    p->root_permute = 0;
+  } else {
+    for (int32_t l = 0; l < L; ++l) p->order[l] = declared[l];
+    for (int32_t s = 0; s < S; ++s) {
+      std::vector<int32_t> ra, rb;
+      for (int32_t x : p->order[p->lhs[s]])
+        if (!std::binary_search(K[s].begin(), K[s].end(), x)) ra.push_back(x);
+      for (int32_t x : p->order[p->rhs[s]])
+        if (!std::binary_search(K[s].begin(), K[s].end(), x)) rb.push_back(x);
+      p->gemm_a[s] = ra;
+      p->gemm_a[s].insert(p->gemm_a[s].end(), K[s].begin(), K[s].end());
+      p->gemm_b[s] = rb;
+      p->gemm_b[s].insert(p->gemm_b[s].end(), K[s].begin(), K[s].end());
+      ra.insert(ra.end(), rb.begin(), rb.end());
+      p->order[L + s] = ra;
+    }
+    p->root_permute = (S > 0 && p->order[T - 1] != p->out_modes) ? 1 : 0;
+  }
+  if (S == 0) p->order[0] = p->out_modes;
+
+  // ---- nodes
+  p->staged_leaf.assign(L, 0);
+  p->nodes.assign(S, Node{});
+  double flops = 0, flops_u = 0, bytes = 0;
+  uint64_t max_elems = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    Node &nd = p->nodes[s];
+    nd.lhs = p->lhs[s];
+    nd.rhs = p->rhs[s];
+    nd.out = L + s;
+    nd.is_root = (s == S - 1) ? 1 : 0;
+    nd.m = prod(ext, M[s]);
+    nd.n = prod(ext, N[s]);
+    nd.k = prod(ext, K[s]);
+    nd.mu = prod(p->extents, M[s]);
+    nd.nu = prod(p->extents, N[s]);
+    nd.ku = prod(p->extents, K[s]);
+    flops += 8.0 * (double)nd.m * (double)nd.n * (double)nd.k;
+    flops_u += 8.0 * (double)nd.mu * (double)nd.nu * (double)nd.ku;
+    bytes += 8.0 * ((double)nd.m * nd.k + (double)nd.n * nd.k + (double)nd.m * nd.n);
+    max_elems = std::max<uint64_t>(max_elems, (uint64_t)(nd.m * nd.n));
+    __int128 mnk = (__int128)nd.m * nd.n * nd.k;
+    if (mnk <= (__int128)o.tiny_mnk) nd.cls = TNC_CLASS_TINY;
+    else if (std::min(nd.m, nd.n) <= kSkinnyMaxSide) nd.cls = TNC_CLASS_SKINNY;
+    else nd.cls = TNC_CLASS_GEMM;
+    const auto &c_order = p->order[L + s];
+    int32_t last_eff = -1;
+    for (int32_t x : c_order)
+      if (ext[x] > 1) last_eff = x;
+    if (nd.cls == TNC_CLASS_SKINNY) nd.swap = nd.n > nd.m ? 1 : 0;
+    else nd.swap = (last_eff >= 0 && std::binary_search(M[s].begin(), M[s].end(), last_eff)) ? 1 : 0;
+    make_runs(c_order, ext, nd.swap ? N[s] : M[s], &nd);
+    int64_t R = nd.swap ? nd.n : nd.m, Sx = nd.swap ? nd.m : nd.n;
+    nd.splits = split_rule(nd.cls, R, Sx, nd.k);
+    if (nd.splits > 1) nd.scratch_bytes = (uint64_t)nd.splits * (uint64_t)R * (uint64_t)Sx * 8;
+    // operand copies
+    for (int w = 0; w < 2; ++w) {
+      int32_t t = w == 0 ? nd.lhs : nd.rhs;
+      const auto &want = w == 0 ? p->gemm_a[s] : p->gemm_b[s];
+      int need;
+      if (t < L) {
+        need = (has_sliced[t] || declared[t] != want) ? 1 : 0;
+        if (need) p->staged_leaf[t] = 1;
+      } else {
+        need = p->order[t] != want ? 1 : 0;
+      }
+      (w == 0 ? nd.copy_a : nd.copy_b) = need;
+    }
+  }
+  if (S == 0) p->staged_leaf.assign(L, 0);
+
+  // ---- launch groups: consecutive tiny steps with no dependency inside the group
+  p->groups.clear();
+  bool open_tiny = false;
+  std::vector<int32_t> produced;
+  for (int32_t s = 0; s < S; ++s) {
+    Node &nd = p->nodes[s];
+    if (nd.cls == TNC_CLASS_TINY) {
+      if (open_tiny && (int32_t)p->groups.back().size() < o.max_group && !contains(produced, nd.lhs) &&
+          !contains(produced, nd.rhs)) {
+        p->groups.back().push_back(s);
+      } else {
+        p->groups.push_back({s});
+        open_tiny = true;
+        produced.clear();
+      }
+      produced.push_back(nd.out);
+    } else {
+      p->groups.push_back({s});
+      open_tiny = false;
+      produced.clear();
+    }
+  }
+  for (size_t g = 0; g < p->groups.size(); ++g)
+    for (int32_t s : p->groups[g]) p->nodes[s].group = (int32_t)g;
+
+  // ---- arena
+  auto rbytes = [&](int64_t elems) { return round_up((uint64_t)elems * 8, o.align); };
+  std::vector<int64_t> elems(T);
+  for (int32_t t = 0; t < T; ++t) elems[t] = prod(ext, sets[t]);
+  Arena arena;
+  p->tensor_off.assign(T, kNone);
+  for (auto &members : p->groups) {
+    std::vector<std::pair<uint64_t, uint64_t>> to_free;
+    for (int32_t s : members) {
+      Node &nd = p->nodes[s];
+      for (int w = 0; w < 2; ++w) {
+        int32_t t = w == 0 ? nd.lhs : nd.rhs;
+        int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
+        uint64_t &off = w == 0 ? nd.a_off : nd.b_off;
+        if (copy) {
+          off = arena.alloc(rbytes(elems[t]));
+          to_free.push_back({off, rbytes(elems[t])});
+          if (t < L && !naive) p->tensor_off[t] = off;
+        } else if (t >= L) {
+          off = p->tensor_off[t];
+          to_free.push_back({off, rbytes(elems[t])});
+        }
+      }
+      if (nd.is_root && !p->root_permute) {
+        nd.c_off = kNone;
+      } else {
+        nd.c_off = arena.alloc(rbytes(elems[nd.out]));
+        p->tensor_off[nd.out] = nd.c_off;
+      }
+      if (nd.splits > 1) {
+        uint64_t sb = round_up(nd.scratch_bytes, o.align);
+        nd.scratch_off = arena.alloc(sb);
+        to_free.push_back({nd.scratch_off, sb});
+      }
+    }
+    for (auto &f : to_free) arena.release(f.first, f.second);
+  }
+  p->arena_bytes = arena.peak();
+
+  // ---- copies and the launch program
+  p->slice_extents.clear();
+  for (int32_t x : p->sliced) p->slice_extents.push_back(p->extents[x]);
+  auto leaf_strides = [&](int32_t l) {
+    // declared row-major strides with full (unsliced) extents
+    std::vector<int64_t> st(p->leaves[l].size());
+    int64_t s = 1;
+    for (int q = (int)p->leaves[l].size() - 1; q >= 0; --q) {
+      st[q] = s;
+      s *= p->extents[p->leaves[l][q]];
+    }
+    return st;
+  };
+  auto make_copy = [&](int32_t src_tensor, int32_t src_buf, uint64_t src_off, int32_t dst_buf, uint64_t dst_off,
+                       const std::vector<int32_t> &dst_order, int32_t is_root) {
+    CopyOp c;
+    c.src_buf = src_buf;
+    c.src_off_bytes = src_off;
+    c.dst_buf = dst_buf;
+    c.dst_off_bytes = dst_off;
+    c.is_root = is_root;
+    // source strides of every mode
+    std::vector<int32_t> src_modes;
+    std::vector<int64_t> src_st;
+    if (src_tensor < L) {
+      src_modes = p->leaves[src_tensor];
+      src_st = leaf_strides(src_tensor);
+    } else {
+      src_modes = p->order[src_tensor];
+      src_st.resize(src_modes.size());
+      int64_t s = 1;
+      for (int q = (int)src_modes.size() - 1; q >= 0; --q) {
+        src_st[q] = s;
+        s *= ext[src_modes[q]];
+      }
+    }
+    auto stride_of = [&](int32_t x) -> int64_t {
+      for (size_t q = 0; q < src_modes.size(); ++q)
+        if (src_modes[q] == x) return src_st[q];
+      return 0;
+    };
+    std::vector<int64_t> dims, sst;
+    for (int32_t x : dst_order) {
+      if (ext[x] <= 1) continue;
+      int64_t d = ext[x], ss = stride_of(x);
+      if (!dims.empty() && sst.back() == ss * d) {
+        dims.back() *= d;
+        sst.back() = ss;
+      } else {
+        dims.push_back(d);
+        sst.push_back(ss);
+      }
+    }
+    c.dims = dims;
+    c.src_strides = sst;
+    c.count = prod(ext, dst_order);
+    for (int32_t x : p->sliced) c.slice_strides.push_back(src_tensor < L ? stride_of(x) : 0);
+    return c;
+  };
+  p->copies.clear();
+  p->program.clear();
+  auto push_copy_op = [&](int32_t idx) {
+    const int64_t kBig = int64_t(1) << 20;
+    int64_t cnt = p->copies[idx].count;
+    if (!p->program.empty() && p->program.back().kind == OP_COPY && cnt <= kBig &&
+        p->program.back().max_count <= kBig && p->program.back().first + p->program.back().count == idx) {
+      p->program.back().count++;
+      p->program.back().max_count = std::max(p->program.back().max_count, cnt);
+    } else {
+      p->program.push_back({OP_COPY, idx, 1, cnt});
+    }
+  };
+  if (S == 0) {
+    p->copies.push_back(make_copy(0, kBufLeaf0 + 0, 0, kBufOut, 0, p->out_modes, 1));
+    push_copy_op(0);
+  }
+  std::vector<TinyDesc> tiny;
+  std::vector<RunDev> runs;
+  for (auto &members : p->groups) {
+    // staging / re-layout copies of this group's operands
+    for (int32_t s : members) {
+      Node &nd = p->nodes[s];
+      for (int w = 0; w < 2; ++w) {
+        int32_t t = w == 0 ? nd.lhs : nd.rhs;
+        if (!(w == 0 ? nd.copy_a : nd.copy_b)) continue;
+        uint64_t dst = w == 0 ? nd.a_off : nd.b_off;
+        const auto &want = w == 0 ? p->gemm_a[s] : p->gemm_b[s];
+        int32_t src_buf = t < L ? kBufLeaf0 + t : kBufArena;
+        uint64_t src_off = t < L ? 0 : p->tensor_off[t];
+        p->copies.push_back(make_copy(t, src_buf, src_off, kBufArena, dst, want, 0));
+        push_copy_op((int32_t)p->copies.size() - 1);
+      }
+    }
+    // compute
+    const Node &first = p->nodes[members[0]];
+    if (first.cls == TNC_CLASS_TINY) {
+      Op op{OP_TINY_GROUP, (int32_t)tiny.size(), (int32_t)members.size(), 0};
+      for (int32_t s : members) {
+        Node &nd = p->nodes[s];
+        nd.runs_index = (int32_t)runs.size();
+        for (auto &r : nd.row_runs) runs.push_back({r.size, r.stride});
+        for (auto &r : nd.col_runs) runs.push_back({r.size, r.stride});
+        TinyDesc d{};
+        auto operand = [&](int w, int32_t *buf, int64_t *off) {
+          int32_t t = w == 0 ? nd.lhs : nd.rhs;
+          int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
+          uint64_t ao = w == 0 ? nd.a_off : nd.b_off;
+          if (copy || t >= L) { *buf = kBufArena; *off = (int64_t)(ao / 8); }
+          else { *buf = kBufLeaf0 + t; *off = 0; }
+        };
+        operand(nd.swap ? 1 : 0, &d.x_buf, &d.x_off);
+        operand(nd.swap ? 0 : 1, &d.y_buf, &d.y_off);
+        if (nd.c_off == kNone) { d.c_buf = kBufOut; d.c_off = 0; }
+        else { d.c_buf = kBufArena; d.c_off = (int64_t)(nd.c_off / 8); }
+        d.is_root = nd.is_root && !p->root_permute;
+        d.R = (int32_t)(nd.swap ? nd.n : nd.m);
+        d.S = (int32_t)(nd.swap ? nd.m : nd.n);
+        d.K = (int32_t)nd.k;
+        d.nrr = (int32_t)nd.row_runs.size();
+        d.ncr = (int32_t)nd.col_runs.size();
+        d.runs_index = nd.runs_index;
+        tiny.push_back(d);
+      }
+      p->program.push_back(op);
+    } else {
+      Node &nd = p->nodes[members[0]];
+      nd.runs_index = (int32_t)runs.size();
+      for (auto &r : nd.row_runs) runs.push_back({r.size, r.stride});
+      for (auto &r : nd.col_runs) runs.push_back({r.size, r.stride});
+      p->program.push_back({first.cls == TNC_CLASS_SKINNY ? OP_SKINNY : OP_GEMM, members[0], 1, 0});
+    }
+  }
+  if (p->root_permute) {
+    p->copies.push_back(make_copy(T - 1, kBufArena, p->tensor_off[T - 1], kBufOut, 0, p->out_modes, 1));
+    push_copy_op((int32_t)p->copies.size() - 1);
+  }
+
+  // ---- descriptor blob: [runs][copy descs][tiny descs][int64 table]
+  std::vector<CopyDesc> cdesc;
+  std::vector<int64_t> ints;
+  for (auto &c : p->copies) {
+    CopyDesc d{};
+    d.src_buf = c.src_buf;
+    d.dst_buf = c.dst_buf;
+    d.rank = (int32_t)c.dims.size();
+    d.is_root = c.is_root;
+    d.src_off = (int64_t)(c.src_off_bytes / 8);
+    d.dst_off = (int64_t)(c.dst_off_bytes / 8);
+    d.count = c.count;
+    d.ints_index = (int32_t)ints.size();
+    ints.insert(ints.end(), c.dims.begin(), c.dims.end());
+    ints.insert(ints.end(), c.src_strides.begin(), c.src_strides.end());
+    ints.insert(ints.end(), c.slice_strides.begin(), c.slice_strides.end());
+    cdesc.push_back(d);
+  }
+  auto append = [&](const void *src, size_t n) {
+    size_t at = round_up(p->blob.size(), 16);
+    p->blob.resize(at + n);
+    if (n) std::memcpy(p->blob.data() + at, src, n);
+    return (uint64_t)at;
+  };
+  p->blob.clear();
+  p->blob_runs = append(runs.data(), runs.size() * sizeof(RunDev));
+  p->blob_copies = append(cdesc.data(), cdesc.size() * sizeof(CopyDesc));
+  p->blob_tiny = append(tiny.data(), tiny.size() * sizeof(TinyDesc));
+  p->blob_ints = append(ints.data(), ints.size() * sizeof(int64_t));
+  if (p->blob.empty()) p->blob.resize(16);
+
+  p->ptab_bytes = round_up(8ull * (uint64_t)(2 + L), 256);
+  p->blob_bytes = round_up(p->blob.size(), 256);
+  p->header_bytes = p->ptab_bytes + p->blob_bytes;
+
+  // ---- stats
+  tnc_plan_stats &stt = p->stats;
+  std::memset(&stt, 0, sizeof(stt));
+  stt.num_leaves = L;
+  stt.num_steps = S;
+  stt.num_groups = (int32_t)p->groups.size();
+  stt.min_inner_run = S > 0 ? INT32_MAX : 0;
+  for (auto &nd : p->nodes) {
+    if (nd.cls == TNC_CLASS_TINY) stt.nodes_tiny++;
+    else if (nd.cls == TNC_CLASS_SKINNY) stt.nodes_skinny++;
+    else stt.nodes_gemm++;
+    if (nd.splits > 1) stt.nodes_split++;
+    stt.nodes_interleaved += nd.interleaved;
+    stt.min_inner_run = std::min<int32_t>(stt.min_inner_run, (int32_t)std::min<int64_t>(nd.inner_run, INT32_MAX));
+    if (nd.lhs >= L) stt.relayouts += nd.copy_a;
+    if (nd.rhs >= L) stt.relayouts += nd.copy_b;
+  }
+  for (int32_t l = 0; l < L; ++l) stt.staged_leaves += p->staged_leaf[l];
+  stt.root_permute = p->root_permute;
+  stt.num_slices = 1;
+  for (int64_t e : p->slice_extents) stt.num_slices *= e;
+  stt.flops = flops;
+  stt.flops_unsliced = flops_u;
+  stt.bytes = bytes;
+  stt.max_intermediate = max_elems;
+  stt.header_bytes = p->header_bytes;
+  stt.arena_bytes = p->arena_bytes;
+  stt.workspace_bytes = p->header_bytes + p->arena_bytes;
+  if (o.capacity_bytes > 0 && stt.workspace_bytes > o.capacity_bytes) return TNC_ERR_OUT_OF_MEMORY;
+  return TNC_OK;
+}
+
+}  // namespace tnc

@@ -1,0 +1,106 @@
+// Host-side plan of a tree contraction: mode orders, per-step GEMM
+// descriptors, launch groups, arena offsets and the device descriptor blob.
+//
+// Mode orders follow the reverse-tree "lifetime ordering" of the page
+// "Parallelizing Large-Scale Tensor Network Contraction on Multiple GPUs",
+// section 1.4.  The rest (kernel classes, orientation, output runs, split-K,
+// grouping, first-fit arena) is this library's execution design.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tnc.h"
+#include "device_desc.hpp"
+
+namespace tnc {
+
+constexpr uint64_t kNone = UINT64_MAX;
+constexpr int kMaxRank = 64;
+constexpr int64_t kSkinnyMaxSide = 16;   // skinny when min(m, n) <= this
+constexpr int64_t kGemmNominalTile = 128;
+
+struct Run {
+  int64_t size;
+  int64_t stride;  // stride in C (entries) of the run's innermost mode
+};
+
+// A copy of one tensor into a new layout (leaf staging, NAIVE re-layout,
+// NAIVE root permute, single-leaf networks).
+struct CopyOp {
+  int32_t src_buf;             // buffer id: kBufArena, kBufOut, kBufLeaf0 + leaf
+  uint64_t src_off_bytes;      // offset inside the source buffer
+  int32_t dst_buf;
+  uint64_t dst_off_bytes;
+  int64_t count;               // entries copied
+  int32_t is_root;             // destination is `out` (beta applies across slices)
+  std::vector<int64_t> dims;   // destination dims, outermost first (merged, extent > 1)
+  std::vector<int64_t> src_strides;
+  std::vector<int64_t> slice_strides;  // per sliced mode: source stride (0 if absent)
+};
+
+struct Node {
+  int32_t lhs = -1, rhs = -1, out = -1;
+  int64_t m = 1, n = 1, k = 1;        // with sliced modes fixed
+  int64_t mu = 1, nu = 1, ku = 1;     // unsliced
+  int32_t cls = TNC_CLASS_TINY;
+  int32_t swap = 0;
+  int32_t group = -1;
+  int32_t splits = 1;
+  std::vector<Run> row_runs, col_runs;
+  int64_t inner_run = 1;
+  int32_t interleaved = 0;
+  int32_t copy_a = 0, copy_b = 0;
+  uint64_t a_off = kNone, b_off = kNone, c_off = kNone;
+  uint64_t scratch_off = kNone, scratch_bytes = 0;
+  int32_t is_root = 0;
+  // device run table location (entries into the blob's run array)
+  int32_t runs_index = 0;
+};
+
+enum OpKind : int32_t { OP_COPY = 0, OP_TINY_GROUP = 1, OP_SKINNY = 2, OP_GEMM = 3 };
+
+struct Op {
+  OpKind kind;
+  int32_t first;   // OP_COPY: first index into copy descriptors; TINY: first tiny desc; else node
+  int32_t count;   // OP_COPY / OP_TINY_GROUP: descriptors in the launch
+  int64_t max_count;  // OP_COPY: largest copy in the launch (grid sizing)
+};
+
+struct PlanImpl {
+  // ---- inputs (copied)
+  int32_t num_modes = 0;
+  std::vector<int64_t> extents;      // as given
+  std::vector<int64_t> ext;          // sliced modes set to 1
+  std::vector<std::vector<int32_t>> leaves;
+  std::vector<int32_t> out_modes;
+  std::vector<int32_t> lhs, rhs;
+  std::vector<int32_t> sliced;
+  tnc_plan_options opts{};
+
+  // ---- derived
+  int32_t L = 0, S = 0;
+  std::vector<std::vector<int32_t>> order;     // planned order per SSA tensor
+  std::vector<std::vector<int32_t>> gemm_a, gemm_b;
+  std::vector<Node> nodes;
+  std::vector<std::vector<int32_t>> groups;
+  std::vector<uint64_t> tensor_off;
+  std::vector<int32_t> staged_leaf;
+  int32_t root_permute = 0;
+  uint64_t arena_bytes = 0;
+  uint64_t ptab_bytes = 0, blob_bytes = 0, header_bytes = 0;
+  tnc_plan_stats stats{};
+
+  // ---- execution program
+  std::vector<CopyOp> copies;
+  std::vector<Op> program;
+  std::vector<uint8_t> blob;                   // host image of the device descriptor blob
+  uint64_t blob_runs = 0, blob_copies = 0, blob_tiny = 0, blob_ints = 0;  // byte offsets in blob
+  std::vector<int64_t> slice_extents;          // extents of sliced modes
+};
+
+tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
+                      PlanImpl *p);
+
+}  // namespace tnc

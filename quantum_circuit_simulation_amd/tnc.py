@@ -1,0 +1,240 @@
+"""ctypes binding of libtnc.so (include/tnc.h).
+
+Argument marshalling only: every step of the contraction runs in the HIP
+library.  PyTorch supplies device memory and the stream; nothing here falls
+back to a CPU path.  If the library has not been built this module raises on
+import (build it with ``python quantum_circuit_simulation_amd/build.py``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtnc.so")
+
+TNC_OK = 0
+STATUS = {0: "TNC_OK", 1: "TNC_ERR_INVALID_ARG", 2: "TNC_ERR_INVALID_NETWORK", 3: "TNC_ERR_INVALID_TREE",
+          4: "TNC_ERR_UNSUPPORTED", 5: "TNC_ERR_OUT_OF_MEMORY", 6: "TNC_ERR_WORKSPACE_TOO_SMALL",
+          7: "TNC_ERR_HIP"}
+TNC_C64, TNC_C128 = 0, 1
+ORDER_LIFETIME, ORDER_NAIVE = 0, 1
+CLASS_TINY, CLASS_SKINNY, CLASS_GEMM = 0, 1, 2
+NONE = (1 << 64) - 1
+
+P = ctypes.POINTER
+
+
+class TncError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+
+
+class Network(ctypes.Structure):
+    _fields_ = [("num_modes", ctypes.c_int32), ("extents", P(ctypes.c_int64)),
+                ("num_leaves", ctypes.c_int32), ("leaf_rank", P(ctypes.c_int32)),
+                ("leaf_modes", P(ctypes.c_int32)), ("out_rank", ctypes.c_int32),
+                ("out_modes", P(ctypes.c_int32)), ("dtype", ctypes.c_int)]
+
+
+class Tree(ctypes.Structure):
+    _fields_ = [("num_steps", ctypes.c_int32), ("lhs", P(ctypes.c_int32)), ("rhs", P(ctypes.c_int32))]
+
+
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int), ("num_sliced", ctypes.c_int32), ("sliced_modes", P(ctypes.c_int32)),
+                ("align", ctypes.c_uint64), ("capacity_bytes", ctypes.c_uint64), ("tiny_mnk", ctypes.c_uint64),
+                ("max_group", ctypes.c_int32)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [("num_leaves", ctypes.c_int32), ("num_steps", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("nodes_tiny", ctypes.c_int32), ("nodes_skinny", ctypes.c_int32), ("nodes_gemm", ctypes.c_int32),
+                ("nodes_split", ctypes.c_int32), ("nodes_interleaved", ctypes.c_int32),
+                ("min_inner_run", ctypes.c_int32), ("staged_leaves", ctypes.c_int32),
+                ("relayouts", ctypes.c_int32), ("root_permute", ctypes.c_int32), ("num_slices", ctypes.c_int64),
+                ("flops", ctypes.c_double), ("flops_unsliced", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("max_intermediate", ctypes.c_uint64), ("header_bytes", ctypes.c_uint64),
+                ("arena_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class NodeInfo(ctypes.Structure):
+    _fields_ = [("lhs", ctypes.c_int32), ("rhs", ctypes.c_int32), ("out", ctypes.c_int32),
+                ("kernel_class", ctypes.c_int32), ("swap", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("row_runs", ctypes.c_int32), ("col_runs", ctypes.c_int32),
+                ("inner_run", ctypes.c_int32), ("interleaved", ctypes.c_int32), ("copy_a", ctypes.c_int32),
+                ("copy_b", ctypes.c_int32), ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("a_off", ctypes.c_uint64), ("b_off", ctypes.c_uint64), ("c_off", ctypes.c_uint64),
+                ("scratch_off", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
+           "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
+           "tnc_execute", "tnc_status_string"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python quantum_circuit_simulation_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    lib.tnc_plan_options_default.argtypes = [P(PlanOptions)]
+    lib.tnc_plan_options_default.restype = None
+    lib.tnc_plan.argtypes = [P(Network), P(Tree), P(PlanOptions), P(ctypes.c_void_p)]
+    lib.tnc_plan.restype = ctypes.c_int
+    lib.tnc_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.tnc_plan_destroy.restype = None
+    lib.tnc_plan_workspace_bytes.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64)]
+    lib.tnc_plan_workspace_bytes.restype = ctypes.c_int
+    lib.tnc_plan_stats_get.argtypes = [ctypes.c_void_p, P(PlanStats)]
+    lib.tnc_plan_stats_get.restype = ctypes.c_int
+    lib.tnc_plan_tensor_order.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32)]
+    lib.tnc_plan_tensor_order.restype = ctypes.c_int
+    lib.tnc_plan_tensor_offset.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_uint64)]
+    lib.tnc_plan_tensor_offset.restype = ctypes.c_int
+    lib.tnc_plan_node.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(NodeInfo)]
+    lib.tnc_plan_node.restype = ctypes.c_int
+    lib.tnc_execute.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_uint64, ctypes.c_void_p]
+    lib.tnc_execute.restype = ctypes.c_int
+    lib.tnc_status_string.argtypes = [ctypes.c_int]
+    lib.tnc_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str):
+    if code != TNC_OK:
+        raise TncError(code, where)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a if a.size else np.zeros(1, dtype=np.int32)
+
+
+def _i64(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    return a if a.size else np.zeros(1, dtype=np.int64)
+
+
+class Plan:
+    """A tnc plan built from a network description and a tree (host only)."""
+
+    def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
+                 order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
+                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256):
+        lib = load_library()
+        self._lib = lib
+        self.num_leaves = len(leaves)
+        self.num_steps = len(lhs)
+        ext = _i64(extents)
+        rank = _i32([len(l) for l in leaves])
+        modes = _i32([x for l in leaves for x in l])
+        outm = _i32(out_modes)
+        lhs_a, rhs_a = _i32(lhs), _i32(rhs)
+        sl = _i32(sliced)
+        self._keep = (ext, rank, modes, outm, lhs_a, rhs_a, sl)
+        net = Network(len(extents), ext.ctypes.data_as(P(ctypes.c_int64)), len(leaves),
+                      rank.ctypes.data_as(P(ctypes.c_int32)), modes.ctypes.data_as(P(ctypes.c_int32)),
+                      len(out_modes), outm.ctypes.data_as(P(ctypes.c_int32)), TNC_C64)
+        tree = Tree(len(lhs), lhs_a.ctypes.data_as(P(ctypes.c_int32)), rhs_a.ctypes.data_as(P(ctypes.c_int32)))
+        opts = PlanOptions()
+        lib.tnc_plan_options_default(ctypes.byref(opts))
+        opts.order = order
+        opts.num_sliced = len(sliced)
+        opts.sliced_modes = sl.ctypes.data_as(P(ctypes.c_int32))
+        opts.align = align
+        opts.capacity_bytes = capacity_bytes
+        opts.tiny_mnk = tiny_mnk
+        opts.max_group = max_group
+        h = ctypes.c_void_p()
+        _check(lib.tnc_plan(ctypes.byref(net), ctypes.byref(tree), ctypes.byref(opts), ctypes.byref(h)), "tnc_plan")
+        self._h = h
+        self.out_shape = tuple(int(extents[x]) for x in out_modes)
+
+    @classmethod
+    def from_network(cls, net, tree, **kw) -> "Plan":
+        return cls(net.extents, net.leaves, net.out_modes, tree.lhs, tree.rhs, **kw)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.tnc_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def workspace_bytes(self) -> int:
+        v = ctypes.c_uint64()
+        _check(self._lib.tnc_plan_workspace_bytes(self._h, ctypes.byref(v)), "tnc_plan_workspace_bytes")
+        return int(v.value)
+
+    def stats(self) -> dict:
+        s = PlanStats()
+        _check(self._lib.tnc_plan_stats_get(self._h, ctypes.byref(s)), "tnc_plan_stats_get")
+        return s.as_dict()
+
+    def tensor_order(self, tid: int) -> List[int]:
+        buf = (ctypes.c_int32 * 64)()
+        r = ctypes.c_int32()
+        _check(self._lib.tnc_plan_tensor_order(self._h, tid, buf, ctypes.byref(r)), "tnc_plan_tensor_order")
+        return [int(buf[i]) for i in range(r.value)]
+
+    def tensor_offset(self, tid: int) -> int:
+        v = ctypes.c_uint64()
+        _check(self._lib.tnc_plan_tensor_offset(self._h, tid, ctypes.byref(v)), "tnc_plan_tensor_offset")
+        return int(v.value)
+
+    def node(self, step: int) -> dict:
+        n = NodeInfo()
+        _check(self._lib.tnc_plan_node(self._h, step, ctypes.byref(n)), "tnc_plan_node")
+        return n.as_dict()
+
+    def execute_ptrs(self, leaf_ptrs: Sequence[int], out_ptr: int, ws_ptr: int, ws_bytes: int, stream: int = 0):
+        """Raw-pointer form: device addresses as Python ints."""
+        arr = (ctypes.c_void_p * max(1, len(leaf_ptrs)))(*[int(p) for p in leaf_ptrs])
+        _check(self._lib.tnc_execute(self._h, arr, ctypes.c_void_p(int(out_ptr)), ctypes.c_void_p(int(ws_ptr)),
+                                     ctypes.c_uint64(int(ws_bytes)), ctypes.c_void_p(int(stream))), "tnc_execute")
+
+    def execute(self, leaves, out, workspace, stream=None):
+        """leaves: torch complex64 tensors on the GPU (declared layouts), out:
+        complex64 tensor of the output size, workspace: uint8 tensor of at
+        least ``workspace_bytes``.  Enqueued on ``stream`` (default: torch's
+        current stream); returns without synchronising."""
+        import torch
+        if len(leaves) != self.num_leaves:
+            raise ValueError("wrong number of leaves")
+        for t in list(leaves) + [out]:
+            if t.dtype != torch.complex64 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("leaves and out must be contiguous complex64 GPU tensors")
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        self.execute_ptrs([t.data_ptr() for t in leaves], out.data_ptr(), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), s)
+
+
+def alloc_workspace(plan: Plan, device="cuda"):
+    import torch
+    n = max(256, plan.workspace_bytes)
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,172 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, on the same
+seeded inputs.  Tolerance (single precision arithmetic against complex128):
+|g - r| <= 1e-4 * max(|r|, rms(r)) per output entry."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import rel_err_ok
+from workloads import circuits, lattice, randnet, sweep, trees
+from workloads.network import Network, Tree
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util  # noqa: F401
+    yield
+
+
+def _gpu_run(net, tree, **kw):
+    from tests.gpu_util import run
+    print(f"[gpu] {net.name or 'network'} leaves={net.num_leaves} kw={kw}", flush=True)
+    return run(net, tree, **kw)
+
+
+def _assert_close(got, ref, tol=TOL):
+    ok, err = rel_err_ok(got, ref, tol)
+    assert ok, f"max scaled error {err:.3e} > {tol}"
+
+
+def _pair(R, S, K, seed, ext=2, permuted=False):
+    """A pairwise network with m = ext^R modes ... built from explicit mode counts."""
+    rng = np.random.default_rng(seed)
+    M = list(range(R))
+    N = list(range(R, R + S))
+    Kx = list(range(R + S, R + S + K))
+    A, B, out = M + Kx, N + Kx, M + N
+    if permuted:
+        A = [A[i] for i in rng.permutation(len(A))]
+        B = [B[i] for i in rng.permutation(len(B))]
+        out = [out[i] for i in rng.permutation(len(out))]
+    extents = np.full(R + S + K, ext, dtype=np.int64)
+    data = [sweep.complex_gaussian(rng, tuple(int(extents[x]) for x in A)),
+            sweep.complex_gaussian(rng, tuple(int(extents[x]) for x in B))]
+    return Network(extents, [A, B], out, data, name=f"pair{R},{S},{K}x{ext}"), Tree([0], [1])
+
+
+# (log2 m, log2 n, log2 k): tiny, skinny (incl. split-K), every GEMM tile
+# variant, ragged edges via extent-3 modes, outer products
+PAIR_CASES = [
+    (2, 3, 2, 2), (5, 5, 5, 2),              # tiny
+    (12, 2, 2, 2), (14, 4, 3, 2), (10, 0, 12, 2), (0, 0, 16, 2), (3, 1, 13, 2),   # skinny
+    (9, 9, 6, 2), (10, 6, 6, 2), (10, 5, 7, 2), (9, 7, 13, 2), (6, 6, 14, 2),     # gemm
+    (6, 5, 3, 3), (5, 4, 4, 3), (4, 4, 0, 3), (7, 6, 1, 2),                       # ragged / k = 1
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES)
+@pytest.mark.parametrize("permuted", [False, True])
+def test_pairwise_shapes(case, permuted):
+    R, S, K, ext = case
+    net, tree = _pair(R, S, K, seed=hash(case) % 1000 + permuted, ext=ext, permuted=permuted)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree)
+    _assert_close(got, ref)
+
+
+@pytest.mark.parametrize("case", [(9, 9, 6, 2), (10, 2, 3, 2), (5, 5, 3, 2)])
+def test_naive_order_matches(case):
+    R, S, K, ext = case
+    net, tree = _pair(R, S, K, seed=7, ext=ext, permuted=True)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, order=1)
+    _assert_close(got, ref)
+
+
+def test_brickwork_12q_amplitude():
+    c = circuits.brickwork(12, 8, 101)
+    net = c.to_network(name="brickwork12x8")
+    tree = trees.greedy_tree(net)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree)
+    _assert_close(got, ref)
+
+
+def test_brickwork_12q_all_open_unit_norm():
+    c = circuits.brickwork(12, 8, 101)
+    net = c.to_network(open_qubits=range(12), name="brickwork12x8_open")
+    tree = trees.greedy_tree(net)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree)
+    _assert_close(got, ref)
+    assert abs(np.sum(np.abs(got) ** 2) - 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_networks(seed):
+    rng = np.random.default_rng(3000 + seed)
+    net = randnet.random_network(rng, n_leaves=int(rng.integers(2, 10)), n_closed=int(rng.integers(1, 16)),
+                                 n_open=int(rng.integers(0, 4)), extent_choices=(1, 2, 3, 4, 5))
+    tree = randnet.random_tree(rng, net.num_leaves)
+    if trees.tree_cost(net, tree)["max_elems"] > 1 << 20:
+        pytest.skip("too wide")
+    ref = oracle.contract_network(net, tree)
+    for order in (0, 1):
+        got, plan = _gpu_run(net, tree, order=order, tiny_mnk=int(rng.choice([0, 256, 1 << 15])),
+                             max_group=int(rng.integers(1, 8)))
+        _assert_close(got, ref)
+
+
+def test_sliced_equals_unsliced():
+    c = circuits.brickwork(16, 10, 3)
+    net = c.to_network(open_qubits=[0, 1], name="brickwork16x10")
+    tree = trees.greedy_tree(net)
+    ref = oracle.contract_network(net, tree)
+    unsliced, _ = _gpu_run(net, tree)
+    sl = trees.choose_slices(net, tree, 3)
+    sliced, plan = _gpu_run(net, tree, sliced=sl)
+    assert plan.stats()["num_slices"] == 8
+    _assert_close(unsliced, ref)
+    _assert_close(sliced, ref)
+
+
+def test_single_leaf_network():
+    rng = np.random.default_rng(2)
+    d = sweep.complex_gaussian(rng, (3, 4, 5))
+    net = Network(np.array([3, 4, 5], dtype=np.int64), [[0, 1, 2]], [2, 0, 1], [d], name="single")
+    got, _ = _gpu_run(net, Tree([], []))
+    assert np.array_equal(got, np.transpose(d, [2, 0, 1]).astype(np.complex128))
+
+
+def test_peps_all_ones_closed_form():
+    net = lattice.peps(8, 8, 0, fill=lambda i, j, shape, rng: np.ones(shape, dtype=np.float32))
+    got, plan = _gpu_run(net, lattice.row_major_tree(8))
+    # all-ones sites scaled by 1/(0.5 D^(deg/2)): Z = 2^64 exactly (D = 8: exact scales)
+    assert abs(got - 2.0 ** 64) <= TOL * 2.0 ** 64
+
+
+def test_peps_8x8_matches_oracle_golden():
+    g = json.load(open(os.path.join(GOLDEN, "oracle_values.json")))["peps8x8_D8_seed404"]
+    net = lattice.peps(8, 8, 404)
+    assert net.digest() == g["input_sha256"]
+    got, plan = _gpu_run(net, lattice.row_major_tree(8))
+    ref = complex(g["re"], g["im"])
+    _assert_close(got, ref)
+
+
+def test_brickwork_30q_batch_and_amplitude():
+    g = json.load(open(os.path.join(GOLDEN, "oracle_values.json")))["brickwork30x14_seed303"]
+    c = circuits.brickwork(30, 14, 303)
+    net = c.to_network(open_qubits=range(6), name="brickwork30x14_batch")
+    assert net.digest() == g["batch_sha256"]
+    tree = trees.greedy_tree(net)
+    got, plan = _gpu_run(net, tree)
+    ref = np.array(g["batch_re"]) + 1j * np.array(g["batch_im"])
+    _assert_close(got.reshape(-1), ref)
+    # single amplitude: the same tree plus six steps absorbing <0| on q0..q5
+    from workloads.network import close_open_wires
+    net1, tree1 = close_open_wires(net, tree)
+    amp, _ = _gpu_run(net1, tree1)
+    _assert_close(amp, ref[0])

@@ -84,3 +84,35 @@ def caterpillar(num_leaves: int, order=None) -> Tree:
         lhs.append(num_leaves + s - 1)
         rhs.append(leaf)
     return Tree(lhs, rhs)
+
+
+def close_open_wires(net: Network, tree: Tree, bits=None):
+    """Close every open mode of ``net`` with a basis-vector leaf ([1, 0, ...]
+    for bit 0) and extend ``tree`` by one step per closed mode, absorbing them
+    into the old root in output order.  Returns (network, tree) with the
+    new leaves placed after the old ones (SSA ids of intermediates shift)."""
+    import numpy as _np
+    L, S = net.num_leaves, tree.num_steps
+    nopen = len(net.out_modes)
+    bits = [0] * nopen if bits is None else list(bits)
+    leaves = [list(l) for l in net.leaves]
+    data = list(net.data) if net.data is not None else None
+    for x, b in zip(net.out_modes, bits):
+        leaves.append([x])
+        if data is not None:
+            v = _np.zeros(int(net.extents[x]), dtype=_np.complex64)
+            v[b] = 1
+            data.append(v)
+
+    def remap(t):
+        return t if t < L else t + nopen
+
+    lhs = [remap(a) for a in tree.lhs]
+    rhs = [remap(b) for b in tree.rhs]
+    root = remap(L + S - 1) if S > 0 else 0
+    for j in range(nopen):
+        lhs.append(root)
+        rhs.append(L + j)
+        root = (L + nopen) + S + j
+    out = Network(net.extents.copy(), leaves, [], data, name=net.name + "_closed", meta=dict(net.meta))
+    return out, Tree(lhs, rhs)
