@@ -43,6 +43,25 @@ def fill_gaussian(t, seed):
         flat[s:e] = torch.randn(e - s, dtype=torch.complex64, device=t.device, generator=g)
 
 
+def gemm_kernel_name(R, S, K, splits):
+    """The k_cgemm instance the library launches for an oriented GEMM step
+    (same rule as its launcher): one tile per workgroup for K chunks above
+    256, persistent workgroups otherwise; tile shape by the short side."""
+    kchunk = K if splits <= 1 else -(-(-(-K // splits)) // 8) * 8
+    base = "k_cgemm_tile" if kchunk > 256 else "k_cgemm"
+    if S > 64 and R <= 32:
+        t = "32,256"
+    elif S > 64 and R <= 64:
+        t = "64,256"
+    elif S > 64:
+        t = "128,128"
+    elif S > 32:
+        t = "256,64"
+    else:
+        t = "256,32"
+    return f"{base}<{t}>"
+
+
 class SweepWorkload:
     name = "pairwise sweep m,n,k in {2^6,2^10,2^14,2^18}, k<=2^14, 45 feasible cases, aligned"
 
@@ -80,9 +99,55 @@ class SweepWorkload:
             if events is not None:
                 events[idx][1].record()
 
+    def ablation(self, steps, max_operand=1 << 30):
+        """Permuted declarations: lifetime order (stage the operands, write C
+        through runs) against naive order (permute A and B, GEMM, permute C),
+        next to the aligned case, for every case whose operands fit."""
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import sweep
+        rows = []
+        tot = {"aligned_ms": 0.0, "lifetime_ms": 0.0, "naive_ms": 0.0, "flop": 0.0}
+        for c, plan_al, m, n, k in self.plans:
+            if max(m * k, n * k, m * n) > max_operand:
+                continue
+            net, tree = sweep.network(c["logm"], c["logn"], c["logk"], permuted=True, seed=c["seed"])
+            res = {}
+            for name, plan in (("aligned", plan_al), ("lifetime", qa.Plan.from_network(net, tree, order=0)),
+                               ("naive", qa.Plan.from_network(net, tree, order=1))):
+                ws = torch.empty(max(256, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+                args = ([self.A[: m * k], self.B[: n * k]], self.C[: m * n], ws)
+                plan.execute(*args)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(steps)]
+                for e0, e1 in ev:
+                    e0.record()
+                    plan.execute(*args)
+                    e1.record()
+                torch.cuda.synchronize()
+                res[name] = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+                del ws
+                st = plan.stats()
+                res[name + "_staged_leaves"] = st["staged_leaves"]
+                res[name + "_relayouts"] = st["relayouts"] + st["root_permute"]
+            rows.append({"logm": c["logm"], "logn": c["logn"], "logk": c["logk"], **res})
+            tot["aligned_ms"] += res["aligned"]
+            tot["lifetime_ms"] += res["lifetime"]
+            tot["naive_ms"] += res["naive"]
+            tot["flop"] += 8.0 * m * n * k
+            log(f"ablation m=2^{c['logm']} n=2^{c['logn']} k=2^{c['logk']}: aligned {res['aligned']:.3f} ms, "
+                f"lifetime {res['lifetime']:.3f} ms, naive {res['naive']:.3f} ms")
+        tot["cases"] = len(rows)
+        tot["naive_over_lifetime"] = tot["naive_ms"] / tot["lifetime_ms"] if tot["lifetime_ms"] else None
+        tot["lifetime_tflops"] = tot["flop"] / (tot["lifetime_ms"] / 1e3) / 1e12 if tot["lifetime_ms"] else None
+        tot["naive_tflops"] = tot["flop"] / (tot["naive_ms"] / 1e3) / 1e12 if tot["naive_ms"] else None
+        return tot, rows
+
     def kernel_of(self, idx):
         c, plan, m, n, k = self.plans[idx]
-        return "k_cgemm<128,128>" if n > 64 else ("k_cgemm<256,64>" if n > 32 else "k_cgemm<256,32>")
+        nd = plan.node(0)
+        R, S = (n, m) if nd["swap"] else (m, n)
+        return gemm_kernel_name(R, S, k, nd["splits"])
 
     def launch_flops(self, idx):
         _, _, m, n, k = self.plans[idx]
@@ -153,6 +218,30 @@ class TreeWorkload:
         if events is not None:
             events[0][1].record()
 
+    def ablation(self, steps):
+        """The whole tree under naive order (operands and root re-laid before
+        and after each GEMM) against lifetime order."""
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        res = {}
+        for name, order in (("lifetime", 0), ("naive", 1)):
+            plan = qa.Plan.from_network(self.net, self.tree, order=order)
+            ws = qa.alloc_workspace(plan)
+            plan.execute(self.leaves, self.out, ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                plan.execute(self.leaves, self.out, ws)
+                e1.record()
+            torch.cuda.synchronize()
+            st = plan.stats()
+            res[name + "_ms"] = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+            res[name + "_relayouts"] = st["relayouts"] + st["root_permute"]
+            res[name + "_workspace_bytes"] = st["workspace_bytes"]
+            del ws
+        res["naive_over_lifetime"] = res["naive_ms"] / res["lifetime_ms"]
+        return res, []
+
     def kernel_of(self, idx):
         return "whole tree"
 
@@ -169,6 +258,23 @@ class TreeWorkload:
                 "sample": f"full contraction ({self.flops:.3g} flop in {el:.1f} s)"}
 
 
+def calibrate_copy(entries=1 << 27):
+    """One k_copy of `entries` complex64 (a single-leaf network in its own
+    order): 8*entries bytes read and 8*entries bytes written.  Under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the scale of the byte
+    counters."""
+    import torch
+    import quantum_circuit_simulation_amd as qa
+    plan = qa.Plan([entries], [[0]], [0], [], [])
+    src = torch.zeros(entries, dtype=torch.complex64, device="cuda")
+    dst = torch.empty_like(src)
+    ws = qa.alloc_workspace(plan)
+    torch.cuda.synchronize()
+    plan.execute([src], dst, ws)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {entries} entries, {16 * entries} bytes moved")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +284,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cases", default="", help="comma-separated sweep case indices (default: all feasible)")
     ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB identity copy (k_copy) to scale HBM byte counters")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time naive mode order (permute, GEMM, permute) against lifetime order")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this executor contracts on a single MI355X "
@@ -186,6 +296,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
 
+    if args.calibrate_copy:
+        calibrate_copy()
     t0 = time.time()
     if args.workload == "sweep":
         cases = None
@@ -238,6 +350,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": None,
                 "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
+    rep = {}
     if args.report:
         rep = {"per_kernel": {k: {"flop": v[0], "ms": v[1], "launches": v[2]} for k, v in per.items()},
                "cases": []}
@@ -248,6 +361,13 @@ def main():
                                      "tflops": 8.0 * m * n * k / (ms / 1e3) / 1e12})
         os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
         json.dump(rep, open(args.report, "w"), indent=1)
+
+    ablation = None
+    if args.ablation:
+        ablation, abl_rows = wl.ablation(max(1, args.steps))
+        if args.report:
+            rep["ablation_cases"] = abl_rows
+            json.dump(rep, open(args.report, "w"), indent=1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,6 +380,7 @@ def main():
             "pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2),
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
+            **({"ablation": ablation} if ablation is not None else {}),
             "host_wall_s": round(wall, 3)}
     print(json.dumps(line), flush=True)
 

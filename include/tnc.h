@@ -48,7 +48,8 @@ typedef enum {
   TNC_ERR_INVALID_TREE = 3,       /* steps != leaves - 1, operand id out of range or reused */
   TNC_ERR_UNSUPPORTED = 4,        /* mode in more than two tensors (hyperedge / batch mode),
                                      a mode repeated inside one leaf, rank > 64,
-                                     complex128 data, a size that overflows 64 bits */
+                                     complex128 data, a size that overflows 64 bits,
+                                     a GEMM-class step with m, n or k >= 2^31 */
   TNC_ERR_OUT_OF_MEMORY = 5,      /* planned workspace exceeds options.capacity_bytes */
   TNC_ERR_WORKSPACE_TOO_SMALL = 6,/* tnc_execute got less workspace than planned */
   TNC_ERR_HIP = 7                 /* a HIP runtime call or kernel launch failed */
@@ -184,6 +185,11 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
 
 /* Static text for a status code. */
 const char *tnc_status_string(tnc_status status);
+
+/* Detail of the most recent failure on the calling thread (e.g. which launch
+ * failed and the HIP error string), or "" if none.  Valid until the thread's
+ * next tnc_* call. */
+const char *tnc_last_error(void);
 
 #ifdef __cplusplus
 }

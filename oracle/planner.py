@@ -280,16 +280,18 @@ def _runs(c_order, ext, row_set):
 
 
 def _split_rule(cls, R, S, k):
+    """K split count: enough workgroups to fill the chip, K chunks of at
+    least 256 (GEMM) / 1024 (skinny) entries."""
     if cls == CLASS_GEMM:
         tiles = _ceil_div(R, GEMM_NOMINAL_TILE) * _ceil_div(S, GEMM_NOMINAL_TILE)
-        if tiles >= 128 or k < 4096:
+        if tiles >= 256 or k < 512:
             return 1
-        return max(1, min(_pow2_floor(256 // tiles), _pow2_floor(k // 2048)))
+        return max(1, min(_pow2_floor(512 // tiles), _pow2_floor(k // 256)))
     if cls == CLASS_SKINNY:
         blocks = _ceil_div(R, 256)
-        if blocks >= 512 or k < 4096:
+        if blocks >= 512 or k < 2048:
             return 1
-        return max(1, min(_pow2_floor(1024 // blocks), _pow2_floor(k // 2048)))
+        return max(1, min(_pow2_floor(1024 // blocks), _pow2_floor(k // 1024)))
     return 1
 
 
@@ -373,6 +375,8 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
         row_set = N if swap else M
         row_runs, col_runs, inner, nruns = _runs(c_order, ext, row_set)
         R, Sx = (n, m) if swap else (m, n)
+        if cls == CLASS_GEMM and max(R, Sx, k) >= 1 << 31:
+            raise PlanError("UNSUPPORTED", "GEMM step with a side or K of 2^31 or more")
         splits = _split_rule(cls, R, Sx, k)
         node = Node(step=s, lhs=a, rhs=b, out=L + s, m=m, n=n, k=k, cls=cls, swap=swap, splits=splits,
                     row_runs=row_runs, col_runs=col_runs, inner_run=inner, interleaved=int(nruns > 2))

@@ -5,6 +5,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <string>
 
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -15,6 +16,8 @@ struct tnc_plan_s {
 
 namespace {
 
+thread_local std::string g_last_error;
+
 bool debug_sync() {
   static int v = -1;
   if (v < 0) {
@@ -24,10 +27,24 @@ bool debug_sync() {
   return v == 1;
 }
 
-tnc_status check(hipError_t e, hipStream_t stream) {
-  if (e != hipSuccess) return TNC_ERR_HIP;
-  if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return TNC_ERR_HIP;
+tnc_status check(hipError_t e, hipStream_t stream, const char *what) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return TNC_ERR_HIP;
+  }
   return TNC_OK;
+}
+
+const char *op_name(int kind) {
+  switch (kind) {
+    case tnc::OP_COPY: return "k_copy launch";
+    case tnc::OP_COPY_TILED: return "k_copy_tiled launch";
+    case tnc::OP_TINY_GROUP: return "k_tiny launch";
+    case tnc::OP_SKINNY: return "k_skinny launch";
+    case tnc::OP_GEMM: return "k_cgemm launch";
+  }
+  return "launch";
 }
 
 }  // namespace
@@ -48,6 +65,7 @@ void tnc_plan_options_default(tnc_plan_options *o) {
 
 tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
                     tnc_plan_t *plan) {
+  g_last_error.clear();
   if (!plan) return TNC_ERR_INVALID_ARG;
   tnc_plan_s *p = new (std::nothrow) tnc_plan_s();
   if (!p) return TNC_ERR_OUT_OF_MEMORY;
@@ -134,8 +152,11 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
 
 tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
                        uint64_t workspace_bytes, void *stream_ptr) {
+  g_last_error.clear();
   if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
   const tnc::PlanImpl &p = plan->impl;
+  // an error left behind by an earlier, unrelated HIP call is not ours
+  (void)hipGetLastError();
   for (int32_t l = 0; l < p.L; ++l)
     if (!leaves[l]) return TNC_ERR_INVALID_ARG;
   if (workspace_bytes < p.stats.workspace_bytes) return TNC_ERR_WORKSPACE_TOO_SMALL;
@@ -147,10 +168,11 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
   char *blob = ws + p.ptab_bytes;
   char *arena = ws + p.header_bytes;
 
-  tnc_status st = check(tnc::launch_write_ptrs(ptab, arena, out, leaves, p.L, stream), stream);
+  tnc_status st = check(tnc::launch_write_ptrs(ptab, arena, out, leaves, p.L, stream), stream, "k_write_ptrs launch");
   if (st != TNC_OK) return st;
-  if (hipMemcpyAsync(blob, p.blob.data(), p.blob.size(), hipMemcpyHostToDevice, stream) != hipSuccess)
-    return TNC_ERR_HIP;
+  st = check(hipMemcpyAsync(blob, p.blob.data(), p.blob.size(), hipMemcpyHostToDevice, stream), stream,
+             "descriptor upload (hipMemcpyAsync)");
+  if (st != TNC_OK) return st;
 
   const auto *runs = reinterpret_cast<const tnc::RunDev *>(blob + p.blob_runs);
   const auto *cdesc = reinterpret_cast<const tnc::CopyDesc *>(blob + p.blob_copies);
@@ -187,6 +209,9 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
         case tnc::OP_COPY:
           e = tnc::launch_copy(cdesc + op.first, op.count, op.max_count, ptab, ints, sd, beta, stream);
           break;
+        case tnc::OP_COPY_TILED:
+          e = tnc::launch_copy_tiled(cdesc + op.first, op.max_count, ptab, ints, sd, beta, stream);
+          break;
         case tnc::OP_TINY_GROUP:
           e = tnc::launch_tiny(tdesc + op.first, op.count, ptab, runs, beta, stream);
           break;
@@ -211,12 +236,14 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
           break;
         }
       }
-      st = check(e, stream);
+      st = check(e, stream, op_name(op.kind));
       if (st != TNC_OK) return st;
     }
   }
   return TNC_OK;
 }
+
+const char *tnc_last_error(void) { return g_last_error.c_str(); }
 
 const char *tnc_status_string(tnc_status s) {
   switch (s) {

@@ -24,8 +24,11 @@ struct CopyDesc {
   int32_t rank, is_root;
   int64_t src_off, dst_off;   // in complex64 entries
   int64_t count;
-  int32_t ints_index;         // into the int64 table: dims[rank], src_strides[rank], slice[num_sliced]
-  int32_t pad;
+  int32_t ints_index;         // into the int64 table, see below
+  int32_t tiled;              // 0: ints = dims[rank], src_strides[rank], slice[num_sliced]
+                              // 1: ints = tile, n_outer, outer_pow2, outer_dims[n_outer],
+                              //    outer_src[n_outer], outer_dst[n_outer], slice[num_sliced],
+                              //    ld_src[tile], ld_lds[tile], st_dst[tile]
 };
 
 // One tiny pairwise step of a grouped launch, already oriented: C[i, j] =

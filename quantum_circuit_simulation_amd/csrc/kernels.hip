@@ -33,8 +33,25 @@ __device__ __forceinline__ void cmac(float2 &acc, float2 a, float2 b) {
 }
 
 // Offset in C (entries) of index `idx` along one side, runs outermost first.
+// Indices below 2^32 (every run size then fits too) take 32-bit division.
 __device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int n) {
   int64_t off = 0;
+  if (idx < (int64_t(1) << 32)) {
+    uint32_t i = (uint32_t)idx;
+    for (int q = n - 1; q >= 0 && i != 0; --q) {
+      const int64_t sz = r[q].size;
+      if (sz >= (int64_t(1) << 32)) {
+        off += (int64_t)i * r[q].stride;
+        i = 0;
+        break;
+      }
+      const uint32_t s32 = (uint32_t)sz;
+      const uint32_t nx = i / s32;
+      off += (int64_t)(i - nx * s32) * r[q].stride;
+      i = nx;
+    }
+    return off;
+  }
   for (int q = n - 1; q >= 0; --q) {
     const int64_t sz = r[q].size;
     const int64_t d = idx % sz;
@@ -94,6 +111,67 @@ __global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int
   }
 }
 
+// Tiled permuting copy: reads go along the source's smallest strides, writes
+// along the destination's innermost dims, with the tile transposed in LDS.
+// The per-entry offset tables are built on the host (they hold the index
+// arithmetic) and staged into LDS once per workgroup.
+constexpr int kTileMax = 1024;
+
+__global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const void *const *ptab, const int64_t *ints,
+                                                    SliceDigits sd, int32_t beta) {
+  __shared__ float2 buf[kTileMax];
+  __shared__ int64_t s_src[kTileMax];
+  __shared__ int32_t s_lds[kTileMax];
+  __shared__ int64_t s_dst[kTileMax];
+  const CopyDesc d = *desc;
+  const int64_t *t = ints + d.ints_index;
+  const int tile = (int)t[0];
+  const int nout = (int)t[1];
+  const int pow2 = (int)t[2];
+  const int64_t *od = t + 3;
+  const int64_t *osrc = od + nout;
+  const int64_t *odst = osrc + nout;
+  const int64_t *slc = odst + nout;
+  const int64_t *ld_src = slc + sd.n;
+  const int64_t *ld_lds = ld_src + tile;
+  const int64_t *st_dst = ld_lds + tile;
+  for (int e = threadIdx.x; e < tile; e += blockDim.x) {
+    s_src[e] = ld_src[e];
+    s_lds[e] = (int32_t)ld_lds[e];
+    s_dst[e] = st_dst[e];
+  }
+  int64_t base = d.src_off;
+  for (int q = 0; q < sd.n; ++q) base += (int64_t)sd.digit[q] * slc[q];
+  const float2 *src = (const float2 *)ptab[d.src_buf] + base;
+  float2 *dst = (float2 *)ptab[d.dst_buf] + d.dst_off;
+  const int b = beta && d.is_root;
+  const int64_t ntiles = d.count / tile;
+  __syncthreads();
+  for (int64_t o = blockIdx.x; o < ntiles; o += gridDim.x) {
+    int64_t r = o, bs = 0, bd = 0;
+    if (pow2) {
+      for (int q = nout - 1; q >= 0; --q) {
+        const int64_t e = od[q];
+        bs += (r & (e - 1)) * osrc[q];
+        bd += (r & (e - 1)) * odst[q];
+        r >>= __builtin_ctzll((unsigned long long)e);
+      }
+    } else {
+      for (int q = nout - 1; q >= 0; --q) {
+        const int64_t e = od[q];
+        const int64_t dg = r % e;
+        r /= e;
+        bs += dg * osrc[q];
+        bd += dg * odst[q];
+      }
+    }
+    for (int e = threadIdx.x; e < tile; e += blockDim.x) buf[s_lds[e]] = src[bs + s_src[e]];
+    __syncthreads();
+    for (int e = threadIdx.x; e < tile; e += blockDim.x) store_c(dst + bd + s_dst[e], buf[e], b);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // grouped tiny steps: one workgroup per step
 
@@ -140,6 +218,9 @@ __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void 
 constexpr int kSkinnyMax = 16;
 
 __global__ __launch_bounds__(256) void k_skinny(StepArgs a, int64_t kchunk, int G) {
+  __shared__ int64_t coloff[kSkinnyMax];
+  if (threadIdx.x < a.S) coloff[threadIdx.x] = run_offset(threadIdx.x, a.runs + a.nrr, a.ncr);
+  __syncthreads();
   const int rows_per_block = 256 / G;
   const int lane = threadIdx.x % G;
   const int64_t i = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / G;
@@ -176,7 +257,65 @@ __global__ __launch_bounds__(256) void k_skinny(StepArgs a, int64_t kchunk, int 
       const int64_t ro = run_offset(i, a.runs, a.nrr);
 #pragma unroll
       for (int s = 0; s < kSkinnyMax; ++s)
-        if (s < S) store_c(a.C + ro + run_offset(s, a.runs + a.nrr, a.ncr), acc[s], a.beta);
+        if (s < S) store_c(a.C + ro + coloff[s], acc[s], a.beta);
+    }
+  }
+}
+
+// Skinny steps with many rows: one row per thread.  Each K chunk of the
+// workgroup's 256 rows is loaded into LDS with coalesced reads (a row's chunk
+// is contiguous), the small operand's chunk sits in LDS and is read by
+// broadcast, and every thread accumulates its row's S outputs in registers.
+constexpr int kRowsKC = 16;
+
+__global__ __launch_bounds__(256) void k_skinny_rows(StepArgs a, int64_t kchunk) {
+  __shared__ float2 xs[256][kRowsKC + 1];
+  __shared__ float2 ys[kSkinnyMax][kRowsKC];
+  __shared__ int64_t coloff[kSkinnyMax];
+  const int tid = threadIdx.x;
+  const int S = (int)a.S;
+  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  float2 acc[kSkinnyMax];
+#pragma unroll
+  for (int q = 0; q < kSkinnyMax; ++q) acc[q] = make_float2(0.f, 0.f);
+  for (int64_t kc = k0; kc < k1; kc += kRowsKC) {
+    const int w = (int)min((int64_t)kRowsKC, k1 - kc);
+    __syncthreads();
+    // X chunk: 256 rows x w entries; thread t loads entry (row t / 16 + 16 p, col t % 16)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int row = tid / kRowsKC + 16 * p, col = tid % kRowsKC;
+      const int64_t gi = r0 + row;
+      xs[row][col] = (gi < a.R && col < w) ? a.X[gi * a.K + kc + col] : make_float2(0.f, 0.f);
+    }
+    if (tid < kSkinnyMax * kRowsKC) {
+      const int sr = tid / kRowsKC, col = tid % kRowsKC;
+      ys[sr][col] = (sr < S && col < w) ? a.Y[(int64_t)sr * a.K + kc + col] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+    for (int l = 0; l < w; ++l) {
+      const float2 x = xs[tid][l];
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) cmac(acc[q], x, ys[q][l]);
+    }
+  }
+  const int64_t i = r0 + tid;
+  if (i < a.R) {
+    if (a.splits > 1) {
+      float2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) p[q] = acc[q];
+    } else {
+      const int64_t ro = run_offset(i, a.runs, a.nrr);
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) store_c(a.C + ro + coloff[q], acc[q], a.beta);
     }
   }
 }
@@ -209,13 +348,40 @@ __global__ void k_split_reduce(StepArgs a) {
 // (yi, yr).  So one complex l costs two MFMAs per 32x32 complex block and
 // the operation count is exactly 8 R S K.
 //
-// LDS holds the X tile de-interleaved as two planes (re, im) and the Y tile
-// as three planes (yr, -yi, yi), each [rows][BK + pad]; a lane reads four
-// consecutive l of its plane with one 16-byte load.  Two LDS stages overlap
+// LDS holds the X tile and the Y tile de-interleaved as two planes (re, im),
+// each [rows][BK + pad]; a lane reads four consecutive l of a plane with one
+// 16-byte load.  Lanes 0-31 feed (yr | yi) to the (real | imaginary) MFMA,
+// lanes 32-63 feed (-yi | yr): plane h for the real part with its sign
+// flipped when h = 1, plane 1 - h for the imaginary part.  Two LDS stages overlap
 // the global loads of the next K tile with the MFMAs of the current one.
 
+// Workgroups are persistent: workgroup b takes tiles L = b, b + G, b + 2G, ...
+// (G = grid size) and keeps its LDS pipeline running across tile
+// boundaries, so the first K chunk of the next tile loads while the last
+// chunk of the current tile is multiplied and stored.  Tile order: workgroups
+// are dealt to the 8 XCDs round-robin, so L is first permuted to give each
+// XCD a contiguous range of tiles, which is then walked in groups of 8 tile
+// rows (column by column inside a group); an XCD's resident workgroups thus
+// cover a compact square of C and share their A and B slabs in its L2.
+constexpr uint32_t kSwizzleRows = 8;
+
+__device__ __forceinline__ void tile_coords(uint32_t L, uint32_t tiles_r, uint32_t tiles_c, uint32_t *tr,
+                                            uint32_t *tc) {
+  const uint32_t ntiles = tiles_r * tiles_c;
+  const uint32_t n8 = ntiles / 8 * 8;
+  const uint32_t Lp = L < n8 ? (L % 8) * (n8 / 8) + L / 8 : L;
+  const uint32_t group = Lp / (kSwizzleRows * tiles_c);
+  const uint32_t first = group * kSwizzleRows;
+  const uint32_t gsz = min(tiles_r - first, kSwizzleRows);
+  const uint32_t in_g = Lp - group * kSwizzleRows * tiles_c;
+  *tr = first + in_g % gsz;
+  *tc = in_g / gsz;
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, int64_t tiles_c) {
+// Row, column and tile indices are 32-bit: the planner keeps R, S and K of
+// GEMM-class steps below 2^31.
+__global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, uint32_t tiles_r, uint32_t tiles_c) {
   constexpr int PAD = 4;
   constexpr int LDK = BK + PAD;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -227,15 +393,201 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, in
   static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for 256 threads");
 
   __shared__ float As[2][2][BM][LDK];
-  __shared__ float Bs[2][3][BN][LDK];
+  __shared__ float Bs[2][2][BN][LDK];
+  __shared__ int64_t rowoff[2][BM];
+  __shared__ int64_t coloff[2][BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WAVES_C, wc = wave % WAVES_C;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int split = blockIdx.y;
+  const int32_t R = (int32_t)a.R, S = (int32_t)a.S, K = (int32_t)a.K;
+  const int32_t k0 = split * kchunk;
+  const int32_t k1 = min(K, k0 + kchunk);
+  const int32_t nkt = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+  const uint32_t G = gridDim.x;
+  const uint32_t ntiles = tiles_r * tiles_c;
+  const int32_t my_tiles = (blockIdx.x < ntiles) ? (int32_t)((ntiles - blockIdx.x + G - 1) / G) : 0;
+  const bool partial = a.splits > 1;
+
+  f32x16 accR[MB][NB], accI[MB][NB];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          accR[mb][nb][r] = 0.f;
+          accI[mb][nb][r] = 0.f;
+        }
+      }
+  };
+  auto origin = [&](int32_t j, int32_t *r0, int32_t *c0) {
+    uint32_t tr, tc;
+    tile_coords(blockIdx.x + (uint32_t)j * G, tiles_r, tiles_c, &tr, &tc);
+    *r0 = (int32_t)(tr * BM);
+    *c0 = (int32_t)(tc * BN);
+  };
+  auto tables = [&](int par, int32_t r0, int32_t c0) {
+    if (partial) return;
+    for (int t = tid; t < BM; t += 256) rowoff[par][t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += 256) coloff[par][t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+  };
+  auto epilogue = [&](int par, int32_t r0, int32_t c0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = wc * WN + nb * 32 + l32;
+        const int32_t gj = c0 + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wr * WM + mb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+          const int32_t gi = r0 + row;
+          if (gi < R && gj < S) {
+            const float2 v = make_float2(accR[mb][nb][r], accI[mb][nb][r]);
+            if (partial) a.scratch[((int64_t)split * R + gi) * S + gj] = v;
+            else store_c(a.C + rowoff[par][row] + coloff[par][col], v, a.beta);
+          }
+        }
+      }
+  };
+
+  zero_acc();
+  if (nkt == 0) {
+    // an empty K chunk of a split step: its partial sums are zero
+    for (int32_t j = 0; j < my_tiles; ++j) {
+      int32_t r0, c0;
+      origin(j, &r0, &c0);
+      epilogue(0, r0, c0);
+    }
+    return;
+  }
+
+  float2 ra[A_PER], rb[B_PER];
+  auto gload = [&](int32_t r0, int32_t c0, int32_t kt) {
+    const int32_t kb = k0 + kt * BK;
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      const int32_t gi = r0 + row, gl = kb + l;
+      ra[q] = (gi < R && gl < k1) ? a.X[(int64_t)gi * K + gl] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      const int32_t gj = c0 + col, gl = kb + l;
+      rb[q] = (gj < S && gl < k1) ? a.Y[(int64_t)gj * K + gl] : make_float2(0.f, 0.f);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      As[st][0][row][l] = ra[q].x;
+      As[st][1][row][l] = ra[q].y;
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      Bs[st][0][col][l] = rb[q].x;
+      Bs[st][1][col][l] = rb[q].y;
+    }
+  };
+
+  const int arow = wr * WM + l32;
+  const int bcol = wc * WN + l32;
+  const float sgn = h ? -1.f : 1.f;  // real-part operand: yr (lanes 0-31), -yi (lanes 32-63)
+
+  const int32_t total = my_tiles * nkt;
+  int32_t j = 0, kt = 0;        // tile and K chunk of the current iteration
+  int32_t r0 = 0, c0 = 0;
+  if (total > 0) {
+    origin(0, &r0, &c0);
+    gload(r0, c0, 0);
+    lstore(0);
+    tables(0, r0, c0);
+  }
+  __syncthreads();
+  for (int32_t it = 0; it < total; ++it) {
+    const int st = it & 1;
+    // the next iteration's chunk, possibly of the next tile
+    int32_t jn = j, ktn = kt + 1, nr0 = r0, nc0 = c0;
+    if (ktn == nkt) {
+      ktn = 0;
+      ++jn;
+      if (jn < my_tiles) origin(jn, &nr0, &nc0);
+    }
+    const bool more = it + 1 < total;
+    if (more) gload(nr0, nc0, ktn);
+#pragma unroll
+    for (int l4 = 0; l4 < BK; l4 += 4) {
+      f32x4 av[MB], brv[NB], biv[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[mb] = *(const f32x4 *)&As[st][h][arow + mb * 32][l4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        brv[nb] = sgn * *(const f32x4 *)&Bs[st][h][bcol + nb * 32][l4];
+        biv[nb] = *(const f32x4 *)&Bs[st][1 - h][bcol + nb * 32][l4];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            accR[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb][kk], brv[nb][kk], accR[mb][nb], 0, 0, 0);
+            accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb][kk], biv[nb][kk], accI[mb][nb], 0, 0, 0);
+          }
+    }
+    if (kt == nkt - 1) {
+      epilogue(j & 1, r0, c0);
+      zero_acc();
+    }
+    if (more) {
+      lstore(st ^ 1);
+      if (ktn == 0) tables(jn & 1, nr0, nc0);
+    }
+    __syncthreads();
+    j = jn;
+    kt = ktn;
+    r0 = nr0;
+    c0 = nc0;
+  }
+}
+
+// One tile per workgroup (long K chunks).  Same MFMA scheme and LDS pipeline
+// as k_cgemm, without the multi-tile loop; the tile comes from the same
+// XCD-aware order.
+template <int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchunk, uint32_t tiles_r,
+                                                       uint32_t tiles_c) {
+  constexpr int PAD = 4;
+  constexpr int LDK = BK + PAD;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int WAVES_C = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert(BK % 4 == 0, "BK");
+  constexpr int A_PER = BM * BK / 256;
+  constexpr int B_PER = BN * BK / 256;
+  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for 256 threads");
+
+  __shared__ float As[2][2][BM][LDK];
+  __shared__ float Bs[2][2][BN][LDK];
   __shared__ int64_t rowoff[BM];
   __shared__ int64_t coloff[BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WAVES_C, wc = wave % WAVES_C;
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t tile = blockIdx.x;
-  const int64_t r0 = (tile / tiles_c) * BM, c0 = (tile % tiles_c) * BN;
+  uint32_t tr, tc;
+  tile_coords(blockIdx.x, tiles_r, tiles_c, &tr, &tc);
+  const int64_t r0 = (int64_t)tr * BM, c0 = (int64_t)tc * BN;
   const int split = blockIdx.y;
   const int64_t k0 = (int64_t)split * kchunk;
   const int64_t k1 = min(a.K, k0 + kchunk);
@@ -285,15 +637,13 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, in
       const int e = tid + 256 * q;
       const int col = e / BK, l = e % BK;
       Bs[st][0][col][l] = rb[q].x;
-      Bs[st][1][col][l] = -rb[q].y;
-      Bs[st][2][col][l] = rb[q].y;
+      Bs[st][1][col][l] = rb[q].y;
     }
   };
 
   const int arow = wr * WM + l32;
   const int bcol = wc * WN + l32;
-  const int pbr = h ? 1 : 0;  // plane feeding the real-part MFMA: yr (lanes 0-31), -yi (32-63)
-  const int pbi = h ? 0 : 2;  // imaginary part: yi (lanes 0-31), yr (32-63)
+  const float sgn = h ? -1.f : 1.f;  // real-part operand: yr (lanes 0-31), -yi (lanes 32-63)
 
   if (nkt > 0) {
     gload(0);
@@ -310,8 +660,8 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, in
       for (int mb = 0; mb < MB; ++mb) av[mb] = *(const f32x4 *)&As[st][h][arow + mb * 32][l4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        brv[nb] = *(const f32x4 *)&Bs[st][pbr][bcol + nb * 32][l4];
-        biv[nb] = *(const f32x4 *)&Bs[st][pbi][bcol + nb * 32][l4];
+        brv[nb] = sgn * *(const f32x4 *)&Bs[st][h][bcol + nb * 32][l4];
+        biv[nb] = *(const f32x4 *)&Bs[st][1 - h][bcol + nb * 32][l4];
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -327,7 +677,6 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, in
     __syncthreads();
   }
 
-  // epilogue: output offsets of this tile's rows and columns
   const bool partial = a.splits > 1;
   if (!partial) {
     for (int t = tid; t < BM; t += 256) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
@@ -353,6 +702,20 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int64_t kchunk, in
     }
 }
 
+int g_num_cus = 0;
+
+int num_cus() {
+  if (g_num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
 int pow2_floor_i(int64_t v) {
   int p = 1;
   while ((int64_t)p * 2 <= v && p < (1 << 30)) p *= 2;
@@ -364,8 +727,28 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   const int64_t tiles_r = (a.R + BM - 1) / BM, tiles_c = (a.S + BN - 1) / BN;
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
-  dim3 grid((unsigned)(tiles_r * tiles_c), (unsigned)a.splits);
-  hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, kchunk, tiles_c);
+  if (a.R >= (int64_t(1) << 31) || a.S >= (int64_t(1) << 31) || a.K >= (int64_t(1) << 31) ||
+      tiles_r * tiles_c >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  // Short K chunks: a persistent grid (two workgroups per CU over the K
+  // splits, a multiple of 8 so every XCD gets an equal share) hides each
+  // tile's load latency behind the previous tile.  Long K chunks: one tile
+  // per workgroup, so co-resident workgroups stay in step through K and
+  // share their L2 lines (persistent workgroups drift apart over many tiles).
+  const int64_t ntiles = tiles_r * tiles_c;
+  if (kchunk > 256) {
+    dim3 grid((unsigned)ntiles, (unsigned)a.splits);
+    hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, kchunk,
+                       (uint32_t)tiles_r, (uint32_t)tiles_c);
+    return hipGetLastError();
+  }
+  int64_t g = (2 * (int64_t)num_cus() + a.splits - 1) / a.splits;
+  if (g >= 8) g = g / 8 * 8;
+  if (g > ntiles) g = ntiles;
+  if (g < 1) g = 1;
+  dim3 grid((unsigned)g, (unsigned)a.splits);
+  hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, (int32_t)kchunk,
+                     (uint32_t)tiles_r, (uint32_t)tiles_c);
   return hipGetLastError();
 }
 
@@ -407,6 +790,16 @@ hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, 
   return hipGetLastError();
 }
 
+hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
+                             const SliceDigits &digits, int32_t beta, hipStream_t stream) {
+  // one workgroup per tile of >= 32 entries, at most 8192 workgroups
+  int64_t blocks = count / 32;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_copy_tiled, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits, beta);
+  return hipGetLastError();
+}
+
 hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
                        int32_t beta, hipStream_t stream) {
   hipLaunchKernelGGL(k_tiny, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
@@ -416,6 +809,14 @@ hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
+  if (a.R >= 4096) {
+    // many rows: one row per thread, operand chunks staged through LDS
+    dim3 grid((unsigned)((a.R + 255) / 256), (unsigned)a.splits);
+    hipLaunchKernelGGL(k_skinny_rows, grid, dim3(256), 0, stream, a, kchunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits <= 1) return e;
+    return run_split_reduce(a, stream);
+  }
   int G = pow2_floor_i(kchunk / 8);
   if (G > 64) G = 64;
   if (G < 1) G = 1;
@@ -428,8 +829,11 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
+  // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
-  if (a.S > 64) e = run_cgemm<128, 128, 8, 64, 64>(a, stream);
+  if (a.S > 64 && a.R <= 32) e = run_cgemm<32, 256, 8, 32, 64>(a, stream);
+  else if (a.S > 64 && a.R <= 64) e = run_cgemm<64, 256, 8, 64, 64>(a, stream);
+  else if (a.S > 64) e = run_cgemm<128, 128, 8, 64, 64>(a, stream);
   else if (a.S > 32) e = run_cgemm<256, 64, 8, 64, 64>(a, stream);
   else e = run_cgemm<256, 32, 8, 64, 32>(a, stream);
   if (e != hipSuccess || a.splits <= 1) return e;

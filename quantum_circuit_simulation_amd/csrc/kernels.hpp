@@ -36,6 +36,8 @@ hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *con
                              hipStream_t stream);
 hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, const void *const *ptab,
                        const int64_t *ints, const SliceDigits &digits, int32_t beta, hipStream_t stream);
+hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
+                             const SliceDigits &digits, int32_t beta, hipStream_t stream);
 hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
                        int32_t beta, hipStream_t stream);
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream);

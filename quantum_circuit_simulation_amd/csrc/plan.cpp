@@ -81,15 +81,16 @@ class Arena {
 };
 
 int32_t split_rule(int32_t cls, int64_t R, int64_t S, int64_t k) {
+  // enough workgroups to fill the chip; K chunks of >= 256 (GEMM) / 1024 (skinny)
   if (cls == TNC_CLASS_GEMM) {
     int64_t tiles = ceil_div(R, kGemmNominalTile) * ceil_div(S, kGemmNominalTile);
-    if (tiles >= 128 || k < 4096) return 1;
-    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(256 / tiles), pow2_floor(k / 2048)));
+    if (tiles >= 256 || k < 512) return 1;
+    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(512 / tiles), pow2_floor(k / 256)));
   }
   if (cls == TNC_CLASS_SKINNY) {
     int64_t blocks = ceil_div(R, 256);
-    if (blocks >= 512 || k < 4096) return 1;
-    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(1024 / blocks), pow2_floor(k / 2048)));
+    if (blocks >= 512 || k < 2048) return 1;
+    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(1024 / blocks), pow2_floor(k / 1024)));
   }
   return 1;
 }
@@ -122,6 +123,102 @@ void make_runs(const std::vector<int32_t> &c_order, const std::vector<int64_t> &
   for (auto &r : runs) (r.row ? nd->row_runs : nd->col_runs).push_back({r.size, r.stride});
   nd->inner_run = runs.empty() ? 1 : runs.back().size;
   nd->interleaved = runs.size() > 2 ? 1 : 0;
+}
+
+// Tile a large copy (see CopyOp).  Leaves c->tiled = 0 when no tile of at
+// most kCopyTileMax entries covers both innermost runs.
+void make_tile(CopyOp *c) {
+  struct Dim { int64_t e, src; };
+  std::vector<Dim> d;
+  for (size_t q = 0; q < c->dims.size(); ++q) {
+    // refine dims above 32 into (e / 32, 32) so a tile can take their inner part
+    int64_t e = c->dims[q], st = c->src_strides[q];
+    std::vector<Dim> parts;
+    while (e > 32 && e % 32 == 0) {
+      parts.push_back({32, st});
+      st *= 32;
+      e /= 32;
+    }
+    parts.push_back({e, st});
+    for (auto it = parts.rbegin(); it != parts.rend(); ++it) d.push_back(*it);
+  }
+  const int n = (int)d.size();
+  if (n < 2) return;
+  std::vector<int64_t> dst(n);
+  int64_t acc = 1;
+  for (int q = n - 1; q >= 0; --q) {
+    dst[q] = acc;
+    acc *= d[q].e;
+  }
+  std::vector<char> in(n, 0);
+  int64_t tprod = 1;
+  for (int q = n - 1; q >= 0 && tprod < 32; --q) {  // innermost destination dims
+    in[q] = 1;
+    tprod *= d[q].e;
+  }
+  std::vector<int> by_src(n);
+  for (int q = 0; q < n; ++q) by_src[q] = q;
+  std::stable_sort(by_src.begin(), by_src.end(), [&](int a, int b) { return d[a].src < d[b].src; });
+  int64_t sprod = 1;
+  for (int q : by_src) {  // smallest source strides
+    if (sprod >= 32) break;
+    if (!in[q]) {
+      in[q] = 1;
+      tprod *= d[q].e;
+    }
+    sprod *= d[q].e;
+  }
+  for (int q = n - 1; q >= 0; --q)  // widen the tile along the destination while it fits
+    if (!in[q] && tprod * d[q].e <= kCopyTileMax) {
+      in[q] = 1;
+      tprod *= d[q].e;
+    }
+  if (tprod > kCopyTileMax || tprod < 32) return;
+  std::vector<int> tdst, tsrc, outer;
+  for (int q = 0; q < n; ++q) (in[q] ? tdst : outer).push_back(q);
+  tsrc = tdst;
+  std::stable_sort(tsrc.begin(), tsrc.end(), [&](int a, int b) { return d[a].src < d[b].src; });
+  std::vector<int64_t> lds_stride(n, 0);
+  acc = 1;
+  for (int i = (int)tdst.size() - 1; i >= 0; --i) {
+    lds_stride[tdst[i]] = acc;
+    acc *= d[tdst[i]].e;
+  }
+  c->tile = tprod;
+  c->ld_src.assign(tprod, 0);
+  c->ld_lds.assign(tprod, 0);
+  c->st_dst.assign(tprod, 0);
+  for (int64_t e = 0; e < tprod; ++e) {
+    int64_t r = e, so = 0, lo = 0;
+    for (int q : tsrc) {  // fastest = smallest source stride
+      int64_t dg = r % d[q].e;
+      r /= d[q].e;
+      so += dg * d[q].src;
+      lo += dg * lds_stride[q];
+    }
+    c->ld_src[e] = so;
+    c->ld_lds[e] = lo;
+    r = e;
+    int64_t dof = 0;
+    for (int i = (int)tdst.size() - 1; i >= 0; --i) {
+      int q = tdst[i];
+      int64_t dg = r % d[q].e;
+      r /= d[q].e;
+      dof += dg * dst[q];
+    }
+    c->st_dst[e] = dof;
+  }
+  c->outer_dims.clear();
+  c->outer_src.clear();
+  c->outer_dst.clear();
+  c->outer_pow2 = 1;
+  for (int q : outer) {
+    c->outer_dims.push_back(d[q].e);
+    c->outer_src.push_back(d[q].src);
+    c->outer_dst.push_back(dst[q]);
+    if ((d[q].e & (d[q].e - 1)) != 0) c->outer_pow2 = 0;
+  }
+  c->tiled = 1;
 }
 
 tnc_status validate(PlanImpl *p, const tnc_network *net, const tnc_tree *tree) {
@@ -331,6 +428,10 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     else nd.swap = (last_eff >= 0 && std::binary_search(M[s].begin(), M[s].end(), last_eff)) ? 1 : 0;
     make_runs(c_order, ext, nd.swap ? N[s] : M[s], &nd);
     int64_t R = nd.swap ? nd.n : nd.m, Sx = nd.swap ? nd.m : nd.n;
+    // the GEMM kernel indexes rows, columns and K with 32-bit integers
+    if (nd.cls == TNC_CLASS_GEMM && (R >= (int64_t(1) << 31) || Sx >= (int64_t(1) << 31) ||
+                                     nd.k >= (int64_t(1) << 31)))
+      return TNC_ERR_UNSUPPORTED;
     nd.splits = split_rule(nd.cls, R, Sx, nd.k);
     if (nd.splits > 1) nd.scratch_bytes = (uint64_t)nd.splits * (uint64_t)R * (uint64_t)Sx * 8;
     // operand copies
@@ -426,6 +527,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     }
     return st;
   };
+  bool copy_bounds_ok = true;
   auto make_copy = [&](int32_t src_tensor, int32_t src_buf, uint64_t src_off, int32_t dst_buf, uint64_t dst_off,
                        const std::vector<int32_t> &dst_order, int32_t is_root) {
     CopyOp c;
@@ -470,6 +572,13 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     c.src_strides = sst;
     c.count = prod(ext, dst_order);
     for (int32_t x : p->sliced) c.slice_strides.push_back(src_tensor < L ? stride_of(x) : 0);
+    // every source offset the copy can form must lie inside the source buffer
+    int64_t src_size = src_tensor < L ? prod(p->extents, p->leaves[src_tensor]) : prod(ext, src_modes);
+    int64_t max_off = 0;
+    for (size_t q = 0; q < dims.size(); ++q) max_off += (dims[q] - 1) * sst[q];
+    for (size_t t = 0; t < p->sliced.size(); ++t) max_off += (p->slice_extents[t] - 1) * c.slice_strides[t];
+    if (max_off >= src_size) copy_bounds_ok = false;
+    if (c.count >= kCopyTiledMin) make_tile(&c);
     return c;
   };
   p->copies.clear();
@@ -477,6 +586,10 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   auto push_copy_op = [&](int32_t idx) {
     const int64_t kBig = int64_t(1) << 20;
     int64_t cnt = p->copies[idx].count;
+    if (p->copies[idx].tiled) {
+      p->program.push_back({OP_COPY_TILED, idx, 1, cnt});
+      return;
+    }
     if (!p->program.empty() && p->program.back().kind == OP_COPY && cnt <= kBig &&
         p->program.back().max_count <= kBig && p->program.back().first + p->program.back().count == idx) {
       p->program.back().count++;
@@ -550,6 +663,8 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     push_copy_op((int32_t)p->copies.size() - 1);
   }
 
+  if (!copy_bounds_ok) return TNC_ERR_UNSUPPORTED;  // internal layout error: never launch it
+
   // ---- descriptor blob: [runs][copy descs][tiny descs][int64 table]
   std::vector<CopyDesc> cdesc;
   std::vector<int64_t> ints;
@@ -563,9 +678,23 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     d.dst_off = (int64_t)(c.dst_off_bytes / 8);
     d.count = c.count;
     d.ints_index = (int32_t)ints.size();
-    ints.insert(ints.end(), c.dims.begin(), c.dims.end());
-    ints.insert(ints.end(), c.src_strides.begin(), c.src_strides.end());
-    ints.insert(ints.end(), c.slice_strides.begin(), c.slice_strides.end());
+    d.tiled = c.tiled;
+    if (!c.tiled) {
+      ints.insert(ints.end(), c.dims.begin(), c.dims.end());
+      ints.insert(ints.end(), c.src_strides.begin(), c.src_strides.end());
+      ints.insert(ints.end(), c.slice_strides.begin(), c.slice_strides.end());
+    } else {
+      ints.push_back(c.tile);
+      ints.push_back((int64_t)c.outer_dims.size());
+      ints.push_back(c.outer_pow2);
+      ints.insert(ints.end(), c.outer_dims.begin(), c.outer_dims.end());
+      ints.insert(ints.end(), c.outer_src.begin(), c.outer_src.end());
+      ints.insert(ints.end(), c.outer_dst.begin(), c.outer_dst.end());
+      ints.insert(ints.end(), c.slice_strides.begin(), c.slice_strides.end());
+      ints.insert(ints.end(), c.ld_src.begin(), c.ld_src.end());
+      ints.insert(ints.end(), c.ld_lds.begin(), c.ld_lds.end());
+      ints.insert(ints.end(), c.st_dst.begin(), c.st_dst.end());
+    }
     cdesc.push_back(d);
   }
   auto append = [&](const void *src, size_t n) {

@@ -20,6 +20,8 @@ constexpr uint64_t kNone = UINT64_MAX;
 constexpr int kMaxRank = 64;
 constexpr int64_t kSkinnyMaxSide = 16;   // skinny when min(m, n) <= this
 constexpr int64_t kGemmNominalTile = 128;
+constexpr int64_t kCopyTileMax = 1024;     // entries per LDS tile of a tiled copy
+constexpr int64_t kCopyTiledMin = 1 << 16;  // copies at least this large use the tiled kernel
 
 struct Run {
   int64_t size;
@@ -38,6 +40,15 @@ struct CopyOp {
   std::vector<int64_t> dims;   // destination dims, outermost first (merged, extent > 1)
   std::vector<int64_t> src_strides;
   std::vector<int64_t> slice_strides;  // per sliced mode: source stride (0 if absent)
+  // Tiled variant (large copies): a tile over the innermost destination dims
+  // and the smallest-source-stride dims goes through LDS; the tables give,
+  // per tile entry, its source offset and LDS slot in source order, and its
+  // destination offset in destination order.  Outer dims enumerate tiles.
+  int32_t tiled = 0;
+  int64_t tile = 0;
+  std::vector<int64_t> ld_src, ld_lds, st_dst;
+  std::vector<int64_t> outer_dims, outer_src, outer_dst;
+  int32_t outer_pow2 = 0;
 };
 
 struct Node {
@@ -59,7 +70,7 @@ struct Node {
   int32_t runs_index = 0;
 };
 
-enum OpKind : int32_t { OP_COPY = 0, OP_TINY_GROUP = 1, OP_SKINNY = 2, OP_GEMM = 3 };
+enum OpKind : int32_t { OP_COPY = 0, OP_TINY_GROUP = 1, OP_SKINNY = 2, OP_GEMM = 3, OP_COPY_TILED = 4 };
 
 struct Op {
   OpKind kind;

@@ -63,6 +63,8 @@ PAIR_CASES = [
     (12, 2, 2, 2), (14, 4, 3, 2), (10, 0, 12, 2), (0, 0, 16, 2), (3, 1, 13, 2),   # skinny
     (9, 9, 6, 2), (10, 6, 6, 2), (10, 5, 7, 2), (9, 7, 13, 2), (6, 6, 14, 2),     # gemm
     (6, 5, 3, 3), (5, 4, 4, 3), (4, 4, 0, 3), (7, 6, 1, 2),                       # ragged / k = 1
+    (3, 6, 3, 3), (4, 7, 2, 3), (6, 16, 4, 2), (5, 15, 6, 2), (12, 12, 6, 2),     # short-R tiles, many tiles
+    (11, 13, 3, 2), (6, 9, 11, 2), (5, 12, 10, 2),                                # tiles not a multiple of 8, split K
 ]
 
 
@@ -170,3 +172,34 @@ def test_brickwork_30q_batch_and_amplitude():
     net1, tree1 = close_open_wires(net, tree)
     amp, _ = _gpu_run(net1, tree1)
     _assert_close(amp, ref[0])
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_large_single_leaf_permutes_are_exact(seed):
+    """0-step networks: the result is the leaf re-laid in the output order,
+    through the tiled permute (>= 2^16 entries), so it must be bit-exact."""
+    rng = np.random.default_rng(700 + seed)
+    choices = (2, 2, 2, 4, 8) if seed < 5 else (2, 3, 4, 5, 6, 7)
+    while True:
+        r = int(rng.integers(4, 14))
+        ext = [int(rng.choice(choices)) for _ in range(r)]
+        if 1 << 16 <= int(np.prod(ext)) <= 1 << 22:
+            break
+    d = sweep.complex_gaussian(rng, tuple(ext))
+    perm = [int(x) for x in rng.permutation(r)]
+    net = Network(np.array(ext, dtype=np.int64), [list(range(r))], perm, [d], name=f"permute{ext}")
+    got, plan = _gpu_run(net, Tree([], []))
+    assert np.array_equal(got, np.transpose(d, perm).astype(np.complex128))
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("seed", range(4))
+def test_large_permuted_pairs(seed, order):
+    """Pairwise steps whose operands are re-laid by the tiled permute
+    (staging under lifetime order; operand and root permutes under naive)."""
+    rng = np.random.default_rng(900 + seed)
+    R, S, K = [int(x) for x in rng.integers(5, 9, size=3)]
+    net, tree = _pair(R, S, K, seed=seed + 40, ext=2, permuted=True)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, order=order)
+    _assert_close(got, ref)
