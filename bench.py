@@ -193,6 +193,13 @@ class TreeWorkload:
             net = circuits.brickwork(12, 8, 101).to_network()
             tree = trees.greedy_tree(net)
             self.config = {"workload": "brickwork-12q-d8-amplitude", "seed": 101, "tree": "greedy"}
+        elif which == "grid":
+            net = circuits.grid_fsim(6, 6, 14, 505).to_network()
+            tree = trees.search_tree(net, trials=200, seed=1)
+            self.config = {"workload": "grid-6x6-d14-amplitude", "seed": 505,
+                           "tree": "best of 200 seeded randomized-greedy trees (seed 1)",
+                           "note": "largest fSim grid instance whose in-house tree fits one GPU unsliced; "
+                                   "7x8 depth 16 reaches width 2^59 with this search"}
         elif which == "brickwork30":
             net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
             tree = trees.greedy_tree(net)
@@ -242,6 +249,44 @@ class TreeWorkload:
         res["naive_over_lifetime"] = res["naive_ms"] / res["lifetime_ms"]
         return res, []
 
+    def slicing(self, steps, s_list):
+        """The same tree sliced on s closed modes (chosen greedily), run
+        slice after slice: time t_s and flops F_s = slices x (flops of one
+        slice) against the unsliced t_1, F_1."""
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import trees
+        res = {}
+        chosen = trees.choose_slices(self.net, self.tree, max(s_list))
+        t1 = None
+        f1 = self.flops
+        for s in [0] + list(s_list):
+            plan = qa.Plan.from_network(self.net, self.tree, sliced=chosen[:s]) if s else self.plan
+            if s == 0:
+                ws = self.ws
+            else:
+                self.ws = None  # the unsliced workspace can be the largest buffer on the GPU
+                torch.cuda.empty_cache()
+                ws = qa.alloc_workspace(plan)
+            plan.execute(self.leaves, self.out, ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                plan.execute(self.leaves, self.out, ws)
+                e1.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+            st = plan.stats()
+            fs = st["flops"] * st["num_slices"]
+            if s == 0:
+                t1 = ms
+            res[f"s{s}"] = {"ms": ms, "slices": st["num_slices"], "flop": fs, "max_intermediate": st["max_intermediate"],
+                            "workspace_bytes": st["workspace_bytes"], "R_s": fs / f1, "E_s": ms / t1,
+                            "capture": (ms / t1) / (fs / f1), "tflops": fs / (ms / 1e3) / 1e12}
+            log(f"slicing s={s}: {ms:.1f} ms, {st['num_slices']} slices, R_s={fs / f1:.3f}, E_s={ms / t1:.3f}")
+            del ws
+        return res
+
     def kernel_of(self, idx):
         return "whole tree"
 
@@ -251,11 +296,36 @@ class TreeWorkload:
     def cpu_baseline(self, budget_s=12.0):
         import oracle
         threads = oracle.max_threads()
+        if self.flops > 5e12:
+            # far beyond a bounded CPU run: time exact complex128 entries of the
+            # tree's largest step on gathered rows instead (same rate measure)
+            return self._cpu_largest_step(budget_s, threads)
         t0 = time.perf_counter()
         oracle.contract_network(self.net, self.tree, threads=threads)
         el = time.perf_counter() - t0
         return {"value": self.flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                 "sample": f"full contraction ({self.flops:.3g} flop in {el:.1f} s)"}
+
+    def _cpu_largest_step(self, budget_s, threads):
+        import oracle
+        best = max(range(self.plan.num_steps), key=lambda s: (lambda n: n["m"] * n["n"] * n["k"])(self.plan.node(s)))
+        nd = self.plan.node(best)
+        k = int(nd["k"])
+        rng = np.random.default_rng(5)
+        a = (rng.standard_normal((64, k)) + 1j * rng.standard_normal((64, k))).astype(np.complex64)
+        b = (rng.standard_normal((64, k)) + 1j * rng.standard_normal((64, k))).astype(np.complex64)
+        t0 = time.perf_counter()
+        done = 0
+        ni = 4
+        while True:
+            oracle.pair_block(a[:ni], b, threads=threads)
+            done += ni * 64
+            el = time.perf_counter() - t0
+            if el > budget_s:
+                break
+            ni = min(64, ni * 2)
+        return {"value": 8.0 * done * k / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} exact complex128 entries of the tree's largest step (k = {k}) in {el:.1f} s"}
 
 
 def calibrate_copy(entries=1 << 27):
@@ -280,7 +350,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "peps", "brickwork12", "brickwork30"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "peps", "brickwork12", "brickwork30", "grid"])
+    ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
+                                                 "e.g. 2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cases", default="", help="comma-separated sweep case indices (default: all feasible)")
     ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
@@ -369,6 +441,10 @@ def main():
             rep["ablation_cases"] = abl_rows
             json.dump(rep, open(args.report, "w"), indent=1)
 
+    slicing = None
+    if args.slices:
+        slicing = wl.slicing(max(1, args.steps), [int(x) for x in args.slices.split(",")])
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -381,6 +457,7 @@ def main():
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
             **({"ablation": ablation} if ablation is not None else {}),
+            **({"slicing": slicing} if slicing is not None else {}),
             "host_wall_s": round(wall, 3)}
     print(json.dumps(line), flush=True)
 

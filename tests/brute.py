@@ -37,3 +37,22 @@ def einsum_full(extents, leaves, out_modes, data) -> np.ndarray:
         ops.append([letters[x] for x in l])
     ops.append([letters[x] for x in out_modes])
     return np.einsum(*ops, optimize="greedy")
+
+
+def track_basis_state(n: int, gates, bits0=None):
+    """For a circuit of monomial gates (one non-zero per column), follow the
+    basis state |bits0> through every gate.  Returns (bits, amplitude) with
+    U|bits0> = amplitude |bits>.  Gate matrices are taken as given (pass the
+    complex64-rounded ones to match the network leaves)."""
+    bits = [0] * n if bits0 is None else list(bits0)
+    amp = complex(1.0)
+    for a, b, u in gates:
+        u = np.asarray(u)
+        i = 2 * bits[a] + bits[b]
+        col = u[:, i]
+        nz = np.flatnonzero(np.abs(col) > 0)
+        assert len(nz) == 1, "gate is not monomial"
+        o = int(nz[0])
+        amp *= complex(col[o])
+        bits[a], bits[b] = o >> 1, o & 1
+    return bits, amp

@@ -244,3 +244,42 @@ def test_sampled_entries_match_full_contraction():
     b = net.data[1].reshape(-1)[ob]
     got = oracle.dot_rows(a, b)
     assert np.allclose(got, full[idx], rtol=1e-13, atol=1e-13)
+
+
+def test_monomial_circuit_amplitude_is_tracked_phase():
+    from tests.brute import track_basis_state
+    c = circuits.grid_monomial(3, 4, 8, 12)
+    g64 = _gates64(c)
+    bits, amp = track_basis_state(12, g64)
+    assert abs(abs(amp) - 1.0) < 1e-6
+    net = c.to_network(bits=bits)
+    got = oracle.contract_network(net, trees.greedy_tree(net))
+    ok, err = rel_err_ok(got, amp, TOL128)
+    assert ok, err
+    # any other bra gives exactly zero
+    other = list(bits)
+    other[5] ^= 1
+    net0 = c.to_network(bits=other)
+    assert oracle.contract_network(net0, trees.greedy_tree(net0)) == 0
+
+
+def test_monomial_tracking_matches_statevector():
+    from tests.brute import track_basis_state
+    c = circuits.grid_monomial(2, 4, 8, 3)
+    g = _gates64(c)
+    bits, amp = track_basis_state(8, g)
+    psi = statevector(8, g)
+    idx = int("".join(map(str, bits)), 2)
+    assert abs(psi[idx] - amp) < 1e-12
+    assert abs(np.sum(np.abs(psi) ** 2) - 1) < 1e-6
+
+
+def test_random_greedy_search_is_deterministic_and_valid():
+    net = circuits.grid_fsim(3, 4, 8, 1).to_network(open_qubits=[0])
+    t1 = trees.search_tree(net, trials=10, seed=3)
+    t2 = trees.search_tree(net, trials=10, seed=3)
+    assert t1.lhs == t2.lhs and t1.rhs == t2.rhs
+    ref = oracle.contract_network(net, trees.greedy_tree(net))
+    got = oracle.contract_network(net, t1)
+    ok, err = rel_err_ok(got, ref, TOL128)
+    assert ok, err

@@ -174,3 +174,29 @@ def from_gates(n_qubits: int, gates: Iterable[Tuple[int, int, np.ndarray]]) -> C
 
 
 HADAMARD = np.array([[1, 1], [1, -1]], dtype=np.complex128) / np.sqrt(2.0)
+
+
+def grid_monomial(rows: int, cols: int, depth: int, seed: int) -> Circuit:
+    """Same couplers as ``grid_fsim`` but every gate is a permutation times
+    phases: fSim(pi/2, phi) (an iSWAP-like monomial) times single-qubit
+    factors that are diagonal or anti-diagonal with random phases.  The
+    circuit maps each basis state to one basis state with a phase, so a single
+    amplitude is known exactly by tracking one basis state."""
+    rng = np.random.default_rng(seed)
+    pats = grid_patterns(rows, cols)
+
+    def one_qubit():
+        a, b = np.exp(1j * rng.uniform(0, 2 * np.pi, size=2))
+        if rng.random() < 0.5:
+            return np.array([[a, 0], [0, b]], dtype=np.complex128)
+        return np.array([[0, a], [b, 0]], dtype=np.complex128)
+
+    c = Circuit(rows * cols)
+    for t in range(depth):
+        for a, b in pats[t % 4]:
+            phi = rng.uniform(0.0, 2 * np.pi)
+            # fSim(pi/2, phi) written out exactly (cos(pi/2) is not 0 in floating point)
+            g = np.array([[1, 0, 0, 0], [0, 0, -1j, 0], [0, -1j, 0, 0], [0, 0, 0, np.exp(-1j * phi)]],
+                         dtype=np.complex128)
+            c.add(a, b, g @ np.kron(one_qubit(), one_qubit()))
+    return c

@@ -137,3 +137,97 @@ def choose_slices(net: Network, tree: Tree, s: int) -> List[int]:
             break
         chosen.append(best[2])
     return chosen
+
+
+def random_greedy_tree(net: Network, seed: int, alpha: float = 1.0, temperature: float = 0.3) -> Tree:
+    """One randomized greedy contraction: among pairs sharing a mode, take the
+    pair minimising log2|C| - alpha (log2|A| + log2|B|) plus Gumbel noise of
+    scale `temperature` (temperature 0 gives a deterministic greedy)."""
+    import heapq
+    import math
+    rng = np.random.default_rng(seed)
+    ext = net.extents
+    lg = {x: math.log2(float(ext[x])) for x in range(len(ext))}
+    L = net.num_leaves
+    live: Dict[int, frozenset] = {i: frozenset(m) for i, m in enumerate(net.leaves)}
+    size = {i: sum(lg[x] for x in m) for i, m in live.items()}
+    holders: Dict[int, set] = {}
+    for i, ms in live.items():
+        for x in ms:
+            holders.setdefault(x, set()).add(i)
+    heap = []
+
+    def push(a, b):
+        A, B = live[a], live[b]
+        K = A & B
+        kk = sum(lg[x] for x in K)
+        c = size[a] + size[b] - 2 * kk
+        score = c - alpha * (size[a] + size[b])
+        if temperature > 0:
+            score -= temperature * float(-np.log(-np.log(rng.random() + 1e-300) + 1e-300))
+        heapq.heappush(heap, (score, a, b))
+
+    for x, hs in holders.items():
+        if len(hs) == 2:
+            a, b = sorted(hs)
+            push(a, b)
+    lhs, rhs = [], []
+    nxt = L
+    while len(live) > 1:
+        pair = None
+        while heap:
+            _, a, b = heapq.heappop(heap)
+            if a in live and b in live:
+                pair = (a, b)
+                break
+        if pair is None:
+            ids = sorted(live)
+            pair = (ids[0], ids[1])
+        a, b = pair
+        K = live[a] & live[b]
+        C = (live[a] | live[b]) - K
+        for x in live[a]:
+            holders[x].discard(a)
+        for x in live[b]:
+            holders[x].discard(b)
+        for x in K:
+            holders.pop(x, None)
+        del live[a], live[b]
+        live[nxt] = C
+        size[nxt] = sum(lg[x] for x in C)
+        neigh = set()
+        for x in C:
+            holders.setdefault(x, set()).add(nxt)
+            neigh |= holders[x]
+        neigh.discard(nxt)
+        for o in neigh:
+            push(min(o, nxt), max(o, nxt))
+        lhs.append(a)
+        rhs.append(b)
+        nxt += 1
+    return Tree(lhs, rhs)
+
+
+def search_tree(net: Network, trials: int, seed: int = 0, max_elems: Optional[int] = None,
+                alphas=(0.5, 1.0, 1.5), temperatures=(0.1, 0.3, 1.0)) -> Tree:
+    """Best of `trials` randomized greedy trees (seeded, deterministic), by
+    (largest intermediate, total flops).  Stops early once a tree's largest
+    intermediate is at most `max_elems` and no better width is found within
+    the next trials/4 attempts."""
+    rng = np.random.default_rng(seed)
+    best = None
+    best_key = None
+    since = 0
+    for t in range(trials):
+        a = float(alphas[int(rng.integers(len(alphas)))])
+        temp = float(temperatures[int(rng.integers(len(temperatures)))])
+        tr = random_greedy_tree(net, int(rng.integers(1 << 31)), alpha=a, temperature=temp)
+        c = tree_cost(net, tr)
+        key = (c["max_elems"], c["flops"])
+        if best_key is None or key < best_key:
+            best, best_key, since = tr, key, 0
+        else:
+            since += 1
+        if max_elems is not None and best_key[0] <= max_elems and since > trials // 4:
+            break
+    return best
