@@ -153,6 +153,10 @@ class SweepWorkload:
         _, _, m, n, k = self.plans[idx]
         return 8.0 * m * n * k
 
+    def launch_bytes(self, idx):
+        _, _, m, n, k = self.plans[idx]
+        return 8.0 * (m * k + n * k + m * n)
+
     def cpu_baseline(self, budget_s=12.0):
         """Oracle on the host: exact complex128 entries of the largest case,
         on a sub-grid of gathered rows, for about `budget_s` seconds."""
@@ -293,6 +297,9 @@ class TreeWorkload:
     def launch_flops(self, idx):
         return self.flops
 
+    def launch_bytes(self, idx):
+        return self.plan.stats()["bytes"]
+
     def cpu_baseline(self, budget_s=12.0):
         import oracle
         threads = oracle.max_threads()
@@ -328,7 +335,64 @@ class TreeWorkload:
                 "sample": f"{done} exact complex128 entries of the tree's largest step (k = {k}) in {el:.1f} s"}
 
 
-def calibrate_copy(entries=1 << 27):
+KERNEL_SRC = os.path.join(ROOT, "quantum_circuit_simulation_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+CALIB_ENTRIES = 1 << 27
+
+
+def kernel_source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"(k_cgemm\w*)<(\d+), (\d+)", name)
+    if m:
+        return f"{m.group(1)}<{m.group(2)},{m.group(3)}>"
+    m = re.search(r"::(k_\w+)\(", name)
+    return m.group(1) if m else name.split("(")[0]
+
+
+def ingest_pmc(fetch_csv, write_csv, workload, kernel, commands):
+    """Per-launch HBM bytes of `kernel` from a FETCH_SIZE run and a
+    WRITE_SIZE run (each with --calibrate-copy), scaled by what the same
+    counter read for the calibration copy (8 * CALIB_ENTRIES bytes each way).
+    Writes profiles/traffic_<workload>.json stamped with the kernel source
+    digest, so a later kernel change makes bench.py report null."""
+    import csv
+    out = {"workload": workload, "kernel": kernel, "kernels_hip_sha256": kernel_source_digest(),
+           "commands": commands}
+    known = 8 * CALIB_ENTRIES
+    for path, ctr in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == ctr]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        calib = next(float(r["Counter_Value"]) * 1024 for r in rows if "k_copy" in r["Kernel_Name"])
+        scale = known / calib
+        vals = [float(r["Counter_Value"]) * 1024 * scale for r in rows if _short_kernel(r["Kernel_Name"]) == kernel]
+        key = "fetch" if ctr == "FETCH_SIZE" else "write"
+        out[key + "_scale"] = scale
+        out[key + "_bytes_per_launch"] = sum(vals) / len(vals)
+        out[key + "_launches"] = len(vals)
+    out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    path = TRAFFIC_FILE.format(workload=workload)
+    json.dump(out, open(path, "w"), indent=1)
+    return path
+
+
+def measured_traffic(workload, kernel):
+    """Bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel") != kernel or t.get("kernels_hip_sha256") != kernel_source_digest():
+        return None
+    return t["bytes_per_launch"]
+
+
+def calibrate_copy(entries=CALIB_ENTRIES):
     """One k_copy of `entries` complex64 (a single-leaf network in its own
     order): 8*entries bytes read and 8*entries bytes written.  Under
     rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the scale of the byte
@@ -358,9 +422,18 @@ def main():
     ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB identity copy (k_copy) to scale HBM byte counters")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--ablation", action="store_true",
                     help="also time naive mode order (permute, GEMM, permute) against lifetime order")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        kernel = "k_cgemm_tile<128,128>" if args.workload == "sweep" else args.workload
+        cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.split('_')[0].lower()} -o {c.split('_')[0].lower()} -f csv "
+                f"-- python3 -u bench.py --calibrate-copy --steps 1 --warmup 0 --no-cpu-baseline"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        print(ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, kernel, cmds))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this executor contracts on a single MI355X "
               "(multi-GPU distribution is not part of it); run with --gpus 1", file=sys.stderr)
@@ -413,14 +486,18 @@ def main():
             d = evs[s][i][0].elapsed_time(evs[s][i][1])
             key = wl.kernel_of(i)
             f = wl.launch_flops(i)
-            acc = per.setdefault(key, [0.0, 0.0, 0])
+            acc = per.setdefault(key, [0.0, 0.0, 0, 0.0])
             acc[0] += f
             acc[1] += d
             acc[2] += 1
+            acc[3] += wl.launch_bytes(i)
     dom = max(per.items(), key=lambda kv: kv[1][1])
     achieved = dom[1][0] / (dom[1][1] / 1e3) / 1e12
+    traffic = measured_traffic(args.workload, dom[0])
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": None,
+                "frac": round(achieved / PEAK_FP32_MFMA, 4),
+                "traffic": round(traffic) if traffic is not None else None,
+                "alg_bytes_per_launch": round(dom[1][3] / dom[1][2]),
                 "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
     rep = {}
     if args.report:
