@@ -41,6 +41,7 @@ CLASS_GEMM = 2
 
 SKINNY_MAX_SIDE = 16        # skinny when the smaller of m, n is at most this
 GEMM_NOMINAL_TILE = 128     # nominal tile edge used only by the split-K rule
+EARLY_STAGE_MAX = 1 << 16   # staged leaves up to this many entries are copied before the first group
 NONE = (1 << 64) - 1        # "not in the arena"
 
 
@@ -393,24 +394,39 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
             node.scratch_bytes = splits * R * Sx * 8
         nodes.append(node)
 
-    # launch groups
+    # launch groups: the tiny steps between two non-tiny steps (a segment)
+    # run in dependency-level order, one group per level (split at max_group
+    # members, list order inside a level); non-tiny steps are groups of their
+    # own.  Level = 0 unless an operand was produced in the same segment, then
+    # one more than that producer's level.
     groups: List[List[int]] = []
-    open_tiny = False
-    produced_in_group = set()
+    segment: List[int] = []
+
+    def flush_segment():
+        if not segment:
+            return
+        level = {}
+        for s in segment:
+            nd = nodes[s]
+            lv = 0
+            for t in (nd.lhs, nd.rhs):
+                if t in level:
+                    lv = max(lv, level[t] + 1)
+            level[nd.out] = lv
+        depth = max(level.values()) + 1
+        for lv in range(depth):
+            members = [s for s in segment if level[nodes[s].out] == lv]
+            for i in range(0, len(members), max_group):
+                groups.append(members[i:i + max_group])
+        segment.clear()
+
     for s, nd in enumerate(nodes):
         if nd.cls == CLASS_TINY:
-            if (open_tiny and len(groups[-1]) < max_group and nd.lhs not in produced_in_group
-                    and nd.rhs not in produced_in_group):
-                groups[-1].append(s)
-            else:
-                groups.append([s])
-                open_tiny = True
-                produced_in_group = set()
-            produced_in_group.add(nd.out)
+            segment.append(s)
         else:
+            flush_segment()
             groups.append([s])
-            open_tiny = False
-            produced_in_group = set()
+    flush_segment()
     for g, members in enumerate(groups):
         for s in members:
             nodes[s].group = g
@@ -424,13 +440,28 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
     elems_of = [_prod(ext, st) for st in sets]
     root = L + S - 1
     root_off = NONE
-    live_size = {}
+    # early staging: copies of leaves with at most EARLY_STAGE_MAX entries are
+    # made in one launch before the first group, so they are allocated first
+    # (in execution order, A before B) and freed with their consumer group
+    early = set()
+    for members in groups:
+        for s in members:
+            nd = nodes[s]
+            for which, t in (("a", nd.lhs), ("b", nd.rhs)):
+                if getattr(nd, "copy_" + which) and t < L and elems_of[t] <= EARLY_STAGE_MAX:
+                    off = arena.alloc(rbytes(elems_of[t]))
+                    setattr(nd, which + "_off", off)
+                    if policy == LIFETIME:
+                        tensor_off[t] = off
+                    early.add((s, which))
     for members in groups:
         to_free = []
         for s in members:
             nd = nodes[s]
             for which, t in (("a", nd.lhs), ("b", nd.rhs)):
-                if getattr(nd, "copy_" + which):
+                if (s, which) in early:
+                    to_free.append((getattr(nd, which + "_off"), rbytes(elems_of[t])))
+                elif getattr(nd, "copy_" + which):
                     off = arena.alloc(rbytes(elems_of[t]))
                     to_free.append((off, rbytes(elems_of[t])))
                     if t < L and policy == LIFETIME:

@@ -3,6 +3,7 @@
 #include "plan.hpp"
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <list>
 #include <set>
@@ -450,27 +451,46 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   }
   if (S == 0) p->staged_leaf.assign(L, 0);
 
-  // ---- launch groups: consecutive tiny steps with no dependency inside the group
+  // ---- launch groups: the tiny steps between two non-tiny steps (a segment)
+  // run in dependency-level order, one group per level (split at max_group
+  // members, list order inside a level); non-tiny steps are groups of their
+  // own.  Level = 0 unless an operand was produced in the same segment, then
+  // one more than that producer's level.
   p->groups.clear();
-  bool open_tiny = false;
-  std::vector<int32_t> produced;
-  for (int32_t s = 0; s < S; ++s) {
-    Node &nd = p->nodes[s];
-    if (nd.cls == TNC_CLASS_TINY) {
-      if (open_tiny && (int32_t)p->groups.back().size() < o.max_group && !contains(produced, nd.lhs) &&
-          !contains(produced, nd.rhs)) {
-        p->groups.back().push_back(s);
-      } else {
-        p->groups.push_back({s});
-        open_tiny = true;
-        produced.clear();
+  {
+    std::vector<int32_t> segment;
+    std::vector<int32_t> level(T, -1);  // level of outputs produced in the open segment
+    auto flush = [&]() {
+      if (segment.empty()) return;
+      int32_t depth = 0;
+      for (int32_t s : segment) {
+        const Node &nd = p->nodes[s];
+        int32_t lv = 0;
+        for (int32_t t : {nd.lhs, nd.rhs})
+          if (level[t] >= 0) lv = std::max(lv, level[t] + 1);
+        level[nd.out] = lv;
+        depth = std::max(depth, lv + 1);
       }
-      produced.push_back(nd.out);
-    } else {
-      p->groups.push_back({s});
-      open_tiny = false;
-      produced.clear();
+      for (int32_t lv = 0; lv < depth; ++lv) {
+        std::vector<int32_t> members;
+        for (int32_t s : segment)
+          if (level[p->nodes[s].out] == lv) members.push_back(s);
+        for (size_t i = 0; i < members.size(); i += (size_t)o.max_group)
+          p->groups.emplace_back(members.begin() + i,
+                                 members.begin() + std::min(members.size(), i + (size_t)o.max_group));
+      }
+      for (int32_t s : segment) level[p->nodes[s].out] = -1;
+      segment.clear();
+    };
+    for (int32_t s = 0; s < S; ++s) {
+      if (p->nodes[s].cls == TNC_CLASS_TINY) {
+        segment.push_back(s);
+      } else {
+        flush();
+        p->groups.push_back({s});
+      }
     }
+    flush();
   }
   for (size_t g = 0; g < p->groups.size(); ++g)
     for (int32_t s : p->groups[g]) p->nodes[s].group = (int32_t)g;
@@ -481,6 +501,24 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   for (int32_t t = 0; t < T; ++t) elems[t] = prod(ext, sets[t]);
   Arena arena;
   p->tensor_off.assign(T, kNone);
+  // early staging: copies of leaves with at most kEarlyStageMax entries are
+  // made in one launch before the first group, so they are allocated first
+  // (in execution order, A before B) and freed with their consumer group
+  std::vector<std::array<char, 2>> early(S, {0, 0});
+  for (auto &members : p->groups)
+    for (int32_t s : members) {
+      Node &nd = p->nodes[s];
+      for (int w = 0; w < 2; ++w) {
+        int32_t t = w == 0 ? nd.lhs : nd.rhs;
+        int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
+        if (copy && t < L && elems[t] <= kEarlyStageMax) {
+          uint64_t &off = w == 0 ? nd.a_off : nd.b_off;
+          off = arena.alloc(rbytes(elems[t]));
+          if (!naive) p->tensor_off[t] = off;
+          early[s][w] = 1;
+        }
+      }
+    }
   for (auto &members : p->groups) {
     std::vector<std::pair<uint64_t, uint64_t>> to_free;
     for (int32_t s : members) {
@@ -489,7 +527,9 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
         int32_t t = w == 0 ? nd.lhs : nd.rhs;
         int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
         uint64_t &off = w == 0 ? nd.a_off : nd.b_off;
-        if (copy) {
+        if (early[s][w]) {
+          to_free.push_back({off, rbytes(elems[t])});
+        } else if (copy) {
           off = arena.alloc(rbytes(elems[t]));
           to_free.push_back({off, rbytes(elems[t])});
           if (t < L && !naive) p->tensor_off[t] = off;
@@ -604,20 +644,26 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   }
   std::vector<TinyDesc> tiny;
   std::vector<RunDev> runs;
+  auto emit_copy = [&](int32_t s, int w) {
+    Node &nd = p->nodes[s];
+    int32_t t = w == 0 ? nd.lhs : nd.rhs;
+    uint64_t dst = w == 0 ? nd.a_off : nd.b_off;
+    const auto &want = w == 0 ? p->gemm_a[s] : p->gemm_b[s];
+    int32_t src_buf = t < L ? kBufLeaf0 + t : kBufArena;
+    uint64_t src_off = t < L ? 0 : p->tensor_off[t];
+    p->copies.push_back(make_copy(t, src_buf, src_off, kBufArena, dst, want, 0));
+    push_copy_op((int32_t)p->copies.size() - 1);
+  };
+  for (auto &members : p->groups)
+    for (int32_t s : members)
+      for (int w = 0; w < 2; ++w)
+        if (early[s][w]) emit_copy(s, w);
   for (auto &members : p->groups) {
     // staging / re-layout copies of this group's operands
     for (int32_t s : members) {
-      Node &nd = p->nodes[s];
-      for (int w = 0; w < 2; ++w) {
-        int32_t t = w == 0 ? nd.lhs : nd.rhs;
-        if (!(w == 0 ? nd.copy_a : nd.copy_b)) continue;
-        uint64_t dst = w == 0 ? nd.a_off : nd.b_off;
-        const auto &want = w == 0 ? p->gemm_a[s] : p->gemm_b[s];
-        int32_t src_buf = t < L ? kBufLeaf0 + t : kBufArena;
-        uint64_t src_off = t < L ? 0 : p->tensor_off[t];
-        p->copies.push_back(make_copy(t, src_buf, src_off, kBufArena, dst, want, 0));
-        push_copy_op((int32_t)p->copies.size() - 1);
-      }
+      const Node &nd = p->nodes[s];
+      for (int w = 0; w < 2; ++w)
+        if ((w == 0 ? nd.copy_a : nd.copy_b) && !early[s][w]) emit_copy(s, w);
     }
     // compute
     const Node &first = p->nodes[members[0]];

@@ -22,6 +22,7 @@ constexpr int64_t kSkinnyMaxSide = 16;   // skinny when min(m, n) <= this
 constexpr int64_t kGemmNominalTile = 128;
 constexpr int64_t kCopyTileMax = 1024;     // entries per LDS tile of a tiled copy
 constexpr int64_t kCopyTiledMin = 1 << 16;  // copies at least this large use the tiled kernel
+constexpr int64_t kEarlyStageMax = 1 << 16; // staged leaves up to this size are copied before the first group
 
 struct Run {
   int64_t size;

@@ -109,19 +109,29 @@ def test_arena_buffers_live_together_do_not_overlap(seed, policy):
 
 
 @pytest.mark.parametrize("seed", range(20))
-def test_groups_have_no_internal_dependency(seed):
+def test_groups_are_a_valid_schedule(seed):
+    """Every step runs exactly once, after the steps producing its operands
+    (in an earlier group), never beside them; non-tiny steps run alone and
+    keep their list order relative to each other."""
     net, tree = _random_case(seed)
     plan = P.make_plan(net.extents, net.leaves, net.out_modes, tree.lhs, tree.rhs, tiny_mnk=1 << 10,
                        max_group=3)
-    for members in plan.groups:
-        assert len(members) <= 3
-        outs = {plan.nodes[s].out for s in members}
+    L = net.num_leaves
+    done_group = {t: -1 for t in range(L)}
+    seen = []
+    for g, members in enumerate(plan.groups):
+        assert 1 <= len(members) <= 3
         for s in members:
             nd = plan.nodes[s]
-            assert nd.lhs not in outs and nd.rhs not in outs
+            assert done_group[nd.lhs] < g and done_group[nd.rhs] < g
             if len(members) > 1:
                 assert nd.cls == P.CLASS_TINY
-        assert members == list(range(members[0], members[0] + len(members)))
+        for s in members:
+            done_group[plan.nodes[s].out] = g
+            seen.append(s)
+    assert sorted(seen) == list(range(len(tree.lhs)))
+    big = [s for s in seen if plan.nodes[s].cls != P.CLASS_TINY]
+    assert big == sorted(big)
 
 
 def test_aligned_sweep_case_needs_no_copies():
