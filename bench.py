@@ -184,6 +184,82 @@ class SweepWorkload:
                           f"2^{c['logk']}) case ({flops:.3g} flop in {el:.1f} s)"}
 
 
+class SkinnyWorkload:
+    """HBM-bound steps with one side of at most 16 (k_skinny_rows, or k_skinny
+    with split K for the dot product), all modes of extent 2, CN(0,1) data,
+    GEMM-aligned declarations.  Measured in algorithmic bytes per second."""
+    CASES = [(28, 2, 2), (24, 4, 4), (21, 3, 6), (20, 4, 8), (0, 0, 30)]   # log2 of m, n, k
+
+    def __init__(self):
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import sweep
+        self.plans = []
+        maxa = maxb = maxc = maxws = 0
+        for a, b, c in self.CASES:
+            net, tree = sweep.network(a, b, c)
+            plan = qa.Plan.from_network(net, tree)
+            m, n, k = 1 << a, 1 << b, 1 << c
+            self.plans.append(((a, b, c), plan, m, n, k))
+            maxa, maxb, maxc = max(maxa, m * k), max(maxb, n * k), max(maxc, m * n)
+            maxws = max(maxws, plan.workspace_bytes)
+        self.A = torch.empty(maxa, dtype=torch.complex64, device="cuda")
+        self.B = torch.empty(maxb, dtype=torch.complex64, device="cuda")
+        self.C = torch.empty(maxc, dtype=torch.complex64, device="cuda")
+        fill_gaussian(self.A, 300)
+        fill_gaussian(self.B, 301)
+        self.ws = torch.empty(max(256, maxws), dtype=torch.uint8, device="cuda")
+        self.flops = sum(8.0 * m * n * k for _, _, m, n, k in self.plans)
+        self.bytes = sum(8.0 * (m * k + n * k + m * n) for _, _, m, n, k in self.plans)
+        self.config = {"workload": "skinny-steps", "cases_log2_mnk": [list(c) for c in self.CASES],
+                       "bytes_per_step": self.bytes, "flop_per_step": self.flops}
+
+    def step(self, events=None):
+        for idx, (c, plan, m, n, k) in enumerate(self.plans):
+            if events is not None:
+                events[idx][0].record()
+            plan.execute([self.A[: m * k], self.B[: n * k]], self.C[: m * n], self.ws)
+            if events is not None:
+                events[idx][1].record()
+
+    def kernel_of(self, idx):
+        c, plan, m, n, k = self.plans[idx]
+        if max(m, n) < 4096:
+            return "k_skinny"
+        return "k_skinny_small" if 8 <= k <= 16 and plan.node(0)["splits"] == 1 else "k_skinny_rows"
+
+    def launch_flops(self, idx):
+        _, _, m, n, k = self.plans[idx]
+        return 8.0 * m * n * k
+
+    def launch_bytes(self, idx):
+        _, _, m, n, k = self.plans[idx]
+        return 8.0 * (m * k + n * k + m * n)
+
+    def cpu_baseline(self, budget_s=12.0):
+        import oracle
+        (a, b, c), plan, m, n, k = self.plans[0]
+        rng = np.random.default_rng(9)
+        rows = np.sort(rng.choice(m, size=1 << 16, replace=False))
+        A = self.A[: m * k].view(m, k)[torch_index(rows)].cpu().numpy()
+        B = self.B[: n * k].view(n, k).cpu().numpy()
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < budget_s:
+            oracle.pair_block(A, B, threads=threads)
+            done += A.shape[0]
+        el = time.perf_counter() - t0
+        by = done * 8.0 * (k + n)
+        return {"value": by / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} rows of the (2^{a},2^{b},2^{c}) step, exact complex128 ({el:.1f} s)"}
+
+
+def torch_index(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.int64)).cuda()
+
+
 class TreeWorkload:
     def __init__(self, which):
         import torch
@@ -414,7 +490,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "peps", "brickwork12", "brickwork30", "grid"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid"])
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -451,6 +527,9 @@ def main():
             allc = sweep.cases()
             cases = [allc[int(i)] for i in args.cases.split(",")]
         wl = SweepWorkload(cases)
+        nlaunch = len(wl.plans)
+    elif args.workload == "skinny":
+        wl = SkinnyWorkload()
         nlaunch = len(wl.plans)
     else:
         wl = TreeWorkload(args.workload)
@@ -494,7 +573,15 @@ def main():
     dom = max(per.items(), key=lambda kv: kv[1][1])
     achieved = dom[1][0] / (dom[1][1] / 1e3) / 1e12
     traffic = measured_traffic(args.workload, dom[0])
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
+    if args.workload == "skinny":
+        # HBM-bound steps: algorithmic bytes / time against the HBM peak
+        ach_bw = dom[1][3] / (dom[1][1] / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach_bw, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                    "frac": round(ach_bw / PEAK_HBM, 4), "traffic": round(traffic) if traffic is not None else None,
+                    "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
+    else:
+        roofline = None
+    roofline = roofline or {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP32_MFMA, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "alg_bytes_per_launch": round(dom[1][3] / dom[1][2]),
@@ -503,6 +590,11 @@ def main():
     if args.report:
         rep = {"per_kernel": {k: {"flop": v[0], "ms": v[1], "launches": v[2]} for k, v in per.items()},
                "cases": []}
+        if args.workload == "skinny":
+            for i, (c, plan, m, n, k) in enumerate(wl.plans):
+                ms = np.median([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])
+                rep["cases"].append({"log2_mnk": list(c), "kernel": wl.kernel_of(i), "ms": float(ms),
+                                     "GB/s": wl.launch_bytes(i) / (ms / 1e3) / 1e9, "splits": plan.node(0)["splits"]})
         if args.workload == "sweep":
             for i, (c, plan, m, n, k) in enumerate(wl.plans):
                 ms = np.median([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])

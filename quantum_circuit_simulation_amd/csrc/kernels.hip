@@ -217,55 +217,82 @@ __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void 
 
 constexpr int kSkinnyMax = 16;
 
-__global__ __launch_bounds__(256) void k_skinny(StepArgs a, int64_t kchunk, int G) {
-  __shared__ int64_t coloff[kSkinnyMax];
-  if (threadIdx.x < a.S) coloff[threadIdx.x] = run_offset(threadIdx.x, a.runs + a.nrr, a.ncr);
-  __syncthreads();
-  const int rows_per_block = 256 / G;
-  const int lane = threadIdx.x % G;
-  const int64_t i = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / G;
+__device__ __forceinline__ float2 ld_pair_lo(const float4 &v) { return make_float2(v.x, v.y); }
+__device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+__device__ __forceinline__ float2 ld_pair_hi(const float4 &v) { return make_float2(v.z, v.w); }
+
+// Few rows (R < 4096): one workgroup per (row, K chunk); all 256 threads
+// stride over the chunk with 16-byte loads (two entries), accumulate the
+// row's S outputs, and reduce through shuffles and LDS.
+__global__ __launch_bounds__(256) void k_skinny(StepArgs a, int64_t kchunk) {
+  __shared__ float2 red[4][kSkinnyMax];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i = blockIdx.x;
   const int split = blockIdx.y;
   const int64_t k0 = (int64_t)split * kchunk;
   const int64_t k1 = min(a.K, k0 + kchunk);
   const int S = (int)a.S;
   float2 acc[kSkinnyMax];
 #pragma unroll
-  for (int s = 0; s < kSkinnyMax; ++s) acc[s] = make_float2(0.f, 0.f);
-  if (i < a.R) {
-    const float2 *xr = a.X + i * a.K;
-    for (int64_t l = k0 + lane; l < k1; l += G) {
+  for (int q = 0; q < kSkinnyMax; ++q) acc[q] = make_float2(0.f, 0.f);
+  const float2 *xr = a.X + i * a.K;
+  // 16-byte loads need 16-byte aligned row starts; otherwise 8-byte ones
+  const bool pairs = aligned16(xr + k0) && aligned16(a.Y + k0) && (a.K % 2 == 0);
+  if (pairs) {
+    const int64_t np = (k1 - k0) / 2;
+    const float4 *x4 = (const float4 *)(xr + k0);
+    for (int64_t p = tid; p < np; p += 256) {
+      const float4 xv = x4[p];
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) {
+          const float4 yv = ((const float4 *)(a.Y + (int64_t)q * a.K + k0))[p];
+          cmac(acc[q], ld_pair_lo(xv), ld_pair_lo(yv));
+          cmac(acc[q], ld_pair_hi(xv), ld_pair_hi(yv));
+        }
+    }
+    if ((k1 - k0) % 2 == 1 && tid == 0) {
+      const int64_t l = k1 - 1;
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) cmac(acc[q], xr[l], a.Y[(int64_t)q * a.K + l]);
+    }
+  } else {
+    for (int64_t l = k0 + tid; l < k1; l += 256) {
       const float2 x = xr[l];
 #pragma unroll
-      for (int s = 0; s < kSkinnyMax; ++s)
-        if (s < S) cmac(acc[s], x, a.Y[(int64_t)s * a.K + l]);
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) cmac(acc[q], x, a.Y[(int64_t)q * a.K + l]);
     }
   }
 #pragma unroll
-  for (int s = 0; s < kSkinnyMax; ++s) {
-    for (int w = 1; w < G; w *= 2) {
-      acc[s].x += __shfl_xor(acc[s].x, w, 64);
-      acc[s].y += __shfl_xor(acc[s].y, w, 64);
+  for (int q = 0; q < kSkinnyMax; ++q) {
+    for (int w = 1; w < 64; w *= 2) {
+      acc[q].x += __shfl_xor(acc[q].x, w, 64);
+      acc[q].y += __shfl_xor(acc[q].y, w, 64);
     }
+    if (lane == 0 && q < S) red[wave][q] = acc[q];
   }
-  if (i < a.R && lane == 0) {
-    if (a.splits > 1) {
-      float2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
-#pragma unroll
-      for (int s = 0; s < kSkinnyMax; ++s)
-        if (s < S) p[s] = acc[s];
-    } else {
-      const int64_t ro = run_offset(i, a.runs, a.nrr);
-#pragma unroll
-      for (int s = 0; s < kSkinnyMax; ++s)
-        if (s < S) store_c(a.C + ro + coloff[s], acc[s], a.beta);
+  __syncthreads();
+  if (tid < S) {
+    float2 v = red[0][tid];
+    for (int w = 1; w < 4; ++w) {
+      v.x += red[w][tid].x;
+      v.y += red[w][tid].y;
     }
+    if (a.splits > 1) a.scratch[((int64_t)split * a.R + i) * a.S + tid] = v;
+    else store_c(a.C + run_offset(i, a.runs, a.nrr) + run_offset(tid, a.runs + a.nrr, a.ncr), v, a.beta);
   }
 }
 
-// Skinny steps with many rows: one row per thread.  Each K chunk of the
-// workgroup's 256 rows is loaded into LDS with coalesced reads (a row's chunk
-// is contiguous), the small operand's chunk sits in LDS and is read by
-// broadcast, and every thread accumulates its row's S outputs in registers.
+// Many rows: workgroups walk tiles of 256 rows (grid-stride), one row per
+// thread.  Each K chunk of a tile goes into LDS (row stride 17 entries,
+// conflict-free); when the chunk is the whole K, the tile's rows are one
+// contiguous block read with 16-byte loads and the small operand is loaded
+// once per workgroup.  The small operand is read from LDS by broadcast and
+// each thread keeps its row's <= 16 outputs in registers.  A row-major C
+// (one run per side, unit column stride) is written through LDS with
+// 16-byte stores; other layouts go through the runs per entry.
 constexpr int kRowsKC = 16;
 
 __global__ __launch_bounds__(256) void k_skinny_rows(StepArgs a, int64_t kchunk) {
@@ -274,45 +301,181 @@ __global__ __launch_bounds__(256) void k_skinny_rows(StepArgs a, int64_t kchunk)
   __shared__ int64_t coloff[kSkinnyMax];
   const int tid = threadIdx.x;
   const int S = (int)a.S;
-  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
-  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int64_t K = a.K;
   const int split = blockIdx.y;
   const int64_t k0 = (int64_t)split * kchunk;
-  const int64_t k1 = min(a.K, k0 + kchunk);
-  float2 acc[kSkinnyMax];
+  const int64_t k1 = min(K, k0 + kchunk);
+  const bool whole = (k0 == 0 && k1 == K && K <= kRowsKC);
+  const bool rowmajor = a.splits == 1 && a.nrr == 1 && a.ncr == 1 && a.runs[1].stride == 1 &&
+                        a.runs[0].stride == a.S;
+  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  if (whole && tid < kSkinnyMax * kRowsKC) {
+    const int sr = tid / kRowsKC, col = tid % kRowsKC;
+    ys[sr][col] = (sr < S && col < K) ? a.Y[(int64_t)sr * K + col] : make_float2(0.f, 0.f);
+  }
+  const int64_t ntiles = (a.R + 255) / 256;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t r0 = tile * 256;
+    const int rows = (int)min((int64_t)256, a.R - r0);
+    float2 acc[kSkinnyMax];
 #pragma unroll
-  for (int q = 0; q < kSkinnyMax; ++q) acc[q] = make_float2(0.f, 0.f);
-  for (int64_t kc = k0; kc < k1; kc += kRowsKC) {
-    const int w = (int)min((int64_t)kRowsKC, k1 - kc);
-    __syncthreads();
-    // X chunk: 256 rows x w entries; thread t loads entry (row t / 16 + 16 p, col t % 16)
+    for (int q = 0; q < kSkinnyMax; ++q) acc[q] = make_float2(0.f, 0.f);
+    for (int64_t kc = k0; kc < k1; kc += kRowsKC) {
+      const int w = (int)min((int64_t)kRowsKC, k1 - kc);
+      __syncthreads();
+      if (whole) {
+        // rows r0 .. r0+rows-1 of X are one contiguous block of rows*K entries
+        const int64_t n = (int64_t)rows * K;
+        const float2 *src = a.X + r0 * K;
+        if (aligned16(src)) {
+          const float4 *src4 = (const float4 *)src;
+          for (int64_t p = tid; p < n / 2; p += 256) {
+            const float4 v = src4[p];
+            const int e = (int)(2 * p);
+            xs[e / K][e % K] = ld_pair_lo(v);
+            xs[(e + 1) / K][(e + 1) % K] = ld_pair_hi(v);
+          }
+          if ((n % 2) == 1 && tid == 0) xs[(n - 1) / K][(n - 1) % K] = src[n - 1];
+        } else {
+          for (int64_t e = tid; e < n; e += 256) xs[e / K][e % K] = src[e];
+        }
+      } else {
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int row = tid / kRowsKC + 16 * p, col = tid % kRowsKC;
-      const int64_t gi = r0 + row;
-      xs[row][col] = (gi < a.R && col < w) ? a.X[gi * a.K + kc + col] : make_float2(0.f, 0.f);
+        for (int p = 0; p < 16; ++p) {
+          const int row = tid / kRowsKC + 16 * p, col = tid % kRowsKC;
+          xs[row][col] = (row < rows && col < w) ? a.X[(r0 + row) * K + kc + col] : make_float2(0.f, 0.f);
+        }
+        if (tid < kSkinnyMax * kRowsKC) {
+          const int sr = tid / kRowsKC, col = tid % kRowsKC;
+          ys[sr][col] = (sr < S && col < w) ? a.Y[(int64_t)sr * K + kc + col] : make_float2(0.f, 0.f);
+        }
+      }
+      __syncthreads();
+      if (tid < rows) {
+        for (int l = 0; l < w; ++l) {
+          const float2 x = xs[tid][l];
+#pragma unroll
+          for (int q = 0; q < kSkinnyMax; ++q)
+            if (q < S) cmac(acc[q], x, ys[q][l]);
+        }
+      }
     }
-    if (tid < kSkinnyMax * kRowsKC) {
-      const int sr = tid / kRowsKC, col = tid % kRowsKC;
-      ys[sr][col] = (sr < S && col < w) ? a.Y[(int64_t)sr * a.K + kc + col] : make_float2(0.f, 0.f);
-    }
-    __syncthreads();
-    for (int l = 0; l < w; ++l) {
-      const float2 x = xs[tid][l];
+    const int64_t i = r0 + tid;
+    if (a.splits > 1) {
+      if (tid < rows) {
+        float2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
+#pragma unroll
+        for (int q = 0; q < kSkinnyMax; ++q)
+          if (q < S) p[q] = acc[q];
+      }
+    } else if (rowmajor) {
+      // the tile's outputs are rows*S contiguous entries: stage them in LDS
+      // (xs holds 256 x 17 entries >= 256 x 16) and store 16 bytes per lane
+      __syncthreads();
+      float2 *stage = &xs[0][0];
 #pragma unroll
       for (int q = 0; q < kSkinnyMax; ++q)
-        if (q < S) cmac(acc[q], x, ys[q][l]);
+        if (q < S && tid < rows) stage[tid * S + q] = acc[q];
+      __syncthreads();
+      const int64_t n = (int64_t)rows * S;
+      float2 *dst = a.C + a.runs[0].stride * r0;
+      if (aligned16(dst)) {
+        for (int64_t p = tid; p < n / 2; p += 256) {
+          float2 lo = stage[2 * p], hi = stage[2 * p + 1];
+          if (a.beta) {
+            const float4 o = ((const float4 *)dst)[p];
+            lo.x += o.x; lo.y += o.y; hi.x += o.z; hi.y += o.w;
+          }
+          ((float4 *)dst)[p] = make_float4(lo.x, lo.y, hi.x, hi.y);
+        }
+        if ((n % 2) == 1 && tid == 0) store_c(dst + n - 1, stage[n - 1], a.beta);
+      } else {
+        for (int64_t e = tid; e < n; e += 256) store_c(dst + e, stage[e], a.beta);
+      }
+    } else if (tid < rows) {
+      const int64_t ro = run_offset(i, a.runs, a.nrr);
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) store_c(a.C + ro + coloff[q], acc[q], a.beta);
     }
   }
-  const int64_t i = r0 + tid;
-  if (i < a.R) {
-    if (a.splits > 1) {
-      float2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
+}
+
+// Many rows, whole K <= 16, no split: no LDS staging of X at all.  Each
+// thread streams ROWS rows (row r of the step is row
+// (blockIdx.x * ROWS + u) * 256 + tid, so every u is a coalesced group of
+// 256 rows) with 16-byte loads where aligned, keeps every output in
+// registers, and reads the small operand from LDS by broadcast.  No barrier
+// inside the loop, so many waves keep loads in flight.
+template <int ROWS>
+__global__ __launch_bounds__(256) void k_skinny_small(StepArgs a) {
+  static_assert(ROWS >= 1 && ROWS <= 2, "rows per thread");
+  __shared__ float2 ys[kSkinnyMax][kRowsKC];
+  __shared__ int64_t coloff[kSkinnyMax];
+  const int tid = threadIdx.x;
+  const int K = (int)a.K, S = (int)a.S;
+  if (tid < kSkinnyMax * kRowsKC) {
+    const int sr = tid / kRowsKC, col = tid % kRowsKC;
+    ys[sr][col] = (sr < S && col < K) ? a.Y[(int64_t)sr * K + col] : make_float2(0.f, 0.f);
+  }
+  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  __syncthreads();
+  const bool rowmajor = a.nrr == 1 && a.ncr == 1 && a.runs[1].stride == 1 && a.runs[0].stride == a.S;
+  float2 x[ROWS][kRowsKC];
+  int64_t row[ROWS];
 #pragma unroll
-      for (int q = 0; q < kSkinnyMax; ++q)
-        if (q < S) p[q] = acc[q];
+  for (int u = 0; u < ROWS; ++u) {
+    row[u] = ((int64_t)blockIdx.x * ROWS + u) * 256 + tid;
+    const float2 *src = a.X + row[u] * K;
+    if (row[u] < a.R) {
+      if ((K % 2) == 0 && aligned16(src)) {
+#pragma unroll
+        for (int l = 0; l < kRowsKC; l += 2)
+          if (l < K) {
+            const float4 v = *(const float4 *)(src + l);
+            x[u][l] = ld_pair_lo(v);
+            x[u][l + 1] = ld_pair_hi(v);
+          }
+      } else {
+#pragma unroll
+        for (int l = 0; l < kRowsKC; ++l)
+          if (l < K) x[u][l] = src[l];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < ROWS; ++u) {
+    if (row[u] >= a.R) continue;
+    float2 acc[kSkinnyMax];
+#pragma unroll
+    for (int q = 0; q < kSkinnyMax; ++q) {
+      acc[q] = make_float2(0.f, 0.f);
+      if (q < S) {
+#pragma unroll
+        for (int l = 0; l < kRowsKC; ++l)
+          if (l < K) cmac(acc[q], x[u][l], ys[q][l]);
+      }
+    }
+    if (rowmajor) {
+      float2 *dst = a.C + row[u] * a.S;
+      if ((S % 2) == 0 && aligned16(dst)) {
+#pragma unroll
+        for (int q = 0; q < kSkinnyMax; q += 2)
+          if (q < S) {
+            float2 lo = acc[q], hi = acc[q + 1];
+            if (a.beta) {
+              const float4 o = *(const float4 *)(dst + q);
+              lo.x += o.x; lo.y += o.y; hi.x += o.z; hi.y += o.w;
+            }
+            *(float4 *)(dst + q) = make_float4(lo.x, lo.y, hi.x, hi.y);
+          }
+      } else {
+#pragma unroll
+        for (int q = 0; q < kSkinnyMax; ++q)
+          if (q < S) store_c(dst + q, acc[q], a.beta);
+      }
     } else {
-      const int64_t ro = run_offset(i, a.runs, a.nrr);
+      const int64_t ro = run_offset(row[u], a.runs, a.nrr);
 #pragma unroll
       for (int q = 0; q < kSkinnyMax; ++q)
         if (q < S) store_c(a.C + ro + coloff[q], acc[q], a.beta);
@@ -809,20 +972,28 @@ hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
-  if (a.R >= 4096) {
-    // many rows: one row per thread, operand chunks staged through LDS
-    dim3 grid((unsigned)((a.R + 255) / 256), (unsigned)a.splits);
-    hipLaunchKernelGGL(k_skinny_rows, grid, dim3(256), 0, stream, a, kchunk);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.splits <= 1) return e;
-    return run_split_reduce(a, stream);
+  // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
+  // straight into registers; shorter rows are read as one contiguous block
+  // per 256 rows through LDS (grid-stride); chunked K one tile per workgroup
+  if (a.R >= 4096 && a.splits == 1 && a.K >= 8 && a.K <= kRowsKC) {
+    const int rows = a.K <= 8 ? 2 : 1;
+    const int64_t blocks = (a.R + 256 * rows - 1) / (256 * rows);
+    if (rows == 2) hipLaunchKernelGGL(k_skinny_small<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(k_skinny_small<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  } else if (a.R >= 4096 && a.splits == 1 && a.K < 8) {
+    const int64_t tiles = (a.R + 255) / 256;
+    int64_t g = 8 * (int64_t)num_cus();
+    if (g > tiles) g = tiles;
+    hipLaunchKernelGGL(k_skinny_rows, dim3((unsigned)g, 1), dim3(256), 0, stream, a, kchunk);
+    return hipGetLastError();
+  } else if (a.R >= 4096) {
+    // many rows, K in chunks: one tile of 256 rows per workgroup
+    const int64_t tiles = (a.R + 255) / 256;
+    hipLaunchKernelGGL(k_skinny_rows, dim3((unsigned)tiles, (unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
+  } else {
+    hipLaunchKernelGGL(k_skinny, dim3((unsigned)a.R, (unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
   }
-  int G = pow2_floor_i(kchunk / 8);
-  if (G > 64) G = 64;
-  if (G < 1) G = 1;
-  const int rows_per_block = 256 / G;
-  dim3 grid((unsigned)((a.R + rows_per_block - 1) / rows_per_block), (unsigned)a.splits);
-  hipLaunchKernelGGL(k_skinny, grid, dim3(256), 0, stream, a, kchunk, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   return run_split_reduce(a, stream);

@@ -203,3 +203,57 @@ def test_large_permuted_pairs(seed, order):
     ref = oracle.contract_network(net, tree)
     got, plan = _gpu_run(net, tree, order=order)
     _assert_close(got, ref)
+
+
+# skinny steps: (mode counts of M, N, K, extent) chosen to hit the row-tile
+# kernel with whole-K blocks (odd and non-power-of-two K included), chunked K,
+# interleaved outputs, and the few-row kernel with split K
+SKINNY_CASES = [(13, 2, 2, 2), (8, 1, 1, 3), (9, 1, 2, 3), (12, 4, 4, 2), (12, 3, 5, 2), (6, 2, 3, 5),
+                (0, 0, 17, 2), (2, 1, 12, 3), (1, 1, 15, 2)]
+
+
+@pytest.mark.parametrize("case", SKINNY_CASES)
+@pytest.mark.parametrize("permuted", [False, True])
+def test_skinny_shapes(case, permuted):
+    R, S, K, ext = case
+    net, tree = _pair(R, S, K, seed=sum(case) + 3 * permuted, ext=ext, permuted=permuted)
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree)
+    _assert_close(got, ref)
+
+
+@pytest.mark.parametrize("ext_sliced", [2, 3])
+def test_sliced_skinny_step_accumulates(ext_sliced):
+    """A pairwise step whose shared modes include a sliced one: every slice's
+    product is added into `out` (beta = 1 after the first)."""
+    rng = np.random.default_rng(41)
+    M, N, K = list(range(13)), [13, 14], [15, 16]
+    x = 17
+    extents = np.array([2] * 17 + [ext_sliced], dtype=np.int64)
+    A, B = M + K + [x], N + [x] + K
+    data = [sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in A)),
+            sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in B))]
+    net = Network(extents, [A, B], M + N, data, name="sliced-skinny")
+    tree = Tree([0], [1])
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, sliced=[x])
+    assert plan.stats()["num_slices"] == ext_sliced
+    _assert_close(got, ref)
+
+
+def test_skinny_on_misaligned_views():
+    """Leaves handed over as views starting at an odd entry (8-byte, not
+    16-byte aligned): the 16-byte load paths must fall back."""
+    import torch
+    from tests.gpu_util import run
+    rng = np.random.default_rng(8)
+    for (R, S, K) in [(13, 2, 2), (0, 0, 14)]:
+        net, tree = _pair(R, S, K, seed=5, ext=2)
+        dev = []
+        for d in net.data:
+            buf = torch.zeros(d.size + 1, dtype=torch.complex64, device="cuda")
+            buf[1:] = torch.from_numpy(d.reshape(-1)).cuda()
+            dev.append(buf[1:])
+        ref = oracle.contract_network(net, tree)
+        got, _ = run(net, tree, leaves_dev=dev)
+        _assert_close(got, ref)
