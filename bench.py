@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense FP32 matrix
+PEAK_FP64_MFMA = 78.6    # TFLOP/s, MI355X dense FP64 matrix
 PEAK_HBM = 8000.0        # GB/s
 
 
@@ -32,7 +33,8 @@ def log(*a):
 
 
 def fill_gaussian(t, seed):
-    """CN(0,1) complex64 in place, chunked, from a seeded device generator."""
+    """CN(0,1) entries of t's complex dtype in place, chunked, from a seeded
+    device generator."""
     import torch
     g = torch.Generator(device=t.device)
     g.manual_seed(seed)
@@ -40,7 +42,7 @@ def fill_gaussian(t, seed):
     chunk = 1 << 28
     for s in range(0, flat.numel(), chunk):
         e = min(flat.numel(), s + chunk)
-        flat[s:e] = torch.randn(e - s, dtype=torch.complex64, device=t.device, generator=g)
+        flat[s:e] = torch.randn(e - s, dtype=t.dtype, device=t.device, generator=g)
 
 
 def gemm_kernel_name(R, S, K, splits):
@@ -65,31 +67,35 @@ def gemm_kernel_name(R, S, K, splits):
 class SweepWorkload:
     name = "pairwise sweep m,n,k in {2^6,2^10,2^14,2^18}, k<=2^14, 45 feasible cases, aligned"
 
-    def __init__(self, cases=None):
+    def __init__(self, cases=None, z=False):
         import torch
         import quantum_circuit_simulation_amd as qa
         from workloads import sweep
+        self.z = z
+        cdt = torch.complex128 if z else torch.complex64
+        self.eb = 16 if z else 8
         self.cases = [c for c in sweep.cases() if c["feasible"]] if cases is None else cases
         self.plans = []
         maxa = maxb = maxc = maxws = 0
         for c in self.cases:
             m, n, k = 1 << c["logm"], 1 << c["logn"], 1 << c["logk"]
             net, tree = sweep.network(c["logm"], c["logn"], c["logk"])
-            plan = qa.Plan.from_network(net, tree)
+            plan = qa.Plan.from_network(net, tree, dtype=qa.TNC_C128 if z else qa.TNC_C64)
             self.plans.append((c, plan, m, n, k))
             maxa, maxb, maxc = max(maxa, m * k), max(maxb, n * k), max(maxc, m * n)
             maxws = max(maxws, plan.workspace_bytes)
         dev = "cuda"
-        self.A = torch.empty(maxa, dtype=torch.complex64, device=dev)
-        self.B = torch.empty(maxb, dtype=torch.complex64, device=dev)
-        self.C = torch.empty(maxc, dtype=torch.complex64, device=dev)
+        self.A = torch.empty(maxa, dtype=cdt, device=dev)
+        self.B = torch.empty(maxb, dtype=cdt, device=dev)
+        self.C = torch.empty(maxc, dtype=cdt, device=dev)
         fill_gaussian(self.A, 200)
         fill_gaussian(self.B, 201)
         self.ws = torch.empty(max(256, maxws), dtype=torch.uint8, device=dev)
         self.flops = sum(8.0 * m * n * k for _, _, m, n, k in self.plans)
         self.config = {"workload": "pairwise-sweep", "cases": len(self.plans),
                        "m_n_k": "each in {2^6,2^10,2^14,2^18}, k<=2^14, m=n=2^18 excluded",
-                       "layout": "GEMM-aligned (lifetime order)", "flop_per_step": self.flops}
+                       "layout": "GEMM-aligned (lifetime order)", "flop_per_step": self.flops,
+                       "entries": "complex128" if z else "complex64"}
 
     def step(self, events=None):
         for idx, (c, plan, m, n, k) in enumerate(self.plans):
@@ -146,6 +152,8 @@ class SweepWorkload:
     def kernel_of(self, idx):
         c, plan, m, n, k = self.plans[idx]
         nd = plan.node(0)
+        if self.z:
+            return "k_zgemm" if nd["kernel_class"] == 2 else "k_skinny_z"
         R, S = (n, m) if nd["swap"] else (m, n)
         return gemm_kernel_name(R, S, k, nd["splits"])
 
@@ -155,18 +163,19 @@ class SweepWorkload:
 
     def launch_bytes(self, idx):
         _, _, m, n, k = self.plans[idx]
-        return 8.0 * (m * k + n * k + m * n)
+        return float(self.eb) * (m * k + n * k + m * n)
 
     def cpu_baseline(self, budget_s=12.0):
         """Oracle on the host: exact complex128 entries of the largest case,
         on a sub-grid of gathered rows, for about `budget_s` seconds."""
+        import torch
         import oracle
         c, plan, m, n, k = max(self.plans, key=lambda p: p[2] * p[3] * p[4])
         rng = np.random.default_rng(7)
         rows = np.sort(rng.choice(m, size=64, replace=False))
         cols = np.sort(rng.choice(n, size=64, replace=False))
-        a = self.A[: m * k].view(m, k)[rows].cpu().numpy()
-        b = self.B[: n * k].view(n, k)[cols].cpu().numpy()
+        a = self.A[: m * k].view(m, k)[rows].to(torch.complex64).cpu().numpy()
+        b = self.B[: n * k].view(n, k)[cols].to(torch.complex64).cpu().numpy()
         threads = oracle.max_threads()
         t0 = time.perf_counter()
         done = 0
@@ -234,7 +243,7 @@ class SkinnyWorkload:
 
     def launch_bytes(self, idx):
         _, _, m, n, k = self.plans[idx]
-        return 8.0 * (m * k + n * k + m * n)
+        return float(self.eb) * (m * k + n * k + m * n)
 
     def cpu_baseline(self, budget_s=12.0):
         import oracle
@@ -493,6 +502,8 @@ def main():
     ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid"])
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
+    ap.add_argument("--dtype", default="c64", choices=["c64", "c128"],
+                    help="sweep workload: entry type (c128 runs the FP64 matrix-core path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cases", default="", help="comma-separated sweep case indices (default: all feasible)")
     ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
@@ -526,7 +537,7 @@ def main():
             from workloads import sweep
             allc = sweep.cases()
             cases = [allc[int(i)] for i in args.cases.split(",")]
-        wl = SweepWorkload(cases)
+        wl = SweepWorkload(cases, z=args.dtype == "c128")
         nlaunch = len(wl.plans)
     elif args.workload == "skinny":
         wl = SkinnyWorkload()
@@ -581,8 +592,10 @@ def main():
                     "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
     else:
         roofline = None
-    roofline = roofline or {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_MFMA, 4),
+    z = getattr(wl, "z", False)
+    peak = PEAK_FP64_MFMA if z else PEAK_FP32_MFMA
+    roofline = roofline or {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "alg_bytes_per_launch": round(dom[1][3] / dom[1][2]),
                 "kernel": dom[0], "launches": dom[1][2], "avg_launch_ms": round(dom[1][1] / dom[1][2], 4)}
@@ -621,8 +634,9 @@ def main():
     line = {"metric": "contraction-tree TFLOP/s (complex64) + % FP32 MFMA peak; wall time per result",
             "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2),
+            "vs_baseline": None, "dtype": "f64" if z else "f32", "data": "synthetic",
+            **({"pct_fp64_mfma_peak": round(100.0 * value / PEAK_FP64_MFMA, 2)} if z else
+               {"pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2)}),
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
             **({"ablation": ablation} if ablation is not None else {}),

@@ -22,7 +22,9 @@
  *
  * Conventions common to all calls:
  *   - Tensors are dense, row-major in their mode order (first mode slowest),
- *     complex64 entries stored as interleaved (float re, float im).
+ *     complex64 entries stored as interleaved (float re, float im), or, for a
+ *     network declared TNC_C128, complex128 entries as interleaved
+ *     (double re, double im).  All buffers of one plan share its dtype.
  *   - Mode labels are 0 .. num_modes-1.  Every mode appears in exactly two
  *     tensors counting the output: two leaves (closed mode, summed) or one
  *     leaf and the output (open mode).
@@ -48,13 +50,16 @@ typedef enum {
   TNC_ERR_INVALID_TREE = 3,       /* steps != leaves - 1, operand id out of range or reused */
   TNC_ERR_UNSUPPORTED = 4,        /* mode in more than two tensors (hyperedge / batch mode),
                                      a mode repeated inside one leaf, rank > 64,
-                                     complex128 data, a size that overflows 64 bits,
+                                     a size that overflows 64 bits,
                                      a GEMM-class step with m, n or k >= 2^31 */
   TNC_ERR_OUT_OF_MEMORY = 5,      /* planned workspace exceeds options.capacity_bytes */
   TNC_ERR_WORKSPACE_TOO_SMALL = 6,/* tnc_execute got less workspace than planned */
   TNC_ERR_HIP = 7                 /* a HIP runtime call or kernel launch failed */
 } tnc_status;
 
+/* Entry type of every buffer of a plan.  C64 steps run on FP32 matrix cores
+ * (FP32 accumulation, the precision the page's own kernels use); C128 steps
+ * run on FP64 matrix cores for callers that need double precision. */
 typedef enum { TNC_C64 = 0, TNC_C128 = 1 } tnc_dtype;
 
 /* Mode-order policy.  LIFETIME: the page's reverse-tree ordering (section
@@ -78,7 +83,7 @@ typedef struct {
   const int32_t *leaf_modes;  /* concatenated mode lists, each in its buffer's row-major order */
   int32_t out_rank;
   const int32_t *out_modes;   /* [out_rank]: the result's mode order */
-  tnc_dtype dtype;            /* TNC_C64 */
+  tnc_dtype dtype;            /* TNC_C64 or TNC_C128 */
 } tnc_network;
 
 /* The tree, in SSA form: leaves are ids 0 .. L-1, step s creates id L + s
@@ -169,7 +174,8 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
 /*
  * Run the plan.
  *   leaves[L]   device pointers to the leaf buffers (declared orders)
- *   out         device pointer, prod(out extents) complex64 entries, overwritten
+ *   out         device pointer, prod(out extents) entries of the plan's dtype,
+ *               overwritten
  *   workspace   device pointer, >= tnc_plan_workspace_bytes, 256-byte aligned
  *   stream      hipStream_t to enqueue on (NULL = the default stream)
  * Asynchronous: returns once the work is enqueued; no host synchronisation,

@@ -45,7 +45,7 @@ def _load():
     lib.oracle_contract.argtypes = [
         ctypes.c_int32, P(ctypes.c_int64),
         ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32),
-        P(ctypes.c_void_p),
+        P(ctypes.c_void_p), ctypes.c_int32,
         ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32),
         ctypes.c_int32, P(ctypes.c_int32),
         ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int64),
@@ -81,12 +81,15 @@ def _ptr(a, ct):
 def contract(extents, leaves, out_modes, data, lhs, rhs, fixed: Optional[dict] = None,
              threads: Optional[int] = None) -> np.ndarray:
     """Evaluate the network along the tree; returns complex128 with the shape
-    of ``out_modes`` (a 0-d array for a scalar)."""
+    of ``out_modes`` (a 0-d array for a scalar).  Leaf data are read as
+    complex128 when every leaf is complex128, else as complex64."""
     lib = _load()
     ext = _i64(extents)
     rank = _i32([len(l) for l in leaves])
     modes = _i32([x for l in leaves for x in l]) if rank.sum() else np.zeros(1, np.int32)
-    bufs = [np.ascontiguousarray(np.asarray(d, dtype=np.complex64)) for d in data]
+    c128 = all(np.asarray(d).dtype == np.complex128 for d in data)
+    dt = np.complex128 if c128 else np.complex64
+    bufs = [np.ascontiguousarray(np.asarray(d, dtype=dt)) for d in data]
     for d, l in zip(bufs, leaves):
         assert d.size == int(np.prod([ext[x] for x in l], dtype=np.int64)), "leaf data size"
     ptrs = (ctypes.c_void_p * len(bufs))(*[d.ctypes.data for d in bufs])
@@ -101,7 +104,7 @@ def contract(extents, leaves, out_modes, data, lhs, rhs, fixed: Optional[dict] =
     out = np.zeros(int(np.prod(shape, dtype=np.int64)) * 2, dtype=np.float64)
     nt = threads if threads else max_threads()
     rc = lib.oracle_contract(len(ext), _ptr(ext, ctypes.c_int64), len(leaves), _ptr(rank, ctypes.c_int32),
-                             _ptr(modes, ctypes.c_int32), ptrs, len(lhs), _ptr(lhs_a, ctypes.c_int32),
+                             _ptr(modes, ctypes.c_int32), ptrs, int(c128), len(lhs), _ptr(lhs_a, ctypes.c_int32),
                              _ptr(rhs_a, ctypes.c_int32), len(out_modes), _ptr(outm, ctypes.c_int32),
                              len(fixed), _ptr(fm, ctypes.c_int32), _ptr(fv, ctypes.c_int64),
                              _ptr(out, ctypes.c_double), nt)

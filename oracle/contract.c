@@ -166,7 +166,8 @@ static int permute_to(const otensor *T, const int32_t *order, int rank, double *
  * Contract a whole network along a tree.
  *   extents[num_modes]            mode extents
  *   leaf_rank[L], leaf_modes[...]  declared mode order of each leaf
- *   leaf_data[L]                   complex64 (interleaved float re, im) row-major buffers
+ *   leaf_data[L]                   row-major buffers: complex64 (interleaved float re, im),
+ *                                  or complex128 (interleaved double) when leaf_c128 != 0
  *   lhs[S], rhs[S]                 SSA operand ids; step s creates L + s
  *   out_modes[out_rank]            output order
  *   fixed_modes/values[num_fixed]  closed modes pinned to one value
@@ -174,7 +175,7 @@ static int permute_to(const otensor *T, const int32_t *order, int rank, double *
  */
 int oracle_contract(int32_t num_modes, const int64_t *extents,
                     int32_t num_leaves, const int32_t *leaf_rank, const int32_t *leaf_modes,
-                    const float *const *leaf_data,
+                    const void *const *leaf_data, int32_t leaf_c128,
                     int32_t num_steps, const int32_t *lhs, const int32_t *rhs,
                     int32_t out_rank, const int32_t *out_modes,
                     int32_t num_fixed, const int32_t *fixed_modes, const int64_t *fixed_values,
@@ -223,8 +224,15 @@ int oracle_contract(int32_t num_modes, const int64_t *extents,
     for (int64_t e = 0; e < size; ++e) {
       int64_t rr = e, src = base;
       for (int p = keep - 1; p >= 0; --p) { src += (rr % T[l].dims[p]) * kst[p]; rr /= T[l].dims[p]; }
-      T[l].data[2 * e] = (double)leaf_data[l][2 * src];
-      T[l].data[2 * e + 1] = (double)leaf_data[l][2 * src + 1];
+      if (leaf_c128) {
+        const double *d = (const double *)leaf_data[l];
+        T[l].data[2 * e] = d[2 * src];
+        T[l].data[2 * e + 1] = d[2 * src + 1];
+      } else {
+        const float *f = (const float *)leaf_data[l];
+        T[l].data[2 * e] = (double)f[2 * src];
+        T[l].data[2 * e + 1] = (double)f[2 * src + 1];
+      }
     }
     free(kst); free(full_st);
   }

@@ -329,7 +329,9 @@ class _Arena:
 
 
 def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), align=256,
-              tiny_mnk=1 << 15, max_group=256) -> Plan:
+              tiny_mnk=1 << 15, max_group=256, dtype=0) -> Plan:
+    """dtype 0: complex64 (8-byte entries), 1: complex128 (16-byte entries)."""
+    eb = 16 if dtype == 1 else 8
     validate(extents, leaves, out_modes, lhs, rhs, sliced)
     L, S = len(leaves), len(lhs)
     sl = set(sliced)
@@ -358,7 +360,7 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
         mu = _prod(extents, M); nu = _prod(extents, N); ku = _prod(extents, K)
         flops += 8 * m * n * k
         flops_u += 8 * mu * nu * ku
-        nbytes += 8 * (m * k + n * k + m * n)
+        nbytes += eb * (m * k + n * k + m * n)
         max_elems = max(max_elems, m * n)
         if m * n * k <= tiny_mnk:
             cls = CLASS_TINY
@@ -391,7 +393,7 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
                 need = order[t] != want
             setattr(node, "copy_" + which, int(need))
         if splits > 1:
-            node.scratch_bytes = splits * R * Sx * 8
+            node.scratch_bytes = splits * R * Sx * eb
         nodes.append(node)
 
     # launch groups: the tiny steps between two non-tiny steps (a segment)
@@ -433,7 +435,7 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
 
     # arena
     def rbytes(elems):
-        return _ceil_div(elems * 8, align) * align
+        return _ceil_div(elems * eb, align) * align
 
     arena = _Arena()
     tensor_off = [NONE] * (L + S)

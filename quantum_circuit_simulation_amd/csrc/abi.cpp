@@ -184,13 +184,14 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
     if (buf == tnc::kBufOut) return static_cast<char *>(out) + off_bytes;
     return const_cast<char *>(static_cast<const char *>(leaves[buf - tnc::kBufLeaf0])) + off_bytes;
   };
-  auto operand = [&](const tnc::Node &nd, int w) -> const float2 * {
+  auto operand = [&](const tnc::Node &nd, int w) -> const void * {
     int32_t t = w == 0 ? nd.lhs : nd.rhs;
     int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
     uint64_t off = w == 0 ? nd.a_off : nd.b_off;
-    if (copy || t >= p.L) return reinterpret_cast<const float2 *>(arena + off);
-    return static_cast<const float2 *>(leaves[t]);
+    if (copy || t >= p.L) return arena + off;
+    return leaves[t];
   };
+  const bool z = p.dtype == TNC_C128;
 
   int64_t num_slices = p.stats.num_slices;
   tnc::SliceDigits sd{};
@@ -207,20 +208,20 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
       hipError_t e = hipSuccess;
       switch (op.kind) {
         case tnc::OP_COPY:
-          e = tnc::launch_copy(cdesc + op.first, op.count, op.max_count, ptab, ints, sd, beta, stream);
+          e = tnc::launch_copy(cdesc + op.first, op.count, op.max_count, ptab, ints, sd, beta, z, stream);
           break;
         case tnc::OP_COPY_TILED:
-          e = tnc::launch_copy_tiled(cdesc + op.first, op.max_count, ptab, ints, sd, beta, stream);
+          e = tnc::launch_copy_tiled(cdesc + op.first, op.max_count, ptab, ints, sd, beta, z, stream);
           break;
         case tnc::OP_TINY_GROUP:
-          e = tnc::launch_tiny(tdesc + op.first, op.count, ptab, runs, beta, stream);
+          e = tnc::launch_tiny(tdesc + op.first, op.count, ptab, runs, beta, z, stream);
           break;
         case tnc::OP_SKINNY:
         case tnc::OP_GEMM: {
           const tnc::Node &nd = p.nodes[op.first];
-          tnc::StepArgs a{};
-          a.X = operand(nd, nd.swap ? 1 : 0);
-          a.Y = operand(nd, nd.swap ? 0 : 1);
+          tnc::StepArgsT<float2> a{};
+          a.X = reinterpret_cast<const float2 *>(operand(nd, nd.swap ? 1 : 0));
+          a.Y = reinterpret_cast<const float2 *>(operand(nd, nd.swap ? 0 : 1));
           a.C = reinterpret_cast<float2 *>(nd.c_off == tnc::kNone ? resolve(tnc::kBufOut, 0)
                                                                    : resolve(tnc::kBufArena, nd.c_off));
           a.R = nd.swap ? nd.n : nd.m;
@@ -232,7 +233,25 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
           a.beta = (nd.is_root && !p.root_permute) ? beta : 0;
           a.splits = nd.splits;
           a.scratch = nd.splits > 1 ? reinterpret_cast<float2 *>(arena + nd.scratch_off) : nullptr;
-          e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm(a, stream) : tnc::launch_skinny(a, stream);
+          if (z) {
+            // same fields, complex128 entries
+            tnc::StepArgsZ az{};
+            az.X = reinterpret_cast<const double2 *>(a.X);
+            az.Y = reinterpret_cast<const double2 *>(a.Y);
+            az.C = reinterpret_cast<double2 *>(a.C);
+            az.R = a.R;
+            az.S = a.S;
+            az.K = a.K;
+            az.runs = a.runs;
+            az.nrr = a.nrr;
+            az.ncr = a.ncr;
+            az.beta = a.beta;
+            az.splits = a.splits;
+            az.scratch = reinterpret_cast<double2 *>(a.scratch);
+            e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm_z(az, stream) : tnc::launch_skinny_z(az, stream);
+          } else {
+            e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm(a, stream) : tnc::launch_skinny(a, stream);
+          }
           break;
         }
       }

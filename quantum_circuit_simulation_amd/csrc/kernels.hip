@@ -32,6 +32,21 @@ __device__ __forceinline__ void cmac(float2 &acc, float2 a, float2 b) {
   acc.y = fmaf(a.y, b.x, acc.y);
 }
 
+__device__ __forceinline__ void cmac(double2 &acc, double2 a, double2 b) {
+  acc.x = fma(a.x, b.x, acc.x);
+  acc.x = fma(-a.y, b.y, acc.x);
+  acc.y = fma(a.x, b.y, acc.y);
+  acc.y = fma(a.y, b.x, acc.y);
+}
+
+template <typename T>
+__device__ __forceinline__ T czero() {
+  T z;
+  z.x = 0;
+  z.y = 0;
+  return z;
+}
+
 // Offset in C (entries) of index `idx` along one side, runs outermost first.
 // Indices below 2^32 (every run size then fits too) take 32-bit division.
 __device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int n) {
@@ -61,9 +76,10 @@ __device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int 
   return off;
 }
 
-__device__ __forceinline__ void store_c(float2 *p, float2 v, int beta) {
+template <typename T>
+__device__ __forceinline__ void store_c(T *p, T v, int beta) {
   if (beta) {
-    float2 o = *p;
+    T o = *p;
     v.x += o.x;
     v.y += o.y;
   }
@@ -88,6 +104,7 @@ __global__ void k_write_ptrs(void **dst, PtrChunk c) {
 // ---------------------------------------------------------------------------
 // permuting copy (leaf staging, naive-order re-layout, root permute)
 
+template <typename T>
 __global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int64_t *ints, SliceDigits sd,
                        int32_t beta) {
   const CopyDesc d = descs[blockIdx.y];
@@ -96,8 +113,8 @@ __global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int
   const int64_t *slc = sst + d.rank;
   int64_t base = d.src_off;
   for (int t = 0; t < sd.n; ++t) base += (int64_t)sd.digit[t] * slc[t];
-  const float2 *src = (const float2 *)ptab[d.src_buf] + base;
-  float2 *dst = (float2 *)ptab[d.dst_buf] + d.dst_off;
+  const T *src = (const T *)ptab[d.src_buf] + base;
+  T *dst = (T *)ptab[d.dst_buf] + d.dst_off;
   const int b = beta && d.is_root;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < d.count; e += step) {
@@ -117,9 +134,10 @@ __global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int
 // arithmetic) and staged into LDS once per workgroup.
 constexpr int kTileMax = 1024;
 
+template <typename T>
 __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const void *const *ptab, const int64_t *ints,
                                                     SliceDigits sd, int32_t beta) {
-  __shared__ float2 buf[kTileMax];
+  __shared__ T buf[kTileMax];
   __shared__ int64_t s_src[kTileMax];
   __shared__ int32_t s_lds[kTileMax];
   __shared__ int64_t s_dst[kTileMax];
@@ -142,8 +160,8 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
   }
   int64_t base = d.src_off;
   for (int q = 0; q < sd.n; ++q) base += (int64_t)sd.digit[q] * slc[q];
-  const float2 *src = (const float2 *)ptab[d.src_buf] + base;
-  float2 *dst = (float2 *)ptab[d.dst_buf] + d.dst_off;
+  const T *src = (const T *)ptab[d.src_buf] + base;
+  T *dst = (T *)ptab[d.dst_buf] + d.dst_off;
   const int b = beta && d.is_root;
   const int64_t ntiles = d.count / tile;
   __syncthreads();
@@ -175,12 +193,13 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
 // ---------------------------------------------------------------------------
 // grouped tiny steps: one workgroup per step
 
+template <typename T>
 __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
                                               int32_t beta) {
   const TinyDesc d = descs[blockIdx.x];
-  const float2 *X = (const float2 *)ptab[d.x_buf] + d.x_off;
-  const float2 *Y = (const float2 *)ptab[d.y_buf] + d.y_off;
-  float2 *C = (float2 *)ptab[d.c_buf] + d.c_off;
+  const T *X = (const T *)ptab[d.x_buf] + d.x_off;
+  const T *Y = (const T *)ptab[d.y_buf] + d.y_off;
+  T *C = (T *)ptab[d.c_buf] + d.c_off;
   const RunDev *rr = runs + d.runs_index;
   const RunDev *cr = rr + d.nrr;
   const int R = d.R, S = d.S, K = d.K;
@@ -194,11 +213,11 @@ __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void 
   const int b = beta && d.is_root;
   for (int o0 = 0; o0 < outputs; o0 += per_pass) {
     const int o = o0 + grp;
-    float2 acc = make_float2(0.f, 0.f);
+    T acc = czero<T>();
     if (o < outputs) {
       const int i = o / S, j = o - (o / S) * S;
-      const float2 *xr = X + (int64_t)i * K;
-      const float2 *yr = Y + (int64_t)j * K;
+      const T *xr = X + (int64_t)i * K;
+      const T *yr = Y + (int64_t)j * K;
       for (int l = lane; l < K; l += G) cmac(acc, xr[l], yr[l]);
     }
     for (int w = 1; w < G; w *= 2) {
@@ -484,13 +503,14 @@ __global__ __launch_bounds__(256) void k_skinny_small(StepArgs a) {
 }
 
 // sum split-K partials [splits, R, S] into C through the runs
-__global__ void k_split_reduce(StepArgs a) {
+template <typename T>
+__global__ void k_split_reduce(StepArgsT<T> a) {
   const int64_t total = a.R * a.S;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
-    float2 acc = make_float2(0.f, 0.f);
+    T acc = czero<T>();
     for (int sp = 0; sp < a.splits; ++sp) {
-      const float2 v = a.scratch[(int64_t)sp * total + e];
+      const T v = a.scratch[(int64_t)sp * total + e];
       acc.x += v.x;
       acc.y += v.y;
     }
@@ -915,11 +935,211 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t run_split_reduce(const StepArgs &a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// complex128 (FP64) kernels
+
+// Skinny complex128 steps (one side <= 16): one row per thread, each 16-entry
+// K chunk of a 256-row tile staged through LDS, the small operand read by
+// broadcast, outputs accumulated in registers.
+__global__ __launch_bounds__(256) void k_skinny_z(StepArgsZ a, int64_t kchunk) {
+  __shared__ double2 xs[256][kRowsKC + 1];
+  __shared__ double2 ys[kSkinnyMax][kRowsKC];
+  __shared__ int64_t coloff[kSkinnyMax];
+  const int tid = threadIdx.x;
+  const int S = (int)a.S;
+  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  double2 acc[kSkinnyMax];
+#pragma unroll
+  for (int q = 0; q < kSkinnyMax; ++q) acc[q] = czero<double2>();
+  for (int64_t kc = k0; kc < k1; kc += kRowsKC) {
+    const int w = (int)min((int64_t)kRowsKC, k1 - kc);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int row = tid / kRowsKC + 16 * p, col = tid % kRowsKC;
+      const int64_t gi = r0 + row;
+      xs[row][col] = (gi < a.R && col < w) ? a.X[gi * a.K + kc + col] : czero<double2>();
+    }
+    if (tid < kSkinnyMax * kRowsKC) {
+      const int sr = tid / kRowsKC, col = tid % kRowsKC;
+      ys[sr][col] = (sr < S && col < w) ? a.Y[(int64_t)sr * a.K + kc + col] : czero<double2>();
+    }
+    __syncthreads();
+    for (int l = 0; l < w; ++l) {
+      const double2 x = xs[tid][l];
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) cmac(acc[q], x, ys[q][l]);
+    }
+  }
+  const int64_t i = r0 + tid;
+  if (i < a.R) {
+    if (a.splits > 1) {
+      double2 *p = a.scratch + ((int64_t)split * a.R + i) * a.S;
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) p[q] = acc[q];
+    } else {
+      const int64_t ro = run_offset(i, a.runs, a.nrr);
+#pragma unroll
+      for (int q = 0; q < kSkinnyMax; ++q)
+        if (q < S) store_c(a.C + ro + coloff[q], acc[q], a.beta);
+    }
+  }
+}
+
+// Complex128 GEMM on FP64 MFMA (v_mfma_f64_16x16x4_f64: a 16x4 block times a
+// 4x16 block).  Its 4-long reduction axis carries (re, im) of two complex l:
+// lanes with k' = lane / 16 in {0, 1, 2, 3} supply x_re(l0), x_im(l0),
+// x_re(l1), x_im(l1); the second operand supplies (y_re, -y_im) for the real
+// part and (y_im, y_re) for the imaginary part, so two complex l cost two
+// MFMAs per 16x16 complex block and the count is exactly 8 m n k flops.
+// LDS holds both tiles as (re, im) planes of doubles, [rows][BK + 2]; tiles
+// 64x64 (four waves of 32x32), BK = 8, two LDS stages, XCD-aware tile order,
+// one tile per workgroup.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256, 2) void k_zgemm(StepArgsZ a, int64_t kchunk, uint32_t tiles_r, uint32_t tiles_c) {
+  constexpr int BM = 64, BN = 64, BK = 8, WM = 32, WN = 32;
+  constexpr int LDK = BK + 2;
+  constexpr int MB = WM / 16, NB = WN / 16;
+  constexpr int WAVES_C = BN / WN;
+  constexpr int A_PER = BM * BK / 256, B_PER = BN * BK / 256;
+
+  __shared__ double As[2][2][BM][LDK];
+  __shared__ double Bs[2][2][BN][LDK];
+  __shared__ int64_t rowoff[BM];
+  __shared__ int64_t coloff[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WAVES_C, wc = wave % WAVES_C;
+  const int kq = lane >> 4, l16 = lane & 15;
+  const int plane = kq & 1, lofs = kq >> 1;
+  const double sgn = plane ? -1.0 : 1.0;
+  uint32_t tr, tc;
+  tile_coords(blockIdx.x, tiles_r, tiles_c, &tr, &tc);
+  const int64_t r0 = (int64_t)tr * BM, c0 = (int64_t)tc * BN;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  const int64_t nkt = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+  const int64_t R = a.R, S = a.S, K = a.K;
+
+  f64x4 accR[MB][NB], accI[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        accR[mb][nb][r] = 0.0;
+        accI[mb][nb][r] = 0.0;
+      }
+
+  double2 ra[A_PER], rb[B_PER];
+  auto gload = [&](int64_t kt) {
+    const int64_t kb = k0 + kt * BK;
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      const int64_t gi = r0 + row, gl = kb + l;
+      ra[q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : czero<double2>();
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      const int64_t gj = c0 + col, gl = kb + l;
+      rb[q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : czero<double2>();
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int row = e / BK, l = e % BK;
+      As[st][0][row][l] = ra[q].x;
+      As[st][1][row][l] = ra[q].y;
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+      const int e = tid + 256 * q;
+      const int col = e / BK, l = e % BK;
+      Bs[st][0][col][l] = rb[q].x;
+      Bs[st][1][col][l] = rb[q].y;
+    }
+  };
+
+  if (nkt > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    const int st = (int)(kt & 1);
+    if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+    for (int l2 = 0; l2 < BK; l2 += 2) {
+      double av[MB], brv[NB], biv[NB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[mb] = As[st][plane][wr * WM + mb * 16 + l16][l2 + lofs];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        brv[nb] = sgn * Bs[st][plane][wc * WN + nb * 16 + l16][l2 + lofs];
+        biv[nb] = Bs[st][1 - plane][wc * WN + nb * 16 + l16][l2 + lofs];
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          accR[mb][nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mb], brv[nb], accR[mb][nb], 0, 0, 0);
+          accI[mb][nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mb], biv[nb], accI[mb][nb], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nkt) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  const bool partial = a.splits > 1;
+  if (!partial) {
+    for (int t = tid; t < BM; t += 256) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += 256) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wc * WN + nb * 16 + l16;
+      const int64_t gj = c0 + col;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // the FP64 16x16x4 result puts row kq + 4r in register r of lane
+        // (kq, col) (the FP32 shapes use 4kq + r)
+        const int row = wr * WM + mb * 16 + kq + 4 * r;
+        const int64_t gi = r0 + row;
+        if (gi < R && gj < S) {
+          double2 v;
+          v.x = accR[mb][nb][r];
+          v.y = accI[mb][nb][r];
+          if (partial) a.scratch[((int64_t)split * R + gi) * S + gj] = v;
+          else store_c(a.C + rowoff[row] + coloff[col], v, a.beta);
+        }
+      }
+    }
+}
+
+template <typename T>
+hipError_t run_split_reduce(const StepArgsT<T> &a, hipStream_t stream) {
   const int64_t total = a.R * a.S;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_split_reduce<T>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -944,28 +1164,40 @@ hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *con
 }
 
 hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, const void *const *ptab,
-                       const int64_t *ints, const SliceDigits &digits, int32_t beta, hipStream_t stream) {
+                       const int64_t *ints, const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream) {
   int64_t blocks = (max_count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, descs, ptab, ints,
-                     digits, beta);
+  if (z)
+    hipLaunchKernelGGL(k_copy<double2>, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, descs, ptab,
+                       ints, digits, beta);
+  else
+    hipLaunchKernelGGL(k_copy<float2>, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, descs, ptab,
+                       ints, digits, beta);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
-                             const SliceDigits &digits, int32_t beta, hipStream_t stream) {
+                             const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream) {
   // one workgroup per tile of >= 32 entries, at most 8192 workgroups
   int64_t blocks = count / 32;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_copy_tiled, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits, beta);
+  if (z)
+    hipLaunchKernelGGL(k_copy_tiled<double2>, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits,
+                       beta);
+  else
+    hipLaunchKernelGGL(k_copy_tiled<float2>, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits,
+                       beta);
   return hipGetLastError();
 }
 
 hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
-                       int32_t beta, hipStream_t stream) {
-  hipLaunchKernelGGL(k_tiny, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
+                       int32_t beta, bool z, hipStream_t stream) {
+  if (z)
+    hipLaunchKernelGGL(k_tiny<double2>, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
+  else
+    hipLaunchKernelGGL(k_tiny<float2>, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
   return hipGetLastError();
 }
 
@@ -1007,6 +1239,29 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
   else if (a.S > 64) e = run_cgemm<128, 128, 8, 64, 64>(a, stream);
   else if (a.S > 32) e = run_cgemm<256, 64, 8, 64, 64>(a, stream);
   else e = run_cgemm<256, 32, 8, 64, 32>(a, stream);
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return run_split_reduce(a, stream);
+}
+
+hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream) {
+  int64_t kchunk = a.K;
+  if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
+  dim3 grid((unsigned)((a.R + 255) / 256), (unsigned)a.splits);
+  hipLaunchKernelGGL(k_skinny_z, grid, dim3(256), 0, stream, a, kchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return run_split_reduce(a, stream);
+}
+
+hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream) {
+  constexpr int64_t BM = 64, BN = 64, BK = 8;
+  const int64_t tiles_r = (a.R + BM - 1) / BM, tiles_c = (a.S + BN - 1) / BN;
+  if (tiles_r * tiles_c >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  int64_t kchunk = a.K;
+  if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  dim3 grid((unsigned)(tiles_r * tiles_c), (unsigned)a.splits);
+  hipLaunchKernelGGL(k_zgemm, grid, dim3(256), 0, stream, a, kchunk, (uint32_t)tiles_r, (uint32_t)tiles_c);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   return run_split_reduce(a, stream);
 }

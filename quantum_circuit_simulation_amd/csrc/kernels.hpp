@@ -15,32 +15,38 @@ struct SliceDigits {
 };
 
 // Operands of one oriented pairwise step: C[i, j] = sum_l X[i, l] * Y[j, l],
-// X row-major [R, K], Y row-major [S, K], complex64.  C is written at
-// rowoff(i) + coloff(j) through `runs` (nrr row runs then ncr col runs,
-// outermost first).  beta = 1 adds into C.  splits > 1: K is cut into
-// `splits` chunks whose partial sums go to `scratch` [splits, R, S] and are
-// then reduced into C.
-struct StepArgs {
-  const float2 *X;
-  const float2 *Y;
-  float2 *C;
+// X row-major [R, K], Y row-major [S, K]; T = float2 (complex64) or double2
+// (complex128).  C is written at rowoff(i) + coloff(j) through `runs` (nrr row
+// runs then ncr col runs, outermost first).  beta = 1 adds into C.
+// splits > 1: K is cut into `splits` chunks whose partial sums go to
+// `scratch` [splits, R, S] and are then reduced into C.
+template <typename T>
+struct StepArgsT {
+  const T *X;
+  const T *Y;
+  T *C;
   int64_t R, S, K;
   const RunDev *runs;
   int32_t nrr, ncr;
   int32_t beta;
   int32_t splits;
-  float2 *scratch;
+  T *scratch;
 };
+using StepArgs = StepArgsT<float2>;    // complex64
+using StepArgsZ = StepArgsT<double2>;  // complex128
 
+// `z` selects complex128 entries (16 bytes) instead of complex64 (8 bytes).
 hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *const *leaves, int32_t num_leaves,
                              hipStream_t stream);
 hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, const void *const *ptab,
-                       const int64_t *ints, const SliceDigits &digits, int32_t beta, hipStream_t stream);
+                       const int64_t *ints, const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream);
 hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
-                             const SliceDigits &digits, int32_t beta, hipStream_t stream);
+                             const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream);
 hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
-                       int32_t beta, hipStream_t stream);
+                       int32_t beta, bool z, hipStream_t stream);
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const StepArgs &a, hipStream_t stream);
+hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream);
+hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream);
 
 }  // namespace tnc

@@ -26,7 +26,7 @@ bool checked_prod(const std::vector<int64_t> &ext, const std::vector<int32_t> &m
   __int128 p = 1;
   for (int32_t x : modes) {
     p *= ext[x];
-    if (p > (__int128)(INT64_MAX / 8)) return false;
+    if (p > (__int128)(INT64_MAX / 16)) return false;
   }
   *out = (int64_t)p;
   return true;
@@ -314,7 +314,10 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   if (o.align < 256 || (o.align & (o.align - 1)) != 0) return TNC_ERR_INVALID_ARG;
   if (o.max_group < 1) return TNC_ERR_INVALID_ARG;
   if (o.order != TNC_ORDER_LIFETIME && o.order != TNC_ORDER_NAIVE) return TNC_ERR_INVALID_ARG;
-  if (net->dtype != TNC_C64) return TNC_ERR_UNSUPPORTED;
+  if (net->dtype != TNC_C64 && net->dtype != TNC_C128) return TNC_ERR_INVALID_ARG;
+  p->dtype = net->dtype;
+  const uint64_t eb = net->dtype == TNC_C128 ? 16 : 8;  // bytes per entry
+  p->elem_bytes = eb;
   tnc_status st = validate(p, net, tree);
   if (st != TNC_OK) return st;
 
@@ -415,7 +418,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     nd.ku = prod(p->extents, K[s]);
     flops += 8.0 * (double)nd.m * (double)nd.n * (double)nd.k;
     flops_u += 8.0 * (double)nd.mu * (double)nd.nu * (double)nd.ku;
-    bytes += 8.0 * ((double)nd.m * nd.k + (double)nd.n * nd.k + (double)nd.m * nd.n);
+    bytes += (double)eb * ((double)nd.m * nd.k + (double)nd.n * nd.k + (double)nd.m * nd.n);
     max_elems = std::max<uint64_t>(max_elems, (uint64_t)(nd.m * nd.n));
     __int128 mnk = (__int128)nd.m * nd.n * nd.k;
     if (mnk <= (__int128)o.tiny_mnk) nd.cls = TNC_CLASS_TINY;
@@ -434,7 +437,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
                                      nd.k >= (int64_t(1) << 31)))
       return TNC_ERR_UNSUPPORTED;
     nd.splits = split_rule(nd.cls, R, Sx, nd.k);
-    if (nd.splits > 1) nd.scratch_bytes = (uint64_t)nd.splits * (uint64_t)R * (uint64_t)Sx * 8;
+    if (nd.splits > 1) nd.scratch_bytes = (uint64_t)nd.splits * (uint64_t)R * (uint64_t)Sx * eb;
     // operand copies
     for (int w = 0; w < 2; ++w) {
       int32_t t = w == 0 ? nd.lhs : nd.rhs;
@@ -496,7 +499,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     for (int32_t s : p->groups[g]) p->nodes[s].group = (int32_t)g;
 
   // ---- arena
-  auto rbytes = [&](int64_t elems) { return round_up((uint64_t)elems * 8, o.align); };
+  auto rbytes = [&](int64_t elems) { return round_up((uint64_t)elems * eb, o.align); };
   std::vector<int64_t> elems(T);
   for (int32_t t = 0; t < T; ++t) elems[t] = prod(ext, sets[t]);
   Arena arena;
@@ -679,13 +682,13 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
           int32_t t = w == 0 ? nd.lhs : nd.rhs;
           int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
           uint64_t ao = w == 0 ? nd.a_off : nd.b_off;
-          if (copy || t >= L) { *buf = kBufArena; *off = (int64_t)(ao / 8); }
+          if (copy || t >= L) { *buf = kBufArena; *off = (int64_t)(ao / eb); }
           else { *buf = kBufLeaf0 + t; *off = 0; }
         };
         operand(nd.swap ? 1 : 0, &d.x_buf, &d.x_off);
         operand(nd.swap ? 0 : 1, &d.y_buf, &d.y_off);
         if (nd.c_off == kNone) { d.c_buf = kBufOut; d.c_off = 0; }
-        else { d.c_buf = kBufArena; d.c_off = (int64_t)(nd.c_off / 8); }
+        else { d.c_buf = kBufArena; d.c_off = (int64_t)(nd.c_off / eb); }
         d.is_root = nd.is_root && !p->root_permute;
         d.R = (int32_t)(nd.swap ? nd.n : nd.m);
         d.S = (int32_t)(nd.swap ? nd.m : nd.n);
@@ -720,8 +723,8 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     d.dst_buf = c.dst_buf;
     d.rank = (int32_t)c.dims.size();
     d.is_root = c.is_root;
-    d.src_off = (int64_t)(c.src_off_bytes / 8);
-    d.dst_off = (int64_t)(c.dst_off_bytes / 8);
+    d.src_off = (int64_t)(c.src_off_bytes / eb);
+    d.dst_off = (int64_t)(c.dst_off_bytes / eb);
     d.count = c.count;
     d.ints_index = (int32_t)ints.size();
     d.tiled = c.tiled;

@@ -91,6 +91,9 @@ struct PlanImpl {
   std::vector<int32_t> sliced;
   tnc_plan_options opts{};
 
+  tnc_dtype dtype = TNC_C64;
+  uint64_t elem_bytes = 8;                     // 8 (complex64) or 16 (complex128)
+
   // ---- derived
   int32_t L = 0, S = 0;
   std::vector<std::vector<int32_t>> order;     // planned order per SSA tensor

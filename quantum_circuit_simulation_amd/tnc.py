@@ -151,7 +151,7 @@ class Plan:
 
     def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
                  order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
-                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256):
+                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256, dtype: int = TNC_C64):
         lib = load_library()
         self._lib = lib
         self.num_leaves = len(leaves)
@@ -165,7 +165,8 @@ class Plan:
         self._keep = (ext, rank, modes, outm, lhs_a, rhs_a, sl)
         net = Network(len(extents), ext.ctypes.data_as(P(ctypes.c_int64)), len(leaves),
                       rank.ctypes.data_as(P(ctypes.c_int32)), modes.ctypes.data_as(P(ctypes.c_int32)),
-                      len(out_modes), outm.ctypes.data_as(P(ctypes.c_int32)), TNC_C64)
+                      len(out_modes), outm.ctypes.data_as(P(ctypes.c_int32)), int(dtype))
+        self.dtype = int(dtype)
         tree = Tree(len(lhs), lhs_a.ctypes.data_as(P(ctypes.c_int32)), rhs_a.ctypes.data_as(P(ctypes.c_int32)))
         opts = PlanOptions()
         lib.tnc_plan_options_default(ctypes.byref(opts))
@@ -236,9 +237,10 @@ class Plan:
         import torch
         if len(leaves) != self.num_leaves:
             raise ValueError("wrong number of leaves")
+        want = torch.complex128 if self.dtype == TNC_C128 else torch.complex64
         for t in list(leaves) + [out]:
-            if t.dtype != torch.complex64 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("leaves and out must be contiguous complex64 GPU tensors")
+            if t.dtype != want or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"leaves and out must be contiguous {want} GPU tensors")
         if stream is None:
             stream = torch.cuda.current_stream()
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

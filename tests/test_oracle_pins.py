@@ -283,3 +283,19 @@ def test_random_greedy_search_is_deterministic_and_valid():
     got = oracle.contract_network(net, t1)
     ok, err = rel_err_ok(got, ref, TOL128)
     assert ok, err
+
+
+def test_complex128_leaves_are_read_at_full_precision():
+    """A network whose exact value needs more than single precision: with
+    complex128 leaves the oracle must reproduce the einsum to 1e-12."""
+    rng = np.random.default_rng(77)
+    net = randnet.random_network(rng, n_leaves=5, n_closed=7, n_open=2, max_leaf_elems=500)
+    data = [(rng.standard_normal(d.shape) + 1j * rng.standard_normal(d.shape)) for d in net.data]
+    tree = randnet.random_tree(rng, net.num_leaves)
+    got = oracle.contract(net.extents, net.leaves, net.out_modes, data, tree.lhs, tree.rhs)
+    ref = einsum_full(net.extents, net.leaves, net.out_modes, data)
+    ok, err = rel_err_ok(got, ref, 1e-12)
+    assert ok, err
+    single = oracle.contract(net.extents, net.leaves, net.out_modes, [d.astype(np.complex64) for d in data],
+                             tree.lhs, tree.rhs)
+    assert np.max(np.abs(single - ref)) > 1e-9 * np.max(np.abs(ref))

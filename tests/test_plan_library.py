@@ -53,10 +53,11 @@ def _compare(plan_lib, ref, L, S):
     assert st["workspace_bytes"] == st["header_bytes"] + st["arena_bytes"]
 
 
-def _check(net, tree, policy=P.LIFETIME, sliced=(), tiny_mnk=1 << 15, max_group=256):
+def _check(net, tree, policy=P.LIFETIME, sliced=(), tiny_mnk=1 << 15, max_group=256, dtype=0):
     ref = P.make_plan(net.extents, net.leaves, net.out_modes, tree.lhs, tree.rhs, policy=policy, sliced=sliced,
-                      tiny_mnk=tiny_mnk, max_group=max_group)
-    lib = qa.Plan.from_network(net, tree, order=policy, sliced=sliced, tiny_mnk=tiny_mnk, max_group=max_group)
+                      tiny_mnk=tiny_mnk, max_group=max_group, dtype=dtype)
+    lib = qa.Plan.from_network(net, tree, order=policy, sliced=sliced, tiny_mnk=tiny_mnk, max_group=max_group,
+                               dtype=dtype)
     _compare(lib, ref, net.num_leaves, tree.num_steps)
     return lib, ref
 
@@ -73,7 +74,7 @@ def test_random_plans_match_oracle(seed, policy):
     nsl = int(rng.integers(0, min(3, len(closed)) + 1))
     sliced = [int(x) for x in rng.choice(closed, size=nsl, replace=False)] if nsl else []
     _check(net, tree, policy=policy, sliced=sliced, tiny_mnk=int(rng.choice([0, 64, 1 << 15])),
-           max_group=int(rng.integers(1, 6)))
+           max_group=int(rng.integers(1, 6)), dtype=int(seed % 2))
 
 
 @pytest.mark.parametrize("policy", [P.LIFETIME, P.NAIVE])
@@ -142,3 +143,13 @@ def test_execute_rejects_small_workspace_without_touching_the_gpu():
     with pytest.raises(tnc.TncError) as e:
         plan.execute_ptrs([256] * net.num_leaves, 256, 128 + 256, need, 0)
     assert e.value.name == "TNC_ERR_INVALID_ARG"
+
+
+def test_complex128_plan_doubles_entry_bytes():
+    net = lattice.peps(4, 4, 1)
+    tree = lattice.row_major_tree(4)
+    p64, r64 = _check(net, tree, dtype=0)
+    p128, r128 = _check(net, tree, dtype=1)
+    assert r128.arena_bytes >= 2 * r64.arena_bytes - 256 * len(tree.lhs)
+    assert p128.stats()["bytes"] == 2 * p64.stats()["bytes"]
+    assert p128.stats()["flops"] == p64.stats()["flops"]
