@@ -233,9 +233,12 @@ class SkinnyWorkload:
 
     def kernel_of(self, idx):
         c, plan, m, n, k = self.plans[idx]
+        splits = plan.node(0)["splits"]
         if max(m, n) < 4096:
             return "k_skinny"
-        return "k_skinny_small" if 8 <= k <= 16 and plan.node(0)["splits"] == 1 else "k_skinny_rows"
+        if splits == 1 and 2 <= k <= 256 and (k & (k - 1)) == 0 and min(m, n) <= 16:
+            return "k_skinny_flat"
+        return "k_skinny_small" if 8 <= k <= 16 and splits == 1 else "k_skinny_rows"
 
     def launch_flops(self, idx):
         _, _, m, n, k = self.plans[idx]
@@ -243,7 +246,7 @@ class SkinnyWorkload:
 
     def launch_bytes(self, idx):
         _, _, m, n, k = self.plans[idx]
-        return float(self.eb) * (m * k + n * k + m * n)
+        return 8.0 * (m * k + n * k + m * n)
 
     def cpu_baseline(self, budget_s=12.0):
         import oracle

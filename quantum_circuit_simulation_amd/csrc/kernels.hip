@@ -502,6 +502,185 @@ __global__ __launch_bounds__(256) void k_skinny_small(StepArgs a) {
   }
 }
 
+// Many rows, whole K a power of two in [2, 256], S <= 16: the rows of X are
+// one contiguous stream and no barrier or LDS staging of X is needed.  G
+// lanes share a row; lane p of a row reads the 16-byte chunks p, p + G, ...
+// (V of them, so a wave's loads cover whole rows) and forms partial sums of
+// all SP outputs (S padded to a power of two; padded Y rows are zero) over
+// its 2V entries of K.  The G partials are combined with DPP lane exchanges
+// inside each 16-lane row: first all-reduce steps while the lanes outnumber
+// the outputs, then reduce-scatter steps, each of which halves the outputs a
+// lane keeps, so lane p ends with SP/G consecutive outputs and a row-major C
+// is written by contiguous lanes.  The small operand sits in registers when
+// it fits, else in LDS (row stride SP + 1, conflict-free).
+constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+constexpr int dpp_ctrl_for_bit(int b) {
+  // partner lane of each exchange flips the lane-index bit b (and only
+  // lower bits): row_mirror (i <-> 15 - i), row_half_mirror (i <-> 7 - i
+  // within 8), quad_perm [2,3,0,1], quad_perm [1,0,3,2]
+  return b == 8 ? 0x140 : b == 4 ? 0x141 : b == 2 ? 0x4E : 0xB1;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// all-reduce step: both lanes of a pair end with the pair's sum of all N
+template <int CTRL, int N>
+__device__ __forceinline__ void xchg_all(float *re, float *im) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    re[j] += dpp_f<CTRL>(re[j]);
+    im[j] += dpp_f<CTRL>(im[j]);
+  }
+}
+
+// reduce-scatter step: the lane with the pair bit set keeps the upper half
+// of its N values, its partner the lower half; each sends the half it drops
+template <int CTRL, int N>
+__device__ __forceinline__ void xchg_scatter(float *re, float *im, bool upper) {
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const float sr = upper ? re[j] : re[j + N / 2], si = upper ? im[j] : im[j + N / 2];
+    const float kr = upper ? re[j + N / 2] : re[j], ki = upper ? im[j + N / 2] : im[j];
+    re[j] = kr + dpp_f<CTRL>(sr);
+    im[j] = ki + dpp_f<CTRL>(si);
+  }
+}
+
+template <int BIT, int AR, int N>
+__device__ __forceinline__ void xchg_group(float *re, float *im, int lpos) {
+  if constexpr (BIT >= 1) {
+    if constexpr (AR > 0) {
+      xchg_all<dpp_ctrl_for_bit(BIT), N>(re, im);
+      xchg_group<BIT / 2, AR - 1, N>(re, im, lpos);
+    } else {
+      xchg_scatter<dpp_ctrl_for_bit(BIT), N>(re, im, (lpos & BIT) != 0);
+      xchg_group<BIT / 2, 0, N / 2>(re, im, lpos);
+    }
+  }
+}
+
+constexpr int flat_lanes(int K, int SP) {
+  int g = SP > K / 16 ? SP : K / 16;
+  if (g > K / 2) g = K / 2;
+  if (g > 16) g = 16;
+  return g < 1 ? 1 : g;
+}
+
+template <int G, int V, int SP, bool YREG, int U>
+__global__ __launch_bounds__(256) void k_skinny_flat(StepArgs a) {
+  constexpr int KH = G * V;                 // 16-byte chunks (entry pairs) per row
+  constexpr int K = 2 * KH;
+  constexpr int RPB = 256 / G;              // rows per workgroup pass
+  constexpr int LG = ilog2c(G), LS = ilog2c(SP);
+  constexpr int RS = LG < LS ? LG : LS;     // reduce-scatter steps
+  constexpr int NOUT = SP >> RS;            // outputs a lane keeps
+  constexpr int GS = G < SP ? G : SP;       // lanes that hold distinct outputs
+  __shared__ float4 ysl[YREG ? 1 : KH * (SP + 1)];
+  __shared__ int64_t coloff[kSkinnyMax];
+  const int tid = threadIdx.x, lpos = tid % G;
+  const int S = (int)a.S;
+  const bool rowmajor = a.nrr == 1 && a.ncr == 1 && a.runs[1].stride == 1 && a.runs[0].stride == a.S;
+  if (tid < S) coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  float4 yr[YREG ? V : 1][YREG ? SP : 1];
+  if constexpr (YREG) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c = lpos + G * v;
+#pragma unroll
+      for (int q = 0; q < SP; ++q) {
+        if (q < S) {
+          const float2 y0 = a.Y[(int64_t)q * K + 2 * c], y1 = a.Y[(int64_t)q * K + 2 * c + 1];
+          yr[v][q] = make_float4(y0.x, y0.y, y1.x, y1.y);
+        } else {
+          yr[v][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < KH * SP; e += 256) {
+      const int c = e / SP, q = e % SP;
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < S) {
+        const float2 y0 = a.Y[(int64_t)q * K + 2 * c], y1 = a.Y[(int64_t)q * K + 2 * c + 1];
+        y = make_float4(y0.x, y0.y, y1.x, y1.y);
+      }
+      ysl[c * (SP + 1) + q] = y;
+    }
+  }
+  __syncthreads();
+  const float4 *X4 = (const float4 *)a.X;
+  const int64_t R = a.R;
+  const int64_t stride = (int64_t)gridDim.x * RPB;
+  const bool pairs = (NOUT % 2) == 0 && S == SP && aligned16(a.C);
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB + tid / G; r0 < R; r0 += stride * U) {
+    float4 xv[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t rr = r0 + u * stride;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        xv[u][v] = rr < R ? X4[rr * KH + lpos + G * v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // re-read the LDS copy of the small operand every pass (an opaque
+    // index stops the compiler from hoisting all V * SP reads into registers)
+    int cb = lpos;
+    if constexpr (!YREG) asm volatile("" : "+v"(cb));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t rr = r0 + u * stride;
+      float re[SP], im[SP];
+#pragma unroll
+      for (int q = 0; q < SP; ++q) re[q] = im[q] = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float4 x = xv[u][v];
+#pragma unroll
+        for (int q = 0; q < SP; ++q) {
+          const float4 y = YREG ? yr[v < V ? v : 0][q] : ysl[(cb + G * v) * (SP + 1) + q];
+          re[q] = fmaf(x.x, y.x, re[q]);
+          re[q] = fmaf(-x.y, y.y, re[q]);
+          re[q] = fmaf(x.z, y.z, re[q]);
+          re[q] = fmaf(-x.w, y.w, re[q]);
+          im[q] = fmaf(x.x, y.y, im[q]);
+          im[q] = fmaf(x.y, y.x, im[q]);
+          im[q] = fmaf(x.z, y.w, im[q]);
+          im[q] = fmaf(x.w, y.z, im[q]);
+        }
+      }
+      xchg_group<G / 2, LG - RS, SP>(re, im, lpos);
+      if (rr < R && (G <= SP || lpos < SP)) {
+        const int base = (lpos % GS) * NOUT;
+        if (rowmajor) {
+          float2 *dst = a.C + rr * S + base;
+          if (pairs) {
+#pragma unroll
+            for (int j = 0; j < NOUT; j += 2) {
+              float4 o = make_float4(re[j], im[j], re[j + 1], im[j + 1]);
+              if (a.beta) {
+                const float4 c = *(const float4 *)(dst + j);
+                o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+              }
+              *(float4 *)(dst + j) = o;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NOUT; ++j)
+              if (base + j < S) store_c(dst + j, make_float2(re[j], im[j]), a.beta);
+          }
+        } else {
+          const int64_t ro = run_offset(rr, a.runs, a.nrr);
+#pragma unroll
+          for (int j = 0; j < NOUT; ++j)
+            if (base + j < S) store_c(a.C + ro + coloff[base + j], make_float2(re[j], im[j]), a.beta);
+        }
+      }
+    }
+  }
+}
+
 // sum split-K partials [splits, R, S] into C through the runs
 template <typename T>
 __global__ void k_split_reduce(StepArgsT<T> a) {
@@ -1201,7 +1380,46 @@ hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *
   return hipGetLastError();
 }
 
+template <int K, int SP>
+static hipError_t run_skinny_flat(const StepArgs &a, hipStream_t stream) {
+  constexpr int G = flat_lanes(K, SP), V = K / (2 * G);
+  constexpr bool YREG = V * SP <= 16;
+  constexpr int U = V <= 2 ? 2 : 1;
+  const int64_t per = (int64_t)(256 / G) * U;
+  int64_t blocks = (a.R + per - 1) / per;
+  const int64_t cap = 16 * (int64_t)num_cus();
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((k_skinny_flat<G, V, SP, YREG, U>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int SP>
+static hipError_t run_skinny_flat_k(const StepArgs &a, hipStream_t stream) {
+  switch (a.K) {
+    case 2: return run_skinny_flat<2, SP>(a, stream);
+    case 4: return run_skinny_flat<4, SP>(a, stream);
+    case 8: return run_skinny_flat<8, SP>(a, stream);
+    case 16: return run_skinny_flat<16, SP>(a, stream);
+    case 32: return run_skinny_flat<32, SP>(a, stream);
+    case 64: return run_skinny_flat<64, SP>(a, stream);
+    case 128: return run_skinny_flat<128, SP>(a, stream);
+    default: return run_skinny_flat<256, SP>(a, stream);
+  }
+}
+
+static bool skinny_flat_ok(const StepArgs &a) {
+  const bool pow2k = a.K >= 2 && a.K <= 256 && (a.K & (a.K - 1)) == 0;
+  return a.splits == 1 && a.R >= 4096 && pow2k && a.S >= 1 && a.S <= kSkinnyMax && ((uintptr_t)a.X & 15) == 0;
+}
+
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
+  if (skinny_flat_ok(a)) {
+    if (a.S <= 1) return run_skinny_flat_k<1>(a, stream);
+    if (a.S <= 2) return run_skinny_flat_k<2>(a, stream);
+    if (a.S <= 4) return run_skinny_flat_k<4>(a, stream);
+    if (a.S <= 8) return run_skinny_flat_k<8>(a, stream);
+    return run_skinny_flat_k<16>(a, stream);
+  }
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
   // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
