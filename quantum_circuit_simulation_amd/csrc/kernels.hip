@@ -86,6 +86,8 @@ __device__ __forceinline__ void store_c(T *p, T v, int beta) {
   *p = v;
 }
 
+__device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 // ---------------------------------------------------------------------------
 // device pointer table
 
@@ -131,16 +133,23 @@ __global__ void k_copy(const CopyDesc *descs, const void *const *ptab, const int
 // Tiled permuting copy: reads go along the source's smallest strides, writes
 // along the destination's innermost dims, with the tile transposed in LDS.
 // The per-entry offset tables are built on the host (they hold the index
-// arithmetic) and staged into LDS once per workgroup.
+// arithmetic) and staged into LDS once per workgroup.  Each pass moves NE
+// entries (as many whole tiles as fit), NE / 256 independent loads per
+// thread between two barriers, so many loads are in flight at once.
 constexpr int kTileMax = 1024;
 
-template <typename T>
+template <typename T, int NE>
 __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const void *const *ptab, const int64_t *ints,
                                                     SliceDigits sd, int32_t beta) {
-  __shared__ T buf[kTileMax];
+  constexpr int EPT = NE / 256;
+  constexpr int kMaxTilesPerPass = NE / 32;
+  constexpr bool kPairsPossible = sizeof(T) == 8;
+  __shared__ __align__(16) T buf[NE];
   __shared__ int64_t s_src[kTileMax];
   __shared__ int32_t s_lds[kTileMax];
   __shared__ int64_t s_dst[kTileMax];
+  __shared__ int64_t s_bs[kMaxTilesPerPass], s_bd[kMaxTilesPerPass];
+  __shared__ int s_pairs;
   const CopyDesc d = *desc;
   const int64_t *t = ints + d.ints_index;
   const int tile = (int)t[0];
@@ -153,39 +162,99 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
   const int64_t *ld_src = slc + sd.n;
   const int64_t *ld_lds = ld_src + tile;
   const int64_t *st_dst = ld_lds + tile;
-  for (int e = threadIdx.x; e < tile; e += blockDim.x) {
-    s_src[e] = ld_src[e];
-    s_lds[e] = (int32_t)ld_lds[e];
-    s_dst[e] = st_dst[e];
-  }
+  const int tid = threadIdx.x;
   int64_t base = d.src_off;
   for (int q = 0; q < sd.n; ++q) base += (int64_t)sd.digit[q] * slc[q];
   const T *src = (const T *)ptab[d.src_buf] + base;
   T *dst = (T *)ptab[d.dst_buf] + d.dst_off;
+  if (tid == 0) {
+    // 16-byte pairs: entries 2i, 2i+1 of the tile adjacent in both the
+    // source and the destination, every pair and every tile base 16-byte
+    // aligned (checked on the tables below)
+    int ok = kPairsPossible && (tile % 2) == 0 && aligned16(src) && aligned16(dst);
+    for (int q = 0; q < nout && ok; ++q) ok = (osrc[q] % 2) == 0 && (odst[q] % 2) == 0;
+    s_pairs = ok;
+  }
+  __syncthreads();
+  for (int e = tid; e < tile; e += blockDim.x) {
+    s_src[e] = ld_src[e];
+    s_lds[e] = (int32_t)ld_lds[e];
+    s_dst[e] = st_dst[e];
+    if ((e % 2) == 0 && e + 1 < tile &&
+        ((ld_src[e] % 2) != 0 || ld_src[e + 1] != ld_src[e] + 1 || (st_dst[e] % 2) != 0 ||
+         st_dst[e + 1] != st_dst[e] + 1))
+      s_pairs = 0;
+  }
   const int b = beta && d.is_root;
   const int64_t ntiles = d.count / tile;
+  const int ut = NE / tile;  // tiles per pass (tile >= 32)
   __syncthreads();
-  for (int64_t o = blockIdx.x; o < ntiles; o += gridDim.x) {
-    int64_t r = o, bs = 0, bd = 0;
-    if (pow2) {
-      for (int q = nout - 1; q >= 0; --q) {
-        const int64_t e = od[q];
-        bs += (r & (e - 1)) * osrc[q];
-        bd += (r & (e - 1)) * odst[q];
-        r >>= __builtin_ctzll((unsigned long long)e);
+  const bool pairs = s_pairs != 0;
+  for (int64_t o0 = (int64_t)blockIdx.x * ut; o0 < ntiles; o0 += (int64_t)gridDim.x * ut) {
+    if (tid < ut) {
+      int64_t r = o0 + tid, bs = 0, bd = 0;
+      if (pow2) {
+        for (int q = nout - 1; q >= 0; --q) {
+          const int64_t e = od[q];
+          bs += (r & (e - 1)) * osrc[q];
+          bd += (r & (e - 1)) * odst[q];
+          r >>= __builtin_ctzll((unsigned long long)e);
+        }
+      } else {
+        for (int q = nout - 1; q >= 0; --q) {
+          const int64_t e = od[q];
+          const int64_t dg = r % e;
+          r /= e;
+          bs += dg * osrc[q];
+          bd += dg * odst[q];
+        }
+      }
+      s_bs[tid] = bs;
+      s_bd[tid] = bd;
+    }
+    __syncthreads();
+    if (kPairsPossible && pairs) {
+#pragma unroll
+      for (int j = 0; j < EPT / 2; ++j) {
+        const int E = 2 * (tid + 256 * j);
+        const int u = E / tile, e = E - u * tile;
+        if (u < ut && o0 + u < ntiles) {
+          const float4 v = *(const float4 *)(src + s_bs[u] + s_src[e]);
+          float2 *bb = (float2 *)buf + u * tile;
+          bb[s_lds[e]] = make_float2(v.x, v.y);
+          bb[s_lds[e + 1]] = make_float2(v.z, v.w);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT / 2; ++j) {
+        const int E = 2 * (tid + 256 * j);
+        const int u = E / tile, e = E - u * tile;
+        if (u < ut && o0 + u < ntiles) {
+          float4 v = *(const float4 *)((float2 *)buf + E);
+          float4 *p = (float4 *)(dst + s_bd[u] + s_dst[e]);
+          if (b) {
+            const float4 o = *p;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *p = v;
+        }
       }
     } else {
-      for (int q = nout - 1; q >= 0; --q) {
-        const int64_t e = od[q];
-        const int64_t dg = r % e;
-        r /= e;
-        bs += dg * osrc[q];
-        bd += dg * odst[q];
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const int E = tid + 256 * j;
+        const int u = E / tile, e = E - u * tile;
+        if (u < ut && o0 + u < ntiles) buf[u * tile + s_lds[e]] = src[s_bs[u] + s_src[e]];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const int E = tid + 256 * j;
+        const int u = E / tile, e = E - u * tile;
+        if (u < ut && o0 + u < ntiles) store_c(dst + s_bd[u] + s_dst[e], buf[E], b);
       }
     }
-    for (int e = threadIdx.x; e < tile; e += blockDim.x) buf[s_lds[e]] = src[bs + s_src[e]];
-    __syncthreads();
-    for (int e = threadIdx.x; e < tile; e += blockDim.x) store_c(dst + bd + s_dst[e], buf[e], b);
     __syncthreads();
   }
 }
@@ -237,7 +306,6 @@ __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void 
 constexpr int kSkinnyMax = 16;
 
 __device__ __forceinline__ float2 ld_pair_lo(const float4 &v) { return make_float2(v.x, v.y); }
-__device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 __device__ __forceinline__ float2 ld_pair_hi(const float4 &v) { return make_float2(v.z, v.w); }
 
 // Few rows (R < 4096): one workgroup per (row, K chunk); all 256 threads
@@ -1358,16 +1426,18 @@ hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, 
 
 hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
                              const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream) {
-  // one workgroup per tile of >= 32 entries, at most 8192 workgroups
-  int64_t blocks = count / 32;
-  if (blocks > 8192) blocks = 8192;
+  // passes of 2048 (complex128: 1024) entries, grid-stride over at most
+  // 2048 workgroups; `count` here is the entry count of the copy
+  const int64_t per = z ? 1024 : 2048;
+  int64_t blocks = (count + per - 1) / per;
+  if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   if (z)
-    hipLaunchKernelGGL(k_copy_tiled<double2>, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits,
-                       beta);
+    hipLaunchKernelGGL((k_copy_tiled<double2, 1024>), dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints,
+                       digits, beta);
   else
-    hipLaunchKernelGGL(k_copy_tiled<float2>, dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints, digits,
-                       beta);
+    hipLaunchKernelGGL((k_copy_tiled<float2, 2048>), dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints,
+                       digits, beta);
   return hipGetLastError();
 }
 

@@ -257,3 +257,47 @@ def test_skinny_on_misaligned_views():
         ref = oracle.contract_network(net, tree)
         got, _ = run(net, tree, leaves_dev=dev)
         _assert_close(got, ref)
+
+
+@pytest.mark.parametrize("aligned", [True, False])
+def test_tiled_permute_pair_and_single_paths(aligned):
+    """The tiled permute moves 16-byte pairs when the innermost source and
+    destination dims have even extent and everything is 16-byte aligned, and
+    single entries otherwise (odd innermost extent, misaligned view)."""
+    import torch
+    from tests.gpu_util import run
+    rng = np.random.default_rng(31 + aligned)
+    for ext, perm in [([2] * 20, list(rng.permutation(20))), ([4, 8, 2, 16, 32, 8], [5, 3, 0, 4, 1, 2]),
+                      ([3, 5, 7, 9, 11, 13], [1, 3, 5, 0, 2, 4]), ([2] * 10 + [3] * 6, list(rng.permutation(16)))]:
+        perm = [int(x) for x in perm]
+        d = sweep.complex_gaussian(rng, tuple(ext))
+        net = Network(np.array(ext, dtype=np.int64), [list(range(len(ext)))], perm, [d], name=f"permute{ext}")
+        dev = torch.from_numpy(d.reshape(-1)).cuda()
+        if not aligned:
+            buf = torch.zeros(d.size + 1, dtype=torch.complex64, device="cuda")
+            buf[1:] = dev
+            dev = buf[1:]
+        print(f"[gpu] tiled permute {ext} {perm} aligned={aligned}", flush=True)
+        got, _ = run(net, Tree([], []), leaves_dev=[dev])
+        assert np.array_equal(got, np.transpose(d, perm).astype(np.complex128))
+
+
+@pytest.mark.parametrize("ext_sliced", [2, 3])
+def test_naive_sliced_root_permute_accumulates(ext_sliced):
+    """Naive order permutes the root after every slice: the tiled permute's
+    accumulate path (beta = 1 after the first slice)."""
+    rng = np.random.default_rng(61 + ext_sliced)
+    M, N, K = list(range(9)), list(range(9, 17)), [17, 18]
+    x = 19
+    extents = np.array([2] * 19 + [ext_sliced], dtype=np.int64)
+    A = [M[i] for i in rng.permutation(len(M))] + K + [x]
+    B = [x] + N + K
+    out = [int(v) for v in rng.permutation(M + N)]
+    data = [sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in A)),
+            sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in B))]
+    net = Network(extents, [A, B], out, data, name="naive-sliced-root")
+    tree = Tree([0], [1])
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, order=1, sliced=[x])
+    assert plan.stats()["root_permute"] == 1
+    _assert_close(got, ref)
