@@ -379,6 +379,83 @@ class TreeWorkload:
             del ws
         return res
 
+    def _step_plan(self, s, fixed=()):
+        """Step s of the tree alone (its planned operand and product orders),
+        with the modes in `fixed` held at one value (extent 1)."""
+        import quantum_circuit_simulation_amd as qa
+        nd = self.plan.node(s)
+        oa, ob, oc = (self.plan.tensor_order(nd[k]) for k in ("lhs", "rhs", "out"))
+        label = {x: i for i, x in enumerate(dict.fromkeys(oa + ob + oc))}
+        ext = [1 if x in fixed else int(self.net.extents[x]) for x in label]
+        return qa.Plan(ext, [[label[x] for x in oa], [label[x] for x in ob]], [label[x] for x in oc], [0], [1])
+
+    def _time_plan(self, plan, pool):
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        ra = int(np.prod(plan.leaf_shapes[0], dtype=np.int64)) if plan.leaf_shapes[0] else 1
+        rb = int(np.prod(plan.leaf_shapes[1], dtype=np.int64)) if plan.leaf_shapes[1] else 1
+        rc = int(np.prod(plan.out_shape, dtype=np.int64)) if plan.out_shape else 1
+        out = torch.empty(rc, dtype=torch.complex64, device="cuda")
+        ws = qa.alloc_workspace(plan)
+        args = ([pool[:ra], pool[:rb]], out, ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        plan.execute(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        if ms < 100:
+            e0.record()
+            plan.execute(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+        del out, ws
+        return ms
+
+    def distribution(self, P, threshold, t1_ms):
+        """The distribution schedule of this tree over P GPUs
+        (tnc_plan_distribute with MI355X / xGMI constants) and, on this one
+        GPU, every split step run at full size and at one GPU's local shape
+        (its split modes fixed; times local_count sub-GEMMs).  Projected time
+        on P GPUs = measured one-GPU tree time - those full steps + their
+        local GEMMs + the modeled communication."""
+        import torch
+        from collections import Counter
+        steps, model_total = self.plan.distribute(num_gpus=P, threshold_bytes=threshold)
+        self.ws = None
+        torch.cuda.empty_cache()
+        split = [s for s, st in enumerate(steps) if st["tag_name"] != "replicated"]
+        biggest = 1
+        for s in split:
+            nd = self.plan.node(s)
+            biggest = max(biggest, nd["m"] * nd["k"], nd["n"] * nd["k"])
+        pool = torch.empty(biggest, dtype=torch.complex64, device="cuda")
+        fill_gaussian(pool, 77)
+        full_ms = local_ms = comm_ms = model_gemm_ms = 0.0
+        rows = []
+        for s in split:
+            st = steps[s]
+            f = self._time_plan(self._step_plan(s), pool)
+            l = self._time_plan(self._step_plan(s, set(st["local_modes"])), pool) * st["local_count"]
+            full_ms += f
+            local_ms += l
+            comm_ms += 1e3 * st["t_comm"]
+            model_gemm_ms += 1e3 * st["t_gemm"]
+            rows.append({"step": s, "tag": st["tag_name"], "local_mnk": [st["local_m"], st["local_n"], st["local_k"]],
+                         "count": st["local_count"], "full_ms": round(f, 3), "local_ms": round(l, 3),
+                         "model_local_ms": round(1e3 * st["t_gemm"], 3), "model_comm_ms": round(1e3 * st["t_comm"], 3)})
+            log(f"dist step {s} {st['tag_name']}: full {f:.2f} ms, local {l:.2f} ms (model {1e3 * st['t_gemm']:.2f}), "
+                f"comm {1e3 * st['t_comm']:.2f} ms")
+        del pool
+        projected = t1_ms - full_ms + local_ms + comm_ms
+        return {"gpus": P, "threshold_bytes": threshold, "tags": dict(Counter(st["tag_name"] for st in steps)),
+                "split_steps": len(split), "one_gpu_ms": round(t1_ms, 3), "split_steps_full_ms": round(full_ms, 3),
+                "split_steps_local_ms": round(local_ms, 3), "model_local_ms": round(model_gemm_ms, 3),
+                "comm_ms": round(comm_ms, 3), "projected_ms": round(projected, 3),
+                "projected_speedup": round(t1_ms / projected, 3), "model_total_ms": round(1e3 * model_total, 3),
+                "steps": rows}
+
     def kernel_of(self, idx):
         return "whole tree"
 
@@ -507,6 +584,10 @@ def main():
                                                  "e.g. 2,3,4")
     ap.add_argument("--dtype", default="c64", choices=["c64", "c128"],
                     help="sweep workload: entry type (c128 runs the FP64 matrix-core path)")
+    ap.add_argument("--distribute", type=int, default=0,
+                    help="tree workloads: distribution schedule over this many GPUs, with every split step's "
+                         "local GEMM timed on this GPU at its real shape")
+    ap.add_argument("--dist-threshold", type=int, default=8 << 30, help="split tensors above this many bytes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cases", default="", help="comma-separated sweep case indices (default: all feasible)")
     ap.add_argument("--report", default="", help="write per-launch timings here (JSON)")
@@ -630,6 +711,10 @@ def main():
     if args.slices:
         slicing = wl.slicing(max(1, args.steps), [int(x) for x in args.slices.split(",")])
 
+    distribution = None
+    if args.distribute:
+        distribution = wl.distribution(args.distribute, args.dist_threshold, ms_per_step)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -644,6 +729,7 @@ def main():
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
             **({"ablation": ablation} if ablation is not None else {}),
             **({"slicing": slicing} if slicing is not None else {}),
+            **({"distribution": distribution} if distribution is not None else {}),
             "host_wall_s": round(wall, 3)}
     print(json.dumps(line), flush=True)
 

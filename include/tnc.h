@@ -189,6 +189,79 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
 tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
                        uint64_t workspace_bytes, void *stream);
 
+/*
+ * Distribution schedule over P GPUs (host only; launches nothing).
+ *
+ * "Parallelizing Large-Scale Tensor Network Contraction on Multiple GPUs",
+ * section 1.5: an intermediate larger than a threshold (8 GiB on the page)
+ * is split over P GPUs on the shortest prefix of its lifetime order whose
+ * extents multiply to at least P, so each GPU holds one contiguous block;
+ * every step is tagged Activate, Keep, Redistribute or Gather.  Section 1.6:
+ * along each chain of split tensors a one-dimensional dynamic program picks,
+ * before every step, keeping the current split (allowed while none of its
+ * modes is reduced by the step) or an All-to-All re-split onto the fresh
+ * prefix of the tensor's order that avoids the step's reduced modes, under
+ * the cost t = t_gemm + t_comm:
+ *   t_gemm = count * max(bytes / B_dev, 8 m n k / F_dev) for the GPU's
+ *            sub-GEMMs (m, n, k), bytes = entry size * (mk + nk + mn);
+ *   t_comm = V / B_net + lambda * n_blk, V the bytes one GPU sends and
+ *            n_blk the contiguous blocks they fall into (a re-split moves
+ *            P - 1 pieces of |T| / P^2; blocks end where the new split modes
+ *            cut the shard's layout).
+ * The page's formulas are stripped; these are readings of its words.  The
+ * remaining rules are this library's: leaves stay replicated; a step whose
+ * operands are both split gathers the smaller one (all-gather); a small
+ * output (or the root) of a split operand is all-gathered, or all-reduced
+ * when split modes were reduced (partial sums).  Ties in the program keep
+ * the earlier choice; any optimal schedule is correct.
+ */
+typedef enum {
+  TNC_DIST_REPLICATED = 0,   /* replicated operands, output not split: every GPU runs the whole step */
+  TNC_DIST_ACTIVATE = 1,     /* replicated operands, output above the threshold: each GPU computes its block */
+  TNC_DIST_KEEP = 2,         /* the split operand keeps its split; local GEMM, no communication */
+  TNC_DIST_REDISTRIBUTE = 3, /* the split operand is re-split (All-to-All) before the local GEMM */
+  TNC_DIST_GATHER = 4        /* output not split: gathered (or all-reduced) after the local GEMM */
+} tnc_dist_tag;
+
+typedef struct {
+  int32_t num_gpus;          /* P, 1 .. 65536 (1: nothing is split) */
+  uint64_t threshold_bytes;  /* step outputs above this many bytes are split */
+  double hbm_bytes_per_s;    /* B_dev, > 0 */
+  double flops_per_s;        /* F_dev (matrix peak for the plan's dtype), > 0 */
+  double net_bytes_per_s;    /* B_net: bytes per second one GPU sends to its peers, > 0 */
+  double latency_s;          /* lambda: cost of one message block, >= 0 */
+} tnc_dist_options;
+
+typedef struct {
+  int32_t tag;               /* tnc_dist_tag */
+  int32_t dist_operand;      /* 0 lhs or 1 rhs: the split operand the step continues; -1 none */
+  int32_t gathered_operand;  /* 0 or 1: a second split operand all-gathered before the step; -1 none */
+  int32_t num_dist;          /* modes the output is split on (0: not split) */
+  int32_t dist_modes[16];    /* those modes, in the output's planned order */
+  int32_t num_local;         /* modes the local GEMM is split on (the operand's split after any */
+  int32_t local_modes[16];   /*   re-split, or the activated output's split); one GPU runs the step */
+                             /*   with these fixed, local_count times (0: whole step) */
+  int64_t local_m;           /* one GPU's sub-GEMM: lhs-side extent, */
+  int64_t local_n;           /*   rhs-side extent, */
+  int64_t local_k;           /*   reduced extent, */
+  int64_t local_count;       /*   and how many such sub-GEMMs it runs */
+  double t_gemm;             /* seconds of local GEMM (cost model) */
+  double t_comm;             /* seconds of communication charged to this step */
+} tnc_dist_step;
+
+/* MI355X defaults for an 8-GPU node: P = 8, threshold 8 GiB, B_dev 8 TB/s,
+ * F_dev 157.3 TFLOP/s (C64) or 78.6 (C128), B_net 537.6 GB/s (7 xGMI links
+ * of 76.8 GB/s per direction), lambda 5 us.  Errors: INVALID_ARG. */
+tnc_status tnc_dist_options_default(tnc_dist_options *opts, tnc_dtype dtype);
+
+/* Compute the schedule of `plan` (its unsliced tree).  steps[num_steps] is
+ * caller-owned and fully written; *total_s = sum of t_gemm + t_comm.
+ * Errors: INVALID_ARG (NULL, options out of range), UNSUPPORTED (a chain
+ * with no feasible split, e.g. a split tensor whose surviving modes cannot
+ * be cut P ways); outputs are untouched on error. */
+tnc_status tnc_plan_distribute(tnc_plan_t plan, const tnc_dist_options *opts, tnc_dist_step *steps,
+                               double *total_s);
+
 /* Static text for a status code. */
 const char *tnc_status_string(tnc_status status);
 

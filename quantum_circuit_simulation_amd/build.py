@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtnc.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["plan.cpp", "abi.cpp", "kernels.hip"]
+SOURCES = ["plan.cpp", "dist.cpp", "abi.cpp", "kernels.hip"]
 ARCH = os.environ.get("TNC_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -259,6 +260,42 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
       if (st != TNC_OK) return st;
     }
   }
+  return TNC_OK;
+}
+
+tnc_status tnc_dist_options_default(tnc_dist_options *o, tnc_dtype dtype) {
+  if (!o || (dtype != TNC_C64 && dtype != TNC_C128)) return TNC_ERR_INVALID_ARG;
+  o->num_gpus = 8;
+  o->threshold_bytes = uint64_t(8) << 30;
+  o->hbm_bytes_per_s = 8.0e12;
+  o->flops_per_s = dtype == TNC_C128 ? 78.6e12 : 157.3e12;
+  o->net_bytes_per_s = 7 * 76.8e9;
+  o->latency_s = 5e-6;
+  return TNC_OK;
+}
+
+tnc_status tnc_plan_distribute(tnc_plan_t plan, const tnc_dist_options *o, tnc_dist_step *steps, double *total) {
+  g_last_error.clear();
+  if (!plan || !o || (!steps && plan->impl.S > 0) || !total) return TNC_ERR_INVALID_ARG;
+  if (o->num_gpus < 1 || o->num_gpus > 65536 || !(o->hbm_bytes_per_s > 0) || !(o->flops_per_s > 0) ||
+      !(o->net_bytes_per_s > 0) || !(o->latency_s >= 0))
+    return TNC_ERR_INVALID_ARG;
+  const auto &p = plan->impl;
+  std::vector<tnc_dist_step> tmp(p.S);
+  double tot = 0;
+  std::string err;
+  tnc_status st;
+  try {
+    st = tnc::plan_distribution(p, *o, tmp.data(), &tot, &err);
+  } catch (const std::bad_alloc &) {
+    return TNC_ERR_OUT_OF_MEMORY;
+  }
+  if (st != TNC_OK) {
+    g_last_error = err;
+    return st;
+  }
+  for (int32_t s = 0; s < p.S; ++s) steps[s] = tmp[s];
+  *total = tot;
   return TNC_OK;
 }
 

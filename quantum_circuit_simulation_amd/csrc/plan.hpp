@@ -118,4 +118,8 @@ struct PlanImpl {
 tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
                       PlanImpl *p);
 
+// Distribution schedule over P GPUs (dist.cpp); `steps` holds p.S records.
+tnc_status plan_distribution(const PlanImpl &p, const tnc_dist_options &o, tnc_dist_step *steps, double *total,
+                             std::string *err);
+
 }  // namespace tnc

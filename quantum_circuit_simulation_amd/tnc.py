@@ -80,9 +80,32 @@ class NodeInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class DistOptions(ctypes.Structure):
+    _fields_ = [("num_gpus", ctypes.c_int32), ("threshold_bytes", ctypes.c_uint64),
+                ("hbm_bytes_per_s", ctypes.c_double), ("flops_per_s", ctypes.c_double),
+                ("net_bytes_per_s", ctypes.c_double), ("latency_s", ctypes.c_double)]
+
+
+class DistStep(ctypes.Structure):
+    _fields_ = [("tag", ctypes.c_int32), ("dist_operand", ctypes.c_int32), ("gathered_operand", ctypes.c_int32),
+                ("num_dist", ctypes.c_int32), ("dist_modes", ctypes.c_int32 * 16), ("num_local", ctypes.c_int32),
+                ("local_modes", ctypes.c_int32 * 16), ("local_m", ctypes.c_int64),
+                ("local_n", ctypes.c_int64), ("local_k", ctypes.c_int64), ("local_count", ctypes.c_int64),
+                ("t_gemm", ctypes.c_double), ("t_comm", ctypes.c_double)]
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name not in ("dist_modes", "local_modes")}
+        d["dist_modes"] = [int(self.dist_modes[i]) for i in range(self.num_dist)]
+        d["local_modes"] = [int(self.local_modes[i]) for i in range(self.num_local)]
+        return d
+
+
+DIST_TAGS = ["replicated", "activate", "keep", "redistribute", "gather"]
+
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
-           "tnc_execute", "tnc_status_string", "tnc_last_error"]
+           "tnc_execute", "tnc_status_string", "tnc_last_error", "tnc_dist_options_default",
+           "tnc_plan_distribute"]
 
 _lib = None
 
@@ -124,6 +147,10 @@ def load_library(path: str = LIB_PATH):
     lib.tnc_status_string.restype = ctypes.c_char_p
     lib.tnc_last_error.argtypes = []
     lib.tnc_last_error.restype = ctypes.c_char_p
+    lib.tnc_dist_options_default.argtypes = [P(DistOptions), ctypes.c_int]
+    lib.tnc_dist_options_default.restype = ctypes.c_int
+    lib.tnc_plan_distribute.argtypes = [ctypes.c_void_p, P(DistOptions), P(DistStep), P(ctypes.c_double)]
+    lib.tnc_plan_distribute.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -181,6 +208,7 @@ class Plan:
         _check(lib.tnc_plan(ctypes.byref(net), ctypes.byref(tree), ctypes.byref(opts), ctypes.byref(h)), "tnc_plan")
         self._h = h
         self.out_shape = tuple(int(extents[x]) for x in out_modes)
+        self.leaf_shapes = [tuple(int(extents[x]) for x in l) for l in leaves]
 
     @classmethod
     def from_network(cls, net, tree, **kw) -> "Plan":
@@ -222,6 +250,28 @@ class Plan:
         n = NodeInfo()
         _check(self._lib.tnc_plan_node(self._h, step, ctypes.byref(n)), "tnc_plan_node")
         return n.as_dict()
+
+    def distribute(self, **overrides):
+        """Distribution schedule over P GPUs (tnc_plan_distribute).  Keyword
+        overrides of the MI355X defaults: num_gpus, threshold_bytes,
+        hbm_bytes_per_s, flops_per_s, net_bytes_per_s, latency_s.  Returns
+        (list of per-step dicts with a "tag_name", total seconds)."""
+        o = DistOptions()
+        _check(self._lib.tnc_dist_options_default(ctypes.byref(o), self.dtype), "tnc_dist_options_default")
+        for k, v in overrides.items():
+            if not hasattr(o, k):
+                raise TypeError(f"unknown distribution option {k}")
+            setattr(o, k, v)
+        steps = (DistStep * max(1, self.num_steps))()
+        tot = ctypes.c_double()
+        _check(self._lib.tnc_plan_distribute(self._h, ctypes.byref(o), steps, ctypes.byref(tot)),
+               "tnc_plan_distribute")
+        out = []
+        for i in range(self.num_steps):
+            d = steps[i].as_dict()
+            d["tag_name"] = DIST_TAGS[d["tag"]]
+            out.append(d)
+        return out, float(tot.value)
 
     def execute_ptrs(self, leaf_ptrs: Sequence[int], out_ptr: int, ws_ptr: int, ws_bytes: int, stream: int = 0):
         """Raw-pointer form: device addresses as Python ints."""
