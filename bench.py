@@ -292,6 +292,11 @@ class TreeWorkload:
                            "tree": "best of 200 seeded randomized-greedy trees (seed 1)",
                            "note": "largest fSim grid instance whose in-house tree fits one GPU unsliced; "
                                    "7x8 depth 16 reaches width 2^59 with this search"}
+        elif which == "hexagonal":
+            from workloads import hexagonal
+            net = hexagonal.honeycomb(16, 16, 8, 606)
+            tree = hexagonal.honeycomb_tree(16, 16)
+            self.config = {"workload": "honeycomb-16x16-D8", "seed": 606, "tree": "row-major caterpillar"}
         elif which == "brickwork30":
             net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
             tree = trees.greedy_tree(net)
@@ -325,6 +330,16 @@ class TreeWorkload:
         res = {}
         for name, order in (("lifetime", 0), ("naive", 1)):
             plan = qa.Plan.from_network(self.net, self.tree, order=order)
+            st = plan.stats()
+            free, _ = torch.cuda.mem_get_info()
+            if st["workspace_bytes"] > free - (1 << 30):
+                # the re-laid copies need more memory than the GPU has left
+                res[name + "_ms"] = None
+                res[name + "_relayouts"] = st["relayouts"] + st["root_permute"]
+                res[name + "_workspace_bytes"] = st["workspace_bytes"]
+                res[name + "_note"] = f"workspace {st['workspace_bytes'] / 2**30:.0f} GiB does not fit in HBM"
+                log(f"ablation {name}: {res[name + '_note']}")
+                continue
             ws = qa.alloc_workspace(plan)
             plan.execute(self.leaves, self.out, ws)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -338,7 +353,8 @@ class TreeWorkload:
             res[name + "_relayouts"] = st["relayouts"] + st["root_permute"]
             res[name + "_workspace_bytes"] = st["workspace_bytes"]
             del ws
-        res["naive_over_lifetime"] = res["naive_ms"] / res["lifetime_ms"]
+        res["naive_over_lifetime"] = (res["naive_ms"] / res["lifetime_ms"]
+                                      if res["naive_ms"] is not None and res["lifetime_ms"] else None)
         return res, []
 
     def slicing(self, steps, s_list):
@@ -579,7 +595,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal"])
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
     ap.add_argument("--dtype", default="c64", choices=["c64", "c128"],

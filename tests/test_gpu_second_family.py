@@ -1,0 +1,77 @@
+"""GPU parity on the second workload family: honeycomb-lattice networks
+(random sites against the oracle; all-ones sites at the full 16 x 16, D = 8
+bench size against their closed form) and Ising partition functions on
+random 3-regular graphs and rings.  Tolerance as for every complex64 path:
+|g - r| <= 1e-4 * |r| (scalars)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import rel_err_ok
+from workloads import hexagonal as H
+from workloads import trees
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _run(net, tree, **kw):
+    from tests.gpu_util import run
+    print(f"[gpu] {net.name} kw={kw}", flush=True)
+    return run(net, tree, **kw)
+
+
+@pytest.mark.parametrize("rows,cols,D,seed", [(8, 8, 8, 1), (12, 12, 8, 2), (10, 14, 4, 3)])
+def test_honeycomb_random_matches_oracle(rows, cols, D, seed):
+    net = H.honeycomb(rows, cols, D, seed)
+    tree = H.honeycomb_tree(rows, cols)
+    ref = oracle.contract_network(net, tree)
+    got, _ = _run(net, tree)
+    ok, err = rel_err_ok(got, ref, TOL)
+    assert ok, err
+
+
+def test_honeycomb_full_size_all_ones_closed_form():
+    """16 x 16, D = 8 (width 2^30): all-ones sites halved, so Z is the
+    product of the stored site scales times 8^bonds (close to 1)."""
+    net = H.honeycomb(16, 16, 8, 0, fill=lambda i, j, shape, rng: np.full(shape, 0.5, np.float32))
+    log2z = sum(math.log2(float(np.asarray(d).reshape(-1)[0].real)) for d in net.data) + 3.0 * net.meta["bonds"]
+    expect = 2.0 ** log2z
+    got, plan = _run(net, H.honeycomb_tree(16, 16))
+    assert plan.stats()["max_intermediate"] == 1 << 30
+    assert abs(got.reshape(-1)[0] - expect) <= TOL * abs(expect)
+
+
+@pytest.mark.parametrize("n,seed", [(80, 11), (120, 12)])
+def test_ising_random_regular_matches_oracle(n, seed):
+    edges = H.random_regular_graph(n, 3, seed)
+    net = H.ising(n, edges, 0.4, seed=seed)
+    tree = trees.search_tree(net, trials=50, seed=1)
+    ref = oracle.contract_network(net, tree)
+    got, _ = _run(net, tree)
+    ok, err = rel_err_ok(got, ref, TOL)
+    assert ok, err
+    sl = trees.choose_slices(net, tree, 3)
+    got, _ = _run(net, tree, sliced=sl)
+    ok, err = rel_err_ok(got, ref, TOL)
+    assert ok, err
+
+
+def test_ising_ring_closed_form():
+    n, beta = 100, 0.2
+    edges = [(i, i + 1) for i in range(n - 1)] + [(0, n - 1)]
+    net = H.ising(n, edges, beta)
+    got, _ = _run(net, trees.greedy_tree(net))
+    expect = (2 * math.cosh(beta)) ** n + (2 * math.sinh(beta)) ** n
+    assert abs(got.reshape(-1)[0] - expect) <= TOL * expect
