@@ -282,12 +282,12 @@ def _runs(c_order, ext, row_set):
 
 def _split_rule(cls, R, S, k):
     """K split count: enough workgroups to fill the chip, K chunks of at
-    least 256 (GEMM) / 1024 (skinny) entries."""
+    least 64 (GEMM) / 1024 (skinny) entries."""
     if cls == CLASS_GEMM:
         tiles = _ceil_div(R, GEMM_NOMINAL_TILE) * _ceil_div(S, GEMM_NOMINAL_TILE)
-        if tiles >= 256 or k < 512:
+        if tiles >= 256 or k < 128:
             return 1
-        return max(1, min(_pow2_floor(512 // tiles), _pow2_floor(k // 256)))
+        return max(1, min(_pow2_floor(512 // tiles), _pow2_floor(k // 64)))
     if cls == CLASS_SKINNY:
         blocks = _ceil_div(R, 256)
         if blocks >= 512 or k < 2048:

@@ -82,11 +82,11 @@ class Arena {
 };
 
 int32_t split_rule(int32_t cls, int64_t R, int64_t S, int64_t k) {
-  // enough workgroups to fill the chip; K chunks of >= 256 (GEMM) / 1024 (skinny)
+  // enough workgroups to fill the chip; K chunks of >= 64 (GEMM) / 1024 (skinny)
   if (cls == TNC_CLASS_GEMM) {
     int64_t tiles = ceil_div(R, kGemmNominalTile) * ceil_div(S, kGemmNominalTile);
-    if (tiles >= 256 || k < 512) return 1;
-    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(512 / tiles), pow2_floor(k / 256)));
+    if (tiles >= 256 || k < 128) return 1;
+    return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(512 / tiles), pow2_floor(k / 64)));
   }
   if (cls == TNC_CLASS_SKINNY) {
     int64_t blocks = ceil_div(R, 256);
