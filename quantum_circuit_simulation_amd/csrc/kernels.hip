@@ -896,8 +896,36 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
   }
 
   float2 ra[A_PER], rb[B_PER];
+  // 16-byte loads of entry pairs (l, l + 1) and 8-byte LDS writes when K is
+  // even (every K chunk then starts and ends on an even entry) and both
+  // operands are 16-byte aligned; single entries otherwise
+  constexpr bool kPairable = (A_PER % 2 == 0) && (B_PER % 2 == 0);
+  const bool pairs = kPairable && (a.K % 2 == 0) && aligned16(a.X) && aligned16(a.Y);
   auto gload = [&](int32_t r0, int32_t c0, int32_t kt) {
     const int32_t kb = k0 + kt * BK;
+    if (kPairable && pairs) {
+#pragma unroll
+      for (int q = 0; q < A_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+        const int32_t gi = r0 + row, gl = kb + l;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gi < R && gl < k1) v = *(const float4 *)(a.X + (int64_t)gi * K + gl);
+        ra[2 * q] = make_float2(v.x, v.y);
+        ra[2 * q + 1] = make_float2(v.z, v.w);
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
+        const int32_t gj = c0 + col, gl = kb + l;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gj < S && gl < k1) v = *(const float4 *)(a.Y + (int64_t)gj * K + gl);
+        rb[2 * q] = make_float2(v.x, v.y);
+        rb[2 * q + 1] = make_float2(v.z, v.w);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
@@ -914,6 +942,23 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     }
   };
   auto lstore = [&](int st) {
+    if (kPairable && pairs) {
+#pragma unroll
+      for (int q = 0; q < A_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+        *(float2 *)&As[st][0][row][l] = make_float2(ra[2 * q].x, ra[2 * q + 1].x);
+        *(float2 *)&As[st][1][row][l] = make_float2(ra[2 * q].y, ra[2 * q + 1].y);
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
+        *(float2 *)&Bs[st][0][col][l] = make_float2(rb[2 * q].x, rb[2 * q + 1].x);
+        *(float2 *)&Bs[st][1][col][l] = make_float2(rb[2 * q].y, rb[2 * q + 1].y);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
@@ -1037,8 +1082,38 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     }
 
   float2 ra[A_PER], rb[B_PER];
+  // 16-byte loads of entry pairs (l, l + 1) and 8-byte LDS writes when K is
+  // even (every K chunk then starts and ends on an even entry) and both
+  // operands are 16-byte aligned; single entries otherwise
+  // (off here: the pair path lifts this kernel past 256 VGPRs, and the
+  // 64x256 / 256x64 tiles then spill)
+  constexpr bool kPairable = false;
+  const bool pairs = false;
   auto gload = [&](int64_t kt) {
     const int64_t kb = k0 + kt * BK;
+    if (kPairable && pairs) {
+#pragma unroll
+      for (int q = 0; q < A_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+        const int64_t gi = r0 + row, gl = kb + l;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gi < R && gl < k1) v = *(const float4 *)(a.X + gi * K + gl);
+        ra[2 * q] = make_float2(v.x, v.y);
+        ra[2 * q + 1] = make_float2(v.z, v.w);
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
+        const int64_t gj = c0 + col, gl = kb + l;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gj < S && gl < k1) v = *(const float4 *)(a.Y + gj * K + gl);
+        rb[2 * q] = make_float2(v.x, v.y);
+        rb[2 * q + 1] = make_float2(v.z, v.w);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
@@ -1055,6 +1130,23 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     }
   };
   auto lstore = [&](int st) {
+    if (kPairable && pairs) {
+#pragma unroll
+      for (int q = 0; q < A_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+        *(float2 *)&As[st][0][row][l] = make_float2(ra[2 * q].x, ra[2 * q + 1].x);
+        *(float2 *)&As[st][1][row][l] = make_float2(ra[2 * q].y, ra[2 * q + 1].y);
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER / 2; ++q) {
+        const int p = tid + 256 * q;
+        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
+        *(float2 *)&Bs[st][0][col][l] = make_float2(rb[2 * q].x, rb[2 * q + 1].x);
+        *(float2 *)&Bs[st][1][col][l] = make_float2(rb[2 * q].y, rb[2 * q + 1].y);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
