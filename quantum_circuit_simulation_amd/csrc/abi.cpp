@@ -2,6 +2,7 @@
 // executor that turns a plan's launch program into kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -205,7 +206,8 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
       r /= p.slice_extents[t];
     }
     const int32_t beta = sigma > 0 ? 1 : 0;
-    for (const tnc::Op &op : p.program) {
+    for (size_t oi = 0; oi < p.program.size(); ++oi) {
+      const tnc::Op &op = p.program[oi];
       hipError_t e = hipSuccess;
       switch (op.kind) {
         case tnc::OP_COPY:

@@ -262,16 +262,31 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
 // ---------------------------------------------------------------------------
 // grouped tiny steps: one workgroup per step
 
+constexpr int tiny_stage_entries(int bytes) { return bytes == 8 ? 4096 : 2048; }
+
+// One member of a tiny group, computed by one workgroup.  Both operands of a
+// member whose (R + S) K entries fit are first copied into LDS with
+// coalesced loads (one round trip), so the passes below read LDS instead of
+// waiting on a global load per pass.  Ends with a barrier, so `stage` may be
+// reused by the next member.
 template <typename T>
-__global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
-                                              int32_t beta) {
-  const TinyDesc d = descs[blockIdx.x];
+__device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const *ptab, const RunDev *runs,
+                                            int32_t beta, T *stage) {
+  constexpr int kStage = tiny_stage_entries(sizeof(T));
   const T *X = (const T *)ptab[d.x_buf] + d.x_off;
   const T *Y = (const T *)ptab[d.y_buf] + d.y_off;
   T *C = (T *)ptab[d.c_buf] + d.c_off;
   const RunDev *rr = runs + d.runs_index;
   const RunDev *cr = rr + d.nrr;
   const int R = d.R, S = d.S, K = d.K;
+  if ((int64_t)(R + S) * K <= kStage) {
+    const int nx = R * K, ny = S * K;
+    for (int e = threadIdx.x; e < nx; e += 256) stage[e] = X[e];
+    for (int e = threadIdx.x; e < ny; e += 256) stage[nx + e] = Y[e];
+    __syncthreads();
+    X = stage;
+    Y = stage + nx;
+  }
   const int outputs = R * S;
   // lanes per output: a power of two <= 64 that keeps the workgroup busy
   int G = 1;
@@ -298,6 +313,14 @@ __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void 
       store_c(C + run_offset(i, rr, d.nrr) + run_offset(j, cr, d.ncr), acc, b);
     }
   }
+  __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
+                                              int32_t beta) {
+  __shared__ T stage[tiny_stage_entries(sizeof(T))];
+  tiny_member<T>(descs[blockIdx.x], ptab, runs, beta, stage);
 }
 
 // ---------------------------------------------------------------------------
