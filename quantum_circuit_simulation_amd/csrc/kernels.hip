@@ -887,7 +887,43 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     for (int t = tid; t < BM; t += 256) rowoff[par][t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
     for (int t = tid; t < BN; t += 256) coloff[par][t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
   };
+  // Paired stores: lanes 2t and 2t + 1 hold columns c and c + 1 of the same
+  // rows; they swap one value (DPP quad_perm [1,0,3,2]) so that the even lane
+  // writes row q and the odd lane row q + 1, each as one 16-byte pair.  Needs
+  // C's innermost run (a column mode) of even extent and unit stride, and C
+  // 16-byte aligned; every row and column offset is then even.
+  const bool pair_store = !partial && a.ncr > 0 && a.runs[a.nrr + a.ncr - 1].stride == 1 &&
+                          (a.runs[a.nrr + a.ncr - 1].size % 2) == 0 && aligned16(a.C);
+  const bool odd_lane = (l32 & 1) != 0;
   auto epilogue = [&](int par, int32_t r0, int32_t c0) {
+    if (pair_store) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col0 = wc * WN + nb * 32 + (l32 & ~1);
+          const int32_t gj0 = c0 + col0;
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const int q = wr * WM + mb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+            const float sr = odd_lane ? accR[mb][nb][r] : accR[mb][nb][r + 1];
+            const float si = odd_lane ? accI[mb][nb][r] : accI[mb][nb][r + 1];
+            const float pr = dpp_f<0xB1>(sr), pi = dpp_f<0xB1>(si);
+            const int row = odd_lane ? q + 1 : q;
+            float4 v = odd_lane ? make_float4(pr, pi, accR[mb][nb][r + 1], accI[mb][nb][r + 1])
+                                : make_float4(accR[mb][nb][r], accI[mb][nb][r], pr, pi);
+            if (r0 + row < R && gj0 < S) {
+              float4 *p = (float4 *)(a.C + rowoff[par][row] + coloff[par][col0]);
+              if (a.beta) {
+                const float4 o = *p;
+                v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+              }
+              *p = v;
+            }
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
