@@ -522,8 +522,16 @@ CALIB_ENTRIES = 1 << 27
 
 
 def kernel_source_digest():
+    """SHA-256 of kernels.hip with // comments and blank lines removed, so
+    that only code changes void a stored traffic measurement."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    import re
+    lines = []
+    for line in open(KERNEL_SRC, encoding="utf-8"):
+        code = re.sub(r"//.*$", "", line).rstrip()
+        if code.strip():
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def _short_kernel(name):

@@ -1,19 +1,25 @@
-// gfx950 kernels for tree contraction (complex64 data, FP32 arithmetic).
+// gfx950 kernels for tree contraction: complex64 data on FP32 arithmetic
+// (FP32 MFMA), complex128 data on FP64 arithmetic (FP64 MFMA).
 //
 // Every pairwise step of the page "Parallelizing Large-Scale Tensor Network
 // Contraction on Multiple GPUs" (section 1.1) is, after lifetime ordering
 // (section 1.4), C[i, j] = sum_l X[i, l] * Y[j, l] with both operands stored
-// K-innermost.  Three kernels cover the step shapes:
-//   k_cgemm   - MFMA tiles (v_mfma_f32_32x32x2_f32) for steps with both
-//               sides > 16; the complex product is a real GEMM of shape
-//               (R, 2S, 2K) whose second operand is expanded on the fly;
-//   k_skinny  - VALU streaming for steps with one side <= 16 (HBM-bound);
+// K-innermost.  Kernels by step shape:
+//   k_cgemm, k_cgemm_tile - MFMA tiles (v_mfma_f32_32x32x2_f32) for steps
+//               with both sides > 16: persistent workgroups for short K
+//               chunks, one tile per workgroup for long ones; the complex
+//               product is a real GEMM whose K axis carries (re, im);
+//   k_zgemm   - the same on v_mfma_f64_16x16x4_f64 for complex128;
+//   k_skinny_flat, k_skinny_small, k_skinny_rows, k_skinny, k_skinny_z -
+//               VALU streaming for steps with one side <= 16 (HBM-bound);
 //   k_tiny    - one workgroup per step for the many small early-tree steps,
-//               a whole launch group per launch.
+//               a whole launch group per launch;
+//   k_split_reduce - sums split-K partials into C.
 // Outputs are stored through "runs": rowoff(i) + coloff(j), so a product
 // whose order interleaves the two operands' modes is written in place with
-// no separate permute.  k_copy is a generic strided permute used only for
-// leaf staging and for the naive-order ablation.
+// no separate permute.  k_copy_tiled / k_copy are strided permutes used only
+// for leaf staging and for the naive-order ablation; k_write_ptrs fills the
+// workspace's pointer table.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
