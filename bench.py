@@ -297,6 +297,11 @@ class TreeWorkload:
             net = hexagonal.honeycomb(16, 16, 8, 606)
             tree = hexagonal.honeycomb_tree(16, 16)
             self.config = {"workload": "honeycomb-16x16-D8", "seed": 606, "tree": "row-major caterpillar"}
+        elif which == "brickwork30sv":
+            net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
+            tree = trees.state_vector_tree(net)
+            self.config = {"workload": "brickwork-30q-d14-batch64-statevector", "seed": 303,
+                           "tree": "state-vector order (kets, gates in time order, bras)"}
         elif which == "brickwork30":
             net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
             tree = trees.greedy_tree(net)
@@ -603,7 +608,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal", "brickwork30sv"])
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
     ap.add_argument("--dtype", default="c64", choices=["c64", "c128"],
@@ -692,7 +697,12 @@ def main():
     dom = max(per.items(), key=lambda kv: kv[1][1])
     achieved = dom[1][0] / (dom[1][1] / 1e3) / 1e12
     traffic = measured_traffic(args.workload, dom[0])
-    if args.workload == "skinny":
+    hbm_tree = False
+    if isinstance(wl, TreeWorkload):
+        # a whole tree is HBM-bound when its bytes at 8 TB/s outweigh its flops at the matrix peak
+        st = wl.plan.stats()
+        hbm_tree = st["bytes"] / (PEAK_HBM * 1e9) > st["flops"] / (PEAK_FP32_MFMA * 1e12)
+    if args.workload == "skinny" or hbm_tree:
         # HBM-bound steps: algorithmic bytes / time against the HBM peak
         ach_bw = dom[1][3] / (dom[1][1] / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach_bw, 1), "peak": PEAK_HBM, "unit": "GB/s",

@@ -174,6 +174,18 @@ def test_brickwork_30q_batch_and_amplitude():
     _assert_close(amp, ref[0])
 
 
+def test_brickwork_30q_state_vector_tree():
+    """The same 64 amplitudes along the state-vector tree (width 2^30: every
+    gate is a 2^28 x 4 x 4 product with the full state)."""
+    g = json.load(open(os.path.join(GOLDEN, "oracle_values.json")))["brickwork30x14_seed303"]
+    net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6), name="brickwork30x14_batch")
+    assert net.digest() == g["batch_sha256"]
+    got, plan = _gpu_run(net, trees.state_vector_tree(net))
+    assert plan.stats()["max_intermediate"] == 1 << 30
+    ref = np.array(g["batch_re"]) + 1j * np.array(g["batch_im"])
+    _assert_close(got.reshape(-1), ref)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_large_single_leaf_permutes_are_exact(seed):
     """0-step networks: the result is the leaf re-laid in the output order,

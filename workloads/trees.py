@@ -231,3 +231,13 @@ def search_tree(net: Network, trials: int, seed: int = 0, max_elems: Optional[in
         if max_elems is not None and best_key[0] <= max_elems and since > trials // 4:
             break
     return best
+
+
+def state_vector_tree(net: Network) -> Tree:
+    """For a circuit network built by ``Circuit.to_network`` (kets first, then
+    gates in time order, then bras): absorb the leaves in that order into one
+    growing tensor, i.e. build the product state, apply every gate to the
+    full state vector, then project the closed qubits.  Width 2^n; every gate
+    step is a (2^(n-2) x 4 x 4) product with the state."""
+    from .network import caterpillar
+    return caterpillar(net.num_leaves)
