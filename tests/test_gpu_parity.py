@@ -313,3 +313,26 @@ def test_naive_sliced_root_permute_accumulates(ext_sliced):
     got, plan = _gpu_run(net, tree, order=1, sliced=[x])
     assert plan.stats()["root_permute"] == 1
     _assert_close(got, ref)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_networks_without_tiny_class(seed):
+    """tiny_mnk = 0 sends every step to the skinny or GEMM kernels, whatever
+    its size (1 x 1 outputs, ragged 3 x 5 tiles, k = 1 outer products), and
+    max_group = 1 keeps nothing grouped: edge shapes the default thresholds
+    never route there."""
+    rng = np.random.default_rng(6000 + seed)
+    net = randnet.random_network(rng, n_leaves=int(rng.integers(2, 10)), n_closed=int(rng.integers(1, 16)),
+                                 n_open=int(rng.integers(0, 4)), extent_choices=(1, 2, 3, 4, 5))
+    tree = randnet.random_tree(rng, net.num_leaves)
+    if trees.tree_cost(net, tree)["max_elems"] > 1 << 20:
+        pytest.skip("too wide")
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, tiny_mnk=0, max_group=1)
+    assert plan.stats()["nodes_tiny"] == 0
+    _assert_close(got, ref)
+    got, _ = _gpu_run(net, tree, tiny_mnk=0, max_group=1, order=1)
+    _assert_close(got, ref)
+    import quantum_circuit_simulation_amd as qa
+    got, _ = _gpu_run(net, tree, tiny_mnk=0, max_group=1, dtype=qa.TNC_C128)   # complex128 on the same inputs
+    _assert_close(got, ref, tol=1e-10)
