@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense FP32 matrix
 PEAK_FP64_MFMA = 78.6    # TFLOP/s, MI355X dense FP64 matrix
+PEAK_BF16X3 = 2500.0 / 3  # TFLOP/s of complex64 work: dense bf16 matrix peak over 3 products per multiply
 PEAK_HBM = 8000.0        # GB/s
 
 
@@ -67,11 +68,12 @@ def gemm_kernel_name(R, S, K, splits):
 class SweepWorkload:
     name = "pairwise sweep m,n,k in {2^6,2^10,2^14,2^18}, k<=2^14, 45 feasible cases, aligned"
 
-    def __init__(self, cases=None, z=False):
+    def __init__(self, cases=None, z=False, prec=0):
         import torch
         import quantum_circuit_simulation_amd as qa
         from workloads import sweep
         self.z = z
+        self.prec = prec
         cdt = torch.complex128 if z else torch.complex64
         self.eb = 16 if z else 8
         self.cases = [c for c in sweep.cases() if c["feasible"]] if cases is None else cases
@@ -80,7 +82,7 @@ class SweepWorkload:
         for c in self.cases:
             m, n, k = 1 << c["logm"], 1 << c["logn"], 1 << c["logk"]
             net, tree = sweep.network(c["logm"], c["logn"], c["logk"])
-            plan = qa.Plan.from_network(net, tree, dtype=qa.TNC_C128 if z else qa.TNC_C64)
+            plan = qa.Plan.from_network(net, tree, dtype=qa.TNC_C128 if z else qa.TNC_C64, precision=prec)
             self.plans.append((c, plan, m, n, k))
             maxa, maxb, maxc = max(maxa, m * k), max(maxb, n * k), max(maxc, m * n)
             maxws = max(maxws, plan.workspace_bytes)
@@ -95,7 +97,8 @@ class SweepWorkload:
         self.config = {"workload": "pairwise-sweep", "cases": len(self.plans),
                        "m_n_k": "each in {2^6,2^10,2^14,2^18}, k<=2^14, m=n=2^18 excluded",
                        "layout": "GEMM-aligned (lifetime order)", "flop_per_step": self.flops,
-                       "entries": "complex128" if z else "complex64"}
+                       "entries": "complex128" if z else "complex64",
+                       **({"precision": "bf16x3 (split-bf16 products, FP32 accumulation)"} if prec else {})}
 
     def step(self, events=None):
         for idx, (c, plan, m, n, k) in enumerate(self.plans):
@@ -154,6 +157,8 @@ class SweepWorkload:
         nd = plan.node(0)
         if self.z:
             return "k_zgemm" if nd["kernel_class"] == 2 else "k_skinny_z"
+        if self.prec:
+            return "k_cgemm_bf3"
         R, S = (n, m) if nd["swap"] else (m, n)
         return gemm_kernel_name(R, S, k, nd["splits"])
 
@@ -682,6 +687,8 @@ def main():
     ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal", "brickwork30sv", "grid7x8"])
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
+    ap.add_argument("--precision", default="exact", choices=["exact", "bf16x3"],
+                    help="sweep workload: GEMM-class arithmetic (bf16x3: opt-in split-bf16 products)")
     ap.add_argument("--dtype", default="c64", choices=["c64", "c128"],
                     help="sweep workload: entry type (c128 runs the FP64 matrix-core path)")
     ap.add_argument("--distribute", type=int, default=0,
@@ -724,7 +731,7 @@ def main():
             from workloads import sweep
             allc = sweep.cases()
             cases = [allc[int(i)] for i in args.cases.split(",")]
-        wl = SweepWorkload(cases, z=args.dtype == "c128")
+        wl = SweepWorkload(cases, z=args.dtype == "c128", prec=1 if args.precision == "bf16x3" else 0)
         nlaunch = len(wl.plans)
     elif args.workload == "skinny":
         wl = SkinnyWorkload()
@@ -786,7 +793,8 @@ def main():
     else:
         roofline = None
     z = getattr(wl, "z", False)
-    peak = PEAK_FP64_MFMA if z else PEAK_FP32_MFMA
+    prec = getattr(wl, "prec", 0)
+    peak = PEAK_FP64_MFMA if z else (PEAK_BF16X3 if prec else PEAK_FP32_MFMA)
     roofline = roofline or {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
                 "traffic": round(traffic) if traffic is not None else None,
@@ -835,7 +843,7 @@ def main():
     line = {"metric": "contraction-tree TFLOP/s (complex64) + % FP32 MFMA peak; wall time per result",
             "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f64" if z else "f32", "data": "synthetic",
+            "vs_baseline": None, "dtype": "f64" if z else ("f32 via bf16x3" if prec else "f32"), "data": "synthetic",
             **({"pct_fp64_mfma_peak": round(100.0 * value / PEAK_FP64_MFMA, 2)} if z else
                {"pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2)}),
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),

@@ -105,7 +105,19 @@ typedef struct {
   uint64_t capacity_bytes;    /* 0: no limit; else fail with OUT_OF_MEMORY above it */
   uint64_t tiny_mnk;          /* 32768: steps with m*n*k <= this share grouped launches */
   int32_t max_group;          /* 256: most steps in one grouped launch */
+  int32_t precision;          /* TNC_PREC_EXACT: arithmetic of GEMM-class complex64 steps */
 } tnc_plan_options;
+
+/* Arithmetic of the GEMM-class steps of a complex64 plan.  EXACT: FP32
+ * matrix cores on the FP32 entries (products exact, FP32 accumulation).
+ * BF16X3: each FP32 entry is split into bf16 hi + lo (round to nearest
+ * even twice) and each product is hi*hi + hi*lo + lo*hi on the bf16 matrix
+ * cores with FP32 accumulation; the dropped lo*lo term and the split leave
+ * about 2^-16 relative error per product.  This is the split / emulated
+ * precision variant the page lists among the extensions (page 1, the
+ * outlook on extended and mixed precision); it is opt-in and never the
+ * default.  Complex128 plans accept only EXACT. */
+typedef enum { TNC_PREC_EXACT = 0, TNC_PREC_BF16X3 = 1 } tnc_precision;
 
 /* Fill `opts` with the defaults. */
 void tnc_plan_options_default(tnc_plan_options *opts);

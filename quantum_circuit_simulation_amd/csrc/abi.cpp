@@ -63,6 +63,7 @@ void tnc_plan_options_default(tnc_plan_options *o) {
   o->capacity_bytes = 0;
   o->tiny_mnk = 32768;
   o->max_group = 256;
+  o->precision = TNC_PREC_EXACT;
 }
 
 tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
@@ -236,6 +237,7 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
           a.beta = (nd.is_root && !p.root_permute) ? beta : 0;
           a.splits = nd.splits;
           a.scratch = nd.splits > 1 ? reinterpret_cast<float2 *>(arena + nd.scratch_off) : nullptr;
+          a.prec = p.opts.precision;
           if (z) {
             // same fields, complex128 entries
             tnc::StepArgsZ az{};

@@ -1340,6 +1340,166 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// complex64 GEMM in split bf16 (plans with TNC_PREC_BF16X3)
+//
+// Each FP32 entry x becomes hi = bf16(x) and lo = bf16(x - hi) (round to
+// nearest even); a complex entry (re, im) packs into one 32-bit word per
+// part (re in the low half).  The product's K axis carries (re, im) as in
+// k_cgemm: the first operand's words are used as they are, the second's as
+// (yr, -yi) (sign bit of the high half flipped) for the real part and as
+// (yi, yr) (halves swapped) for the imaginary part.  Each of the two is
+// hi*hi + hi*lo + lo*hi on v_mfma_f32_32x32x16_bf16 (16 K entries = 8
+// complex entries per instruction) with FP32 accumulation.  Tiles 128 x 128,
+// four waves of 64 x 64, 16 complex entries of K per stage; one LDS buffer
+// with the next stage prefetched into registers.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void split_complex(float2 v, uint32_t &whi, uint32_t &wlo) {
+  const uint32_t rh = bf16_rne(v.x), ih = bf16_rne(v.y);
+  const uint32_t rl = bf16_rne(v.x - __uint_as_float(rh << 16));
+  const uint32_t il = bf16_rne(v.y - __uint_as_float(ih << 16));
+  whi = rh | (ih << 16);
+  wlo = rl | (il << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+constexpr int kBf3Tile = 128;
+constexpr int kBf3BK = 16;               // complex entries of K per stage
+constexpr int kBf3LD = kBf3BK + 4;       // words per LDS row: conflict-free 16-byte reads
+
+__global__ __launch_bounds__(256, 2) void k_cgemm_bf3(StepArgs a, int64_t kchunk, uint32_t tiles_r,
+                                                      uint32_t tiles_c) {
+  constexpr int BM = kBf3Tile, BN = kBf3Tile, BK = kBf3BK, LD = kBf3LD;
+  constexpr int WM = 64, WN = 64, MB = 2, NB = 2, WAVES_C = BN / WN;
+  constexpr int PER = BM * BK / 2 / 256;  // entry pairs per thread per operand
+  __shared__ uint32_t Xh[BM][LD], Xl[BM][LD], Yh[BN][LD], Yl[BN][LD];
+  __shared__ int64_t rowoff[BM], coloff[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WAVES_C, wc = wave % WAVES_C;
+  const int h = lane >> 5, l32 = lane & 31;
+  uint32_t tr, tc;
+  tile_coords(blockIdx.x, tiles_r, tiles_c, &tr, &tc);
+  const int64_t r0 = (int64_t)tr * BM, c0 = (int64_t)tc * BN;
+  const int split = blockIdx.y;
+  const int64_t k0 = (int64_t)split * kchunk;
+  const int64_t k1 = min(a.K, k0 + kchunk);
+  const int64_t nkt = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+  const int64_t R = a.R, S = a.S, K = a.K;
+  const bool partial = a.splits > 1;
+
+  if (!partial) {
+    for (int t = tid; t < BM; t += 256) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += 256) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+  }
+
+  f32x16 accR[MB][NB], accI[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accR[mb][nb][r] = 0.f;
+        accI[mb][nb][r] = 0.f;
+      }
+
+  // stage registers: entry pairs (l, l + 1) of row p / (BK / 2)
+  float2 rx[PER][2], ry[PER][2];
+  auto gload = [&](int64_t kt) {
+    const int64_t kb = k0 + kt * BK;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int p = tid + 256 * q;
+      const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+      const int64_t gi = r0 + row, gj = c0 + row, gl = kb + l;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        rx[q][u] = (gi < R && gl + u < k1) ? a.X[gi * K + gl + u] : make_float2(0.f, 0.f);
+        ry[q][u] = (gj < S && gl + u < k1) ? a.Y[gj * K + gl + u] : make_float2(0.f, 0.f);
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int p = tid + 256 * q;
+      const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
+      uint32_t h0, l0, h1, l1;
+      split_complex(rx[q][0], h0, l0);
+      split_complex(rx[q][1], h1, l1);
+      *(uint2 *)&Xh[row][l] = make_uint2(h0, h1);
+      *(uint2 *)&Xl[row][l] = make_uint2(l0, l1);
+      split_complex(ry[q][0], h0, l0);
+      split_complex(ry[q][1], h1, l1);
+      *(uint2 *)&Yh[row][l] = make_uint2(h0, h1);
+      *(uint2 *)&Yl[row][l] = make_uint2(l0, l1);
+    }
+  };
+
+  if (nkt > 0) gload(0);
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    __syncthreads();  // the previous stage's fragment reads are done
+    lstore();
+    __syncthreads();
+    if (kt + 1 < nkt) gload(kt + 1);
+#pragma unroll
+    for (int s2 = 0; s2 < BK / 8; ++s2) {
+      const int off = s2 * 8 + h * 4;  // this lane's 4 complex entries (8 K entries) of the step
+      bf16x8 ah[MB], al[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        ah[mb] = as_bf16x8(*(const u32x4 *)&Xh[wr * WM + mb * 32 + l32][off]);
+        al[mb] = as_bf16x8(*(const u32x4 *)&Xl[wr * WM + mb * 32 + l32][off]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 bh = *(const u32x4 *)&Yh[wc * WN + nb * 32 + l32][off];
+        const u32x4 bl = *(const u32x4 *)&Yl[wc * WN + nb * 32 + l32][off];
+        const u32x4 sgn = {0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u};
+        const bf16x8 brh = as_bf16x8(bh ^ sgn), brl = as_bf16x8(bl ^ sgn);
+        const bf16x8 bih = as_bf16x8((bh >> 16) | (bh << 16)), bil = as_bf16x8((bl >> 16) | (bl << 16));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          accR[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], brh, accR[mb][nb], 0, 0, 0);
+          accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bih, accI[mb][nb], 0, 0, 0);
+          accR[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], brl, accR[mb][nb], 0, 0, 0);
+          accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bil, accI[mb][nb], 0, 0, 0);
+          accR[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], brh, accR[mb][nb], 0, 0, 0);
+          accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bih, accI[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wc * WN + nb * 32 + l32;
+      const int64_t gj = c0 + col;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * WM + mb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+        const int64_t gi = r0 + row;
+        if (gi < R && gj < S) {
+          const float2 v = make_float2(accR[mb][nb][r], accI[mb][nb][r]);
+          if (partial) a.scratch[((int64_t)split * R + gi) * S + gj] = v;
+          else store_c(a.C + rowoff[row] + coloff[col], v, a.beta);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // complex128 (FP64) kernels
 
 // Skinny complex128 steps (one side <= 16): one row per thread, each 16-entry
@@ -1677,6 +1837,17 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
+  if (a.prec == kPrecBf16x3) {
+    const int64_t tiles_r = (a.R + kBf3Tile - 1) / kBf3Tile, tiles_c = (a.S + kBf3Tile - 1) / kBf3Tile;
+    int64_t kchunk = a.K;
+    if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + kBf3BK - 1) / kBf3BK * kBf3BK;
+    if (tiles_r * tiles_c >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_cgemm_bf3, dim3((unsigned)(tiles_r * tiles_c), (unsigned)a.splits), dim3(256), 0, stream, a,
+                       kchunk, (uint32_t)tiles_r, (uint32_t)tiles_c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits <= 1) return e;
+    return run_split_reduce(a, stream);
+  }
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
   if (a.S > 64 && a.R <= 32) e = run_cgemm<32, 256, 8, 32, 64>(a, stream);

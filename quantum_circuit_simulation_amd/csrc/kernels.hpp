@@ -31,7 +31,10 @@ struct StepArgsT {
   int32_t beta;
   int32_t splits;
   T *scratch;
+  int32_t prec;  // kPrecExact or kPrecBf16x3 (the plan's tnc_precision)
 };
+constexpr int32_t kPrecExact = 0;   // TNC_PREC_EXACT
+constexpr int32_t kPrecBf16x3 = 1;  // TNC_PREC_BF16X3
 using StepArgs = StepArgsT<float2>;    // complex64
 using StepArgsZ = StepArgsT<double2>;  // complex128
 

@@ -315,6 +315,8 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   if (o.max_group < 1) return TNC_ERR_INVALID_ARG;
   if (o.order != TNC_ORDER_LIFETIME && o.order != TNC_ORDER_NAIVE) return TNC_ERR_INVALID_ARG;
   if (net->dtype != TNC_C64 && net->dtype != TNC_C128) return TNC_ERR_INVALID_ARG;
+  if (o.precision != TNC_PREC_EXACT && o.precision != TNC_PREC_BF16X3) return TNC_ERR_INVALID_ARG;
+  if (o.precision == TNC_PREC_BF16X3 && net->dtype != TNC_C64) return TNC_ERR_INVALID_ARG;
   p->dtype = net->dtype;
   const uint64_t eb = net->dtype == TNC_C128 ? 16 : 8;  // bytes per entry
   p->elem_bytes = eb;

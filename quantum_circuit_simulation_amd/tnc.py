@@ -22,6 +22,7 @@ STATUS = {0: "TNC_OK", 1: "TNC_ERR_INVALID_ARG", 2: "TNC_ERR_INVALID_NETWORK", 3
           4: "TNC_ERR_UNSUPPORTED", 5: "TNC_ERR_OUT_OF_MEMORY", 6: "TNC_ERR_WORKSPACE_TOO_SMALL",
           7: "TNC_ERR_HIP"}
 TNC_C64, TNC_C128 = 0, 1
+PREC_EXACT, PREC_BF16X3 = 0, 1
 ORDER_LIFETIME, ORDER_NAIVE = 0, 1
 CLASS_TINY, CLASS_SKINNY, CLASS_GEMM = 0, 1, 2
 NONE = (1 << 64) - 1
@@ -50,7 +51,7 @@ class Tree(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int), ("num_sliced", ctypes.c_int32), ("sliced_modes", P(ctypes.c_int32)),
                 ("align", ctypes.c_uint64), ("capacity_bytes", ctypes.c_uint64), ("tiny_mnk", ctypes.c_uint64),
-                ("max_group", ctypes.c_int32)]
+                ("max_group", ctypes.c_int32), ("precision", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -178,7 +179,8 @@ class Plan:
 
     def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
                  order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
-                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256, dtype: int = TNC_C64):
+                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256, dtype: int = TNC_C64,
+                 precision: int = 0):
         lib = load_library()
         self._lib = lib
         self.num_leaves = len(leaves)
@@ -204,6 +206,7 @@ class Plan:
         opts.capacity_bytes = capacity_bytes
         opts.tiny_mnk = tiny_mnk
         opts.max_group = max_group
+        opts.precision = precision
         h = ctypes.c_void_p()
         _check(lib.tnc_plan(ctypes.byref(net), ctypes.byref(tree), ctypes.byref(opts), ctypes.byref(h)), "tnc_plan")
         self._h = h
