@@ -3,7 +3,9 @@ configuration), checked against the oracle on sampled output entries:
 exact complex128 sums over the gathered rows of the inputs.  Also checks
 properties that hold at any size: every entry finite, and mean |C|^2 / k
 close to 1 (i.i.d. CN(0,1) inputs give E|C_ij|^2 = k), which would catch
-unwritten or doubly-written tiles anywhere in C.
+unwritten or doubly-written tiles anywhere in C, and a Freivalds probe over
+the whole of C: C x against A (B^T x) for a random x, both in complex128
+through torch's matrix-vector products.
 
 Inputs: CN(0,1) complex64 pools filled on the device from a seeded torch
 generator; each case uses prefixes of the pools as its A, B buffers.
@@ -66,6 +68,32 @@ def _properties(C, m, n, k):
     assert 0.8 < ms < 1.2, f"mean |C|^2 / k = {ms}"
 
 
+def _freivalds(A, B, C, m, n, k, seed):
+    """C x against A (B^T x) for a random complex x, in complex128 with
+    torch's own matrix-vector products (chunked over rows): every entry of
+    C enters C x, so a wrong or missing tile anywhere shows up with high
+    probability.  Returns (C x, A B^T x) as numpy arrays."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(n, dtype=torch.complex128, device="cuda", generator=g)
+    v = torch.zeros(k, dtype=torch.complex128, device="cuda")
+    rows = max(1, (1 << 26) // k)
+    Bm = B[: n * k].view(n, k)
+    for j0 in range(0, n, rows):
+        v += Bm[j0:j0 + rows].to(torch.complex128).transpose(0, 1) @ x[j0:j0 + rows]
+    Am = A[: m * k].view(m, k)
+    Cm = C[: m * n].view(m, n)
+    ref, got = [], []
+    rows_a = max(1, (1 << 26) // k)
+    for i0 in range(0, m, rows_a):
+        ref.append(Am[i0:i0 + rows_a].to(torch.complex128) @ v)
+    rows_c = max(1, (1 << 26) // n)
+    for i0 in range(0, m, rows_c):
+        got.append(Cm[i0:i0 + rows_c].to(torch.complex128) @ x)
+    return torch.cat(got).cpu().numpy(), torch.cat(ref).cpu().numpy()
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"m{c['logm']}n{c['logn']}k{c['logk']}")
 def test_aligned_full_size(case, pools):
     import torch
@@ -88,6 +116,9 @@ def test_aligned_full_size(case, pools):
     got = C[: m * n].view(m, n).index_select(0, ri).index_select(1, ci).cpu().numpy()
     ok, err = rel_err_ok(got, ref, TOL)
     assert ok, err
+    got, ref = _freivalds(A, B, C, m, n, k, seed=case["index"])
+    ok, err = rel_err_ok(got, ref, TOL)
+    assert ok, f"Freivalds probe: {err}"
 
 
 @pytest.mark.parametrize("order", [0, 1], ids=["lifetime", "naive"])
