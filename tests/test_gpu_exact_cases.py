@@ -31,10 +31,13 @@ def _gpu():
     yield
 
 
-def _delta_network(R, Kc, ext, seed, permuted, delta_lhs):
+def _delta_network(R, Kc, ext, seed, permuted, delta_lhs, row_inner=0):
     """Data leaf over [M | K] (R and Kc modes of extent ext), delta leaf over
     [N' | K] with N'_i paired to K_i; output [M | N'].  With ``permuted`` the
-    declared orders of both leaves and of the output are seeded shuffles.
+    declared orders of both leaves and of the output are seeded shuffles;
+    ``row_inner`` > 0 instead lays the output out as [M_hi | N' | M_lo] with
+    the last ``row_inner`` modes of M innermost (an interleaved order whose
+    innermost run belongs to the data leaf).
     Returns (network, tree, expected output ndarray)."""
     rng = np.random.default_rng(seed)
     M = list(range(R))
@@ -45,6 +48,8 @@ def _delta_network(R, Kc, ext, seed, permuted, delta_lhs):
         A = [A[i] for i in rng.permutation(len(A))]
         B = [B[i] for i in rng.permutation(len(B))]
         out = [out[i] for i in rng.permutation(len(out))]
+    elif row_inner:
+        out = M[:R - row_inner] + Np + M[R - row_inner:]
     extents = np.full(R + 2 * Kc, ext, dtype=np.int64)
     a = sweep.complex_gaussian(rng, tuple([ext] * len(A)))
     k = ext ** Kc
@@ -83,6 +88,29 @@ def test_delta_relayout_is_exact(case, permuted, delta_lhs):
     bad = np.flatnonzero(got.ravel() != expected.ravel().astype(np.complex128))
     assert bad.size == 0, (f"{bad.size} entries differ (class {node['kernel_class']}, splits {node['splits']}); "
                            f"first at {bad[0]}: {got.ravel()[bad[0]]} vs {expected.ravel()[bad[0]]}")
+
+
+# (R, Kc, ext, row_inner): interleaved outputs [M_hi | N' | M_lo] whose
+# innermost run (extent 2, 8 or 3) belongs to the data leaf, which the
+# planner therefore places on the column side (paired stores for even
+# extents, single stores for odd); persistent and one-tile GEMM, split K
+ROW_INNER_CASES = [(12, 8, 2, 1), (12, 8, 2, 3), (12, 10, 2, 3), (8, 11, 2, 1), (8, 6, 3, 1), (14, 6, 2, 3)]
+
+
+@pytest.mark.parametrize("delta_lhs", [False, True], ids=["delta_rhs", "delta_lhs"])
+@pytest.mark.parametrize("case", ROW_INNER_CASES, ids=lambda c: f"R{c[0]}K{c[1]}x{c[2]}in{c[3]}")
+def test_delta_interleaved_output_is_exact(case, delta_lhs):
+    from tests.gpu_util import run
+    R, Kc, ext, inner = case
+    net, tree, expected = _delta_network(R, Kc, ext, seed=4000 + R + Kc, permuted=False, delta_lhs=delta_lhs,
+                                         row_inner=inner)
+    print(f"[gpu] {net.name} row_inner={inner} delta_lhs={delta_lhs}", flush=True)
+    got, plan = run(net, tree)
+    node = plan.node(0)
+    assert node["interleaved"] == 1
+    # the data leaf's modes (holding the innermost run) are the columns
+    assert node["swap"] == (0 if delta_lhs else 1)
+    assert np.array_equal(got, expected.astype(np.complex128))
 
 
 @pytest.mark.parametrize("case", [(12, 8, 2), (8, 11, 2), (7, 5, 3)], ids=lambda c: f"R{c[0]}K{c[1]}x{c[2]}")
