@@ -22,6 +22,8 @@
 // workspace's pointer table.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace tnc {
@@ -1101,9 +1103,11 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
   }
 }
 
-// One tile per workgroup (long K chunks).  Same MFMA scheme and LDS pipeline
-// as k_cgemm, without the multi-tile loop; the tile comes from the same
-// XCD-aware order.
+// One tile per workgroup (long K chunks).  Same MFMA scheme and LDS double
+// buffer as k_cgemm, without the multi-tile loop; the tile comes from the
+// same XCD-aware order.  Loads run two K stages ahead (two register stages),
+// and tiles wholly inside C with a K chunk that is a multiple of BK load
+// without bounds checks.
 template <int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchunk, uint32_t tiles_r,
                                                        uint32_t tiles_c) {
@@ -1146,7 +1150,9 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
       }
     }
 
-  float2 ra[A_PER], rb[B_PER];
+  // two register stages: the loads of K stage kt + 2 are in flight while
+  // stage kt + 1 is written to LDS and stage kt is multiplied
+  float2 ra[2][A_PER], rb[2][B_PER];
   // 16-byte loads of entry pairs (l, l + 1) and 8-byte LDS writes when K is
   // even (every K chunk then starts and ends on an even entry) and both
   // operands are 16-byte aligned; single entries otherwise
@@ -1154,7 +1160,11 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
   // 64x256 / 256x64 tiles then spill)
   constexpr bool kPairable = false;
   const bool pairs = false;
-  auto gload = [&](int64_t kt) {
+  // every load of the tile in bounds: full rows and columns, K chunk a
+  // multiple of BK
+  const bool interior = r0 + BM <= R && c0 + BN <= S && (k1 - k0) % BK == 0;
+  auto gload = [&](auto bufc, int64_t kt) {
+    constexpr int buf = decltype(bufc)::value;
     const int64_t kb = k0 + kt * BK;
     if (kPairable && pairs) {
 #pragma unroll
@@ -1164,8 +1174,8 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
         const int64_t gi = r0 + row, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (gi < R && gl < k1) v = *(const float4 *)(a.X + gi * K + gl);
-        ra[2 * q] = make_float2(v.x, v.y);
-        ra[2 * q + 1] = make_float2(v.z, v.w);
+        ra[buf][2 * q] = make_float2(v.x, v.y);
+        ra[buf][2 * q + 1] = make_float2(v.z, v.w);
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
@@ -1174,8 +1184,21 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
         const int64_t gj = c0 + col, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (gj < S && gl < k1) v = *(const float4 *)(a.Y + gj * K + gl);
-        rb[2 * q] = make_float2(v.x, v.y);
-        rb[2 * q + 1] = make_float2(v.z, v.w);
+        rb[buf][2 * q] = make_float2(v.x, v.y);
+        rb[buf][2 * q + 1] = make_float2(v.z, v.w);
+      }
+      return;
+    }
+    if (interior) {
+#pragma unroll
+      for (int q = 0; q < A_PER; ++q) {
+        const int e = tid + 256 * q;
+        ra[buf][q] = a.X[(r0 + e / BK) * K + kb + e % BK];
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER; ++q) {
+        const int e = tid + 256 * q;
+        rb[buf][q] = a.Y[(c0 + e / BK) * K + kb + e % BK];
       }
       return;
     }
@@ -1184,31 +1207,32 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
       const int e = tid + 256 * q;
       const int row = e / BK, l = e % BK;
       const int64_t gi = r0 + row, gl = kb + l;
-      ra[q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : make_float2(0.f, 0.f);
+      ra[buf][q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : make_float2(0.f, 0.f);
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
       const int e = tid + 256 * q;
       const int col = e / BK, l = e % BK;
       const int64_t gj = c0 + col, gl = kb + l;
-      rb[q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : make_float2(0.f, 0.f);
+      rb[buf][q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : make_float2(0.f, 0.f);
     }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](auto bufc, int st) {
+    constexpr int buf = decltype(bufc)::value;
     if (kPairable && pairs) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
         const int p = tid + 256 * q;
         const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
-        *(float2 *)&As[st][0][row][l] = make_float2(ra[2 * q].x, ra[2 * q + 1].x);
-        *(float2 *)&As[st][1][row][l] = make_float2(ra[2 * q].y, ra[2 * q + 1].y);
+        *(float2 *)&As[st][0][row][l] = make_float2(ra[buf][2 * q].x, ra[buf][2 * q + 1].x);
+        *(float2 *)&As[st][1][row][l] = make_float2(ra[buf][2 * q].y, ra[buf][2 * q + 1].y);
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
         const int p = tid + 256 * q;
         const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
-        *(float2 *)&Bs[st][0][col][l] = make_float2(rb[2 * q].x, rb[2 * q + 1].x);
-        *(float2 *)&Bs[st][1][col][l] = make_float2(rb[2 * q].y, rb[2 * q + 1].y);
+        *(float2 *)&Bs[st][0][col][l] = make_float2(rb[buf][2 * q].x, rb[buf][2 * q + 1].x);
+        *(float2 *)&Bs[st][1][col][l] = make_float2(rb[buf][2 * q].y, rb[buf][2 * q + 1].y);
       }
       return;
     }
@@ -1216,15 +1240,15 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
       const int row = e / BK, l = e % BK;
-      As[st][0][row][l] = ra[q].x;
-      As[st][1][row][l] = ra[q].y;
+      As[st][0][row][l] = ra[buf][q].x;
+      As[st][1][row][l] = ra[buf][q].y;
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
       const int e = tid + 256 * q;
       const int col = e / BK, l = e % BK;
-      Bs[st][0][col][l] = rb[q].x;
-      Bs[st][1][col][l] = rb[q].y;
+      Bs[st][0][col][l] = rb[buf][q].x;
+      Bs[st][1][col][l] = rb[buf][q].y;
     }
   };
 
@@ -1232,16 +1256,28 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
   const int bcol = wc * WN + l32;
   const float sgn = h ? -1.f : 1.f;  // real-part operand: yr (lanes 0-31), -yi (lanes 32-63)
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   if (nkt > 0) {
-    gload(0);
-    lstore(0);
+    gload(I0{}, 0);
+    if (nkt > 1) gload(I1{}, 1);
+    lstore(I0{}, 0);
   }
   __syncthreads();
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int st = (int)(kt & 1);
-    if (kt + 1 < nkt) gload(kt + 1);
+  // one K stage; the register stage and LDS buffer indices are compile-time
+  // constants (kt & 1), so the stage loop is unrolled by two
+  auto iter = [&](int64_t kt, auto cur) {
+    constexpr int st = decltype(cur)::value;
+    using Other = std::integral_constant<int, 1 - st>;
 #pragma unroll
     for (int l4 = 0; l4 < BK; l4 += 4) {
+      if (l4 == BK / 2) {
+        // stage kt + 1 (loaded one stage ago) into the other LDS buffer, whose
+        // readers finished before the last barrier; then the loads of stage
+        // kt + 2 into the registers this frees
+        if (kt + 1 < nkt) lstore(Other{}, 1 - st);
+        if (kt + 2 < nkt) gload(cur, kt + 2);
+      }
       f32x4 av[MB], brv[NB], biv[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) av[mb] = *(const f32x4 *)&As[st][h][arow + mb * 32][l4];
@@ -1260,9 +1296,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
             accI[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mb][kk], biv[nb][kk], accI[mb][nb], 0, 0, 0);
           }
     }
-    if (kt + 1 < nkt) lstore(st ^ 1);
     __syncthreads();
+  };
+  int64_t kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    iter(kt, I0{});
+    iter(kt + 1, I1{});
   }
+  if (kt < nkt) iter(kt, I0{});
 
   const bool partial = a.splits > 1;
   if (!partial) {
