@@ -49,9 +49,9 @@ def fill_gaussian(t, seed):
 def gemm_kernel_name(R, S, K, splits):
     """The k_cgemm instance the library launches for an oriented GEMM step
     (same rule as its launcher): one tile per workgroup for K chunks above
-    256, persistent workgroups otherwise; tile shape by the short side."""
+    64, persistent workgroups otherwise; tile shape by the short side."""
     kchunk = K if splits <= 1 else -(-(-(-K // splits)) // 8) * 8
-    base = "k_cgemm_tile" if kchunk > 256 else "k_cgemm"
+    base = "k_cgemm_tile" if kchunk > 64 else "k_cgemm"
     if S > 64 and R <= 32:
         t = "32,256"
     elif S > 64 and R <= 64:

@@ -1103,7 +1103,7 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
   }
 }
 
-// One tile per workgroup (long K chunks).  Same MFMA scheme and LDS double
+// One tile per workgroup (K chunks above 64).  Same MFMA scheme and LDS double
 // buffer as k_cgemm, without the multi-tile loop; the tile comes from the
 // same XCD-aware order.  Loads run two K stages ahead (two register stages),
 // and tiles wholly inside C with a K chunk that is a multiple of BK load
@@ -1311,6 +1311,38 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     for (int t = tid; t < BN; t += 256) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
   }
   __syncthreads();
+  // paired 16-byte stores, as in k_cgemm
+  const bool pair_store = !partial && a.ncr > 0 && a.runs[a.nrr + a.ncr - 1].stride == 1 &&
+                          (a.runs[a.nrr + a.ncr - 1].size % 2) == 0 && aligned16(a.C);
+  if (pair_store) {
+    const bool odd_lane = (l32 & 1) != 0;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col0 = wc * WN + nb * 32 + (l32 & ~1);
+        const int64_t gj0 = c0 + col0;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int q = wr * WM + mb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+          const float sr = odd_lane ? accR[mb][nb][r] : accR[mb][nb][r + 1];
+          const float si = odd_lane ? accI[mb][nb][r] : accI[mb][nb][r + 1];
+          const float pr = dpp_f<0xB1>(sr), pi = dpp_f<0xB1>(si);
+          const int row = odd_lane ? q + 1 : q;
+          float4 v = odd_lane ? make_float4(pr, pi, accR[mb][nb][r + 1], accI[mb][nb][r + 1])
+                              : make_float4(accR[mb][nb][r], accI[mb][nb][r], pr, pi);
+          if (r0 + row < R && gj0 < S) {
+            float4 *p = (float4 *)(a.C + rowoff[row] + coloff[col0]);
+            if (a.beta) {
+              const float4 o = *p;
+              v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+            }
+            *p = v;
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1358,13 +1390,14 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   if (a.R >= (int64_t(1) << 31) || a.S >= (int64_t(1) << 31) || a.K >= (int64_t(1) << 31) ||
       tiles_r * tiles_c >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
-  // Short K chunks: a persistent grid (two workgroups per CU over the K
-  // splits, a multiple of 8 so every XCD gets an equal share) hides each
-  // tile's load latency behind the previous tile.  Long K chunks: one tile
-  // per workgroup, so co-resident workgroups stay in step through K and
-  // share their L2 lines (persistent workgroups drift apart over many tiles).
+  // Short K chunks (up to 64): a persistent grid (two workgroups per CU over
+  // the K splits, a multiple of 8 so every XCD gets an equal share) hides
+  // each tile's load latency behind the previous tile.  Longer K chunks: one
+  // tile per workgroup, so co-resident workgroups stay in step through K and
+  // share their L2 lines (persistent workgroups drift apart over many
+  // tiles), with loads two K stages ahead.
   const int64_t ntiles = tiles_r * tiles_c;
-  if (kchunk > 256) {
+  if (kchunk > 64) {
     dim3 grid((unsigned)ntiles, (unsigned)a.splits);
     hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, kchunk,
                        (uint32_t)tiles_r, (uint32_t)tiles_c);

@@ -66,7 +66,7 @@ def _delta_network(R, Kc, ext, seed, permuted, delta_lhs, row_inner=0):
 
 
 # (R, Kc, ext): tiny, skinny (flat and row kernels), persistent GEMM,
-# one-tile GEMM (K chunk above 256), split K, ragged extent-3 tiles
+# one-tile GEMM (K chunk above 64), split K, ragged extent-3 tiles
 DELTA_CASES = [
     (2, 2, 2), (16, 2, 2), (14, 4, 2), (9, 3, 3), (12, 8, 2), (12, 10, 2),
     (8, 11, 2), (7, 5, 3), (8, 6, 3),
