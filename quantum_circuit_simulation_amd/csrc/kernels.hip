@@ -1105,21 +1105,23 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
 
 // One tile per workgroup (K chunks above 64).  Same MFMA scheme and LDS double
 // buffer as k_cgemm, without the multi-tile loop; the tile comes from the
-// same XCD-aware order.  Loads run two K stages ahead (two register stages),
+// same XCD-aware order.  NT threads, one wave per WM x WN block: the
+// 128x128, 64x256 and 256x64 tiles run 8 waves of 64x32 (128 VGPRs, four
+// waves per SIMD with two workgroups per CU).  Loads run two K stages ahead (two register stages),
 // and tiles wholly inside C with a K chunk that is a multiple of BK load
 // without bounds checks.
-template <int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchunk, uint32_t tiles_r,
+template <int BM, int BN, int BK, int WM, int WN, int NT>
+__global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t kchunk, uint32_t tiles_r,
                                                        uint32_t tiles_c) {
   constexpr int PAD = 4;
   constexpr int LDK = BK + PAD;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int WAVES_C = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert((BM / WM) * (BN / WN) == NT / 64, "one wave per WM x WN block");
   static_assert(BK % 4 == 0, "BK");
-  constexpr int A_PER = BM * BK / 256;
-  constexpr int B_PER = BN * BK / 256;
-  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for 256 threads");
+  constexpr int A_PER = BM * BK / NT;
+  constexpr int B_PER = BN * BK / NT;
+  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for the workgroup");
 
   __shared__ float As[2][2][BM][LDK];
   __shared__ float Bs[2][2][BN][LDK];
@@ -1169,7 +1171,7 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     if (kPairable && pairs) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
         const int64_t gi = r0 + row, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1179,7 +1181,7 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
         const int64_t gj = c0 + col, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1192,26 +1194,26 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     if (interior) {
 #pragma unroll
       for (int q = 0; q < A_PER; ++q) {
-        const int e = tid + 256 * q;
+        const int e = tid + NT * q;
         ra[buf][q] = a.X[(r0 + e / BK) * K + kb + e % BK];
       }
 #pragma unroll
       for (int q = 0; q < B_PER; ++q) {
-        const int e = tid + 256 * q;
+        const int e = tid + NT * q;
         rb[buf][q] = a.Y[(c0 + e / BK) * K + kb + e % BK];
       }
       return;
     }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int row = e / BK, l = e % BK;
       const int64_t gi = r0 + row, gl = kb + l;
       ra[buf][q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : make_float2(0.f, 0.f);
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int col = e / BK, l = e % BK;
       const int64_t gj = c0 + col, gl = kb + l;
       rb[buf][q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : make_float2(0.f, 0.f);
@@ -1222,14 +1224,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     if (kPairable && pairs) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
         *(float2 *)&As[st][0][row][l] = make_float2(ra[buf][2 * q].x, ra[buf][2 * q + 1].x);
         *(float2 *)&As[st][1][row][l] = make_float2(ra[buf][2 * q].y, ra[buf][2 * q + 1].y);
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
         *(float2 *)&Bs[st][0][col][l] = make_float2(rb[buf][2 * q].x, rb[buf][2 * q + 1].x);
         *(float2 *)&Bs[st][1][col][l] = make_float2(rb[buf][2 * q].y, rb[buf][2 * q + 1].y);
@@ -1238,14 +1240,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
     }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int row = e / BK, l = e % BK;
       As[st][0][row][l] = ra[buf][q].x;
       As[st][1][row][l] = ra[buf][q].y;
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int col = e / BK, l = e % BK;
       Bs[st][0][col][l] = rb[buf][q].x;
       Bs[st][1][col][l] = rb[buf][q].y;
@@ -1307,8 +1309,8 @@ __global__ __launch_bounds__(256, 2) void k_cgemm_tile(StepArgs a, int64_t kchun
 
   const bool partial = a.splits > 1;
   if (!partial) {
-    for (int t = tid; t < BM; t += 256) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
-    for (int t = tid; t < BN; t += 256) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+    for (int t = tid; t < BM; t += NT) rowoff[t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += NT) coloff[t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
   }
   __syncthreads();
   // paired 16-byte stores, as in k_cgemm
@@ -1398,8 +1400,13 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   // tiles), with loads two K stages ahead.
   const int64_t ntiles = tiles_r * tiles_c;
   if (kchunk > 64) {
+    // eight waves of WM x WN/2 where both tile sides reach 64; the 32-wide
+    // tiles keep four waves (their narrow operand tile has fewer entries per
+    // K stage than 512 threads)
+    constexpr bool kWide = BM >= 64 && BN >= 64;
+    constexpr int TWN = kWide ? WN / 2 : WN, TNT = kWide ? 512 : 256;
     dim3 grid((unsigned)ntiles, (unsigned)a.splits);
-    hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, kchunk,
+    hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, TWN, TNT>), grid, dim3(TNT), 0, stream, a, kchunk,
                        (uint32_t)tiles_r, (uint32_t)tiles_c);
     return hipGetLastError();
   }
