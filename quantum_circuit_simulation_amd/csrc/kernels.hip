@@ -839,19 +839,19 @@ __device__ __forceinline__ void tile_coords(uint32_t L, uint32_t tiles_r, uint32
   *tc = in_g / gsz;
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int NT>
 // Row, column and tile indices are 32-bit: the planner keeps R, S and K of
 // GEMM-class steps below 2^31.
-__global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, uint32_t tiles_r, uint32_t tiles_c) {
+__global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchunk, uint32_t tiles_r, uint32_t tiles_c) {
   constexpr int PAD = 4;
   constexpr int LDK = BK + PAD;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int WAVES_C = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert((BM / WM) * (BN / WN) == NT / 64, "one wave per WM x WN block");
   static_assert(BK % 4 == 0, "BK");
-  constexpr int A_PER = BM * BK / 256;
-  constexpr int B_PER = BN * BK / 256;
-  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for 256 threads");
+  constexpr int A_PER = BM * BK / NT;
+  constexpr int B_PER = BN * BK / NT;
+  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small for the workgroup");
 
   __shared__ float As[2][2][BM][LDK];
   __shared__ float Bs[2][2][BN][LDK];
@@ -892,8 +892,8 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
   };
   auto tables = [&](int par, int32_t r0, int32_t c0) {
     if (partial) return;
-    for (int t = tid; t < BM; t += 256) rowoff[par][t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
-    for (int t = tid; t < BN; t += 256) coloff[par][t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
+    for (int t = tid; t < BM; t += NT) rowoff[par][t] = (r0 + t < R) ? run_offset(r0 + t, a.runs, a.nrr) : 0;
+    for (int t = tid; t < BN; t += NT) coloff[par][t] = (c0 + t < S) ? run_offset(c0 + t, a.runs + a.nrr, a.ncr) : 0;
   };
   // Paired stores: lanes 2t and 2t + 1 hold columns c and c + 1 of the same
   // rows; they swap one value (DPP quad_perm [1,0,3,2]) so that the even lane
@@ -973,7 +973,7 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     if (kPairable && pairs) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
         const int32_t gi = r0 + row, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
         const int32_t gj = c0 + col, gl = kb + l;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -995,14 +995,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int row = e / BK, l = e % BK;
       const int32_t gi = r0 + row, gl = kb + l;
       ra[q] = (gi < R && gl < k1) ? a.X[(int64_t)gi * K + gl] : make_float2(0.f, 0.f);
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int col = e / BK, l = e % BK;
       const int32_t gj = c0 + col, gl = kb + l;
       rb[q] = (gj < S && gl < k1) ? a.Y[(int64_t)gj * K + gl] : make_float2(0.f, 0.f);
@@ -1012,14 +1012,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     if (kPairable && pairs) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
         *(float2 *)&As[st][0][row][l] = make_float2(ra[2 * q].x, ra[2 * q + 1].x);
         *(float2 *)&As[st][1][row][l] = make_float2(ra[2 * q].y, ra[2 * q + 1].y);
       }
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + 256 * q;
+        const int p = tid + NT * q;
         const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
         *(float2 *)&Bs[st][0][col][l] = make_float2(rb[2 * q].x, rb[2 * q + 1].x);
         *(float2 *)&Bs[st][1][col][l] = make_float2(rb[2 * q].y, rb[2 * q + 1].y);
@@ -1028,14 +1028,14 @@ __global__ __launch_bounds__(256, 2) void k_cgemm(StepArgs a, int32_t kchunk, ui
     }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int row = e / BK, l = e % BK;
       As[st][0][row][l] = ra[q].x;
       As[st][1][row][l] = ra[q].y;
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int col = e / BK, l = e % BK;
       Bs[st][0][col][l] = rb[q].x;
       Bs[st][1][col][l] = rb[q].y;
@@ -1399,12 +1399,12 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   // share their L2 lines (persistent workgroups drift apart over many
   // tiles), with loads two K stages ahead.
   const int64_t ntiles = tiles_r * tiles_c;
+  // eight waves of WM x WN/2 where both tile sides reach 64 (four waves per
+  // SIMD at 128 VGPRs); the 32-wide tiles keep four waves (their narrow
+  // operand tile has fewer entries per K stage than 512 threads)
+  constexpr bool kWide = BM >= 64 && BN >= 64;
+  constexpr int TWN = kWide ? WN / 2 : WN, TNT = kWide ? 512 : 256;
   if (kchunk > 64) {
-    // eight waves of WM x WN/2 where both tile sides reach 64; the 32-wide
-    // tiles keep four waves (their narrow operand tile has fewer entries per
-    // K stage than 512 threads)
-    constexpr bool kWide = BM >= 64 && BN >= 64;
-    constexpr int TWN = kWide ? WN / 2 : WN, TNT = kWide ? 512 : 256;
     dim3 grid((unsigned)ntiles, (unsigned)a.splits);
     hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, TWN, TNT>), grid, dim3(TNT), 0, stream, a, kchunk,
                        (uint32_t)tiles_r, (uint32_t)tiles_c);
@@ -1415,7 +1415,7 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   dim3 grid((unsigned)g, (unsigned)a.splits);
-  hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, WN>), grid, dim3(256), 0, stream, a, (int32_t)kchunk,
+  hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, TWN, TNT>), grid, dim3(TNT), 0, stream, a, (int32_t)kchunk,
                      (uint32_t)tiles_r, (uint32_t)tiles_c);
   return hipGetLastError();
 }
