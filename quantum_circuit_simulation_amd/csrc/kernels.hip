@@ -1645,7 +1645,8 @@ __global__ __launch_bounds__(256) void k_skinny_z(StepArgsZ a, int64_t kchunk) {
 // MFMAs per 16x16 complex block and the count is exactly 8 m n k flops.
 // LDS holds both tiles as (re, im) planes of doubles, [rows][BK + 2]; tiles
 // 64x64 (four waves of 32x32), BK = 8, two LDS stages, XCD-aware tile order,
-// one tile per workgroup.
+// one tile per workgroup; loads two K stages ahead and unchecked loads for
+// interior tiles, as in k_cgemm_tile.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256, 2) void k_zgemm(StepArgsZ a, int64_t kchunk, uint32_t tiles_r, uint32_t tiles_c) {
@@ -1685,51 +1686,76 @@ __global__ __launch_bounds__(256, 2) void k_zgemm(StepArgsZ a, int64_t kchunk, u
         accI[mb][nb][r] = 0.0;
       }
 
-  double2 ra[A_PER], rb[B_PER];
-  auto gload = [&](int64_t kt) {
+  // two register stages, as in k_cgemm_tile
+  double2 ra[2][A_PER], rb[2][B_PER];
+  const bool interior = r0 + BM <= R && c0 + BN <= S && (k1 - k0) % BK == 0;
+  auto gload = [&](auto bufc, int64_t kt) {
+    constexpr int buf = decltype(bufc)::value;
     const int64_t kb = k0 + kt * BK;
+    if (interior) {
+#pragma unroll
+      for (int q = 0; q < A_PER; ++q) {
+        const int e = tid + 256 * q;
+        ra[buf][q] = a.X[(r0 + e / BK) * K + kb + e % BK];
+      }
+#pragma unroll
+      for (int q = 0; q < B_PER; ++q) {
+        const int e = tid + 256 * q;
+        rb[buf][q] = a.Y[(c0 + e / BK) * K + kb + e % BK];
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
       const int row = e / BK, l = e % BK;
       const int64_t gi = r0 + row, gl = kb + l;
-      ra[q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : czero<double2>();
+      ra[buf][q] = (gi < R && gl < k1) ? a.X[gi * K + gl] : czero<double2>();
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
       const int e = tid + 256 * q;
       const int col = e / BK, l = e % BK;
       const int64_t gj = c0 + col, gl = kb + l;
-      rb[q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : czero<double2>();
+      rb[buf][q] = (gj < S && gl < k1) ? a.Y[gj * K + gl] : czero<double2>();
     }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](auto bufc, int st) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + 256 * q;
       const int row = e / BK, l = e % BK;
-      As[st][0][row][l] = ra[q].x;
-      As[st][1][row][l] = ra[q].y;
+      As[st][0][row][l] = ra[buf][q].x;
+      As[st][1][row][l] = ra[buf][q].y;
     }
 #pragma unroll
     for (int q = 0; q < B_PER; ++q) {
       const int e = tid + 256 * q;
       const int col = e / BK, l = e % BK;
-      Bs[st][0][col][l] = rb[q].x;
-      Bs[st][1][col][l] = rb[q].y;
+      Bs[st][0][col][l] = rb[buf][q].x;
+      Bs[st][1][col][l] = rb[buf][q].y;
     }
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   if (nkt > 0) {
-    gload(0);
-    lstore(0);
+    gload(I0{}, 0);
+    if (nkt > 1) gload(I1{}, 1);
+    lstore(I0{}, 0);
   }
   __syncthreads();
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int st = (int)(kt & 1);
-    if (kt + 1 < nkt) gload(kt + 1);
+  auto iter = [&](int64_t kt, auto cur) {
+    constexpr int st = decltype(cur)::value;
+    using Other = std::integral_constant<int, 1 - st>;
 #pragma unroll
     for (int l2 = 0; l2 < BK; l2 += 2) {
+      if (l2 == BK / 2) {
+        // stage kt + 1 into the other LDS buffer, then the loads of kt + 2
+        if (kt + 1 < nkt) lstore(Other{}, 1 - st);
+        if (kt + 2 < nkt) gload(cur, kt + 2);
+      }
       double av[MB], brv[NB], biv[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) av[mb] = As[st][plane][wr * WM + mb * 16 + l16][l2 + lofs];
@@ -1746,9 +1772,14 @@ __global__ __launch_bounds__(256, 2) void k_zgemm(StepArgsZ a, int64_t kchunk, u
           accI[mb][nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mb], biv[nb], accI[mb][nb], 0, 0, 0);
         }
     }
-    if (kt + 1 < nkt) lstore(st ^ 1);
     __syncthreads();
+  };
+  int64_t kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    iter(kt, I0{});
+    iter(kt + 1, I1{});
   }
+  if (kt < nkt) iter(kt, I0{});
 
   const bool partial = a.splits > 1;
   if (!partial) {
