@@ -94,7 +94,9 @@ def test_delta_relayout_is_exact(case, permuted, delta_lhs):
 # innermost run (extent 2, 8 or 3) belongs to the data leaf, which the
 # planner therefore places on the column side (paired stores for even
 # extents, single stores for odd); persistent and one-tile GEMM, split K
-ROW_INNER_CASES = [(12, 8, 2, 1), (12, 8, 2, 3), (12, 10, 2, 3), (8, 11, 2, 1), (8, 6, 3, 1), (14, 6, 2, 3)]
+# (17, 6, ...) and (17, 5, ...): 2^17 columns, 64 / 32 rows, K = 64 / 32
+ROW_INNER_CASES = [(12, 8, 2, 1), (12, 8, 2, 3), (12, 10, 2, 3), (8, 11, 2, 1), (8, 6, 3, 1), (14, 6, 2, 3),
+                   (17, 6, 2, 3), (17, 5, 2, 1)]
 
 
 @pytest.mark.parametrize("delta_lhs", [False, True], ids=["delta_rhs", "delta_lhs"])
@@ -135,11 +137,13 @@ def test_delta_relayout_complex128_is_exact(case):
     assert np.array_equal(got, expected.astype(np.complex128))
 
 
-# (log2 m, log2 n, log2 k, precision): GEMM (persistent, one-tile and
-# split-K), skinny; the split-bf16 mode represents 1 exactly (lo part 0)
+# (log2 m, log2 n, log2 k, precision): GEMM (persistent, one-tile,
+# split-K, few rows with short K), skinny; the split-bf16 mode represents 1
+# exactly (lo part 0)
 ONES_CASES = [
     (12, 12, 12, 0), (12, 12, 8, 0), (9, 9, 14, 0), (20, 2, 6, 0), (2, 20, 6, 0), (16, 4, 4, 0),
     (12, 12, 12, 1), (9, 9, 14, 1),
+    (6, 17, 3, 0), (5, 17, 7, 0),            # few rows, short K, many columns
 ]
 
 
