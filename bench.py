@@ -299,12 +299,13 @@ class TreeWorkload:
                                    "7x8 depth 16 reaches width 2^59 with this search"}
         elif which == "grid7x8":
             net = circuits.grid_fsim(7, 8, 11, 505).to_network()
-            tree = trees.search_tree(net, trials=200, seed=1)
+            log("building the 7x8 tree: best of 200 recursive-bisection trees ...")
+            tree = trees.partition_search(net, trials=200, seed=1)
             self.config = {"workload": "grid-7x8-d11-amplitude", "seed": 505,
-                           "tree": "best of 200 seeded randomized-greedy trees (seed 1)",
+                           "tree": "best of 200 seeded recursive-bisection trees (seed 1)",
                            "note": "the 56-qubit grid of the slicing comparison at the depth whose in-house tree "
-                                   "reaches width 2^34; unsliced it needs 394 GiB, so it runs at the smallest "
-                                   "slicing whose workspace fits"}
+                                   "fits one GPU (width 2^32; the randomized greedy reaches 2^34 with 5x the "
+                                   "flops); runs at the smallest slicing whose workspace fits"}
         elif which == "hexagonal":
             from workloads import hexagonal
             net = hexagonal.honeycomb(16, 16, 8, 606)

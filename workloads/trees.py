@@ -241,3 +241,144 @@ def state_vector_tree(net: Network) -> Tree:
     step is a (2^(n-2) x 4 x 4) product with the state."""
     from .network import caterpillar
     return caterpillar(net.num_leaves)
+
+
+def _bisect(W: np.ndarray, rng, imbalance: float, passes: int = 6) -> np.ndarray:
+    """Balanced two-way split of a weighted graph (dense symmetric W, zero
+    diagonal) with a small cut: the graph Laplacian's Fiedler vector, split
+    at a random point inside the balance window, then Fiduccia-Mattheyses
+    passes (move the unlocked vertex of largest cut reduction that keeps the
+    balance, keep the best prefix of the moves).  Returns a boolean side per
+    vertex."""
+    n = W.shape[0]
+    lo = max(1, int(np.floor(n * (1.0 - imbalance) / 2)))
+    hi = min(n - 1, int(np.ceil(n * (1.0 + imbalance) / 2)))
+    lap = np.diag(W.sum(axis=1)) - W
+    _, vecs = np.linalg.eigh(lap)
+    f = vecs[:, 1] + 1e-6 * rng.standard_normal(n)
+    order = np.argsort(f)
+    n0 = int(rng.integers(lo, hi + 1))          # vertices on side False
+    side = np.zeros(n, dtype=bool)
+    side[order[n0:]] = True
+    for _ in range(passes):
+        s = side.astype(np.float64)
+        other = np.where(side, W @ (1.0 - s), W @ s)
+        same = W.sum(axis=1) - other
+        gain = other - same
+        locked = np.zeros(n, dtype=bool)
+        count0 = int(n - side.sum())
+        cut = 0.0
+        best, best_k = 0.0, 0
+        moves = []
+        for _step in range(n):
+            can = ~locked & np.where(side, count0 + 1 <= hi, count0 - 1 >= lo)
+            if not can.any():
+                break
+            g = np.where(can, gain + 1e-9 * rng.random(n), -np.inf)
+            i = int(np.argmax(g))
+            cut -= gain[i]
+            new = not side[i]
+            side[i] = new
+            count0 += -1 if new else 1
+            locked[i] = True
+            # neighbours now on i's side lose 2 w, the others gain 2 w
+            gain += np.where(side == new, -2.0, 2.0) * W[i]
+            gain[i] = -gain[i]
+            moves.append(i)
+            if cut < best - 1e-12:
+                best, best_k = cut, len(moves)
+        for i in moves[best_k:]:
+            side[i] = not side[i]
+        if best_k == 0:
+            break
+    return side
+
+
+def partition_tree(net: Network, seed: int = 0, imbalance: float = 0.2, cutoff: int = 10) -> Tree:
+    """Contraction tree by recursive balanced bisection of the leaves: each
+    set of leaves is split in two with a small cut (the closed modes joining
+    the halves, weighted by log2 of their extents), both halves are
+    contracted recursively and their results are contracted last; sets of at
+    most ``cutoff`` leaves are contracted by the greedy rule (smallest result
+    first).  Seeded; ``imbalance`` bounds each split's size ratio."""
+    import math
+    rng = np.random.default_rng(seed)
+    L = net.num_leaves
+    ext = net.extents
+    lg = [math.log2(float(e)) for e in ext]
+    W = np.zeros((L, L))
+    holders: Dict[int, List[int]] = {}
+    for i, ms in enumerate(net.leaves):
+        for x in ms:
+            holders.setdefault(x, []).append(i)
+    for x, hs in holders.items():
+        if len(hs) == 2:
+            a, b = hs
+            W[a, b] += lg[x]
+            W[b, a] += lg[x]
+    modes: Dict[int, frozenset] = {i: frozenset(m) for i, m in enumerate(net.leaves)}
+    lhs: List[int] = []
+    rhs: List[int] = []
+
+    def contract(a: int, b: int) -> int:
+        K = modes[a] & modes[b]
+        c = L + len(lhs)
+        modes[c] = (modes[a] | modes[b]) - K
+        lhs.append(a)
+        rhs.append(b)
+        return c
+
+    def size(ms) -> float:
+        return sum(lg[x] for x in ms)
+
+    def greedy(ids: List[int]) -> int:
+        live = list(ids)
+        while len(live) > 1:
+            best = None
+            for u in range(len(live)):
+                for v in range(u + 1, len(live)):
+                    a, b = live[u], live[v]
+                    K = modes[a] & modes[b]
+                    if not K:
+                        continue
+                    c = size(modes[a]) + size(modes[b]) - 2 * size(K)
+                    key = (c, c - size(modes[a]) - size(modes[b]), min(a, b), max(a, b))
+                    if best is None or key < best[0]:
+                        best = (key, a, b)
+            if best is None:
+                a, b = sorted(live)[:2]
+            else:
+                a, b = best[1], best[2]
+            live.remove(a)
+            live.remove(b)
+            live.append(contract(a, b))
+        return live[0]
+
+    def build(nodes: List[int]) -> int:
+        if len(nodes) <= cutoff:
+            return greedy(nodes)
+        idx = np.array(nodes)
+        side = _bisect(W[np.ix_(idx, idx)], rng, imbalance)
+        p = [int(v) for v in idx[~side]]
+        q = [int(v) for v in idx[side]]
+        return contract(build(p), build(q))
+
+    build(list(range(L)))
+    return Tree(lhs, rhs)
+
+
+def partition_search(net: Network, trials: int, seed: int = 0, imbalances=(0.05, 0.1, 0.2, 0.3, 0.45),
+                     cutoffs=(6, 10, 16)) -> Tree:
+    """Best of ``trials`` seeded partition trees (random imbalance and
+    cutoff per trial) by (largest intermediate, total flops)."""
+    rng = np.random.default_rng(seed)
+    best, best_key = None, None
+    for _ in range(trials):
+        im = float(imbalances[int(rng.integers(len(imbalances)))])
+        co = int(cutoffs[int(rng.integers(len(cutoffs)))])
+        tr = partition_tree(net, seed=int(rng.integers(1 << 31)), imbalance=im, cutoff=co)
+        c = tree_cost(net, tr)
+        key = (c["max_elems"], c["flops"])
+        if best_key is None or key < best_key:
+            best, best_key = tr, key
+    return best
