@@ -764,6 +764,10 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     value = wl.flops / (ms_per_step / 1e3) / 1e12
+    # each timed step on its own: first launch's start to last launch's end
+    step_ms = [evs[s][0][0].elapsed_time(evs[s][-1][1]) for s in range(args.steps)]
+    step_stats = {"median": round(float(np.median(step_ms)), 3), "min": round(float(min(step_ms)), 3),
+                  "max": round(float(max(step_ms)), 3)} if step_ms else None
 
     # per-launch durations (HIP events on the stream the library enqueues on)
     per = {}
@@ -843,7 +847,7 @@ def main():
         cpu = wl.cpu_baseline()
     line = {"metric": "contraction-tree TFLOP/s (complex64) + % FP32 MFMA peak; wall time per result",
             "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+            "ms_per_step": round(ms_per_step, 3), "step_ms": step_stats, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f64" if z else ("f32 via bf16x3" if prec else "f32"), "data": "synthetic",
             **({"pct_fp64_mfma_peak": round(100.0 * value / PEAK_FP64_MFMA, 2)} if z else
                {"pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2)}),
