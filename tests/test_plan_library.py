@@ -153,3 +153,24 @@ def test_complex128_plan_doubles_entry_bytes():
     assert r128.arena_bytes >= 2 * r64.arena_bytes - 256 * len(tree.lhs)
     assert p128.stats()["bytes"] == 2 * p64.stats()["bytes"]
     assert p128.stats()["flops"] == p64.stats()["flops"]
+
+
+def test_precision_option_is_validated_and_leaves_the_plan_unchanged():
+    net = lattice.peps(4, 4, 2)
+    tree = lattice.row_major_tree(4)
+    with pytest.raises(tnc.TncError) as e:
+        qa.Plan.from_network(net, tree, precision=2)
+    assert e.value.name == "TNC_ERR_INVALID_ARG"
+    with pytest.raises(tnc.TncError) as e:
+        qa.Plan.from_network(net, tree, precision=qa.PREC_BF16X3, dtype=qa.TNC_C128)
+    assert e.value.name == "TNC_ERR_INVALID_ARG"
+    exact = qa.Plan.from_network(net, tree)
+    split = qa.Plan.from_network(net, tree, precision=qa.PREC_BF16X3)
+    # the split-bf16 mode changes only the product kernel: same orders, offsets, descriptors
+    assert split.workspace_bytes == exact.workspace_bytes
+    L = net.num_leaves
+    for t in range(L + len(tree.lhs)):
+        assert split.tensor_order(t) == exact.tensor_order(t)
+        assert split.tensor_offset(t) == exact.tensor_offset(t)
+    for s in range(len(tree.lhs)):
+        assert split.node(s) == exact.node(s)
