@@ -1155,42 +1155,13 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t
   // two register stages: the loads of K stage kt + 2 are in flight while
   // stage kt + 1 is written to LDS and stage kt is multiplied
   float2 ra[2][A_PER], rb[2][B_PER];
-  // 16-byte loads of entry pairs (l, l + 1) and 8-byte LDS writes when K is
-  // even (every K chunk then starts and ends on an even entry) and both
-  // operands are 16-byte aligned; single entries otherwise
-  // (off here: the pair path lifts this kernel past 256 VGPRs, and the
-  // 64x256 / 256x64 tiles then spill)
-  constexpr bool kPairable = false;
-  const bool pairs = false;
-  // every load of the tile in bounds: full rows and columns, K chunk a
-  // multiple of BK
+  // single 8-byte entries per load (16-byte pair loads were slower here on
+  // the largest shapes); a tile wholly inside C whose K chunk is a multiple
+  // of BK loads without bounds checks
   const bool interior = r0 + BM <= R && c0 + BN <= S && (k1 - k0) % BK == 0;
   auto gload = [&](auto bufc, int64_t kt) {
     constexpr int buf = decltype(bufc)::value;
     const int64_t kb = k0 + kt * BK;
-    if (kPairable && pairs) {
-#pragma unroll
-      for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + NT * q;
-        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
-        const int64_t gi = r0 + row, gl = kb + l;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gi < R && gl < k1) v = *(const float4 *)(a.X + gi * K + gl);
-        ra[buf][2 * q] = make_float2(v.x, v.y);
-        ra[buf][2 * q + 1] = make_float2(v.z, v.w);
-      }
-#pragma unroll
-      for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + NT * q;
-        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
-        const int64_t gj = c0 + col, gl = kb + l;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gj < S && gl < k1) v = *(const float4 *)(a.Y + gj * K + gl);
-        rb[buf][2 * q] = make_float2(v.x, v.y);
-        rb[buf][2 * q + 1] = make_float2(v.z, v.w);
-      }
-      return;
-    }
     if (interior) {
 #pragma unroll
       for (int q = 0; q < A_PER; ++q) {
@@ -1221,23 +1192,6 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t
   };
   auto lstore = [&](auto bufc, int st) {
     constexpr int buf = decltype(bufc)::value;
-    if (kPairable && pairs) {
-#pragma unroll
-      for (int q = 0; q < A_PER / 2; ++q) {
-        const int p = tid + NT * q;
-        const int row = p / (BK / 2), l = 2 * (p % (BK / 2));
-        *(float2 *)&As[st][0][row][l] = make_float2(ra[buf][2 * q].x, ra[buf][2 * q + 1].x);
-        *(float2 *)&As[st][1][row][l] = make_float2(ra[buf][2 * q].y, ra[buf][2 * q + 1].y);
-      }
-#pragma unroll
-      for (int q = 0; q < B_PER / 2; ++q) {
-        const int p = tid + NT * q;
-        const int col = p / (BK / 2), l = 2 * (p % (BK / 2));
-        *(float2 *)&Bs[st][0][col][l] = make_float2(rb[buf][2 * q].x, rb[buf][2 * q + 1].x);
-        *(float2 *)&Bs[st][1][col][l] = make_float2(rb[buf][2 * q].y, rb[buf][2 * q + 1].y);
-      }
-      return;
-    }
 #pragma unroll
     for (int q = 0; q < A_PER; ++q) {
       const int e = tid + NT * q;
