@@ -103,7 +103,8 @@ typedef struct {
                                  prod(extents) slices into `out` (page section 1.1) */
   uint64_t align;             /* 256: arena alignment in bytes (power of two, >= 256) */
   uint64_t capacity_bytes;    /* 0: no limit; else fail with OUT_OF_MEMORY above it */
-  uint64_t tiny_mnk;          /* 32768: steps with m*n*k <= this share grouped launches */
+  uint64_t tiny_mnk;          /* 131072: steps with m*n*k <= this and at most tiny_mnk / 4
+                                 operand + output entries share grouped launches */
   int32_t max_group;          /* 256: most steps in one grouped launch */
   int32_t precision;          /* TNC_PREC_EXACT: arithmetic of GEMM-class complex64 steps */
 } tnc_plan_options;

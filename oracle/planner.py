@@ -329,7 +329,7 @@ class _Arena:
 
 
 def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), align=256,
-              tiny_mnk=1 << 15, max_group=256, dtype=0) -> Plan:
+              tiny_mnk=1 << 17, max_group=256, dtype=0) -> Plan:
     """dtype 0: complex64 (8-byte entries), 1: complex128 (16-byte entries)."""
     eb = 16 if dtype == 1 else 8
     validate(extents, leaves, out_modes, lhs, rhs, sliced)
@@ -362,7 +362,7 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
         flops_u += 8 * mu * nu * ku
         nbytes += eb * (m * k + n * k + m * n)
         max_elems = max(max_elems, m * n)
-        if m * n * k <= tiny_mnk:
+        if m * n * k <= tiny_mnk and m * k + n * k + m * n <= tiny_mnk // 4:
             cls = CLASS_TINY
         elif min(m, n) <= SKINNY_MAX_SIDE:
             cls = CLASS_SKINNY

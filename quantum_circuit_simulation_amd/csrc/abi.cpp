@@ -61,7 +61,7 @@ void tnc_plan_options_default(tnc_plan_options *o) {
   o->sliced_modes = nullptr;
   o->align = 256;
   o->capacity_bytes = 0;
-  o->tiny_mnk = 32768;
+  o->tiny_mnk = 131072;
   o->max_group = 256;
   o->precision = TNC_PREC_EXACT;
 }

@@ -272,6 +272,49 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
 
 constexpr int tiny_stage_entries(int bytes) { return bytes == 8 ? 4096 : 2048; }
 
+// Complex64 member with 32 <= R, S <= 128 whose operands are staged in LDS:
+// the four waves take 32 x 32 output blocks in turn, each on the FP32 matrix
+// cores with the (re, im) scheme of k_cgemm (lanes 0-31 supply xr and (yr,
+// yi), lanes 32-63 xi and (-yi, yr)); row and column offsets of the output
+// come from a table built once per member.
+__device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *Y, float2 *C, int R, int S, int K,
+                                                 const RunDev *rr, int nrr, const RunDev *cr, int ncr, int b,
+                                                 int64_t *toff) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  if (tid < 128) toff[tid] = tid < R ? run_offset(tid, rr, nrr) : 0;
+  else toff[tid] = tid - 128 < S ? run_offset(tid - 128, cr, ncr) : 0;
+  __syncthreads();
+  const float *Xf = (const float *)X, *Yf = (const float *)Y;
+  const int bc = (S + 31) / 32, nblk = ((R + 31) / 32) * bc;
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int i0 = (blk / bc) * 32, j0 = (blk % bc) * 32;
+    const int row = i0 + l32, col = j0 + l32;
+    const bool rv = row < R, cv = col < S;
+    f32x16 aR, aI;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      aR[r] = 0.f;
+      aI[r] = 0.f;
+    }
+    for (int l = 0; l < K; ++l) {
+      const float xa = rv ? Xf[2 * (row * K + l) + h] : 0.f;
+      const float yre = cv ? Yf[2 * (col * K + l)] : 0.f;
+      const float yim = cv ? Yf[2 * (col * K + l) + 1] : 0.f;
+      aR = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, h ? -yim : yre, aR, 0, 0, 0);
+      aI = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, h ? yre : yim, aI, 0, 0, 0);
+    }
+    if (cv) {
+      const int64_t co = toff[128 + col];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gi = i0 + (r / 4) * 8 + h * 4 + (r % 4);
+        if (gi < R) store_c(C + toff[gi] + co, make_float2(aR[r], aI[r]), b);
+      }
+    }
+  }
+}
+
 // One member of a tiny group, computed by one workgroup.  Both operands of a
 // member whose (R + S) K entries fit are first copied into LDS with
 // coalesced loads (one round trip), so the passes below read LDS instead of
@@ -279,7 +322,7 @@ constexpr int tiny_stage_entries(int bytes) { return bytes == 8 ? 4096 : 2048; }
 // reused by the next member.
 template <typename T>
 __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const *ptab, const RunDev *runs,
-                                            int32_t beta, T *stage) {
+                                            int32_t beta, T *stage, int64_t *toff) {
   constexpr int kStage = tiny_stage_entries(sizeof(T));
   const T *X = (const T *)ptab[d.x_buf] + d.x_off;
   const T *Y = (const T *)ptab[d.y_buf] + d.y_off;
@@ -294,6 +337,13 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
     __syncthreads();
     X = stage;
     Y = stage + nx;
+    if constexpr (sizeof(T) == 8) {
+      if (R >= 32 && S >= 32 && R <= 128 && S <= 128) {
+        tiny_member_mfma(X, Y, C, R, S, K, rr, d.nrr, cr, d.ncr, beta && d.is_root, toff);
+        __syncthreads();
+        return;
+      }
+    }
   }
   const int outputs = R * S;
   // lanes per output: a power of two <= 64 that keeps the workgroup busy
@@ -328,7 +378,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
                                               int32_t beta) {
   __shared__ T stage[tiny_stage_entries(sizeof(T))];
-  tiny_member<T>(descs[blockIdx.x], ptab, runs, beta, stage);
+  __shared__ int64_t toff[256];
+  tiny_member<T>(descs[blockIdx.x], ptab, runs, beta, stage, toff);
 }
 
 // ---------------------------------------------------------------------------

@@ -423,7 +423,9 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     bytes += (double)eb * ((double)nd.m * nd.k + (double)nd.n * nd.k + (double)nd.m * nd.n);
     max_elems = std::max<uint64_t>(max_elems, (uint64_t)(nd.m * nd.n));
     __int128 mnk = (__int128)nd.m * nd.n * nd.k;
-    if (mnk <= (__int128)o.tiny_mnk) nd.cls = TNC_CLASS_TINY;
+    // a tiny step runs in one workgroup: its flops and its entries are bounded
+    const __int128 entries = (__int128)nd.m * nd.k + (__int128)nd.n * nd.k + (__int128)nd.m * nd.n;
+    if (mnk <= (__int128)o.tiny_mnk && entries <= (__int128)(o.tiny_mnk / 4)) nd.cls = TNC_CLASS_TINY;
     else if (std::min(nd.m, nd.n) <= kSkinnyMaxSide) nd.cls = TNC_CLASS_SKINNY;
     else nd.cls = TNC_CLASS_GEMM;
     const auto &c_order = p->order[L + s];

@@ -179,7 +179,7 @@ class Plan:
 
     def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
                  order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
-                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 15, max_group: int = 256, dtype: int = TNC_C64,
+                 capacity_bytes: int = 0, tiny_mnk: int = 1 << 17, max_group: int = 256, dtype: int = TNC_C64,
                  precision: int = 0):
         lib = load_library()
         self._lib = lib

@@ -36,7 +36,7 @@ def _run(net, tree, **kw):
     return run(net, tree, precision=qa.PREC_BF16X3, **kw)
 
 
-GEMM_CASES = [c for c in PAIR_CASES if min(c[3] ** c[0], c[3] ** c[1]) > 16 and c[3] ** (c[0] + c[1] + c[2]) > 1 << 15]
+GEMM_CASES = [c for c in PAIR_CASES if min(c[3] ** c[0], c[3] ** c[1]) > 16 and c[3] ** (c[0] + c[1] + c[2]) > 1 << 17]
 
 
 @pytest.mark.parametrize("case", GEMM_CASES)

@@ -116,7 +116,7 @@ def test_random_networks(seed):
         pytest.skip("too wide")
     ref = oracle.contract_network(net, tree)
     for order in (0, 1):
-        got, plan = _gpu_run(net, tree, order=order, tiny_mnk=int(rng.choice([0, 256, 1 << 15])),
+        got, plan = _gpu_run(net, tree, order=order, tiny_mnk=int(rng.choice([0, 256, 1 << 15, 1 << 17])),
                              max_group=int(rng.integers(1, 8)))
         _assert_close(got, ref)
 

@@ -54,7 +54,7 @@ def test_flat_skinny_shapes(S, K):
         net, tree = _net(S, K, layout, seed=1000 + 37 * S + K + i)
         print(f"[gpu] {net.name}", flush=True)
         ref = oracle.contract_network(net, tree)
-        got, plan = run(net, tree)
+        got, plan = run(net, tree, tiny_mnk=0)
         nd = plan.node(0)
         assert nd["kernel_class"] == qa.CLASS_SKINNY and nd["splits"] == 1
         ok, err = rel_err_ok(got, ref, TOL)
@@ -67,7 +67,7 @@ def test_flat_skinny_slices_accumulate(S, K):
     net, tree = _net(S, K, "row", seed=77 + S + K, sliced_ext=3)
     print(f"[gpu] {net.name} sliced", flush=True)
     ref = oracle.contract_network(net, tree)
-    got, plan = run(net, tree, sliced=[4])
+    got, plan = run(net, tree, sliced=[4], tiny_mnk=0)
     assert plan.stats()["num_slices"] == 3
     ok, err = rel_err_ok(got, ref, TOL)
     assert ok, f"max scaled error {err:.3e}"

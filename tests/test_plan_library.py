@@ -73,7 +73,7 @@ def test_random_plans_match_oracle(seed, policy):
     closed = trees.closed_modes(net)
     nsl = int(rng.integers(0, min(3, len(closed)) + 1))
     sliced = [int(x) for x in rng.choice(closed, size=nsl, replace=False)] if nsl else []
-    _check(net, tree, policy=policy, sliced=sliced, tiny_mnk=int(rng.choice([0, 64, 1 << 15])),
+    _check(net, tree, policy=policy, sliced=sliced, tiny_mnk=int(rng.choice([0, 64, 1 << 15, 1 << 17])),
            max_group=int(rng.integers(1, 6)), dtype=int(seed % 2))
 
 
