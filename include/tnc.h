@@ -191,13 +191,17 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  *               overwritten
  *   workspace   device pointer, >= tnc_plan_workspace_bytes, 256-byte aligned
  *   stream      hipStream_t to enqueue on (NULL = the default stream)
- * Asynchronous: returns once the work is enqueued; no host synchronisation,
- * no allocation.  The caller keeps the plan, leaves, out and workspace alive
- * until the stream has finished.  One plan may run concurrently on different
+ * Asynchronous: returns once the work is enqueued; no host synchronisation
+ * and no device allocation.  The first call on a plan outside stream capture
+ * allocates a pinned host copy of the plan's step descriptors (a few KB to a
+ * few MB, freed by tnc_plan_destroy) which a kernel then reads on every call;
+ * a call captured into a graph before that copy exists records an ordinary
+ * host-to-device copy of the descriptors instead.  The caller keeps the plan,
+ * leaves, out and workspace alive until the stream has finished.  One plan may run concurrently on different
  * streams given distinct workspaces and outputs.  A sliced plan loops over all
  * slices and leaves their sum in `out`.
- * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP (launch failure; faults
- * surface at the caller's next synchronisation).
+ * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP (pinned allocation or launch
+ * failure; faults surface at the caller's next synchronisation).
  */
 tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
                        uint64_t workspace_bytes, void *stream);

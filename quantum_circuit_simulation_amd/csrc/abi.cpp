@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -14,6 +15,13 @@
 
 struct tnc_plan_s {
   tnc::PlanImpl impl;
+  // pinned host copy of the descriptor blob (blob_bytes, zero padded), made by
+  // the first tnc_execute and read by the upload kernel on every call
+  std::mutex pin_mu;
+  void *blob_pinned = nullptr;
+  ~tnc_plan_s() {
+    if (blob_pinned) (void)hipHostFree(blob_pinned);
+  }
 };
 
 namespace {
@@ -171,10 +179,44 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
   char *blob = ws + p.ptab_bytes;
   char *arena = ws + p.header_bytes;
 
-  tnc_status st = check(tnc::launch_write_ptrs(ptab, arena, out, leaves, p.L, stream), stream, "k_write_ptrs launch");
-  if (st != TNC_OK) return st;
-  st = check(hipMemcpyAsync(blob, p.blob.data(), p.blob.size(), hipMemcpyHostToDevice, stream), stream,
-             "descriptor upload (hipMemcpyAsync)");
+  // The pinned descriptor copy is made by the first call outside stream
+  // capture; a call captured before it exists records a plain copy from the
+  // plan's host memory instead (a memcpy node of the graph).
+  const void *pinned = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(plan->pin_mu);
+    if (!plan->blob_pinned) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        cs = hipStreamCaptureStatusActive;
+      }
+      if (cs == hipStreamCaptureStatusNone) {
+        void *h = nullptr;
+        hipError_t e = hipHostMalloc(&h, p.blob_bytes, hipHostMallocDefault);
+        if (e != hipSuccess || !h) {
+          (void)hipGetLastError();
+          g_last_error = std::string("pinned descriptor copy (hipHostMalloc): ") + hipGetErrorString(e);
+          return TNC_ERR_HIP;
+        }
+        std::memset(h, 0, p.blob_bytes);
+        std::memcpy(h, p.blob.data(), p.blob.size());
+        plan->blob_pinned = h;
+      }
+    }
+    pinned = plan->blob_pinned;
+  }
+  tnc_status st;
+  if (pinned) {
+    st = check(tnc::launch_header(ptab, arena, out, leaves, p.L, pinned, blob, p.blob_bytes, stream), stream,
+               "k_header launch");
+  } else {
+    st = check(hipMemcpyAsync(blob, p.blob.data(), p.blob.size(), hipMemcpyHostToDevice, stream), stream,
+               "descriptor upload (hipMemcpyAsync)");
+    if (st == TNC_OK)
+      st = check(tnc::launch_header(ptab, arena, out, leaves, p.L, nullptr, blob, 0, stream), stream,
+                 "k_header launch");
+  }
   if (st != TNC_OK) return st;
 
   const auto *runs = reinterpret_cast<const tnc::RunDev *>(blob + p.blob_runs);

@@ -18,8 +18,8 @@
 // Outputs are stored through "runs": rowoff(i) + coloff(j), so a product
 // whose order interleaves the two operands' modes is written in place with
 // no separate permute.  k_copy_tiled / k_copy are strided permutes used only
-// for leaf staging and for the naive-order ablation; k_write_ptrs fills the
-// workspace's pointer table.
+// for leaf staging and for the naive-order ablation; k_header fills the
+// workspace's pointer table and descriptor blob.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -106,9 +106,14 @@ struct PtrChunk {
   int32_t first;
 };
 
-__global__ void k_write_ptrs(void **dst, PtrChunk c) {
-  int t = threadIdx.x;
-  for (int i = t; i < c.count; i += blockDim.x) dst[c.first + i] = c.p[i];
+// Workspace header in one launch: block 0 also writes the first pointer chunk;
+// every block copies 16-byte words of the descriptor blob straight from the
+// plan's pinned host copy (visible to the GPU) into the workspace.
+__global__ __launch_bounds__(256) void k_header(void **ptab, PtrChunk c, const uint4 *src, uint4 *dst, int64_t n16) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < c.count; i += 256) ptab[c.first + i] = c.p[i];
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += step) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -1826,9 +1831,10 @@ hipError_t run_split_reduce(const StepArgsT<T> &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *const *leaves, int32_t num_leaves,
-                             hipStream_t stream) {
+hipError_t launch_header(void **ptab, void *arena, void *out, const void *const *leaves, int32_t num_leaves,
+                         const void *blob_src, void *blob_dst, uint64_t blob_bytes, hipStream_t stream) {
   const int32_t total = num_leaves + 2;
+  const int64_t n16 = (int64_t)(blob_bytes / 16);
   for (int32_t first = 0; first < total; first += kPtrsPerLaunch) {
     PtrChunk c;
     c.first = first;
@@ -1837,7 +1843,13 @@ hipError_t launch_write_ptrs(void **dst, void *arena, void *out, const void *con
       int32_t id = first + i;
       c.p[i] = id == 0 ? arena : id == 1 ? out : const_cast<void *>(leaves[id - 2]);
     }
-    hipLaunchKernelGGL(k_write_ptrs, dim3(1), dim3(64), 0, stream, dst, c);
+    // the blob rides with the first chunk
+    const int64_t words = first == 0 ? n16 : 0;
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 64) blocks = 64;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_header, dim3((unsigned)blocks), dim3(256), 0, stream, ptab, c, (const uint4 *)blob_src,
+                       (uint4 *)blob_dst, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,7 +1,8 @@
-"""tnc_execute enqueues only kernel launches and one host-to-device copy of
-plan-owned descriptors, so a caller may capture it in a HIP graph: every
-replay (with unrelated eager work and synchronisations in between) must give
-the eager result bit for bit."""
+"""tnc_execute enqueues only kernel launches (the descriptors come from a
+pinned host copy read by a kernel, or, when the first call on a plan is
+captured, from one host-to-device copy), so a caller may capture it in a HIP
+graph: every replay (with unrelated eager work and synchronisations in
+between) must give the eager result bit for bit."""
 
 import numpy as np
 import pytest
@@ -55,3 +56,39 @@ def test_graph_replays_match_eager(which):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep} differs from the eager result"
+
+
+def test_graph_captured_before_first_eager_call():
+    """A plan whose first call is captured records the descriptor copy in the
+    graph; its replays and its later eager calls match a second plan's eager
+    result bit for bit."""
+    import torch
+    import quantum_circuit_simulation_amd as qa
+    net = circuits.brickwork(12, 8, 103).to_network(open_qubits=[0, 1, 2])
+    tree = trees.greedy_tree(net)
+    print("[gpu] graph capture before the first eager call", flush=True)
+    captured, reference = qa.Plan.from_network(net, tree), qa.Plan.from_network(net, tree)
+    leaves = [torch.from_numpy(d).cuda() for d in net.data]
+    size = int(np.prod(captured.out_shape))
+    out = torch.empty(size, dtype=torch.complex64, device="cuda")
+    ref = torch.empty_like(out)
+    ws, ws_ref = qa.alloc_workspace(captured), qa.alloc_workspace(reference)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured.execute(leaves, out, ws)
+    reference.execute(leaves, ref, ws_ref)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager result"
+    out.fill_(float("nan"))
+    captured.execute(leaves, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
