@@ -1020,13 +1020,15 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchu
 
   float2 ra[A_PER], rb[B_PER];
   // 16-byte loads of entry pairs (l, l + 1) and 8-byte LDS writes when K is
-  // even (every K chunk then starts and ends on an even entry) and both
-  // operands are 16-byte aligned; single entries otherwise
-  constexpr bool kPairable = (A_PER % 2 == 0) && (B_PER % 2 == 0);
-  const bool pairs = kPairable && (a.K % 2 == 0) && aligned16(a.X) && aligned16(a.Y);
+  // even (every K chunk then starts and ends on an even entry), the operand
+  // is 16-byte aligned and each thread holds an even number of its entries
+  // per stage; decided per operand, single entries otherwise
+  constexpr bool kPairA = A_PER % 2 == 0, kPairB = B_PER % 2 == 0;
+  const bool pairs_a = kPairA && (a.K % 2 == 0) && aligned16(a.X);
+  const bool pairs_b = kPairB && (a.K % 2 == 0) && aligned16(a.Y);
   auto gload = [&](int32_t r0, int32_t c0, int32_t kt) {
     const int32_t kb = k0 + kt * BK;
-    if (kPairable && pairs) {
+    if (kPairA && pairs_a) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
         const int p = tid + NT * q;
@@ -1037,6 +1039,16 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchu
         ra[2 * q] = make_float2(v.x, v.y);
         ra[2 * q + 1] = make_float2(v.z, v.w);
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < A_PER; ++q) {
+        const int e = tid + NT * q;
+        const int row = e / BK, l = e % BK;
+        const int32_t gi = r0 + row, gl = kb + l;
+        ra[q] = (gi < R && gl < k1) ? a.X[(int64_t)gi * K + gl] : make_float2(0.f, 0.f);
+      }
+    }
+    if (kPairB && pairs_b) {
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
         const int p = tid + NT * q;
@@ -1047,25 +1059,18 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchu
         rb[2 * q] = make_float2(v.x, v.y);
         rb[2 * q + 1] = make_float2(v.z, v.w);
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + NT * q;
-      const int row = e / BK, l = e % BK;
-      const int32_t gi = r0 + row, gl = kb + l;
-      ra[q] = (gi < R && gl < k1) ? a.X[(int64_t)gi * K + gl] : make_float2(0.f, 0.f);
-    }
-#pragma unroll
-    for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + NT * q;
-      const int col = e / BK, l = e % BK;
-      const int32_t gj = c0 + col, gl = kb + l;
-      rb[q] = (gj < S && gl < k1) ? a.Y[(int64_t)gj * K + gl] : make_float2(0.f, 0.f);
+      for (int q = 0; q < B_PER; ++q) {
+        const int e = tid + NT * q;
+        const int col = e / BK, l = e % BK;
+        const int32_t gj = c0 + col, gl = kb + l;
+        rb[q] = (gj < S && gl < k1) ? a.Y[(int64_t)gj * K + gl] : make_float2(0.f, 0.f);
+      }
     }
   };
   auto lstore = [&](int st) {
-    if (kPairable && pairs) {
+    if (kPairA && pairs_a) {
 #pragma unroll
       for (int q = 0; q < A_PER / 2; ++q) {
         const int p = tid + NT * q;
@@ -1073,6 +1078,16 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchu
         *(float2 *)&As[st][0][row][l] = make_float2(ra[2 * q].x, ra[2 * q + 1].x);
         *(float2 *)&As[st][1][row][l] = make_float2(ra[2 * q].y, ra[2 * q + 1].y);
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < A_PER; ++q) {
+        const int e = tid + NT * q;
+        const int row = e / BK, l = e % BK;
+        As[st][0][row][l] = ra[q].x;
+        As[st][1][row][l] = ra[q].y;
+      }
+    }
+    if (kPairB && pairs_b) {
 #pragma unroll
       for (int q = 0; q < B_PER / 2; ++q) {
         const int p = tid + NT * q;
@@ -1080,21 +1095,14 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm(StepArgs a, int32_t kchu
         *(float2 *)&Bs[st][0][col][l] = make_float2(rb[2 * q].x, rb[2 * q + 1].x);
         *(float2 *)&Bs[st][1][col][l] = make_float2(rb[2 * q].y, rb[2 * q + 1].y);
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int q = 0; q < A_PER; ++q) {
-      const int e = tid + NT * q;
-      const int row = e / BK, l = e % BK;
-      As[st][0][row][l] = ra[q].x;
-      As[st][1][row][l] = ra[q].y;
-    }
-#pragma unroll
-    for (int q = 0; q < B_PER; ++q) {
-      const int e = tid + NT * q;
-      const int col = e / BK, l = e % BK;
-      Bs[st][0][col][l] = rb[q].x;
-      Bs[st][1][col][l] = rb[q].y;
+      for (int q = 0; q < B_PER; ++q) {
+        const int e = tid + NT * q;
+        const int col = e / BK, l = e % BK;
+        Bs[st][0][col][l] = rb[q].x;
+        Bs[st][1][col][l] = rb[q].y;
+      }
     }
   };
 
