@@ -4,8 +4,8 @@ the PEPS and honeycomb bulk shapes, run by the persistent GEMM kernel with
 64 x 256 or 32 x 256 tiles).  Every output entry is compared with the oracle
 on the same seeded inputs (|g - r| <= 1e-4 max(|r|, rms(r))).
 
-Cases: both row-tile heights (R <= 32 and R <= 64), K = 8 (one K stage), 64
-and 128, ragged R and S (extent-3 modes: S not a multiple of the tile width),
+Cases: both row-tile heights (R <= 32 and R <= 64), K = 8 (one K stage), 20,
+24 and 40 (odd stage counts, K not a power of two), 64 and 128, ragged R and S (extent-3 modes: S not a multiple of the tile width),
 outputs that allow paired 16-byte stores and ones that do not (odd innermost
 extent), staged (re-laid) leaves, and a sliced shared mode, whose slices are
 added into the output."""
@@ -74,7 +74,7 @@ def _check(net, tree, sliced=()):
     k = nd["k"]
     # a few-rows, short-K, many-columns GEMM step
     assert nd["kernel_class"] == 2 and nd["splits"] == 1
-    assert 16 < R <= 64 and S >= 1 << 16 and k % 8 == 0 and 8 <= k <= 128, (R, S, k)
+    assert 16 < R <= 64 and S >= 1 << 16 and k % 4 == 0 and 8 <= k <= 128, (R, S, k)
     ref = oracle.contract_network(net, tree)
     ok, err = rel_err_ok(got, ref, TOL)
     assert ok, f"max scaled error {err:.3e}"
@@ -87,6 +87,9 @@ CASES = [
     ([2] * 6, [2] * 16, [2] * 7),        # R = 64, K = 128
     ([3] * 3, [3] * 11, [2] * 4),        # R = 27, S = 3^11 (last tile partial), K = 16
     ([2, 3, 7], [2] * 15 + [3], [2] * 5),  # R = 42, S = 3 * 2^15, K = 32
+    ([2] * 6, [2] * 16, [2, 2, 2, 3]),   # R = 64, K = 24: three K stages per block
+    ([3, 2, 2, 2, 2], [2] * 14 + [5], [2, 2, 2, 5]),  # R = 48, S = 5 * 2^14, K = 40
+    ([2] * 5, [2] * 16, [2, 2, 5]),      # R = 32, K = 20: the last K stage partly empty
 ]
 
 
