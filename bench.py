@@ -47,9 +47,12 @@ def fill_gaussian(t, seed):
 
 
 def gemm_kernel_name(R, S, K, splits):
-    """The k_cgemm instance the library launches for an oriented GEMM step
-    (same rule as its launcher): one tile per workgroup for K chunks above
-    64, persistent workgroups otherwise; tile shape by the short side."""
+    """The GEMM kernel the library launches for an oriented complex64 step
+    (same rule as its launcher): k_cgemm_small for R S <= 2^19 and K <= 512;
+    otherwise one tile per workgroup for K chunks above 64, persistent
+    workgroups below, tile shape by the short side."""
+    if R * S <= 1 << 19 and K <= 512:
+        return "k_cgemm_small"
     kchunk = K if splits <= 1 else -(-(-(-K // splits)) // 8) * 8
     base = "k_cgemm_tile" if kchunk > 64 else "k_cgemm"
     if S > 64 and R <= 32:

@@ -99,7 +99,7 @@ __device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p 
 // ---------------------------------------------------------------------------
 // device pointer table
 
-constexpr int kPtrsPerLaunch = 250;
+constexpr int kPtrsPerLaunch = 400;  // 3.2 KB of kernel arguments
 struct PtrChunk {
   void *p[kPtrsPerLaunch];
   int32_t count;
@@ -276,20 +276,18 @@ __global__ __launch_bounds__(256) void k_copy_tiled(const CopyDesc *desc, const 
 // grouped tiny steps: one workgroup per step
 
 constexpr int tiny_stage_entries(int bytes) { return bytes == 8 ? 4096 : 2048; }
+constexpr int kTinyTable = 256;  // rows (and columns) covered by a member's offset table
 
-// Complex64 member with 32 <= R, S <= 128 whose operands are staged in LDS:
+// Complex64 member with 32 <= R, S <= 256 whose operands are staged in LDS:
 // the four waves take 32 x 32 output blocks in turn, each on the FP32 matrix
 // cores with the (re, im) scheme of k_cgemm (lanes 0-31 supply xr and (yr,
 // yi), lanes 32-63 xi and (-yi, yr)); row and column offsets of the output
-// come from a table built once per member.
+// come from the member's offset table (rows at toff[0..255], columns at
+// toff[256..511]).
 __device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *Y, float2 *C, int R, int S, int K,
-                                                 const RunDev *rr, int nrr, const RunDev *cr, int ncr, int b,
-                                                 int64_t *toff) {
+                                                 int b, const int64_t *toff) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  if (tid < 128) toff[tid] = tid < R ? run_offset(tid, rr, nrr) : 0;
-  else toff[tid] = tid - 128 < S ? run_offset(tid - 128, cr, ncr) : 0;
-  __syncthreads();
   const float *Xf = (const float *)X, *Yf = (const float *)Y;
   const int bc = (S + 31) / 32, nblk = ((R + 31) / 32) * bc;
   for (int blk = wave; blk < nblk; blk += 4) {
@@ -310,7 +308,7 @@ __device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *
       aI = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, h ? yre : yim, aI, 0, 0, 0);
     }
     if (cv) {
-      const int64_t co = toff[128 + col];
+      const int64_t co = toff[kTinyTable + col];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int gi = i0 + (r / 4) * 8 + h * 4 + (r % 4);
@@ -323,8 +321,10 @@ __device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *
 // One member of a tiny group, computed by one workgroup.  Both operands of a
 // member whose (R + S) K entries fit are first copied into LDS with
 // coalesced loads (one round trip), so the passes below read LDS instead of
-// waiting on a global load per pass.  Ends with a barrier, so `stage` may be
-// reused by the next member.
+// waiting on a global load per pass.  A member with R, S <= 256 first tabulates
+// the output offsets of its rows and columns (one run walk per row and per
+// column instead of two per output).  Ends with a barrier, so `stage` and
+// `toff` may be reused by the next member.
 template <typename T>
 __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const *ptab, const RunDev *runs,
                                             int32_t beta, T *stage, int64_t *toff) {
@@ -335,19 +335,25 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
   const RunDev *rr = runs + d.runs_index;
   const RunDev *cr = rr + d.nrr;
   const int R = d.R, S = d.S, K = d.K;
-  if ((int64_t)(R + S) * K <= kStage) {
+  const bool table = R <= kTinyTable && S <= kTinyTable;
+  const bool staged = (int64_t)(R + S) * K <= kStage;
+  if (table)
+    for (int t = threadIdx.x; t < 2 * kTinyTable; t += 256)
+      toff[t] = t < kTinyTable ? (t < R ? run_offset(t, rr, d.nrr) : 0)
+                               : (t - kTinyTable < S ? run_offset(t - kTinyTable, cr, d.ncr) : 0);
+  if (staged) {
     const int nx = R * K, ny = S * K;
     for (int e = threadIdx.x; e < nx; e += 256) stage[e] = X[e];
     for (int e = threadIdx.x; e < ny; e += 256) stage[nx + e] = Y[e];
-    __syncthreads();
     X = stage;
     Y = stage + nx;
-    if constexpr (sizeof(T) == 8) {
-      if (R >= 32 && S >= 32 && R <= 128 && S <= 128) {
-        tiny_member_mfma(X, Y, C, R, S, K, rr, d.nrr, cr, d.ncr, beta && d.is_root, toff);
-        __syncthreads();
-        return;
-      }
+  }
+  if (table || staged) __syncthreads();
+  if constexpr (sizeof(T) == 8) {
+    if (staged && table && R >= 32 && S >= 32) {
+      tiny_member_mfma(X, Y, C, R, S, K, beta && d.is_root, toff);
+      __syncthreads();
+      return;
     }
   }
   const int outputs = R * S;
@@ -373,7 +379,8 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
     }
     if (o < outputs && lane == 0) {
       const int i = o / S, j = o - (o / S) * S;
-      store_c(C + run_offset(i, rr, d.nrr) + run_offset(j, cr, d.ncr), acc, b);
+      const int64_t off = table ? toff[i] + toff[kTinyTable + j] : run_offset(i, rr, d.nrr) + run_offset(j, cr, d.ncr);
+      store_c(C + off, acc, b);
     }
   }
   __syncthreads();
@@ -383,7 +390,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
                                               int32_t beta) {
   __shared__ T stage[tiny_stage_entries(sizeof(T))];
-  __shared__ int64_t toff[256];
+  __shared__ int64_t toff[2 * kTinyTable];
   tiny_member<T>(descs[blockIdx.x], ptab, runs, beta, stage, toff);
 }
 
@@ -1382,6 +1389,133 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t
     }
 }
 
+// Small GEMM-class steps (R S <= 2^19, K <= 512): too few 128 x 128 tiles
+// to occupy the chip, so the tiled kernels wait on one tile's K loop per
+// CU.  Here one workgroup of four waves takes one 32 x 32 block of C and the
+// waves split its K range in four (chunks of whole 8-entry stages); each
+// wave reads its rows of X and Y straight from global memory (the operands
+// of a small step sit in L2), one stage ahead, into the (re, im) MFMA scheme
+// of k_cgemm; the four partial blocks are summed through LDS and wave 0
+// stores the block (16-byte row pairs when C's innermost run is an even
+// unit-stride column run).
+constexpr int64_t kSmallGemmRS = int64_t(1) << 19;
+constexpr int64_t kSmallGemmK = 512;
+
+template <bool PAIR>
+__global__ __launch_bounds__(256) void k_cgemm_small(StepArgs a, uint32_t blocks_c) {
+  __shared__ float red[3][32][64];
+  __shared__ int64_t rowoff[32], coloff[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int32_t R = (int32_t)a.R, S = (int32_t)a.S, K = (int32_t)a.K;
+  const int32_t r0 = (int32_t)(blockIdx.x / blocks_c) * 32, c0 = (int32_t)(blockIdx.x % blocks_c) * 32;
+  if (tid < 32) rowoff[tid] = r0 + tid < R ? run_offset(r0 + tid, a.runs, a.nrr) : 0;
+  else if (tid < 64) coloff[tid - 32] = c0 + tid - 32 < S ? run_offset(c0 + tid - 32, a.runs + a.nrr, a.ncr) : 0;
+
+  // this wave's K range, in whole stages of 8 entries
+  const int32_t kq = ((K + 31) / 32) * 8;
+  const int32_t kb = wave * kq, ke = min(K, kb + kq);
+  const int nst = ke > kb ? (ke - kb + 7) / 8 : 0;
+  const int32_t row = r0 + l32, col = c0 + l32;
+  const bool rv = row < R, cv = col < S;
+  const float2 *xrow = a.X + (int64_t)(rv ? row : 0) * K;
+  const float2 *yrow = a.Y + (int64_t)(cv ? col : 0) * K;
+
+  f32x16 accR, accI;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    accR[r] = 0.f;
+    accI[r] = 0.f;
+  }
+  // a stage: entries l0 .. l0 + 7 of this lane's X row and Y row
+  auto load = [&](float4 (&x)[4], float4 (&y)[4], int st) {
+    const int32_t l0 = kb + st * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t l = l0 + 2 * q;
+      if constexpr (PAIR) {
+        x[q] = rv && l < ke ? *(const float4 *)(xrow + l) : make_float4(0.f, 0.f, 0.f, 0.f);
+        y[q] = cv && l < ke ? *(const float4 *)(yrow + l) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        const float2 z = make_float2(0.f, 0.f);
+        const float2 x0 = rv && l < ke ? xrow[l] : z, x1 = rv && l + 1 < ke ? xrow[l + 1] : z;
+        const float2 y0 = cv && l < ke ? yrow[l] : z, y1 = cv && l + 1 < ke ? yrow[l + 1] : z;
+        x[q] = make_float4(x0.x, x0.y, x1.x, x1.y);
+        y[q] = make_float4(y0.x, y0.y, y1.x, y1.y);
+      }
+    }
+  };
+  auto compute = [&](const float4 (&x)[4], const float4 (&y)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float xa0 = h ? x[q].y : x[q].x, xa1 = h ? x[q].w : x[q].z;
+      const float br0 = h ? -y[q].y : y[q].x, bi0 = h ? y[q].x : y[q].y;
+      const float br1 = h ? -y[q].w : y[q].z, bi1 = h ? y[q].z : y[q].w;
+      accR = __builtin_amdgcn_mfma_f32_32x32x2f32(xa0, br0, accR, 0, 0, 0);
+      accI = __builtin_amdgcn_mfma_f32_32x32x2f32(xa0, bi0, accI, 0, 0, 0);
+      accR = __builtin_amdgcn_mfma_f32_32x32x2f32(xa1, br1, accR, 0, 0, 0);
+      accI = __builtin_amdgcn_mfma_f32_32x32x2f32(xa1, bi1, accI, 0, 0, 0);
+    }
+  };
+  float4 xa[4], ya[4], xb[4], yb[4];
+  if (nst > 0) load(xa, ya, 0);
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) load(xb, yb, st + 1);
+    compute(xa, ya);
+    if (st + 1 >= nst) break;
+    if (st + 2 < nst) load(xa, ya, st + 2);
+    compute(xb, yb);
+  }
+
+  // sum the four waves' blocks in wave 0
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[wave - 1][r][lane] = accR[r];
+      red[wave - 1][16 + r][lane] = accI[r];
+    }
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      accR[r] += red[w][r][lane];
+      accI[r] += red[w][16 + r][lane];
+    }
+  const bool pair_store = a.ncr > 0 && a.runs[a.nrr + a.ncr - 1].stride == 1 &&
+                          (a.runs[a.nrr + a.ncr - 1].size % 2) == 0 && aligned16(a.C);
+  if (pair_store) {
+    const bool odd_lane = (l32 & 1) != 0;
+    const int cl0 = l32 & ~1;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int q = (r / 4) * 8 + h * 4 + (r % 4);
+      const float sr = odd_lane ? accR[r] : accR[r + 1];
+      const float si = odd_lane ? accI[r] : accI[r + 1];
+      const float pr = dpp_f<0xB1>(sr), pi = dpp_f<0xB1>(si);
+      const int rr = odd_lane ? q + 1 : q;
+      float4 v = odd_lane ? make_float4(pr, pi, accR[r + 1], accI[r + 1]) : make_float4(accR[r], accI[r], pr, pi);
+      if (r0 + rr < R && c0 + cl0 < S) {
+        float4 *p = (float4 *)(a.C + rowoff[rr] + coloff[cl0]);
+        if (a.beta) {
+          const float4 o = *p;
+          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        }
+        *p = v;
+      }
+    }
+    return;
+  }
+  if (!cv) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int q = (r / 4) * 8 + h * 4 + (r % 4);
+    if (r0 + q < R) store_c(a.C + rowoff[q] + coloff[l32], make_float2(accR[r], accI[r]), a.beta);
+  }
+}
+
 int g_num_cus = 0;
 
 int num_cus() {
@@ -1984,6 +2118,16 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits <= 1) return e;
     return run_split_reduce(a, stream);
+  }
+  // small steps: one workgroup per 32 x 32 block, K split over its waves
+  if (a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK) {
+    const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
+    const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
+    if (pair)
+      hipLaunchKernelGGL(k_cgemm_small<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a, (uint32_t)bc);
+    else
+      hipLaunchKernelGGL(k_cgemm_small<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a, (uint32_t)bc);
+    return hipGetLastError();
   }
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;

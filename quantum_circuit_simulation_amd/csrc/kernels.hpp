@@ -41,7 +41,7 @@ using StepArgsZ = StepArgsT<double2>;  // complex128
 // `z` selects complex128 entries (16 bytes) instead of complex64 (8 bytes).
 // Writes the pointer table [arena, out, leaves...] to ptab and copies
 // blob_bytes (a multiple of 16) of descriptors from pinned host memory to
-// blob_dst; one launch per 250 pointers, the blob with the first.
+// blob_dst; one launch per 400 pointers, the blob with the first.
 hipError_t launch_header(void **ptab, void *arena, void *out, const void *const *leaves, int32_t num_leaves,
                          const void *blob_src, void *blob_dst, uint64_t blob_bytes, hipStream_t stream);
 hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, const void *const *ptab,

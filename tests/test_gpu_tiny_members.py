@@ -1,0 +1,97 @@
+"""GPU parity for single tiny-class steps (grouped-launch kernel, one
+workgroup per step) across its three paths: operands staged in LDS and
+multiplied on the matrix cores (complex64, 32 <= R, S <= 256), staged and
+multiplied by scalar lanes (R or S below 32, or complex128), and members too
+wide for the per-member offset table (R or S above 256), whose output
+offsets are walked per entry.  Ragged extents (3, 5, 7), interleaved output
+orders and a sliced shared mode (slices added into the output) are
+included.  Every output entry is compared with the oracle on the same seeded
+inputs (|g - r| <= tol max(|r|, rms(r)))."""
+
+import numpy as np
+import pytest
+
+import oracle
+import quantum_circuit_simulation_amd as qa
+from tests.conftest import rel_err_ok
+from workloads import sweep
+from workloads.network import Network, Tree
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _pair(m_ext, n_ext, k_ext, seed, interleave=False, sliced_ext=0):
+    """lhs over [M | K], rhs over [N | K]; output [M | N], or with
+    ``interleave`` the modes of M and N alternating (many short runs)."""
+    rng = np.random.default_rng(seed)
+    nm, nn, nk = len(m_ext), len(n_ext), len(k_ext)
+    M = list(range(nm))
+    N = list(range(nm, nm + nn))
+    K = list(range(nm + nn, nm + nn + nk))
+    ext = list(m_ext) + list(n_ext) + list(k_ext)
+    if sliced_ext:
+        K = K + [len(ext)]
+        ext.append(sliced_ext)
+    extents = np.array(ext, dtype=np.int64)
+    out = M + N
+    if interleave:
+        out = []
+        for i in range(max(nm, nn)):
+            out += ([M[i]] if i < nm else []) + ([N[i]] if i < nn else [])
+    A, B = M + K, N + K
+    data = [sweep.complex_gaussian(rng, tuple(int(extents[x]) for x in A)),
+            sweep.complex_gaussian(rng, tuple(int(extents[x]) for x in B))]
+    name = f"tiny m={int(np.prod(m_ext))} n={int(np.prod(n_ext))} k={int(np.prod(k_ext))}"
+    return Network(extents, [A, B], out, data, name=name), Tree([0], [1])
+
+
+CASES = [
+    # (M extents, N extents, K extents, interleave)
+    ([2] * 5, [2] * 8, [2, 2], False),            # 32 x 256 x 4: matrix cores, table of 256 columns
+    ([2] * 5, [2] * 8, [2, 2], True),             # same, interleaved output
+    ([3, 2, 2, 2, 2], [5, 5, 2, 2, 2], [3], True),  # 48 x 200 x 3: ragged blocks
+    ([3] + [2] * 5, [2] * 8, [2], False),         # 96 x 256 x 2
+    ([3] * 4, [7, 2, 2, 2, 2], [2, 2], True),     # 81 x 112 x 4
+    ([2] * 4, [2] * 6, [2, 2], True),             # 16 x 64 x 4: scalar lanes, table
+    ([2] * 9, [2] * 5, [2], True),                # 512 x 32 x 2: beyond the table, run walks
+    ([5], [2] * 8, [2] * 4, False),               # 5 x 256 x 16: not staged (too many entries), table
+]
+
+
+def _check(net, tree, dtype=qa.TNC_C64, tol=1e-4, sliced=()):
+    from tests.gpu_util import run
+    print(f"[gpu] {net.name} dtype={dtype} sliced={list(sliced)}", flush=True)
+    got, plan = run(net, tree, dtype=dtype, tiny_mnk=1 << 17, sliced=list(sliced))
+    assert plan.node(0)["kernel_class"] == 0
+    ref = oracle.contract_network(net, tree)
+    ok, err = rel_err_ok(got, ref, tol)
+    assert ok, f"max scaled error {err:.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"R{int(np.prod(c[0]))}S{int(np.prod(c[1]))}K{int(np.prod(c[2]))}{'i' if c[3] else ''}")
+def test_tiny_member_paths(case):
+    m, n, k, inter = case
+    net, tree = _pair(m, n, k, seed=8100 + int(np.prod(m)) + int(np.prod(n)), interleave=inter)
+    _check(net, tree)
+
+
+@pytest.mark.parametrize("case", CASES[:3] + CASES[5:7], ids=lambda c: f"R{int(np.prod(c[0]))}S{int(np.prod(c[1]))}")
+def test_tiny_member_paths_complex128(case):
+    m, n, k, inter = case
+    net, tree = _pair(m, n, k, seed=8200 + int(np.prod(m)), interleave=inter)
+    _check(net, tree, dtype=qa.TNC_C128, tol=1e-10)
+
+
+def test_tiny_member_sliced_accumulates():
+    """A shared mode of extent 3 sliced: each slice's 32 x 256 x 4 tiny step
+    is added into the output."""
+    net, tree = _pair([2] * 5, [2] * 8, [2, 2], seed=8300, sliced_ext=3)
+    _check(net, tree, sliced=[net.num_modes - 1])
