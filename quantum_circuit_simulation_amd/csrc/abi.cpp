@@ -260,7 +260,7 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
           e = tnc::launch_copy_tiled(cdesc + op.first, op.max_count, ptab, ints, sd, beta, z, stream);
           break;
         case tnc::OP_TINY_GROUP:
-          e = tnc::launch_tiny(tdesc + op.first, op.count, ptab, runs, beta, z, stream);
+          e = tnc::launch_tiny(tdesc + op.first, op.count, op.max_count, ptab, runs, beta, z, stream);
           break;
         case tnc::OP_SKINNY:
         case tnc::OP_GEMM: {

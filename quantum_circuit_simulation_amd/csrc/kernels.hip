@@ -285,12 +285,12 @@ constexpr int kTinyTable = 256;  // rows (and columns) covered by a member's off
 // come from the member's offset table (rows at toff[0..255], columns at
 // toff[256..511]).
 __device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *Y, float2 *C, int R, int S, int K,
-                                                 int b, const int64_t *toff) {
+                                                 int b, const int64_t *toff, int part, int parts) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const float *Xf = (const float *)X, *Yf = (const float *)Y;
   const int bc = (S + 31) / 32, nblk = ((R + 31) / 32) * bc;
-  for (int blk = wave; blk < nblk; blk += 4) {
+  for (int blk = wave + 4 * part; blk < nblk; blk += 4 * parts) {
     const int i0 = (blk / bc) * 32, j0 = (blk % bc) * 32;
     const int row = i0 + l32, col = j0 + l32;
     const bool rv = row < R, cv = col < S;
@@ -327,7 +327,7 @@ __device__ __forceinline__ void tiny_member_mfma(const float2 *X, const float2 *
 // `toff` may be reused by the next member.
 template <typename T>
 __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const *ptab, const RunDev *runs,
-                                            int32_t beta, T *stage, int64_t *toff) {
+                                            int32_t beta, T *stage, int64_t *toff, int part, int parts) {
   constexpr int kStage = tiny_stage_entries(sizeof(T));
   const T *X = (const T *)ptab[d.x_buf] + d.x_off;
   const T *Y = (const T *)ptab[d.y_buf] + d.y_off;
@@ -351,7 +351,7 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
   if (table || staged) __syncthreads();
   if constexpr (sizeof(T) == 8) {
     if (staged && table && R >= 32 && S >= 32) {
-      tiny_member_mfma(X, Y, C, R, S, K, beta && d.is_root, toff);
+      tiny_member_mfma(X, Y, C, R, S, K, beta && d.is_root, toff, part, parts);
       __syncthreads();
       return;
     }
@@ -364,7 +364,7 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
   const int lane = threadIdx.x % G;
   const int grp = threadIdx.x / G;
   const int b = beta && d.is_root;
-  for (int o0 = 0; o0 < outputs; o0 += per_pass) {
+  for (int o0 = part * per_pass; o0 < outputs; o0 += per_pass * parts) {
     const int o = o0 + grp;
     T acc = czero<T>();
     if (o < outputs) {
@@ -386,12 +386,14 @@ __device__ __forceinline__ void tiny_member(const TinyDesc &d, const void *const
   __syncthreads();
 }
 
+// `parts` workgroups per member: workgroup b takes member b / parts and the
+// output blocks (or passes) congruent to b % parts.
 template <typename T>
 __global__ __launch_bounds__(256) void k_tiny(const TinyDesc *descs, const void *const *ptab, const RunDev *runs,
-                                              int32_t beta) {
+                                              int32_t beta, int parts) {
   __shared__ T stage[tiny_stage_entries(sizeof(T))];
   __shared__ int64_t toff[2 * kTinyTable];
-  tiny_member<T>(descs[blockIdx.x], ptab, runs, beta, stage, toff);
+  tiny_member<T>(descs[blockIdx.x / parts], ptab, runs, beta, stage, toff, (int)(blockIdx.x % parts), parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -2029,12 +2031,19 @@ hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *co
   return hipGetLastError();
 }
 
-hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
-                       int32_t beta, bool z, hipStream_t stream) {
+hipError_t launch_tiny(const TinyDesc *descs, int32_t count, int64_t max_rs, const void *const *ptab,
+                       const RunDev *runs, int32_t beta, bool z, hipStream_t stream) {
+  // a group of few large members spreads each over several workgroups (one
+  // per 2048 outputs of the largest member, at most 8, at most 256 in all)
+  int64_t parts = count > 0 ? 256 / count : 1;
+  if (parts > 8) parts = 8;
+  if (parts > max_rs / 2048) parts = max_rs / 2048;
+  if (parts < 1) parts = 1;
+  const dim3 grid((unsigned)(count * parts));
   if (z)
-    hipLaunchKernelGGL(k_tiny<double2>, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
+    hipLaunchKernelGGL(k_tiny<double2>, grid, dim3(256), 0, stream, descs, ptab, runs, beta, (int)parts);
   else
-    hipLaunchKernelGGL(k_tiny<float2>, dim3((unsigned)count), dim3(256), 0, stream, descs, ptab, runs, beta);
+    hipLaunchKernelGGL(k_tiny<float2>, grid, dim3(256), 0, stream, descs, ptab, runs, beta, (int)parts);
   return hipGetLastError();
 }
 

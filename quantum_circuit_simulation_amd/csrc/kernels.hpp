@@ -48,8 +48,9 @@ hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, 
                        const int64_t *ints, const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream);
 hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *const *ptab, const int64_t *ints,
                              const SliceDigits &digits, int32_t beta, bool z, hipStream_t stream);
-hipError_t launch_tiny(const TinyDesc *descs, int32_t count, const void *const *ptab, const RunDev *runs,
-                       int32_t beta, bool z, hipStream_t stream);
+// max_rs: the largest member's R S (sets the workgroups per member).
+hipError_t launch_tiny(const TinyDesc *descs, int32_t count, int64_t max_rs, const void *const *ptab,
+                       const RunDev *runs, int32_t beta, bool z, hipStream_t stream);
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const StepArgs &a, hipStream_t stream);
 hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream);

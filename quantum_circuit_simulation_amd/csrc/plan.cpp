@@ -701,6 +701,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
         d.ncr = (int32_t)nd.col_runs.size();
         d.runs_index = nd.runs_index;
         tiny.push_back(d);
+        op.max_count = std::max(op.max_count, (int64_t)d.R * d.S);
       }
       p->program.push_back(op);
     } else {

@@ -77,7 +77,7 @@ struct Op {
   OpKind kind;
   int32_t first;   // OP_COPY: first index into copy descriptors; TINY: first tiny desc; else node
   int32_t count;   // OP_COPY / OP_TINY_GROUP: descriptors in the launch
-  int64_t max_count;  // OP_COPY: largest copy in the launch (grid sizing)
+  int64_t max_count;  // OP_COPY: largest copy in the launch; OP_TINY_GROUP: largest member R S (grid sizing)
 };
 
 struct PlanImpl {

@@ -5,7 +5,9 @@ multiplied by scalar lanes (R or S below 32, or complex128), and members too
 wide for the per-member offset table (R or S above 256), whose output
 offsets are walked per entry.  Ragged extents (3, 5, 7), interleaved output
 orders and a sliced shared mode (slices added into the output) are
-included.  Every output entry is compared with the oracle on the same seeded
+included; a single large member spreads over up to 8 workgroups (one per
+2048 outputs), each taking every 8th output block or pass.  Every output
+entry is compared with the oracle on the same seeded
 inputs (|g - r| <= tol max(|r|, rms(r)))."""
 
 import numpy as np
@@ -63,6 +65,7 @@ CASES = [
     ([2] * 4, [2] * 6, [2, 2], True),             # 16 x 64 x 4: scalar lanes, table
     ([2] * 9, [2] * 5, [2], True),                # 512 x 32 x 2: beyond the table, run walks
     ([5], [2] * 8, [2] * 4, False),               # 5 x 256 x 16: not staged (too many entries), table
+    ([5, 2, 2], [2] * 8, [2, 2], True),           # 20 x 256 x 4: scalar lanes on two workgroups
 ]
 
 
