@@ -1393,19 +1393,21 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t
 
 // Small GEMM-class steps (R S <= 2^19, K <= 512): too few 128 x 128 tiles
 // to occupy the chip, so the tiled kernels wait on one tile's K loop per
-// CU.  Here one workgroup of four waves takes one 32 x 32 block of C and the
-// waves split its K range in four (chunks of whole 8-entry stages); each
+// CU.  Here one workgroup of NW waves takes one 32 x 32 block of C and the
+// waves split its K range NW ways (chunks of whole 8-entry stages); each
 // wave reads its rows of X and Y straight from global memory (the operands
 // of a small step sit in L2), one stage ahead, into the (re, im) MFMA scheme
-// of k_cgemm; the four partial blocks are summed through LDS and wave 0
+// of k_cgemm; the NW partial blocks are summed through LDS and wave 0
 // stores the block (16-byte row pairs when C's innermost run is an even
 // unit-stride column run).
 constexpr int64_t kSmallGemmRS = int64_t(1) << 19;
 constexpr int64_t kSmallGemmK = 512;
 
-template <bool PAIR>
-__global__ __launch_bounds__(256) void k_cgemm_small(StepArgs a, uint32_t blocks_c) {
-  __shared__ float red[3][32][64];
+constexpr int kSmallGemmWaves = 4;
+
+template <bool PAIR, int NW>
+__global__ __launch_bounds__(64 * NW) void k_cgemm_small(StepArgs a, uint32_t blocks_c) {
+  __shared__ float red[NW - 1][32][64];
   __shared__ int64_t rowoff[32], coloff[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -1415,7 +1417,7 @@ __global__ __launch_bounds__(256) void k_cgemm_small(StepArgs a, uint32_t blocks
   else if (tid < 64) coloff[tid - 32] = c0 + tid - 32 < S ? run_offset(c0 + tid - 32, a.runs + a.nrr, a.ncr) : 0;
 
   // this wave's K range, in whole stages of 8 entries
-  const int32_t kq = ((K + 31) / 32) * 8;
+  const int32_t kq = ((K + 8 * NW - 1) / (8 * NW)) * 8;
   const int32_t kb = wave * kq, ke = min(K, kb + kq);
   const int nst = ke > kb ? (ke - kb + 7) / 8 : 0;
   const int32_t row = r0 + l32, col = c0 + l32;
@@ -1469,7 +1471,7 @@ __global__ __launch_bounds__(256) void k_cgemm_small(StepArgs a, uint32_t blocks
     compute(xb, yb);
   }
 
-  // sum the four waves' blocks in wave 0
+  // sum the waves' blocks in wave 0
   if (wave > 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1480,7 +1482,7 @@ __global__ __launch_bounds__(256) void k_cgemm_small(StepArgs a, uint32_t blocks
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
+  for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       accR[r] += red[w][r][lane];
@@ -2132,10 +2134,11 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
   if (a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK) {
     const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
     const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
+    constexpr int NW = kSmallGemmWaves;
     if (pair)
-      hipLaunchKernelGGL(k_cgemm_small<true>, dim3((unsigned)blocks), dim3(256), 0, stream, a, (uint32_t)bc);
+      hipLaunchKernelGGL((k_cgemm_small<true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
     else
-      hipLaunchKernelGGL(k_cgemm_small<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a, (uint32_t)bc);
+      hipLaunchKernelGGL((k_cgemm_small<false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
     return hipGetLastError();
   }
   // tile shape: keep the short side of the step inside one tile edge
