@@ -280,10 +280,14 @@ def _runs(c_order, ext, row_set):
     return row_runs, col_runs, inner, len(runs)
 
 
-def _split_rule(cls, R, S, k):
+def _split_rule(cls, R, S, k, c64):
     """K split count: enough workgroups to fill the chip, K chunks of at
-    least 64 (GEMM) / 1024 (skinny) entries."""
+    least 64 (GEMM) / 1024 (skinny) entries.  Complex64 GEMM-class steps
+    with R S <= 2^19 and K <= 512 are not split (the small-GEMM kernel
+    splits their K inside each workgroup)."""
     if cls == CLASS_GEMM:
+        if c64 and R * S <= 1 << 19 and k <= 512:
+            return 1
         tiles = _ceil_div(R, GEMM_NOMINAL_TILE) * _ceil_div(S, GEMM_NOMINAL_TILE)
         if tiles >= 256 or k < 128:
             return 1
@@ -380,7 +384,7 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
         R, Sx = (n, m) if swap else (m, n)
         if cls == CLASS_GEMM and max(R, Sx, k) >= 1 << 31:
             raise PlanError("UNSUPPORTED", "GEMM step with a side or K of 2^31 or more")
-        splits = _split_rule(cls, R, Sx, k)
+        splits = _split_rule(cls, R, Sx, k, eb == 8)
         node = Node(step=s, lhs=a, rhs=b, out=L + s, m=m, n=n, k=k, cls=cls, swap=swap, splits=splits,
                     row_runs=row_runs, col_runs=col_runs, inner_run=inner, interleaved=int(nruns > 2))
         # operand copies

@@ -81,9 +81,12 @@ class Arena {
   uint64_t peak_ = 0;
 };
 
-int32_t split_rule(int32_t cls, int64_t R, int64_t S, int64_t k) {
+int32_t split_rule(int32_t cls, int64_t R, int64_t S, int64_t k, bool c64) {
   // enough workgroups to fill the chip; K chunks of >= 64 (GEMM) / 1024 (skinny)
   if (cls == TNC_CLASS_GEMM) {
+    // complex64 steps with R S <= 2^19 and K <= 512 run whole in the
+    // small-GEMM kernel, which splits K over the waves of each block
+    if (c64 && R * S <= (int64_t(1) << 19) && k <= 512) return 1;
     int64_t tiles = ceil_div(R, kGemmNominalTile) * ceil_div(S, kGemmNominalTile);
     if (tiles >= 256 || k < 128) return 1;
     return (int32_t)std::max<int64_t>(1, std::min(pow2_floor(512 / tiles), pow2_floor(k / 64)));
@@ -440,7 +443,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     if (nd.cls == TNC_CLASS_GEMM && (R >= (int64_t(1) << 31) || Sx >= (int64_t(1) << 31) ||
                                      nd.k >= (int64_t(1) << 31)))
       return TNC_ERR_UNSUPPORTED;
-    nd.splits = split_rule(nd.cls, R, Sx, nd.k);
+    nd.splits = split_rule(nd.cls, R, Sx, nd.k, eb == 8);
     if (nd.splits > 1) nd.scratch_bytes = (uint64_t)nd.splits * (uint64_t)R * (uint64_t)Sx * eb;
     // operand copies
     for (int w = 0; w < 2; ++w) {
