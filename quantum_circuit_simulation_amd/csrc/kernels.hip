@@ -2081,6 +2081,19 @@ static bool skinny_flat_ok(const StepArgs &a) {
   return a.splits == 1 && a.R >= 4096 && pow2k && a.S >= 1 && a.S <= kSkinnyMax && ((uintptr_t)a.X & 15) == 0;
 }
 
+bool small_gemm_ok(const StepArgs &a) { return a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK; }
+
+hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
+  const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
+  const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
+  constexpr int NW = kSmallGemmWaves;
+  if (pair)
+    hipLaunchKernelGGL((k_cgemm_small<true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
+  else
+    hipLaunchKernelGGL((k_cgemm_small<false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
+  return hipGetLastError();
+}
+
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   if (skinny_flat_ok(a)) {
     if (a.S <= 1) return run_skinny_flat_k<1>(a, stream);
@@ -2089,6 +2102,9 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
     if (a.S <= 8) return run_skinny_flat_k<8>(a, stream);
     return run_skinny_flat_k<16>(a, stream);
   }
+  // few rows and a short K: the small-GEMM kernel (one workgroup per 32-row
+  // block) instead of one workgroup per row
+  if (a.R < 4096 && a.splits <= 1 && small_gemm_ok(a)) return run_cgemm_small(a, stream);
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
   // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
@@ -2131,16 +2147,7 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
     return run_split_reduce(a, stream);
   }
   // small steps: one workgroup per 32 x 32 block, K split over its waves
-  if (a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK) {
-    const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
-    const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
-    constexpr int NW = kSmallGemmWaves;
-    if (pair)
-      hipLaunchKernelGGL((k_cgemm_small<true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
-    else
-      hipLaunchKernelGGL((k_cgemm_small<false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
-    return hipGetLastError();
-  }
+  if (small_gemm_ok(a)) return run_cgemm_small(a, stream);
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
   if (a.S > 64 && a.R <= 32) e = run_cgemm<32, 256, 8, 32, 64>(a, stream);

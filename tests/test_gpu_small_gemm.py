@@ -5,7 +5,8 @@ ragged blocks (extent-3 and extent-5 modes), K odd (single-entry loads), K
 that leaves some waves without a stage (K = 20, 12), K at its bound (512,
 128 entries per wave), outputs with and without paired 16-byte stores, a
 re-laid operand, a sliced shared mode (slices added into the output), and
-K just above the bound (the tiled kernel).  Every output entry is compared
+K just above the bound (the tiled kernel), and skinny-class steps with
+fewer than 4096 rows, which take the same kernel.  Every output entry is compared
 with the oracle on the same seeded inputs
 (|g - r| <= 1e-4 max(|r|, rms(r)))."""
 
@@ -99,3 +100,27 @@ def test_small_shape_above_k_bound_uses_tiled_kernel():
     """32 x 64 x 1024: K above the bound, split K on the tiled kernel."""
     net, tree = _pair([2] * 5, [2] * 6, [2] * 10, seed=9300)
     _check(net, tree, small=False)
+
+
+SKINNY_CASES = [
+    # (M extents, N extents, K extents, interleave): skinny class (S <= 16), R < 4096
+    ([2] * 9, [2] * 4, [2] * 6, False),     # 512 x 16 x 64
+    ([3] * 5, [5], [2, 2, 2, 5], True),     # 243 x 5 x 40, ragged
+    ([2] * 10, [2], [3, 3, 3], False),      # 1024 x 2 x 27: K odd
+]
+
+
+@pytest.mark.parametrize("case", SKINNY_CASES, ids=lambda c: f"R{int(np.prod(c[0]))}S{int(np.prod(c[1]))}K{int(np.prod(c[2]))}")
+def test_small_skinny_steps(case):
+    """Skinny-class steps with fewer than 4096 rows and K <= 512 also run in
+    the small-GEMM kernel."""
+    from tests.gpu_util import run
+    m, n, k, inter = case
+    net, tree = _pair(m, n, k, seed=9400 + int(np.prod(k)), interleave=inter)
+    print(f"[gpu] {net.name} skinny", flush=True)
+    got, plan = run(net, tree, tiny_mnk=0)
+    nd = plan.node(0)
+    assert nd["kernel_class"] == 1 and nd["splits"] == 1
+    ref = oracle.contract_network(net, tree)
+    ok, err = rel_err_ok(got, ref, TOL)
+    assert ok, f"max scaled error {err:.3e}"
