@@ -82,13 +82,18 @@ class SweepWorkload:
         self.cases = [c for c in sweep.cases() if c["feasible"]] if cases is None else cases
         self.plans = []
         maxa = maxb = maxc = maxws = 0
+        plan_s = 0.0
         for c in self.cases:
             m, n, k = 1 << c["logm"], 1 << c["logn"], 1 << c["logk"]
             net, tree = sweep.network(c["logm"], c["logn"], c["logk"])
+            t_plan = time.perf_counter()
             plan = qa.Plan.from_network(net, tree, dtype=qa.TNC_C128 if z else qa.TNC_C64, precision=prec)
+            plan_s += time.perf_counter() - t_plan
             self.plans.append((c, plan, m, n, k))
             maxa, maxb, maxc = max(maxa, m * k), max(maxb, n * k), max(maxc, m * n)
             maxws = max(maxws, plan.workspace_bytes)
+        # host planning (tnc_plan) for all cases, outside the timed region
+        self.plan_ms_host = round(1e3 * plan_s, 3)
         dev = "cuda"
         self.A = torch.empty(maxa, dtype=cdt, device=dev)
         self.B = torch.empty(maxb, dtype=cdt, device=dev)
@@ -335,6 +340,10 @@ class TreeWorkload:
             self.base_s += 1
             self.sliced = trees.choose_slices(net, tree, self.base_s)
             self.plan = qa.Plan.from_network(net, tree, sliced=self.sliced)
+        # host planning (tnc_plan) of the timed plan, outside the timed region
+        t_plan = time.perf_counter()
+        qa.Plan.from_network(net, tree, sliced=self.sliced)
+        self.plan_ms_host = round(1e3 * (time.perf_counter() - t_plan), 3)
         st = self.plan.stats()
         if self.base_s:
             # algorithmic flops: the unsliced tree's; the sliced run does R_s times that
@@ -855,6 +864,7 @@ def main():
             **({"pct_fp64_mfma_peak": round(100.0 * value / PEAK_FP64_MFMA, 2)} if z else
                {"pct_fp32_mfma_peak": round(100.0 * value / PEAK_FP32_MFMA, 2)}),
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
+            "plan_ms_host": getattr(wl, "plan_ms_host", None),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
             **({"ablation": ablation} if ablation is not None else {}),
             **({"slicing": slicing} if slicing is not None else {}),
