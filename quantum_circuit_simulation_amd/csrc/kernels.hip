@@ -1399,10 +1399,10 @@ __global__ __launch_bounds__(NT, NT / 128) void k_cgemm_tile(StepArgs a, int64_t
 // of a small step sit in L2), one stage ahead, into the (re, im) MFMA scheme
 // of k_cgemm; the NW partial blocks are summed through LDS and wave 0
 // stores the block (16-byte row pairs when C's innermost run is an even
-// unit-stride column run).
+// unit-stride column run).  Skinny-class steps with fewer than 4096 rows and
+// the same bounds run here too.
 constexpr int64_t kSmallGemmRS = int64_t(1) << 19;
 constexpr int64_t kSmallGemmK = 512;
-
 constexpr int kSmallGemmWaves = 4;
 
 template <bool PAIR, int NW>
