@@ -79,6 +79,8 @@ CASES = [
     ([2] * 5, [2] * 5, [3, 2, 2], False, True),          # 32 x 32 x 12, re-laid lhs
     ([2] * 5, [2] * 6, [2] * 9, False, False),           # 32 x 64 x 512: K at its bound
     ([2] * 4 + [3], [2] * 6, [2] * 8, True, False),      # 48 x 64 x 256
+    ([2] * 6, [2] * 7, [], False, False),                # 64 x 128 x 1: outer product
+    ([3] * 4, [2] * 5 + [3], [3], True, False),          # 81 x 96 x 3, interleaved, K odd
 ]
 
 
@@ -107,6 +109,7 @@ SKINNY_CASES = [
     ([2] * 9, [2] * 4, [2] * 6, False),     # 512 x 16 x 64
     ([3] * 5, [5], [2, 2, 2, 5], True),     # 243 x 5 x 40, ragged
     ([2] * 10, [2], [3, 3, 3], False),      # 1024 x 2 x 27: K odd
+    ([2, 2, 2, 5, 5, 5], [], [3, 2, 2], False),  # 1000 x 1 x 12: matrix-vector
 ]
 
 
