@@ -56,7 +56,9 @@ __device__ __forceinline__ T czero() {
 }
 
 // Offset in C (entries) of index `idx` along one side, runs outermost first.
-// Indices below 2^32 (every run size then fits too) take 32-bit division.
+// Indices below 2^32 (every run size then fits too) take 32-bit division, or
+// a shift and a mask for a run size that is a power of two (every run of a
+// network whose modes have extent 2).
 __device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int n) {
   int64_t off = 0;
   if (idx < (int64_t(1) << 32)) {
@@ -69,8 +71,15 @@ __device__ __forceinline__ int64_t run_offset(int64_t idx, const RunDev *r, int 
         break;
       }
       const uint32_t s32 = (uint32_t)sz;
-      const uint32_t nx = i / s32;
-      off += (int64_t)(i - nx * s32) * r[q].stride;
+      uint32_t nx, rem;
+      if ((s32 & (s32 - 1u)) == 0u) {
+        nx = i >> (__ffs(s32) - 1);
+        rem = i & (s32 - 1u);
+      } else {
+        nx = i / s32;
+        rem = i - nx * s32;
+      }
+      off += (int64_t)rem * r[q].stride;
       i = nx;
     }
     return off;
