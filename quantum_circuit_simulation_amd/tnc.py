@@ -210,8 +210,9 @@ class Plan:
         h = ctypes.c_void_p()
         _check(lib.tnc_plan(ctypes.byref(net), ctypes.byref(tree), ctypes.byref(opts), ctypes.byref(h)), "tnc_plan")
         self._h = h
-        self.out_shape = tuple(int(extents[x]) for x in out_modes)
-        self.leaf_shapes = [tuple(int(extents[x]) for x in l) for l in leaves]
+        ext_list = [int(e) for e in extents]
+        self.out_shape = tuple(ext_list[int(x)] for x in out_modes)
+        self.leaf_shapes = [tuple(ext_list[int(x)] for x in l) for l in leaves]
 
     @classmethod
     def from_network(cls, net, tree, **kw) -> "Plan":
