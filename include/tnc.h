@@ -197,7 +197,9 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  * few MB, freed by tnc_plan_destroy) which a kernel then reads on every call;
  * a call captured into a graph before that copy exists records an ordinary
  * host-to-device copy of the descriptors instead.  The caller keeps the plan,
- * leaves, out and workspace alive until the stream has finished.  One plan may run concurrently on different
+ * leaves, out and workspace alive until the stream has finished; a HIP graph
+ * that captured a call reads the plan's host descriptors on every replay, so
+ * the plan must also outlive every such graph.  One plan may run concurrently on different
  * streams given distinct workspaces and outputs.  A sliced plan loops over all
  * slices and leaves their sum in `out`.
  * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP (pinned allocation or launch

@@ -366,19 +366,25 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   p->gemm_b.assign(S, {});
   const bool naive = o.order == TNC_ORDER_NAIVE;
   if (!naive) {
-    // Reverse pass (page section 1.4): the root takes the output order; each
-    // operand keeps its product's order restricted to its own modes and gets
-    // the reduced modes (ascending label) appended.
-    p->order[T - 1] = p->out_modes;
-    for (int32_t s = S - 1; s >= 0; --s) {
-      const auto &c_order = p->order[L + s];
-      for (int32_t operand : {p->lhs[s], p->rhs[s]}) {
-        std::vector<int32_t> o2;
-        for (int32_t x : c_order)
-          if (std::binary_search(sets[operand].begin(), sets[operand].end(), x)) o2.push_back(x);
-        o2.insert(o2.end(), K[s].begin(), K[s].end());
-        p->order[operand] = std::move(o2);
-      }
+    // Lifetime ordering (page section 1.4): a mode that stays alive longer
+    // sits further left.  Each mode gets a rank: open modes outlive every
+    // step and rank by their place in the output order; a closed mode ranks
+    // by the step that reduces it, later steps first, and modes reduced by
+    // the same step by ascending label, so that both operands of that step
+    // carry the reduced modes innermost in one common order.  Every tensor
+    // lists its modes by ascending rank, which puts each operand in the form
+    // [modes it hands on to its product, in the product's order | reduced
+    // modes]: the GEMM layout the page's reverse pass over the tree builds.
+    std::vector<int64_t> rank_of(p->num_modes, 0);
+    const int64_t nout = (int64_t)p->out_modes.size();
+    for (int64_t i = 0; i < nout; ++i) rank_of[p->out_modes[i]] = i;
+    for (int32_t s = 0; s < S; ++s)
+      for (size_t q = 0; q < K[s].size(); ++q)  // K[s] is ascending
+        rank_of[K[s][q]] = nout + (int64_t)(S - 1 - s) * (p->num_modes + 1) + (int64_t)q;
+    for (int32_t t = 0; t < T; ++t) {
+      std::vector<int32_t> o2 = sets[t];
+      std::sort(o2.begin(), o2.end(), [&](int32_t a, int32_t b) { return rank_of[a] < rank_of[b]; });
+      p->order[t] = std::move(o2);
     }
     for (int32_t s = 0; s < S; ++s) {
       p->gemm_a[s] = p->order[p->lhs[s]];

@@ -283,18 +283,41 @@ class Plan:
         _check(self._lib.tnc_execute(self._h, arr, ctypes.c_void_p(int(out_ptr)), ctypes.c_void_p(int(ws_ptr)),
                                      ctypes.c_uint64(int(ws_bytes)), ctypes.c_void_p(int(stream))), "tnc_execute")
 
+    def check_buffers(self, leaves, out, workspace):
+        """Raise ValueError unless every buffer has the plan's entry count,
+        dtype and layout and all of them sit on one GPU.  The C ABI receives
+        bare pointers, so a short buffer would otherwise be read or written
+        past its end by the kernels."""
+        import torch
+        if len(leaves) != self.num_leaves:
+            raise ValueError(f"wrong number of leaves: {len(leaves)} given, plan has {self.num_leaves}")
+        want = torch.complex128 if self.dtype == TNC_C128 else torch.complex64
+        for i, (t, shape) in enumerate(zip(leaves, self.leaf_shapes)):
+            need = int(np.prod(shape, dtype=np.int64))
+            if t.numel() != need:
+                raise ValueError(f"leaf {i} holds {t.numel()} entries, its modes need {need}")
+        need = int(np.prod(self.out_shape, dtype=np.int64))
+        if out.numel() != need:
+            raise ValueError(f"out holds {out.numel()} entries, the output modes need {need}")
+        if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                             f"the plan needs {self.workspace_bytes}")
+        for t in list(leaves) + [out]:
+            if t.dtype != want or not t.is_contiguous():
+                raise ValueError(f"leaves and out must be contiguous {want} tensors")
+        devices = {t.device for t in list(leaves) + [out, workspace]}
+        if len(devices) != 1 or next(iter(devices)).type != "cuda":
+            raise ValueError(f"leaves, out and workspace must all be on one GPU (got {sorted(map(str, devices))})")
+
     def execute(self, leaves, out, workspace, stream=None):
         """leaves: torch complex64 tensors on the GPU (declared layouts), out:
         complex64 tensor of the output size, workspace: uint8 tensor of at
         least ``workspace_bytes``.  Enqueued on ``stream`` (default: torch's
-        current stream); returns without synchronising."""
+        current stream); returns without synchronising.  A HIP graph that
+        captured this call reads the plan's descriptors on every replay, so
+        keep this Plan alive as long as any such graph."""
         import torch
-        if len(leaves) != self.num_leaves:
-            raise ValueError("wrong number of leaves")
-        want = torch.complex128 if self.dtype == TNC_C128 else torch.complex64
-        for t in list(leaves) + [out]:
-            if t.dtype != want or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"leaves and out must be contiguous {want} GPU tensors")
+        self.check_buffers(leaves, out, workspace)
         if stream is None:
             stream = torch.cuda.current_stream()
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

@@ -248,3 +248,50 @@ def test_options_and_errors():
             plan.distribute(**bad)
     steps, total = plan.distribute(num_gpus=1)
     assert all(s["tag_name"] == "replicated" for s in steps)
+
+
+def _comm_model(P):
+    """One tensor T laid out [a(4), b(4), c(8), d(2)] (complex64, 2048 bytes):
+    the root of a two-leaf network whose output order is that layout (a
+    closed extent-1 mode joins the leaves).  B_net = 1e9 B/s, lambda = 1 us."""
+    ext = [4, 4, 8, 2, 1]
+    net_leaves = [[0, 1, 2, 3, 4], [4]]
+    return OD.model(ext, net_leaves, [0, 1, 2, 3], [0], [1], eb=8, P=P, threshold=1, B_net=1e9, lam=1e-6)
+
+
+def test_comm_time_hand_worked_cases():
+    """t_comm = V / B_net + lambda * n_blk (section 1.6, in words), worked out
+    by hand for one tensor; T is id 2 in the model.
+
+    P = 4, re-split from [a] onto [c]: each GPU holds 2048 / 4 = 512 bytes
+    laid out [b, c, d]; it keeps one of P pieces of 2048 / 16 = 128 bytes and
+    sends the other three: V = 384.  Contiguous runs end where the new cut
+    (c) falls: the bytes right of c are d's 2 entries = 16 bytes, so
+    n_blk = 384 / 16 = 24.
+    P = 4, all-gather of T split on [a]: V = 3 * 512 = 1536 in blocks of
+    the 512 bytes right of a (b c d = 64 entries): n_blk = 3.  Split on [c]:
+    blocks of 16 bytes (d), n_blk = 96.
+    P = 4, all-reduce: V = 2 (P - 1) |T| / P = 3072 bytes in 2 (P - 1) = 6
+    messages.
+    P = 2, re-split [a] -> [d]: pieces of 2048 / 4 = 512 bytes, V = 512 in
+    blocks of 8 bytes (nothing right of d): n_blk = 64; [a] -> [b]: blocks
+    of 128 bytes (c d = 16 entries): n_blk = 4.  All-gather on [a]: V = 1024
+    in blocks of 512: n_blk = 2.  All-reduce: V = 2048 in 2 messages."""
+    a, b, c, d = 0, 1, 2, 3
+    m4 = _comm_model(4)
+    assert m4.size[2] == 2048 and m4.order[2] == [a, b, c, d]
+    cases = [
+        (m4.resplit_time(2, [a], [c]), 384e-9 + 24e-6),
+        (m4.allgather_time(2, [a]), 1536e-9 + 3e-6),
+        (m4.allgather_time(2, [c]), 1536e-9 + 96e-6),
+        (m4.allreduce_time(2), 3072e-9 + 6e-6),
+    ]
+    m2 = _comm_model(2)
+    cases += [
+        (m2.resplit_time(2, [a], [d]), 512e-9 + 64e-6),
+        (m2.resplit_time(2, [a], [b]), 512e-9 + 4e-6),
+        (m2.allgather_time(2, [a]), 1024e-9 + 2e-6),
+        (m2.allreduce_time(2), 2048e-9 + 2e-6),
+    ]
+    for i, (got, want) in enumerate(cases):
+        assert math.isclose(got, want, rel_tol=1e-12), (i, got, want)

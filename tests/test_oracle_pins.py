@@ -299,3 +299,55 @@ def test_complex128_leaves_are_read_at_full_precision():
     single = oracle.contract(net.extents, net.leaves, net.out_modes, [d.astype(np.complex64) for d in data],
                              tree.lhs, tree.rhs)
     assert np.max(np.abs(single - ref)) > 1e-9 * np.max(np.abs(ref))
+
+
+def _cn(rng, shape):
+    return ((rng.standard_normal(shape) + 1j * rng.standard_normal(shape)) / np.sqrt(2)).astype(np.complex64)
+
+
+@pytest.mark.parametrize("ni,nj,k", [(5, 7, 3), (9, 4, 1), (3, 3, 27), (6, 11, 40), (1, 13, 2)])
+def test_pair_block_is_a_times_b_transposed(ni, nj, k):
+    """oracle.pair_block(a, b) = a @ b^T over K (no conjugate), against numpy's
+    own complex128 matrix product on non-square blocks (so a transposed
+    index into b, or a swapped i / j, reads the wrong entries)."""
+    rng = np.random.default_rng(ni * 1000 + nj * 10 + k)
+    a, b = _cn(rng, (ni, k)), _cn(rng, (nj, k))
+    got = oracle.pair_block(a, b)
+    ref = a.astype(np.complex128) @ b.astype(np.complex128).T
+    assert got.shape == (ni, nj)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_pair_block_closed_forms():
+    """Identity rows of B give A back exactly; all-ones operands give k."""
+    rng = np.random.default_rng(3)
+    a = _cn(rng, (6, 9))
+    eye = np.eye(9, dtype=np.complex64)
+    assert np.array_equal(oracle.pair_block(a, eye), a.astype(np.complex128))
+    ones_a = np.ones((4, 37), np.complex64)
+    ones_b = np.ones((5, 37), np.complex64)
+    assert np.array_equal(oracle.pair_block(ones_a, ones_b), np.full((4, 5), 37.0 + 0j))
+    # (i * 1) * (i * 1) = -1 per term: the sign of the imaginary product
+    ij = np.full((2, 5), 1j, np.complex64)
+    assert np.array_equal(oracle.pair_block(ij, ij), np.full((2, 2), -5.0 + 0j))
+
+
+def test_pair_block_matches_the_contractor_on_gathered_rows():
+    """A pairwise network with extent-3 and extent-5 modes, contracted whole by
+    the oracle contractor (pinned above against einsum and brute force); the
+    block of randomly gathered rows of A and of B must equal the same block
+    of the full product."""
+    rng = np.random.default_rng(41)
+    # modes: m0 (3), m1 (2) | n0 (5) | k0 (3), k1 (2)
+    ext = [3, 2, 5, 3, 2]
+    A_modes, B_modes, out = [0, 1, 3, 4], [2, 3, 4], [0, 1, 2]
+    A, B = _cn(rng, (3, 2, 3, 2)), _cn(rng, (5, 3, 2))
+    full = oracle.contract(ext, [A_modes, B_modes], out, [A, B], [0], [1]).reshape(6, 5)
+    rows = rng.permutation(6)[:4]
+    cols = rng.permutation(5)[:3]
+    got = oracle.pair_block(A.reshape(6, 6)[rows], B.reshape(5, 6)[cols])
+    assert np.max(np.abs(got - full[np.ix_(rows, cols)])) <= 1e-12 * np.max(np.abs(full))
+    # K = {} (outer product): a column of A times a row of B
+    a1, b1 = _cn(rng, (7, 1)), _cn(rng, (4, 1))
+    outer = oracle.contract([7, 4], [[0], [1]], [0, 1], [a1.reshape(7), b1.reshape(4)], [0], [1])
+    assert np.max(np.abs(oracle.pair_block(a1, b1) - outer)) <= 1e-14

@@ -174,3 +174,31 @@ def test_precision_option_is_validated_and_leaves_the_plan_unchanged():
         assert split.tensor_offset(t) == exact.tensor_offset(t)
     for s in range(len(tree.lhs)):
         assert split.node(s) == exact.node(s)
+
+
+def test_execute_rejects_wrongly_sized_or_placed_buffers_before_any_launch():
+    """The C ABI takes bare pointers, so the binding checks every buffer's
+    entry count against the plan's leaf and output shapes (and that all of
+    them share one GPU) before it calls tnc_execute.  On the CPU every call
+    below must stop at that check."""
+    import torch
+    net = circuits.brickwork(6, 4, 3).to_network(open_qubits=[0, 1])
+    tree = trees.greedy_tree(net)
+    plan = qa.Plan.from_network(net, tree)
+    good = [torch.from_numpy(d.copy()) for d in net.data]
+    out = torch.empty(4, dtype=torch.complex64)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8)
+    short = list(good)
+    short[3] = good[3][:-1].clone()
+    with pytest.raises(ValueError, match="leaf 3 holds"):
+        plan.execute(short, out, ws)
+    with pytest.raises(ValueError, match="out holds"):
+        plan.execute(good, torch.empty(3, dtype=torch.complex64), ws)
+    with pytest.raises(ValueError, match="workspace holds"):
+        plan.execute(good, out, torch.empty(max(0, plan.workspace_bytes - 1), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="wrong number of leaves"):
+        plan.execute(good[:-1], out, ws)
+    with pytest.raises(ValueError, match="complex64"):
+        plan.execute([g.to(torch.complex128) for g in good], out, ws)
+    with pytest.raises(ValueError, match="one GPU"):
+        plan.execute(good, out, ws)
