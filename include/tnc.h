@@ -209,6 +209,28 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
                        uint64_t workspace_bytes, void *stream);
 
 /*
+ * Run the plan without allocating anything: for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as tnc_execute, except that the
+ * workspace is a static array inside the library, one copy per GPU of
+ * TNC_NOALLOC_MAX_WORKSPACE_BYTES bytes, held from the library's load until
+ * the process ends.  The call makes no hipMalloc, hipFree, hipHostMalloc or
+ * other allocation: if the plan already has its pinned descriptor copy (from
+ * an earlier tnc_execute) a kernel reads it, otherwise the descriptors are
+ * uploaded by a host-to-device copy from the plan's own host memory.  The
+ * first call on a device looks up that device's copy of the array (with the
+ * device current).  Nothing in the workspace needs to start at zero: every
+ * region a call reads was written earlier in the same call.  All calls on
+ * one GPU share its array, so two calls whose work overlaps in time on the
+ * same GPU (other streams, other threads) race and corrupt each other's
+ * results; serialise them.
+ * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL (the plan's workspace exceeds
+ * TNC_NOALLOC_MAX_WORKSPACE_BYTES; checked before any HIP call), HIP.
+ */
+#define TNC_NOALLOC_MAX_WORKSPACE_BYTES (UINT64_C(64) << 20)
+tnc_status tnc_execute_noalloc(tnc_plan_t plan, const void *const *leaves, void *out, void *stream);
+
+/*
  * Distribution schedule over P GPUs (host only; launches nothing).
  *
  * "Parallelizing Large-Scale Tensor Network Contraction on Multiple GPUs",

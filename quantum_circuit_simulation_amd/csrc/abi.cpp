@@ -161,10 +161,16 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
   return TNC_OK;
 }
 
-tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
-                       uint64_t workspace_bytes, void *stream_ptr) {
-  g_last_error.clear();
-  if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Runs `plan` with its workspace at `workspace`.  may_pin: the first call on
+// the plan outside stream capture may allocate the pinned descriptor copy;
+// without it, a plan that has no pinned copy yet uploads its descriptors
+// with a host-to-device copy from the plan's own host memory.
+tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                    uint64_t workspace_bytes, void *stream_ptr, bool may_pin) {
   const tnc::PlanImpl &p = plan->impl;
   // an error left behind by an earlier, unrelated HIP call is not ours
   (void)hipGetLastError();
@@ -185,7 +191,7 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
   const void *pinned = nullptr;
   {
     std::lock_guard<std::mutex> lock(plan->pin_mu);
-    if (!plan->blob_pinned) {
+    if (!plan->blob_pinned && may_pin) {
       hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
       if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
         (void)hipGetLastError();
@@ -307,6 +313,71 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
     }
   }
   return TNC_OK;
+}
+
+// Static workspace of tnc_execute_noalloc: one copy per GPU, held from the
+// library's load until the process ends.  Host code never passes `scratch`
+// itself to a kernel or a copy (on the host the name is only a stand-in);
+// it uses the device address that hipGetSymbolAddress returns per device.
+constexpr uint64_t kScratchBytes = TNC_NOALLOC_MAX_WORKSPACE_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current).
+tnc_status scratch_for_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    g_last_error = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return TNC_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    g_last_error = "device index beyond the static scratch table";
+    return TNC_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a) {
+      (void)hipGetLastError();
+      g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return TNC_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TNC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                       uint64_t workspace_bytes, void *stream_ptr) {
+  g_last_error.clear();
+  if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
+  return run_plan(plan, leaves, out, workspace, workspace_bytes, stream_ptr, true);
+}
+
+tnc_status tnc_execute_noalloc(tnc_plan_t plan, const void *const *leaves, void *out, void *stream_ptr) {
+  g_last_error.clear();
+  if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
+  if (plan->impl.stats.workspace_bytes > kScratchBytes) {
+    g_last_error = "plan needs " + std::to_string(plan->impl.stats.workspace_bytes) +
+                   " bytes of workspace; the static scratch holds " + std::to_string(kScratchBytes);
+    return TNC_ERR_WORKSPACE_TOO_SMALL;
+  }
+  void *ws = nullptr;
+  tnc_status st = scratch_for_current_device(&ws);
+  if (st != TNC_OK) return st;
+  return run_plan(plan, leaves, out, ws, kScratchBytes, stream_ptr, false);
 }
 
 tnc_status tnc_dist_options_default(tnc_dist_options *o, tnc_dtype dtype) {

@@ -106,7 +106,8 @@ DIST_TAGS = ["replicated", "activate", "keep", "redistribute", "gather"]
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
            "tnc_execute", "tnc_status_string", "tnc_last_error", "tnc_dist_options_default",
-           "tnc_plan_distribute"]
+           "tnc_plan_distribute", "tnc_execute_noalloc"]
+NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # TNC_NOALLOC_MAX_WORKSPACE_BYTES
 
 _lib = None
 
@@ -144,6 +145,8 @@ def load_library(path: str = LIB_PATH):
     lib.tnc_execute.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_uint64, ctypes.c_void_p]
     lib.tnc_execute.restype = ctypes.c_int
+    lib.tnc_execute_noalloc.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p]
+    lib.tnc_execute_noalloc.restype = ctypes.c_int
     lib.tnc_status_string.argtypes = [ctypes.c_int]
     lib.tnc_status_string.restype = ctypes.c_char_p
     lib.tnc_last_error.argtypes = []
@@ -299,15 +302,32 @@ class Plan:
         need = int(np.prod(self.out_shape, dtype=np.int64))
         if out.numel() != need:
             raise ValueError(f"out holds {out.numel()} entries, the output modes need {need}")
-        if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+        if workspace is not None and workspace.numel() * workspace.element_size() < self.workspace_bytes:
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                              f"the plan needs {self.workspace_bytes}")
         for t in list(leaves) + [out]:
             if t.dtype != want or not t.is_contiguous():
                 raise ValueError(f"leaves and out must be contiguous {want} tensors")
-        devices = {t.device for t in list(leaves) + [out, workspace]}
+        devices = {t.device for t in list(leaves) + [out] + ([workspace] if workspace is not None else [])}
         if len(devices) != 1 or next(iter(devices)).type != "cuda":
             raise ValueError(f"leaves, out and workspace must all be on one GPU (got {sorted(map(str, devices))})")
+
+    def execute_noalloc_ptrs(self, leaf_ptrs: Sequence[int], out_ptr: int, stream: int = 0):
+        """tnc_execute_noalloc: the library's static per-GPU workspace."""
+        arr = (ctypes.c_void_p * max(1, len(leaf_ptrs)))(*[int(p) for p in leaf_ptrs])
+        _check(self._lib.tnc_execute_noalloc(self._h, arr, ctypes.c_void_p(int(out_ptr)),
+                                             ctypes.c_void_p(int(stream))), "tnc_execute_noalloc")
+
+    def execute_noalloc(self, leaves, out, stream=None):
+        """Like ``execute`` but with the library's static per-GPU workspace
+        (at most ``NOALLOC_MAX_WORKSPACE_BYTES``); calls that overlap in time
+        on one GPU share it and race."""
+        import torch
+        self.check_buffers(leaves, out, None)
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        self.execute_noalloc_ptrs([t.data_ptr() for t in leaves], out.data_ptr(), s)
 
     def execute(self, leaves, out, workspace, stream=None):
         """leaves: torch complex64 tensors on the GPU (declared layouts), out:

@@ -202,3 +202,21 @@ def test_execute_rejects_wrongly_sized_or_placed_buffers_before_any_launch():
         plan.execute([g.to(torch.complex128) for g in good], out, ws)
     with pytest.raises(ValueError, match="one GPU"):
         plan.execute(good, out, ws)
+
+
+def test_noalloc_rejects_a_plan_beyond_the_static_workspace_before_any_hip_call():
+    """tnc_execute_noalloc checks the plan's workspace against the static
+    array's size first, so on a machine without a GPU it still returns
+    WORKSPACE_TOO_SMALL (the pointers are never touched)."""
+    from workloads.network import Network, Tree
+    # A[M, k] B[N, k] -> C[M, N] (2^24 entries, 128 MiB in the arena), then C D[N] -> out[M]
+    M, N, k = list(range(12)), list(range(12, 24)), [24]
+    net = Network(np.full(25, 2, dtype=np.int64), [M + k, N + k, N], M, None)
+    plan = qa.Plan.from_network(net, Tree([0, 3], [1, 2]))
+    assert plan.workspace_bytes > tnc.NOALLOC_MAX_WORKSPACE_BYTES
+    with pytest.raises(tnc.TncError) as e:
+        plan.execute_noalloc_ptrs([1, 2, 3], 4)
+    assert e.value.name == "TNC_ERR_WORKSPACE_TOO_SMALL"
+    header = open(os.path.join(ROOT, "include", "tnc.h")).read()
+    m = re.search(r"#define TNC_NOALLOC_MAX_WORKSPACE_BYTES \(UINT64_C\((\d+)\) << (\d+)\)", header)
+    assert m and int(m.group(1)) << int(m.group(2)) == tnc.NOALLOC_MAX_WORKSPACE_BYTES
