@@ -300,20 +300,15 @@ class TreeWorkload:
             self.config = {"workload": "brickwork-12q-d8-amplitude", "seed": 101, "tree": "greedy"}
         elif which == "grid":
             net = circuits.grid_fsim(6, 6, 14, 505).to_network()
-            tree = trees.search_tree(net, trials=200, seed=1)
+            tree, stored_sliced, _ = trees.stored_tree("grid_6x6_d14", net)
             self.config = {"workload": "grid-6x6-d14-amplitude", "seed": 505,
-                           "tree": "best of 200 seeded randomized-greedy trees (seed 1)",
-                           "note": "largest fSim grid instance whose in-house tree fits one GPU unsliced; "
-                                   "7x8 depth 16 reaches width 2^59 with this search"}
+                           "tree": "stored search result (workloads/data/grid_6x6_d14.json)"}
         elif which == "grid7x8":
             net = circuits.grid_fsim(7, 8, 11, 505).to_network()
-            log("building the 7x8 tree: best of 200 recursive-bisection trees ...")
-            tree = trees.partition_search(net, trials=200, seed=1)
+            tree, stored_sliced, _ = trees.stored_tree("grid_7x8_d11", net)
             self.config = {"workload": "grid-7x8-d11-amplitude", "seed": 505,
-                           "tree": "best of 200 seeded recursive-bisection trees (seed 1)",
-                           "note": "the 56-qubit grid of the slicing comparison at the depth whose in-house tree "
-                                   "fits one GPU (width 2^32; the randomized greedy reaches 2^34 with 5x the "
-                                   "flops); runs at the smallest slicing whose workspace fits"}
+                           "tree": "stored search result (workloads/data/grid_7x8_d11.json); runs at the "
+                                   "smallest slicing whose workspace fits"}
         elif which == "hexagonal":
             from workloads import hexagonal
             net = hexagonal.honeycomb(16, 16, 8, 606)
@@ -332,10 +327,13 @@ class TreeWorkload:
             raise ValueError(which)
         self.name = self.config["workload"]
         self.net, self.tree = net, tree
-        # the smallest slicing (greedy slice modes) whose workspace fits in HBM
+        # the stored slicing of a searched tree, else the smallest slicing
+        # (greedy slice modes) whose workspace fits in HBM
         free, _ = torch.cuda.mem_get_info()
         self.base_s, self.sliced = 0, []
-        self.plan = qa.Plan.from_network(net, tree)
+        if which in ("grid", "grid7x8") and stored_sliced:
+            self.base_s, self.sliced = len(stored_sliced), list(stored_sliced)
+        self.plan = qa.Plan.from_network(net, tree, sliced=self.sliced)
         while self.plan.workspace_bytes > free - (8 << 30) and self.base_s < 8:
             self.base_s += 1
             self.sliced = trees.choose_slices(net, tree, self.base_s)
@@ -570,6 +568,12 @@ class TreeWorkload:
         log(f"monomial check: |amp| = {abs(got):.7f}, relative error {err:.2e}")
         return {"expected": [amp.real, amp.imag], "got": [got.real, got.imag], "rel_err": err, "pass": err <= 1e-4}
 
+    def tree_roofline(self, ms_per_step):
+        ops = self.plan.execute_timed(self.leaves, self.out, self.ws)
+        line, roof_ms, kernels = tree_kernel_roofline(self.plan, ops, runs=self.plan.stats()["num_slices"])
+        return line, {"sum_t_roof_ms": round(roof_ms, 3), "frac": round(roof_ms / ms_per_step, 4),
+                      "kernels": kernels}
+
     def kernel_of(self, idx):
         return "whole tree"
 
@@ -612,6 +616,206 @@ class TreeWorkload:
             ni = min(64, ni * 2)
         return {"value": 8.0 * done * k / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                 "sample": f"{done} exact complex128 entries of the tree's largest step (k = {k}) in {el:.1f} s"}
+
+
+def step_roofline_ms(m, n, k, eb=8):
+    """Roofline time of one pairwise step (page section 1.6 words for t_gemm):
+    max(algorithmic bytes / HBM peak, 8 m n k / FP32 matrix peak), in ms."""
+    return 1e3 * max(eb * (m * k + n * k + m * n) / (PEAK_HBM * 1e9), 8.0 * m * n * k / (PEAK_FP32_MFMA * 1e12))
+
+
+def tree_kernel_roofline(plan, ops, runs=1):
+    """Per-kernel totals of one timed run (tnc_execute_timed records, whose
+    times sum over `runs` slices): algorithmic flops and bytes of the GEMM
+    and skinny launches, grouped by the kernel each launch used; the
+    dominant kernel (most time) with its achieved rate against its own
+    bound, and the tree's sum of per-step roofline times."""
+    per = {}
+    roof_ms = 0.0
+    for o in ops:
+        if o["kind"] in ("gemm", "skinny"):
+            nd = plan.node(o["step"])
+            m, n, k = nd["m"], nd["n"], nd["k"]
+            f, b = 8.0 * m * n * k * o["launches"], 8.0 * (m * k + n * k + m * n) * o["launches"]
+        else:
+            f = b = 0.0
+        acc = per.setdefault(o["kernel"], {"ms": 0.0, "flop": 0.0, "bytes": 0.0, "launches": 0})
+        acc["ms"] += o["ms"]
+        acc["flop"] += f
+        acc["bytes"] += b
+        acc["launches"] += o["launches"]
+    for s in range(plan.num_steps):
+        nd = plan.node(s)
+        roof_ms += step_roofline_ms(nd["m"], nd["n"], nd["k"]) * runs
+    name, d = max(per.items(), key=lambda kv: kv[1]["ms"])
+    mfma = d["bytes"] == 0 or d["flop"] / d["bytes"] > (PEAK_FP32_MFMA * 1e12) / (PEAK_HBM * 1e9)
+    sec = d["ms"] / 1e3
+    if mfma:
+        ach = d["flop"] / sec / 1e12 if sec > 0 else 0.0
+        line = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP32_MFMA, 4)}
+    else:
+        ach = d["bytes"] / sec / 1e9 if sec > 0 else 0.0
+        line = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM, 4)}
+    line.update({"kernel": name, "launches": d["launches"], "avg_launch_ms": round(d["ms"] / max(1, d["launches"]), 4),
+                 "kernel_share_of_time": round(d["ms"] / sum(v["ms"] for v in per.values()), 4)})
+    kernels = {k: {"ms": round(v["ms"], 3), "launches": v["launches"],
+                   **({"tflops": round(v["flop"] / (v["ms"] / 1e3) / 1e12, 2),
+                       "GBps": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)} if v["flop"] and v["ms"] > 0 else {})}
+               for k, v in sorted(per.items(), key=lambda kv: -kv[1]["ms"])}
+    return line, roof_ms, kernels
+
+
+class SlicedGridWorkload:
+    """The 56-qubit 7x8 grid circuit at depth 16 (fSim couplers, seed 505),
+    single amplitude <0...0|U|0...0>, along the stored searched tree and its
+    sliced modes (``workloads/data/grid_7x8_d16.json``).  Its unsliced
+    intermediates do not fit one GPU, so the run is sliced; one timed step
+    runs a fixed range of complete slices (each the whole sliced tree), and
+    the time to the full result is projected from them (marked as such)."""
+
+    def __init__(self, timed_slices=2):
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import circuits, trees
+        self.net = circuits.grid_fsim(7, 8, 16, 505).to_network()
+        self.tree, self.sliced, rec = trees.stored_tree("grid_7x8_d16", self.net)
+        self.timed_slices = timed_slices
+        t_plan = time.perf_counter()
+        self.plan = qa.Plan.from_network(self.net, self.tree, sliced=self.sliced, slice_range=(0, timed_slices))
+        self.plan_ms_host = round(1e3 * (time.perf_counter() - t_plan), 3)
+        st = self.plan.stats()
+        self.num_slices = st["num_slices"]
+        self.flops_slice = st["flops"]
+        self.flops_unsliced = float(rec["flop_unsliced"])
+        # algorithmic flops of one step: the unsliced tree's share of the slices run
+        self.flops = self.flops_unsliced * timed_slices / self.num_slices
+        self.name = "grid-7x8-d16-amplitude"
+        self.config = {"workload": self.name, "seed": 505, "qubits": 56, "depth": 16,
+                       "tree": "stored search result (workloads/data/grid_7x8_d16.json: recursive multilevel "
+                               "bisection, subtree reconfiguration, slicing; seed 1)",
+                       "sliced_modes": len(self.sliced), "slices": self.num_slices,
+                       "slices_per_step": timed_slices, "max_intermediate_sliced": st["max_intermediate"],
+                       "workspace_bytes": st["workspace_bytes"], "flop_per_slice": self.flops_slice,
+                       "flop_unsliced_F1": self.flops_unsliced, "flop_sliced_Fs": self.flops_slice * self.num_slices,
+                       "R_s": self.flops_slice * self.num_slices / self.flops_unsliced,
+                       "flop_per_step": self.flops, "steps_in_tree": st["num_steps"],
+                       "launch_groups": st["num_groups"]}
+        self.leaves = [torch.from_numpy(d).to("cuda") for d in self.net.data]
+        self.out = torch.empty(1, dtype=torch.complex64, device="cuda")
+        self.ws = qa.alloc_workspace(self.plan)
+
+    def step(self, events=None):
+        if events is not None:
+            events[0][0].record()
+        self.plan.execute(self.leaves, self.out, self.ws)
+        if events is not None:
+            events[0][1].record()
+
+    def finish(self, ms_per_step):
+        """Projection of the whole amplitude from the timed slices."""
+        per_slice_s = ms_per_step / 1e3 / self.timed_slices
+        self.config.update({"ms_per_slice": round(1e3 * per_slice_s, 3),
+                            "time_to_result_s": round(per_slice_s * self.num_slices, 1),
+                            "time_to_result_is_projection": True,
+                            "projection": f"{self.num_slices} slices x the measured time per slice"})
+
+    def tree_roofline(self, ms_per_step):
+        ops = self.plan.execute_timed(self.leaves, self.out, self.ws)
+        line, roof_ms, kernels = tree_kernel_roofline(self.plan, ops, runs=self.timed_slices)
+        return line, {"sum_t_roof_ms": round(roof_ms, 3), "frac": round(roof_ms / ms_per_step, 4),
+                      "kernels": kernels}
+
+    def check_monomial(self):
+        """The monomial-gate circuit of the same shape, same tree and slicing:
+        one basis-state path carries the whole amplitude e^(i alpha).  The
+        slice whose digits are that path's values of the sliced modes returns
+        it; two other slices return exactly zero."""
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from tests.brute import monomial_mode_values, track_basis_state
+        from workloads import circuits
+        c = circuits.grid_monomial(7, 8, 16, 505)
+        gates = [(a, b, u.astype(np.complex64).astype(np.complex128)) for a, b, u in c.gates]
+        bits, amp = track_basis_state(56, gates)
+        net = c.to_network(bits=bits)
+        vals, amp2 = monomial_mode_values(net, gates, 56)
+        assert abs(amp2 - amp) < 1e-12
+        s = len(self.sliced)
+        star = sum(vals[x] << (s - 1 - i) for i, x in enumerate(self.sliced))
+        leaves = [torch.from_numpy(d).to("cuda") for d in net.data]
+        res = {"slice_star": star, "expected": [amp.real, amp.imag]}
+        for tag, sigma in (("star", star), ("other1", star ^ 1), ("other2", star ^ (1 << (s - 1)))):
+            plan = qa.Plan.from_network(net, self.tree, sliced=self.sliced, slice_range=(sigma, sigma + 1))
+            plan.execute(leaves, self.out, self.ws)
+            torch.cuda.synchronize()
+            got = complex(self.out.cpu().numpy()[0])
+            res[tag] = [got.real, got.imag]
+            log(f"monomial check slice {sigma} ({tag}): {got:.7f}")
+        err = abs(complex(*res["star"]) - amp) / abs(amp)
+        res["rel_err"] = err
+        res["pass"] = bool(err <= 1e-4 and res["other1"] == [0.0, 0.0] and res["other2"] == [0.0, 0.0])
+        return res
+
+    def kernel_of(self, idx):
+        return "whole tree"
+
+    def launch_flops(self, idx):
+        return self.flops
+
+    def launch_bytes(self, idx):
+        return self.plan.stats()["bytes"] * self.timed_slices
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The oracle on a bounded sample of the same contraction: the stored
+        tree with its sliced modes and a few more modes fixed (each time the
+        mode held by the widest intermediates that carries the most
+        operations), until one sub-slice has at most 2^24-entry
+        intermediates and 2e11 flop; rate = its flops / its time."""
+        import oracle
+        from workloads import trees
+        fixed = list(self.sliced)
+        ext = [int(e) for e in self.net.extents]
+        sets = [0] * (len(self.net.leaves) + len(self.tree.lhs))
+        for i, l in enumerate(self.net.leaves):
+            for x in l:
+                sets[i] |= 1 << x
+        L = len(self.net.leaves)
+        for s, (a, b) in enumerate(zip(self.tree.lhs, self.tree.rhs)):
+            sets[L + s] = sets[a] ^ sets[b]
+        unions = [sets[a] | sets[b] for a, b in zip(self.tree.lhs, self.tree.rhs)]
+        while True:
+            mask = sum(1 << x for x in fixed)
+            w = max((t & ~mask).bit_count() for t in sets)
+            fl = sum(8.0 * 2.0 ** (u & ~mask).bit_count() for u in unions)
+            if w <= 24 and fl <= 2e11:
+                break
+            contrib = {}
+            for u in unions:
+                c = 2.0 ** (u & ~mask).bit_count()
+                v = u & ~mask
+                while v:
+                    x = (v & -v).bit_length() - 1
+                    contrib[x] = contrib.get(x, 0.0) + c
+                    v &= v - 1
+            widest = [t & ~mask for t in sets if (t & ~mask).bit_count() == w]
+            cand = set()
+            for t in widest:
+                v = t
+                while v:
+                    cand.add((v & -v).bit_length() - 1)
+                    v &= v - 1
+            x = max(cand, key=lambda y: (sum(1 for t in widest if t >> y & 1), contrib.get(y, 0.0), -y))
+            fixed.append(x)
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        oracle.contract_network(self.net, self.tree, fixed={x: 0 for x in fixed}, threads=threads)
+        el = time.perf_counter() - t0
+        return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"one sub-slice of the same tree ({len(fixed)} modes fixed: the {len(self.sliced)} "
+                          f"sliced modes and {len(fixed) - len(self.sliced)} more; width 2^{w}, {fl:.3g} flop "
+                          f"in {el:.1f} s)"}
 
 
 KERNEL_SRC = os.path.join(ROOT, "quantum_circuit_simulation_amd", "csrc", "kernels.hip")
@@ -701,7 +905,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal", "brickwork30sv", "grid7x8"])
+    ap.add_argument("--workload", default="sweep",
+                    choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal",
+                             "brickwork30sv", "grid7x8", "grid7x8d16"])
+    ap.add_argument("--timed-slices", type=int, default=2,
+                    help="grid7x8d16: complete slices run per timed step")
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
                                                  "e.g. 2,3,4")
     ap.add_argument("--precision", default="exact", choices=["exact", "bf16x3"],
@@ -753,6 +961,9 @@ def main():
     elif args.workload == "skinny":
         wl = SkinnyWorkload()
         nlaunch = len(wl.plans)
+    elif args.workload == "grid7x8d16":
+        wl = SlicedGridWorkload(args.timed_slices)
+        nlaunch = 1
     else:
         wl = TreeWorkload(args.workload)
         nlaunch = 1
@@ -800,12 +1011,20 @@ def main():
     dom = max(per.items(), key=lambda kv: kv[1][1])
     achieved = dom[1][0] / (dom[1][1] / 1e3) / 1e12
     traffic = measured_traffic(args.workload, dom[0])
-    hbm_tree = False
-    if isinstance(wl, TreeWorkload):
-        # a whole tree is HBM-bound when its bytes at 8 TB/s outweigh its flops at the matrix peak
-        st = wl.plan.stats()
-        hbm_tree = st["bytes"] / (PEAK_HBM * 1e9) > st["flops"] / (PEAK_FP32_MFMA * 1e12)
-    if args.workload == "skinny" or hbm_tree:
+    tree_roof = None
+    if hasattr(wl, "finish"):
+        wl.finish(ms_per_step)
+    if hasattr(wl, "tree_roofline"):
+        # trees: the dominant kernel from a per-launch timed run of the same
+        # step (HIP events around every launch on the library's stream), and
+        # the sum of per-step roofline times against the measured step
+        roofline, tree_roof = wl.tree_roofline(ms_per_step)
+        t = measured_traffic(args.workload, roofline["kernel"])
+        roofline["traffic"] = round(t) if t is not None else None
+        log(f"dominant kernel {roofline['kernel']}: {roofline['achieved']} {roofline['unit']} "
+            f"({roofline['frac']:.3f} of peak); sum of step rooflines {tree_roof['sum_t_roof_ms']} ms = "
+            f"{tree_roof['frac']:.3f} of the measured step")
+    elif args.workload == "skinny":
         # HBM-bound steps: algorithmic bytes / time against the HBM peak
         ach_bw = dom[1][3] / (dom[1][1] / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach_bw, 1), "peak": PEAK_HBM, "unit": "GB/s",
@@ -850,7 +1069,7 @@ def main():
         slicing = wl.slicing(max(1, args.steps), [int(x) for x in args.slices.split(",")], base_ms=ms_per_step)
 
     monomial = None
-    if args.check_monomial:
+    if args.check_monomial or isinstance(wl, SlicedGridWorkload):
         monomial = wl.check_monomial()
 
     distribution = None
@@ -870,6 +1089,7 @@ def main():
             "wall_s_per_result": round(ms_per_step / 1e3 / max(1, nlaunch), 6),
             "plan_ms_host": getattr(wl, "plan_ms_host", None),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
+            **({"tree_roofline": tree_roof} if tree_roof is not None else {}),
             **({"ablation": ablation} if ablation is not None else {}),
             **({"slicing": slicing} if slicing is not None else {}),
             **({"distribution": distribution} if distribution is not None else {}),

@@ -107,6 +107,10 @@ typedef struct {
                                  operand + output entries share grouped launches */
   int32_t max_group;          /* 256: most steps in one grouped launch */
   int32_t precision;          /* TNC_PREC_EXACT: arithmetic of GEMM-class complex64 steps */
+  int64_t slice_begin;        /* 0, 0: all slices.  Otherwise tnc_execute runs only slices */
+  int64_t slice_end;          /*   slice_begin <= sigma < slice_end (0 <= begin < end <= number of
+                                   slices) and leaves their sum in `out`: partial sums that add up to
+                                   the whole result, e.g. one range per process or per call */
 } tnc_plan_options;
 
 /* Arithmetic of the GEMM-class steps of a complex64 plan.  EXACT: FP32
@@ -200,13 +204,51 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  * leaves, out and workspace alive until the stream has finished; a HIP graph
  * that captured a call reads the plan's host descriptors on every replay, so
  * the plan must also outlive every such graph.  One plan may run concurrently on different
- * streams given distinct workspaces and outputs.  A sliced plan loops over all
- * slices and leaves their sum in `out`.
+ * streams given distinct workspaces and outputs.  A sliced plan loops over its
+ * slices (all of them, or options.slice_begin .. slice_end - 1) and leaves
+ * their sum in `out`.  Slice sigma fixes the sliced modes to the digits of
+ * sigma in the mixed radix of their extents, the first sliced mode most
+ * significant.
  * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP (pinned allocation or launch
  * failure; faults surface at the caller's next synchronisation).
  */
 tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
                        uint64_t workspace_bytes, void *stream);
+
+/*
+ * Profiling: run the plan like tnc_execute, with a pair of HIP events around
+ * every launch, and report each launch's kernel and time.  Synchronous: it
+ * waits for the stream after every slice to read the events (so it is for
+ * measurement, not for production runs), and it creates HIP events.
+ *   ops[max_ops]  caller-owned records, one per launch of the plan's program
+ *                 plus one (index 0) for the descriptor header; at most
+ *                 3 * num_steps + 2 are needed
+ *   *num_ops      records written
+ * A launch of a sliced plan runs once per slice: `ms` sums them and
+ * `launches` counts them.  Errors: INVALID_ARG (also when max_ops is too
+ * small; tnc_last_error says how many are needed), WORKSPACE_TOO_SMALL, HIP.
+ */
+typedef enum {
+  TNC_OP_COPY = 0,          /* permuting copies (leaf staging, naive-order re-layouts) */
+  TNC_OP_TINY_GROUP = 1,    /* one grouped launch of small steps */
+  TNC_OP_SKINNY = 2,        /* one step with a side of at most 16 */
+  TNC_OP_GEMM = 3,          /* one matrix-core GEMM step */
+  TNC_OP_COPY_TILED = 4,    /* one large permuting copy through LDS tiles */
+  TNC_OP_HEADER = 5         /* pointer table and descriptor upload */
+} tnc_op_kind;
+
+typedef struct {
+  int32_t kind;             /* tnc_op_kind */
+  int32_t step;             /* the step of a SKINNY or GEMM launch, else -1 */
+  int32_t count;            /* copies or steps in the launch */
+  int32_t launches;         /* times the launch ran */
+  double ms;                /* its total time over those runs */
+  char kernel[64];          /* the kernel the launcher chose, e.g. "k_cgemm_tile<128,128>" */
+} tnc_op_timing;
+
+tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                             uint64_t workspace_bytes, void *stream, tnc_op_timing *ops, int32_t max_ops,
+                             int32_t *num_ops);
 
 /*
  * Run the plan without allocating anything: for callers that cannot allocate

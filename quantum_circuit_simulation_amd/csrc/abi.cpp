@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -72,6 +73,8 @@ void tnc_plan_options_default(tnc_plan_options *o) {
   o->tiny_mnk = 131072;
   o->max_group = 256;
   o->precision = TNC_PREC_EXACT;
+  o->slice_begin = 0;
+  o->slice_end = 0;
 }
 
 tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
@@ -165,12 +168,37 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
 
 namespace {
 
+// Per-launch timing for tnc_execute_timed: an event pair around every
+// launch of the program, read back after each slice.
+struct OpTimer {
+  std::vector<hipEvent_t> ev;   // 2 per op: [header, program ops...]
+  std::vector<tnc_op_timing> *ops = nullptr;
+  hipError_t err = hipSuccess;
+  ~OpTimer() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  void record(size_t i, int end, hipStream_t s) {
+    if (err == hipSuccess) err = hipEventRecord(ev[2 * i + end], s);
+  }
+  // after a slice: wait, add each op's time, keep its kernel name
+  void collect(hipStream_t s) {
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    for (size_t i = 0; err == hipSuccess && i < ops->size(); ++i) {
+      float ms = 0;
+      err = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+      (*ops)[i].ms += ms;
+      (*ops)[i].launches += 1;
+    }
+  }
+};
+
 // Runs `plan` with its workspace at `workspace`.  may_pin: the first call on
 // the plan outside stream capture may allocate the pinned descriptor copy;
 // without it, a plan that has no pinned copy yet uploads its descriptors
 // with a host-to-device copy from the plan's own host memory.
 tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
-                    uint64_t workspace_bytes, void *stream_ptr, bool may_pin) {
+                    uint64_t workspace_bytes, void *stream_ptr, bool may_pin, OpTimer *tm = nullptr) {
   const tnc::PlanImpl &p = plan->impl;
   // an error left behind by an earlier, unrelated HIP call is not ours
   (void)hipGetLastError();
@@ -213,6 +241,7 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
     pinned = plan->blob_pinned;
   }
   tnc_status st;
+  if (tm) tm->record(0, 0, stream);
   if (pinned) {
     st = check(tnc::launch_header(ptab, arena, out, leaves, p.L, pinned, blob, p.blob_bytes, stream), stream,
                "k_header launch");
@@ -224,6 +253,7 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
                  "k_header launch");
   }
   if (st != TNC_OK) return st;
+  if (tm) tm->record(0, 1, stream);
 
   const auto *runs = reinterpret_cast<const tnc::RunDev *>(blob + p.blob_runs);
   const auto *cdesc = reinterpret_cast<const tnc::CopyDesc *>(blob + p.blob_copies);
@@ -244,20 +274,24 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
   };
   const bool z = p.dtype == TNC_C128;
 
-  int64_t num_slices = p.stats.num_slices;
+  const int64_t s_begin = p.slice_begin, s_end = p.slice_end;
   tnc::SliceDigits sd{};
   sd.n = (int32_t)p.slice_extents.size();
-  for (int64_t sigma = 0; sigma < num_slices; ++sigma) {
+  for (int64_t sigma = s_begin; sigma < s_end; ++sigma) {
     // digits of sigma over the sliced extents, first sliced mode most significant
     int64_t r = sigma;
     for (int t = sd.n - 1; t >= 0; --t) {
       sd.digit[t] = (int32_t)(r % p.slice_extents[t]);
       r /= p.slice_extents[t];
     }
-    const int32_t beta = sigma > 0 ? 1 : 0;
+    const int32_t beta = sigma > s_begin ? 1 : 0;
     for (size_t oi = 0; oi < p.program.size(); ++oi) {
       const tnc::Op &op = p.program[oi];
       hipError_t e = hipSuccess;
+      if (tm) {
+        tm->record(oi + 1, 0, stream);
+        tnc::clear_kernel_name();
+      }
       switch (op.kind) {
         case tnc::OP_COPY:
           e = tnc::launch_copy(cdesc + op.first, op.count, op.max_count, ptab, ints, sd, beta, z, stream);
@@ -310,6 +344,17 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
       }
       st = check(e, stream, op_name(op.kind));
       if (st != TNC_OK) return st;
+      if (tm) {
+        tm->record(oi + 1, 1, stream);
+        std::snprintf((*tm->ops)[oi + 1].kernel, sizeof((*tm->ops)[oi + 1].kernel), "%s",
+                      tnc::last_kernel_name());
+      }
+    }
+    if (tm) {
+      tm->collect(stream);
+      if (tm->err != hipSuccess) return check(tm->err, stream, "per-launch timing events");
+      // the header runs once per call, not per slice
+      if (sigma + 1 < s_end) (*tm->ops)[0].launches -= 1;
     }
   }
   return TNC_OK;
@@ -364,6 +409,53 @@ tnc_status tnc_execute(tnc_plan_t plan, const void *const *leaves, void *out, vo
   g_last_error.clear();
   if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;
   return run_plan(plan, leaves, out, workspace, workspace_bytes, stream_ptr, true);
+}
+
+tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *out, void *workspace,
+                             uint64_t workspace_bytes, void *stream_ptr, tnc_op_timing *ops, int32_t max_ops,
+                             int32_t *num_ops) {
+  g_last_error.clear();
+  if (!plan || !leaves || !out || !ops || !num_ops) return TNC_ERR_INVALID_ARG;
+  const tnc::PlanImpl &p = plan->impl;
+  const size_t n = p.program.size() + 1;
+  if (max_ops < 0 || (size_t)max_ops < n) {
+    g_last_error = "ops holds " + std::to_string(max_ops) + " records, the plan has " + std::to_string(n);
+    return TNC_ERR_INVALID_ARG;
+  }
+  std::vector<tnc_op_timing> rec(n);
+  for (size_t i = 0; i < n; ++i) {
+    std::memset(&rec[i], 0, sizeof(rec[i]));
+    rec[i].step = -1;
+    rec[i].count = 1;
+  }
+  rec[0].kind = TNC_OP_HEADER;
+  std::snprintf(rec[0].kernel, sizeof(rec[0].kernel), "k_header");
+  for (size_t i = 1; i < n; ++i) {
+    const tnc::Op &op = p.program[i - 1];
+    rec[i].kind = op.kind == tnc::OP_COPY ? TNC_OP_COPY
+                  : op.kind == tnc::OP_COPY_TILED ? TNC_OP_COPY_TILED
+                  : op.kind == tnc::OP_TINY_GROUP ? TNC_OP_TINY_GROUP
+                  : op.kind == tnc::OP_SKINNY ? TNC_OP_SKINNY : TNC_OP_GEMM;
+    if (op.kind == tnc::OP_SKINNY || op.kind == tnc::OP_GEMM) rec[i].step = op.first;
+    if (op.kind == tnc::OP_COPY || op.kind == tnc::OP_TINY_GROUP) rec[i].count = op.count;
+  }
+  OpTimer tm;
+  tm.ops = &rec;
+  tm.ev.assign(2 * n, nullptr);
+  for (auto &e : tm.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      (void)hipGetLastError();
+      e = nullptr;
+      g_last_error = std::string("hipEventCreate: ") + hipGetErrorString(r);
+      return TNC_ERR_HIP;
+    }
+  }
+  tnc_status st = run_plan(plan, leaves, out, workspace, workspace_bytes, stream_ptr, true, &tm);
+  if (st != TNC_OK) return st;
+  for (size_t i = 0; i < n; ++i) ops[i] = rec[i];
+  *num_ops = (int32_t)n;
+  return TNC_OK;
 }
 
 tnc_status tnc_execute_noalloc(tnc_plan_t plan, const void *const *leaves, void *out, void *stream_ptr) {

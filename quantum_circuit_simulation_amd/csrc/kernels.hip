@@ -22,13 +22,32 @@
 // workspace's pointer table and descriptor blob.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstring>
 #include <type_traits>
 
 #include "kernels.hpp"
 
 namespace tnc {
 
+// Name of the last kernel a launcher enqueued on this thread (for the timed
+// executor's per-launch report).
+thread_local char g_kernel_name[64];
+
+const char *last_kernel_name() { return g_kernel_name; }
+void clear_kernel_name() { g_kernel_name[0] = 0; }
+
 namespace {
+
+void note_kernel(const char *name) { std::snprintf(g_kernel_name, sizeof(g_kernel_name), "%s", name); }
+template <typename... A>
+void note_kernel(const char *fmt, A... args) {
+  std::snprintf(g_kernel_name, sizeof(g_kernel_name), fmt, args...);
+}
+void note_append(const char *what) {
+  size_t n = std::strlen(g_kernel_name);
+  std::snprintf(g_kernel_name + n, sizeof(g_kernel_name) - n, "%s", what);
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -1574,6 +1593,7 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   constexpr int TWN = kWide ? WN / 2 : WN, TNT = kWide ? 512 : 256;
   if (kchunk > 64) {
     dim3 grid((unsigned)ntiles, (unsigned)a.splits);
+    note_kernel("k_cgemm_tile<%d,%d>", BM, BN);
     hipLaunchKernelGGL((k_cgemm_tile<BM, BN, BK, WM, TWN, TNT>), grid, dim3(TNT), 0, stream, a, kchunk,
                        (uint32_t)tiles_r, (uint32_t)tiles_c);
     return hipGetLastError();
@@ -1583,6 +1603,7 @@ hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   dim3 grid((unsigned)g, (unsigned)a.splits);
+  note_kernel("k_cgemm<%d,%d>", BM, BN);
   hipLaunchKernelGGL((k_cgemm<BM, BN, BK, WM, TWN, TNT>), grid, dim3(TNT), 0, stream, a, (int32_t)kchunk,
                      (uint32_t)tiles_r, (uint32_t)tiles_c);
   return hipGetLastError();
@@ -1983,6 +2004,7 @@ hipError_t run_split_reduce(const StepArgsT<T> &a, hipStream_t stream) {
   const int64_t total = a.R * a.S;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  note_append("+k_split_reduce");
   hipLaunchKernelGGL(k_split_reduce<T>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -2019,6 +2041,7 @@ hipError_t launch_copy(const CopyDesc *descs, int32_t count, int64_t max_count, 
   int64_t blocks = (max_count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
+  note_kernel("k_copy");
   if (z)
     hipLaunchKernelGGL(k_copy<double2>, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, descs, ptab,
                        ints, digits, beta);
@@ -2036,6 +2059,7 @@ hipError_t launch_copy_tiled(const CopyDesc *desc, int64_t count, const void *co
   int64_t blocks = (count + per - 1) / per;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
+  note_kernel("k_copy_tiled");
   if (z)
     hipLaunchKernelGGL((k_copy_tiled<double2, 1024>), dim3((unsigned)blocks), dim3(256), 0, stream, desc, ptab, ints,
                        digits, beta);
@@ -2054,6 +2078,7 @@ hipError_t launch_tiny(const TinyDesc *descs, int32_t count, int64_t max_rs, con
   if (parts > max_rs / 2048) parts = max_rs / 2048;
   if (parts < 1) parts = 1;
   const dim3 grid((unsigned)(count * parts));
+  note_kernel("k_tiny");
   if (z)
     hipLaunchKernelGGL(k_tiny<double2>, grid, dim3(256), 0, stream, descs, ptab, runs, beta, (int)parts);
   else
@@ -2070,6 +2095,7 @@ static hipError_t run_skinny_flat(const StepArgs &a, hipStream_t stream) {
   int64_t blocks = (a.R + per - 1) / per;
   const int64_t cap = 16 * (int64_t)num_cus();
   if (blocks > cap) blocks = cap;
+  note_kernel("k_skinny_flat<%d,%d,%d,%s,%d>", G, V, SP, YREG ? "true" : "false", U);
   hipLaunchKernelGGL((k_skinny_flat<G, V, SP, YREG, U>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -2099,6 +2125,7 @@ hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
   const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
   const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
   constexpr int NW = kSmallGemmWaves;
+  note_kernel("k_cgemm_small<%s,%d>", pair ? "true" : "false", NW);
   if (pair)
     hipLaunchKernelGGL((k_cgemm_small<true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
   else
@@ -2125,6 +2152,7 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   if (a.R >= 4096 && a.splits == 1 && a.K >= 8 && a.K <= kRowsKC) {
     const int rows = a.K <= 8 ? 2 : 1;
     const int64_t blocks = (a.R + 256 * rows - 1) / (256 * rows);
+    note_kernel("k_skinny_small<%d>", rows);
     if (rows == 2) hipLaunchKernelGGL(k_skinny_small<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(k_skinny_small<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -2132,13 +2160,16 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
     const int64_t tiles = (a.R + 255) / 256;
     int64_t g = 8 * (int64_t)num_cus();
     if (g > tiles) g = tiles;
+    note_kernel("k_skinny_rows");
     hipLaunchKernelGGL(k_skinny_rows, dim3((unsigned)g, 1), dim3(256), 0, stream, a, kchunk);
     return hipGetLastError();
   } else if (a.R >= 4096) {
     // many rows, K in chunks: one tile of 256 rows per workgroup
     const int64_t tiles = (a.R + 255) / 256;
+    note_kernel("k_skinny_rows");
     hipLaunchKernelGGL(k_skinny_rows, dim3((unsigned)tiles, (unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
   } else {
+    note_kernel("k_skinny");
     hipLaunchKernelGGL(k_skinny, dim3((unsigned)a.R, (unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
   }
   hipError_t e = hipGetLastError();
@@ -2152,6 +2183,7 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
     int64_t kchunk = a.K;
     if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + kBf3BK - 1) / kBf3BK * kBf3BK;
     if (tiles_r * tiles_c >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    note_kernel("k_cgemm_bf3");
     hipLaunchKernelGGL(k_cgemm_bf3, dim3((unsigned)(tiles_r * tiles_c), (unsigned)a.splits), dim3(256), 0, stream, a,
                        kchunk, (uint32_t)tiles_r, (uint32_t)tiles_c);
     hipError_t e = hipGetLastError();
@@ -2175,6 +2207,7 @@ hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream) {
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
   dim3 grid((unsigned)((a.R + 255) / 256), (unsigned)a.splits);
+  note_kernel("k_skinny_z");
   hipLaunchKernelGGL(k_skinny_z, grid, dim3(256), 0, stream, a, kchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
@@ -2188,6 +2221,7 @@ hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream) {
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   dim3 grid((unsigned)(tiles_r * tiles_c), (unsigned)a.splits);
+  note_kernel("k_zgemm");
   hipLaunchKernelGGL(k_zgemm, grid, dim3(256), 0, stream, a, kchunk, (uint32_t)tiles_r, (uint32_t)tiles_c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;

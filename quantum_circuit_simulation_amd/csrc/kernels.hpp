@@ -56,4 +56,9 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream);
 hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream);
 hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream);
 
+// Name of the kernel the last launcher call on this thread enqueued (a split
+// K step appends "+k_split_reduce"); "" after clear_kernel_name().
+const char *last_kernel_name();
+void clear_kernel_name();
+
 }  // namespace tnc

@@ -796,8 +796,23 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   }
   for (int32_t l = 0; l < L; ++l) stt.staged_leaves += p->staged_leaf[l];
   stt.root_permute = p->root_permute;
-  stt.num_slices = 1;
-  for (int64_t e : p->slice_extents) stt.num_slices *= e;
+  {
+    __int128 ns = 1;
+    for (int64_t e : p->slice_extents) {
+      ns *= e;
+      if (ns > (__int128)(INT64_MAX / 2)) return TNC_ERR_UNSUPPORTED;
+    }
+    stt.num_slices = (int64_t)ns;
+  }
+  if (o.slice_begin == 0 && o.slice_end == 0) {
+    p->slice_begin = 0;
+    p->slice_end = stt.num_slices;
+  } else {
+    if (o.slice_begin < 0 || o.slice_end <= o.slice_begin || o.slice_end > stt.num_slices)
+      return TNC_ERR_INVALID_ARG;
+    p->slice_begin = o.slice_begin;
+    p->slice_end = o.slice_end;
+  }
   stt.flops = flops;
   stt.flops_unsliced = flops_u;
   stt.bytes = bytes;

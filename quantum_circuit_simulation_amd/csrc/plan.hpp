@@ -113,6 +113,7 @@ struct PlanImpl {
   std::vector<uint8_t> blob;                   // host image of the device descriptor blob
   uint64_t blob_runs = 0, blob_copies = 0, blob_tiny = 0, blob_ints = 0;  // byte offsets in blob
   std::vector<int64_t> slice_extents;          // extents of sliced modes
+  int64_t slice_begin = 0, slice_end = 1;      // slices tnc_execute runs
 };
 
 tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,

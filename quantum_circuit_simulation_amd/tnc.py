@@ -51,7 +51,8 @@ class Tree(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int), ("num_sliced", ctypes.c_int32), ("sliced_modes", P(ctypes.c_int32)),
                 ("align", ctypes.c_uint64), ("capacity_bytes", ctypes.c_uint64), ("tiny_mnk", ctypes.c_uint64),
-                ("max_group", ctypes.c_int32), ("precision", ctypes.c_int32)]
+                ("max_group", ctypes.c_int32), ("precision", ctypes.c_int32), ("slice_begin", ctypes.c_int64),
+                ("slice_end", ctypes.c_int64)]
 
 
 class PlanStats(ctypes.Structure):
@@ -103,10 +104,18 @@ class DistStep(ctypes.Structure):
 
 DIST_TAGS = ["replicated", "activate", "keep", "redistribute", "gather"]
 
+
+class OpTiming(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("step", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("ms", ctypes.c_double), ("kernel", ctypes.c_char * 64)]
+
+
+OP_KINDS = ["copy", "tiny_group", "skinny", "gemm", "copy_tiled", "header"]
+
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
            "tnc_execute", "tnc_status_string", "tnc_last_error", "tnc_dist_options_default",
-           "tnc_plan_distribute", "tnc_execute_noalloc"]
+           "tnc_plan_distribute", "tnc_execute_noalloc", "tnc_execute_timed"]
 NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # TNC_NOALLOC_MAX_WORKSPACE_BYTES
 
 _lib = None
@@ -147,6 +156,10 @@ def load_library(path: str = LIB_PATH):
     lib.tnc_execute.restype = ctypes.c_int
     lib.tnc_execute_noalloc.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p]
     lib.tnc_execute_noalloc.restype = ctypes.c_int
+    lib.tnc_execute_timed.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_uint64, ctypes.c_void_p, P(OpTiming), ctypes.c_int32,
+                                      P(ctypes.c_int32)]
+    lib.tnc_execute_timed.restype = ctypes.c_int
     lib.tnc_status_string.argtypes = [ctypes.c_int]
     lib.tnc_status_string.restype = ctypes.c_char_p
     lib.tnc_last_error.argtypes = []
@@ -183,7 +196,7 @@ class Plan:
     def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
                  order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
                  capacity_bytes: int = 0, tiny_mnk: int = 1 << 17, max_group: int = 256, dtype: int = TNC_C64,
-                 precision: int = 0):
+                 precision: int = 0, slice_range: Optional[Sequence[int]] = None):
         lib = load_library()
         self._lib = lib
         self.num_leaves = len(leaves)
@@ -210,6 +223,8 @@ class Plan:
         opts.tiny_mnk = tiny_mnk
         opts.max_group = max_group
         opts.precision = precision
+        if slice_range is not None:
+            opts.slice_begin, opts.slice_end = int(slice_range[0]), int(slice_range[1])
         h = ctypes.c_void_p()
         _check(lib.tnc_plan(ctypes.byref(net), ctypes.byref(tree), ctypes.byref(opts), ctypes.byref(h)), "tnc_plan")
         self._h = h
@@ -328,6 +343,27 @@ class Plan:
             stream = torch.cuda.current_stream()
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         self.execute_noalloc_ptrs([t.data_ptr() for t in leaves], out.data_ptr(), s)
+
+    def execute_timed(self, leaves, out, workspace, stream=None):
+        """tnc_execute_timed: run once with HIP events around every launch
+        (synchronous).  Returns one dict per launch of the program (index 0:
+        the descriptor header) with kind, step, count, launches, ms (summed
+        over slices) and kernel name."""
+        import torch
+        self.check_buffers(leaves, out, workspace)
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        cap = 3 * self.num_steps + 8
+        recs = (OpTiming * cap)()
+        n = ctypes.c_int32(0)
+        arr = (ctypes.c_void_p * max(1, len(leaves)))(*[int(t.data_ptr()) for t in leaves])
+        _check(self._lib.tnc_execute_timed(self._h, arr, ctypes.c_void_p(int(out.data_ptr())),
+                                           ctypes.c_void_p(int(workspace.data_ptr())),
+                                           ctypes.c_uint64(workspace.numel() * workspace.element_size()),
+                                           ctypes.c_void_p(s), recs, cap, ctypes.byref(n)), "tnc_execute_timed")
+        return [{"kind": OP_KINDS[r.kind], "step": r.step, "count": r.count, "launches": r.launches, "ms": r.ms,
+                 "kernel": r.kernel.decode()} for r in recs[:n.value]]
 
     def execute(self, leaves, out, workspace, stream=None):
         """leaves: torch complex64 tensors on the GPU (declared layouts), out:

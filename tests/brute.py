@@ -56,3 +56,27 @@ def track_basis_state(n: int, gates, bits0=None):
         amp *= complex(col[o])
         bits[a], bits[b] = o >> 1, o & 1
     return bits, amp
+
+
+def monomial_mode_values(net, gates, n: int):
+    """For the network of a circuit of monomial gates built by
+    ``Circuit.to_network`` (n ket leaves, then one leaf [out_a, out_b, in_a,
+    in_b] per gate in time order): the value every wire mode takes on the one
+    basis-state path that starts at |0...0>, and the path's amplitude (the
+    product of the gates' non-zero entries along it).  With the bra set to
+    the path's final bits, every mode assignment that leaves this path
+    contributes exactly zero."""
+    vals = {}
+    for q in range(n):
+        vals[net.leaves[q][0]] = 0
+    amp = complex(1.0)
+    for g, (a, b, u) in enumerate(gates):
+        oa, ob, ia, ib = net.leaves[n + g]
+        i = 2 * vals[ia] + vals[ib]
+        col = np.asarray(u)[:, i]
+        nz = np.flatnonzero(np.abs(col) > 0)
+        assert len(nz) == 1, "gate is not monomial"
+        o = int(nz[0])
+        amp *= complex(col[o])
+        vals[oa], vals[ob] = o >> 1, o & 1
+    return vals, amp

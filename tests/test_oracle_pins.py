@@ -351,3 +351,26 @@ def test_pair_block_matches_the_contractor_on_gathered_rows():
     a1, b1 = _cn(rng, (7, 1)), _cn(rng, (4, 1))
     outer = oracle.contract([7, 4], [[0], [1]], [0, 1], [a1.reshape(7), b1.reshape(4)], [0], [1])
     assert np.max(np.abs(oracle.pair_block(a1, b1) - outer)) <= 1e-14
+
+
+def test_monomial_path_values_select_the_one_nonzero_slice():
+    """For a monomial circuit every mode takes one value on the tracked
+    basis-state path: fixing any modes to those values keeps the whole
+    amplitude, fixing one of them to the other value gives exactly zero."""
+    from tests.brute import monomial_mode_values, track_basis_state
+    c = circuits.grid_monomial(3, 4, 8, 21)
+    g64 = _gates64(c)
+    bits, amp = track_basis_state(12, g64)
+    net = c.to_network(bits=bits)
+    vals, amp2 = monomial_mode_values(net, g64, 12)
+    assert abs(amp2 - amp) < 1e-12
+    tree = trees.greedy_tree(net)
+    closed = trees.closed_modes(net)
+    rng = np.random.default_rng(4)
+    pick = [int(x) for x in rng.choice(closed, size=3, replace=False)]
+    on = oracle.contract_network(net, tree, fixed={x: vals[x] for x in pick})
+    ok, err = rel_err_ok(on, amp, TOL128)
+    assert ok, err
+    off = {x: vals[x] for x in pick}
+    off[pick[1]] ^= 1
+    assert oracle.contract_network(net, tree, fixed=off) == 0

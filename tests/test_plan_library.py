@@ -220,3 +220,14 @@ def test_noalloc_rejects_a_plan_beyond_the_static_workspace_before_any_hip_call(
     header = open(os.path.join(ROOT, "include", "tnc.h")).read()
     m = re.search(r"#define TNC_NOALLOC_MAX_WORKSPACE_BYTES \(UINT64_C\((\d+)\) << (\d+)\)", header)
     assert m and int(m.group(1)) << int(m.group(2)) == tnc.NOALLOC_MAX_WORKSPACE_BYTES
+
+
+def test_slice_range_is_checked_at_plan_time():
+    net = circuits.brickwork(8, 4, 1).to_network()
+    tree = trees.greedy_tree(net)
+    sl = trees.choose_slices(net, tree, 2)
+    assert qa.Plan.from_network(net, tree, sliced=sl, slice_range=(1, 3)).stats()["num_slices"] == 4
+    for bad in ((2, 2), (3, 1), (-1, 2), (0, 5)):
+        with pytest.raises(tnc.TncError) as e:
+            qa.Plan.from_network(net, tree, sliced=sl, slice_range=bad)
+        assert e.value.name == "TNC_ERR_INVALID_ARG", bad

@@ -1,0 +1,79 @@
+"""Write the stored contraction trees of the grid-circuit workloads
+(``workloads/data/*.json``) with the native search of ``treeopt.cpp``.
+
+A tree is an input of a workload, like its seeded leaf data: the search is
+deterministic for its seed and parameters but takes minutes on 8 cores, so
+the benchmark and the tests read the stored result.  Each file records the
+network it belongs to (structure digest), the search parameters, the steps,
+the sliced modes and the tree's cost.
+
+    python workloads/make_trees.py [name ...]
+"""
+
+from __future__ import annotations
+
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+
+from workloads import circuits, trees  # noqa: E402
+
+# name -> (rows, cols, depth, seed, search parameters)
+SPECS = {
+    # the 56-qubit grid at depth 16: slices of at most 2^33 entries, at most
+    # 2^34.6 entries live (a slice's workspace must fit the 288 GB of HBM)
+    # trials ranked by roofline time at the MI355X ridge (19.7 multiply-adds
+    # per complex64 entry moved)
+    "grid_7x8_d16": (7, 8, 16, 505, dict(trials=768, seed=1, max_log_width=34.0, max_log_peak=34.6,
+                                         reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66)),
+    "grid_7x8_d11": (7, 8, 11, 505, dict(trials=256, seed=1, max_log_width=34.0, max_log_peak=34.6,
+                                         reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66)),
+    "grid_6x6_d14": (6, 6, 14, 505, dict(trials=256, seed=1, max_log_width=34.0, max_log_peak=34.6,
+                                         reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66)),
+}
+
+
+def structure_digest(net) -> str:
+    h = hashlib.sha256()
+    for l in net.leaves:
+        h.update(",".join(map(str, l)).encode() + b"|")
+    h.update(",".join(map(str, net.extents)).encode())
+    h.update(b"out:" + ",".join(map(str, net.out_modes)).encode())
+    return h.hexdigest()
+
+
+def path(name: str) -> str:
+    return os.path.join(HERE, "data", name + ".json")
+
+
+def make(name: str, threads: int = 8) -> dict:
+    rows, cols, depth, seed, params = SPECS[name]
+    net = circuits.grid_fsim(rows, cols, depth, seed).to_network()
+    t0 = time.time()
+    tree, sliced, st = trees.optimize_tree(net, threads=threads, **params)
+    el = time.time() - t0
+    c = trees.tree_cost(net, tree, sliced)
+    rec = {"name": name, "network": {"family": "grid_fsim", "rows": rows, "cols": cols, "depth": depth,
+                                     "seed": seed, "structure_sha256": structure_digest(net)},
+           "search": {k: list(v) if isinstance(v, tuple) else v for k, v in params.items()},
+           "search_seconds": round(el, 1), "lhs": tree.lhs, "rhs": tree.rhs, "sliced": sliced,
+           "log2_width": math.log2(c["max_elems"]), "flop_per_slice": c["flops"],
+           "flop_sliced_total": c["flops"] * c["num_slices"],
+           "flop_unsliced": trees.tree_cost(net, tree)["flops"], "search_stats": st}
+    os.makedirs(os.path.dirname(path(name)), exist_ok=True)
+    with open(path(name), "w") as f:
+        json.dump(rec, f)
+    return rec
+
+
+if __name__ == "__main__":
+    for name in sys.argv[1:] or list(SPECS):
+        r = make(name)
+        print(name, f"{r['search_seconds']}s width 2^{r['log2_width']:.0f} sliced {len(r['sliced'])} "
+              f"flop/slice {r['flop_per_slice']:.3e} total {r['flop_sliced_total']:.3e}", flush=True)

@@ -382,3 +382,112 @@ def partition_search(net: Network, trials: int, seed: int = 0, imbalances=(0.05,
         if best_key is None or key < best_key:
             best, best_key = tr, key
     return best
+
+
+# ---------------------------------------------------------------------------
+# native tree and slice search (treeopt.cpp)
+
+_TREEOPT = None
+
+
+def _treeopt_lib():
+    global _TREEOPT
+    if _TREEOPT is None:
+        import ctypes
+        import os
+        from . import treeopt_build
+        if not os.path.exists(treeopt_build.LIB):
+            treeopt_build.build()
+        lib = ctypes.CDLL(treeopt_build.LIB)
+        P = ctypes.POINTER
+        lib.treeopt_search.restype = ctypes.c_int
+        lib.treeopt_search.argtypes = [ctypes.c_int32, ctypes.c_int32, P(ctypes.c_double), P(ctypes.c_int32),
+                                       P(ctypes.c_int32), P(ctypes.c_double), P(ctypes.c_int32),
+                                       P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int32),
+                                       P(ctypes.c_double)]
+        lib.treeopt_refine.restype = ctypes.c_int
+        lib.treeopt_refine.argtypes = lib.treeopt_search.argtypes
+        _TREEOPT = lib
+    return _TREEOPT
+
+
+def _treeopt_call(fn: str, net: Network, params, tree: Optional[Tree] = None, sliced: Sequence[int] = (),
+                  max_sliced: int = 64):
+    import ctypes
+    import math
+    lib = _treeopt_lib()
+    L = net.num_leaves
+    logw = np.ascontiguousarray([math.log2(float(e)) for e in net.extents], dtype=np.float64)
+    rank = np.ascontiguousarray([len(l) for l in net.leaves], dtype=np.int32)
+    modes = np.ascontiguousarray([x for l in net.leaves for x in l] or [0], dtype=np.int32)
+    params = np.ascontiguousarray(params, dtype=np.float64)
+    lhs = np.zeros(max(1, L - 1), np.int32)
+    rhs = np.zeros(max(1, L - 1), np.int32)
+    sl = np.zeros(max(1, max_sliced, len(sliced)), np.int32)
+    if tree is not None:
+        lhs[:L - 1] = tree.lhs
+        rhs[:L - 1] = tree.rhs
+    sl[:len(sliced)] = list(sliced)
+    ns = ctypes.c_int32(len(sliced))
+    st = np.zeros(4, np.float64)
+    P = ctypes.POINTER
+    rc = getattr(lib, fn)(L, len(net.extents), logw.ctypes.data_as(P(ctypes.c_double)),
+                          rank.ctypes.data_as(P(ctypes.c_int32)), modes.ctypes.data_as(P(ctypes.c_int32)),
+                          params.ctypes.data_as(P(ctypes.c_double)), lhs.ctypes.data_as(P(ctypes.c_int32)),
+                          rhs.ctypes.data_as(P(ctypes.c_int32)), sl.ctypes.data_as(P(ctypes.c_int32)),
+                          ctypes.byref(ns), st.ctypes.data_as(P(ctypes.c_double)))
+    if rc != 0:
+        raise RuntimeError(f"{fn} failed ({rc})")
+    out = Tree([int(x) for x in lhs[:L - 1]], [int(x) for x in rhs[:L - 1]])
+    return out, [int(x) for x in sl[:ns.value]], dict(log2_cost=float(st[0]), width=float(st[1]),
+                                                      peak_log2=float(st[2]), trial=int(st[3]))
+
+
+def optimize_tree(net: Network, trials: int = 64, seed: int = 0, max_log_width: float = 1e9,
+                  max_log_peak: float = 1e9, reconf_k: int = 8, reconf_rounds: int = 4, imbalance=(0.0, 0.3),
+                  cutoff=(6, 10), threads: int = 8, time_limit_s: float = 0.0, max_sliced: int = 64,
+                  ridge: float = 0.0, score_ridge: float = 0.0):
+    """Tree and sliced modes from the native search (recursive multilevel
+    bisection, subtree reconfiguration, slicing interleaved with
+    reconfiguration; see treeopt.cpp).  Slices until the widest sliced
+    intermediate has at most 2^max_log_width entries and at most
+    2^max_log_peak entries are live at once (in the returned step order).
+    Returns (Tree, sliced modes, stats) with stats = dict(log2_cost: log2 of
+    2^s * sum of m n k, width: log2 entries of the largest sliced
+    intermediate, peak_log2, trial).  Deterministic for a given seed and
+    parameters (the best trial wins, ties to the lowest index).  With
+    ``ridge`` > 0 a step costs max(m n k, ridge (m k + n k + m n)) instead of
+    m n k: its roofline time on a device doing ``ridge`` multiply-adds per
+    entry moved (a complex64 step on MI355X: 157.3e12 / 8 flop per
+    multiply-add against 8e12 / 8 entries per second gives 19.7).
+    ``score_ridge`` > 0 ranks the finished trials by that roofline cost
+    while each trial still minimises its own cost (log2_cost is then in
+    roofline units)."""
+    params = [trials, threads, seed, max_log_width, reconf_k, reconf_rounds, imbalance[0], imbalance[1],
+              cutoff[0], cutoff[1], time_limit_s, max_sliced, max_log_peak, ridge, score_ridge]
+    return _treeopt_call("treeopt_search", net, params, max_sliced=max_sliced)
+
+
+def refine_tree(net: Network, tree: Tree, sliced: Sequence[int] = (), reconf_k: int = 10, reconf_rounds: int = 8,
+                max_log_width: float = 1e9, max_log_peak: float = 1e9, seed: int = 0, max_sliced: int = 64,
+                ridge: float = 0.0):
+    """Reconfigure a given tree (frontier of ``reconf_k`` tensors) with its
+    sliced modes, slicing further if a bound is exceeded; same returns as
+    ``optimize_tree``."""
+    params = [1, 1, seed, max_log_width, reconf_k, reconf_rounds, 0.0, 0.0, 1, 1, 0.0, max_sliced, max_log_peak,
+              ridge, 0.0]
+    return _treeopt_call("treeopt_refine", net, params, tree=tree, sliced=sliced, max_sliced=max_sliced)
+
+
+def stored_tree(name: str, net: Optional[Network] = None):
+    """(Tree, sliced modes, record) of a stored search result
+    (``workloads/data/<name>.json``, written by ``workloads/make_trees.py``).
+    With ``net`` given, checks that the record belongs to that network."""
+    import json
+    import os
+    from . import make_trees
+    with open(make_trees.path(name)) as f:
+        rec = json.load(f)
+    if net is not None and make_trees.structure_digest(net) != rec["network"]["structure_sha256"]:
+        raise ValueError(f"stored tree {name} belongs to another network")
+    return Tree(rec["lhs"], rec["rhs"]), list(rec["sliced"]), rec
