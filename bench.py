@@ -758,6 +758,36 @@ class SlicedGridWorkload:
         res["pass"] = bool(err <= 1e-4 and res["other1"] == [0.0, 0.0] and res["other2"] == [0.0, 0.0])
         return res
 
+    def slicing(self, steps, extra_list, base_ms):
+        """The same tree sliced on e more modes (greedy, trees.more_slices):
+        the same share of the whole work, 2^e times as many slices, timed
+        against the minimal slicing; R = flop ratio, E = time ratio."""
+        import torch
+        import quantum_circuit_simulation_amd as qa
+        from workloads import trees
+        res = {"base": {"sliced_modes": len(self.sliced), "ms": base_ms,
+                        "flop": self.flops_slice * self.timed_slices}}
+        chosen = trees.more_slices(self.net, self.tree, self.sliced, max(extra_list))
+        f0 = self.flops_slice * self.timed_slices
+        for e in extra_list:
+            sl = chosen[:len(self.sliced) + e]
+            n = self.timed_slices << e
+            plan = qa.Plan.from_network(self.net, self.tree, sliced=sl, slice_range=(0, n))
+            plan.execute(self.leaves, self.out, self.ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                plan.execute(self.leaves, self.out, self.ws)
+                e1.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            fl = plan.stats()["flops"] * n
+            res[f"extra{e}"] = {"sliced_modes": len(sl), "slices_run": n, "ms": round(ms, 3), "flop": fl,
+                                "R": round(fl / f0, 4), "E": round(ms / base_ms, 4),
+                                "capture": round((ms / base_ms) / (fl / f0), 4)}
+            log(f"slicing +{e} modes: {n} slices in {ms:.1f} ms, R={fl / f0:.3f}, E={ms / base_ms:.3f}")
+        return res
+
     def kernel_of(self, idx):
         return "whole tree"
 
@@ -772,50 +802,27 @@ class SlicedGridWorkload:
         tree with its sliced modes and a few more modes fixed (each time the
         mode held by the widest intermediates that carries the most
         operations), until one sub-slice has at most 2^24-entry
-        intermediates and 2e11 flop; rate = its flops / its time."""
+        intermediates and 3e11 flop; rate = its flops / its time."""
         import oracle
         from workloads import trees
-        fixed = list(self.sliced)
-        ext = [int(e) for e in self.net.extents]
-        sets = [0] * (len(self.net.leaves) + len(self.tree.lhs))
-        for i, l in enumerate(self.net.leaves):
-            for x in l:
-                sets[i] |= 1 << x
-        L = len(self.net.leaves)
-        for s, (a, b) in enumerate(zip(self.tree.lhs, self.tree.rhs)):
-            sets[L + s] = sets[a] ^ sets[b]
-        unions = [sets[a] | sets[b] for a, b in zip(self.tree.lhs, self.tree.rhs)]
-        while True:
-            mask = sum(1 << x for x in fixed)
-            w = max((t & ~mask).bit_count() for t in sets)
-            fl = sum(8.0 * 2.0 ** (u & ~mask).bit_count() for u in unions)
-            if w <= 24 and fl <= 2e11:
-                break
-            contrib = {}
-            for u in unions:
-                c = 2.0 ** (u & ~mask).bit_count()
-                v = u & ~mask
-                while v:
-                    x = (v & -v).bit_length() - 1
-                    contrib[x] = contrib.get(x, 0.0) + c
-                    v &= v - 1
-            widest = [t & ~mask for t in sets if (t & ~mask).bit_count() == w]
-            cand = set()
-            for t in widest:
-                v = t
-                while v:
-                    cand.add((v & -v).bit_length() - 1)
-                    v &= v - 1
-            x = max(cand, key=lambda y: (sum(1 for t in widest if t >> y & 1), contrib.get(y, 0.0), -y))
-            fixed.append(x)
+        fixed = trees.more_slices(self.net, self.tree, self.sliced, 0, max_log_width=24, max_flop=3e11)
+        c = trees.tree_cost(self.net, self.tree, fixed)
+        w, fl = int(np.log2(c["max_elems"])), float(c["flops"])
         threads = oracle.max_threads()
         t0 = time.perf_counter()
-        oracle.contract_network(self.net, self.tree, fixed={x: 0 for x in fixed}, threads=threads)
+        done = 0
+        while done < 64:
+            # sub-slice `done`: its digits over the fixed modes, last mode fastest
+            vals = {x: (done >> (len(fixed) - 1 - i)) & 1 for i, x in enumerate(fixed)}
+            oracle.contract_network(self.net, self.tree, fixed=vals, threads=threads)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
         el = time.perf_counter() - t0
-        return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                "sample": f"one sub-slice of the same tree ({len(fixed)} modes fixed: the {len(self.sliced)} "
+        return {"value": done * fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} sub-slices of the same tree ({len(fixed)} modes fixed: the {len(self.sliced)} "
                           f"sliced modes and {len(fixed) - len(self.sliced)} more; width 2^{w}, {fl:.3g} flop "
-                          f"in {el:.1f} s)"}
+                          f"each, {el:.1f} s)"}
 
 
 KERNEL_SRC = os.path.join(ROOT, "quantum_circuit_simulation_amd", "csrc", "kernels.hip")

@@ -320,6 +320,10 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           a.splits = nd.splits;
           a.scratch = nd.splits > 1 ? reinterpret_cast<float2 *>(arena + nd.scratch_off) : nullptr;
           a.prec = p.opts.precision;
+          a.pow2_runs = 1;
+          for (const auto *side : {&nd.row_runs, &nd.col_runs})
+            for (const auto &r : *side)
+              if (r.size < 1 || (r.size & (r.size - 1)) != 0) a.pow2_runs = 0;
           if (z) {
             // same fields, complex128 entries
             tnc::StepArgsZ az{};
@@ -335,6 +339,7 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
             az.beta = a.beta;
             az.splits = a.splits;
             az.scratch = reinterpret_cast<double2 *>(a.scratch);
+            az.pow2_runs = a.pow2_runs;
             e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm_z(az, stream) : tnc::launch_skinny_z(az, stream);
           } else {
             e = op.kind == tnc::OP_GEMM ? tnc::launch_gemm(a, stream) : tnc::launch_skinny(a, stream);

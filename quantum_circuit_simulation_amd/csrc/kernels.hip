@@ -873,6 +873,182 @@ __global__ __launch_bounds__(256) void k_skinny_flat(StepArgs a) {
   }
 }
 
+// Skinny steps with many rows, S <= 16 outputs per row (a power of two),
+// K in {2, 4, ..., 32}, on the FP32 matrix cores, written in address order.
+//
+// Each wave owns blocks of 32 rows: it loads the block's X rows (one
+// contiguous stretch of 32 K entries) with coalesced 16-byte loads into a
+// wave-private LDS area, runs K v_mfma_f32_32x32x2_f32 over it and writes
+// the 32 x S results back into the same area (LDS operations of one wave
+// complete in order, so no barrier is needed).  The 32 MFMA columns carry
+// the real parts of the S outputs (columns 0-15) and their imaginary parts
+// (16-31): with the (re, im) K-slot scheme of k_cgemm, column j < 16 takes
+// (yr, -yi) of output j and column 16 + j takes (yi, yr), so one MFMA per
+// complex entry of K yields both parts.  The next block's loads are issued
+// before this block's MFMAs and stores.
+//
+// Stores: when every run of C has a power-of-two size, the offset of row
+// r0 + t (r0 a multiple of 32) is rowoff(r0) + rowoff(t), so the block's
+// 32 S outputs sit at rowoff(r0) + rowoff(t) + coloff(j), and the offset is
+// a sum of one stride per set bit of (t, j).  Ordering those 5 + log2 S bits
+// by stride gives a fixed permutation of the block's entries into ascending
+// addresses; the wave stores the block in that order, so lanes write
+// consecutive addresses wherever C is contiguous (16-byte pairs when the
+// smallest stride is one entry), whatever the interleaving of C's modes.
+constexpr int kSmRows = 32;
+
+// NB 32-row sub-blocks per wave iteration (NB * S <= 32): small K and S move
+// few bytes per block, so a wave takes several blocks per pass.
+template <int K, int NB>
+__global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
+  constexpr int KH = K / 2;                  // 16-byte entry pairs per X row
+  constexpr int RSX = KH + 1;                // LDS row stride (16-byte units), one pad
+  constexpr int ROWS = kSmRows * NB;         // rows per wave pass
+  constexpr int XW = ROWS * RSX;             // X rows of one pass
+  constexpr int CW = kSmRows * 32 / 2;       // ROWS x S complex results (NB S <= 32)
+  constexpr int WB = XW > CW ? XW : CW;
+  constexpr int LPT = (ROWS * KH + 63) / 64;  // 16-byte loads per lane per pass
+  constexpr int LB = 5 + (NB >= 8 ? 3 : NB >= 4 ? 2 : NB >= 2 ? 1 : 0);  // row bits of a pass
+  __shared__ float4 buf[4][WB];
+  __shared__ int64_t rowoff[ROWS], coloff[16];
+  __shared__ uint16_t perm[kSmRows * 32];
+  __shared__ int32_t bit_of[12];
+  __shared__ int32_t nbits_s, pairs_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int S = (int)a.S;
+  const int sb = 31 - __clz(S);  // S is a power of two
+  for (int t = tid; t < ROWS + 16; t += 256) {
+    if (t < ROWS) rowoff[t] = run_offset(t, a.runs, a.nrr);
+    else coloff[t - ROWS] = t - ROWS < S ? run_offset(t - ROWS, a.runs + a.nrr, a.ncr) : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // permutation bits: bits 0 .. sb-1 of an entry index are its column, bits 4 .. 4+LB-1 its row
+    int64_t st[12];
+    int pb[12], nb = 0;
+    for (int b = 0; b < sb; ++b) {
+      st[nb] = coloff[1 << b];
+      pb[nb++] = b;
+    }
+    for (int b = 0; b < LB; ++b) {
+      st[nb] = rowoff[1 << b];
+      pb[nb++] = 4 + b;
+    }
+    for (int i = 1; i < nb; ++i)
+      for (int q = i; q > 0 && st[q] < st[q - 1]; --q) {
+        const int64_t ts = st[q];
+        st[q] = st[q - 1];
+        st[q - 1] = ts;
+        const int tp = pb[q];
+        pb[q] = pb[q - 1];
+        pb[q - 1] = tp;
+      }
+    for (int i = 0; i < nb; ++i) bit_of[i] = pb[i];
+    nbits_s = nb;
+    pairs_s = nb > 0 && st[0] == 1;
+  }
+  __syncthreads();
+  const int nent = ROWS << sb;
+  for (int e = tid; e < nent; e += 256) {
+    int p = 0;
+    for (int i = 0; i < nbits_s; ++i)
+      if ((e >> i) & 1) p |= 1 << bit_of[i];
+    perm[e] = (uint16_t)p;
+  }
+  // second operand, per lane and K entry: MFMA column l32 = (real | imaginary part of output l32 % 16)
+  float bv[K];
+  {
+    const int j = l32 & 15;
+    const bool imc = l32 >= 16;
+#pragma unroll
+    for (int l = 0; l < K; ++l) {
+      const float2 y = j < S ? a.Y[(int64_t)j * K + l] : make_float2(0.f, 0.f);
+      bv[l] = imc ? (h ? y.x : y.y) : (h ? -y.y : y.x);
+    }
+  }
+  __syncthreads();
+  const bool pairs = pairs_s && aligned16(a.C);
+  const int64_t R = a.R, npass = (R + ROWS - 1) / ROWS;
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  const int64_t lim = R * KH;
+  const float4 *X4 = (const float4 *)a.X;
+  float4 *xb = buf[wave];
+  float4 ld[LPT];
+  auto load = [&](int64_t b) {
+    const int64_t base = b * ROWS * KH;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i;
+      ld[i] = (g < ROWS * KH && base + g < lim) ? X4[base + g] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  if (blk < npass) load(blk);
+  for (; blk < npass; blk += wstride) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i;
+      if (g < ROWS * KH) xb[(g / KH) * RSX + g % KH] = ld[i];
+    }
+    if (blk + wstride < npass) load(blk + wstride);
+    f32x16 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < KH; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float4 f = xb[(nb * kSmRows + l32) * RSX + q];
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? f.y : f.x, bv[2 * q], acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? f.w : f.z, bv[2 * q + 1], acc[nb], 0, 0, 0);
+      }
+    // results as complex [ROWS][S] in the same LDS area
+    float *cf = (float *)xb;
+    const float2 *cv = (const float2 *)xb;
+    {
+      const int j = l32 & 15, part = l32 >> 4;
+      if (j < S) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * S + j) * 2 + part] = acc[nb][r];
+      }
+    }
+    const int64_t r0 = blk * ROWS;
+    const int64_t base = run_offset(r0, a.runs, a.nrr);
+    const int rows = (int)(R - r0 < ROWS ? R - r0 : ROWS);
+    if (pairs) {
+      for (int e = 2 * lane; e < nent; e += 128) {
+        const int p0 = perm[e], p1 = perm[e + 1];
+        const int t0 = p0 >> 4, j0 = p0 & 15, t1 = p1 >> 4, j1 = p1 & 15;
+        const int64_t o0 = base + rowoff[t0] + coloff[j0];
+        const float2 v0 = cv[t0 * S + j0], v1 = cv[t1 * S + j1];
+        if (t0 < rows && t1 < rows && (o0 & 1) == 0) {
+          float4 v = make_float4(v0.x, v0.y, v1.x, v1.y);
+          float4 *dst = (float4 *)(a.C + o0);
+          if (a.beta) {
+            const float4 c = *dst;
+            v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+          }
+          *dst = v;
+        } else {
+          if (t0 < rows) store_c(a.C + o0, v0, a.beta);
+          if (t1 < rows) store_c(a.C + base + rowoff[t1] + coloff[j1], v1, a.beta);
+        }
+      }
+    } else {
+      for (int e = lane; e < nent; e += 64) {
+        const int p = perm[e];
+        const int t = p >> 4, j = p & 15;
+        if (t < rows) store_c(a.C + base + rowoff[t] + coloff[j], cv[t * S + j], a.beta);
+      }
+    }
+  }
+}
+
 // sum split-K partials [splits, R, S] into C through the runs
 template <typename T>
 __global__ void k_split_reduce(StepArgsT<T> a) {
@@ -2121,6 +2297,47 @@ static bool skinny_flat_ok(const StepArgs &a) {
 
 bool small_gemm_ok(const StepArgs &a) { return a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK; }
 
+static bool skinny_mfma_ok(const StepArgs &a) {
+  const bool pow2s = a.S >= 1 && a.S <= 16 && (a.S & (a.S - 1)) == 0;
+  const bool pow2k = a.K >= 2 && a.K <= 32 && (a.K & (a.K - 1)) == 0;
+  return a.splits == 1 && a.R >= 4096 && pow2s && pow2k && a.pow2_runs && ((uintptr_t)a.X & 15) == 0;
+}
+
+template <int K, int NB>
+static hipError_t run_skinny_mfma_kn(const StepArgs &a, hipStream_t stream) {
+  const int64_t npass = (a.R + kSmRows * NB - 1) / (kSmRows * NB);
+  int64_t blocks = (npass + 3) / 4;
+  const int64_t cap = 8 * (int64_t)num_cus();
+  if (blocks > cap) blocks = cap;
+  note_kernel("k_skinny_mfma<%d,%d>", K, NB);
+  hipLaunchKernelGGL((k_skinny_mfma<K, NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// sub-blocks per wave pass: about 8 KB of operand and result rows per pass
+// (32 NB rows of K + S entries), with NB S <= 32
+template <int K>
+static hipError_t run_skinny_mfma_k(const StepArgs &a, hipStream_t stream) {
+  const int64_t fit = 32 / (K + a.S);
+  if constexpr (K <= 2)
+    if (fit >= 8 && a.S <= 4) return run_skinny_mfma_kn<K, 8>(a, stream);
+  if constexpr (K <= 4)
+    if (fit >= 4 && a.S <= 8) return run_skinny_mfma_kn<K, 4>(a, stream);
+  if constexpr (K <= 8)
+    if (fit >= 2) return run_skinny_mfma_kn<K, 2>(a, stream);
+  return run_skinny_mfma_kn<K, 1>(a, stream);
+}
+
+static hipError_t run_skinny_mfma(const StepArgs &a, hipStream_t stream) {
+  switch (a.K) {
+    case 2: return run_skinny_mfma_k<2>(a, stream);
+    case 4: return run_skinny_mfma_k<4>(a, stream);
+    case 8: return run_skinny_mfma_k<8>(a, stream);
+    case 16: return run_skinny_mfma_k<16>(a, stream);
+    default: return run_skinny_mfma_k<32>(a, stream);
+  }
+}
+
 hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
   const int64_t bc = (a.S + 31) / 32, blocks = ((a.R + 31) / 32) * bc;
   const bool pair = a.K % 2 == 0 && ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
@@ -2134,6 +2351,7 @@ hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
+  if (skinny_mfma_ok(a)) return run_skinny_mfma(a, stream);
   if (skinny_flat_ok(a)) {
     if (a.S <= 1) return run_skinny_flat_k<1>(a, stream);
     if (a.S <= 2) return run_skinny_flat_k<2>(a, stream);

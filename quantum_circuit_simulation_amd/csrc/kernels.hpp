@@ -32,6 +32,7 @@ struct StepArgsT {
   int32_t splits;
   T *scratch;
   int32_t prec;  // kPrecExact or kPrecBf16x3 (the plan's tnc_precision)
+  int32_t pow2_runs;  // every row and column run has a power-of-two size
 };
 constexpr int32_t kPrecExact = 0;   // TNC_PREC_EXACT
 constexpr int32_t kPrecBf16x3 = 1;  // TNC_PREC_BF16X3

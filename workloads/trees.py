@@ -491,3 +491,68 @@ def stored_tree(name: str, net: Optional[Network] = None):
     if net is not None and make_trees.structure_digest(net) != rec["network"]["structure_sha256"]:
         raise ValueError(f"stored tree {name} belongs to another network")
     return Tree(rec["lhs"], rec["rhs"]), list(rec["sliced"]), rec
+
+
+def more_slices(net: Network, tree: Tree, sliced: Sequence[int], extra: int,
+                max_log_width: Optional[float] = None, max_flop: Optional[float] = None) -> List[int]:
+    """Extend ``sliced`` greedily: each time the mode held by the most
+    intermediates of the largest (sliced) width, ties broken by the operation
+    count of the steps holding it (slicing it removes the most work), then
+    the lowest label.  Takes ``extra`` modes, or, with bounds given, as many
+    as needed until the widest sliced intermediate has at most
+    2^max_log_width entries and one slice at most max_flop (8 m n k)."""
+    L = net.num_leaves
+    sets = [0] * (L + len(tree.lhs))
+    for i, l in enumerate(net.leaves):
+        for x in l:
+            sets[i] |= 1 << x
+    for s, (a, b) in enumerate(zip(tree.lhs, tree.rhs)):
+        sets[L + s] = sets[a] ^ sets[b]
+    unions = [sets[a] | sets[b] for a, b in zip(tree.lhs, tree.rhs)]
+    lw = [float(np.log2(float(e))) for e in net.extents]
+
+    def size(bits):
+        t = 0.0
+        while bits:
+            x = (bits & -bits).bit_length() - 1
+            t += lw[x]
+            bits &= bits - 1
+        return t
+
+    out = list(sliced)
+    added = 0
+    while True:
+        mask = 0
+        for x in out:
+            mask |= 1 << x
+        widths = [size(t & ~mask) for t in sets]
+        w = max(widths)
+        if max_log_width is None and added >= extra:
+            break
+        if max_log_width is not None:
+            fl = sum(8.0 * 2.0 ** size(u & ~mask) for u in unions)
+            if w <= max_log_width and (max_flop is None or fl <= max_flop):
+                break
+        contrib: Dict[int, float] = {}
+        for u in unions:
+            c = 2.0 ** size(u & ~mask)
+            v = u & ~mask
+            while v:
+                x = (v & -v).bit_length() - 1
+                contrib[x] = contrib.get(x, 0.0) + c
+                v &= v - 1
+        widest = [t & ~mask for t, wt in zip(sets, widths) if wt >= w - 1e-9]
+        hits: Dict[int, int] = {}
+        for t in widest:
+            v = t
+            while v:
+                x = (v & -v).bit_length() - 1
+                if lw[x] > 0:
+                    hits[x] = hits.get(x, 0) + 1
+                v &= v - 1
+        if not hits:
+            break
+        x = max(hits, key=lambda y: (hits[y], contrib.get(y, 0.0), -y))
+        out.append(x)
+        added += 1
+    return out
