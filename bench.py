@@ -1,13 +1,20 @@
 """Benchmark: contraction TFLOP/s (complex64 on FP32 arithmetic), % of the
 MI355X FP32 MFMA peak and wall time per result, on one GPU.
 
-    python bench.py [--steps K] [--warmup W] [--workload sweep|peps|brickwork12|brickwork30]
+    python bench.py [--steps K] [--warmup W] [--workload grid7x8d16|sweep|peps|...]
 
-Default workload: the isolated pairwise-contraction sweep (m, n, k each in
-{2^6, 2^10, 2^14, 2^18}, k <= 2^14, all modes of extent 2, i.i.d. CN(0,1)
-entries, GEMM-aligned declarations; the three m = n = 2^18 cases do not fit
-one GPU and are left out).  One step runs every feasible case once through
-tnc_execute.  Inputs are resident in HBM before timing.  Prints one JSON line.
+Default workload: one amplitude <0...0|U|0...0> of the 56-qubit 7x8 grid
+circuit of depth 16 (fSim couplers, seed 505) along its stored searched tree.
+Its intermediates need slicing to fit one GPU (2^18 slices of at most
+2^33-entry intermediates); one timed step runs a fixed range of complete
+slices through tnc_execute, `value` counts the unsliced tree's flops for
+that share of the slices, and the time to the whole amplitude is projected
+from them (marked as a projection).  The same run checks the monomial
+circuit of the same shape (tracked slice = e^(i alpha), two other slices
+exactly zero).  Other workloads: the isolated pairwise-contraction sweep
+(`sweep`), the 8x8 PEPS (`peps`), brickwork circuits, smaller grids, the
+honeycomb lattice.  Inputs are resident in HBM before timing.  Prints one
+JSON line.
 """
 
 from __future__ import annotations
@@ -659,6 +666,8 @@ def tree_kernel_roofline(plan, ops, runs=1):
         line = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM, 4)}
     line.update({"kernel": name, "launches": d["launches"], "avg_launch_ms": round(d["ms"] / max(1, d["launches"]), 4),
+                 "alg_bytes_per_launch": round(d["bytes"] / max(1, d["launches"])),
+                 "alg_flop_per_launch": round(d["flop"] / max(1, d["launches"])),
                  "kernel_share_of_time": round(d["ms"] / sum(v["ms"] for v in per.values()), 4)})
     kernels = {k: {"ms": round(v["ms"], 3), "launches": v["launches"],
                    **({"tflops": round(v["flop"] / (v["ms"] / 1e3) / 1e12, 2),
@@ -844,12 +853,17 @@ def kernel_source_digest():
 
 
 def _short_kernel(name):
+    """A profiler's kernel name in the form the library's timed executor
+    reports: GEMM tiles by their first two template arguments, other
+    templates with all arguments, spaces removed."""
     import re
     m = re.search(r"(k_cgemm\w*)<(\d+), (\d+)", name)
     if m:
         return f"{m.group(1)}<{m.group(2)},{m.group(3)}>"
-    m = re.search(r"::(k_\w+)\(", name)
-    return m.group(1) if m else name.split("(")[0]
+    m = re.search(r"(k_\w+)(<[^()]*>)?\(", name)
+    if m:
+        return m.group(1) + (m.group(2) or "").replace(" ", "")
+    return name.split("(")[0]
 
 
 def ingest_pmc(fetch_csv, write_csv, workload, kernel, commands):
@@ -912,7 +926,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="sweep",
+    ap.add_argument("--workload", default="grid7x8d16",
                     choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal",
                              "brickwork30sv", "grid7x8", "grid7x8d16"])
     ap.add_argument("--timed-slices", type=int, default=2,
@@ -939,12 +953,13 @@ def main():
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--ablation", action="store_true",
                     help="also time naive mode order (permute, GEMM, permute) against lifetime order")
+    ap.add_argument("--kernel", default="", help="--ingest-pmc: the kernel to summarise")
     args = ap.parse_args()
     if args.ingest_pmc:
-        kernel = "k_cgemm_tile<128,128>" if args.workload == "sweep" else args.workload
+        kernel = args.kernel or ("k_cgemm_tile<128,128>" if args.workload == "sweep" else args.workload)
         cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.split('_')[0].lower()} -o {c.split('_')[0].lower()} -f csv "
-                f"-- python3 -u bench.py --calibrate-copy --steps 1 --warmup 0 --no-cpu-baseline"
-                for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                f"-- python3 -u bench.py --workload {args.workload} --calibrate-copy --steps 1 --warmup 0 "
+                f"--no-cpu-baseline" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         print(ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, kernel, cmds))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
