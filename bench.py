@@ -123,7 +123,7 @@ class SweepWorkload:
             if events is not None:
                 events[idx][1].record()
 
-    def ablation(self, steps, max_operand=1 << 30):
+    def ablation(self, steps, max_operand=1 << 32):
         """Permuted declarations: lifetime order (stage the operands, write C
         through runs) against naive order (permute A and B, GEMM, permute C),
         next to the aligned case, for every case whose operands fit."""
@@ -139,6 +139,7 @@ class SweepWorkload:
             res = {}
             for name, plan in (("aligned", plan_al), ("lifetime", qa.Plan.from_network(net, tree, order=0)),
                                ("naive", qa.Plan.from_network(net, tree, order=1))):
+                torch.cuda.empty_cache()
                 ws = torch.empty(max(256, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
                 args = ([self.A[: m * k], self.B[: n * k]], self.C[: m * n], ws)
                 plan.execute(*args)
@@ -368,11 +369,14 @@ class TreeWorkload:
         size = int(np.prod(self.plan.out_shape, dtype=np.int64)) if self.plan.out_shape else 1
         self.out = torch.empty(size, dtype=torch.complex64, device="cuda")
         self.ws = qa.alloc_workspace(self.plan)
+        self._run = None
 
     def step(self, events=None):
+        if self._run is None:
+            self._run = self.plan.bind(self.leaves, self.out, self.ws)
         if events is not None:
             events[0][0].record()
-        self.plan.execute(self.leaves, self.out, self.ws)
+        self._run()
         if events is not None:
             events[0][1].record()
 
@@ -395,11 +399,12 @@ class TreeWorkload:
                 log(f"ablation {name}: {res[name + '_note']}")
                 continue
             ws = qa.alloc_workspace(plan)
-            plan.execute(self.leaves, self.out, ws)
+            run = plan.bind(self.leaves, self.out, ws)
+            run()
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
             for e0, e1 in ev:
                 e0.record()
-                plan.execute(self.leaves, self.out, ws)
+                run()
                 e1.record()
             torch.cuda.synchronize()
             st = plan.stats()
@@ -428,7 +433,7 @@ class TreeWorkload:
             if s == self.base_s:
                 ws = self.ws
             else:
-                self.ws = None  # the unsliced workspace can be the largest buffer on the GPU
+                self.ws = self._run = None  # the unsliced workspace can be the largest buffer on the GPU
                 torch.cuda.empty_cache()
                 ws = qa.alloc_workspace(plan)
             log(f"slicing s={s}: running {plan.stats()['num_slices']} slices")
@@ -516,7 +521,7 @@ class TreeWorkload:
         import torch
         from collections import Counter
         steps, model_total = self.plan.distribute(num_gpus=P, threshold_bytes=threshold)
-        self.ws = None
+        self.ws = self._run = None
         torch.cuda.empty_cache()
         split = [s for s, st in enumerate(steps) if st["tag_name"] != "replicated"]
         biggest = 1
@@ -714,11 +719,12 @@ class SlicedGridWorkload:
         self.leaves = [torch.from_numpy(d).to("cuda") for d in self.net.data]
         self.out = torch.empty(1, dtype=torch.complex64, device="cuda")
         self.ws = qa.alloc_workspace(self.plan)
+        self._run = self.plan.bind(self.leaves, self.out, self.ws)
 
     def step(self, events=None):
         if events is not None:
             events[0][0].record()
-        self.plan.execute(self.leaves, self.out, self.ws)
+        self._run()
         if events is not None:
             events[0][1].record()
 

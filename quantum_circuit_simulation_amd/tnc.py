@@ -231,6 +231,8 @@ class Plan:
         ext_list = [int(e) for e in extents]
         self.out_shape = tuple(ext_list[int(x)] for x in out_modes)
         self.leaf_shapes = [tuple(ext_list[int(x)] for x in l) for l in leaves]
+        self._leaf_numel = [int(np.prod(sh, dtype=np.int64)) for sh in self.leaf_shapes]
+        self._out_numel = int(np.prod(self.out_shape, dtype=np.int64))
 
     @classmethod
     def from_network(cls, net, tree, **kw) -> "Plan":
@@ -310,11 +312,10 @@ class Plan:
         if len(leaves) != self.num_leaves:
             raise ValueError(f"wrong number of leaves: {len(leaves)} given, plan has {self.num_leaves}")
         want = torch.complex128 if self.dtype == TNC_C128 else torch.complex64
-        for i, (t, shape) in enumerate(zip(leaves, self.leaf_shapes)):
-            need = int(np.prod(shape, dtype=np.int64))
+        for i, (t, need) in enumerate(zip(leaves, self._leaf_numel)):
             if t.numel() != need:
                 raise ValueError(f"leaf {i} holds {t.numel()} entries, its modes need {need}")
-        need = int(np.prod(self.out_shape, dtype=np.int64))
+        need = self._out_numel
         if out.numel() != need:
             raise ValueError(f"out holds {out.numel()} entries, the output modes need {need}")
         if workspace is not None and workspace.numel() * workspace.element_size() < self.workspace_bytes:
@@ -343,6 +344,29 @@ class Plan:
             stream = torch.cuda.current_stream()
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         self.execute_noalloc_ptrs([t.data_ptr() for t in leaves], out.data_ptr(), s)
+
+    def bind(self, leaves, out, workspace, stream=None):
+        """Check the buffers once and return a callable that enqueues
+        tnc_execute on them with no further Python-side work (for loops that
+        run one plan many times on the same buffers; the buffers must stay
+        alive and unchanged in size while the callable is used)."""
+        import torch
+        self.check_buffers(leaves, out, workspace)
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        s = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        arr = (ctypes.c_void_p * max(1, len(leaves)))(*[int(t.data_ptr()) for t in leaves])
+        args = (self._h, arr, ctypes.c_void_p(int(out.data_ptr())), ctypes.c_void_p(int(workspace.data_ptr())),
+                ctypes.c_uint64(workspace.numel() * workspace.element_size()), s)
+        keep = (list(leaves), out, workspace, self)
+        fn = self._lib.tnc_execute
+
+        def run():
+            code = fn(*args)
+            if code != TNC_OK:
+                _check(code, "tnc_execute")
+        run.keep = keep
+        return run
 
     def execute_timed(self, leaves, out, workspace, stream=None):
         """tnc_execute_timed: run once with HIP events around every launch

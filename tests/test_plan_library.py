@@ -231,3 +231,14 @@ def test_slice_range_is_checked_at_plan_time():
         with pytest.raises(tnc.TncError) as e:
             qa.Plan.from_network(net, tree, sliced=sl, slice_range=bad)
         assert e.value.name == "TNC_ERR_INVALID_ARG", bad
+
+
+def test_bind_checks_buffers_once():
+    import torch
+    net = circuits.brickwork(6, 4, 3).to_network(open_qubits=[0, 1])
+    plan = qa.Plan.from_network(net, trees.greedy_tree(net))
+    good = [torch.from_numpy(d.copy()) for d in net.data]
+    with pytest.raises(ValueError, match="one GPU"):
+        plan.bind(good, torch.empty(4, dtype=torch.complex64), torch.empty(plan.workspace_bytes, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="out holds"):
+        plan.bind(good, torch.empty(5, dtype=torch.complex64), torch.empty(plan.workspace_bytes, dtype=torch.uint8))

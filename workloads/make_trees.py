@@ -31,7 +31,8 @@ SPECS = {
     # trials ranked by roofline time at the MI355X ridge (19.7 multiply-adds
     # per complex64 entry moved)
     "grid_7x8_d16": (7, 8, 16, 505, dict(trials=768, seed=1, max_log_width=34.0, max_log_peak=34.6,
-                                         reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66)),
+                                         reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66,
+                                         refine_ridge=19.66)),
     "grid_7x8_d11": (7, 8, 11, 505, dict(trials=256, seed=1, max_log_width=34.0, max_log_peak=34.6,
                                          reconf_k=10, imbalance=(0.0, 0.3), score_ridge=19.66)),
     "grid_6x6_d14": (6, 6, 14, 505, dict(trials=256, seed=1, max_log_width=34.0, max_log_peak=34.6,
@@ -56,7 +57,17 @@ def make(name: str, threads: int = 8) -> dict:
     rows, cols, depth, seed, params = SPECS[name]
     net = circuits.grid_fsim(rows, cols, depth, seed).to_network()
     t0 = time.time()
+    params = dict(params)
+    refine_ridge = params.pop("refine_ridge", 0.0)
     tree, sliced, st = trees.optimize_tree(net, threads=threads, **params)
+    if refine_ridge:
+        # a last reconfiguration under roofline step costs: trade operations
+        # for fewer bytes on the memory-bound steps
+        tree, sliced, st = trees.refine_tree(net, tree, sliced, reconf_k=params.get("reconf_k", 10),
+                                             reconf_rounds=8, ridge=refine_ridge,
+                                             max_log_width=params.get("max_log_width", 1e9),
+                                             max_log_peak=params.get("max_log_peak", 1e9))
+        params["refine_ridge"] = refine_ridge
     el = time.time() - t0
     c = trees.tree_cost(net, tree, sliced)
     rec = {"name": name, "network": {"family": "grid_fsim", "rows": rows, "cols": cols, "depth": depth,
