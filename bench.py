@@ -243,6 +243,11 @@ class SkinnyWorkload:
         self.bytes = sum(8.0 * (m * k + n * k + m * n) for _, _, m, n, k in self.plans)
         self.config = {"workload": "skinny-steps", "cases_log2_mnk": [list(c) for c in self.CASES],
                        "bytes_per_step": self.bytes, "flop_per_step": self.flops}
+        # the kernel each case runs, as the library reports it
+        self.names = []
+        for c, plan, m, n, k in self.plans:
+            ops = plan.execute_timed([self.A[: m * k], self.B[: n * k]], self.C[: m * n], self.ws)
+            self.names.append(next(o["kernel"] for o in ops if o["kind"] in ("skinny", "gemm", "tiny_group")))
 
     def step(self, events=None):
         for idx, (c, plan, m, n, k) in enumerate(self.plans):
@@ -253,13 +258,7 @@ class SkinnyWorkload:
                 events[idx][1].record()
 
     def kernel_of(self, idx):
-        c, plan, m, n, k = self.plans[idx]
-        splits = plan.node(0)["splits"]
-        if max(m, n) < 4096:
-            return "k_skinny"
-        if splits == 1 and 2 <= k <= 256 and (k & (k - 1)) == 0 and min(m, n) <= 16:
-            return "k_skinny_flat"
-        return "k_skinny_small" if 8 <= k <= 16 and splits == 1 else "k_skinny_rows"
+        return self.names[idx]
 
     def launch_flops(self, idx):
         _, _, m, n, k = self.plans[idx]
@@ -934,7 +933,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="grid7x8d16",
                     choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal",
-                             "brickwork30sv", "grid7x8", "grid7x8d16"])
+                             "brickwork30sv", "grid7x8", "grid7x8d16", "peaks"])
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--timed-slices", type=int, default=2,
                     help="grid7x8d16: complete slices run per timed step")
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
@@ -974,6 +974,17 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
+    if args.workload == "peaks":
+        import quantum_circuit_simulation_amd as qa
+        buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+        f, c = qa.tnc.probe_peaks(buf)
+        print(json.dumps({"metric": "measured device peaks (FP32 MFMA TFLOP/s, HBM copy GB/s)", "value": round(f, 2),
+                          "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+                          "fp32_mfma_tflops": round(f, 2), "hbm_copy_gbps": round(c, 1),
+                          "nominal": {"fp32_mfma_tflops": PEAK_FP32_MFMA, "hbm_gbps": PEAK_HBM},
+                          "frac_of_nominal": {"mfma": round(f / PEAK_FP32_MFMA, 4), "hbm": round(c / PEAK_HBM, 4)},
+                          "config": {"workload": "peak-probes", "copy_bytes": 8 << 30}}), flush=True)
+        return
 
     if args.calibrate_copy:
         calibrate_copy()
@@ -1104,6 +1115,22 @@ def main():
     if args.distribute:
         distribution = wl.distribution(args.distribute, args.dist_threshold, ms_per_step)
 
+    peaks = None
+    if not args.no_peaks:
+        # measured denominators: a no-memory MFMA loop and a 16-byte copy
+        # (tnc_probe_peaks), on part of the workspace or a fresh 8 GiB buffer
+        import quantum_circuit_simulation_amd as qa
+        ws = getattr(wl, "ws", None)
+        buf = ws[: 8 << 30] if ws is not None and ws.numel() >= (1 << 30) else \
+            torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+        f, c = qa.tnc.probe_peaks(buf)
+        del buf
+        peaks = {"fp32_mfma_tflops": round(f, 2), "hbm_copy_gbps": round(c, 1)}
+        meas = f if roofline["unit"] == "TFLOP/s" else c
+        if roofline.get("peak") in (PEAK_FP32_MFMA, PEAK_HBM):
+            roofline["frac_of_measured_peak"] = round(roofline["achieved"] / meas, 4)
+        log(f"measured peaks: {f:.1f} TFLOP/s FP32 MFMA, {c:.0f} GB/s copy")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -1118,6 +1145,8 @@ def main():
             "plan_ms_host": getattr(wl, "plan_ms_host", None),
             "config": wl.config, "roofline": roofline, "cpu_baseline": cpu,
             **({"tree_roofline": tree_roof} if tree_roof is not None else {}),
+            **({"measured_peaks": peaks, "pct_measured_fp32_mfma_peak": round(100.0 * value / peaks["fp32_mfma_tflops"], 2)}
+               if peaks is not None and not z and not prec else {}),
             **({"ablation": ablation} if ablation is not None else {}),
             **({"slicing": slicing} if slicing is not None else {}),
             **({"distribution": distribution} if distribution is not None else {}),

@@ -463,6 +463,64 @@ tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *o
   return TNC_OK;
 }
 
+tnc_status tnc_probe_peaks(void *buffer, uint64_t bytes, void *stream_ptr, double *mfma_tflops,
+                           double *copy_gbps) {
+  g_last_error.clear();
+  const int32_t cus = tnc::device_cus();
+  const uint64_t need_mfma = (uint64_t)4 * cus * 256 * sizeof(float);
+  if (!buffer || !mfma_tflops || !copy_gbps || bytes < (uint64_t(64) << 20) || bytes < need_mfma ||
+      (reinterpret_cast<uintptr_t>(buffer) & 255) != 0)
+    return TNC_ERR_INVALID_ARG;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  (void)hipGetLastError();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  const int32_t iters = 20000;
+  double best_mfma = 0, best_copy = 0;
+  const int64_t half16 = (int64_t)(bytes / 2 / 16);
+  char *buf = static_cast<char *>(buffer);
+  auto timed = [&](auto launch, float *ms) {
+    if (e == hipSuccess) e = hipEventRecord(e0, stream);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = hipEventRecord(e1, stream);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+  };
+  // launch shapes: 4 or 8 chains per wave at 2 or 4 waves per SIMD; copies
+  // with 1 or 4 loads in flight per thread.  Best of three runs after one
+  // untimed run, best over the shapes.
+  for (int32_t waves : {2, 4})
+    for (int32_t chains : {4, 8}) {
+      const int64_t blocks = (int64_t)waves * cus;
+      for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {
+        float ms = 0.f;
+        timed([&] { return tnc::launch_probe_mfma(static_cast<float *>(buffer), blocks, iters, chains, stream); },
+              &ms);
+        // flops: blocks x 4 waves x iters x chains x (32 x 32 x 2 x 2)
+        const double tf = (double)blocks * 4 * iters * chains * 4096.0 / (ms * 1e-3) / 1e12;
+        if (e == hipSuccess && rep > 0 && tf > best_mfma) best_mfma = tf;
+      }
+    }
+  for (int32_t inflight : {1, 4})
+    for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {
+      float ms = 0.f;
+      timed([&] { return tnc::launch_probe_copy(buf, buf + half16 * 16, half16, inflight, stream); }, &ms);
+      const double gbps = 2.0 * (double)half16 * 16 / (ms * 1e-3) / 1e9;
+      if (e == hipSuccess && rep > 0 && gbps > best_copy) best_copy = gbps;
+    }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) {
+    g_last_error = std::string("peak probe: ") + hipGetErrorString(e);
+    (void)hipGetLastError();
+    return TNC_ERR_HIP;
+  }
+  *mfma_tflops = best_mfma;
+  *copy_gbps = best_copy;
+  return TNC_OK;
+}
+
 tnc_status tnc_execute_noalloc(tnc_plan_t plan, const void *const *leaves, void *out, void *stream_ptr) {
   g_last_error.clear();
   if (!plan || !leaves || !out) return TNC_ERR_INVALID_ARG;

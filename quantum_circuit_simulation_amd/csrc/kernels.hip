@@ -1049,6 +1049,47 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// measurement probes (not part of a contraction): the device's sustained
+// FP32 matrix-core rate and HBM copy rate, the denominators a roofline is
+// checked against.
+
+// NCH independent chains of v_mfma_f32_32x32x2_f32 per wave, no memory
+// traffic in the loop; each thread writes one sum so the chains stay live.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_probe_mfma(float *out, int32_t iters) {
+  f32x16 acc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  const float x = 1e-3f * (float)(threadIdx.x & 7), y = 1.0f - 1e-3f * (float)(threadIdx.x & 3);
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(c & 1 ? y : x, c & 2 ? x : y, acc[c], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Grid-stride 16-byte copy of n entries, U loads in flight per thread.
+template <int U>
+__global__ __launch_bounds__(256) void k_probe_copy(const float4 *src, float4 *dst, int64_t n) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (U - 1) * step < n; i += U * step) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * step];
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[i + u * step] = v[u];
+  }
+  for (; i < n; i += step) dst[i] = src[i];
+}
+
 // sum split-K partials [splits, R, S] into C through the runs
 template <typename T>
 __global__ void k_split_reduce(StepArgsT<T> a) {
@@ -2445,5 +2486,24 @@ hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream) {
   if (e != hipSuccess || a.splits <= 1) return e;
   return run_split_reduce(a, stream);
 }
+
+hipError_t launch_probe_mfma(float *out, int64_t blocks, int32_t iters, int32_t chains, hipStream_t stream) {
+  if (chains >= 8) hipLaunchKernelGGL(k_probe_mfma<8>, dim3((unsigned)blocks), dim3(256), 0, stream, out, iters);
+  else hipLaunchKernelGGL(k_probe_mfma<4>, dim3((unsigned)blocks), dim3(256), 0, stream, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t inflight, hipStream_t stream) {
+  const int64_t blocks = 8 * (int64_t)num_cus();
+  if (inflight >= 4)
+    hipLaunchKernelGGL(k_probe_copy<4>, dim3((unsigned)blocks), dim3(256), 0, stream, (const float4 *)src,
+                       (float4 *)dst, n16);
+  else
+    hipLaunchKernelGGL(k_probe_copy<1>, dim3((unsigned)blocks), dim3(256), 0, stream, (const float4 *)src,
+                       (float4 *)dst, n16);
+  return hipGetLastError();
+}
+
+int32_t device_cus() { return (int32_t)num_cus(); }
 
 }  // namespace tnc

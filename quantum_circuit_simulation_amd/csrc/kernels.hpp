@@ -57,6 +57,14 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream);
 hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream);
 hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream);
 
+// Peak probes: `blocks` workgroups of 256 threads running `chains` (4 or 8)
+// MFMA chains of `iters` steps each (writes blocks * 256 floats to out); a
+// copy of n16 16-byte entries with `inflight` (1 or 4) loads per thread in
+// flight.  device_cus(): compute units of the current device.
+hipError_t launch_probe_mfma(float *out, int64_t blocks, int32_t iters, int32_t chains, hipStream_t stream);
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t inflight, hipStream_t stream);
+int32_t device_cus();
+
 // Name of the kernel the last launcher call on this thread enqueued (a split
 // K step appends "+k_split_reduce"); "" after clear_kernel_name().
 const char *last_kernel_name();

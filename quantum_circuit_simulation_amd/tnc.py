@@ -115,7 +115,7 @@ OP_KINDS = ["copy", "tiny_group", "skinny", "gemm", "copy_tiled", "header"]
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
            "tnc_execute", "tnc_status_string", "tnc_last_error", "tnc_dist_options_default",
-           "tnc_plan_distribute", "tnc_execute_noalloc", "tnc_execute_timed"]
+           "tnc_plan_distribute", "tnc_execute_noalloc", "tnc_execute_timed", "tnc_probe_peaks"]
 NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # TNC_NOALLOC_MAX_WORKSPACE_BYTES
 
 _lib = None
@@ -160,6 +160,9 @@ def load_library(path: str = LIB_PATH):
                                       ctypes.c_uint64, ctypes.c_void_p, P(OpTiming), ctypes.c_int32,
                                       P(ctypes.c_int32)]
     lib.tnc_execute_timed.restype = ctypes.c_int
+    lib.tnc_probe_peaks.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, P(ctypes.c_double),
+                                    P(ctypes.c_double)]
+    lib.tnc_probe_peaks.restype = ctypes.c_int
     lib.tnc_status_string.argtypes = [ctypes.c_int]
     lib.tnc_status_string.restype = ctypes.c_char_p
     lib.tnc_last_error.argtypes = []
@@ -403,6 +406,20 @@ class Plan:
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
         self.execute_ptrs([t.data_ptr() for t in leaves], out.data_ptr(), workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), s)
+
+
+def probe_peaks(buffer, stream=None):
+    """tnc_probe_peaks on a uint8 device tensor (>= 64 MiB, overwritten):
+    returns (sustained FP32 MFMA TFLOP/s, HBM copy GB/s) of the device."""
+    import torch
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    f, c = ctypes.c_double(), ctypes.c_double()
+    _check(lib.tnc_probe_peaks(ctypes.c_void_p(buffer.data_ptr()), buffer.numel() * buffer.element_size(),
+                               ctypes.c_void_p(s), ctypes.byref(f), ctypes.byref(c)), "tnc_probe_peaks")
+    return float(f.value), float(c.value)
 
 
 def alloc_workspace(plan: Plan, device="cuda"):

@@ -78,3 +78,17 @@ def test_timed_execute_matches_execute_and_names_every_launch():
     assert ops[0]["launches"] == 1
     for o in ops[1:]:
         assert o["launches"] == 4 and o["kernel"].startswith("k_"), o
+
+
+def test_peak_probes_are_near_the_published_peaks():
+    """tnc_probe_peaks: the no-memory FP32 MFMA loop must sustain most of
+    the published 157.3 TFLOP/s, and the copy a sizeable share of 8 TB/s
+    (both well below any impossible value)."""
+    import torch
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    f, c = qa.tnc.probe_peaks(buf)
+    print(f"[gpu] peaks: {f:.1f} TFLOP/s, {c:.0f} GB/s", flush=True)
+    assert 100.0 < f < 170.0, f
+    assert 2000.0 < c < 8500.0, c
+    with pytest.raises(qa.tnc.TncError):
+        qa.tnc.probe_peaks(buf[: 1 << 20])
