@@ -873,34 +873,44 @@ __global__ __launch_bounds__(256) void k_skinny_flat(StepArgs a) {
   }
 }
 
-// Skinny steps with many rows, S <= 16 outputs per row (a power of two),
-// K in {2, 4, ..., 32}, on the FP32 matrix cores, written in address order.
+// Skinny steps with many rows, S <= 32 outputs per row (a power of two),
+// K a power of two (up to 64 for S <= 16, 32 for S = 32), on the FP32
+// matrix cores, written in address order.  Also takes GEMM-class steps whose
+// short side is at most 32, with the operands (and C's row and column runs)
+// exchanged when the long side is the column side.
 //
-// Each wave owns blocks of 32 rows: it loads the block's X rows (one
-// contiguous stretch of 32 K entries) with coalesced 16-byte loads into a
-// wave-private LDS area, runs K v_mfma_f32_32x32x2_f32 over it and writes
-// the 32 x S results back into the same area (LDS operations of one wave
-// complete in order, so no barrier is needed).  The 32 MFMA columns carry
+// Each wave owns passes of NB blocks of 32 rows: it loads the pass's X rows
+// (one contiguous stretch of 32 NB K entries) with coalesced 16-byte loads
+// into a wave-private LDS area, runs the MFMAs over it and writes the
+// results back into the same area (LDS operations of one wave complete in
+// order, so no barrier is needed).  With SW = 16 the 32 MFMA columns carry
 // the real parts of the S outputs (columns 0-15) and their imaginary parts
 // (16-31): with the (re, im) K-slot scheme of k_cgemm, column j < 16 takes
 // (yr, -yi) of output j and column 16 + j takes (yi, yr), so one MFMA per
-// complex entry of K yields both parts.  The next block's loads are issued
-// before this block's MFMAs and stores.
+// complex entry of K yields both parts.  With SW = 32 the real and the
+// imaginary parts take one MFMA each, as in k_cgemm.  The next pass's loads
+// are issued before this pass's MFMAs and stores.
 //
 // Stores: when every run of C has a power-of-two size, the offset of row
-// r0 + t (r0 a multiple of 32) is rowoff(r0) + rowoff(t), so the block's
-// 32 S outputs sit at rowoff(r0) + rowoff(t) + coloff(j), and the offset is
-// a sum of one stride per set bit of (t, j).  Ordering those 5 + log2 S bits
-// by stride gives a fixed permutation of the block's entries into ascending
-// addresses; the wave stores the block in that order, so lanes write
+// r0 + t (r0 a multiple of the pass) is rowoff(r0) + rowoff(t), so the
+// pass's outputs sit at rowoff(r0) + rowoff(t) + coloff(j), and the offset
+// is a sum of one stride per set bit of (t, j).  Ordering those bits by
+// stride gives a fixed permutation of the pass's entries into ascending
+// addresses; the wave stores the pass in that order, so lanes write
 // consecutive addresses wherever C is contiguous (16-byte pairs when the
 // smallest stride is one entry), whatever the interleaving of C's modes.
 constexpr int kSmRows = 32;
 
-// NB 32-row sub-blocks per wave iteration (NB * S <= 32): small K and S move
-// few bytes per block, so a wave takes several blocks per pass.
-template <int K, int NB>
-__global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
+struct SkinnyRuns {
+  const RunDev *rows;  // C's runs over the row (long) side, outermost first
+  const RunDev *cols;  // over the column (short) side
+  int32_t nr, nc;
+};
+
+// NB 32-row sub-blocks per wave pass (NB * S <= 32 for SW = 16): small K and
+// S move few bytes per block, so a wave takes several blocks per pass.
+template <int K, int NB, int SW>
+__global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) {
   constexpr int KH = K / 2;                  // 16-byte entry pairs per X row
   constexpr int RSX = KH + 1;                // LDS row stride (16-byte units), one pad
   constexpr int ROWS = kSmRows * NB;         // rows per wave pass
@@ -909,30 +919,31 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
   constexpr int WB = XW > CW ? XW : CW;
   constexpr int LPT = (ROWS * KH + 63) / 64;  // 16-byte loads per lane per pass
   constexpr int LB = 5 + (NB >= 8 ? 3 : NB >= 4 ? 2 : NB >= 2 ? 1 : 0);  // row bits of a pass
+  constexpr int JB = SW == 32 ? 5 : 4;       // column bits of a permutation entry
   __shared__ float4 buf[4][WB];
-  __shared__ int64_t rowoff[ROWS], coloff[16];
+  __shared__ int64_t rowoff[ROWS], coloff[32];
   __shared__ uint16_t perm[kSmRows * 32];
-  __shared__ int32_t bit_of[12];
+  __shared__ int32_t bit_of[13];
   __shared__ int32_t nbits_s, pairs_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int S = (int)a.S;
   const int sb = 31 - __clz(S);  // S is a power of two
-  for (int t = tid; t < ROWS + 16; t += 256) {
-    if (t < ROWS) rowoff[t] = run_offset(t, a.runs, a.nrr);
-    else coloff[t - ROWS] = t - ROWS < S ? run_offset(t - ROWS, a.runs + a.nrr, a.ncr) : 0;
+  for (int t = tid; t < ROWS + 32; t += 256) {
+    if (t < ROWS) rowoff[t] = run_offset(t, rn.rows, rn.nr);
+    else coloff[t - ROWS] = t - ROWS < S ? run_offset(t - ROWS, rn.cols, rn.nc) : 0;
   }
   __syncthreads();
   if (tid == 0) {
-    // permutation bits: bits 0 .. sb-1 of an entry index are its column, bits 4 .. 4+LB-1 its row
-    int64_t st[12];
-    int pb[12], nb = 0;
+    // permutation bits: bits 0 .. sb-1 of an entry index are its column, bits JB .. JB+LB-1 its row
+    int64_t st[13];
+    int pb[13], nb = 0;
     for (int b = 0; b < sb; ++b) {
       st[nb] = coloff[1 << b];
       pb[nb++] = b;
     }
     for (int b = 0; b < LB; ++b) {
       st[nb] = rowoff[1 << b];
-      pb[nb++] = 4 + b;
+      pb[nb++] = JB + b;
     }
     for (int i = 1; i < nb; ++i)
       for (int q = i; q > 0 && st[q] < st[q - 1]; --q) {
@@ -955,15 +966,24 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
       if ((e >> i) & 1) p |= 1 << bit_of[i];
     perm[e] = (uint16_t)p;
   }
-  // second operand, per lane and K entry: MFMA column l32 = (real | imaginary part of output l32 % 16)
-  float bv[K];
-  {
+  // second operand, per lane and K entry
+  float bv[K], bw[SW == 32 ? K : 1];
+  if constexpr (SW == 16) {
+    // MFMA column l32 = (real | imaginary part of output l32 % 16)
     const int j = l32 & 15;
     const bool imc = l32 >= 16;
 #pragma unroll
     for (int l = 0; l < K; ++l) {
       const float2 y = j < S ? a.Y[(int64_t)j * K + l] : make_float2(0.f, 0.f);
       bv[l] = imc ? (h ? y.x : y.y) : (h ? -y.y : y.x);
+    }
+  } else {
+    // MFMA column l32 = output l32: (yr, -yi) for the real part, (yi, yr) for the imaginary part
+#pragma unroll
+    for (int l = 0; l < K; ++l) {
+      const float2 y = l32 < S ? a.Y[(int64_t)l32 * K + l] : make_float2(0.f, 0.f);
+      bv[l] = h ? -y.y : y.x;
+      bw[l] = h ? y.x : y.y;
     }
   }
   __syncthreads();
@@ -991,23 +1011,29 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
       if (g < ROWS * KH) xb[(g / KH) * RSX + g % KH] = ld[i];
     }
     if (blk + wstride < npass) load(blk + wstride);
-    f32x16 acc[NB];
+    f32x16 acc[NB], acw[SW == 32 ? NB : 1];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        acc[nb][r] = 0.f;
+        if constexpr (SW == 32) acw[nb][r] = 0.f;
+      }
 #pragma unroll
     for (int q = 0; q < KH; ++q)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float4 f = xb[(nb * kSmRows + l32) * RSX + q];
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? f.y : f.x, bv[2 * q], acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? f.w : f.z, bv[2 * q + 1], acc[nb], 0, 0, 0);
+        const float x0 = h ? f.y : f.x, x1 = h ? f.w : f.z;
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, bv[2 * q], acc[nb], 0, 0, 0);
+        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, bw[2 * q], acw[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, bv[2 * q + 1], acc[nb], 0, 0, 0);
+        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, bw[2 * q + 1], acw[nb], 0, 0, 0);
       }
     // results as complex [ROWS][S] in the same LDS area
     float *cf = (float *)xb;
     const float2 *cv = (const float2 *)xb;
-    {
+    if constexpr (SW == 16) {
       const int j = l32 & 15, part = l32 >> 4;
       if (j < S) {
 #pragma unroll
@@ -1016,14 +1042,24 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
           for (int r = 0; r < 16; ++r)
             cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * S + j) * 2 + part] = acc[nb][r];
       }
+    } else {
+      if (l32 < S) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *(float2 *)&cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * S + l32) * 2] =
+                make_float2(acc[nb][r], acw[nb][r]);
+      }
     }
     const int64_t r0 = blk * ROWS;
-    const int64_t base = run_offset(r0, a.runs, a.nrr);
+    const int64_t base = run_offset(r0, rn.rows, rn.nr);
     const int rows = (int)(R - r0 < ROWS ? R - r0 : ROWS);
+    constexpr int JM = (1 << JB) - 1;
     if (pairs) {
       for (int e = 2 * lane; e < nent; e += 128) {
         const int p0 = perm[e], p1 = perm[e + 1];
-        const int t0 = p0 >> 4, j0 = p0 & 15, t1 = p1 >> 4, j1 = p1 & 15;
+        const int t0 = p0 >> JB, j0 = p0 & JM, t1 = p1 >> JB, j1 = p1 & JM;
         const int64_t o0 = base + rowoff[t0] + coloff[j0];
         const float2 v0 = cv[t0 * S + j0], v1 = cv[t1 * S + j1];
         if (t0 < rows && t1 < rows && (o0 & 1) == 0) {
@@ -1042,7 +1078,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a) {
     } else {
       for (int e = lane; e < nent; e += 64) {
         const int p = perm[e];
-        const int t = p >> 4, j = p & 15;
+        const int t = p >> JB, j = p & JM;
         if (t < rows) store_c(a.C + base + rowoff[t] + coloff[j], cv[t * S + j], a.beta);
       }
     }
@@ -2338,45 +2374,75 @@ static bool skinny_flat_ok(const StepArgs &a) {
 
 bool small_gemm_ok(const StepArgs &a) { return a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK; }
 
-static bool skinny_mfma_ok(const StepArgs &a) {
-  const bool pow2s = a.S >= 1 && a.S <= 16 && (a.S & (a.S - 1)) == 0;
-  const bool pow2k = a.K >= 2 && a.K <= 32 && (a.K & (a.K - 1)) == 0;
-  return a.splits == 1 && a.R >= 4096 && pow2s && pow2k && a.pow2_runs && ((uintptr_t)a.X & 15) == 0;
+// a step on k_skinny_mfma: long side (rows after orientation) >= 4096, short
+// side S a power of two <= 32, K a power of two (<= 64; <= 32 when S = 32)
+static bool skinny_mfma_shape_ok(int64_t R, int64_t S, int64_t K) {
+  const bool pow2s = S >= 1 && S <= 32 && (S & (S - 1)) == 0;
+  const bool pow2k = K >= 2 && K <= (S > 16 ? 32 : 64) && (K & (K - 1)) == 0;
+  return R >= 4096 && pow2s && pow2k;
 }
 
-template <int K, int NB>
-static hipError_t run_skinny_mfma_kn(const StepArgs &a, hipStream_t stream) {
+static bool skinny_mfma_ok(const StepArgs &a) {
+  return a.splits == 1 && a.pow2_runs && skinny_mfma_shape_ok(a.R, a.S, a.K) && ((uintptr_t)a.X & 15) == 0;
+}
+
+template <int K, int NB, int SW>
+static hipError_t run_skinny_mfma_kn(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
   const int64_t npass = (a.R + kSmRows * NB - 1) / (kSmRows * NB);
   int64_t blocks = (npass + 3) / 4;
   const int64_t cap = 8 * (int64_t)num_cus();
   if (blocks > cap) blocks = cap;
-  note_kernel("k_skinny_mfma<%d,%d>", K, NB);
-  hipLaunchKernelGGL((k_skinny_mfma<K, NB>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  note_kernel("k_skinny_mfma<%d,%d,%d>", K, NB, SW);
+  hipLaunchKernelGGL((k_skinny_mfma<K, NB, SW>), dim3((unsigned)blocks), dim3(256), 0, stream, a, rn);
   return hipGetLastError();
 }
 
 // sub-blocks per wave pass: about 8 KB of operand and result rows per pass
 // (32 NB rows of K + S entries), with NB S <= 32
 template <int K>
-static hipError_t run_skinny_mfma_k(const StepArgs &a, hipStream_t stream) {
+static hipError_t run_skinny_mfma_k(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
+  if constexpr (K <= 32)
+    if (a.S > 16) return run_skinny_mfma_kn<K, 1, 32>(a, rn, stream);
   const int64_t fit = 32 / (K + a.S);
   if constexpr (K <= 2)
-    if (fit >= 8 && a.S <= 4) return run_skinny_mfma_kn<K, 8>(a, stream);
+    if (fit >= 8 && a.S <= 4) return run_skinny_mfma_kn<K, 8, 16>(a, rn, stream);
   if constexpr (K <= 4)
-    if (fit >= 4 && a.S <= 8) return run_skinny_mfma_kn<K, 4>(a, stream);
+    if (fit >= 4 && a.S <= 8) return run_skinny_mfma_kn<K, 4, 16>(a, rn, stream);
   if constexpr (K <= 8)
-    if (fit >= 2) return run_skinny_mfma_kn<K, 2>(a, stream);
-  return run_skinny_mfma_kn<K, 1>(a, stream);
+    if (fit >= 2) return run_skinny_mfma_kn<K, 2, 16>(a, rn, stream);
+  return run_skinny_mfma_kn<K, 1, 16>(a, rn, stream);
 }
 
-static hipError_t run_skinny_mfma(const StepArgs &a, hipStream_t stream) {
+static hipError_t run_skinny_mfma(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
   switch (a.K) {
-    case 2: return run_skinny_mfma_k<2>(a, stream);
-    case 4: return run_skinny_mfma_k<4>(a, stream);
-    case 8: return run_skinny_mfma_k<8>(a, stream);
-    case 16: return run_skinny_mfma_k<16>(a, stream);
-    default: return run_skinny_mfma_k<32>(a, stream);
+    case 2: return run_skinny_mfma_k<2>(a, rn, stream);
+    case 4: return run_skinny_mfma_k<4>(a, rn, stream);
+    case 8: return run_skinny_mfma_k<8>(a, rn, stream);
+    case 16: return run_skinny_mfma_k<16>(a, rn, stream);
+    case 32: return run_skinny_mfma_k<32>(a, rn, stream);
+    default: return run_skinny_mfma_k<64>(a, rn, stream);
   }
+}
+
+// The step as given (rows = R) or exchanged (rows = S): the long side must
+// be the row side of k_skinny_mfma.
+static bool gemm_as_skinny(const StepArgs &a, hipStream_t stream, hipError_t *err) {
+  if (a.splits != 1 || !a.pow2_runs || a.prec != kPrecExact) return false;
+  const RunDev *rr = a.runs, *cr = a.runs + a.nrr;
+  if (skinny_mfma_shape_ok(a.R, a.S, a.K) && ((uintptr_t)a.X & 15) == 0) {
+    *err = run_skinny_mfma(a, SkinnyRuns{rr, cr, a.nrr, a.ncr}, stream);
+    return true;
+  }
+  if (skinny_mfma_shape_ok(a.S, a.R, a.K) && ((uintptr_t)a.Y & 15) == 0) {
+    StepArgs b = a;
+    b.X = a.Y;
+    b.Y = a.X;
+    b.R = a.S;
+    b.S = a.R;
+    *err = run_skinny_mfma(b, SkinnyRuns{cr, rr, a.ncr, a.nrr}, stream);
+    return true;
+  }
+  return false;
 }
 
 hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
@@ -2392,7 +2458,7 @@ hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
-  if (skinny_mfma_ok(a)) return run_skinny_mfma(a, stream);
+  if (skinny_mfma_ok(a)) return run_skinny_mfma(a, SkinnyRuns{a.runs, a.runs + a.nrr, a.nrr, a.ncr}, stream);
   if (skinny_flat_ok(a)) {
     if (a.S <= 1) return run_skinny_flat_k<1>(a, stream);
     if (a.S <= 2) return run_skinny_flat_k<2>(a, stream);
@@ -2451,6 +2517,11 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
   }
   // small steps: one workgroup per 32 x 32 block, K split over its waves
   if (small_gemm_ok(a)) return run_cgemm_small(a, stream);
+  // a short side of at most 32 with a short K: memory-bound, streamed like a skinny step
+  {
+    hipError_t e = hipSuccess;
+    if (gemm_as_skinny(a, stream, &e)) return e;
+  }
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
   if (a.S > 64 && a.R <= 32) e = run_cgemm<32, 256, 8, 32, 64>(a, stream);

@@ -1,9 +1,11 @@
 """Skinny steps on the matrix-core kernel with address-ordered stores
 (k_skinny_mfma): every output entry against the oracle, for S = 1 ... 16
-outputs per row, K = 2 ... 32, both operand sides, random interleavings of
-the output modes (so the stores walk runs of every length), a sliced run
-(beta accumulation) and shapes that must fall back to the other skinny
-kernels.  |g - r| <= 1e-4 * max(|r|, rms(r))."""
+outputs per row with K = 2 ... 64, GEMM-class steps with a short side of 32
+(K = 2 ... 32, the long side on either operand, so that the kernel also runs
+with operands and runs exchanged), random interleavings of the output modes
+(so the stores walk runs of every length), a sliced run (beta accumulation)
+and shapes that must fall back to the other kernels.
+|g - r| <= 1e-4 * max(|r|, rms(r))."""
 
 import numpy as np
 import pytest
@@ -27,7 +29,7 @@ def _gpu():
     yield
 
 
-def _check(net, tree, expect_kernel=None, **kw):
+def _check(net, tree, expect_kernel=None, kind="skinny", **kw):
     import torch
     plan = qa.Plan.from_network(net, tree, **kw)
     leaves = [torch.from_numpy(np.ascontiguousarray(d)).cuda() for d in net.data]
@@ -39,7 +41,7 @@ def _check(net, tree, expect_kernel=None, **kw):
     got = out.cpu().numpy().astype(np.complex128).reshape(plan.out_shape)
     ref = oracle.contract_network(net, tree)
     ok, err = rel_err_ok(got, ref, TOL)
-    kernels = [o["kernel"] for o in ops if o["kind"] == "skinny"]
+    kernels = [o["kernel"] for o in ops if o["kind"] == kind]
     print(f"[gpu] {net.name} kw={kw} kernels={kernels} err {err:.2e}", flush=True)
     assert ok, err
     if expect_kernel is not None:
@@ -48,7 +50,10 @@ def _check(net, tree, expect_kernel=None, **kw):
 
 
 CASES = [(14, 0, 1), (12, 4, 4), (13, 3, 3), (14, 4, 2), (12, 2, 5), (15, 1, 4), (16, 4, 1), (13, 0, 5),
-         (13, 3, 2), (14, 2, 3), (17, 4, 4), (14, 1, 1)]
+         (13, 3, 2), (14, 2, 3), (17, 4, 4), (14, 1, 1), (13, 4, 6), (12, 2, 6), (14, 0, 6)]
+# GEMM-class steps (short side 32): log2 of (long side, K); below 2^14 rows
+# the small-GEMM kernel takes them
+GEMM_CASES = [(15, 1), (16, 2), (15, 3), (17, 4), (15, 5), (16, 5)]
 
 
 @pytest.mark.parametrize("i", range(len(CASES)))
@@ -58,6 +63,15 @@ def test_skinny_mfma_interleaved_outputs(i, side):
     lm, ln = (logr, logs) if side == 0 else (logs, logr)
     net, tree = sweep.network(lm, ln, logk, permuted=True, seed=40 + 7 * i + side, with_data=True)
     _check(net, tree, expect_kernel="k_skinny_mfma")
+
+
+@pytest.mark.parametrize("i", range(len(GEMM_CASES)))
+@pytest.mark.parametrize("side", [0, 1])
+def test_short_side_32_gemm_steps(i, side):
+    logr, logk = GEMM_CASES[i]
+    lm, ln = (logr, 5) if side == 0 else (5, logr)
+    net, tree = sweep.network(lm, ln, logk, permuted=True, seed=90 + 5 * i + side, with_data=True)
+    _check(net, tree, expect_kernel="k_skinny_mfma", kind="gemm")
 
 
 def test_skinny_mfma_aligned_and_sliced():
@@ -83,6 +97,11 @@ def test_fallbacks_keep_the_other_skinny_kernels():
     net, tree = _with_extent3()
     ks = _check(net, tree)
     assert ks and not ks[0].startswith("k_skinny_mfma"), ks
-    net, tree = sweep.network(13, 3, 6, permuted=True, seed=9, with_data=True)   # K = 64
+    net, tree = sweep.network(13, 3, 7, permuted=True, seed=9, with_data=True)   # K = 128
     ks = _check(net, tree)
     assert ks and not ks[0].startswith("k_skinny_mfma"), ks
+    # short side 32 with K = 64, and short side 64: the tiled GEMM kernel
+    for lm, ln, lk in [(15, 5, 6), (6, 15, 3)]:
+        net, tree = sweep.network(lm, ln, lk, permuted=True, seed=lm + ln + lk, with_data=True)
+        ks = _check(net, tree, kind="gemm")
+        assert ks and ks[0].startswith("k_cgemm"), ks
