@@ -915,12 +915,23 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   constexpr int RSX = KH + 1;                // LDS row stride (16-byte units), one pad
   constexpr int ROWS = kSmRows * NB;         // rows per wave pass
   constexpr int XW = ROWS * RSX;             // X rows of one pass
-  constexpr int CW = kSmRows * 32 / 2;       // ROWS x S complex results (NB S <= 32)
+  // ROWS x S complex results with an odd row stride S + 1, so that a walk
+  // down a column (the store order when a row mode has the smallest
+  // stride) spreads over the LDS banks; NB S <= 32
+  constexpr int SMAX = SW == 32 ? 32 : (32 / NB < 16 ? 32 / NB : 16);
+  constexpr int CW = (ROWS * (SMAX + 1) + 1) / 2;
   constexpr int WB = XW > CW ? XW : CW;
   constexpr int LPT = (ROWS * KH + 63) / 64;  // 16-byte loads per lane per pass
   constexpr int LB = 5 + (NB >= 8 ? 3 : NB >= 4 ? 2 : NB >= 2 ? 1 : 0);  // row bits of a pass
   constexpr int JB = SW == 32 ? 5 : 4;       // column bits of a permutation entry
+  // the second operand from LDS for 32-wide steps with K >= 32 (in
+  // registers that would take 64 or more of them per lane): entry pairs
+  // (y[c][2q], y[c][2q + 1]) at [q][c]; 16-wide steps keep it in registers
+  // (measured faster there, K = 64 included)
+  constexpr bool BL = SW == 32 && K >= 32;
+  constexpr int YC = SW == 32 ? 32 : 16;
   __shared__ float4 buf[4][WB];
+  __shared__ float4 ysh[BL ? (K / 2) * YC : 1];
   __shared__ int64_t rowoff[ROWS], coloff[32];
   __shared__ uint16_t perm[kSmRows * 32];
   __shared__ int32_t bit_of[13];
@@ -928,6 +939,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int S = (int)a.S;
   const int sb = 31 - __clz(S);  // S is a power of two
+  const int SP = S + 1;          // LDS row stride of the staged results
   for (int t = tid; t < ROWS + 32; t += 256) {
     if (t < ROWS) rowoff[t] = run_offset(t, rn.rows, rn.nr);
     else coloff[t - ROWS] = t - ROWS < S ? run_offset(t - ROWS, rn.cols, rn.nc) : 0;
@@ -967,8 +979,18 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
     perm[e] = (uint16_t)p;
   }
   // second operand, per lane and K entry
-  float bv[K], bw[SW == 32 ? K : 1];
-  if constexpr (SW == 16) {
+  float bv[BL ? 1 : K], bw[(SW == 32 && !BL) ? K : 1];
+  if constexpr (BL) {
+    for (int e = tid; e < (K / 2) * YC; e += 256) {
+      const int q = e / YC, c = e % YC;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < S) {
+        const float2 y0 = a.Y[(int64_t)c * K + 2 * q], y1 = a.Y[(int64_t)c * K + 2 * q + 1];
+        v = make_float4(y0.x, y0.y, y1.x, y1.y);
+      }
+      ysh[e] = v;
+    }
+  } else if constexpr (SW == 16) {
     // MFMA column l32 = (real | imaginary part of output l32 % 16)
     const int j = l32 & 15;
     const bool imc = l32 >= 16;
@@ -1020,16 +1042,38 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
         if constexpr (SW == 32) acw[nb][r] = 0.f;
       }
 #pragma unroll
-    for (int q = 0; q < KH; ++q)
+    for (int q = 0; q < KH; ++q) {
+      float b0, b1, w0 = 0.f, w1 = 0.f;
+      if constexpr (BL) {
+        const float4 y = ysh[q * YC + (SW == 32 ? l32 : (l32 & 15))];
+        if constexpr (SW == 16) {
+          const bool imc = l32 >= 16;
+          b0 = imc ? (h ? y.x : y.y) : (h ? -y.y : y.x);
+          b1 = imc ? (h ? y.z : y.w) : (h ? -y.w : y.z);
+        } else {
+          b0 = h ? -y.y : y.x;
+          w0 = h ? y.x : y.y;
+          b1 = h ? -y.w : y.z;
+          w1 = h ? y.z : y.w;
+        }
+      } else {
+        b0 = bv[2 * q];
+        b1 = bv[2 * q + 1];
+        if constexpr (SW == 32) {
+          w0 = bw[2 * q];
+          w1 = bw[2 * q + 1];
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float4 f = xb[(nb * kSmRows + l32) * RSX + q];
         const float x0 = h ? f.y : f.x, x1 = h ? f.w : f.z;
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, bv[2 * q], acc[nb], 0, 0, 0);
-        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, bw[2 * q], acw[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, bv[2 * q + 1], acc[nb], 0, 0, 0);
-        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, bw[2 * q + 1], acw[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b0, acc[nb], 0, 0, 0);
+        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, w0, acw[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, b1, acc[nb], 0, 0, 0);
+        if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, w1, acw[nb], 0, 0, 0);
       }
+    }
     // results as complex [ROWS][S] in the same LDS area
     float *cf = (float *)xb;
     const float2 *cv = (const float2 *)xb;
@@ -1040,7 +1084,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * S + j) * 2 + part] = acc[nb][r];
+            cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
       }
     } else {
       if (l32 < S) {
@@ -1048,7 +1092,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            *(float2 *)&cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * S + l32) * 2] =
+            *(float2 *)&cf[((nb * kSmRows + (r / 4) * 8 + h * 4 + (r % 4)) * SP + l32) * 2] =
                 make_float2(acc[nb][r], acw[nb][r]);
       }
     }
@@ -1061,7 +1105,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
         const int p0 = perm[e], p1 = perm[e + 1];
         const int t0 = p0 >> JB, j0 = p0 & JM, t1 = p1 >> JB, j1 = p1 & JM;
         const int64_t o0 = base + rowoff[t0] + coloff[j0];
-        const float2 v0 = cv[t0 * S + j0], v1 = cv[t1 * S + j1];
+        const float2 v0 = cv[t0 * SP + j0], v1 = cv[t1 * SP + j1];
         if (t0 < rows && t1 < rows && (o0 & 1) == 0) {
           float4 v = make_float4(v0.x, v0.y, v1.x, v1.y);
           float4 *dst = (float4 *)(a.C + o0);
@@ -1079,7 +1123,212 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
       for (int e = lane; e < nent; e += 64) {
         const int p = perm[e];
         const int t = p >> JB, j = p & JM;
-        if (t < rows) store_c(a.C + base + rowoff[t] + coloff[j], cv[t * S + j], a.beta);
+        if (t < rows) store_c(a.C + base + rowoff[t] + coloff[j], cv[t * SP + j], a.beta);
+      }
+    }
+  }
+}
+
+// Thin GEMM-class steps: a short side of T = 32 NCB entries (64 or 128)
+// against a long side of many rows, K a power of two from 16 to 64.  Such a
+// step sits near the ridge of the FP32 roofline (for T = K = 64 about 32
+// flop per byte), so the matrix cores and HBM must both stay busy.  The
+// short operand W (T x K) is staged once per workgroup in LDS, as entry pairs
+// (w[c][2q], w[c][2q + 1]) at [q][c].  Each wave then streams passes of 32
+// long-side rows with no barrier: the rows of a pass are loaded with
+// coalesced 16-byte loads (K in chunks of up to 32 entries) into a
+// wave-private LDS area and multiplied against W (real and imaginary parts
+// on two MFMAs per column block, as in k_cgemm); the next chunk's or pass's
+// loads are issued before the current chunk's MFMAs.
+//
+// Each 32 x 32 block of results goes back through the same LDS area and
+// out in address order, as in k_skinny_mfma (every run of C has a
+// power-of-two size, so an offset is rowoff(r0) + rowoff(t) + coloff(j) and
+// a fixed permutation of the block's entries sorts it).  That permutation,
+// the LDS index of each lane's entries and their offsets relative to the
+// pass and column block are the same for every pass: when the smallest
+// stride is one entry (16-byte pairs), each lane computes them once, and a
+// pass costs one batch of independent LDS reads and one 16-byte store per
+// pair.  Otherwise the entries are stored one at a time.
+template <int K, int NCB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_thin_mfma(StepArgs a, SkinnyRuns rn) {
+  constexpr int KC = K < 32 ? K : 32;          // K entries staged per chunk
+  constexpr int NCH = K / KC;
+  constexpr int KH = KC / 2;                   // 16-byte entry pairs per staged row
+  constexpr int RSX = KH + 1;                  // LDS row stride (16-byte units), one pad
+  constexpr int XW = kSmRows * RSX;
+  constexpr int CS = 33;                       // result row stride (odd: column walks spread over the banks)
+  constexpr int CW = (kSmRows * CS + 1) / 2;   // one 32 x 32 complex result block
+  constexpr int WB = XW > CW ? XW : CW;
+  constexpr int LPT = kSmRows * KH / 64;       // 16-byte loads per lane per chunk
+  constexpr int T = 32 * NCB;
+  constexpr int NPR = kSmRows * 32 / 128;      // 16-byte pairs per lane per block
+  static_assert(kSmRows * KH % 64 == 0, "chunk loads");
+  __shared__ float4 buf[NW][WB];
+  __shared__ float4 wsh[(K / 2) * T];
+  __shared__ int64_t rowoff[kSmRows], coloff[T];
+  __shared__ uint16_t perm[kSmRows * 32];
+  __shared__ int32_t bit_of[10];
+  __shared__ int32_t pairs_s;
+  // per lane (the same for every wave) and pair: the two entries' LDS
+  // indices (t * CS + j) and the first entry's offset within its pass and
+  // column block
+  __shared__ int32_t pidx_s[NPR * 64];
+  __shared__ int64_t poff_s[NPR * 64];
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int S = (int)a.S;
+  for (int t = tid; t < kSmRows + T; t += NT) {
+    if (t < kSmRows) rowoff[t] = run_offset(t, rn.rows, rn.nr);
+    else coloff[t - kSmRows] = t - kSmRows < S ? run_offset(t - kSmRows, rn.cols, rn.nc) : 0;
+  }
+  // W as entry pairs (w[c][2q], w[c][2q + 1]) at [q][c]
+  for (int e = tid; e < (K / 2) * T; e += NT) {
+    const int q = e / T, c = e % T;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < S) {
+      const float2 w0 = a.Y[(int64_t)c * K + 2 * q], w1 = a.Y[(int64_t)c * K + 2 * q + 1];
+      v = make_float4(w0.x, w0.y, w1.x, w1.y);
+    }
+    wsh[e] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // bits 0-4 of a permutation entry are its column in a 32-wide block, bits 5-9 its row
+    int64_t st[10];
+    int pb[10];
+    for (int b = 0; b < 5; ++b) {
+      st[b] = coloff[1 << b];
+      pb[b] = b;
+      st[5 + b] = rowoff[1 << b];
+      pb[5 + b] = 5 + b;
+    }
+    for (int i = 1; i < 10; ++i)
+      for (int q = i; q > 0 && st[q] < st[q - 1]; --q) {
+        const int64_t ts = st[q];
+        st[q] = st[q - 1];
+        st[q - 1] = ts;
+        const int tp = pb[q];
+        pb[q] = pb[q - 1];
+        pb[q - 1] = tp;
+      }
+    for (int i = 0; i < 10; ++i) bit_of[i] = pb[i];
+    pairs_s = st[0] == 1;
+  }
+  __syncthreads();
+  for (int e = tid; e < kSmRows * 32; e += NT) {
+    int p = 0;
+    for (int i = 0; i < 10; ++i)
+      if ((e >> i) & 1) p |= 1 << bit_of[i];
+    perm[e] = (uint16_t)p;
+  }
+  __syncthreads();
+  for (int q = tid; q < NPR * 64; q += NT) {
+    const int e = 2 * (q % 64) + 128 * (q / 64);
+    const int p0 = perm[e], p1 = perm[e + 1];
+    pidx_s[q] = ((p0 >> 5) * CS + (p0 & 31)) | (((p1 >> 5) * CS + (p1 & 31)) << 16);
+    poff_s[q] = rowoff[p0 >> 5] + coloff[p0 & 31];
+  }
+  __syncthreads();
+  // every other stride is then a multiple of two, so a pair's first offset is even
+  const bool pairs = pairs_s && aligned16(a.C);
+  const int64_t R = a.R, npass = (R + kSmRows - 1) / kSmRows;
+  const int64_t wstride = (int64_t)gridDim.x * NW;
+  const float4 *X4 = (const float4 *)a.X;
+  float4 *xb = buf[wave];
+  float4 ld[LPT];
+  auto load = [&](int64_t b, int ch) {
+    if ((b + 1) * kSmRows <= R) {
+      // a full pass: no bounds checks
+      const float4 *src = X4 + b * kSmRows * (K / 2) + ch * KH;
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int g = lane + 64 * i;
+        ld[i] = src[(g / KH) * (K / 2) + g % KH];
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i;
+      const int64_t row = b * kSmRows + g / KH;
+      ld[i] = row < R ? X4[row * (K / 2) + ch * KH + g % KH] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  int64_t blk = (int64_t)blockIdx.x * NW + wave;
+  if (blk < npass) load(blk, 0);
+  for (; blk < npass; blk += wstride) {
+    f32x16 accR[NCB], accI[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accR[cb][r] = 0.f;
+        accI[cb][r] = 0.f;
+      }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int g = lane + 64 * i;
+        xb[(g / KH) * RSX + g % KH] = ld[i];
+      }
+      if (ch + 1 < NCH) load(blk, ch + 1);
+      else if (blk + wstride < npass) load(blk + wstride, 0);
+#pragma unroll
+      for (int q = 0; q < KH; ++q) {
+        const float4 f = xb[l32 * RSX + q];
+        const float x0 = h ? f.y : f.x, x1 = h ? f.w : f.z;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const float4 w = wsh[(ch * KH + q) * T + cb * 32 + l32];
+          // real part: (wr, -wi) on the (re, im) K slots; imaginary part: (wi, wr)
+          const float r0 = h ? -w.y : w.x, i0 = h ? w.x : w.y, r1 = h ? -w.w : w.z, i1 = h ? w.z : w.w;
+          accR[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, r0, accR[cb], 0, 0, 0);
+          accI[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, i0, accI[cb], 0, 0, 0);
+          accR[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, r1, accR[cb], 0, 0, 0);
+          accI[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, i1, accI[cb], 0, 0, 0);
+        }
+      }
+    }
+    const int64_t p0 = blk * kSmRows;
+    const int64_t base = run_offset(p0, rn.rows, rn.nr);
+    const int rows = (int)(R - p0 < kSmRows ? R - p0 : kSmRows);
+    float *cf = (float *)xb;
+    const float2 *cv = (const float2 *)xb;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *(float2 *)&cf[(((r / 4) * 8 + h * 4 + (r % 4)) * CS + l32) * 2] = make_float2(accR[cb][r], accI[cb][r]);
+      float2 *cc = a.C + base + coloff[cb * 32];
+      if (pairs && rows == kSmRows) {
+        float2 v0[NPR], v1[NPR];
+        int64_t off[NPR];
+#pragma unroll
+        for (int i = 0; i < NPR; ++i) {
+          const int32_t pi = pidx_s[i * 64 + lane];
+          off[i] = poff_s[i * 64 + lane];
+          v0[i] = cv[pi & 0xffff];  // t * CS + j
+          v1[i] = cv[pi >> 16];
+        }
+#pragma unroll
+        for (int i = 0; i < NPR; ++i) {
+          float4 v = make_float4(v0[i].x, v0[i].y, v1[i].x, v1[i].y);
+          float4 *dst = (float4 *)(cc + off[i]);
+          if (a.beta) {
+            const float4 o = *dst;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *dst = v;
+        }
+      } else {
+        const int64_t *co = coloff + cb * 32;
+        for (int e = lane; e < kSmRows * 32; e += 64) {
+          const int p = perm[e];
+          const int t = p >> 5, j = p & 31;
+          if (t < rows) store_c(a.C + base + rowoff[t] + co[j], cv[t * CS + j], a.beta);
+        }
       }
     }
   }
@@ -2424,6 +2673,64 @@ static hipError_t run_skinny_mfma(const StepArgs &a, const SkinnyRuns &rn, hipSt
   }
 }
 
+// thin steps on k_thin_mfma: short side 64 or 128, K in {16, 32, 64} (K <= 32
+// for a short side of 128), long side >= 16384
+static bool thin_shape_ok(int64_t R, int64_t S, int64_t K) {
+  const bool kk = K == 16 || K == 32 || (K == 64 && S == 64);
+  return R >= 16384 && (S == 64 || S == 128) && kk;
+}
+
+template <int K, int NCB, int NW>
+static hipError_t run_thin_kn(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
+  const int64_t npass = (a.R + kSmRows - 1) / kSmRows;
+  int64_t blocks = (npass + NW - 1) / NW;
+  // persistent: as many workgroups as fit on the device at once (LDS bound)
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)k_thin_mfma<K, NCB, NW>, 64 * NW, 0) !=
+            hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int64_t cap = (int64_t)per_cu * num_cus();
+  if (blocks > cap) blocks = cap;
+  note_kernel("k_thin_mfma<%d,%d,%d>", K, NCB, NW);
+  hipLaunchKernelGGL((k_thin_mfma<K, NCB, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, rn);
+  return hipGetLastError();
+}
+
+static hipError_t run_thin(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
+  if (a.S == 64) {
+    // twelve waves (three per SIMD; at most 168 VGPRs, up to 146 KB of LDS)
+    if (a.K == 16) return run_thin_kn<16, 2, 12>(a, rn, stream);
+    if (a.K == 32) return run_thin_kn<32, 2, 12>(a, rn, stream);
+    return run_thin_kn<64, 2, 12>(a, rn, stream);
+  }
+  if (a.K == 16) return run_thin_kn<16, 4, 8>(a, rn, stream);
+  return run_thin_kn<32, 4, 8>(a, rn, stream);
+}
+
+static bool gemm_as_thin(const StepArgs &a, hipStream_t stream, hipError_t *err) {
+  if (a.splits != 1 || !a.pow2_runs || a.prec != kPrecExact) return false;
+  const RunDev *rr = a.runs, *cr = a.runs + a.nrr;
+  if (thin_shape_ok(a.R, a.S, a.K) && ((uintptr_t)a.X & 15) == 0) {
+    *err = run_thin(a, SkinnyRuns{rr, cr, a.nrr, a.ncr}, stream);
+    return true;
+  }
+  if (thin_shape_ok(a.S, a.R, a.K) && ((uintptr_t)a.Y & 15) == 0) {
+    StepArgs b = a;
+    b.X = a.Y;
+    b.Y = a.X;
+    b.R = a.S;
+    b.S = a.R;
+    *err = run_thin(b, SkinnyRuns{cr, rr, a.ncr, a.nrr}, stream);
+    return true;
+  }
+  return false;
+}
+
 // The step as given (rows = R) or exchanged (rows = S): the long side must
 // be the row side of k_skinny_mfma.
 static bool gemm_as_skinny(const StepArgs &a, hipStream_t stream, hipError_t *err) {
@@ -2521,6 +2828,7 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
   {
     hipError_t e = hipSuccess;
     if (gemm_as_skinny(a, stream, &e)) return e;
+    if (gemm_as_thin(a, stream, &e)) return e;
   }
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
