@@ -874,7 +874,7 @@ __global__ __launch_bounds__(256) void k_skinny_flat(StepArgs a) {
 }
 
 // Skinny steps with many rows, S <= 32 outputs per row (a power of two),
-// K a power of two (up to 64 for S <= 16, 32 for S = 32), on the FP32
+// K a power of two (up to 64 for S <= 16, 8 for S = 32), on the FP32
 // matrix cores, written in address order.  Also takes GEMM-class steps whose
 // short side is at most 32, with the operands (and C's row and column runs)
 // exchanged when the long side is the column side.
@@ -924,14 +924,8 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   constexpr int LPT = (ROWS * KH + 63) / 64;  // 16-byte loads per lane per pass
   constexpr int LB = 5 + (NB >= 8 ? 3 : NB >= 4 ? 2 : NB >= 2 ? 1 : 0);  // row bits of a pass
   constexpr int JB = SW == 32 ? 5 : 4;       // column bits of a permutation entry
-  // the second operand from LDS for 32-wide steps with K >= 32 (in
-  // registers that would take 64 or more of them per lane): entry pairs
-  // (y[c][2q], y[c][2q + 1]) at [q][c]; 16-wide steps keep it in registers
-  // (measured faster there, K = 64 included)
-  constexpr bool BL = SW == 32 && K >= 32;
-  constexpr int YC = SW == 32 ? 32 : 16;
+  static_assert(SW == 16 || K <= 8, "32-wide steps with K > 8 run on k_thin_mfma");
   __shared__ float4 buf[4][WB];
-  __shared__ float4 ysh[BL ? (K / 2) * YC : 1];
   __shared__ int64_t rowoff[ROWS], coloff[32];
   __shared__ uint16_t perm[kSmRows * 32];
   __shared__ int32_t bit_of[13];
@@ -979,18 +973,8 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
     perm[e] = (uint16_t)p;
   }
   // second operand, per lane and K entry
-  float bv[BL ? 1 : K], bw[(SW == 32 && !BL) ? K : 1];
-  if constexpr (BL) {
-    for (int e = tid; e < (K / 2) * YC; e += 256) {
-      const int q = e / YC, c = e % YC;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < S) {
-        const float2 y0 = a.Y[(int64_t)c * K + 2 * q], y1 = a.Y[(int64_t)c * K + 2 * q + 1];
-        v = make_float4(y0.x, y0.y, y1.x, y1.y);
-      }
-      ysh[e] = v;
-    }
-  } else if constexpr (SW == 16) {
+  float bv[K], bw[SW == 32 ? K : 1];
+  if constexpr (SW == 16) {
     // MFMA column l32 = (real | imaginary part of output l32 % 16)
     const int j = l32 & 15;
     const bool imc = l32 >= 16;
@@ -1043,26 +1027,11 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
       }
 #pragma unroll
     for (int q = 0; q < KH; ++q) {
-      float b0, b1, w0 = 0.f, w1 = 0.f;
-      if constexpr (BL) {
-        const float4 y = ysh[q * YC + (SW == 32 ? l32 : (l32 & 15))];
-        if constexpr (SW == 16) {
-          const bool imc = l32 >= 16;
-          b0 = imc ? (h ? y.x : y.y) : (h ? -y.y : y.x);
-          b1 = imc ? (h ? y.z : y.w) : (h ? -y.w : y.z);
-        } else {
-          b0 = h ? -y.y : y.x;
-          w0 = h ? y.x : y.y;
-          b1 = h ? -y.w : y.z;
-          w1 = h ? y.z : y.w;
-        }
-      } else {
-        b0 = bv[2 * q];
-        b1 = bv[2 * q + 1];
-        if constexpr (SW == 32) {
-          w0 = bw[2 * q];
-          w1 = bw[2 * q + 1];
-        }
+      const float b0 = bv[2 * q], b1 = bv[2 * q + 1];
+      float w0 = 0.f, w1 = 0.f;
+      if constexpr (SW == 32) {
+        w0 = bw[2 * q];
+        w1 = bw[2 * q + 1];
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -1129,7 +1098,7 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   }
 }
 
-// Thin GEMM-class steps: a short side of T = 32 NCB entries (64 or 128)
+// Thin GEMM-class steps: a short side of T = 32 NCB entries (32, 64 or 128)
 // against a long side of many rows, K a power of two from 16 to 64.  Such a
 // step sits near the ridge of the FP32 roofline (for T = K = 64 about 32
 // flop per byte), so the matrix cores and HBM must both stay busy.  The
@@ -2624,10 +2593,10 @@ static bool skinny_flat_ok(const StepArgs &a) {
 bool small_gemm_ok(const StepArgs &a) { return a.R * a.S <= kSmallGemmRS && a.K <= kSmallGemmK; }
 
 // a step on k_skinny_mfma: long side (rows after orientation) >= 4096, short
-// side S a power of two <= 32, K a power of two (<= 64; <= 32 when S = 32)
+// side S a power of two <= 32, K a power of two (<= 64; <= 8 when S = 32)
 static bool skinny_mfma_shape_ok(int64_t R, int64_t S, int64_t K) {
   const bool pow2s = S >= 1 && S <= 32 && (S & (S - 1)) == 0;
-  const bool pow2k = K >= 2 && K <= (S > 16 ? 32 : 64) && (K & (K - 1)) == 0;
+  const bool pow2k = K >= 2 && K <= (S > 16 ? 8 : 64) && (K & (K - 1)) == 0;
   return R >= 4096 && pow2s && pow2k;
 }
 
@@ -2650,7 +2619,7 @@ static hipError_t run_skinny_mfma_kn(const StepArgs &a, const SkinnyRuns &rn, hi
 // (32 NB rows of K + S entries), with NB S <= 32
 template <int K>
 static hipError_t run_skinny_mfma_k(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
-  if constexpr (K <= 32)
+  if constexpr (K <= 8)
     if (a.S > 16) return run_skinny_mfma_kn<K, 1, 32>(a, rn, stream);
   const int64_t fit = 32 / (K + a.S);
   if constexpr (K <= 2)
@@ -2673,11 +2642,11 @@ static hipError_t run_skinny_mfma(const StepArgs &a, const SkinnyRuns &rn, hipSt
   }
 }
 
-// thin steps on k_thin_mfma: short side 64 or 128, K in {16, 32, 64} (K <= 32
-// for a short side of 128), long side >= 16384
+// thin steps on k_thin_mfma: short side 32, 64 or 128, K in {16, 32, 64}
+// (K <= 32 for a short side of 128), long side >= 16384
 static bool thin_shape_ok(int64_t R, int64_t S, int64_t K) {
-  const bool kk = K == 16 || K == 32 || (K == 64 && S == 64);
-  return R >= 16384 && (S == 64 || S == 128) && kk;
+  const bool kk = K == 16 || K == 32 || (K == 64 && S <= 64);
+  return R >= 16384 && (S == 32 || S == 64 || S == 128) && kk;
 }
 
 template <int K, int NCB, int NW>
@@ -2702,6 +2671,11 @@ static hipError_t run_thin_kn(const StepArgs &a, const SkinnyRuns &rn, hipStream
 }
 
 static hipError_t run_thin(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
+  if (a.S == 32) {
+    if (a.K == 16) return run_thin_kn<16, 1, 12>(a, rn, stream);
+    if (a.K == 32) return run_thin_kn<32, 1, 12>(a, rn, stream);
+    return run_thin_kn<64, 1, 12>(a, rn, stream);
+  }
   if (a.S == 64) {
     // twelve waves (three per SIMD; at most 168 VGPRs, up to 146 KB of LDS)
     if (a.K == 16) return run_thin_kn<16, 2, 12>(a, rn, stream);
@@ -2827,8 +2801,8 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
   // a short side of at most 32 with a short K: memory-bound, streamed like a skinny step
   {
     hipError_t e = hipSuccess;
-    if (gemm_as_skinny(a, stream, &e)) return e;
     if (gemm_as_thin(a, stream, &e)) return e;
+    if (gemm_as_skinny(a, stream, &e)) return e;
   }
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;

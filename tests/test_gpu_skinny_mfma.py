@@ -1,7 +1,7 @@
 """Skinny steps on the matrix-core kernel with address-ordered stores
 (k_skinny_mfma): every output entry against the oracle, for S = 1 ... 16
 outputs per row with K = 2 ... 64, GEMM-class steps with a short side of 32
-(K = 2 ... 32, the long side on either operand, so that the kernel also runs
+(K = 2 ... 8; the long side on either operand, so that the kernel also runs
 with operands and runs exchanged), random interleavings of the output modes
 (so the stores walk runs of every length), a sliced run (beta accumulation)
 and shapes that must fall back to the other kernels.
@@ -51,9 +51,9 @@ def _check(net, tree, expect_kernel=None, kind="skinny", **kw):
 
 CASES = [(14, 0, 1), (12, 4, 4), (13, 3, 3), (14, 4, 2), (12, 2, 5), (15, 1, 4), (16, 4, 1), (13, 0, 5),
          (13, 3, 2), (14, 2, 3), (17, 4, 4), (14, 1, 1), (13, 4, 6), (12, 2, 6), (14, 0, 6)]
-# GEMM-class steps (short side 32): log2 of (long side, K); below 2^14 rows
-# the small-GEMM kernel takes them
-GEMM_CASES = [(15, 1), (16, 2), (15, 3), (17, 4), (15, 5), (16, 5)]
+# GEMM-class steps (short side 32, K <= 8): log2 of (long side, K); up to
+# 2^14 rows the small-GEMM kernel takes them
+GEMM_CASES = [(15, 1), (16, 2), (15, 3), (17, 2), (18, 1), (17, 3)]
 
 
 @pytest.mark.parametrize("i", range(len(CASES)))
@@ -100,8 +100,8 @@ def test_fallbacks_keep_the_other_skinny_kernels():
     net, tree = sweep.network(13, 3, 7, permuted=True, seed=9, with_data=True)   # K = 128
     ks = _check(net, tree)
     assert ks and not ks[0].startswith("k_skinny_mfma"), ks
-    # short side 32 with K = 64, and short side 64: the tiled GEMM kernel
-    for lm, ln, lk in [(15, 5, 6), (6, 15, 3)]:
+    # short side 32 with K = 128, and short side 64 with K = 8: the tiled GEMM kernels
+    for lm, ln, lk in [(15, 5, 7), (6, 15, 3)]:
         net, tree = sweep.network(lm, ln, lk, permuted=True, seed=lm + ln + lk, with_data=True)
         ks = _check(net, tree, kind="gemm")
         assert ks and ks[0].startswith("k_cgemm"), ks

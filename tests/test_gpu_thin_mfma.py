@@ -1,6 +1,6 @@
 """Thin GEMM-class steps on the streaming matrix-core kernel (k_thin_mfma):
-a short side of 64 or 128 against a long side of 2^14 rows or more, K = 16,
-32 (and 64 for a short side of 64), the long side on either operand, random
+a short side of 32, 64 or 128 against a long side of 2^14 rows or more,
+K = 16, 32 (and 64 for a short side of 32 or 64), the long side on either operand, random
 interleavings of the output modes, a sliced run (beta accumulation), and
 shapes that must stay on the tiled GEMM kernels.  Every output entry against
 the oracle, |g - r| <= 1e-4 * max(|r|, rms(r))."""
@@ -13,7 +13,8 @@ from workloads import sweep
 pytestmark = pytest.mark.gpu
 
 # log2 of (long side, short side, K)
-CASES = [(14, 6, 4), (15, 6, 5), (14, 6, 6), (16, 6, 6), (14, 7, 4), (15, 7, 5), (17, 6, 4)]
+CASES = [(14, 6, 4), (15, 6, 5), (14, 6, 6), (16, 6, 6), (14, 7, 4), (15, 7, 5), (17, 6, 4), (15, 5, 4), (16, 5, 5),
+         (15, 5, 6)]
 
 
 @pytest.fixture(scope="module", autouse=True)
