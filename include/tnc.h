@@ -349,9 +349,11 @@ tnc_status tnc_plan_distribute(tnc_plan_t plan, const tnc_dist_options *opts, tn
  * Measurement probe (not part of a contraction): the current device's
  * sustained FP32 matrix-core rate (4 or 8 independent chains of the 32x32x2
  * FP32 MFMA per wave, 2 or 4 waves per SIMD, no memory traffic) and HBM copy
- * rate (16-byte grid-stride copy of bytes / 2 from the first half of
- * `buffer` to the second, 1 or 4 loads in flight per thread), each the best
- * over those launch shapes of three timed runs after one untimed run.  `buffer`: caller-owned device memory of `bytes` >= 64 MiB,
+ * rate (16-byte copy of bytes / 2 from the first half of `buffer` to the
+ * second: grid-stride with 1 or 4 loads in flight per thread, or one
+ * contiguous 256 KiB chunk per workgroup with plain or nontemporal loads and
+ * stores), each the best over those launch shapes of three timed runs after
+ * one untimed run.  `buffer`: caller-owned device memory of `bytes` >= 64 MiB,
  * 256-byte aligned, overwritten.  Synchronous.  These are the measured
  * denominators beside the published peaks (157.3 TFLOP/s, 8 TB/s).
  * Errors: INVALID_ARG, HIP.

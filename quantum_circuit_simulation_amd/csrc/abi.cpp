@@ -502,10 +502,12 @@ tnc_status tnc_probe_peaks(void *buffer, uint64_t bytes, void *stream_ptr, doubl
         if (e == hipSuccess && rep > 0 && tf > best_mfma) best_mfma = tf;
       }
     }
-  for (int32_t inflight : {1, 4})
+  // copy patterns: grid-stride with 1 or 4 loads in flight per thread, one
+  // contiguous chunk per workgroup with plain or nontemporal accesses
+  for (int32_t pattern : {0, 1, 2, 3})
     for (int rep = 0; rep < 4 && e == hipSuccess; ++rep) {
       float ms = 0.f;
-      timed([&] { return tnc::launch_probe_copy(buf, buf + half16 * 16, half16, inflight, stream); }, &ms);
+      timed([&] { return tnc::launch_probe_copy(buf, buf + half16 * 16, half16, pattern, stream); }, &ms);
       const double gbps = 2.0 * (double)half16 * 16 / (ms * 1e-3) / 1e9;
       if (e == hipSuccess && rep > 0 && gbps > best_copy) best_copy = gbps;
     }

@@ -1344,6 +1344,29 @@ __global__ __launch_bounds__(256) void k_probe_copy(const float4 *src, float4 *d
   for (; i < n; i += step) dst[i] = src[i];
 }
 
+// 16-byte copy with one contiguous chunk of `chunk` entries per workgroup
+// (measured faster than grid-stride order here), loads and stores
+// nontemporal when NT.
+typedef float probe_v4f __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(256) void k_probe_copy_chunk(const float4 *src, float4 *dst, int64_t n, int64_t chunk) {
+  const int64_t b0 = (int64_t)blockIdx.x * chunk, b1 = b0 + chunk < n ? b0 + chunk : n;
+  const probe_v4f *s = (const probe_v4f *)src;
+  probe_v4f *d = (probe_v4f *)dst;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 1024) {
+    probe_v4f v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 256 * u < b1) v[u] = NT ? __builtin_nontemporal_load(&s[i + 256 * u]) : s[i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 256 * u < b1) {
+        if (NT) __builtin_nontemporal_store(v[u], &d[i + 256 * u]);
+        else d[i + 256 * u] = v[u];
+      }
+  }
+}
+
 // sum split-K partials [splits, R, S] into C through the runs
 template <typename T>
 __global__ void k_split_reduce(StepArgsT<T> a) {
@@ -2846,14 +2869,24 @@ hipError_t launch_probe_mfma(float *out, int64_t blocks, int32_t iters, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t inflight, hipStream_t stream) {
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t pattern, hipStream_t stream) {
+  const float4 *s = (const float4 *)src;
+  float4 *d = (float4 *)dst;
+  if (pattern >= 2) {
+    const int64_t chunk = int64_t(1) << 14;
+    const int64_t blocks = (n16 + chunk - 1) / chunk;
+    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (pattern == 3)
+      hipLaunchKernelGGL(k_probe_copy_chunk<true>, dim3((unsigned)blocks), dim3(256), 0, stream, s, d, n16, chunk);
+    else
+      hipLaunchKernelGGL(k_probe_copy_chunk<false>, dim3((unsigned)blocks), dim3(256), 0, stream, s, d, n16, chunk);
+    return hipGetLastError();
+  }
   const int64_t blocks = 8 * (int64_t)num_cus();
-  if (inflight >= 4)
-    hipLaunchKernelGGL(k_probe_copy<4>, dim3((unsigned)blocks), dim3(256), 0, stream, (const float4 *)src,
-                       (float4 *)dst, n16);
+  if (pattern == 1)
+    hipLaunchKernelGGL(k_probe_copy<4>, dim3((unsigned)blocks), dim3(256), 0, stream, s, d, n16);
   else
-    hipLaunchKernelGGL(k_probe_copy<1>, dim3((unsigned)blocks), dim3(256), 0, stream, (const float4 *)src,
-                       (float4 *)dst, n16);
+    hipLaunchKernelGGL(k_probe_copy<1>, dim3((unsigned)blocks), dim3(256), 0, stream, s, d, n16);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream);
 // copy of n16 16-byte entries with `inflight` (1 or 4) loads per thread in
 // flight.  device_cus(): compute units of the current device.
 hipError_t launch_probe_mfma(float *out, int64_t blocks, int32_t iters, int32_t chains, hipStream_t stream);
-hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t inflight, hipStream_t stream);
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t n16, int32_t pattern, hipStream_t stream);
 int32_t device_cus();
 
 // Name of the kernel the last launcher call on this thread enqueued (a split
