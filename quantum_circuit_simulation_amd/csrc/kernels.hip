@@ -1303,6 +1303,148 @@ __global__ __launch_bounds__(64 * NW) void k_thin_mfma(StepArgs a, SkinnyRuns rn
   }
 }
 
+// K-reduction steps: both output sides at most 32 (R, S <= 32) and a long K
+// split into `splits` chunks, as in the closing steps of amplitude trees
+// (32 x 32 x 2^25, 4 x 4 x 2^30).  One workgroup per K chunk computes the
+// whole R x S partial product of its chunk, reading each operand row once
+// with coalesced 16-byte loads, and writes it to the split-K scratch
+// [splits, R, S]; k_split_reduce then sums the chunks into C.  (The tiled
+// GEMM kernel ran such steps with 7/8 of its 256-row tile empty, and the
+// skinny row kernel re-read the second operand once per row.)
+//
+// Matrix-core form: each wave takes 32-entry sub-chunks of K in turn,
+// stages both operands' rows through a wave-private LDS area and
+// accumulates the 32 x 32 block (rows or columns beyond R or S are zero)
+// with the (re, im) K-slot scheme of k_cgemm; the waves' blocks are summed
+// through LDS at the end.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_kred_mfma(StepArgs a, int64_t kchunk) {
+  constexpr int KC = 32, KH = KC / 2, RSX = KH + 1, XW = kSmRows * RSX;
+  constexpr int LPT = kSmRows * KH / 64;       // 16-byte loads per lane and operand
+  __shared__ float4 buf[NW][2 * XW];           // staged X rows, then Y rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int R = (int)a.R, S = (int)a.S;
+  const int64_t K = a.K, KH2 = a.K / 2;
+  const int64_t k0 = (int64_t)blockIdx.x * kchunk, k1 = k0 + kchunk < K ? k0 + kchunk : K;
+  const int64_t nsub = k1 > k0 ? (k1 - k0) / KC : 0;
+  const float4 *X4 = (const float4 *)a.X, *Y4 = (const float4 *)a.Y;
+  float4 *xb = buf[wave], *yb = buf[wave] + XW;
+  f32x16 accR, accI;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    accR[r] = 0.f;
+    accI[r] = 0.f;
+  }
+  float4 lx[LPT], ly[LPT];
+  auto load = [&](int64_t sub) {
+    const int64_t c = (k0 + sub * KC) / 2;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i, row = g / KH, q = g % KH;
+      lx[i] = row < R ? X4[row * KH2 + c + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      ly[i] = row < S ? Y4[row * KH2 + c + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  int64_t sub = wave;
+  if (sub < nsub) load(sub);
+  for (; sub < nsub; sub += NW) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i;
+      xb[(g / KH) * RSX + g % KH] = lx[i];
+      yb[(g / KH) * RSX + g % KH] = ly[i];
+    }
+    if (sub + NW < nsub) load(sub + NW);
+#pragma unroll
+    for (int q = 0; q < KH; ++q) {
+      const float4 f = xb[l32 * RSX + q], w = yb[l32 * RSX + q];
+      const float x0 = h ? f.y : f.x, x1 = h ? f.w : f.z;
+      // real part: (yr, -yi) on the (re, im) K slots; imaginary part: (yi, yr)
+      const float r0 = h ? -w.y : w.x, i0 = h ? w.x : w.y, r1 = h ? -w.w : w.z, i1 = h ? w.z : w.w;
+      accR = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, r0, accR, 0, 0, 0);
+      accI = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, i0, accI, 0, 0, 0);
+      accR = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, r1, accR, 0, 0, 0);
+      accI = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, i1, accI, 0, 0, 0);
+    }
+  }
+  // this wave's 32 x 32 block into its own LDS area (after its last reads
+  // of it: one wave's LDS operations complete in order), then the sum over
+  // the waves
+  float2 *cv = (float2 *)buf[wave];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cv[((r / 4) * 8 + h * 4 + (r % 4)) * 32 + l32] = make_float2(accR[r], accI[r]);
+  __syncthreads();
+  for (int e = tid; e < R * S; e += 64 * NW) {
+    const int i = e / S, j = e - (e / S) * S;
+    float2 t = make_float2(0.f, 0.f);
+    for (int w = 0; w < NW; ++w) {
+      const float2 v = ((const float2 *)buf[w])[i * 32 + j];
+      t.x += v.x;
+      t.y += v.y;
+    }
+    a.scratch[(int64_t)blockIdx.x * R * S + e] = t;
+  }
+}
+
+// Vector-ALU form for R S <= 16 outputs, R >= S (RM x SM covers R x S): each thread
+// takes entry pairs of the chunk in turn, with the R + S operand rows read
+// as 16-byte pairs (one contiguous kilobyte per row and wave instruction),
+// and keeps all R S complex sums in registers; wave shuffles and LDS sum
+// them over the workgroup.
+template <int RM, int SM>
+__global__ __launch_bounds__(256) void k_kred_valu(StepArgs a, int64_t kchunk) {
+  const int R = (int)a.R, S = (int)a.S;
+  const int64_t K = a.K, KH2 = a.K / 2;
+  const int64_t k0 = (int64_t)blockIdx.x * kchunk, k1 = k0 + kchunk < K ? k0 + kchunk : K;
+  const float4 *X4 = (const float4 *)a.X, *Y4 = (const float4 *)a.Y;
+  float2 acc[RM][SM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int c = 0; c < SM; ++c) acc[r][c] = make_float2(0.f, 0.f);
+  const int64_t pend = k1 > k0 ? k1 / 2 : 0;
+#pragma unroll 2
+  for (int64_t p = k0 / 2 + threadIdx.x; p < pend; p += 256) {
+    float4 x[RM], y[SM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) x[r] = r < R ? X4[r * KH2 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < SM; ++c) y[c] = c < S ? Y4[c * KH2 + p] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int c = 0; c < SM; ++c) {
+        acc[r][c].x += x[r].x * y[c].x - x[r].y * y[c].y + x[r].z * y[c].z - x[r].w * y[c].w;
+        acc[r][c].y += x[r].x * y[c].y + x[r].y * y[c].x + x[r].z * y[c].w + x[r].w * y[c].z;
+      }
+  }
+  __shared__ float2 red[4][RM * SM];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int c = 0; c < SM; ++c) {
+      float vx = acc[r][c].x, vy = acc[r][c].y;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        vx += __shfl_xor(vx, off);
+        vy += __shfl_xor(vy, off);
+      }
+      if (lane == 0) red[wave][r * SM + c] = make_float2(vx, vy);
+    }
+  __syncthreads();
+  if ((int)threadIdx.x < R * S) {
+    const int e = threadIdx.x, i = e / S, j = e - (e / S) * S;
+    float2 t = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      t.x += red[w][i * SM + j].x;
+      t.y += red[w][i * SM + j].y;
+    }
+    a.scratch[(int64_t)blockIdx.x * R * S + e] = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // measurement probes (not part of a contraction): the device's sustained
 // FP32 matrix-core rate and HBM copy rate, the denominators a roofline is
@@ -2665,6 +2807,39 @@ static hipError_t run_skinny_mfma(const StepArgs &a, const SkinnyRuns &rn, hipSt
   }
 }
 
+// K-reduction steps (k_kred_*): a split-K step with both output sides at
+// most 32 whose K chunks are whole multiples of 32 entries
+static bool kred_ok(const StepArgs &a) {
+  if (a.splits <= 1 || a.prec != kPrecExact || a.scratch == nullptr) return false;
+  if (a.R < 1 || a.S < 1 || a.R > 32 || a.S > 32) return false;
+  if (a.K % ((int64_t)a.splits * 32) != 0) return false;
+  return ((uintptr_t)a.X & 15) == 0 && ((uintptr_t)a.Y & 15) == 0;
+}
+
+template <int RM, int SM>
+static hipError_t run_kred_valu_rs(const StepArgs &a, int64_t kchunk, hipStream_t stream) {
+  note_kernel("k_kred_valu<%d,%d>", RM, SM);
+  hipLaunchKernelGGL((k_kred_valu<RM, SM>), dim3((unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
+  return hipGetLastError();
+}
+
+static hipError_t run_kred(const StepArgs &a, hipStream_t stream) {
+  const int64_t kchunk = a.K / a.splits;
+  hipError_t e;
+  // skinny-class steps put the longer side on the rows (R >= S)
+  if (a.R * a.S <= 16 && a.R >= a.S) {
+    if (a.R <= 4) e = run_kred_valu_rs<4, 4>(a, kchunk, stream);
+    else if (a.R <= 8) e = run_kred_valu_rs<8, 2>(a, kchunk, stream);
+    else e = run_kred_valu_rs<16, 1>(a, kchunk, stream);
+  } else {
+    note_kernel("k_kred_mfma<%d>", 4);
+    hipLaunchKernelGGL((k_kred_mfma<4>), dim3((unsigned)a.splits), dim3(256), 0, stream, a, kchunk);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  return run_split_reduce(a, stream);
+}
+
 // thin steps on k_thin_mfma: short side 32, 64 or 128, K in {16, 32, 64}
 // (K <= 32 for a short side of 128), long side >= 16384
 static bool thin_shape_ok(int64_t R, int64_t S, int64_t K) {
@@ -2773,6 +2948,8 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   // few rows and a short K: the small-GEMM kernel (one workgroup per 32-row
   // block) instead of one workgroup per row
   if (a.R < 4096 && a.splits <= 1 && small_gemm_ok(a)) return run_cgemm_small(a, stream);
+  // at most 32 x 32 outputs over a long, split K: one workgroup per K chunk
+  if (kred_ok(a)) return run_kred(a, stream);
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
   // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
@@ -2827,6 +3004,7 @@ hipError_t launch_gemm(const StepArgs &a, hipStream_t stream) {
     if (gemm_as_thin(a, stream, &e)) return e;
     if (gemm_as_skinny(a, stream, &e)) return e;
   }
+  if (kred_ok(a)) return run_kred(a, stream);
   // tile shape: keep the short side of the step inside one tile edge
   hipError_t e;
   if (a.S > 64 && a.R <= 32) e = run_cgemm<32, 256, 8, 32, 64>(a, stream);
