@@ -888,8 +888,12 @@ __global__ __launch_bounds__(256) void k_skinny_flat(StepArgs a) {
 // (16-31): with the (re, im) K-slot scheme of k_cgemm, column j < 16 takes
 // (yr, -yi) of output j and column 16 + j takes (yi, yr), so one MFMA per
 // complex entry of K yields both parts.  With SW = 32 the real and the
-// imaginary parts take one MFMA each, as in k_cgemm.  The next pass's loads
-// are issued before this pass's MFMAs and stores.
+// imaginary parts take one MFMA each, as in k_cgemm.  With SW = 8 (S <= 8)
+// the 16 x 16 x 4 MFMA takes an entry pair per instruction: lane group
+// g = lane / 16 supplies K slot g of (re, im, re', im'), read from LDS as
+// one float, and its 16 columns carry the real (0-7) and imaginary (8-15)
+// parts, with second operands (yr, -yi, yr', -yi') and (yi, yr, yi', yr').
+// The next pass's loads are issued before this pass's MFMAs and stores.
 //
 // Stores: when every run of C has a power-of-two size, the offset of row
 // r0 + t (r0 a multiple of the pass) is rowoff(r0) + rowoff(t), so the
@@ -918,13 +922,14 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   // ROWS x S complex results with an odd row stride S + 1, so that a walk
   // down a column (the store order when a row mode has the smallest
   // stride) spreads over the LDS banks; NB S <= 32
-  constexpr int SMAX = SW == 32 ? 32 : (32 / NB < 16 ? 32 / NB : 16);
+  constexpr int SMAX = SW == 32 ? 32 : (32 / NB < SW ? 32 / NB : SW);
   constexpr int CW = (ROWS * (SMAX + 1) + 1) / 2;
   constexpr int WB = XW > CW ? XW : CW;
   constexpr int LPT = (ROWS * KH + 63) / 64;  // 16-byte loads per lane per pass
   constexpr int LB = 5 + (NB >= 8 ? 3 : NB >= 4 ? 2 : NB >= 2 ? 1 : 0);  // row bits of a pass
   constexpr int JB = SW == 32 ? 5 : 4;       // column bits of a permutation entry
-  static_assert(SW == 16 || K <= 8, "32-wide steps with K > 8 run on k_thin_mfma");
+  static_assert(SW != 32 || K <= 8, "32-wide steps with K > 8 run on k_thin_mfma");
+  constexpr int RT = ROWS / 16;              // 16-row tiles of a pass (SW = 8)
   __shared__ float4 buf[4][WB];
   __shared__ int64_t rowoff[ROWS], coloff[32];
   __shared__ uint16_t perm[kSmRows * 32];
@@ -972,9 +977,26 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
       if ((e >> i) & 1) p |= 1 << bit_of[i];
     perm[e] = (uint16_t)p;
   }
-  // second operand, per lane and K entry
-  float bv[K], bw[SW == 32 ? K : 1];
-  if constexpr (SW == 16) {
+  // second operand, per lane and K entry (SW = 8: per lane and entry pair)
+  float bv[SW == 8 ? 1 : K], bw[SW == 32 ? K : 1], bv8[SW == 8 ? KH : 1];
+  if constexpr (SW == 8) {
+    // 16 x 16 x 4 MFMA: lane group g = lane / 16 supplies K slot g of an entry
+    // pair, (re, im, re, im); column c = lane % 16 carries the real part of
+    // output c (c < 8) or the imaginary part of output c - 8
+    const int g = lane >> 4, c = lane & 15, j = c & 7;
+#pragma unroll
+    for (int q = 0; q < KH; ++q) {
+      float2 y0 = make_float2(0.f, 0.f), y1 = y0;
+      if (j < S) {
+        y0 = a.Y[(int64_t)j * K + 2 * q];
+        y1 = a.Y[(int64_t)j * K + 2 * q + 1];
+      }
+      // slot g: (yr, -yi, yr', -yi') for a real-part column, (yi, yr, yi', yr') for an imaginary one
+      const float2 y = g < 2 ? y0 : y1;
+      const bool odd = (g & 1) != 0;
+      bv8[q] = c < 8 ? (odd ? -y.y : y.x) : (odd ? y.x : y.y);
+    }
+  } else if constexpr (SW == 16) {
     // MFMA column l32 = (real | imaginary part of output l32 % 16)
     const int j = l32 & 15;
     const bool imc = l32 >= 16;
@@ -1017,7 +1039,24 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
       if (g < ROWS * KH) xb[(g / KH) * RSX + g % KH] = ld[i];
     }
     if (blk + wstride < npass) load(blk + wstride);
-    f32x16 acc[NB], acw[SW == 32 ? NB : 1];
+    f32x16 acc[SW == 8 ? 1 : NB], acw[SW == 32 ? NB : 1];
+    f32x4 acc8[SW == 8 ? RT : 1];
+    if constexpr (SW == 8) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc8[t][r] = 0.f;
+      // A operand: row t * 16 + lane % 16, K slot lane / 16 of the pair, one
+      // 4-byte LDS read
+      const float *xf = (const float *)xb;
+#pragma unroll
+      for (int q = 0; q < KH; ++q)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const float av = xf[((t * 16 + (lane & 15)) * RSX + q) * 4 + (lane >> 4)];
+          acc8[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv8[q], acc8[t], 0, 0, 0);
+        }
+    } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1043,10 +1082,20 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
         if constexpr (SW == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, w1, acw[nb], 0, 0, 0);
       }
     }
+    }
     // results as complex [ROWS][S] in the same LDS area
     float *cf = (float *)xb;
     const float2 *cv = (const float2 *)xb;
-    if constexpr (SW == 16) {
+    if constexpr (SW == 8) {
+      // 16 x 16 result tile t: lane holds rows t * 16 + 4 (lane / 16) + r of column lane % 16
+      const int c = lane & 15, j = c & 7, part = c >> 3;
+      if (j < S) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cf[((t * 16 + 4 * (lane >> 4) + r) * SP + j) * 2 + part] = acc8[t][r];
+      }
+    } else if constexpr (SW == 16) {
       const int j = l32 & 15, part = l32 >> 4;
       if (j < S) {
 #pragma unroll
@@ -2780,19 +2829,22 @@ static hipError_t run_skinny_mfma_kn(const StepArgs &a, const SkinnyRuns &rn, hi
   return hipGetLastError();
 }
 
-// sub-blocks per wave pass: about 8 KB of operand and result rows per pass
-// (32 NB rows of K + S entries), with NB S <= 32
+// Tile and sub-blocks per wave pass (32 NB rows; NB S <= 32 and the pass's
+// entries ROWS S <= 1024):
+// - up to 8 outputs with K <= 8: 16 x 16 x 4 MFMA tiles, which need half the
+//   accumulator registers and MFMA time per row of the 32-wide tile there;
+//   256 rows per pass for K = 2 (S <= 4), else 128;
+// - 16 outputs, or K >= 16: the 32-wide tile (real and imaginary parts in
+//   its two column halves), one 32-row block per pass;
+// - 32 outputs (K <= 8): real and imaginary parts on two MFMAs.
 template <int K>
 static hipError_t run_skinny_mfma_k(const StepArgs &a, const SkinnyRuns &rn, hipStream_t stream) {
-  if constexpr (K <= 8)
-    if (a.S > 16) return run_skinny_mfma_kn<K, 1, 32>(a, rn, stream);
-  const int64_t fit = 32 / (K + a.S);
   if constexpr (K <= 2)
-    if (fit >= 8 && a.S <= 4) return run_skinny_mfma_kn<K, 8, 16>(a, rn, stream);
-  if constexpr (K <= 4)
-    if (fit >= 4 && a.S <= 8) return run_skinny_mfma_kn<K, 4, 16>(a, rn, stream);
-  if constexpr (K <= 8)
-    if (fit >= 2) return run_skinny_mfma_kn<K, 2, 16>(a, rn, stream);
+    if (a.S <= 4) return run_skinny_mfma_kn<K, 8, 8>(a, rn, stream);
+  if constexpr (K <= 8) {
+    if (a.S <= 8) return run_skinny_mfma_kn<K, 4, 8>(a, rn, stream);
+    if (a.S > 16) return run_skinny_mfma_kn<K, 1, 32>(a, rn, stream);
+  }
   return run_skinny_mfma_kn<K, 1, 16>(a, rn, stream);
 }
 
