@@ -2250,12 +2250,6 @@ int num_cus() {
   return g_num_cus;
 }
 
-int pow2_floor_i(int64_t v) {
-  int p = 1;
-  while ((int64_t)p * 2 <= v && p < (1 << 30)) p *= 2;
-  return p;
-}
-
 template <int BM, int BN, int BK, int WM, int WN>
 hipError_t run_cgemm(const StepArgs &a, hipStream_t stream) {
   const int64_t tiles_r = (a.R + BM - 1) / BM, tiles_c = (a.S + BN - 1) / BN;
