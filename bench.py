@@ -375,9 +375,43 @@ class TreeWorkload:
             self._run = self.plan.bind(self.leaves, self.out, self.ws)
         if events is not None:
             events[0][0].record()
-        self._run()
+        if self._graph is not None:
+            self._graph.replay()
+        else:
+            self._run()
         if events is not None:
             events[0][1].record()
+
+    _graph = None
+
+    def enable_graph(self):
+        """Capture one tnc_execute of the plan in a HIP graph (torch's
+        CUDAGraph over the library's launches); steps then replay it.  The
+        replay's output must equal the eager output bit for bit."""
+        import torch
+        eager_run = self.plan.bind(self.leaves, self.out, self.ws)
+        eager_run()
+        torch.cuda.synchronize()
+        eager = self.out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.plan.bind(self.leaves, self.out, self.ws)()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self._graph_run = self.plan.bind(self.leaves, self.out, self.ws)
+            self._graph_run()
+        self.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(self.out, eager))
+        if not same:
+            raise RuntimeError("graph replay differs from the eager result")
+        self._graph = g
+        self.config["launch"] = "HIP graph replay of one tnc_execute (replay checked bit for bit against eager)"
 
     def ablation(self, steps):
         """The whole tree under naive order (operands and root re-laid before
@@ -935,6 +969,8 @@ def main():
                     choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal",
                              "brickwork30sv", "grid7x8", "grid7x8d16", "peaks"])
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--graph", action="store_true",
+                    help="tree workloads: time replays of one tnc_execute captured in a HIP graph")
     ap.add_argument("--timed-slices", type=int, default=2,
                     help="grid7x8d16: complete slices run per timed step")
     ap.add_argument("--slices", default="", help="tree workloads: also run the tree sliced on these numbers of modes, "
@@ -1006,6 +1042,8 @@ def main():
     else:
         wl = TreeWorkload(args.workload)
         nlaunch = 1
+        if args.graph:
+            wl.enable_graph()
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s; flop/step {wl.flops:.4g}")
 
