@@ -5,7 +5,7 @@ MI355X FP32 MFMA peak and wall time per result, on one GPU.
 
 Default workload: one amplitude <0...0|U|0...0> of the 56-qubit 7x8 grid
 circuit of depth 16 (fSim couplers, seed 505) along its stored searched tree.
-Its intermediates need slicing to fit one GPU (2^18 slices of at most
+Its intermediates need slicing to fit one GPU (2^16 slices of at most
 2^33-entry intermediates); one timed step runs a fixed range of complete
 slices through tnc_execute, `value` counts the unsliced tree's flops for
 that share of the slices, and the time to the whole amplitude is projected
@@ -741,7 +741,7 @@ class SlicedGridWorkload:
         self.name = "grid-7x8-d16-amplitude"
         self.config = {"workload": self.name, "seed": 505, "qubits": 56, "depth": 16,
                        "tree": "stored search result (workloads/data/grid_7x8_d16.json: recursive multilevel "
-                               "bisection, subtree reconfiguration, slicing; seed 1)",
+                               f"bisection, subtree reconfiguration, slicing; seed {rec['search'].get('seed')})",
                        "sliced_modes": len(self.sliced), "slices": self.num_slices,
                        "slices_per_step": timed_slices, "max_intermediate_sliced": st["max_intermediate"],
                        "workspace_bytes": st["workspace_bytes"], "flop_per_slice": self.flops_slice,

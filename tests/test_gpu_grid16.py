@@ -1,6 +1,6 @@
 """The 56-qubit 7x8 grid at depth 16 on its stored tree and slicing, at full
 size (one slice has intermediates of up to 2^33 entries and a workspace of
-about 200 GiB).  Pinned by the monomial circuit of the same shape: one
+144 GiB).  Pinned by the monomial circuit of the same shape: one
 basis-state path carries the whole amplitude e^(i alpha), so the slice whose
 digits are that path's values of the sliced modes returns e^(i alpha) (to
 the complex64 tolerance) and every other slice returns exactly zero."""
