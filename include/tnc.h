@@ -111,6 +111,12 @@ typedef struct {
   int64_t slice_end;          /*   slice_begin <= sigma < slice_end (0 <= begin < end <= number of
                                    slices) and leaves their sum in `out`: partial sums that add up to
                                    the whole result, e.g. one range per process or per call */
+  int32_t fuse;               /* 1: where a long tensor absorbs a small one (16 or 32 entries of
+                                 K, as many outputs) and the product is reduced at once against
+                                 another such small tensor, both steps run in one pass over the
+                                 long operand and the first product is never stored (complex64,
+                                 exact, lifetime order, every extent a power of two, long side
+                                 >= 2^16 rows).  0: every step runs on its own. */
 } tnc_plan_options;
 
 /* Arithmetic of the GEMM-class steps of a complex64 plan.  EXACT: FP32
@@ -157,6 +163,7 @@ typedef struct {
   uint64_t header_bytes;         /* workspace prefix holding kernel descriptors */
   uint64_t arena_bytes;          /* arena high-water mark */
   uint64_t workspace_bytes;      /* header_bytes + arena_bytes */
+  int32_t fused_pairs;           /* step pairs run as one pass (tnc_plan_options.fuse) */
 } tnc_plan_stats;
 
 tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats);
@@ -166,8 +173,8 @@ tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats);
 tnc_status tnc_plan_tensor_order(tnc_plan_t plan, int32_t id, int32_t *modes, int32_t *rank);
 
 /* Arena offset (bytes, from the arena start) of SSA tensor `id`: a staged
- * leaf copy or an intermediate.  UINT64_MAX: read in place (leaf) or written
- * to `out` (root). */
+ * leaf copy or an intermediate.  UINT64_MAX: read in place (leaf), written
+ * to `out` (root) or never stored (the first product of a fused pair). */
 tnc_status tnc_plan_tensor_offset(tnc_plan_t plan, int32_t id, uint64_t *offset);
 
 typedef struct {
@@ -184,6 +191,8 @@ typedef struct {
   uint64_t a_off, b_off, c_off;  /* arena offsets of the GEMM operands / product
                                     (UINT64_MAX: leaf in place or `out`) */
   uint64_t scratch_off, scratch_bytes;
+  int32_t fused_with;            /* the other step of its fused pair (both run in the second
+                                    step's launch), or -1 */
 } tnc_node_info;
 
 tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
@@ -234,12 +243,13 @@ typedef enum {
   TNC_OP_SKINNY = 2,        /* one step with a side of at most 16 */
   TNC_OP_GEMM = 3,          /* one matrix-core GEMM step */
   TNC_OP_COPY_TILED = 4,    /* one large permuting copy through LDS tiles */
-  TNC_OP_HEADER = 5         /* pointer table and descriptor upload */
+  TNC_OP_HEADER = 5,        /* pointer table and descriptor upload */
+  TNC_OP_FUSED = 6          /* one pass running a fused pair of steps (`step`: the second) */
 } tnc_op_kind;
 
 typedef struct {
   int32_t kind;             /* tnc_op_kind */
-  int32_t step;             /* the step of a SKINNY or GEMM launch, else -1 */
+  int32_t step;             /* the step of a SKINNY, GEMM or FUSED launch, else -1 */
   int32_t count;            /* copies or steps in the launch */
   int32_t launches;         /* times the launch ran */
   double ms;                /* its total time over those runs */

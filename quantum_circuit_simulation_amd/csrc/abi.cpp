@@ -47,6 +47,9 @@ tnc_status check(hipError_t e, hipStream_t stream, const char *what) {
   return TNC_OK;
 }
 
+static_assert(tnc::kFuseEntries == tnc::kFusePassEntries && tnc::kFuseMaxOuter == tnc::kFuseOuterMax,
+              "fused-pair pass size and table length agree between planner and kernel");
+
 const char *op_name(int kind) {
   switch (kind) {
     case tnc::OP_COPY: return "k_copy launch";
@@ -54,6 +57,7 @@ const char *op_name(int kind) {
     case tnc::OP_TINY_GROUP: return "k_tiny launch";
     case tnc::OP_SKINNY: return "k_skinny launch";
     case tnc::OP_GEMM: return "k_cgemm launch";
+    case tnc::OP_FUSED: return "k_fused2 launch";
   }
   return "launch";
 }
@@ -75,6 +79,7 @@ void tnc_plan_options_default(tnc_plan_options *o) {
   o->precision = TNC_PREC_EXACT;
   o->slice_begin = 0;
   o->slice_end = 0;
+  o->fuse = 1;
 }
 
 tnc_status tnc_plan(const tnc_network *net, const tnc_tree *tree, const tnc_plan_options *opts,
@@ -161,6 +166,7 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
   info->c_off = n.c_off;
   info->scratch_off = n.scratch_off;
   info->scratch_bytes = n.scratch_bytes;
+  info->fused_with = n.fuse_next >= 0 ? n.fuse_next : n.fuse_prev;
   return TNC_OK;
 }
 
@@ -346,6 +352,32 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           }
           break;
         }
+        case tnc::OP_FUSED: {
+          const tnc::FusedPair &f = p.fused[op.first];
+          const tnc::Node &n1 = p.nodes[f.first], &n2 = p.nodes[f.second];
+          tnc::Fused2Args fa{};
+          fa.X = reinterpret_cast<const float2 *>(operand(n1, f.long1));
+          fa.W1 = reinterpret_cast<const float2 *>(operand(n1, 1 - f.long1));
+          fa.W2 = reinterpret_cast<const float2 *>(operand(n2, 1 - f.long2));
+          fa.C = reinterpret_cast<float2 *>(resolve(tnc::kBufArena, n2.c_off));
+          fa.R = f.rows;
+          fa.K1 = f.k1;
+          fa.K2 = f.k2;
+          fa.nouter = f.nouter;
+          fa.wbit[0] = f.wbit[0];
+          fa.wbit[1] = f.wbit[1];
+          for (int i = 0; i < 8; ++i) {
+            fa.lrow[i] = f.lrow[i];
+            fa.hole[i] = f.hole[i];
+            fa.pos_row[i] = f.pos_row[i];
+            fa.pos_col[i] = f.pos_col[i];
+            fa.out_row[i] = f.out_row[i];
+            fa.out_col[i] = f.out_col[i];
+          }
+          for (int i = 0; i < tnc::kFuseMaxOuter && i < tnc::kFuseOuterMax; ++i) fa.out_pass[i] = f.out_pass[i];
+          e = tnc::launch_fused2(fa, stream);
+          break;
+        }
       }
       st = check(e, stream, op_name(op.kind));
       if (st != TNC_OK) return st;
@@ -440,8 +472,13 @@ tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *o
     rec[i].kind = op.kind == tnc::OP_COPY ? TNC_OP_COPY
                   : op.kind == tnc::OP_COPY_TILED ? TNC_OP_COPY_TILED
                   : op.kind == tnc::OP_TINY_GROUP ? TNC_OP_TINY_GROUP
-                  : op.kind == tnc::OP_SKINNY ? TNC_OP_SKINNY : TNC_OP_GEMM;
+                  : op.kind == tnc::OP_SKINNY ? TNC_OP_SKINNY
+                  : op.kind == tnc::OP_FUSED ? TNC_OP_FUSED : TNC_OP_GEMM;
     if (op.kind == tnc::OP_SKINNY || op.kind == tnc::OP_GEMM) rec[i].step = op.first;
+    if (op.kind == tnc::OP_FUSED) {
+      rec[i].step = p.fused[op.first].second;
+      rec[i].count = 2;
+    }
     if (op.kind == tnc::OP_COPY || op.kind == tnc::OP_TINY_GROUP) rec[i].count = op.count;
   }
   OpTimer tm;

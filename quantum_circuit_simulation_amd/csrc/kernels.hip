@@ -1147,6 +1147,311 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two chained skinny-class steps in one pass (k_fused2; see Fused2Args).
+//
+// A long tensor T absorbs a small W1 (K1 = S1 = 16 or 32 entries) and the
+// product T1 is reduced at once against another small W2 (K2 = S2).  With
+// every mode of extent 2 and the lifetime order of the operands, the modes
+// the second step reduces sit right above the first step's reduced modes in
+// T, so a block of consecutive rows of T yields whole rows of T1 for the
+// second step (the planner checks this per pair).  Each wave takes passes of
+// 1024 entries of T: it multiplies the block by W1 on the matrix cores (one
+// 32x32x2 MFMA per complex entry of K for 16 outputs, real and imaginary
+// parts in the two column halves; two MFMAs for 32 outputs, as in
+// k_skinny_mfma), writes the products into its LDS block at their places in
+// the second step's rows, multiplies those by W2 and stores T2 in address
+// order (the pass's fixed permutation, as in k_skinny_mfma).  T1 never
+// reaches HBM: the pair reads T and writes T2 once, half the bytes of the two
+// steps run one after the other.  The second operands sit in LDS, one float
+// per lane and K entry in the MFMA's column order.  Every LDS write of a pass
+// consumes MFMA results that need all of the block's earlier reads, and LDS
+// operations of one wave complete in order, so the block is reused in place
+// with no barrier; the next pass's loads are issued before this pass's
+// MFMAs.
+
+// second-operand table of one phase (K = S): lane l of K entry q at [q][l];
+// with K = 32 the imaginary-part columns follow at [K + q][l]
+template <int K>
+__device__ __forceinline__ void fused_btable(const float2 *W, float *bt, int tid) {
+  for (int e = tid; e < K * 64; e += 256) {
+    const int l = e >> 6, ln = e & 63, hh = ln >> 5, c = ln & 31;
+    if constexpr (K == 32) {
+      const float2 y = W[c * K + l];
+      bt[e] = hh ? -y.y : y.x;
+      bt[K * 64 + e] = hh ? y.x : y.y;
+    } else {
+      const float2 y = W[(c & 15) * K + l];
+      bt[e] = c >= 16 ? (hh ? y.x : y.y) : (hh ? -y.y : y.x);
+    }
+  }
+}
+
+// one phase: NB blocks of 32 rows [row][K / 2 + 1 entry pairs] times the
+// table; K = 16: acc holds (re | im) of 16 outputs, K = 32: acc re, acw im
+template <int K, int NB>
+__device__ __forceinline__ void fused_phase(const float4 *xb, const float *bt, int lane, f32x16 (&acc)[NB],
+                                            f32x16 (&acw)[NB]) {
+  constexpr int RS = K / 2 + 1;
+  const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[nb][r] = 0.f;
+      acw[nb][r] = 0.f;
+    }
+#pragma unroll
+  for (int q = 0; q < K / 2; ++q) {
+    const float b0 = bt[(2 * q) * 64 + lane], b1 = bt[(2 * q + 1) * 64 + lane];
+    float w0 = 0.f, w1 = 0.f;
+    if constexpr (K == 32) {
+      w0 = bt[(K + 2 * q) * 64 + lane];
+      w1 = bt[(K + 2 * q + 1) * 64 + lane];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float4 f = xb[(nb * 32 + l32) * RS + q];
+      const float x0 = h ? f.y : f.x, x1 = h ? f.w : f.z;
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b0, acc[nb], 0, 0, 0);
+      if constexpr (K == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, w0, acw[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, b1, acc[nb], 0, 0, 0);
+      if constexpr (K == 32) acw[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, w1, acw[nb], 0, 0, 0);
+    }
+  }
+}
+
+template <int K1, int K2>
+__global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
+  constexpr int E = kFuseEntries;
+  constexpr int ROWS1 = E / K1, ROWS2 = E / K2;
+  constexpr int NB1 = ROWS1 / 32, NB2 = ROWS2 / 32;
+  constexpr int RS1 = K1 / 2 + 1, RS2 = K2 / 2 + 1;  // 16-byte units per LDS row, one pad
+  constexpr int SP = K2 + 1;                         // staged products: complex entries per row
+  constexpr int W1F = ROWS1 * RS1, W2F = ROWS2 * RS2, W3F = (ROWS2 * SP + 1) / 2;
+  constexpr int WB = W1F > W2F ? (W1F > W3F ? W1F : W3F) : (W2F > W3F ? W2F : W3F);
+  constexpr int LPT = E / 2 / 64;  // 16-byte loads per lane per pass
+  constexpr int JB2 = K2 == 32 ? 5 : 4, LB2 = 10 - JB2;
+  constexpr int LKH = K1 == 32 ? 4 : 3;  // log2(K1 / 2)
+  constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
+  constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
+  constexpr int BT1 = (K1 == 32 ? 2 : 1) * K1 * 64, BT2 = (K2 == 32 ? 2 : 1) * K2 * 64;
+  static_assert((1 << LB1) == ROWS1 && NB1 >= 1 && NB2 >= 1 && 8 * WB < 65536, "fused block layout");
+  static_assert(kFuseMaxOuter % 6 == 0, "pass-index chunks");
+  __shared__ float4 buf[4][WB];
+  __shared__ float bt1[BT1], bt2[BT2];
+  __shared__ int64_t rowoff[ROWS2], coloff[K2];
+  __shared__ int64_t ochunk[kFuseMaxOuter / 6][64];  // round-index offsets, 6 bits per chunk
+  __shared__ int32_t bit_of[12];
+  __shared__ int32_t pairs_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+
+  fused_btable<K1>(a.W1, bt1, tid);
+  fused_btable<K2>(a.W2, bt2, tid);
+  for (int t = tid; t < ROWS2 + K2; t += 256) {
+    int64_t o = 0;
+    if (t < ROWS2) {
+#pragma unroll
+      for (int e = 0; e < LB2; ++e)
+        if ((t >> e) & 1) o += a.out_row[e];
+      rowoff[t] = o;
+    } else {
+      const int j = t - ROWS2;
+#pragma unroll
+      for (int c = 0; c < JB2; ++c)
+        if ((j >> c) & 1) o += a.out_col[c];
+      coloff[j] = o;
+    }
+  }
+  // a round's pass index is 4 round + wave: its bits 2 .. come from the round
+  for (int t = tid; t < kFuseMaxOuter / 6 * 64; t += 256) {
+    const int c = t >> 6, v = t & 63;
+    int64_t o = 0;
+#pragma unroll
+    for (int q = 2; q < kFuseMaxOuter; ++q)
+      if (((q - 2) / 6) == c && ((v >> ((q - 2) % 6)) & 1) && q < a.nouter) o += a.out_pass[q];
+    ochunk[c][v] = o;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // the round's entry bits (columns 0 .. JB2-1, rows JB2 .. 9, wave 10, 11) ordered by stride
+    int64_t st[12];
+    int pb[12];
+    for (int c = 0; c < JB2; ++c) {
+      st[c] = coloff[1 << c];
+      pb[c] = c;
+    }
+    for (int e = 0; e < LB2; ++e) {
+      st[JB2 + e] = rowoff[1 << e];
+      pb[JB2 + e] = JB2 + e;
+    }
+    st[10] = a.out_pass[0];
+    pb[10] = 10;
+    st[11] = a.out_pass[1];
+    pb[11] = 11;
+    for (int i = 1; i < 12; ++i)
+      for (int q = i; q > 0 && st[q] < st[q - 1]; --q) {
+        const int64_t ts = st[q];
+        st[q] = st[q - 1];
+        st[q - 1] = ts;
+        const int tp = pb[q];
+        pb[q] = pb[q - 1];
+        pb[q - 1] = tp;
+      }
+    for (int i = 0; i < 12; ++i) bit_of[i] = pb[i];
+    pairs_s = st[0] == 1;
+  }
+  __syncthreads();
+  // The workgroup stores its four passes together, in address order: thread
+  // tid's pair i is entries 2 (tid + 256 i), +1 of that order, the same in
+  // every round.  Its staged indices (wave w's block at 2 WB w complex
+  // entries) and offset within the round are kept in registers.
+  auto place = [&](int e, int *idx, int64_t *off) {
+    int p = 0;
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+      if ((e >> i) & 1) p |= 1 << bit_of[i];
+    const int w = p >> 10, t = (p >> JB2) & (ROWS2 - 1), c = p & (K2 - 1);
+    *idx = w * 2 * WB + t * SP + c;
+    *off = rowoff[t] + coloff[c] + ((w & 1) ? a.out_pass[0] : 0) + ((w & 2) ? a.out_pass[1] : 0);
+  };
+  int32_t sidx[NPT];
+  int64_t soff[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    int i0, i1;
+    int64_t o1;
+    place(2 * (tid + 256 * i), &i0, &soff[i]);
+    place(2 * (tid + 256 * i) + 1, &i1, &o1);
+    sidx[i] = i0 | (i1 << 16);
+  }
+
+  // place of a phase-1 product in the phase-2 block: lane part (its column
+  // and the row bit h) plus the row bits fixed by (nb, r)
+  const int j1 = K1 == 32 ? l32 : (l32 & 15);
+  int lane_pos = h ? a.pos_row[2] : 0;
+#pragma unroll
+  for (int c = 0; c < (K1 == 32 ? 5 : 4); ++c)
+    if ((j1 >> c) & 1) lane_pos += a.pos_col[c];
+  auto rpos = [&](int nb, int r) {
+    int p = 0;
+    if (r & 1) p += a.pos_row[0];
+    if (r & 2) p += a.pos_row[1];
+    if (r & 4) p += a.pos_row[3];
+    if (r & 8) p += a.pos_row[4];
+    if (nb & 1) p += a.pos_row[5];
+    return p;
+  };
+
+  const bool pairs = pairs_s && aligned16(a.C);
+  const int64_t nround = (a.R / ROWS1) >> 2;
+  // 16-byte entries as a vector type: values, not structs copied through memory
+  const f32x4 *X4 = (const f32x4 *)a.X;
+  float4 *xb = buf[wave];
+  f32x4 *xv = (f32x4 *)xb;
+  float *xf = (float *)xb;
+  const float2 *cw = (const float2 *)&buf[0][0];
+  f32x4 ld[LPT];
+  // lane l's load i reads entry pair l % (K1 / 2) of pass row rho = l / (K1 / 2)
+  // + i 64 / (K1 / 2); a pass row's X row spreads rho's bits over lrow
+  auto spread = [&](int rho) {
+    int64_t v = 0;
+#pragma unroll
+    for (int j = 0; j < LB1; ++j)
+      if ((rho >> j) & 1) v += int64_t(1) << a.lrow[j];
+    return v;
+  };
+  const int64_t lane_row = spread(lane >> LKH) + (((int64_t)(wave & 1)) << a.wbit[0]) +
+                           (((int64_t)(wave >> 1)) << a.wbit[1]);
+  auto load = [&](int64_t rnd) {
+    // the round's first X row: its index with zeros put in at the local and wave bits
+    uint64_t v = (uint64_t)rnd;
+#pragma unroll
+    for (int j = 0; j < LB1 + 2; ++j) {
+      const int p = a.hole[j];
+      v = ((v >> p) << (p + 1)) | (v & ((uint64_t(1) << p) - 1));
+    }
+    const f32x4 *src = X4 + ((int64_t)v + lane_row) * (K1 / 2) + (lane & (K1 / 2 - 1));
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) ld[i] = src[spread(i << (6 - LKH)) * (K1 / 2)];
+  };
+  int64_t rnd = blockIdx.x;
+  if (rnd < nround) load(rnd);
+  for (; rnd < nround; rnd += gridDim.x) {
+    // every wave has finished the last round's stores from the blocks
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int g = lane + 64 * i;
+      xv[(g / (K1 / 2)) * RS1 + g % (K1 / 2)] = ld[i];
+    }
+    if (rnd + gridDim.x < nround) load(rnd + gridDim.x);
+    {
+      f32x16 acc[NB1], acw[NB1];
+      fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
+      // the lane's base place, opaque per pass so that its 16 NB1 sums with
+      // the (uniform) row parts are formed here rather than held in registers
+      int lp = lane_pos;
+      asm volatile("" : "+v"(lp));
+      if constexpr (K1 == 32) {
+#pragma unroll
+        for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *(float2 *)&xf[2 * (lp + rpos(nb, r))] = make_float2(acc[nb][r], acw[nb][r]);
+      } else {
+        const int part = l32 >> 4;
+#pragma unroll
+        for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
+      }
+    }
+    {
+      f32x16 acc[NB2], acw[NB2];
+      fused_phase<K2, NB2>(xb, bt2, lane, acc, acw);
+      if constexpr (K2 == 32) {
+#pragma unroll
+        for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *(float2 *)&xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + l32) * 2] =
+                make_float2(acc[nb][r], acw[nb][r]);
+      } else {
+        const int j = l32 & 15, part = l32 >> 4;
+#pragma unroll
+        for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
+      }
+    }
+    int64_t base = 0;
+#pragma unroll
+    for (int c = 0; c < kFuseMaxOuter / 6; ++c) base += ochunk[c][(rnd >> (6 * c)) & 63];
+    // the four passes' products are staged
+    __syncthreads();
+    if (pairs) {
+      float2 v0[NPT], v1[NPT];
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        v0[i] = cw[sidx[i] & 0xffff];
+        v1[i] = cw[sidx[i] >> 16];
+      }
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+        *(float4 *)(a.C + base + soff[i]) = make_float4(v0[i].x, v0[i].y, v1[i].x, v1[i].y);
+    } else {
+      for (int e = tid; e < 4 * E; e += 256) {
+        int idx;
+        int64_t off;
+        place(e, &idx, &off);
+        a.C[base + off] = cw[idx];
+      }
+    }
+  }
+}
+
 // Thin GEMM-class steps: a short side of T = 32 NCB entries (32, 64 or 128)
 // against a long side of many rows, K a power of two from 16 to 64.  Such a
 // step sits near the ridge of the FP32 roofline (for T = K = 64 about 32
@@ -2985,6 +3290,28 @@ hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((k_cgemm_small<false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, stream, a, (uint32_t)bc);
   return hipGetLastError();
+}
+
+template <int K1, int K2>
+static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
+  const int64_t nround = (a.R / (kFuseEntries / K1)) / 4;  // four passes per workgroup round
+  int64_t blocks = nround;
+  const int64_t cap = 8 * (int64_t)num_cus();
+  if (blocks > cap) blocks = cap;
+  note_kernel("k_fused2<%d,%d>", K1, K2);
+  hipLaunchKernelGGL((k_fused2<K1, K2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
+  // the planner emits only pairs that meet these; anything else is refused
+  if ((a.K1 != 16 && a.K1 != 32) || (a.K2 != 16 && a.K2 != 32) || a.nouter < 0 || a.nouter > kFuseMaxOuter)
+    return hipErrorInvalidValue;
+  if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.W1 || !a.W2 || !a.C ||
+      ((uintptr_t)a.X & 15) != 0)
+    return hipErrorInvalidValue;
+  if (a.K1 == 16) return a.K2 == 16 ? run_fused2_k<16, 16>(a, stream) : run_fused2_k<16, 32>(a, stream);
+  return a.K2 == 16 ? run_fused2_k<32, 16>(a, stream) : run_fused2_k<32, 32>(a, stream);
 }
 
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {

@@ -39,6 +39,36 @@ constexpr int32_t kPrecBf16x3 = 1;  // TNC_PREC_BF16X3
 using StepArgs = StepArgsT<float2>;    // complex64
 using StepArgsZ = StepArgsT<double2>;  // complex128
 
+// Two chained complex64 steps run as one pass over the first step's long
+// operand (k_fused2): T1[i, j] = sum_l X[i, l] W1[j, l] (K1 = S1 entries),
+// then T2 = T1 W2 on the second step's layout of T1 (K2 = S2), without
+// writing T1.  Every mode has extent 2, so each place below is a sum over
+// the set bits of an index.  A pass is 1024 entries of X (1024 / K1 rows);
+// within it, phase-1 row bit b and column bit c put their product at
+// pos_row[b] + pos_col[c] (complex entries) of the phase-2 input block
+// [1024 / K2 rows][K2 + 2]; phase-2 row bit e and column bit c add
+// out_row[e] and out_col[c] to the offset in C, and bit q of the pass index
+// adds out_pass[q].  The pass's rows of X are those whose row bits lrow[0 ..
+// log2(1024 / K1) - 1] (ascending) vary.  A workgroup runs passes 4 r + w
+// (w = 0 .. 3, one per wave) together: bits 0 and 1 of the pass index set
+// row bits wbit[0] and wbit[1], and r fills the row bits outside hole[0 ..
+// log2(1024 / K1) + 1] (lrow and wbit, ascending) in ascending order.
+constexpr int kFuseEntries = 1024;
+constexpr int kFuseMaxOuter = 48;
+struct Fused2Args {
+  const float2 *X;   // row-major [R, K1]
+  const float2 *W1;  // row-major [K1, K1] (S1 rows)
+  const float2 *W2;  // row-major [K2, K2]
+  float2 *C;
+  int64_t R;         // a multiple of 1024 / K1; R / (1024 / K1) = 2^nouter passes
+  int32_t K1, K2;    // 16 or 32
+  int32_t nouter;
+  int32_t lrow[8], hole[8], wbit[2];
+  int32_t pos_row[8], pos_col[8];
+  int64_t out_row[8], out_col[8];
+  int64_t out_pass[kFuseMaxOuter];
+};
+
 // `z` selects complex128 entries (16 bytes) instead of complex64 (8 bytes).
 // Writes the pointer table [arena, out, leaves...] to ptab and copies
 // blob_bytes (a multiple of 16) of descriptors from pinned host memory to
@@ -55,6 +85,7 @@ hipError_t launch_tiny(const TinyDesc *descs, int32_t count, int64_t max_rs, con
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const StepArgs &a, hipStream_t stream);
 hipError_t launch_skinny_z(const StepArgsZ &a, hipStream_t stream);
+hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream);
 hipError_t launch_gemm_z(const StepArgsZ &a, hipStream_t stream);
 
 // Peak probes: `blocks` workgroups of 256 threads running `chains` (4 or 8)

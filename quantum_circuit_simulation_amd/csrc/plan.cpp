@@ -225,6 +225,143 @@ void make_tile(CopyOp *c) {
   c->tiled = 1;
 }
 
+// Offsets of the bits of an index over power-of-two runs (innermost run
+// last), lowest bit first; false if a run is not a power of two.
+bool bit_offsets(const std::vector<Run> &runs, std::vector<int64_t> *out) {
+  out->clear();
+  for (int q = (int)runs.size() - 1; q >= 0; --q) {
+    const int64_t sz = runs[q].size;
+    if (sz < 1 || (sz & (sz - 1)) != 0) return false;
+    for (int64_t b = 1; b < sz; b <<= 1) out->push_back(runs[q].stride * b);
+  }
+  return true;
+}
+
+int32_t log2_exact(int64_t v) {  // -1 unless v is a power of two
+  if (v < 1 || (v & (v - 1)) != 0) return -1;
+  int32_t b = 0;
+  while ((int64_t(1) << b) < v) ++b;
+  return b;
+}
+
+// Tables of a fused pair (s1's product is s2's long operand; see FusedPair).
+// False when the pair does not have the required form.
+bool make_fused_pair(const PlanImpl &p, int32_t s1, int32_t s2, FusedPair *f) {
+  const Node &a = p.nodes[s1], &b = p.nodes[s2];
+  // each step is taken with its long operand as the rows, whatever the
+  // orientation its own kernel would use
+  const int32_t la = a.m >= a.n ? 0 : 1, lb = b.m >= b.n ? 0 : 1;
+  const int64_t R1 = la == 0 ? a.m : a.n, S1 = la == 0 ? a.n : a.m;
+  const int64_t R2 = lb == 0 ? b.m : b.n, S2 = lb == 0 ? b.n : b.m;
+  const int64_t K1 = a.k, K2 = b.k;
+  if ((K1 != 16 && K1 != 32) || S1 != K1 || (K2 != 16 && K2 != 32) || S2 != K2) return false;
+  if ((lb == 0 ? b.lhs : b.rhs) != p.L + s1 || (lb == 0 ? b.copy_a : b.copy_b) != 0) return false;
+  // the oriented rows of a node are its N side when swapped, else its M side
+  const auto &a_rows = (la == 1) == (a.swap != 0) ? a.row_runs : a.col_runs;
+  const auto &a_cols = (la == 1) == (a.swap != 0) ? a.col_runs : a.row_runs;
+  const auto &b_rows = (lb == 1) == (b.swap != 0) ? b.row_runs : b.col_runs;
+  const auto &b_cols = (lb == 1) == (b.swap != 0) ? b.col_runs : b.row_runs;
+  const int64_t rows1 = kFusePassEntries / K1;
+  const int32_t lr1 = log2_exact(R1), lr2 = log2_exact(R2), lk1 = log2_exact(K1), lk2 = log2_exact(K2);
+  const int32_t lb1 = log2_exact(rows1), lb2 = log2_exact(kFusePassEntries / K2);
+  if (lr1 < 0 || lr2 < 0 || R1 < kFuseMinRows || lr2 != lr1 + lk1 - lk2) return false;
+  if (lr1 - lb1 > kFuseOuterMax) return false;
+  std::vector<int64_t> r1, c1, r2, c2;
+  if (!bit_offsets(a_rows, &r1) || !bit_offsets(a_cols, &c1) || !bit_offsets(b_rows, &r2) ||
+      !bit_offsets(b_cols, &c2))
+    return false;
+  if ((int)r1.size() != lr1 || (int)c1.size() != lk1 || (int)r2.size() != lr2 || (int)c2.size() != lk2) return false;
+  // bit of the product (step 2's long operand, [rows | K2]) that each index bit of step 1 sets
+  std::vector<int32_t> trow(lr1), tcol(lk1);
+  std::vector<char> seen(lr1 + lk1, 0);
+  for (int32_t i = 0; i < lr1 + lk1; ++i) {
+    const int32_t t = log2_exact(i < lr1 ? r1[i] : c1[i - lr1]);
+    if (t < 0 || t >= lr1 + lk1 || seen[t]) return false;
+    seen[t] = 1;
+    (i < lr1 ? trow[i] : tcol[i - lr1]) = t;
+  }
+  // The pass's local row bits (lb1 of them; its other rows bits count the
+  // passes): every row bit that lands in K2 (so that a pass holds whole rows
+  // of the second step), then the row bits with the smallest offsets in the
+  // second product, so that a pass's stores form the longest contiguous
+  // pieces.  Rows of X are K1 contiguous entries, so any choice loads whole
+  // rows.
+  std::vector<int32_t> local, outer;
+  for (int32_t i = 0; i < lr1; ++i)
+    if (trow[i] < lk2) local.push_back(i);
+  if ((int32_t)local.size() > lb1) return false;
+  {
+    std::vector<int32_t> cand;
+    for (int32_t i = 0; i < lr1; ++i)
+      if (trow[i] >= lk2) cand.push_back(i);
+    std::stable_sort(cand.begin(), cand.end(),
+                     [&](int32_t x, int32_t y) { return r2[trow[x] - lk2] < r2[trow[y] - lk2]; });
+    for (int32_t i : cand) ((int32_t)local.size() < lb1 ? local : outer).push_back(i);
+    std::sort(local.begin(), local.end());
+    std::sort(outer.begin(), outer.end());
+  }
+  // local bits landing in step 2's row index, ascending: the rows of the block
+  std::vector<int32_t> up;
+  for (int32_t i : local)
+    if (trow[i] >= lk2) up.push_back(trow[i] - lk2);
+  for (int32_t c = 0; c < lk1; ++c)
+    if (tcol[c] >= lk2) up.push_back(tcol[c] - lk2);
+  std::sort(up.begin(), up.end());
+  if ((int32_t)up.size() != lb2) return false;
+  auto pos = [&](int32_t t) -> int32_t {
+    if (t < lk2) return int32_t(1) << t;
+    const int32_t e = (int32_t)(std::lower_bound(up.begin(), up.end(), t - lk2) - up.begin());
+    return (int32_t)(K2 + 2) << e;  // block rows are K2 + 2 entries apart
+  };
+  f->first = s1;
+  f->second = s2;
+  f->long1 = la;
+  f->long2 = lb;
+  f->rows = R1;
+  f->k1 = (int32_t)K1;
+  f->k2 = (int32_t)K2;
+  f->nouter = lr1 - lb1;
+  for (int32_t i = 0; i < lb1; ++i) {
+    f->lrow[i] = local[i];
+    f->pos_row[i] = pos(trow[local[i]]);
+  }
+  for (int32_t c = 0; c < lk1; ++c) f->pos_col[c] = pos(tcol[c]);
+  for (int32_t e = 0; e < lb2; ++e) f->out_row[e] = r2[up[e]];
+  for (int32_t c = 0; c < lk2; ++c) f->out_col[c] = c2[c];
+  // a workgroup runs four passes at once (bits 0 and 1 of the pass index):
+  // they take the two outer row bits with the smallest offsets in the second
+  // product, so that the four passes' stores join into longer pieces; the
+  // rest count the workgroup's rounds, in ascending row-bit order
+  if ((int32_t)outer.size() < 2) return false;
+  {
+    std::vector<int32_t> by = outer;
+    std::stable_sort(by.begin(), by.end(),
+                     [&](int32_t x, int32_t y) { return r2[trow[x] - lk2] < r2[trow[y] - lk2]; });
+    f->wbit[0] = by[0];
+    f->wbit[1] = by[1];
+    std::vector<int32_t> rest, holes(local);
+    for (int32_t i : outer)
+      if (i != by[0] && i != by[1]) rest.push_back(i);
+    holes.push_back(by[0]);
+    holes.push_back(by[1]);
+    std::sort(holes.begin(), holes.end());
+    for (size_t j = 0; j < holes.size(); ++j) f->hole[j] = holes[j];
+    f->out_pass[0] = r2[trow[by[0]] - lk2];
+    f->out_pass[1] = r2[trow[by[1]] - lk2];
+    for (size_t q = 0; q < rest.size(); ++q) f->out_pass[2 + q] = r2[trow[rest[q]] - lk2];
+  }
+  // the kernel's writes must cover the second product exactly once: its
+  // offsets, one per bit, are the distinct powers of two below R2 S2
+  std::vector<int64_t> outs(f->out_pass, f->out_pass + f->nouter);
+  outs.insert(outs.end(), f->out_row, f->out_row + lb2);
+  outs.insert(outs.end(), f->out_col, f->out_col + lk2);
+  std::sort(outs.begin(), outs.end());
+  if ((int32_t)outs.size() != lr2 + lk2) return false;
+  for (size_t i = 0; i < outs.size(); ++i)
+    if (outs[i] != (int64_t(1) << i)) return false;
+  return true;
+}
+
 tnc_status validate(PlanImpl *p, const tnc_network *net, const tnc_tree *tree) {
   const int32_t nm = net->num_modes;
   if (nm < 0) return TNC_ERR_INVALID_NETWORK;
@@ -467,6 +604,32 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   }
   if (S == 0) p->staged_leaf.assign(L, 0);
 
+  // ---- fused pairs: a non-tiny step whose product is at once the long
+  // operand of another non-tiny step, both of the FusedPair form; pairs do
+  // not overlap and are taken in step order
+  p->fused.clear();
+  if (o.fuse && !naive && eb == 8 && o.precision == TNC_PREC_EXACT) {
+    std::vector<int32_t> consumer(T, -1);
+    for (int32_t s = 0; s < S; ++s) {
+      consumer[p->lhs[s]] = s;
+      consumer[p->rhs[s]] = s;
+    }
+    for (int32_t s1 = 0; s1 < S; ++s1) {
+      Node &a = p->nodes[s1];
+      if (a.cls == TNC_CLASS_TINY || a.splits > 1 || a.fuse_prev >= 0 || a.is_root) continue;
+      const int32_t s2 = consumer[L + s1];
+      if (s2 < 0) continue;
+      Node &b = p->nodes[s2];
+      if (b.cls == TNC_CLASS_TINY || b.splits > 1 || b.is_root) continue;
+      FusedPair f;
+      if (!make_fused_pair(*p, s1, s2, &f)) continue;
+      a.fuse_next = s2;
+      b.fuse_prev = s1;
+      b.fused_index = (int32_t)p->fused.size();
+      p->fused.push_back(f);
+    }
+  }
+
   // ---- launch groups: the tiny steps between two non-tiny steps (a segment)
   // run in dependency-level order, one group per level (split at max_group
   // members, list order inside a level); non-tiny steps are groups of their
@@ -535,24 +698,38 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
         }
       }
     }
+  // the first step of a fused pair keeps its operands until the pair's
+  // launch (the second step's group) and stores no product
+  std::vector<std::vector<std::pair<uint64_t, uint64_t>>> deferred(S);
   for (auto &members : p->groups) {
     std::vector<std::pair<uint64_t, uint64_t>> to_free;
     for (int32_t s : members) {
       Node &nd = p->nodes[s];
+      if (nd.fuse_prev >= 0) {
+        auto &d = deferred[nd.fuse_prev];
+        to_free.insert(to_free.end(), d.begin(), d.end());
+      }
+      auto &frees = nd.fuse_next >= 0 ? deferred[s] : to_free;
       for (int w = 0; w < 2; ++w) {
         int32_t t = w == 0 ? nd.lhs : nd.rhs;
         int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
         uint64_t &off = w == 0 ? nd.a_off : nd.b_off;
         if (early[s][w]) {
-          to_free.push_back({off, rbytes(elems[t])});
+          frees.push_back({off, rbytes(elems[t])});
         } else if (copy) {
           off = arena.alloc(rbytes(elems[t]));
-          to_free.push_back({off, rbytes(elems[t])});
+          frees.push_back({off, rbytes(elems[t])});
           if (t < L && !naive) p->tensor_off[t] = off;
+        } else if (nd.fuse_prev >= 0 && t == L + nd.fuse_prev) {
+          off = kNone;  // the pair's first product: never stored
         } else if (t >= L) {
           off = p->tensor_off[t];
-          to_free.push_back({off, rbytes(elems[t])});
+          frees.push_back({off, rbytes(elems[t])});
         }
+      }
+      if (nd.fuse_next >= 0) {
+        nd.c_off = kNone;
+        continue;
       }
       if (nd.is_root && !p->root_permute) {
         nd.c_off = kNone;
@@ -718,7 +895,9 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
       nd.runs_index = (int32_t)runs.size();
       for (auto &r : nd.row_runs) runs.push_back({r.size, r.stride});
       for (auto &r : nd.col_runs) runs.push_back({r.size, r.stride});
-      p->program.push_back({first.cls == TNC_CLASS_SKINNY ? OP_SKINNY : OP_GEMM, members[0], 1, 0});
+      if (nd.fuse_prev >= 0) p->program.push_back({OP_FUSED, nd.fused_index, 2, 0});
+      else if (nd.fuse_next < 0)  // a pair's first step runs in the second's launch
+        p->program.push_back({first.cls == TNC_CLASS_SKINNY ? OP_SKINNY : OP_GEMM, members[0], 1, 0});
     }
   }
   if (p->root_permute) {
@@ -820,6 +999,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   stt.header_bytes = p->header_bytes;
   stt.arena_bytes = p->arena_bytes;
   stt.workspace_bytes = p->header_bytes + p->arena_bytes;
+  stt.fused_pairs = (int32_t)p->fused.size();
   if (o.capacity_bytes > 0 && stt.workspace_bytes > o.capacity_bytes) return TNC_ERR_OUT_OF_MEMORY;
   return TNC_OK;
 }

@@ -69,13 +69,43 @@ struct Node {
   int32_t is_root = 0;
   // device run table location (entries into the blob's run array)
   int32_t runs_index = 0;
+  // fused pairs (see FusedPair): the first step's product is never stored;
+  // both steps run in the launch of the second
+  int32_t fuse_next = -1;    // first step: the second step of its pair
+  int32_t fuse_prev = -1;    // second step: the first step of its pair
+  int32_t fused_index = -1;  // second step: index into PlanImpl::fused
 };
 
-enum OpKind : int32_t { OP_COPY = 0, OP_TINY_GROUP = 1, OP_SKINNY = 2, OP_GEMM = 3, OP_COPY_TILED = 4 };
+// Two chained complex64 steps run as one pass over the first step's long
+// operand (k_fused2): a long tensor absorbs a small one (K1 = S1 = 16 or 32
+// entries) and the product is reduced at once against another small tensor
+// (K2 = S2).  Built when every index is a power of two and a pass of
+// kFusePassEntries entries of the long operand holds whole rows of the
+// second step; the tables give, per index bit, the place of an entry (see
+// Fused2Args in kernels.hpp).
+constexpr int64_t kFusePassEntries = 1024;
+constexpr int32_t kFuseOuterMax = 48;
+constexpr int64_t kFuseMinRows = int64_t(1) << 16;  // smaller steps are not worth a pair
+struct FusedPair {
+  int32_t first = -1, second = -1;
+  int32_t long1 = 0, long2 = 0;  // 0: the step's lhs is its long operand, 1: its rhs
+  int64_t rows = 0;          // rows of the first step's long operand
+  int32_t k1 = 0, k2 = 0, nouter = 0;
+  int32_t lrow[8] = {};      // the pass's local row bits of the long operand, ascending
+  int32_t wbit[2] = {};      // row bits set by bits 0, 1 of the pass index (a workgroup's four passes)
+  int32_t hole[8] = {};      // lrow and wbit, ascending: the rest count the workgroup's rounds
+  int32_t pos_row[8] = {}, pos_col[8] = {};
+  int64_t out_row[8] = {}, out_col[8] = {};
+  int64_t out_pass[kFuseOuterMax] = {};
+};
+
+enum OpKind : int32_t { OP_COPY = 0, OP_TINY_GROUP = 1, OP_SKINNY = 2, OP_GEMM = 3, OP_COPY_TILED = 4,
+                        OP_FUSED = 5 };
 
 struct Op {
   OpKind kind;
-  int32_t first;   // OP_COPY: first index into copy descriptors; TINY: first tiny desc; else node
+  int32_t first;   // OP_COPY: first index into copy descriptors; TINY: first tiny desc;
+                   // OP_FUSED: index into PlanImpl::fused; else node
   int32_t count;   // OP_COPY / OP_TINY_GROUP: descriptors in the launch
   int64_t max_count;  // OP_COPY: largest copy in the launch; OP_TINY_GROUP: largest member R S (grid sizing)
 };
@@ -99,6 +129,7 @@ struct PlanImpl {
   std::vector<std::vector<int32_t>> order;     // planned order per SSA tensor
   std::vector<std::vector<int32_t>> gemm_a, gemm_b;
   std::vector<Node> nodes;
+  std::vector<FusedPair> fused;
   std::vector<std::vector<int32_t>> groups;
   std::vector<uint64_t> tensor_off;
   std::vector<int32_t> staged_leaf;

@@ -52,7 +52,7 @@ class PlanOptions(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int), ("num_sliced", ctypes.c_int32), ("sliced_modes", P(ctypes.c_int32)),
                 ("align", ctypes.c_uint64), ("capacity_bytes", ctypes.c_uint64), ("tiny_mnk", ctypes.c_uint64),
                 ("max_group", ctypes.c_int32), ("precision", ctypes.c_int32), ("slice_begin", ctypes.c_int64),
-                ("slice_end", ctypes.c_int64)]
+                ("slice_end", ctypes.c_int64), ("fuse", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -63,7 +63,8 @@ class PlanStats(ctypes.Structure):
                 ("relayouts", ctypes.c_int32), ("root_permute", ctypes.c_int32), ("num_slices", ctypes.c_int64),
                 ("flops", ctypes.c_double), ("flops_unsliced", ctypes.c_double), ("bytes", ctypes.c_double),
                 ("max_intermediate", ctypes.c_uint64), ("header_bytes", ctypes.c_uint64),
-                ("arena_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+                ("arena_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64),
+                ("fused_pairs", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -76,7 +77,8 @@ class NodeInfo(ctypes.Structure):
                 ("inner_run", ctypes.c_int32), ("interleaved", ctypes.c_int32), ("copy_a", ctypes.c_int32),
                 ("copy_b", ctypes.c_int32), ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("a_off", ctypes.c_uint64), ("b_off", ctypes.c_uint64), ("c_off", ctypes.c_uint64),
-                ("scratch_off", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64)]
+                ("scratch_off", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64),
+                ("fused_with", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -110,7 +112,7 @@ class OpTiming(ctypes.Structure):
                 ("launches", ctypes.c_int32), ("ms", ctypes.c_double), ("kernel", ctypes.c_char * 64)]
 
 
-OP_KINDS = ["copy", "tiny_group", "skinny", "gemm", "copy_tiled", "header"]
+OP_KINDS = ["copy", "tiny_group", "skinny", "gemm", "copy_tiled", "header", "fused"]
 
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
@@ -199,7 +201,7 @@ class Plan:
     def __init__(self, extents, leaves: Sequence[Sequence[int]], out_modes: Sequence[int], lhs, rhs,
                  order: int = ORDER_LIFETIME, sliced: Sequence[int] = (), align: int = 256,
                  capacity_bytes: int = 0, tiny_mnk: int = 1 << 17, max_group: int = 256, dtype: int = TNC_C64,
-                 precision: int = 0, slice_range: Optional[Sequence[int]] = None):
+                 precision: int = 0, slice_range: Optional[Sequence[int]] = None, fuse: bool = True):
         lib = load_library()
         self._lib = lib
         self.num_leaves = len(leaves)
@@ -226,6 +228,7 @@ class Plan:
         opts.tiny_mnk = tiny_mnk
         opts.max_group = max_group
         opts.precision = precision
+        opts.fuse = 1 if fuse else 0
         if slice_range is not None:
             opts.slice_begin, opts.slice_end = int(slice_range[0]), int(slice_range[1])
         h = ctypes.c_void_p()

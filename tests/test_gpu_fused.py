@@ -1,0 +1,93 @@
+"""Fused pairs of steps (k_fused2): a long tensor T absorbs a small W1 (16 or
+32 entries of K, as many outputs) and the product is reduced at once
+against another small W2, in one pass over T.  Every output entry of the
+whole contraction against the oracle, for every (K1, K2) in {16, 32}^2, with
+the second step reducing 0 .. all of the first step's new modes, random
+declared orders and output orders (so the pair's product lands in many
+layouts), the innermost output mode local to a pass (16-byte pair stores)
+or not (single stores), a sliced run, and the same plans with fusion off.
+|g - r| <= 1e-4 * max(|r|, rms(r))."""
+
+import numpy as np
+import pytest
+
+from tests.test_gpu_skinny_mfma import _check
+from workloads.network import Network, Tree
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _cn(rng, shape):
+    return ((rng.standard_normal(shape) + 1j * rng.standard_normal(shape)) / np.sqrt(2)).astype(np.complex64)
+
+
+def chain_network(k1, k2, v, log_rows, last, seed, permuted=True):
+    """T (outer modes O, A, K1) absorbs W1 (K1 -> S1, 2^k1 x 2^k1), the
+    product is reduced against W2 over K2 = v modes of S1 plus the k2 - v
+    modes A of T (K2 -> S2), and a last step contracts one mode of the pair's
+    product with a vector V (an outer mode for last = "o", a mode of S2 for
+    last = "s"), so that the pair's product is not the root.  All extents 2;
+    T has 2^log_rows rows of K1 entries."""
+    rng = np.random.default_rng(seed)
+    n_outer = log_rows - (k2 - v)
+    assert n_outer >= 2
+    labels = iter(range(1000))
+    O = [next(labels) for _ in range(n_outer)]
+    K1 = [next(labels) for _ in range(k1)]
+    S1 = [next(labels) for _ in range(k1)]
+    A = [next(labels) for _ in range(k2 - v)]
+    S2 = [next(labels) for _ in range(k2)]
+    K2 = S1[:v] + A
+    vmode = O[0] if last == "o" else S2[0]
+    t_modes, w1_modes, w2_modes = O + A + K1, S1 + K1, S2 + K2
+    out = [x for x in O + S1[v:] + S2 if x != vmode]
+    if permuted:
+        t_modes, w1_modes, w2_modes, out = (list(rng.permutation(m)) for m in (t_modes, w1_modes, w2_modes, out))
+    n = next(labels)
+    ext = np.full(n, 2, dtype=np.int64)
+    leaves = [t_modes, w1_modes, w2_modes, [vmode]]
+    data = [_cn(rng, [2] * len(l)) for l in leaves]
+    net = Network(ext, [list(map(int, l)) for l in leaves], [int(x) for x in out], data,
+                  name=f"chain_k{k1}_{k2}_v{v}_r{log_rows}_{last}")
+    return net, Tree([0, 4, 5], [1, 2, 3])
+
+
+# (log2 K1, log2 K2, shared modes v, log2 rows of T, last-step mode)
+CASES = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "s"), (4, 4, 4, 16, "o"), (4, 5, 2, 17, "s"), (5, 4, 1, 16, "s"),
+         (5, 5, 3, 17, "o"), (4, 5, 0, 16, "o"), (5, 5, 0, 18, "s"), (5, 4, 4, 17, "o"), (4, 4, 1, 19, "s")]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "k{}_{}_v{}_r{}_{}".format(*c))
+def test_fused_pair_matches_oracle(case):
+    net, tree = chain_network(*case, seed=700 + sum(case[:4]))
+    ks = _check(net, tree, expect_kernel="k_fused2", kind="fused")
+    assert len(ks) == 1, ks
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[5]], ids=["k16_16", "k16_32", "k32_32"])
+def test_aligned_orders(case):
+    net, tree = chain_network(*case, seed=31, permuted=False)
+    _check(net, tree, expect_kernel="k_fused2", kind="fused")
+
+
+def test_fuse_off_runs_the_steps_alone():
+    import quantum_circuit_simulation_amd as qa
+    net, tree = chain_network(4, 4, 2, 17, "s", seed=5)
+    assert qa.Plan.from_network(net, tree).stats()["fused_pairs"] == 1
+    assert qa.Plan.from_network(net, tree, fuse=False).stats()["fused_pairs"] == 0
+    assert _check(net, tree, kind="fused", fuse=False) == []
+
+
+def test_sliced_pair():
+    net, tree = chain_network(4, 4, 1, 18, "o", seed=77)
+    # fix the closed outer mode of T (the last step's): T is staged per slice,
+    # the pair runs on half the rows and the root accumulates the two slices
+    _check(net, tree, expect_kernel="k_fused2", kind="fused", sliced=[net.leaves[3][0]])
