@@ -21,8 +21,8 @@ ascending label order).  The page describes this as the emergent property of
 the reverse pass (section 1.4, the paragraph after the algorithm).
 
 Everything else (node classes, operand orientation, output runs, split-K,
-grouping and first-fit arena) is this project's own execution design; the
-rules are restated here from their definitions.
+grouping, fused pairs and first-fit arena) is this project's own execution
+design; the rules are restated here from their definitions.
 """
 
 from __future__ import annotations
@@ -42,6 +42,8 @@ CLASS_GEMM = 2
 SKINNY_MAX_SIDE = 16        # skinny when the smaller of m, n is at most this
 GEMM_NOMINAL_TILE = 128     # nominal tile edge used only by the split-K rule
 EARLY_STAGE_MAX = 1 << 16   # staged leaves up to this many entries are copied before the first group
+FUSE_PASS_ENTRIES = 1024    # entries of the long operand in one pass of a fused pair
+FUSE_MIN_ROWS = 1 << 16     # fused pairs need at least this many rows of the long operand
 NONE = (1 << 64) - 1        # "not in the arena"
 
 
@@ -235,6 +237,12 @@ class Node:
     c_off: int = NONE        # NONE = written to the output buffer
     scratch_off: int = NONE
     scratch_bytes: int = 0
+    fuse_next: int = -1      # first step of a fused pair: the second step
+    fuse_prev: int = -1      # second step of a fused pair: the first step
+
+    @property
+    def fused_with(self) -> int:
+        return self.fuse_next if self.fuse_next >= 0 else self.fuse_prev
 
 
 @dataclass
@@ -254,6 +262,7 @@ class Plan:
     bytes: int
     max_elems: int
     num_slices: int
+    fused: List[tuple] = field(default_factory=list)   # (first, second) step pairs
 
 
 def _runs(c_order, ext, row_set):
@@ -332,8 +341,69 @@ class _Arena:
         self.free = merged
 
 
+def _is_pow2(v: int) -> bool:
+    return v >= 1 and (v & (v - 1)) == 0
+
+
+def _log2(v: int) -> int:
+    return v.bit_length() - 1
+
+
+def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
+    """Pairs (s1, s2) of steps run as one pass: a long tensor T absorbs a small
+    one (K = S = 16 or 32 entries) and the product T1 is at once the long
+    operand of the next step, which reduces it against another small tensor
+    (K = S = 16 or 32), with every extent of the modes involved a power of two,
+    T holding at least 2^16 rows, both steps outside the tiny class, neither
+    split over K nor the root, T1 read in place, and the modes of the second
+    step's K that T carries spanning at most 1024 / K1 index values (so that a
+    pass over 1024 entries of T yields whole rows of the second step).  Pairs
+    are taken in step order and do not overlap.  Complex64, lifetime order."""
+    if not fuse or policy != LIFETIME or eb != 8:
+        return []
+    consumer = {}
+    for nd in nodes:
+        consumer[nd.lhs] = nd.step
+        consumer[nd.rhs] = nd.step
+    pairs = []
+    taken = set()
+
+    def long_short(nd):
+        # (long operand, its rows, the short side) with lhs taken when m >= n
+        return (nd.lhs, nd.m, nd.n) if nd.m >= nd.n else (nd.rhs, nd.n, nd.m)
+
+    for a in nodes:
+        s1 = a.step
+        if a.cls == CLASS_TINY or a.splits > 1 or s1 in taken or (L + s1) not in consumer:
+            continue
+        s2 = consumer[L + s1]
+        b = nodes[s2]
+        if b.cls == CLASS_TINY or b.splits > 1 or s2 == len(nodes) - 1:
+            continue
+        t, r1, s1w = long_short(a)
+        t1, _, s2w = long_short(b)
+        if a.k not in (16, 32) or s1w != a.k or b.k not in (16, 32) or s2w != b.k:
+            continue
+        if t1 != L + s1 or (b.copy_a if t1 == b.lhs else b.copy_b):
+            continue
+        small1 = a.rhs if t == a.lhs else a.lhs
+        small2 = b.rhs if t1 == b.lhs else b.lhs
+        if not _is_pow2(r1) or r1 < FUSE_MIN_ROWS:
+            continue
+        if not all(_is_pow2(ext[x]) for u in (t, small1, small2) for x in sets[u]):
+            continue
+        # the second step's reduced modes that come from T, in index bits
+        k2_from_t = [x for x in sets[t] if x in sets[small2]]
+        if sum(_log2(ext[x]) for x in k2_from_t) > _log2(FUSE_PASS_ENTRIES // a.k):
+            continue
+        a.fuse_next, b.fuse_prev = s2, s1
+        taken.update((s1, s2))
+        pairs.append((s1, s2))
+    return pairs
+
+
 def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), align=256,
-              tiny_mnk=1 << 17, max_group=256, dtype=0) -> Plan:
+              tiny_mnk=1 << 17, max_group=256, dtype=0, fuse=True) -> Plan:
     """dtype 0: complex64 (8-byte entries), 1: complex128 (16-byte entries)."""
     eb = 16 if dtype == 1 else 8
     validate(extents, leaves, out_modes, lhs, rhs, sliced)
@@ -400,6 +470,8 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
             node.scratch_bytes = splits * R * Sx * eb
         nodes.append(node)
 
+    fused = fused_pairs(nodes, sets, ext, L, eb, policy, fuse)
+
     # launch groups: the tiny steps between two non-tiny steps (a segment)
     # run in dependency-level order, one group per level (split at max_group
     # members, list order inside a level); non-tiny steps are groups of their
@@ -460,22 +532,33 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
                     if policy == LIFETIME:
                         tensor_off[t] = off
                     early.add((s, which))
+    # a fused pair's first step keeps its operands until the pair's launch
+    # (the second step's group) and never stores its product
+    deferred = {}
     for members in groups:
         to_free = []
         for s in members:
             nd = nodes[s]
+            if nd.fuse_prev >= 0:
+                to_free.extend(deferred.pop(nd.fuse_prev))
+            frees = deferred.setdefault(s, []) if nd.fuse_next >= 0 else to_free
             for which, t in (("a", nd.lhs), ("b", nd.rhs)):
                 if (s, which) in early:
-                    to_free.append((getattr(nd, which + "_off"), rbytes(elems_of[t])))
+                    frees.append((getattr(nd, which + "_off"), rbytes(elems_of[t])))
                 elif getattr(nd, "copy_" + which):
                     off = arena.alloc(rbytes(elems_of[t]))
-                    to_free.append((off, rbytes(elems_of[t])))
+                    frees.append((off, rbytes(elems_of[t])))
                     if t < L and policy == LIFETIME:
                         tensor_off[t] = off
                     setattr(nd, which + "_off", off)
+                elif nd.fuse_prev >= 0 and t == L + nd.fuse_prev:
+                    setattr(nd, which + "_off", NONE)
                 elif t >= L:
                     setattr(nd, which + "_off", tensor_off[t])
-                    to_free.append((tensor_off[t], rbytes(elems_of[t])))
+                    frees.append((tensor_off[t], rbytes(elems_of[t])))
+            if nd.fuse_next >= 0:
+                nd.c_off = NONE
+                continue
             if nd.out == root and not root_permute:
                 nd.c_off = NONE
             else:
@@ -494,4 +577,4 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
                 arena_bytes=arena.peak, tensor_off=tensor_off, root_permute=root_permute,
                 root_off=root_off, staged_leaf=staged_leaf, flops=flops, flops_unsliced=flops_u,
                 bytes=nbytes, max_elems=max_elems,
-                num_slices=_prod(extents, sliced) if sliced else 1)
+                num_slices=_prod(extents, sliced) if sliced else 1, fused=fused)

@@ -29,7 +29,7 @@ def _cn(rng, shape):
     return ((rng.standard_normal(shape) + 1j * rng.standard_normal(shape)) / np.sqrt(2)).astype(np.complex64)
 
 
-def chain_network(k1, k2, v, log_rows, last, seed, permuted=True):
+def chain_network(k1, k2, v, log_rows, last, seed, permuted=True, with_data=True):
     """T (outer modes O, A, K1) absorbs W1 (K1 -> S1, 2^k1 x 2^k1), the
     product is reduced against W2 over K2 = v modes of S1 plus the k2 - v
     modes A of T (K2 -> S2), and a last step contracts one mode of the pair's
@@ -54,7 +54,7 @@ def chain_network(k1, k2, v, log_rows, last, seed, permuted=True):
     n = next(labels)
     ext = np.full(n, 2, dtype=np.int64)
     leaves = [t_modes, w1_modes, w2_modes, [vmode]]
-    data = [_cn(rng, [2] * len(l)) for l in leaves]
+    data = [_cn(rng, [2] * len(l)) for l in leaves] if with_data else None
     net = Network(ext, [list(map(int, l)) for l in leaves], [int(x) for x in out], data,
                   name=f"chain_k{k1}_{k2}_v{v}_r{log_rows}_{last}")
     return net, Tree([0, 4, 5], [1, 2, 3])

@@ -37,10 +37,11 @@ def _compare(plan_lib, ref, L, S):
         r = ref.nodes[s]
         got = (n["lhs"], n["rhs"], n["out"], n["m"], n["n"], n["k"], n["kernel_class"], n["swap"], n["group"],
                n["splits"], n["row_runs"], n["col_runs"], n["inner_run"], n["interleaved"], n["copy_a"],
-               n["copy_b"], n["a_off"], n["b_off"], n["c_off"], n["scratch_off"], n["scratch_bytes"])
+               n["copy_b"], n["a_off"], n["b_off"], n["c_off"], n["scratch_off"], n["scratch_bytes"],
+               n["fused_with"])
         exp = (r.lhs, r.rhs, r.out, r.m, r.n, r.k, r.cls, r.swap, r.group, r.splits, len(r.row_runs),
                len(r.col_runs), r.inner_run, r.interleaved, r.copy_a, r.copy_b, r.a_off, r.b_off, r.c_off,
-               r.scratch_off, r.scratch_bytes)
+               r.scratch_off, r.scratch_bytes, r.fused_with)
         assert got == exp, ("node", s, got, exp)
     st = plan_lib.stats()
     assert st["arena_bytes"] == ref.arena_bytes
@@ -51,13 +52,14 @@ def _compare(plan_lib, ref, L, S):
     assert st["flops"] == float(ref.flops)
     assert st["num_slices"] == ref.num_slices
     assert st["workspace_bytes"] == st["header_bytes"] + st["arena_bytes"]
+    assert st["fused_pairs"] == len(ref.fused)
 
 
-def _check(net, tree, policy=P.LIFETIME, sliced=(), tiny_mnk=1 << 15, max_group=256, dtype=0):
+def _check(net, tree, policy=P.LIFETIME, sliced=(), tiny_mnk=1 << 15, max_group=256, dtype=0, fuse=True):
     ref = P.make_plan(net.extents, net.leaves, net.out_modes, tree.lhs, tree.rhs, policy=policy, sliced=sliced,
-                      tiny_mnk=tiny_mnk, max_group=max_group, dtype=dtype)
+                      tiny_mnk=tiny_mnk, max_group=max_group, dtype=dtype, fuse=fuse)
     lib = qa.Plan.from_network(net, tree, order=policy, sliced=sliced, tiny_mnk=tiny_mnk, max_group=max_group,
-                               dtype=dtype)
+                               dtype=dtype, fuse=fuse)
     _compare(lib, ref, net.num_leaves, tree.num_steps)
     return lib, ref
 
@@ -91,6 +93,36 @@ def test_config_plans_match_oracle(policy):
         for perm in (False, True):
             net, tree = sweep.network(case["logm"], case["logn"], case["logk"], permuted=perm, seed=case["seed"])
             _check(net, tree, policy)
+
+
+# (log2 K1, log2 K2, shared modes, log2 rows, last-step mode): chained
+# small-operand steps that the planner runs as fused pairs
+CHAINS = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "o"), (4, 5, 2, 17, "s"), (5, 4, 1, 16, "s"), (5, 5, 3, 17, "o"),
+          (4, 4, 4, 18, "s"), (5, 4, 0, 16, "o"), (4, 4, 1, 15, "s"), (4, 5, 0, 17, "s")]
+
+
+@pytest.mark.parametrize("case", CHAINS, ids=lambda c: "k{}_{}_v{}_r{}_{}".format(*c))
+@pytest.mark.parametrize("permuted", [False, True], ids=["aligned", "permuted"])
+def test_fused_pair_plans_match_oracle(case, permuted):
+    from tests.test_gpu_fused import chain_network
+    net, tree = chain_network(*case, seed=40 + sum(case[:4]), permuted=permuted, with_data=False)
+    lib, ref = _check(net, tree)
+    # 2^15 rows is below the fusing threshold; the others pair their first two steps
+    assert ref.fused == ([] if case[3] < 16 else [(0, 1)])
+    if ref.fused:
+        assert lib.tensor_offset(net.num_leaves) == P.NONE  # the first product is never stored
+    _check(net, tree, fuse=False)
+    # fixing the closed outer mode of T keeps the pair on half the rows
+    if case[4] == "o":
+        lib, ref = _check(net, tree, sliced=[net.leaves[3][0]])
+        assert ref.fused == ([] if case[3] - 1 < 16 else [(0, 1)])
+
+
+def test_grid_depth16_plan_with_fused_pairs_matches_oracle():
+    net = circuits.grid_fsim(7, 8, 16, 505).to_network()
+    tree, sl, _ = trees.stored_tree("grid_7x8_d16", net)
+    lib, ref = _check(net, tree, sliced=sl)
+    assert len(ref.fused) == 6
 
 
 def test_sliced_circuit_plan_matches_oracle():
