@@ -1022,7 +1022,7 @@ def main():
         PLAN_KW["fuse"] = False
     if args.ingest_pmc:
         kernel = args.kernel or ("k_cgemm_tile<128,128>" if args.workload == "sweep" else args.workload)
-        cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.split('_')[0].lower()} -o {c.split('_')[0].lower()} -f csv "
+        cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/all/pmc_{c} -o pmc -f csv "
                 f"-- python3 -u bench.py --workload {args.workload} --calibrate-copy --steps 1 --warmup 0 "
                 f"--no-cpu-baseline" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         print(ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, kernel, cmds))
