@@ -197,6 +197,34 @@ typedef struct {
 
 tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
 
+/* A fused pair's pass tables (index 0 .. fused_pairs - 1, in step order),
+ * for inspection and host-side checks.  The pair runs steps `first` and
+ * `second`; their long operands are lhs (long = 0) or rhs (1), and the
+ * second step's long operand is the first step's product.  Every index is a
+ * sum of one offset per set bit.  A pass takes 1024 entries of the first
+ * long operand X (row-major [rows, k1]): its local row rho (0 .. 1024/k1 - 1)
+ * is X row spread(rho) + round part + wave part, where spread puts bit j of
+ * rho at row bit lrow[j]; the workgroup's four passes w = 0 .. 3 add
+ * (w & 1) << wbit[0] and (w >> 1) << wbit[1]; a round index fills the row
+ * bits outside hole[] (lrow and wbit, ascending) in ascending order.  The
+ * first product of (rho, column j) goes to complex entry sum pos_row[bits of
+ * rho] + sum pos_col[bits of j] of the block [1024/k2 rows][k2 + 2]; the
+ * second product of block row l and column j2 goes to the second product's
+ * offset sum out_row[bits of l] + sum out_col[bits of j2] + (w & 1) out_pass[0]
+ * + (w >> 1) out_pass[1] + sum out_pass[2 + q] over bits q of the round.
+ * Errors: INVALID_ARG (no such pair). */
+typedef struct {
+  int32_t first, second, long1, long2;
+  int64_t rows;
+  int32_t k1, k2, nouter;
+  int32_t lrow[8], hole[8], wbit[2];
+  int32_t pos_row[8], pos_col[8];
+  int64_t out_row[8], out_col[8];
+  int64_t out_pass[48];
+} tnc_fused_info;
+
+tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info);
+
 /*
  * Run the plan.
  *   leaves[L]   device pointers to the leaf buffers (declared orders)

@@ -170,6 +170,35 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
   return TNC_OK;
 }
 
+tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info) {
+  if (!plan || !info) return TNC_ERR_INVALID_ARG;
+  const auto &p = plan->impl;
+  if (index < 0 || index >= (int32_t)p.fused.size()) return TNC_ERR_INVALID_ARG;
+  const tnc::FusedPair &f = p.fused[index];
+  std::memset(info, 0, sizeof(*info));
+  info->first = f.first;
+  info->second = f.second;
+  info->long1 = f.long1;
+  info->long2 = f.long2;
+  info->rows = f.rows;
+  info->k1 = f.k1;
+  info->k2 = f.k2;
+  info->nouter = f.nouter;
+  for (int i = 0; i < 8; ++i) {
+    info->lrow[i] = f.lrow[i];
+    info->hole[i] = f.hole[i];
+    info->pos_row[i] = f.pos_row[i];
+    info->pos_col[i] = f.pos_col[i];
+    info->out_row[i] = f.out_row[i];
+    info->out_col[i] = f.out_col[i];
+  }
+  info->wbit[0] = f.wbit[0];
+  info->wbit[1] = f.wbit[1];
+  static_assert(sizeof(info->out_pass) / sizeof(info->out_pass[0]) == tnc::kFuseOuterMax, "out_pass length");
+  for (int i = 0; i < tnc::kFuseOuterMax; ++i) info->out_pass[i] = f.out_pass[i];
+  return TNC_OK;
+}
+
 }  // extern "C"
 
 namespace {

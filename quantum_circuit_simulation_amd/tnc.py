@@ -84,6 +84,18 @@ class NodeInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class FusedInfo(ctypes.Structure):
+    _fields_ = [("first", ctypes.c_int32), ("second", ctypes.c_int32), ("long1", ctypes.c_int32),
+                ("long2", ctypes.c_int32), ("rows", ctypes.c_int64), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
+                ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 8), ("hole", ctypes.c_int32 * 8),
+                ("wbit", ctypes.c_int32 * 2), ("pos_row", ctypes.c_int32 * 8), ("pos_col", ctypes.c_int32 * 8),
+                ("out_row", ctypes.c_int64 * 8), ("out_col", ctypes.c_int64 * 8), ("out_pass", ctypes.c_int64 * 48)]
+
+    def as_dict(self):
+        return {name: (list(getattr(self, name)) if isinstance(getattr(self, name), ctypes.Array)
+                       else getattr(self, name)) for name, _ in self._fields_}
+
+
 class DistOptions(ctypes.Structure):
     _fields_ = [("num_gpus", ctypes.c_int32), ("threshold_bytes", ctypes.c_uint64),
                 ("hbm_bytes_per_s", ctypes.c_double), ("flops_per_s", ctypes.c_double),
@@ -117,7 +129,7 @@ OP_KINDS = ["copy", "tiny_group", "skinny", "gemm", "copy_tiled", "header", "fus
 EXPORTS = ["tnc_plan_options_default", "tnc_plan", "tnc_plan_destroy", "tnc_plan_workspace_bytes",
            "tnc_plan_stats_get", "tnc_plan_tensor_order", "tnc_plan_tensor_offset", "tnc_plan_node",
            "tnc_execute", "tnc_status_string", "tnc_last_error", "tnc_dist_options_default",
-           "tnc_plan_distribute", "tnc_execute_noalloc", "tnc_execute_timed", "tnc_probe_peaks"]
+           "tnc_plan_distribute", "tnc_execute_noalloc", "tnc_execute_timed", "tnc_probe_peaks", "tnc_plan_fused"]
 NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # TNC_NOALLOC_MAX_WORKSPACE_BYTES
 
 _lib = None
@@ -153,6 +165,8 @@ def load_library(path: str = LIB_PATH):
     lib.tnc_plan_tensor_offset.restype = ctypes.c_int
     lib.tnc_plan_node.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(NodeInfo)]
     lib.tnc_plan_node.restype = ctypes.c_int
+    lib.tnc_plan_fused.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(FusedInfo)]
+    lib.tnc_plan_fused.restype = ctypes.c_int
     lib.tnc_execute.argtypes = [ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_uint64, ctypes.c_void_p]
     lib.tnc_execute.restype = ctypes.c_int
@@ -280,6 +294,12 @@ class Plan:
         n = NodeInfo()
         _check(self._lib.tnc_plan_node(self._h, step, ctypes.byref(n)), "tnc_plan_node")
         return n.as_dict()
+
+    def fused(self, index: int) -> dict:
+        """Pass tables of fused pair `index` (tnc_plan_fused)."""
+        f = FusedInfo()
+        _check(self._lib.tnc_plan_fused(self._h, index, ctypes.byref(f)), "tnc_plan_fused")
+        return f.as_dict()
 
     def distribute(self, **overrides):
         """Distribution schedule over P GPUs (tnc_plan_distribute).  Keyword
