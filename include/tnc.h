@@ -227,7 +227,9 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info);
 
 /*
  * Run the plan.
- *   leaves[L]   device pointers to the leaf buffers (declared orders)
+ *   leaves[L]   device pointers to the leaf buffers (declared orders); a leaf
+ *               that a fused pair reads in place as its long operand must be
+ *               16-byte aligned (INVALID_ARG otherwise, before any launch)
  *   out         device pointer, prod(out extents) entries of the plan's dtype,
  *               overwritten
  *   workspace   device pointer, >= tnc_plan_workspace_bytes, 256-byte aligned

@@ -239,6 +239,18 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
   (void)hipGetLastError();
   for (int32_t l = 0; l < p.L; ++l)
     if (!leaves[l]) return TNC_ERR_INVALID_ARG;
+  // a fused pair reads its long operand with 16-byte loads; a leaf read in
+  // place must be 16-byte aligned (checked before anything is enqueued)
+  for (const auto &f : p.fused) {
+    const tnc::Node &n1 = p.nodes[f.first];
+    const int32_t t = f.long1 == 0 ? n1.lhs : n1.rhs;
+    const int32_t copied = f.long1 == 0 ? n1.copy_a : n1.copy_b;
+    if (t < p.L && !copied && (reinterpret_cast<uintptr_t>(leaves[t]) & 15) != 0) {
+      g_last_error = "leaf " + std::to_string(t) + " is the long operand of a fused pair and must be 16-byte "
+                     "aligned (or plan with fuse = 0)";
+      return TNC_ERR_INVALID_ARG;
+    }
+  }
   if (workspace_bytes < p.stats.workspace_bytes) return TNC_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return TNC_ERR_INVALID_ARG;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);

@@ -177,6 +177,19 @@ def test_execute_rejects_small_workspace_without_touching_the_gpu():
     assert e.value.name == "TNC_ERR_INVALID_ARG"
 
 
+def test_execute_rejects_an_unaligned_fused_leaf_without_touching_the_gpu():
+    from tests.test_gpu_fused import chain_network
+    net, tree = chain_network(4, 4, 2, 16, "s", seed=2, permuted=False, with_data=False)
+    plan = qa.Plan.from_network(net, tree)
+    assert plan.stats()["fused_pairs"] == 1 and plan.node(0)["copy_a"] == 0  # leaf 0 read in place
+    need = plan.workspace_bytes
+    ptrs = [1 << 20] * net.num_leaves
+    ptrs[0] += 8
+    with pytest.raises(tnc.TncError) as e:
+        plan.execute_ptrs(ptrs, 1 << 20, 1 << 24, need, 0)
+    assert e.value.name == "TNC_ERR_INVALID_ARG" and "16-byte" in str(e.value)
+
+
 def test_complex128_plan_doubles_entry_bytes():
     net = lattice.peps(4, 4, 1)
     tree = lattice.row_major_tree(4)
