@@ -111,9 +111,10 @@ typedef struct {
   int64_t slice_end;          /*   slice_begin <= sigma < slice_end (0 <= begin < end <= number of
                                    slices) and leaves their sum in `out`: partial sums that add up to
                                    the whole result, e.g. one range per process or per call */
-  int32_t fuse;               /* 1: where a long tensor absorbs a small one (16 or 32 entries of
-                                 K, as many outputs) and the product is reduced at once against
-                                 another such small tensor, both steps run in one pass over the
+  int32_t fuse;               /* 1: where a long tensor absorbs a small one (4, 8, 16 or 32
+                                 entries of K, as many outputs) and the product is reduced at once
+                                 against another such small tensor (both K <= 8 or both >= 16),
+                                 both steps run in one pass over the
                                  long operand and the first product is never stored (complex64,
                                  exact, lifetime order, every extent a power of two, long side
                                  >= 2^16 rows).  0: every step runs on its own. */
@@ -217,7 +218,7 @@ typedef struct {
   int32_t first, second, long1, long2;
   int64_t rows;
   int32_t k1, k2, nouter;
-  int32_t lrow[8], hole[8], wbit[2];
+  int32_t lrow[8], hole[10], wbit[2];
   int32_t pos_row[8], pos_col[8];
   int64_t out_row[8], out_col[8];
   int64_t out_pass[48];

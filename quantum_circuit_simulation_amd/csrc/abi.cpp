@@ -184,9 +184,9 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info) 
   info->k1 = f.k1;
   info->k2 = f.k2;
   info->nouter = f.nouter;
+  for (int i = 0; i < 10; ++i) info->hole[i] = f.hole[i];
   for (int i = 0; i < 8; ++i) {
     info->lrow[i] = f.lrow[i];
-    info->hole[i] = f.hole[i];
     info->pos_row[i] = f.pos_row[i];
     info->pos_col[i] = f.pos_col[i];
     info->out_row[i] = f.out_row[i];
@@ -407,9 +407,9 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           fa.nouter = f.nouter;
           fa.wbit[0] = f.wbit[0];
           fa.wbit[1] = f.wbit[1];
+          for (int i = 0; i < 10; ++i) fa.hole[i] = f.hole[i];
           for (int i = 0; i < 8; ++i) {
             fa.lrow[i] = f.lrow[i];
-            fa.hole[i] = f.hole[i];
             fa.pos_row[i] = f.pos_row[i];
             fa.pos_col[i] = f.pos_col[i];
             fa.out_row[i] = f.out_row[i];

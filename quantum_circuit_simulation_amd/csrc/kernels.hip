@@ -1150,8 +1150,8 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
 // ---------------------------------------------------------------------------
 // Two chained skinny-class steps in one pass (k_fused2; see Fused2Args).
 //
-// A long tensor T absorbs a small W1 (K1 = S1 = 16 or 32 entries) and the
-// product T1 is reduced at once against another small W2 (K2 = S2).  With
+// A long tensor T absorbs a small W1 (K1 = S1 = 4, 8, 16 or 32 entries) and
+// the product T1 is reduced at once against another small W2 (K2 = S2).  With
 // every mode of extent 2 and the lifetime order of the operands, the modes
 // the second step reduces sit right above the first step's reduced modes in
 // T, so a block of consecutive rows of T yields whole rows of T1 for the
@@ -1168,7 +1168,10 @@ __global__ __launch_bounds__(256) void k_skinny_mfma(StepArgs a, SkinnyRuns rn) 
 // consumes MFMA results that need all of the block's earlier reads, and LDS
 // operations of one wave complete in order, so the block is reused in place
 // with no barrier; the next pass's loads are issued before this pass's
-// MFMAs.
+// MFMAs.  Pairs with K1, K2 <= 8 (the gate steps of state-vector trees) run
+// both phases on the vector ALU instead, one lane per row of a block: the
+// 32-wide MFMA tile would hold all 1024 / K rows' accumulators at once, and
+// at 4 or 8 multiply-adds per entry the ALU keeps up with HBM.
 
 // second-operand table of one phase (K = S): lane l of K entry q at [q][l];
 // with K = 32 the imaginary-part columns follow at [K + q][l]
@@ -1231,12 +1234,17 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int W1F = ROWS1 * RS1, W2F = ROWS2 * RS2, W3F = (ROWS2 * SP + 1) / 2;
   constexpr int WB = W1F > W2F ? (W1F > W3F ? W1F : W3F) : (W2F > W3F ? W2F : W3F);
   constexpr int LPT = E / 2 / 64;  // 16-byte loads per lane per pass
-  constexpr int JB2 = K2 == 32 ? 5 : 4, LB2 = 10 - JB2;
-  constexpr int LKH = K1 == 32 ? 4 : 3;  // log2(K1 / 2)
+  constexpr int JB2 = K2 == 32 ? 5 : K2 == 16 ? 4 : K2 == 8 ? 3 : 2, LB2 = 10 - JB2;
+  constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : 1;  // log2(K1 / 2)
   constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
   constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
-  constexpr int BT1 = (K1 == 32 ? 2 : 1) * K1 * 64, BT2 = (K2 == 32 ? 2 : 1) * K2 * 64;
-  static_assert((1 << LB1) == ROWS1 && NB1 >= 1 && NB2 >= 1 && 8 * WB < 65536, "fused block layout");
+  // K <= 8: vector-ALU phases, a lane per row (the 32-wide MFMA tiles would
+  // need all 1024 / K rows' accumulators at once); the tables hold W itself
+  constexpr bool VALU = K1 <= 8;
+  static_assert((K1 <= 8) == (K2 <= 8), "a pair's two K are both <= 8 or both >= 16");
+  constexpr int BT1 = VALU ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
+  constexpr int BT2 = VALU ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
+  static_assert((1 << LB1) == ROWS1 && (VALU || (NB1 >= 1 && NB2 >= 1)) && 8 * WB < 65536, "fused block layout");
   static_assert(kFuseMaxOuter % 6 == 0, "pass-index chunks");
   __shared__ float4 buf[4][WB];
   __shared__ float bt1[BT1], bt2[BT2];
@@ -1246,8 +1254,13 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   __shared__ int32_t pairs_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
 
-  fused_btable<K1>(a.W1, bt1, tid);
-  fused_btable<K2>(a.W2, bt2, tid);
+  if constexpr (VALU) {
+    for (int e = tid; e < K1 * K1; e += 256) *(float2 *)&bt1[2 * e] = a.W1[e];
+    for (int e = tid; e < K2 * K2; e += 256) *(float2 *)&bt2[2 * e] = a.W2[e];
+  } else {
+    fused_btable<K1>(a.W1, bt1, tid);
+    fused_btable<K2>(a.W2, bt2, tid);
+  }
   for (int t = tid; t < ROWS2 + K2; t += 256) {
     int64_t o = 0;
     if (t < ROWS2) {
@@ -1342,6 +1355,12 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
     if (nb & 1) p += a.pos_row[5];
     return p;
   };
+  // vector-ALU phases: lane l takes pass rows l + 64 i; the lane's row bits
+  // (0 .. 5) place its products, bits 6, 7 come from i
+  int lane_pos_v = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((lane >> b) & 1) lane_pos_v += a.pos_row[b];
 
   const bool pairs = pairs_s && aligned16(a.C);
   const int64_t nround = (a.R / ROWS1) >> 2;
@@ -1386,6 +1405,75 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
       xv[(g / (K1 / 2)) * RS1 + g % (K1 / 2)] = ld[i];
     }
     if (rnd + gridDim.x < nround) load(rnd + gridDim.x);
+    if constexpr (VALU) {
+      constexpr int RPL1 = ROWS1 / 64, RPL2 = ROWS2 / 64;
+      float2 *x2 = (float2 *)xb;
+      // an opaque zero per pass keeps the W reads (and the lane's places) in
+      // the loop instead of in registers across it
+      int wo = 0;
+      asm volatile("" : "+v"(wo));
+      const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
+      {
+        // every read of the block comes before the first write (in place)
+        float2 x[RPL1][K1];
+#pragma unroll
+        for (int i = 0; i < RPL1; ++i)
+#pragma unroll
+          for (int q = 0; q < K1 / 2; ++q) {
+            const float4 f = xb[(lane + 64 * i) * RS1 + q];
+            x[i][2 * q] = make_float2(f.x, f.y);
+            x[i][2 * q + 1] = make_float2(f.z, f.w);
+          }
+        const int lp = lane_pos_v + wo;
+#pragma unroll
+        for (int s2 = 0; s2 < K1; ++s2) {
+          float2 w[K1];
+#pragma unroll
+          for (int k = 0; k < K1; ++k) w[k] = w1[s2 * K1 + k];
+          int pc = 0;
+#pragma unroll
+          for (int c = 0; c < LKH + 1; ++c)
+            if ((s2 >> c) & 1) pc += a.pos_col[c];
+#pragma unroll
+          for (int i = 0; i < RPL1; ++i) {
+            float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int k = 0; k < K1; ++k) {
+              y.x += x[i][k].x * w[k].x - x[i][k].y * w[k].y;
+              y.y += x[i][k].x * w[k].y + x[i][k].y * w[k].x;
+            }
+            x2[lp + ((i & 1) ? a.pos_row[6] : 0) + ((i & 2) ? a.pos_row[7] : 0) + pc] = y;
+          }
+        }
+      }
+      {
+        float2 z[RPL2][K2];
+#pragma unroll
+        for (int i = 0; i < RPL2; ++i)
+#pragma unroll
+          for (int q = 0; q < K2 / 2; ++q) {
+            const float4 f = xb[(lane + 64 * i) * RS2 + q];
+            z[i][2 * q] = make_float2(f.x, f.y);
+            z[i][2 * q + 1] = make_float2(f.z, f.w);
+          }
+#pragma unroll
+        for (int s2 = 0; s2 < K2; ++s2) {
+          float2 w[K2];
+#pragma unroll
+          for (int k = 0; k < K2; ++k) w[k] = w2[s2 * K2 + k];
+#pragma unroll
+          for (int i = 0; i < RPL2; ++i) {
+            float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int k = 0; k < K2; ++k) {
+              y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
+              y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
+            }
+            x2[(lane + 64 * i) * SP + s2 + wo] = y;
+          }
+        }
+      }
+    } else {
     {
       f32x16 acc[NB1], acw[NB1];
       fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
@@ -1425,6 +1513,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           for (int r = 0; r < 16; ++r)
             xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
       }
+    }
     }
     int64_t base = 0;
 #pragma unroll
@@ -3305,11 +3394,14 @@ static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
 
 hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
   // the planner emits only pairs that meet these; anything else is refused
-  if ((a.K1 != 16 && a.K1 != 32) || (a.K2 != 16 && a.K2 != 32) || a.nouter < 0 || a.nouter > kFuseMaxOuter)
+  auto kok = [](int32_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
+  if (!kok(a.K1) || !kok(a.K2) || (a.K1 <= 8) != (a.K2 <= 8) || a.nouter < 0 || a.nouter > kFuseMaxOuter)
     return hipErrorInvalidValue;
   if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.W1 || !a.W2 || !a.C ||
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
+  if (a.K1 == 4) return a.K2 == 4 ? run_fused2_k<4, 4>(a, stream) : run_fused2_k<4, 8>(a, stream);
+  if (a.K1 == 8) return a.K2 == 4 ? run_fused2_k<8, 4>(a, stream) : run_fused2_k<8, 8>(a, stream);
   if (a.K1 == 16) return a.K2 == 16 ? run_fused2_k<16, 16>(a, stream) : run_fused2_k<16, 32>(a, stream);
   return a.K2 == 16 ? run_fused2_k<32, 16>(a, stream) : run_fused2_k<32, 32>(a, stream);
 }

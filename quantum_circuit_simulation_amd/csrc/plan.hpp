@@ -77,9 +77,9 @@ struct Node {
 };
 
 // Two chained complex64 steps run as one pass over the first step's long
-// operand (k_fused2): a long tensor absorbs a small one (K1 = S1 = 16 or 32
-// entries) and the product is reduced at once against another small tensor
-// (K2 = S2).  Built when every index is a power of two and a pass of
+// operand (k_fused2): a long tensor absorbs a small one (K1 = S1 = 4, 8, 16
+// or 32 entries) and the product is reduced at once against another small
+// tensor (K2 = S2; both K at most 8, or both at least 16).  Built when every index is a power of two and a pass of
 // kFusePassEntries entries of the long operand holds whole rows of the
 // second step; the tables give, per index bit, the place of an entry (see
 // Fused2Args in kernels.hpp).
@@ -93,7 +93,7 @@ struct FusedPair {
   int32_t k1 = 0, k2 = 0, nouter = 0;
   int32_t lrow[8] = {};      // the pass's local row bits of the long operand, ascending
   int32_t wbit[2] = {};      // row bits set by bits 0, 1 of the pass index (a workgroup's four passes)
-  int32_t hole[8] = {};      // lrow and wbit, ascending: the rest count the workgroup's rounds
+  int32_t hole[10] = {};     // lrow and wbit, ascending: the rest count the workgroup's rounds
   int32_t pos_row[8] = {}, pos_col[8] = {};
   int64_t out_row[8] = {}, out_col[8] = {};
   int64_t out_pass[kFuseOuterMax] = {};

@@ -98,7 +98,8 @@ def test_config_plans_match_oracle(policy):
 # (log2 K1, log2 K2, shared modes, log2 rows, last-step mode): chained
 # small-operand steps that the planner runs as fused pairs
 CHAINS = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "o"), (4, 5, 2, 17, "s"), (5, 4, 1, 16, "s"), (5, 5, 3, 17, "o"),
-          (4, 4, 4, 18, "s"), (5, 4, 0, 16, "o"), (4, 4, 1, 15, "s"), (4, 5, 0, 17, "s")]
+          (4, 4, 4, 18, "s"), (5, 4, 0, 16, "o"), (4, 4, 1, 15, "s"), (4, 5, 0, 17, "s"), (2, 2, 1, 16, "o"),
+          (2, 3, 0, 17, "s"), (3, 3, 2, 16, "o"), (3, 4, 1, 17, "s")]
 
 
 @pytest.mark.parametrize("case", CHAINS, ids=lambda c: "k{}_{}_v{}_r{}_{}".format(*c))
@@ -107,15 +108,17 @@ def test_fused_pair_plans_match_oracle(case, permuted):
     from tests.test_gpu_fused import chain_network
     net, tree = chain_network(*case, seed=40 + sum(case[:4]), permuted=permuted, with_data=False)
     lib, ref = _check(net, tree)
-    # 2^15 rows is below the fusing threshold; the others pair their first two steps
-    assert ref.fused == ([] if case[3] < 16 else [(0, 1)])
+    # 2^15 rows is below the fusing threshold and K = 8 with K = 16 never
+    # pairs; the others pair their first two steps
+    nopair = case[3] < 16 or (case[0] <= 3) != (case[1] <= 3)
+    assert ref.fused == ([] if nopair else [(0, 1)])
     if ref.fused:
         assert lib.tensor_offset(net.num_leaves) == P.NONE  # the first product is never stored
     _check(net, tree, fuse=False)
     # fixing the closed outer mode of T keeps the pair on half the rows
     if case[4] == "o":
         lib, ref = _check(net, tree, sliced=[net.leaves[3][0]])
-        assert ref.fused == ([] if case[3] - 1 < 16 else [(0, 1)])
+        assert ref.fused == ([] if nopair or case[3] - 1 < 16 else [(0, 1)])
 
 
 def test_grid_depth16_plan_with_fused_pairs_matches_oracle():
