@@ -113,8 +113,8 @@ typedef struct {
                                    the whole result, e.g. one range per process or per call */
   int32_t fuse;               /* 1: where a long tensor absorbs a small one (4, 8, 16 or 32
                                  entries of K, as many outputs) and the product is reduced at once
-                                 against another such small tensor (both K <= 8 or both >= 16),
-                                 both steps run in one pass over the
+                                 against another such small tensor, both steps run in one pass
+                                 over the
                                  long operand and the first product is never stored (complex64,
                                  exact, lifetime order, every extent a power of two, long side
                                  >= 2^16 rows).  0: every step runs on its own. */

@@ -353,8 +353,8 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
     """Pairs (s1, s2) of steps run as one pass: a long tensor T absorbs a small
     one (K = S = 4, 8, 16 or 32 entries) and the product T1 is at once the long
     operand of the next step, which reduces it against another small tensor
-    (K = S = 4, 8, 16 or 32; both K at most 8 or both at least 16), with every
-    extent of the modes involved a power of two,
+    (K = S = 4, 8, 16 or 32), with every extent of the modes involved a power
+    of two,
     T holding at least 2^16 rows, both steps outside the tiny class, neither
     split over K nor the root, T1 read in place, and the modes of the second
     step's K that T carries spanning at most 1024 / K1 index values (so that a
@@ -384,8 +384,6 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
         t, r1, s1w = long_short(a)
         t1, _, s2w = long_short(b)
         if a.k not in (4, 8, 16, 32) or s1w != a.k or b.k not in (4, 8, 16, 32) or s2w != b.k:
-            continue
-        if (a.k <= 8) != (b.k <= 8):
             continue
         if t1 != L + s1 or (b.copy_a if t1 == b.lhs else b.copy_b):
             continue

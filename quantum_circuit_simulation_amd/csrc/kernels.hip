@@ -1238,13 +1238,13 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : 1;  // log2(K1 / 2)
   constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
   constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
-  // K <= 8: vector-ALU phases, a lane per row (the 32-wide MFMA tiles would
-  // need all 1024 / K rows' accumulators at once); the tables hold W itself
-  constexpr bool VALU = K1 <= 8;
-  static_assert((K1 <= 8) == (K2 <= 8), "a pair's two K are both <= 8 or both >= 16");
-  constexpr int BT1 = VALU ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
-  constexpr int BT2 = VALU ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
-  static_assert((1 << LB1) == ROWS1 && (VALU || (NB1 >= 1 && NB2 >= 1)) && 8 * WB < 65536, "fused block layout");
+  // a phase with K <= 8 runs on the vector ALU, a lane per row (the 32-wide
+  // MFMA tile would need all 1024 / K rows' accumulators at once); its table
+  // holds W itself
+  constexpr bool V1 = K1 <= 8, V2 = K2 <= 8;
+  constexpr int BT1 = V1 ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
+  constexpr int BT2 = V2 ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
+  static_assert((1 << LB1) == ROWS1 && 8 * WB < 65536, "fused block layout");
   static_assert(kFuseMaxOuter % 6 == 0, "pass-index chunks");
   __shared__ float4 buf[4][WB];
   __shared__ float bt1[BT1], bt2[BT2];
@@ -1254,11 +1254,14 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   __shared__ int32_t pairs_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
 
-  if constexpr (VALU) {
+  if constexpr (V1) {
     for (int e = tid; e < K1 * K1; e += 256) *(float2 *)&bt1[2 * e] = a.W1[e];
-    for (int e = tid; e < K2 * K2; e += 256) *(float2 *)&bt2[2 * e] = a.W2[e];
   } else {
     fused_btable<K1>(a.W1, bt1, tid);
+  }
+  if constexpr (V2) {
+    for (int e = tid; e < K2 * K2; e += 256) *(float2 *)&bt2[2 * e] = a.W2[e];
+  } else {
     fused_btable<K2>(a.W2, bt2, tid);
   }
   for (int t = tid; t < ROWS2 + K2; t += 256) {
@@ -1405,14 +1408,16 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
       xv[(g / (K1 / 2)) * RS1 + g % (K1 / 2)] = ld[i];
     }
     if (rnd + gridDim.x < nround) load(rnd + gridDim.x);
-    if constexpr (VALU) {
+    {
+      // vector-ALU phases: lane l takes block rows l + 64 i.  An opaque zero
+      // per pass keeps their W reads (and the lane's places) in the loop
+      // instead of in registers across it.
       constexpr int RPL1 = ROWS1 / 64, RPL2 = ROWS2 / 64;
-      float2 *x2 = (float2 *)xb;
-      // an opaque zero per pass keeps the W reads (and the lane's places) in
-      // the loop instead of in registers across it
+      [[maybe_unused]] float2 *x2 = (float2 *)xb;
       int wo = 0;
       asm volatile("" : "+v"(wo));
-      const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
+      [[maybe_unused]] const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
+      if constexpr (V1)
       {
         // every read of the block comes before the first write (in place)
         float2 x[RPL1][K1];
@@ -1446,6 +1451,29 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           }
         }
       }
+      else
+    {
+      f32x16 acc[NB1], acw[NB1];
+      fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
+      // the lane's base place, opaque per pass so that its 16 NB1 sums with
+      // the (uniform) row parts are formed here rather than held in registers
+      int lp = lane_pos;
+      asm volatile("" : "+v"(lp));
+      if constexpr (K1 == 32) {
+#pragma unroll
+        for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *(float2 *)&xf[2 * (lp + rpos(nb, r))] = make_float2(acc[nb][r], acw[nb][r]);
+      } else {
+        const int part = l32 >> 4;
+#pragma unroll
+        for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
+      }
+    }
+      if constexpr (V2)
       {
         float2 z[RPL2][K2];
 #pragma unroll
@@ -1473,28 +1501,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           }
         }
       }
-    } else {
-    {
-      f32x16 acc[NB1], acw[NB1];
-      fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
-      // the lane's base place, opaque per pass so that its 16 NB1 sums with
-      // the (uniform) row parts are formed here rather than held in registers
-      int lp = lane_pos;
-      asm volatile("" : "+v"(lp));
-      if constexpr (K1 == 32) {
-#pragma unroll
-        for (int nb = 0; nb < NB1; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            *(float2 *)&xf[2 * (lp + rpos(nb, r))] = make_float2(acc[nb][r], acw[nb][r]);
-      } else {
-        const int part = l32 >> 4;
-#pragma unroll
-        for (int nb = 0; nb < NB1; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
-      }
-    }
+      else
     {
       f32x16 acc[NB2], acw[NB2];
       fused_phase<K2, NB2>(xb, bt2, lane, acc, acw);
@@ -3395,15 +3402,25 @@ static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
 hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
   // the planner emits only pairs that meet these; anything else is refused
   auto kok = [](int32_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
-  if (!kok(a.K1) || !kok(a.K2) || (a.K1 <= 8) != (a.K2 <= 8) || a.nouter < 0 || a.nouter > kFuseMaxOuter)
-    return hipErrorInvalidValue;
+  if (!kok(a.K1) || !kok(a.K2) || a.nouter < 0 || a.nouter > kFuseMaxOuter) return hipErrorInvalidValue;
   if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.W1 || !a.W2 || !a.C ||
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
-  if (a.K1 == 4) return a.K2 == 4 ? run_fused2_k<4, 4>(a, stream) : run_fused2_k<4, 8>(a, stream);
-  if (a.K1 == 8) return a.K2 == 4 ? run_fused2_k<8, 4>(a, stream) : run_fused2_k<8, 8>(a, stream);
-  if (a.K1 == 16) return a.K2 == 16 ? run_fused2_k<16, 16>(a, stream) : run_fused2_k<16, 32>(a, stream);
-  return a.K2 == 16 ? run_fused2_k<32, 16>(a, stream) : run_fused2_k<32, 32>(a, stream);
+  auto second = [&](auto k1c) {
+    constexpr int k1 = decltype(k1c)::value;
+    switch (a.K2) {
+      case 4: return run_fused2_k<k1, 4>(a, stream);
+      case 8: return run_fused2_k<k1, 8>(a, stream);
+      case 16: return run_fused2_k<k1, 16>(a, stream);
+      default: return run_fused2_k<k1, 32>(a, stream);
+    }
+  };
+  switch (a.K1) {
+    case 4: return second(std::integral_constant<int, 4>{});
+    case 8: return second(std::integral_constant<int, 8>{});
+    case 16: return second(std::integral_constant<int, 16>{});
+    default: return second(std::integral_constant<int, 32>{});
+  }
 }
 
 hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {

@@ -61,7 +61,7 @@ struct Fused2Args {
   const float2 *W2;  // row-major [K2, K2]
   float2 *C;
   int64_t R;         // a multiple of 1024 / K1; R / (1024 / K1) = 2^nouter passes
-  int32_t K1, K2;    // 4, 8, 16 or 32; both <= 8 or both >= 16
+  int32_t K1, K2;    // 4, 8, 16 or 32 (K <= 8: vector-ALU phase)
   int32_t nouter;
   int32_t lrow[8], hole[10], wbit[2];
   int32_t pos_row[8], pos_col[8];

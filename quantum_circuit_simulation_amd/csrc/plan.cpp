@@ -255,7 +255,7 @@ bool make_fused_pair(const PlanImpl &p, int32_t s1, int32_t s2, FusedPair *f) {
   const int64_t R2 = lb == 0 ? b.m : b.n, S2 = lb == 0 ? b.n : b.m;
   const int64_t K1 = a.k, K2 = b.k;
   auto kok = [](int64_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
-  if (!kok(K1) || S1 != K1 || !kok(K2) || S2 != K2 || (K1 <= 8) != (K2 <= 8)) return false;
+  if (!kok(K1) || S1 != K1 || !kok(K2) || S2 != K2) return false;
   if ((lb == 0 ? b.lhs : b.rhs) != p.L + s1 || (lb == 0 ? b.copy_a : b.copy_b) != 0) return false;
   // the oriented rows of a node are its N side when swapped, else its M side
   const auto &a_rows = (la == 1) == (a.swap != 0) ? a.row_runs : a.col_runs;

@@ -79,7 +79,7 @@ struct Node {
 // Two chained complex64 steps run as one pass over the first step's long
 // operand (k_fused2): a long tensor absorbs a small one (K1 = S1 = 4, 8, 16
 // or 32 entries) and the product is reduced at once against another small
-// tensor (K2 = S2; both K at most 8, or both at least 16).  Built when every index is a power of two and a pass of
+// tensor (K2 = S2, the same choices).  Built when every index is a power of two and a pass of
 // kFusePassEntries entries of the long operand holds whole rows of the
 // second step; the tables give, per index bit, the place of an entry (see
 // Fused2Args in kernels.hpp).

@@ -108,9 +108,8 @@ def test_fused_pair_plans_match_oracle(case, permuted):
     from tests.test_gpu_fused import chain_network
     net, tree = chain_network(*case, seed=40 + sum(case[:4]), permuted=permuted, with_data=False)
     lib, ref = _check(net, tree)
-    # 2^15 rows is below the fusing threshold and K = 8 with K = 16 never
-    # pairs; the others pair their first two steps
-    nopair = case[3] < 16 or (case[0] <= 3) != (case[1] <= 3)
+    # 2^15 rows is below the fusing threshold; the others pair their first two steps
+    nopair = case[3] < 16
     assert ref.fused == ([] if nopair else [(0, 1)])
     if ref.fused:
         assert lib.tensor_offset(net.num_leaves) == P.NONE  # the first product is never stored
@@ -125,7 +124,7 @@ def test_grid_depth16_plan_with_fused_pairs_matches_oracle():
     net = circuits.grid_fsim(7, 8, 16, 505).to_network()
     tree, sl, _ = trees.stored_tree("grid_7x8_d16", net)
     lib, ref = _check(net, tree, sliced=sl)
-    assert len(ref.fused) == 6
+    assert len(ref.fused) == 8
 
 
 def test_sliced_circuit_plan_matches_oracle():
