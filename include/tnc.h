@@ -164,7 +164,8 @@ typedef struct {
   uint64_t header_bytes;         /* workspace prefix holding kernel descriptors */
   uint64_t arena_bytes;          /* arena high-water mark */
   uint64_t workspace_bytes;      /* header_bytes + arena_bytes */
-  int32_t fused_pairs;           /* step pairs run as one pass (tnc_plan_options.fuse) */
+  int32_t fused_pairs;           /* fused chains (pairs, or three steps with K <= 8) run as one
+                                    pass each (tnc_plan_options.fuse) */
 } tnc_plan_stats;
 
 tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats);
@@ -192,16 +193,21 @@ typedef struct {
   uint64_t a_off, b_off, c_off;  /* arena offsets of the GEMM operands / product
                                     (UINT64_MAX: leaf in place or `out`) */
   uint64_t scratch_off, scratch_bytes;
-  int32_t fused_with;            /* the other step of its fused pair (both run in the second
-                                    step's launch), or -1 */
+  int32_t fused_with;            /* fused chains (all their steps run in the last step's launch):
+                                    for an earlier step the chain's last step, for the last step
+                                    the chain's first; -1 if not fused */
 } tnc_node_info;
 
 tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
 
-/* A fused pair's pass tables (index 0 .. fused_pairs - 1, in step order),
- * for inspection and host-side checks.  The pair runs steps `first` and
- * `second`; their long operands are lhs (long = 0) or rhs (1), and the
- * second step's long operand is the first step's product.  Every index is a
+/* A fused chain's pass tables (index 0 .. fused_pairs - 1, in step order),
+ * for inspection and host-side checks.  The chain runs steps `first`,
+ * `second` and, for a chain of three (all K <= 8), `third`; their long
+ * operands are lhs (long = 0) or rhs (1), and each step's long operand is the
+ * previous step's product.  The tables below describe a pair; in a chain of
+ * three the second product goes to the third step's block through pos2_*
+ * as the first goes to the second's through pos_*, and out_* place the third
+ * product.  Every index is a
  * sum of one offset per set bit.  A pass takes 1024 entries of the first
  * long operand X (row-major [rows, k1]): its local row rho (0 .. 1024/k1 - 1)
  * is X row spread(rho) + round part + wave part, where spread puts bit j of
@@ -215,11 +221,14 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  * + (w >> 1) out_pass[1] + sum out_pass[2 + q] over bits q of the round.
  * Errors: INVALID_ARG (no such pair). */
 typedef struct {
-  int32_t first, second, long1, long2;
+  int32_t first, second, third;  /* third: -1 for a pair */
+  int32_t long1, long2, long3;
   int64_t rows;
-  int32_t k1, k2, nouter;
+  int32_t k1, k2, k3, nouter;    /* k3: 0 for a pair */
   int32_t lrow[8], hole[10], wbit[2];
   int32_t pos_row[8], pos_col[8];
+  int32_t pos2_row[8], pos2_col[8];  /* a chain of three: the second product's places
+                                        in the third step's block, as pos_* */
   int64_t out_row[8], out_col[8];
   int64_t out_pass[48];
 } tnc_fused_info;

@@ -237,12 +237,9 @@ class Node:
     c_off: int = NONE        # NONE = written to the output buffer
     scratch_off: int = NONE
     scratch_bytes: int = 0
-    fuse_next: int = -1      # first step of a fused pair: the second step
-    fuse_prev: int = -1      # second step of a fused pair: the first step
-
-    @property
-    def fused_with(self) -> int:
-        return self.fuse_next if self.fuse_next >= 0 else self.fuse_prev
+    fuse_next: int = -1      # the next step of its fused chain
+    fuse_prev: int = -1      # the previous step of its fused chain
+    fused_with: int = -1     # earlier steps: the chain's last step; the last step: the chain's first
 
 
 @dataclass
@@ -262,7 +259,7 @@ class Plan:
     bytes: int
     max_elems: int
     num_slices: int
-    fused: List[tuple] = field(default_factory=list)   # (first, second) step pairs
+    fused: List[tuple] = field(default_factory=list)   # fused chains: (first, second[, third]) steps
 
 
 def _runs(c_order, ext, row_set):
@@ -358,8 +355,12 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
     T holding at least 2^16 rows, both steps outside the tiny class, neither
     split over K nor the root, T1 read in place, and the modes of the second
     step's K that T carries spanning at most 1024 / K1 index values (so that a
-    pass over 1024 entries of T yields whole rows of the second step).  Pairs
-    are taken in step order and do not overlap.  Complex64, lifetime order."""
+    pass over 1024 entries of T yields whole rows of the second step).  A pair
+    whose two K are at most 8 extends to the next step in the same way (K3 =
+    S3 = 4 or 8, the second product read in place, T's modes reduced by the
+    second and third steps together spanning at most 1024 / K1 values).
+    Chains are taken in step order and do not overlap.  Complex64, lifetime
+    order."""
     if not fuse or policy != LIFETIME or eb != 8:
         return []
     consumer = {}
@@ -395,11 +396,28 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
             continue
         # the second step's reduced modes that come from T, in index bits
         k2_from_t = [x for x in sets[t] if x in sets[small2]]
-        if sum(_log2(ext[x]) for x in k2_from_t) > _log2(FUSE_PASS_ENTRIES // a.k):
+        bits_t = sum(_log2(ext[x]) for x in k2_from_t)
+        if bits_t > _log2(FUSE_PASS_ENTRIES // a.k):
             continue
-        a.fuse_next, b.fuse_prev = s2, s1
-        taken.update((s1, s2))
-        pairs.append((s1, s2))
+        chain = [s1, s2]
+        s3 = consumer.get(L + s2)
+        if s3 is not None and a.k <= 8 and b.k <= 8:
+            c = nodes[s3]
+            t2, _, s3w = long_short(c)
+            small3 = c.rhs if t2 == c.lhs else c.lhs
+            k3_from_t = [x for x in sets[t] if x in sets[small3]]
+            if (c.cls != CLASS_TINY and c.splits == 1 and s3 != len(nodes) - 1 and c.k in (4, 8) and s3w == c.k
+                    and t2 == L + s2 and not (c.copy_a if t2 == c.lhs else c.copy_b)
+                    and all(_is_pow2(ext[x]) for x in sets[small3])
+                    and bits_t + sum(_log2(ext[x]) for x in k3_from_t) <= _log2(FUSE_PASS_ENTRIES // a.k)):
+                chain.append(s3)
+        for x, y in zip(chain, chain[1:]):
+            nodes[x].fuse_next, nodes[y].fuse_prev = y, x
+        for x in chain[:-1]:
+            nodes[x].fused_with = chain[-1]
+        nodes[chain[-1]].fused_with = chain[0]
+        taken.update(chain)
+        pairs.append(tuple(chain))
     return pairs
 
 
@@ -540,9 +558,10 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
         to_free = []
         for s in members:
             nd = nodes[s]
-            if nd.fuse_prev >= 0:
-                to_free.extend(deferred.pop(nd.fuse_prev))
             frees = deferred.setdefault(s, []) if nd.fuse_next >= 0 else to_free
+            if nd.fuse_prev >= 0:
+                # the chain's earlier steps: their operands stay until its last step
+                frees.extend(deferred.pop(nd.fuse_prev))
             for which, t in (("a", nd.lhs), ("b", nd.rhs)):
                 if (s, which) in early:
                     frees.append((getattr(nd, which + "_off"), rbytes(elems_of[t])))

@@ -166,7 +166,17 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info) {
   info->c_off = n.c_off;
   info->scratch_off = n.scratch_off;
   info->scratch_bytes = n.scratch_bytes;
-  info->fused_with = n.fuse_next >= 0 ? n.fuse_next : n.fuse_prev;
+  // earlier steps of a fused chain: the step whose launch runs them (the
+  // chain's last); the last step: the chain's first
+  int32_t w = -1;
+  if (n.fuse_next >= 0) {
+    w = n.fuse_next;
+    while (p.nodes[w].fuse_next >= 0) w = p.nodes[w].fuse_next;
+  } else if (n.fuse_prev >= 0) {
+    w = n.fuse_prev;
+    while (p.nodes[w].fuse_prev >= 0) w = p.nodes[w].fuse_prev;
+  }
+  info->fused_with = w;
   return TNC_OK;
 }
 
@@ -178,15 +188,20 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info) 
   std::memset(info, 0, sizeof(*info));
   info->first = f.first;
   info->second = f.second;
+  info->third = f.third;
   info->long1 = f.long1;
   info->long2 = f.long2;
+  info->long3 = f.long3;
   info->rows = f.rows;
   info->k1 = f.k1;
   info->k2 = f.k2;
+  info->k3 = f.k3;
   info->nouter = f.nouter;
   for (int i = 0; i < 10; ++i) info->hole[i] = f.hole[i];
   for (int i = 0; i < 8; ++i) {
     info->lrow[i] = f.lrow[i];
+    info->pos2_row[i] = f.pos2_row[i];
+    info->pos2_col[i] = f.pos2_col[i];
     info->pos_row[i] = f.pos_row[i];
     info->pos_col[i] = f.pos_col[i];
     info->out_row[i] = f.out_row[i];
@@ -396,20 +411,25 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
         case tnc::OP_FUSED: {
           const tnc::FusedPair &f = p.fused[op.first];
           const tnc::Node &n1 = p.nodes[f.first], &n2 = p.nodes[f.second];
+          const tnc::Node &nl = p.nodes[f.third >= 0 ? f.third : f.second];
           tnc::Fused2Args fa{};
           fa.X = reinterpret_cast<const float2 *>(operand(n1, f.long1));
           fa.W1 = reinterpret_cast<const float2 *>(operand(n1, 1 - f.long1));
           fa.W2 = reinterpret_cast<const float2 *>(operand(n2, 1 - f.long2));
-          fa.C = reinterpret_cast<float2 *>(resolve(tnc::kBufArena, n2.c_off));
+          fa.W3 = f.third >= 0 ? reinterpret_cast<const float2 *>(operand(nl, 1 - f.long3)) : nullptr;
+          fa.C = reinterpret_cast<float2 *>(resolve(tnc::kBufArena, nl.c_off));
           fa.R = f.rows;
           fa.K1 = f.k1;
           fa.K2 = f.k2;
+          fa.K3 = f.k3;
           fa.nouter = f.nouter;
           fa.wbit[0] = f.wbit[0];
           fa.wbit[1] = f.wbit[1];
           for (int i = 0; i < 10; ++i) fa.hole[i] = f.hole[i];
           for (int i = 0; i < 8; ++i) {
             fa.lrow[i] = f.lrow[i];
+            fa.pos2_row[i] = f.pos2_row[i];
+            fa.pos2_col[i] = f.pos2_col[i];
             fa.pos_row[i] = f.pos_row[i];
             fa.pos_col[i] = f.pos_col[i];
             fa.out_row[i] = f.out_row[i];
@@ -517,8 +537,9 @@ tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *o
                   : op.kind == tnc::OP_FUSED ? TNC_OP_FUSED : TNC_OP_GEMM;
     if (op.kind == tnc::OP_SKINNY || op.kind == tnc::OP_GEMM) rec[i].step = op.first;
     if (op.kind == tnc::OP_FUSED) {
-      rec[i].step = p.fused[op.first].second;
-      rec[i].count = 2;
+      const tnc::FusedPair &f = p.fused[op.first];
+      rec[i].step = f.third >= 0 ? f.third : f.second;
+      rec[i].count = f.third >= 0 ? 3 : 2;
     }
     if (op.kind == tnc::OP_COPY || op.kind == tnc::OP_TINY_GROUP) rec[i].count = op.count;
   }

@@ -1224,17 +1224,19 @@ __device__ __forceinline__ void fused_phase(const float4 *xb, const float *bt, i
   }
 }
 
-template <int K1, int K2>
+template <int K1, int K2, int K3>
 __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int E = kFuseEntries;
-  constexpr int ROWS1 = E / K1, ROWS2 = E / K2;
+  constexpr int KL = K3 ? K3 : K2;  // the last phase's K (K3 = 0: a pair)
+  constexpr int ROWS1 = E / K1, ROWS2 = E / K2, ROWS3 = K3 ? E / K3 : 1, ROWSL = E / KL;
   constexpr int NB1 = ROWS1 / 32, NB2 = ROWS2 / 32;
-  constexpr int RS1 = K1 / 2 + 1, RS2 = K2 / 2 + 1;  // 16-byte units per LDS row, one pad
-  constexpr int SP = K2 + 1;                         // staged products: complex entries per row
-  constexpr int W1F = ROWS1 * RS1, W2F = ROWS2 * RS2, W3F = (ROWS2 * SP + 1) / 2;
-  constexpr int WB = W1F > W2F ? (W1F > W3F ? W1F : W3F) : (W2F > W3F ? W2F : W3F);
+  constexpr int RS1 = K1 / 2 + 1, RS2 = K2 / 2 + 1, RS3 = K3 / 2 + 1;  // 16-byte units per LDS row, one pad
+  constexpr int SP = KL + 1;                         // staged products: complex entries per row
+  constexpr int W1F = ROWS1 * RS1, W2F = ROWS2 * RS2, W3F = (ROWSL * SP + 1) / 2, W4F = K3 ? ROWS3 * RS3 : 0;
+  constexpr int WB12 = W1F > W2F ? W1F : W2F, WB34 = W3F > W4F ? W3F : W4F;
+  constexpr int WB = WB12 > WB34 ? WB12 : WB34;
   constexpr int LPT = E / 2 / 64;  // 16-byte loads per lane per pass
-  constexpr int JB2 = K2 == 32 ? 5 : K2 == 16 ? 4 : K2 == 8 ? 3 : 2, LB2 = 10 - JB2;
+  constexpr int JB2 = KL == 32 ? 5 : KL == 16 ? 4 : KL == 8 ? 3 : 2, LB2 = 10 - JB2;  // the stored product's bits
   constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : 1;  // log2(K1 / 2)
   constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
   constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
@@ -1244,11 +1246,14 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr bool V1 = K1 <= 8, V2 = K2 <= 8;
   constexpr int BT1 = V1 ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
   constexpr int BT2 = V2 ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
+  constexpr int BT3 = K3 ? 2 * K3 * K3 : 2;
+  // chains of three run every phase on the vector ALU
+  static_assert(K3 == 0 || (V1 && V2 && K3 <= 8), "three-step chains have K <= 8");
   static_assert((1 << LB1) == ROWS1 && 8 * WB < 65536, "fused block layout");
   static_assert(kFuseMaxOuter % 6 == 0, "pass-index chunks");
   __shared__ float4 buf[4][WB];
-  __shared__ float bt1[BT1], bt2[BT2];
-  __shared__ int64_t rowoff[ROWS2], coloff[K2];
+  __shared__ float bt1[BT1], bt2[BT2], bt3[BT3];
+  __shared__ int64_t rowoff[ROWSL], coloff[KL];
   __shared__ int64_t ochunk[kFuseMaxOuter / 6][64];  // round-index offsets, 6 bits per chunk
   __shared__ int32_t bit_of[12];
   __shared__ int32_t pairs_s;
@@ -1264,15 +1269,17 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   } else {
     fused_btable<K2>(a.W2, bt2, tid);
   }
-  for (int t = tid; t < ROWS2 + K2; t += 256) {
+  if constexpr (K3 != 0)
+    for (int e = tid; e < K3 * K3; e += 256) *(float2 *)&bt3[2 * e] = a.W3[e];
+  for (int t = tid; t < ROWSL + KL; t += 256) {
     int64_t o = 0;
-    if (t < ROWS2) {
+    if (t < ROWSL) {
 #pragma unroll
       for (int e = 0; e < LB2; ++e)
         if ((t >> e) & 1) o += a.out_row[e];
       rowoff[t] = o;
     } else {
-      const int j = t - ROWS2;
+      const int j = t - ROWSL;
 #pragma unroll
       for (int c = 0; c < JB2; ++c)
         if ((j >> c) & 1) o += a.out_col[c];
@@ -1327,7 +1334,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
 #pragma unroll
     for (int i = 0; i < 12; ++i)
       if ((e >> i) & 1) p |= 1 << bit_of[i];
-    const int w = p >> 10, t = (p >> JB2) & (ROWS2 - 1), c = p & (K2 - 1);
+    const int w = p >> 10, t = (p >> JB2) & (ROWSL - 1), c = p & (KL - 1);
     *idx = w * 2 * WB + t * SP + c;
     *off = rowoff[t] + coloff[c] + ((w & 1) ? a.out_pass[0] : 0) + ((w & 2) ? a.out_pass[1] : 0);
   };
@@ -1360,10 +1367,13 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   };
   // vector-ALU phases: lane l takes pass rows l + 64 i; the lane's row bits
   // (0 .. 5) place its products, bits 6, 7 come from i
-  int lane_pos_v = 0;
+  int lane_pos_v = 0, lane_pos_v2 = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b)
-    if ((lane >> b) & 1) lane_pos_v += a.pos_row[b];
+    if ((lane >> b) & 1) {
+      lane_pos_v += a.pos_row[b];
+      lane_pos_v2 += a.pos2_row[b];
+    }
 
   const bool pairs = pairs_s && aligned16(a.C);
   const int64_t nround = (a.R / ROWS1) >> 2;
@@ -1417,6 +1427,8 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
       int wo = 0;
       asm volatile("" : "+v"(wo));
       [[maybe_unused]] const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
+      [[maybe_unused]] const float2 *w3 = (const float2 *)bt3 + wo;
+      [[maybe_unused]] const int lp2 = lane_pos_v2 + wo;
       if constexpr (V1)
       {
         // every read of the block comes before the first write (in place)
@@ -1489,6 +1501,12 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           float2 w[K2];
 #pragma unroll
           for (int k = 0; k < K2; ++k) w[k] = w2[s2 * K2 + k];
+          int pc = 0;
+          if constexpr (K3 != 0) {
+#pragma unroll
+            for (int c = 0; c < (K2 == 8 ? 3 : 2); ++c)
+              if ((s2 >> c) & 1) pc += a.pos2_col[c];
+          }
 #pragma unroll
           for (int i = 0; i < RPL2; ++i) {
             float2 y = make_float2(0.f, 0.f);
@@ -1497,7 +1515,10 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
               y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
             }
-            x2[(lane + 64 * i) * SP + s2 + wo] = y;
+            if constexpr (K3 != 0)  // to its place in the third step's block
+              x2[lp2 + ((i & 1) ? a.pos2_row[6] : 0) + ((i & 2) ? a.pos2_row[7] : 0) + pc] = y;
+            else
+              x2[(lane + 64 * i) * SP + s2 + wo] = y;
           }
         }
       }
@@ -1521,6 +1542,35 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
             xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
       }
     }
+      if constexpr (K3 != 0) {
+        // third phase: the block's rows times W3, staged
+        constexpr int RPL3 = ROWS3 / 64;
+        float2 z[RPL3][K3];
+#pragma unroll
+        for (int i = 0; i < RPL3; ++i)
+#pragma unroll
+          for (int q = 0; q < K3 / 2; ++q) {
+            const float4 f = xb[(lane + 64 * i) * RS3 + q];
+            z[i][2 * q] = make_float2(f.x, f.y);
+            z[i][2 * q + 1] = make_float2(f.z, f.w);
+          }
+#pragma unroll
+        for (int s3 = 0; s3 < K3; ++s3) {
+          float2 w[K3];
+#pragma unroll
+          for (int k = 0; k < K3; ++k) w[k] = w3[s3 * K3 + k];
+#pragma unroll
+          for (int i = 0; i < RPL3; ++i) {
+            float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int k = 0; k < K3; ++k) {
+              y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
+              y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
+            }
+            x2[(lane + 64 * i) * SP + s3 + wo] = y;
+          }
+        }
+      }
     }
     int64_t base = 0;
 #pragma unroll
@@ -3388,14 +3438,15 @@ hipError_t run_cgemm_small(const StepArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int K1, int K2>
+template <int K1, int K2, int K3 = 0>
 static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
   const int64_t nround = (a.R / (kFuseEntries / K1)) / 4;  // four passes per workgroup round
   int64_t blocks = nround;
   const int64_t cap = 8 * (int64_t)num_cus();
   if (blocks > cap) blocks = cap;
-  note_kernel("k_fused2<%d,%d>", K1, K2);
-  hipLaunchKernelGGL((k_fused2<K1, K2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (K3) note_kernel("k_fused2<%d,%d,%d>", K1, K2, K3);
+  else note_kernel("k_fused2<%d,%d>", K1, K2);
+  hipLaunchKernelGGL((k_fused2<K1, K2, K3>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -3403,9 +3454,24 @@ hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
   // the planner emits only pairs that meet these; anything else is refused
   auto kok = [](int32_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
   if (!kok(a.K1) || !kok(a.K2) || a.nouter < 0 || a.nouter > kFuseMaxOuter) return hipErrorInvalidValue;
+  if (a.K3 != 0 && (a.K1 > 8 || a.K2 > 8 || (a.K3 != 4 && a.K3 != 8) || !a.W3)) return hipErrorInvalidValue;
   if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.W1 || !a.W2 || !a.C ||
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
+  if (a.K3 != 0) {
+    // three-step chains: every K is 4 or 8
+    const int code = (a.K1 == 8) * 4 + (a.K2 == 8) * 2 + (a.K3 == 8);
+    switch (code) {
+      case 0: return run_fused2_k<4, 4, 4>(a, stream);
+      case 1: return run_fused2_k<4, 4, 8>(a, stream);
+      case 2: return run_fused2_k<4, 8, 4>(a, stream);
+      case 3: return run_fused2_k<4, 8, 8>(a, stream);
+      case 4: return run_fused2_k<8, 4, 4>(a, stream);
+      case 5: return run_fused2_k<8, 4, 8>(a, stream);
+      case 6: return run_fused2_k<8, 8, 4>(a, stream);
+      default: return run_fused2_k<8, 8, 8>(a, stream);
+    }
+  }
   auto second = [&](auto k1c) {
     constexpr int k1 = decltype(k1c)::value;
     switch (a.K2) {

@@ -59,12 +59,15 @@ struct Fused2Args {
   const float2 *X;   // row-major [R, K1]
   const float2 *W1;  // row-major [K1, K1] (S1 rows)
   const float2 *W2;  // row-major [K2, K2]
+  const float2 *W3;  // row-major [K3, K3] (three-step chains), else unused
   float2 *C;
   int64_t R;         // a multiple of 1024 / K1; R / (1024 / K1) = 2^nouter passes
   int32_t K1, K2;    // 4, 8, 16 or 32 (K <= 8: vector-ALU phase)
+  int32_t K3;        // 0 (a pair), or 4 or 8 after K1, K2 <= 8: a third step whose
+                     // block places come from pos2_row / pos2_col as pos_* for the second
   int32_t nouter;
   int32_t lrow[8], hole[10], wbit[2];
-  int32_t pos_row[8], pos_col[8];
+  int32_t pos_row[8], pos_col[8], pos2_row[8], pos2_col[8];
   int64_t out_row[8], out_col[8];
   int64_t out_pass[kFuseMaxOuter];
 };

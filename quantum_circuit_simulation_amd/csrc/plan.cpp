@@ -244,100 +244,127 @@ int32_t log2_exact(int64_t v) {  // -1 unless v is a power of two
   return b;
 }
 
-// Tables of a fused pair (s1's product is s2's long operand; see FusedPair).
-// False when the pair does not have the required form.
-bool make_fused_pair(const PlanImpl &p, int32_t s1, int32_t s2, FusedPair *f) {
-  const Node &a = p.nodes[s1], &b = p.nodes[s2];
-  // each step is taken with its long operand as the rows, whatever the
-  // orientation its own kernel would use
-  const int32_t la = a.m >= a.n ? 0 : 1, lb = b.m >= b.n ? 0 : 1;
-  const int64_t R1 = la == 0 ? a.m : a.n, S1 = la == 0 ? a.n : a.m;
-  const int64_t R2 = lb == 0 ? b.m : b.n, S2 = lb == 0 ? b.n : b.m;
-  const int64_t K1 = a.k, K2 = b.k;
+// Tables of a fused chain of n = 2 or 3 steps st[0 .. n-1], each step's
+// product the next step's long operand (see FusedPair).  False when the chain
+// does not have the required form.
+bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedPair *f) {
+  struct Phase {
+    int32_t lng = 0;                 // 0: the step's lhs is its long operand
+    int64_t R = 0, K = 0;
+    int32_t lr = 0, lk = 0, lb = 0;  // log2 of rows, K and the block's rows
+    std::vector<int64_t> r, c;       // offsets in the step's product of its row / column bits
+    std::vector<int32_t> tr, tc;     // the product's address bit of each row / column bit
+  } ph[3];
   auto kok = [](int64_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
-  if (!kok(K1) || S1 != K1 || !kok(K2) || S2 != K2) return false;
-  if ((lb == 0 ? b.lhs : b.rhs) != p.L + s1 || (lb == 0 ? b.copy_a : b.copy_b) != 0) return false;
-  // the oriented rows of a node are its N side when swapped, else its M side
-  const auto &a_rows = (la == 1) == (a.swap != 0) ? a.row_runs : a.col_runs;
-  const auto &a_cols = (la == 1) == (a.swap != 0) ? a.col_runs : a.row_runs;
-  const auto &b_rows = (lb == 1) == (b.swap != 0) ? b.row_runs : b.col_runs;
-  const auto &b_cols = (lb == 1) == (b.swap != 0) ? b.col_runs : b.row_runs;
-  const int64_t rows1 = kFusePassEntries / K1;
-  const int32_t lr1 = log2_exact(R1), lr2 = log2_exact(R2), lk1 = log2_exact(K1), lk2 = log2_exact(K2);
-  const int32_t lb1 = log2_exact(rows1), lb2 = log2_exact(kFusePassEntries / K2);
-  if (lr1 < 0 || lr2 < 0 || R1 < kFuseMinRows || lr2 != lr1 + lk1 - lk2) return false;
-  if (lr1 - lb1 > kFuseOuterMax) return false;
-  std::vector<int64_t> r1, c1, r2, c2;
-  if (!bit_offsets(a_rows, &r1) || !bit_offsets(a_cols, &c1) || !bit_offsets(b_rows, &r2) ||
-      !bit_offsets(b_cols, &c2))
-    return false;
-  if ((int)r1.size() != lr1 || (int)c1.size() != lk1 || (int)r2.size() != lr2 || (int)c2.size() != lk2) return false;
-  // bit of the product (step 2's long operand, [rows | K2]) that each index bit of step 1 sets
-  std::vector<int32_t> trow(lr1), tcol(lk1);
-  std::vector<char> seen(lr1 + lk1, 0);
-  for (int32_t i = 0; i < lr1 + lk1; ++i) {
-    const int32_t t = log2_exact(i < lr1 ? r1[i] : c1[i - lr1]);
-    if (t < 0 || t >= lr1 + lk1 || seen[t]) return false;
-    seen[t] = 1;
-    (i < lr1 ? trow[i] : tcol[i - lr1]) = t;
+  for (int q = 0; q < n; ++q) {
+    const Node &nd = p.nodes[st[q]];
+    Phase &h = ph[q];
+    // each step is taken with its long operand as the rows, whatever the
+    // orientation its own kernel would use
+    h.lng = nd.m >= nd.n ? 0 : 1;
+    h.R = h.lng == 0 ? nd.m : nd.n;
+    const int64_t S = h.lng == 0 ? nd.n : nd.m;
+    h.K = nd.k;
+    if (!kok(h.K) || S != h.K) return false;
+    if (q > 0 && ((h.lng == 0 ? nd.lhs : nd.rhs) != p.L + st[q - 1] || (h.lng == 0 ? nd.copy_a : nd.copy_b) != 0))
+      return false;
+    // the oriented rows of a node are its N side when swapped, else its M side
+    const bool rows_are_runs = (h.lng == 1) == (nd.swap != 0);
+    if (!bit_offsets(rows_are_runs ? nd.row_runs : nd.col_runs, &h.r) ||
+        !bit_offsets(rows_are_runs ? nd.col_runs : nd.row_runs, &h.c))
+      return false;
+    h.lr = log2_exact(h.R);
+    h.lk = log2_exact(h.K);
+    h.lb = log2_exact(kFusePassEntries / h.K);
+    if (h.lr < 0 || (int)h.r.size() != h.lr || (int)h.c.size() != h.lk) return false;
+    if (q > 0 && h.lr != ph[q - 1].lr + ph[q - 1].lk - h.lk) return false;
+    h.tr.assign(h.lr, 0);
+    h.tc.assign(h.lk, 0);
+    std::vector<char> seen(h.lr + h.lk, 0);
+    for (int32_t i = 0; i < h.lr + h.lk; ++i) {
+      const int32_t t = log2_exact(i < h.lr ? h.r[i] : h.c[i - h.lr]);
+      if (t < 0 || t >= h.lr + h.lk || seen[t]) return false;
+      seen[t] = 1;
+      (i < h.lr ? h.tr[i] : h.tc[i - h.lr]) = t;
+    }
   }
-  // The pass's local row bits (lb1 of them; its other rows bits count the
-  // passes): every row bit that lands in K2 (so that a pass holds whole rows
-  // of the second step), then the row bits with the smallest offsets in the
-  // second product, so that a pass's stores form the longest contiguous
-  // pieces.  Rows of X are K1 contiguous entries, so any choice loads whole
-  // rows.
-  std::vector<int32_t> local, outer;
-  for (int32_t i = 0; i < lr1; ++i)
-    if (trow[i] < lk2) local.push_back(i);
-  if ((int32_t)local.size() > lb1) return false;
-  {
-    std::vector<int32_t> cand;
-    for (int32_t i = 0; i < lr1; ++i)
-      if (trow[i] >= lk2) cand.push_back(i);
-    std::stable_sort(cand.begin(), cand.end(),
-                     [&](int32_t x, int32_t y) { return r2[trow[x] - lk2] < r2[trow[y] - lk2]; });
-    for (int32_t i : cand) ((int32_t)local.size() < lb1 ? local : outer).push_back(i);
-    std::sort(local.begin(), local.end());
-    std::sort(outer.begin(), outer.end());
+  const Phase &first = ph[0], &last = ph[n - 1];
+  if (first.R < kFuseMinRows || first.lr - first.lb > kFuseOuterMax) return false;
+  // A row bit of the first long operand passes through the chain: at each
+  // later step it either lands in that step's K (it must then be local to a
+  // pass, so that a pass holds whole rows of every step) or stays a row bit;
+  // fin[] is its offset in the last product otherwise.
+  std::vector<int32_t> local, cand, outer;
+  std::vector<int64_t> fin(first.lr, 0);
+  for (int32_t b = 0; b < first.lr; ++b) {
+    int32_t t = first.tr[b];
+    bool reduced = false;
+    for (int q = 1; q < n && !reduced; ++q) {
+      if (t < ph[q].lk) reduced = true;
+      else t = ph[q].tr[t - ph[q].lk];
+    }
+    if (reduced) {
+      local.push_back(b);
+    } else {
+      fin[b] = int64_t(1) << t;
+      cand.push_back(b);
+    }
   }
-  // local bits landing in step 2's row index, ascending: the rows of the block
-  std::vector<int32_t> up;
-  for (int32_t i : local)
-    if (trow[i] >= lk2) up.push_back(trow[i] - lk2);
-  for (int32_t c = 0; c < lk1; ++c)
-    if (tcol[c] >= lk2) up.push_back(tcol[c] - lk2);
-  std::sort(up.begin(), up.end());
-  if ((int32_t)up.size() != lb2) return false;
-  auto pos = [&](int32_t t) -> int32_t {
-    if (t < lk2) return int32_t(1) << t;
-    const int32_t e = (int32_t)(std::lower_bound(up.begin(), up.end(), t - lk2) - up.begin());
-    return (int32_t)(K2 + 2) << e;  // block rows are K2 + 2 entries apart
-  };
-  f->first = s1;
-  f->second = s2;
-  f->long1 = la;
-  f->long2 = lb;
-  f->rows = R1;
-  f->k1 = (int32_t)K1;
-  f->k2 = (int32_t)K2;
-  f->nouter = lr1 - lb1;
-  for (int32_t i = 0; i < lb1; ++i) {
-    f->lrow[i] = local[i];
-    f->pos_row[i] = pos(trow[local[i]]);
+  // The pass's local rows (first.lb of them): those, then the row bits with
+  // the smallest offsets in the last product, so that a pass's stores form
+  // the longest contiguous pieces.  Rows of X are K1 contiguous entries, so
+  // any choice loads whole rows.
+  if ((int32_t)local.size() > first.lb) return false;
+  std::stable_sort(cand.begin(), cand.end(), [&](int32_t x, int32_t y) { return fin[x] < fin[y]; });
+  for (int32_t b : cand) ((int32_t)local.size() < first.lb ? local : outer).push_back(b);
+  std::sort(local.begin(), local.end());
+  std::sort(outer.begin(), outer.end());
+  // Each later step's block: the pass's bits of the previous product that are
+  // not in this step's K, ascending, are the block's rows; a previous bit t
+  // goes to place 2^t (t < lk) or (K + 2) 2^e (block row bit e).
+  std::vector<int32_t> prow = local;  // the previous phase's local rows, ascending
+  for (int q = 1; q < n; ++q) {
+    const Phase &pv = ph[q - 1], &h = ph[q];
+    std::vector<int32_t> up;
+    for (int32_t i : prow)
+      if (pv.tr[i] >= h.lk) up.push_back(pv.tr[i] - h.lk);
+    for (int32_t c = 0; c < pv.lk; ++c)
+      if (pv.tc[c] >= h.lk) up.push_back(pv.tc[c] - h.lk);
+    std::sort(up.begin(), up.end());
+    if ((int32_t)up.size() != h.lb) return false;
+    auto pos = [&](int32_t t) -> int32_t {
+      if (t < h.lk) return int32_t(1) << t;
+      const int32_t e = (int32_t)(std::lower_bound(up.begin(), up.end(), t - h.lk) - up.begin());
+      return (int32_t)(h.K + 2) << e;  // block rows are K + 2 entries apart
+    };
+    int32_t *pr = q == 1 ? f->pos_row : f->pos2_row;
+    int32_t *pc = q == 1 ? f->pos_col : f->pos2_col;
+    for (size_t i = 0; i < prow.size(); ++i) pr[i] = pos(pv.tr[prow[i]]);
+    for (int32_t c = 0; c < pv.lk; ++c) pc[c] = pos(pv.tc[c]);
+    prow = up;
   }
-  for (int32_t c = 0; c < lk1; ++c) f->pos_col[c] = pos(tcol[c]);
-  for (int32_t e = 0; e < lb2; ++e) f->out_row[e] = r2[up[e]];
-  for (int32_t c = 0; c < lk2; ++c) f->out_col[c] = c2[c];
+  for (int32_t e = 0; e < last.lb; ++e) f->out_row[e] = last.r[prow[e]];
+  for (int32_t c = 0; c < last.lk; ++c) f->out_col[c] = last.c[c];
+  f->first = st[0];
+  f->second = st[1];
+  f->third = n == 3 ? st[2] : -1;
+  f->long1 = ph[0].lng;
+  f->long2 = ph[1].lng;
+  f->long3 = n == 3 ? ph[2].lng : 0;
+  f->rows = first.R;
+  f->k1 = (int32_t)ph[0].K;
+  f->k2 = (int32_t)ph[1].K;
+  f->k3 = n == 3 ? (int32_t)ph[2].K : 0;
+  f->nouter = first.lr - first.lb;
+  for (int32_t i = 0; i < first.lb; ++i) f->lrow[i] = local[i];
   // a workgroup runs four passes at once (bits 0 and 1 of the pass index):
-  // they take the two outer row bits with the smallest offsets in the second
+  // they take the two outer row bits with the smallest offsets in the last
   // product, so that the four passes' stores join into longer pieces; the
   // rest count the workgroup's rounds, in ascending row-bit order
   if ((int32_t)outer.size() < 2) return false;
   {
     std::vector<int32_t> by = outer;
-    std::stable_sort(by.begin(), by.end(),
-                     [&](int32_t x, int32_t y) { return r2[trow[x] - lk2] < r2[trow[y] - lk2]; });
+    std::stable_sort(by.begin(), by.end(), [&](int32_t x, int32_t y) { return fin[x] < fin[y]; });
     f->wbit[0] = by[0];
     f->wbit[1] = by[1];
     std::vector<int32_t> rest, holes(local);
@@ -347,17 +374,17 @@ bool make_fused_pair(const PlanImpl &p, int32_t s1, int32_t s2, FusedPair *f) {
     holes.push_back(by[1]);
     std::sort(holes.begin(), holes.end());
     for (size_t j = 0; j < holes.size(); ++j) f->hole[j] = holes[j];
-    f->out_pass[0] = r2[trow[by[0]] - lk2];
-    f->out_pass[1] = r2[trow[by[1]] - lk2];
-    for (size_t q = 0; q < rest.size(); ++q) f->out_pass[2 + q] = r2[trow[rest[q]] - lk2];
+    f->out_pass[0] = fin[by[0]];
+    f->out_pass[1] = fin[by[1]];
+    for (size_t q = 0; q < rest.size(); ++q) f->out_pass[2 + q] = fin[rest[q]];
   }
-  // the kernel's writes must cover the second product exactly once: its
-  // offsets, one per bit, are the distinct powers of two below R2 S2
+  // the kernel's writes must cover the last product exactly once: its
+  // offsets, one per bit, are the distinct powers of two below its size
   std::vector<int64_t> outs(f->out_pass, f->out_pass + f->nouter);
-  outs.insert(outs.end(), f->out_row, f->out_row + lb2);
-  outs.insert(outs.end(), f->out_col, f->out_col + lk2);
+  outs.insert(outs.end(), f->out_row, f->out_row + last.lb);
+  outs.insert(outs.end(), f->out_col, f->out_col + last.lk);
   std::sort(outs.begin(), outs.end());
-  if ((int32_t)outs.size() != lr2 + lk2) return false;
+  if ((int32_t)outs.size() != last.lr + last.lk) return false;
   for (size_t i = 0; i < outs.size(); ++i)
     if (outs[i] != (int64_t(1) << i)) return false;
   return true;
@@ -606,7 +633,8 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   if (S == 0) p->staged_leaf.assign(L, 0);
 
   // ---- fused pairs: a non-tiny step whose product is at once the long
-  // operand of another non-tiny step, both of the FusedPair form; pairs do
+  // operand of another non-tiny step, both of the FusedPair form, extended to
+  // a third such step when all three small operands have K <= 8; chains do
   // not overlap and are taken in step order
   p->fused.clear();
   if (o.fuse && !naive && eb == 8 && o.precision == TNC_PREC_EXACT) {
@@ -622,11 +650,22 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
       if (s2 < 0) continue;
       Node &b = p->nodes[s2];
       if (b.cls == TNC_CLASS_TINY || b.splits > 1 || b.is_root) continue;
+      int32_t st[3] = {s1, s2, -1};
       FusedPair f;
-      if (!make_fused_pair(*p, s1, s2, &f)) continue;
-      a.fuse_next = s2;
-      b.fuse_prev = s1;
-      b.fused_index = (int32_t)p->fused.size();
+      if (!make_fused_chain(*p, st, 2, &f)) continue;
+      const int32_t s3 = consumer[L + s2];
+      if (s3 >= 0 && a.k <= 8 && b.k <= 8 && p->nodes[s3].k <= 8 && p->nodes[s3].cls != TNC_CLASS_TINY &&
+          p->nodes[s3].splits == 1 && !p->nodes[s3].is_root) {
+        st[2] = s3;
+        FusedPair f3;
+        if (make_fused_chain(*p, st, 3, &f3)) f = f3;
+      }
+      const int n = f.third >= 0 ? 3 : 2;
+      for (int q = 0; q + 1 < n; ++q) {
+        p->nodes[st[q]].fuse_next = st[q + 1];
+        p->nodes[st[q + 1]].fuse_prev = st[q];
+      }
+      p->nodes[st[n - 1]].fused_index = (int32_t)p->fused.size();
       p->fused.push_back(f);
     }
   }
@@ -706,11 +745,12 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
     std::vector<std::pair<uint64_t, uint64_t>> to_free;
     for (int32_t s : members) {
       Node &nd = p->nodes[s];
-      if (nd.fuse_prev >= 0) {
-        auto &d = deferred[nd.fuse_prev];
-        to_free.insert(to_free.end(), d.begin(), d.end());
-      }
       auto &frees = nd.fuse_next >= 0 ? deferred[s] : to_free;
+      if (nd.fuse_prev >= 0) {
+        // the chain's earlier steps: their operands stay until its last step
+        auto &d = deferred[nd.fuse_prev];
+        frees.insert(frees.end(), d.begin(), d.end());
+      }
       for (int w = 0; w < 2; ++w) {
         int32_t t = w == 0 ? nd.lhs : nd.rhs;
         int32_t copy = w == 0 ? nd.copy_a : nd.copy_b;
@@ -896,8 +936,9 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
       nd.runs_index = (int32_t)runs.size();
       for (auto &r : nd.row_runs) runs.push_back({r.size, r.stride});
       for (auto &r : nd.col_runs) runs.push_back({r.size, r.stride});
-      if (nd.fuse_prev >= 0) p->program.push_back({OP_FUSED, nd.fused_index, 2, 0});
-      else if (nd.fuse_next < 0)  // a pair's first step runs in the second's launch
+      if (nd.fuse_prev >= 0 && nd.fuse_next < 0)
+        p->program.push_back({OP_FUSED, nd.fused_index, p->fused[nd.fused_index].third >= 0 ? 3 : 2, 0});
+      else if (nd.fuse_next < 0 && nd.fuse_prev < 0)  // a chain's earlier steps run in its last step's launch
         p->program.push_back({first.cls == TNC_CLASS_SKINNY ? OP_SKINNY : OP_GEMM, members[0], 1, 0});
     }
   }

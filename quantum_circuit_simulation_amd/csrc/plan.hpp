@@ -71,9 +71,9 @@ struct Node {
   int32_t runs_index = 0;
   // fused pairs (see FusedPair): the first step's product is never stored;
   // both steps run in the launch of the second
-  int32_t fuse_next = -1;    // first step: the second step of its pair
-  int32_t fuse_prev = -1;    // second step: the first step of its pair
-  int32_t fused_index = -1;  // second step: index into PlanImpl::fused
+  int32_t fuse_next = -1;    // the next step of its fused chain
+  int32_t fuse_prev = -1;    // the previous step of its fused chain
+  int32_t fused_index = -1;  // a chain's last step: index into PlanImpl::fused
 };
 
 // Two chained complex64 steps run as one pass over the first step's long
@@ -87,14 +87,15 @@ constexpr int64_t kFusePassEntries = 1024;
 constexpr int32_t kFuseOuterMax = 48;
 constexpr int64_t kFuseMinRows = int64_t(1) << 16;  // smaller steps are not worth a pair
 struct FusedPair {
-  int32_t first = -1, second = -1;
-  int32_t long1 = 0, long2 = 0;  // 0: the step's lhs is its long operand, 1: its rhs
+  int32_t first = -1, second = -1, third = -1;  // third: a three-step chain (all K <= 8), else -1
+  int32_t long1 = 0, long2 = 0, long3 = 0;  // 0: the step's lhs is its long operand, 1: its rhs
   int64_t rows = 0;          // rows of the first step's long operand
-  int32_t k1 = 0, k2 = 0, nouter = 0;
+  int32_t k1 = 0, k2 = 0, k3 = 0, nouter = 0;
   int32_t lrow[8] = {};      // the pass's local row bits of the long operand, ascending
   int32_t wbit[2] = {};      // row bits set by bits 0, 1 of the pass index (a workgroup's four passes)
   int32_t hole[10] = {};     // lrow and wbit, ascending: the rest count the workgroup's rounds
   int32_t pos_row[8] = {}, pos_col[8] = {};
+  int32_t pos2_row[8] = {}, pos2_col[8] = {};  // the second step's products in the third's block
   int64_t out_row[8] = {}, out_col[8] = {};
   int64_t out_pass[kFuseOuterMax] = {};
 };

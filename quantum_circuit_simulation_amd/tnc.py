@@ -85,10 +85,12 @@ class NodeInfo(ctypes.Structure):
 
 
 class FusedInfo(ctypes.Structure):
-    _fields_ = [("first", ctypes.c_int32), ("second", ctypes.c_int32), ("long1", ctypes.c_int32),
-                ("long2", ctypes.c_int32), ("rows", ctypes.c_int64), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
+    _fields_ = [("first", ctypes.c_int32), ("second", ctypes.c_int32), ("third", ctypes.c_int32),
+                ("long1", ctypes.c_int32), ("long2", ctypes.c_int32), ("long3", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32), ("k3", ctypes.c_int32),
                 ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 8), ("hole", ctypes.c_int32 * 10),
                 ("wbit", ctypes.c_int32 * 2), ("pos_row", ctypes.c_int32 * 8), ("pos_col", ctypes.c_int32 * 8),
+                ("pos2_row", ctypes.c_int32 * 8), ("pos2_col", ctypes.c_int32 * 8),
                 ("out_row", ctypes.c_int64 * 8), ("out_col", ctypes.c_int64 * 8), ("out_pass", ctypes.c_int64 * 48)]
 
     def as_dict(self):

@@ -32,10 +32,25 @@ def _planned(data, declared, planned):
     return np.transpose(data, [declared.index(x) for x in planned])
 
 
-def emulate_pair(f, X, W1, W2, out_size):
-    """The pass kernel's index arithmetic over all rounds and waves (complex128)."""
-    k1, k2 = f["k1"], f["k2"]
-    rows1, rows2 = 1024 // k1, 1024 // k2
+def _to_block(Y, pos_row, pos_col, nrow_bits, k_in, k_next):
+    """Place products Y (round, wave, rows, k_in) in the next step's block
+    [1024 / k_next rows][k_next + 2] by the per-bit tables."""
+    nround = Y.shape[0]
+    rows_next = 1024 // k_next
+    pos = (_bits_sum(np.arange(Y.shape[2]), pos_row, nrow_bits)[:, None]
+           + _bits_sum(np.arange(k_in), pos_col, k_in.bit_length() - 1)[None, :])
+    assert len(np.unique(pos)) == pos.size and np.all(pos % (k_next + 2) < k_next)
+    block = np.zeros((nround, 4, rows_next * (k_next + 2)), dtype=np.complex128)
+    block[:, :, pos.reshape(-1)] = Y.reshape(nround, 4, -1)
+    return block.reshape(nround, 4, rows_next, k_next + 2)[..., :k_next]
+
+
+def emulate_pair(f, X, W1, W2, out_size, W3=None):
+    """The pass kernel's index arithmetic over all rounds and waves (complex128);
+    with W3, a chain of three."""
+    k1, k2, k3 = f["k1"], f["k2"], f["k3"]
+    kl = k3 if k3 else k2
+    rows1, rows2 = 1024 // k1, 1024 // kl
     lb1, lb2 = rows1.bit_length() - 1, rows2.bit_length() - 1
     nround = f["rows"] // rows1 // 4
     rnd = np.arange(nround, dtype=np.int64)
@@ -48,12 +63,11 @@ def emulate_pair(f, X, W1, W2, out_size):
     spread = _bits_sum(rho, [1 << b for b in f["lrow"]], lb1)
     rows = dep[:, None, None] + wrow[None, :, None] + spread[None, None, :]
     Y1 = X[rows] @ W1.T                                   # (round, wave, rho, j)
-    pos = _bits_sum(rho, f["pos_row"], lb1)[:, None] + _bits_sum(np.arange(k1), f["pos_col"], k1.bit_length() - 1)[None, :]
-    assert len(np.unique(pos)) == pos.size and np.all(pos % (k2 + 2) < k2)
-    block = np.zeros((nround, 4, rows2 * (k2 + 2)), dtype=np.complex128)
-    block[:, :, pos.reshape(-1)] = Y1.reshape(nround, 4, -1)
-    Z = block.reshape(nround, 4, rows2, k2 + 2)[..., :k2]
-    Y2 = Z @ W2.T                                         # (round, wave, l, j2)
+    Y2 = _to_block(Y1, f["pos_row"], f["pos_col"], lb1, k1, k2) @ W2.T
+    if k3:
+        lbm = (1024 // k2).bit_length() - 1
+        Y2 = _to_block(Y2, f["pos2_row"], f["pos2_col"], lbm, k2, k3) @ W3.T
+    k2 = kl                                               # the stored product's columns
     base = _bits_sum(rnd, f["out_pass"][2:], f["nouter"] - 2)
     wpart = (w & 1) * f["out_pass"][0] + (w >> 1) * f["out_pass"][1]
     local = (_bits_sum(np.arange(rows2), f["out_row"], lb2)[:, None]
@@ -87,6 +101,30 @@ def test_fused_tables_reproduce_the_two_steps(case, permuted):
     sub = Network(net.extents, net.leaves[:3], T2_modes, net.data[:3], name="pair")
     ref = np.asarray(oracle.contract_network(sub, Tree([0, 3], [1, 2]))).reshape(-1)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("case", [(2, 2, 2, 1, 1, 0, 16, "s"), (3, 2, 3, 1, 1, 1, 16, "o"), (2, 3, 2, 0, 2, 0, 16, "s"),
+                                  (3, 3, 3, 2, 1, 0, 16, "o")], ids=lambda c: "k{}{}{}_v{}{}{}".format(*c))
+@pytest.mark.parametrize("permuted", [False, True], ids=["aligned", "permuted"])
+def test_fused_chain_tables_reproduce_the_three_steps(case, permuted):
+    from tests.test_gpu_fused import chain3_network
+    net, tree = chain3_network(*case, seed=70 + sum(case[:7]), permuted=permuted)
+    plan = qa.Plan.from_network(net, tree)
+    assert plan.stats()["fused_pairs"] == 1
+    f = plan.fused(0)
+    assert (f["first"], f["second"], f["third"]) == (0, 1, 2) and f["long1"] == f["long2"] == f["long3"] == 0
+    L = net.num_leaves
+    order = [plan.tensor_order(t) for t in range(L + 3)]
+    data = [np.asarray(d, dtype=np.complex128) for d in net.data]
+    X = _planned(data[0], net.leaves[0], order[0]).reshape(f["rows"], f["k1"])
+    W = [_planned(data[i], net.leaves[i], order[i]).reshape(k, k) for i, k in ((1, f["k1"]), (2, f["k2"]), (3, f["k3"]))]
+    T3_modes = order[L + 2]
+    got = emulate_pair(f, X, W[0], W[1], int(np.prod([net.extents[x] for x in T3_modes])), W3=W[2])
+    sub = Network(net.extents, net.leaves[:4], T3_modes, net.data[:4], name="chain3")
+    ref = np.asarray(oracle.contract_network(sub, Tree([0, 4, 5], [1, 2, 3]))).reshape(-1)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+    for t in (L, L + 1):
+        assert plan.tensor_offset(t) == (1 << 64) - 1   # neither earlier product is stored
 
 
 def test_unfused_plan_has_no_tables():

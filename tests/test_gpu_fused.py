@@ -61,6 +61,38 @@ def chain_network(k1, k2, v, log_rows, last, seed, permuted=True, with_data=True
     return net, Tree([0, 4, 5], [1, 2, 3])
 
 
+def chain3_network(k1, k2, k3, v2, v3a, v3b, log_rows, last, seed, permuted=True, with_data=True):
+    """Three chained absorbs: T (outer modes O, A2, A3, K1) takes W1 (K1 ->
+    S1), then W2 over K2 = v2 modes of S1 + the k2 - v2 modes A2 of T (K2 ->
+    S2), then W3 over K3 = v3a modes of S2 + v3b further modes of S1 + the
+    rest A3 from T (K3 -> S3); a last step contracts one mode of the third
+    product with a vector (an outer mode for last = "o", a mode of S3 for
+    "s").  All extents 2; T has 2^log_rows rows of K1 entries."""
+    rng = np.random.default_rng(seed)
+    na2, na3 = k2 - v2, k3 - v3a - v3b
+    assert na2 >= 0 and na3 >= 0 and v2 + v3b <= k1 and v3a <= k2
+    n_outer = log_rows - na2 - na3
+    assert n_outer >= 2
+    labels = iter(range(1000))
+    take = lambda n: [next(labels) for _ in range(n)]
+    O, K1, S1, A2, S2, A3, S3 = take(n_outer), take(k1), take(k1), take(na2), take(k2), take(na3), take(k3)
+    K2 = S1[:v2] + A2
+    K3 = S2[:v3a] + S1[v2:v2 + v3b] + A3
+    vmode = O[0] if last == "o" else S3[0]
+    leaves = [O + A2 + A3 + K1, S1 + K1, S2 + K2, S3 + K3]
+    out = [x for x in O + S1[v2 + v3b:] + S2[v3a:] + S3 if x != vmode]
+    if permuted:
+        leaves = [list(rng.permutation(m)) for m in leaves]
+        out = list(rng.permutation(out))
+    leaves.append([vmode])
+    n = next(labels)
+    ext = np.full(n, 2, dtype=np.int64)
+    data = [_cn(rng, [2] * len(l)) for l in leaves] if with_data else None
+    net = Network(ext, [list(map(int, l)) for l in leaves], [int(x) for x in out], data,
+                  name=f"chain3_k{k1}{k2}{k3}_v{v2}{v3a}{v3b}_r{log_rows}_{last}")
+    return net, Tree([0, 5, 6, 7], [1, 2, 3, 4])
+
+
 # (log2 K1, log2 K2, shared modes v, log2 rows of T, last-step mode); a
 # phase with K <= 8 runs on the vector ALU, K >= 16 on the matrix cores
 CASES = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "s"), (4, 4, 4, 16, "o"), (4, 5, 2, 17, "s"), (5, 4, 1, 16, "s"),
@@ -82,6 +114,23 @@ def test_fused_pair_matches_oracle(case):
 def test_aligned_orders(case):
     net, tree = chain_network(*case, seed=31, permuted=False)
     _check(net, tree, expect_kernel="k_fused2", kind="fused")
+
+
+# three-step chains (every K <= 8): (log2 K1, K2, K3, v2, v3a, v3b, log2 rows, last)
+CHAIN3 = [(2, 2, 2, 1, 1, 0, 16, "s"), (2, 2, 2, 2, 0, 0, 17, "o"), (3, 2, 3, 1, 1, 1, 16, "s"),
+          (2, 3, 2, 0, 2, 0, 17, "s"), (3, 3, 3, 2, 1, 0, 16, "o"), (2, 2, 3, 0, 1, 1, 18, "s")]
+
+
+@pytest.mark.parametrize("case", CHAIN3, ids=lambda c: "k{}{}{}_v{}{}{}_r{}_{}".format(*c))
+def test_fused_chain_of_three_matches_oracle(case):
+    net, tree = chain3_network(*case, seed=800 + sum(case[:7]))
+    ks = _check(net, tree, expect_kernel="k_fused2", kind="fused")
+    assert len(ks) == 1 and ks[0].count(",") == 2, ks   # one k_fused2<K1,K2,K3> launch
+
+
+def test_sliced_chain_of_three():
+    net, tree = chain3_network(2, 2, 2, 1, 1, 0, 18, "o", seed=91)
+    _check(net, tree, expect_kernel="k_fused2", kind="fused", sliced=[net.leaves[4][0]])
 
 
 def test_fuse_off_runs_the_steps_alone():

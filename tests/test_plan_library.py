@@ -120,6 +120,26 @@ def test_fused_pair_plans_match_oracle(case, permuted):
         assert ref.fused == ([] if nopair or case[3] - 1 < 16 else [(0, 1)])
 
 
+@pytest.mark.parametrize("case", [(2, 2, 2, 1, 1, 0, 16, "s"), (3, 2, 3, 1, 1, 1, 17, "o"), (2, 3, 2, 0, 2, 0, 16, "o"),
+                                  (3, 3, 3, 2, 1, 0, 16, "s"), (2, 2, 2, 0, 0, 0, 15, "s")],
+                         ids=lambda c: "k{}{}{}_v{}{}{}_r{}".format(*c))
+@pytest.mark.parametrize("permuted", [False, True], ids=["aligned", "permuted"])
+def test_fused_chain_plans_match_oracle(case, permuted):
+    from tests.test_gpu_fused import chain3_network
+    net, tree = chain3_network(*case, seed=50 + sum(case[:7]), permuted=permuted, with_data=False)
+    lib, ref = _check(net, tree)
+    assert ref.fused == ([] if case[6] < 16 else [(0, 1, 2)])
+    if case[7] == "o":
+        lib, ref = _check(net, tree, sliced=[net.leaves[4][0]])
+
+
+def test_state_vector_plan_with_fused_chains_matches_oracle():
+    c = circuits.brickwork(30, 14, 303)
+    net = c.to_network(open_qubits=range(6))
+    lib, ref = _check(net, trees.state_vector_tree(net))
+    assert len(ref.fused) == 68 and sum(len(x) == 3 for x in ref.fused) == 67
+
+
 def test_grid_depth16_plan_with_fused_pairs_matches_oracle():
     net = circuits.grid_fsim(7, 8, 16, 505).to_network()
     tree, sl, _ = trees.stored_tree("grid_7x8_d16", net)
