@@ -679,6 +679,21 @@ def step_roofline_ms(m, n, k, eb=8):
     return 1e3 * max(eb * (m * k + n * k + m * n) / (PEAK_HBM * 1e9), 8.0 * m * n * k / (PEAK_FP32_MFMA * 1e12))
 
 
+def _fused_chain(plan, last):
+    """Steps of the fused chain that ends at step `last`, first to last: each
+    step's product is the next one's operand."""
+    first = plan.node(last)["fused_with"]
+    out_of = {}
+    for s in range(plan.num_steps):
+        nd = plan.node(s)
+        out_of[nd["lhs"]] = s
+        out_of[nd["rhs"]] = s
+    chain = [first]
+    while chain[-1] != last:
+        chain.append(out_of[plan.node(chain[-1])["out"]])
+    return chain
+
+
 def tree_kernel_roofline(plan, ops, runs=1):
     """Per-kernel totals of one timed run (tnc_execute_timed records, whose
     times sum over `runs` slices): algorithmic flops and bytes of the GEMM
@@ -693,14 +708,15 @@ def tree_kernel_roofline(plan, ops, runs=1):
             m, n, k = nd["m"], nd["n"], nd["k"]
             f, b = 8.0 * m * n * k * o["launches"], 8.0 * (m * k + n * k + m * n) * o["launches"]
         elif o["kind"] == "fused":
-            # a fused pair: both steps' flops; its bytes read the first step's
-            # operands and the second's small operand and write the second's
-            # product once (the first product stays on chip)
-            n2 = plan.node(o["step"])
-            n1 = plan.node(n2["fused_with"])
-            f = 8.0 * (n1["m"] * n1["n"] * n1["k"] + n2["m"] * n2["n"] * n2["k"]) * o["launches"]
-            b = 8.0 * (n1["m"] * n1["k"] + n1["n"] * n1["k"] + min(n2["m"], n2["n"]) * n2["k"]
-                       + n2["m"] * n2["n"]) * o["launches"]
+            # a fused chain (its last step's launch): every step's flops; its
+            # bytes read the first step's operands and the later steps' small
+            # operands and write the last product once (the others stay on chip)
+            chain = _fused_chain(plan, o["step"])
+            n1, nl = plan.node(chain[0]), plan.node(chain[-1])
+            f = 8.0 * sum(plan.node(c)["m"] * plan.node(c)["n"] * plan.node(c)["k"] for c in chain) * o["launches"]
+            b = 8.0 * (n1["m"] * n1["k"] + n1["n"] * n1["k"]
+                       + sum(min(plan.node(c)["m"], plan.node(c)["n"]) * plan.node(c)["k"] for c in chain[1:])
+                       + nl["m"] * nl["n"]) * o["launches"]
         else:
             f = b = 0.0
         acc = per.setdefault(o["kernel"], {"ms": 0.0, "flop": 0.0, "bytes": 0.0, "launches": 0})

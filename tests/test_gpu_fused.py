@@ -1,6 +1,7 @@
-"""Fused pairs of steps (k_fused2): a long tensor T absorbs a small W1 (16 or
-32 entries of K, as many outputs) and the product is reduced at once
-against another small W2, in one pass over T.  Every output entry of the
+"""Fused chains of steps (k_fused2): a long tensor T absorbs a small W1 (4,
+8, 16 or 32 entries of K, as many outputs) and the product is reduced at
+once against another small W2 (and, all K <= 8, a third W3), in one pass
+over T.  Every output entry of the
 whole contraction against the oracle, for (K1, K2) in {4, 8, 16, 32}^2 (the
 vector-ALU and matrix-core phases and their mixes), with
 the second step reducing 0 .. all of the first step's new modes, random
