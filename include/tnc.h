@@ -113,11 +113,11 @@ typedef struct {
                                    the whole result, e.g. one range per process or per call */
   int32_t fuse;               /* 1: where a long tensor absorbs a small one (4, 8, 16 or 32
                                  entries of K, as many outputs) and the product is reduced at once
-                                 against another such small tensor, both steps run in one pass
-                                 over the
-                                 long operand and the first product is never stored (complex64,
-                                 exact, lifetime order, every extent a power of two, long side
-                                 >= 2^16 rows).  0: every step runs on its own. */
+                                 against another such small tensor (and, all K 4 or 8, up to
+                                 TNC_FUSE_MAX_STEPS steps in a row), the chain runs in one pass
+                                 over the long operand and only its last product is stored
+                                 (complex64, exact, lifetime order, every extent a power of two,
+                                 long side >= 2^16 rows).  0: every step runs on its own. */
 } tnc_plan_options;
 
 /* Arithmetic of the GEMM-class steps of a complex64 plan.  EXACT: FP32
@@ -164,8 +164,8 @@ typedef struct {
   uint64_t header_bytes;         /* workspace prefix holding kernel descriptors */
   uint64_t arena_bytes;          /* arena high-water mark */
   uint64_t workspace_bytes;      /* header_bytes + arena_bytes */
-  int32_t fused_pairs;           /* fused chains (pairs, or three steps with K <= 8) run as one
-                                    pass each (tnc_plan_options.fuse) */
+  int32_t fused_pairs;           /* fused chains (2 .. TNC_FUSE_MAX_STEPS steps) run as one pass
+                                    each (tnc_plan_options.fuse) */
 } tnc_plan_stats;
 
 tnc_status tnc_plan_stats_get(tnc_plan_t plan, tnc_plan_stats *stats);
@@ -176,7 +176,7 @@ tnc_status tnc_plan_tensor_order(tnc_plan_t plan, int32_t id, int32_t *modes, in
 
 /* Arena offset (bytes, from the arena start) of SSA tensor `id`: a staged
  * leaf copy or an intermediate.  UINT64_MAX: read in place (leaf), written
- * to `out` (root) or never stored (the first product of a fused pair). */
+ * to `out` (root) or never stored (a fused chain's products but the last). */
 tnc_status tnc_plan_tensor_offset(tnc_plan_t plan, int32_t id, uint64_t *offset);
 
 typedef struct {
@@ -201,34 +201,35 @@ typedef struct {
 tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
 
 /* A fused chain's pass tables (index 0 .. fused_pairs - 1, in step order),
- * for inspection and host-side checks.  The chain runs steps `first`,
- * `second` and, for a chain of three (all K <= 8), `third`; their long
- * operands are lhs (long = 0) or rhs (1), and each step's long operand is the
- * previous step's product.  The tables below describe a pair; in a chain of
- * three the second product goes to the third step's block through pos2_*
- * as the first goes to the second's through pos_*, and out_* place the third
- * product.  Every index is a
- * sum of one offset per set bit.  A pass takes 1024 entries of the first
- * long operand X (row-major [rows, k1]): its local row rho (0 .. 1024/k1 - 1)
+ * for inspection and host-side checks.  The chain runs steps step[0 ..
+ * nsteps - 1] (2 .. TNC_FUSE_MAX_STEPS; unused entries -1): each step's long
+ * operand is the previous step's product (the first step's: its lhs for
+ * longop = 0, else its rhs) and its small operand has k[q] x k[q] entries
+ * (4, 8, 16 or 32; in chains of three or more every k is 4 or 8, and the
+ * steps between the first and the last share one k).  Every index is a sum
+ * of one offset per set bit.  A pass takes 1024 entries of the first long
+ * operand X (row-major [rows, k[0]]): its local row rho (0 .. 1024/k[0] - 1)
  * is X row spread(rho) + round part + wave part, where spread puts bit j of
  * rho at row bit lrow[j]; the workgroup's four passes w = 0 .. 3 add
  * (w & 1) << wbit[0] and (w >> 1) << wbit[1]; a round index fills the row
- * bits outside hole[] (lrow and wbit, ascending) in ascending order.  The
- * first product of (rho, column j) goes to complex entry sum pos_row[bits of
- * rho] + sum pos_col[bits of j] of the block [1024/k2 rows][k2 + 2]; the
- * second product of block row l and column j2 goes to the second product's
- * offset sum out_row[bits of l] + sum out_col[bits of j2] + (w & 1) out_pass[0]
+ * bits outside hole[] (lrow and wbit, ascending) in ascending order.  Step
+ * q's product of its block row l and column j goes to complex entry
+ * sum pos_row[q][bits of l] + sum pos_col[q][bits of j] of step q + 1's block
+ * [1024/k[q + 1] rows][k[q + 1] + 2] (step 0's block rows are the pass's rows
+ * rho); the last step's product of block row l and column j goes to offset
+ * sum out_row[bits of l] + sum out_col[bits of j] + (w & 1) out_pass[0]
  * + (w >> 1) out_pass[1] + sum out_pass[2 + q] over bits q of the round.
- * Errors: INVALID_ARG (no such pair). */
+ * Errors: INVALID_ARG (no such chain). */
+#define TNC_FUSE_MAX_STEPS 6
 typedef struct {
-  int32_t first, second, third;  /* third: -1 for a pair */
-  int32_t long1, long2, long3;
+  int32_t nsteps;
+  int32_t step[TNC_FUSE_MAX_STEPS];
+  int32_t longop[TNC_FUSE_MAX_STEPS];
+  int32_t k[TNC_FUSE_MAX_STEPS];
   int64_t rows;
-  int32_t k1, k2, k3, nouter;    /* k3: 0 for a pair */
+  int32_t nouter;
   int32_t lrow[8], hole[10], wbit[2];
-  int32_t pos_row[8], pos_col[8];
-  int32_t pos2_row[8], pos2_col[8];  /* a chain of three: the second product's places
-                                        in the third step's block, as pos_* */
+  int32_t pos_row[TNC_FUSE_MAX_STEPS - 1][8], pos_col[TNC_FUSE_MAX_STEPS - 1][8];
   int64_t out_row[8], out_col[8];
   int64_t out_pass[48];
 } tnc_fused_info;
@@ -238,7 +239,7 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info);
 /*
  * Run the plan.
  *   leaves[L]   device pointers to the leaf buffers (declared orders); a leaf
- *               that a fused pair reads in place as its long operand must be
+ *               that a fused chain reads in place as its long operand must be
  *               16-byte aligned (INVALID_ARG otherwise, before any launch)
  *   out         device pointer, prod(out extents) entries of the plan's dtype,
  *               overwritten
@@ -284,7 +285,7 @@ typedef enum {
   TNC_OP_GEMM = 3,          /* one matrix-core GEMM step */
   TNC_OP_COPY_TILED = 4,    /* one large permuting copy through LDS tiles */
   TNC_OP_HEADER = 5,        /* pointer table and descriptor upload */
-  TNC_OP_FUSED = 6          /* one pass running a fused pair of steps (`step`: the second) */
+  TNC_OP_FUSED = 6          /* one pass running a fused chain of steps (`step`: its last) */
 } tnc_op_kind;
 
 typedef struct {

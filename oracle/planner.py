@@ -21,7 +21,7 @@ ascending label order).  The page describes this as the emergent property of
 the reverse pass (section 1.4, the paragraph after the algorithm).
 
 Everything else (node classes, operand orientation, output runs, split-K,
-grouping, fused pairs and first-fit arena) is this project's own execution
+grouping, fused chains and first-fit arena) is this project's own execution
 design; the rules are restated here from their definitions.
 """
 
@@ -42,8 +42,9 @@ CLASS_GEMM = 2
 SKINNY_MAX_SIDE = 16        # skinny when the smaller of m, n is at most this
 GEMM_NOMINAL_TILE = 128     # nominal tile edge used only by the split-K rule
 EARLY_STAGE_MAX = 1 << 16   # staged leaves up to this many entries are copied before the first group
-FUSE_PASS_ENTRIES = 1024    # entries of the long operand in one pass of a fused pair
-FUSE_MIN_ROWS = 1 << 16     # fused pairs need at least this many rows of the long operand
+FUSE_PASS_ENTRIES = 1024    # entries of the long operand in one pass of a fused chain
+FUSE_MIN_ROWS = 1 << 16     # fused chains need at least this many rows of the long operand
+FUSE_MAX_STEPS = 6          # the longest fused chain
 NONE = (1 << 64) - 1        # "not in the arena"
 
 
@@ -259,7 +260,7 @@ class Plan:
     bytes: int
     max_elems: int
     num_slices: int
-    fused: List[tuple] = field(default_factory=list)   # fused chains: (first, second[, third]) steps
+    fused: List[tuple] = field(default_factory=list)   # fused chains: their steps, in order
 
 
 def _runs(c_order, ext, row_set):
@@ -347,78 +348,87 @@ def _log2(v: int) -> int:
 
 
 def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
-    """Pairs (s1, s2) of steps run as one pass: a long tensor T absorbs a small
-    one (K = S = 4, 8, 16 or 32 entries) and the product T1 is at once the long
+    """Chains of steps run as one pass: a long tensor T absorbs a small one
+    (K = S = 4, 8, 16 or 32 entries) and the product T1 is at once the long
     operand of the next step, which reduces it against another small tensor
     (K = S = 4, 8, 16 or 32), with every extent of the modes involved a power
-    of two,
-    T holding at least 2^16 rows, both steps outside the tiny class, neither
-    split over K nor the root, T1 read in place, and the modes of the second
-    step's K that T carries spanning at most 1024 / K1 index values (so that a
-    pass over 1024 entries of T yields whole rows of the second step).  A pair
-    whose two K are at most 8 extends to the next step in the same way (K3 =
-    S3 = 4 or 8, the second product read in place, T's modes reduced by the
-    second and third steps together spanning at most 1024 / K1 values).
-    Chains are taken in step order and do not overlap.  Complex64, lifetime
-    order."""
+    of two, T holding at least 2^16 rows, both steps outside the tiny class,
+    neither split over K nor the root, T1 read in place, and the modes of the
+    second step's K that T carries spanning at most 1024 / K1 index values (so
+    that a pass over 1024 entries of T yields whole rows of the second step).
+    A chain extends to the next step in the same way, one step at a time up to
+    FUSE_MAX_STEPS steps, while every K of the chain is 4 or 8, the steps
+    between the first and the last share one K, and the modes of T reduced by
+    all later steps together span at most 1024 / K1 values (256 / K1 for
+    chains of four or more, which leaves two of a pass's row bits to give its
+    stores contiguous pieces).  Chains are taken in step order and do not
+    overlap.  Complex64, lifetime order."""
     if not fuse or policy != LIFETIME or eb != 8:
         return []
     consumer = {}
     for nd in nodes:
         consumer[nd.lhs] = nd.step
         consumer[nd.rhs] = nd.step
-    pairs = []
+    chains = []
     taken = set()
 
     def long_short(nd):
         # (long operand, its rows, the short side) with lhs taken when m >= n
         return (nd.lhs, nd.m, nd.n) if nd.m >= nd.n else (nd.rhs, nd.n, nd.m)
 
+    def link(prev, s, ks):
+        """The small operand of step s when it may follow step prev in a
+        chain whose K so far are ks, else None."""
+        c = nodes[s]
+        t, _, sw = long_short(c)
+        if c.cls == CLASS_TINY or c.splits > 1 or s == len(nodes) - 1:
+            return None
+        if t != L + prev or (c.copy_a if t == c.lhs else c.copy_b) or sw != c.k:
+            return None
+        if len(ks) == 1:
+            if c.k not in (4, 8, 16, 32):
+                return None
+        elif c.k not in (4, 8) or any(k not in (4, 8) for k in ks) or any(k != ks[1] for k in ks[1:]):
+            return None   # a chain of three or more: K 4 or 8, one K between the first and the last
+        small = c.rhs if t == c.lhs else c.lhs
+        if not all(_is_pow2(ext[x]) for x in sets[small]):
+            return None
+        return small
+
     for a in nodes:
         s1 = a.step
         if a.cls == CLASS_TINY or a.splits > 1 or s1 in taken or (L + s1) not in consumer:
             continue
-        s2 = consumer[L + s1]
-        b = nodes[s2]
-        if b.cls == CLASS_TINY or b.splits > 1 or s2 == len(nodes) - 1:
-            continue
         t, r1, s1w = long_short(a)
-        t1, _, s2w = long_short(b)
-        if a.k not in (4, 8, 16, 32) or s1w != a.k or b.k not in (4, 8, 16, 32) or s2w != b.k:
-            continue
-        if t1 != L + s1 or (b.copy_a if t1 == b.lhs else b.copy_b):
+        if a.k not in (4, 8, 16, 32) or s1w != a.k or not _is_pow2(r1) or r1 < FUSE_MIN_ROWS:
             continue
         small1 = a.rhs if t == a.lhs else a.lhs
-        small2 = b.rhs if t1 == b.lhs else b.lhs
-        if not _is_pow2(r1) or r1 < FUSE_MIN_ROWS:
+        if not all(_is_pow2(ext[x]) for u in (t, small1) for x in sets[u]):
             continue
-        if not all(_is_pow2(ext[x]) for u in (t, small1, small2) for x in sets[u]):
+        chain, ks, bits_t = [s1], [a.k], 0
+        while len(chain) < FUSE_MAX_STEPS and (L + chain[-1]) in consumer:
+            s = consumer[L + chain[-1]]
+            small = link(chain[-1], s, ks)
+            if small is None:
+                break
+            # the modes of T that the chain's later steps reduce, in index bits;
+            # a chain of four or more leaves two of the pass's rows free
+            bits = bits_t + sum(_log2(ext[x]) for x in sets[t] if x in sets[small])
+            if bits > _log2(FUSE_PASS_ENTRIES // a.k) - (2 if len(chain) >= 3 else 0):
+                break
+            chain.append(s)
+            ks.append(nodes[s].k)
+            bits_t = bits
+        if len(chain) < 2:
             continue
-        # the second step's reduced modes that come from T, in index bits
-        k2_from_t = [x for x in sets[t] if x in sets[small2]]
-        bits_t = sum(_log2(ext[x]) for x in k2_from_t)
-        if bits_t > _log2(FUSE_PASS_ENTRIES // a.k):
-            continue
-        chain = [s1, s2]
-        s3 = consumer.get(L + s2)
-        if s3 is not None and a.k <= 8 and b.k <= 8:
-            c = nodes[s3]
-            t2, _, s3w = long_short(c)
-            small3 = c.rhs if t2 == c.lhs else c.lhs
-            k3_from_t = [x for x in sets[t] if x in sets[small3]]
-            if (c.cls != CLASS_TINY and c.splits == 1 and s3 != len(nodes) - 1 and c.k in (4, 8) and s3w == c.k
-                    and t2 == L + s2 and not (c.copy_a if t2 == c.lhs else c.copy_b)
-                    and all(_is_pow2(ext[x]) for x in sets[small3])
-                    and bits_t + sum(_log2(ext[x]) for x in k3_from_t) <= _log2(FUSE_PASS_ENTRIES // a.k)):
-                chain.append(s3)
         for x, y in zip(chain, chain[1:]):
             nodes[x].fuse_next, nodes[y].fuse_prev = y, x
         for x in chain[:-1]:
             nodes[x].fused_with = chain[-1]
         nodes[chain[-1]].fused_with = chain[0]
         taken.update(chain)
-        pairs.append(tuple(chain))
-    return pairs
+        chains.append(tuple(chain))
+    return chains
 
 
 def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), align=256,
@@ -551,8 +561,8 @@ def make_plan(extents, leaves, out_modes, lhs, rhs, policy=LIFETIME, sliced=(), 
                     if policy == LIFETIME:
                         tensor_off[t] = off
                     early.add((s, which))
-    # a fused pair's first step keeps its operands until the pair's launch
-    # (the second step's group) and never stores its product
+    # a fused chain's earlier steps keep their operands until the chain's
+    # launch (its last step's group) and never store their products
     deferred = {}
     for members in groups:
         to_free = []

@@ -47,7 +47,8 @@ tnc_status check(hipError_t e, hipStream_t stream, const char *what) {
   return TNC_OK;
 }
 
-static_assert(tnc::kFuseEntries == tnc::kFusePassEntries && tnc::kFuseMaxOuter == tnc::kFuseOuterMax,
+static_assert(tnc::kFuseEntries == tnc::kFusePassEntries && tnc::kFuseMaxOuter == tnc::kFuseOuterMax &&
+                  tnc::kFuseMaxChain == tnc::kFuseMaxSteps && TNC_FUSE_MAX_STEPS == tnc::kFuseMaxSteps,
               "fused-pair pass size and table length agree between planner and kernel");
 
 const char *op_name(int kind) {
@@ -184,26 +185,23 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info) 
   if (!plan || !info) return TNC_ERR_INVALID_ARG;
   const auto &p = plan->impl;
   if (index < 0 || index >= (int32_t)p.fused.size()) return TNC_ERR_INVALID_ARG;
-  const tnc::FusedPair &f = p.fused[index];
+  const tnc::FusedChain &f = p.fused[index];
   std::memset(info, 0, sizeof(*info));
-  info->first = f.first;
-  info->second = f.second;
-  info->third = f.third;
-  info->long1 = f.long1;
-  info->long2 = f.long2;
-  info->long3 = f.long3;
+  info->nsteps = f.nsteps;
+  for (int q = 0; q < tnc::kFuseMaxSteps; ++q) {
+    info->step[q] = q < f.nsteps ? f.step[q] : -1;
+    info->longop[q] = f.longop[q];
+    info->k[q] = f.k[q];
+  }
   info->rows = f.rows;
-  info->k1 = f.k1;
-  info->k2 = f.k2;
-  info->k3 = f.k3;
   info->nouter = f.nouter;
   for (int i = 0; i < 10; ++i) info->hole[i] = f.hole[i];
   for (int i = 0; i < 8; ++i) {
     info->lrow[i] = f.lrow[i];
-    info->pos2_row[i] = f.pos2_row[i];
-    info->pos2_col[i] = f.pos2_col[i];
-    info->pos_row[i] = f.pos_row[i];
-    info->pos_col[i] = f.pos_col[i];
+    for (int q = 0; q + 1 < tnc::kFuseMaxSteps; ++q) {
+      info->pos_row[q][i] = f.pos_row[q][i];
+      info->pos_col[q][i] = f.pos_col[q][i];
+    }
     info->out_row[i] = f.out_row[i];
     info->out_col[i] = f.out_col[i];
   }
@@ -254,14 +252,14 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
   (void)hipGetLastError();
   for (int32_t l = 0; l < p.L; ++l)
     if (!leaves[l]) return TNC_ERR_INVALID_ARG;
-  // a fused pair reads its long operand with 16-byte loads; a leaf read in
+  // a fused chain reads its long operand with 16-byte loads; a leaf read in
   // place must be 16-byte aligned (checked before anything is enqueued)
   for (const auto &f : p.fused) {
-    const tnc::Node &n1 = p.nodes[f.first];
-    const int32_t t = f.long1 == 0 ? n1.lhs : n1.rhs;
-    const int32_t copied = f.long1 == 0 ? n1.copy_a : n1.copy_b;
+    const tnc::Node &n1 = p.nodes[f.step[0]];
+    const int32_t t = f.longop[0] == 0 ? n1.lhs : n1.rhs;
+    const int32_t copied = f.longop[0] == 0 ? n1.copy_a : n1.copy_b;
     if (t < p.L && !copied && (reinterpret_cast<uintptr_t>(leaves[t]) & 15) != 0) {
-      g_last_error = "leaf " + std::to_string(t) + " is the long operand of a fused pair and must be 16-byte "
+      g_last_error = "leaf " + std::to_string(t) + " is the long operand of a fused chain and must be 16-byte "
                      "aligned (or plan with fuse = 0)";
       return TNC_ERR_INVALID_ARG;
     }
@@ -409,29 +407,29 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           break;
         }
         case tnc::OP_FUSED: {
-          const tnc::FusedPair &f = p.fused[op.first];
-          const tnc::Node &n1 = p.nodes[f.first], &n2 = p.nodes[f.second];
-          const tnc::Node &nl = p.nodes[f.third >= 0 ? f.third : f.second];
+          const tnc::FusedChain &f = p.fused[op.first];
+          const int ns = f.nsteps;
+          const tnc::Node &n1 = p.nodes[f.step[0]], &nl = p.nodes[f.step[ns - 1]];
           tnc::Fused2Args fa{};
-          fa.X = reinterpret_cast<const float2 *>(operand(n1, f.long1));
-          fa.W1 = reinterpret_cast<const float2 *>(operand(n1, 1 - f.long1));
-          fa.W2 = reinterpret_cast<const float2 *>(operand(n2, 1 - f.long2));
-          fa.W3 = f.third >= 0 ? reinterpret_cast<const float2 *>(operand(nl, 1 - f.long3)) : nullptr;
+          fa.X = reinterpret_cast<const float2 *>(operand(n1, f.longop[0]));
+          for (int q = 0; q < ns; ++q)
+            fa.W[q] = reinterpret_cast<const float2 *>(operand(p.nodes[f.step[q]], 1 - f.longop[q]));
           fa.C = reinterpret_cast<float2 *>(resolve(tnc::kBufArena, nl.c_off));
           fa.R = f.rows;
-          fa.K1 = f.k1;
-          fa.K2 = f.k2;
-          fa.K3 = f.k3;
+          fa.K1 = f.k[0];
+          fa.K2 = f.k[1];
+          fa.K3 = ns > 2 ? f.k[ns - 1] : 0;
+          fa.nsteps = ns;
           fa.nouter = f.nouter;
           fa.wbit[0] = f.wbit[0];
           fa.wbit[1] = f.wbit[1];
           for (int i = 0; i < 10; ++i) fa.hole[i] = f.hole[i];
           for (int i = 0; i < 8; ++i) {
             fa.lrow[i] = f.lrow[i];
-            fa.pos2_row[i] = f.pos2_row[i];
-            fa.pos2_col[i] = f.pos2_col[i];
-            fa.pos_row[i] = f.pos_row[i];
-            fa.pos_col[i] = f.pos_col[i];
+            for (int q = 0; q + 1 < ns; ++q) {
+              fa.pos_row[q][i] = f.pos_row[q][i];
+              fa.pos_col[q][i] = f.pos_col[q][i];
+            }
             fa.out_row[i] = f.out_row[i];
             fa.out_col[i] = f.out_col[i];
           }
@@ -537,9 +535,9 @@ tnc_status tnc_execute_timed(tnc_plan_t plan, const void *const *leaves, void *o
                   : op.kind == tnc::OP_FUSED ? TNC_OP_FUSED : TNC_OP_GEMM;
     if (op.kind == tnc::OP_SKINNY || op.kind == tnc::OP_GEMM) rec[i].step = op.first;
     if (op.kind == tnc::OP_FUSED) {
-      const tnc::FusedPair &f = p.fused[op.first];
-      rec[i].step = f.third >= 0 ? f.third : f.second;
-      rec[i].count = f.third >= 0 ? 3 : 2;
+      const tnc::FusedChain &f = p.fused[op.first];
+      rec[i].step = f.step[f.nsteps - 1];
+      rec[i].count = f.nsteps;
     }
     if (op.kind == tnc::OP_COPY || op.kind == tnc::OP_TINY_GROUP) rec[i].count = op.count;
   }

@@ -1245,10 +1245,11 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   // holds W itself
   constexpr bool V1 = K1 <= 8, V2 = K2 <= 8;
   constexpr int BT1 = V1 ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
-  constexpr int BT2 = V2 ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
+  constexpr int NMID = K3 ? kFuseMaxChain - 2 : 1;  // the most steps with K2 (all but the first and last)
+  constexpr int BT2 = V2 ? NMID * 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
   constexpr int BT3 = K3 ? 2 * K3 * K3 : 2;
-  // chains of three run every phase on the vector ALU
-  static_assert(K3 == 0 || (V1 && V2 && K3 <= 8), "three-step chains have K <= 8");
+  // chains of three or more run every phase on the vector ALU
+  static_assert(K3 == 0 || (V1 && V2 && K3 <= 8), "chains of three or more have K <= 8");
   static_assert((1 << LB1) == ROWS1 && 8 * WB < 65536, "fused block layout");
   static_assert(kFuseMaxOuter % 6 == 0, "pass-index chunks");
   __shared__ float4 buf[4][WB];
@@ -1260,17 +1261,20 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
 
   if constexpr (V1) {
-    for (int e = tid; e < K1 * K1; e += 256) *(float2 *)&bt1[2 * e] = a.W1[e];
+    for (int e = tid; e < K1 * K1; e += 256) *(float2 *)&bt1[2 * e] = a.W[0][e];
   } else {
-    fused_btable<K1>(a.W1, bt1, tid);
+    fused_btable<K1>(a.W[0], bt1, tid);
   }
   if constexpr (V2) {
-    for (int e = tid; e < K2 * K2; e += 256) *(float2 *)&bt2[2 * e] = a.W2[e];
+    // a chain's middle steps' tables one after another
+    const int nmid = K3 ? a.nsteps - 2 : 1;
+    for (int e = tid; e < nmid * K2 * K2; e += 256)
+      *(float2 *)&bt2[2 * e] = a.W[1 + e / (K2 * K2)][e % (K2 * K2)];
   } else {
-    fused_btable<K2>(a.W2, bt2, tid);
+    fused_btable<K2>(a.W[1], bt2, tid);
   }
   if constexpr (K3 != 0)
-    for (int e = tid; e < K3 * K3; e += 256) *(float2 *)&bt3[2 * e] = a.W3[e];
+    for (int e = tid; e < K3 * K3; e += 256) *(float2 *)&bt3[2 * e] = a.W[a.nsteps - 1][e];
   for (int t = tid; t < ROWSL + KL; t += 256) {
     int64_t o = 0;
     if (t < ROWSL) {
@@ -1352,28 +1356,26 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   // place of a phase-1 product in the phase-2 block: lane part (its column
   // and the row bit h) plus the row bits fixed by (nb, r)
   const int j1 = K1 == 32 ? l32 : (l32 & 15);
-  int lane_pos = h ? a.pos_row[2] : 0;
+  const int32_t *prow0 = a.pos_row[0], *pcol0 = a.pos_col[0];
+  int lane_pos = h ? prow0[2] : 0;
 #pragma unroll
   for (int c = 0; c < (K1 == 32 ? 5 : 4); ++c)
-    if ((j1 >> c) & 1) lane_pos += a.pos_col[c];
+    if ((j1 >> c) & 1) lane_pos += pcol0[c];
   auto rpos = [&](int nb, int r) {
     int p = 0;
-    if (r & 1) p += a.pos_row[0];
-    if (r & 2) p += a.pos_row[1];
-    if (r & 4) p += a.pos_row[3];
-    if (r & 8) p += a.pos_row[4];
-    if (nb & 1) p += a.pos_row[5];
+    if (r & 1) p += prow0[0];
+    if (r & 2) p += prow0[1];
+    if (r & 4) p += prow0[3];
+    if (r & 8) p += prow0[4];
+    if (nb & 1) p += prow0[5];
     return p;
   };
-  // vector-ALU phases: lane l takes pass rows l + 64 i; the lane's row bits
+  // vector-ALU phases: lane l takes block rows l + 64 i; the lane's row bits
   // (0 .. 5) place its products, bits 6, 7 come from i
-  int lane_pos_v = 0, lane_pos_v2 = 0;
+  int lane_pos_v = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b)
-    if ((lane >> b) & 1) {
-      lane_pos_v += a.pos_row[b];
-      lane_pos_v2 += a.pos2_row[b];
-    }
+    if ((lane >> b) & 1) lane_pos_v += prow0[b];
 
   const bool pairs = pairs_s && aligned16(a.C);
   const int64_t nround = (a.R / ROWS1) >> 2;
@@ -1428,7 +1430,6 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
       asm volatile("" : "+v"(wo));
       [[maybe_unused]] const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
       [[maybe_unused]] const float2 *w3 = (const float2 *)bt3 + wo;
-      [[maybe_unused]] const int lp2 = lane_pos_v2 + wo;
       if constexpr (V1)
       {
         // every read of the block comes before the first write (in place)
@@ -1450,7 +1451,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           int pc = 0;
 #pragma unroll
           for (int c = 0; c < LKH + 1; ++c)
-            if ((s2 >> c) & 1) pc += a.pos_col[c];
+            if ((s2 >> c) & 1) pc += pcol0[c];
 #pragma unroll
           for (int i = 0; i < RPL1; ++i) {
             float2 y = make_float2(0.f, 0.f);
@@ -1459,7 +1460,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.x += x[i][k].x * w[k].x - x[i][k].y * w[k].y;
               y.y += x[i][k].x * w[k].y + x[i][k].y * w[k].x;
             }
-            x2[lp + ((i & 1) ? a.pos_row[6] : 0) + ((i & 2) ? a.pos_row[7] : 0) + pc] = y;
+            x2[lp + ((i & 1) ? prow0[6] : 0) + ((i & 2) ? prow0[7] : 0) + pc] = y;
           }
         }
       }
@@ -1487,6 +1488,12 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
     }
       if constexpr (V2)
       {
+        // the second step, and in a chain every step up to the last, each
+        // with its own table and places in the next step's block
+        const int nmid = K3 ? a.nsteps - 2 : 1;
+#pragma unroll
+        for (int m = 0; m < NMID; ++m) {
+        if (m >= nmid) break;
         float2 z[RPL2][K2];
 #pragma unroll
         for (int i = 0; i < RPL2; ++i)
@@ -1496,16 +1503,23 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
             z[i][2 * q] = make_float2(f.x, f.y);
             z[i][2 * q + 1] = make_float2(f.z, f.w);
           }
+        [[maybe_unused]] const int32_t *prow = a.pos_row[1 + m], *pcol = a.pos_col[1 + m];
+        [[maybe_unused]] int lp2 = wo;
+        if constexpr (K3 != 0) {
+#pragma unroll
+          for (int b = 0; b < 6; ++b)
+            if ((lane >> b) & 1) lp2 += prow[b];
+        }
 #pragma unroll
         for (int s2 = 0; s2 < K2; ++s2) {
           float2 w[K2];
 #pragma unroll
-          for (int k = 0; k < K2; ++k) w[k] = w2[s2 * K2 + k];
+          for (int k = 0; k < K2; ++k) w[k] = w2[(m * K2 + s2) * K2 + k];
           int pc = 0;
           if constexpr (K3 != 0) {
 #pragma unroll
             for (int c = 0; c < (K2 == 8 ? 3 : 2); ++c)
-              if ((s2 >> c) & 1) pc += a.pos2_col[c];
+              if ((s2 >> c) & 1) pc += pcol[c];
           }
 #pragma unroll
           for (int i = 0; i < RPL2; ++i) {
@@ -1515,11 +1529,12 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
               y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
             }
-            if constexpr (K3 != 0)  // to its place in the third step's block
-              x2[lp2 + ((i & 1) ? a.pos2_row[6] : 0) + ((i & 2) ? a.pos2_row[7] : 0) + pc] = y;
+            if constexpr (K3 != 0)  // to its place in the next step's block
+              x2[lp2 + ((i & 1) ? prow[6] : 0) + ((i & 2) ? prow[7] : 0) + pc] = y;
             else
               x2[(lane + 64 * i) * SP + s2 + wo] = y;
           }
+        }
         }
       }
       else
@@ -3451,15 +3466,18 @@ static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
 }
 
 hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
-  // the planner emits only pairs that meet these; anything else is refused
+  // the planner emits only chains that meet these; anything else is refused
   auto kok = [](int32_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
   if (!kok(a.K1) || !kok(a.K2) || a.nouter < 0 || a.nouter > kFuseMaxOuter) return hipErrorInvalidValue;
-  if (a.K3 != 0 && (a.K1 > 8 || a.K2 > 8 || (a.K3 != 4 && a.K3 != 8) || !a.W3)) return hipErrorInvalidValue;
-  if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.W1 || !a.W2 || !a.C ||
+  if (a.nsteps < 2 || a.nsteps > kFuseMaxChain || (a.nsteps == 2) != (a.K3 == 0)) return hipErrorInvalidValue;
+  if (a.K3 != 0 && (a.K1 > 8 || a.K2 > 8 || (a.K3 != 4 && a.K3 != 8))) return hipErrorInvalidValue;
+  for (int q = 0; q < a.nsteps; ++q)
+    if (!a.W[q]) return hipErrorInvalidValue;
+  if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.C ||
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
   if (a.K3 != 0) {
-    // three-step chains: every K is 4 or 8
+    // chains of three or more: every K is 4 or 8
     const int code = (a.K1 == 8) * 4 + (a.K2 == 8) * 2 + (a.K3 == 8);
     switch (code) {
       case 0: return run_fused2_k<4, 4, 4>(a, stream);

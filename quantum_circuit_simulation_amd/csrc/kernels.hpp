@@ -39,35 +39,37 @@ constexpr int32_t kPrecBf16x3 = 1;  // TNC_PREC_BF16X3
 using StepArgs = StepArgsT<float2>;    // complex64
 using StepArgsZ = StepArgsT<double2>;  // complex128
 
-// Two chained complex64 steps run as one pass over the first step's long
-// operand (k_fused2): T1[i, j] = sum_l X[i, l] W1[j, l] (K1 = S1 entries),
-// then T2 = T1 W2 on the second step's layout of T1 (K2 = S2), without
-// writing T1.  Every mode has extent 2, so each place below is a sum over
-// the set bits of an index.  A pass is 1024 entries of X (1024 / K1 rows);
-// within it, phase-1 row bit b and column bit c put their product at
-// pos_row[b] + pos_col[c] (complex entries) of the phase-2 input block
-// [1024 / K2 rows][K2 + 2]; phase-2 row bit e and column bit c add
-// out_row[e] and out_col[c] to the offset in C, and bit q of the pass index
-// adds out_pass[q].  The pass's rows of X are those whose row bits lrow[0 ..
-// log2(1024 / K1) - 1] (ascending) vary.  A workgroup runs passes 4 r + w
-// (w = 0 .. 3, one per wave) together: bits 0 and 1 of the pass index set
-// row bits wbit[0] and wbit[1], and r fills the row bits outside hole[0 ..
-// log2(1024 / K1) + 1] (lrow and wbit, ascending) in ascending order.
+// A chain of complex64 steps run as one pass over the first step's long
+// operand (k_fused2): T1[i, j] = sum_l X[i, l] W[0][j, l] (K1 = S1 entries),
+// then T2 = T1 W[1] on the second step's layout of T1 (K2 = S2), and so on
+// for nsteps steps, without writing any product but the last.  Every mode
+// has extent 2, so each place below is a sum over the set bits of an index.
+// A pass is 1024 entries of X (1024 / K1 rows); within it, step q's block row
+// bit b and column bit c put its product at pos_row[q][b] + pos_col[q][c]
+// (complex entries) of step q + 1's input block [1024 / K rows][K + 2] (the
+// first block's rows are the pass's rows); the last step's row bit e and
+// column bit c add out_row[e] and out_col[c] to the offset in C, and bit q
+// of the pass index adds out_pass[q].  The pass's rows of X are those whose
+// row bits lrow[0 .. log2(1024 / K1) - 1] (ascending) vary.  A workgroup runs
+// passes 4 r + w (w = 0 .. 3, one per wave) together: bits 0 and 1 of the
+// pass index set row bits wbit[0] and wbit[1], and r fills the row bits
+// outside hole[0 .. log2(1024 / K1) + 1] (lrow and wbit, ascending) in
+// ascending order.
 constexpr int kFuseEntries = 1024;
 constexpr int kFuseMaxOuter = 48;
+constexpr int kFuseMaxChain = 6;
 struct Fused2Args {
-  const float2 *X;   // row-major [R, K1]
-  const float2 *W1;  // row-major [K1, K1] (S1 rows)
-  const float2 *W2;  // row-major [K2, K2]
-  const float2 *W3;  // row-major [K3, K3] (three-step chains), else unused
+  const float2 *X;                   // row-major [R, K1]
+  const float2 *W[kFuseMaxChain];    // step q's small operand, row-major [K, K] (S rows)
   float2 *C;
   int64_t R;         // a multiple of 1024 / K1; R / (1024 / K1) = 2^nouter passes
-  int32_t K1, K2;    // 4, 8, 16 or 32 (K <= 8: vector-ALU phase)
-  int32_t K3;        // 0 (a pair), or 4 or 8 after K1, K2 <= 8: a third step whose
-                     // block places come from pos2_row / pos2_col as pos_* for the second
+  int32_t K1, K2;    // the first and second step's K: 4, 8, 16 or 32 (K <= 8: vector-ALU phase)
+  int32_t K3;        // 0 (a pair), or the last step's K (4 or 8) in a chain of nsteps >= 3
+                     // steps whose every K is 4 or 8 and whose middle steps all have K2
+  int32_t nsteps;
   int32_t nouter;
   int32_t lrow[8], hole[10], wbit[2];
-  int32_t pos_row[8], pos_col[8], pos2_row[8], pos2_col[8];
+  int32_t pos_row[kFuseMaxChain - 1][8], pos_col[kFuseMaxChain - 1][8];
   int64_t out_row[8], out_col[8];
   int64_t out_pass[kFuseMaxOuter];
 };

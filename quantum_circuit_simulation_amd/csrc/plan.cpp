@@ -244,18 +244,20 @@ int32_t log2_exact(int64_t v) {  // -1 unless v is a power of two
   return b;
 }
 
-// Tables of a fused chain of n = 2 or 3 steps st[0 .. n-1], each step's
-// product the next step's long operand (see FusedPair).  False when the chain
-// does not have the required form.
-bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedPair *f) {
+// Tables of a fused chain of n = 2 .. kFuseMaxSteps steps st[0 .. n-1], each
+// step's product the next step's long operand (see FusedChain).  False when
+// the chain does not have the required form.
+bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedChain *f) {
   struct Phase {
     int32_t lng = 0;                 // 0: the step's lhs is its long operand
     int64_t R = 0, K = 0;
     int32_t lr = 0, lk = 0, lb = 0;  // log2 of rows, K and the block's rows
     std::vector<int64_t> r, c;       // offsets in the step's product of its row / column bits
     std::vector<int32_t> tr, tc;     // the product's address bit of each row / column bit
-  } ph[3];
-  auto kok = [](int64_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
+  } ph[kFuseMaxSteps];
+  if (n < 2 || n > kFuseMaxSteps) return false;
+  // longer chains run every step on the vector ALU, the middle ones with one K
+  auto kok = [n](int64_t k) { return k == 4 || k == 8 || (n == 2 && (k == 16 || k == 32)); };
   for (int q = 0; q < n; ++q) {
     const Node &nd = p.nodes[st[q]];
     Phase &h = ph[q];
@@ -265,7 +267,7 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedPair *f)
     h.R = h.lng == 0 ? nd.m : nd.n;
     const int64_t S = h.lng == 0 ? nd.n : nd.m;
     h.K = nd.k;
-    if (!kok(h.K) || S != h.K) return false;
+    if (!kok(h.K) || S != h.K || (q > 1 && q < n - 1 && h.K != ph[1].K)) return false;
     if (q > 0 && ((h.lng == 0 ? nd.lhs : nd.rhs) != p.L + st[q - 1] || (h.lng == 0 ? nd.copy_a : nd.copy_b) != 0))
       return false;
     // the oriented rows of a node are its N side when swapped, else its M side
@@ -313,8 +315,10 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedPair *f)
   // The pass's local rows (first.lb of them): those, then the row bits with
   // the smallest offsets in the last product, so that a pass's stores form
   // the longest contiguous pieces.  Rows of X are K1 contiguous entries, so
-  // any choice loads whole rows.
-  if ((int32_t)local.size() > first.lb) return false;
+  // any choice loads whole rows.  A chain of four or more steps must leave
+  // two local rows to that choice: with none left its stores fall apart into
+  // pieces of a few entries.
+  if ((int32_t)local.size() > first.lb - (n >= 4 ? 2 : 0)) return false;
   std::stable_sort(cand.begin(), cand.end(), [&](int32_t x, int32_t y) { return fin[x] < fin[y]; });
   for (int32_t b : cand) ((int32_t)local.size() < first.lb ? local : outer).push_back(b);
   std::sort(local.begin(), local.end());
@@ -337,24 +341,20 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedPair *f)
       const int32_t e = (int32_t)(std::lower_bound(up.begin(), up.end(), t - h.lk) - up.begin());
       return (int32_t)(h.K + 2) << e;  // block rows are K + 2 entries apart
     };
-    int32_t *pr = q == 1 ? f->pos_row : f->pos2_row;
-    int32_t *pc = q == 1 ? f->pos_col : f->pos2_col;
+    int32_t *pr = f->pos_row[q - 1], *pc = f->pos_col[q - 1];
     for (size_t i = 0; i < prow.size(); ++i) pr[i] = pos(pv.tr[prow[i]]);
     for (int32_t c = 0; c < pv.lk; ++c) pc[c] = pos(pv.tc[c]);
     prow = up;
   }
   for (int32_t e = 0; e < last.lb; ++e) f->out_row[e] = last.r[prow[e]];
   for (int32_t c = 0; c < last.lk; ++c) f->out_col[c] = last.c[c];
-  f->first = st[0];
-  f->second = st[1];
-  f->third = n == 3 ? st[2] : -1;
-  f->long1 = ph[0].lng;
-  f->long2 = ph[1].lng;
-  f->long3 = n == 3 ? ph[2].lng : 0;
+  f->nsteps = n;
+  for (int q = 0; q < n; ++q) {
+    f->step[q] = st[q];
+    f->longop[q] = ph[q].lng;
+    f->k[q] = (int32_t)ph[q].K;
+  }
   f->rows = first.R;
-  f->k1 = (int32_t)ph[0].K;
-  f->k2 = (int32_t)ph[1].K;
-  f->k3 = n == 3 ? (int32_t)ph[2].K : 0;
   f->nouter = first.lr - first.lb;
   for (int32_t i = 0; i < first.lb; ++i) f->lrow[i] = local[i];
   // a workgroup runs four passes at once (bits 0 and 1 of the pass index):
@@ -632,10 +632,10 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
   }
   if (S == 0) p->staged_leaf.assign(L, 0);
 
-  // ---- fused pairs: a non-tiny step whose product is at once the long
-  // operand of another non-tiny step, both of the FusedPair form, extended to
-  // a third such step when all three small operands have K <= 8; chains do
-  // not overlap and are taken in step order
+  // ---- fused chains: a non-tiny step whose product is at once the long
+  // operand of another non-tiny step, both of the FusedChain form, extended
+  // one step at a time while the chain keeps that form (up to kFuseMaxSteps);
+  // chains do not overlap and are taken in step order
   p->fused.clear();
   if (o.fuse && !naive && eb == 8 && o.precision == TNC_PREC_EXACT) {
     std::vector<int32_t> consumer(T, -1);
@@ -650,17 +650,21 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
       if (s2 < 0) continue;
       Node &b = p->nodes[s2];
       if (b.cls == TNC_CLASS_TINY || b.splits > 1 || b.is_root) continue;
-      int32_t st[3] = {s1, s2, -1};
-      FusedPair f;
+      int32_t st[kFuseMaxSteps] = {s1, s2};
+      FusedChain f;
       if (!make_fused_chain(*p, st, 2, &f)) continue;
-      const int32_t s3 = consumer[L + s2];
-      if (s3 >= 0 && a.k <= 8 && b.k <= 8 && p->nodes[s3].k <= 8 && p->nodes[s3].cls != TNC_CLASS_TINY &&
-          p->nodes[s3].splits == 1 && !p->nodes[s3].is_root) {
-        st[2] = s3;
-        FusedPair f3;
-        if (make_fused_chain(*p, st, 3, &f3)) f = f3;
+      int n = 2;
+      while (n < kFuseMaxSteps) {
+        const int32_t sn = consumer[L + st[n - 1]];
+        if (sn < 0) break;
+        const Node &c = p->nodes[sn];
+        if (c.cls == TNC_CLASS_TINY || c.splits > 1 || c.is_root) break;
+        st[n] = sn;
+        FusedChain g;
+        if (!make_fused_chain(*p, st, n + 1, &g)) break;
+        f = g;
+        ++n;
       }
-      const int n = f.third >= 0 ? 3 : 2;
       for (int q = 0; q + 1 < n; ++q) {
         p->nodes[st[q]].fuse_next = st[q + 1];
         p->nodes[st[q + 1]].fuse_prev = st[q];
@@ -738,8 +742,8 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
         }
       }
     }
-  // the first step of a fused pair keeps its operands until the pair's
-  // launch (the second step's group) and stores no product
+  // a fused chain's earlier steps keep their operands until the chain's
+  // launch (its last step's group) and store no product
   std::vector<std::vector<std::pair<uint64_t, uint64_t>>> deferred(S);
   for (auto &members : p->groups) {
     std::vector<std::pair<uint64_t, uint64_t>> to_free;
@@ -762,7 +766,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
           frees.push_back({off, rbytes(elems[t])});
           if (t < L && !naive) p->tensor_off[t] = off;
         } else if (nd.fuse_prev >= 0 && t == L + nd.fuse_prev) {
-          off = kNone;  // the pair's first product: never stored
+          off = kNone;  // the previous product of its chain: never stored
         } else if (t >= L) {
           off = p->tensor_off[t];
           frees.push_back({off, rbytes(elems[t])});
@@ -937,7 +941,7 @@ tnc_status build_plan(const tnc_network *net, const tnc_tree *tree, const tnc_pl
       for (auto &r : nd.row_runs) runs.push_back({r.size, r.stride});
       for (auto &r : nd.col_runs) runs.push_back({r.size, r.stride});
       if (nd.fuse_prev >= 0 && nd.fuse_next < 0)
-        p->program.push_back({OP_FUSED, nd.fused_index, p->fused[nd.fused_index].third >= 0 ? 3 : 2, 0});
+        p->program.push_back({OP_FUSED, nd.fused_index, p->fused[nd.fused_index].nsteps, 0});
       else if (nd.fuse_next < 0 && nd.fuse_prev < 0)  // a chain's earlier steps run in its last step's launch
         p->program.push_back({first.cls == TNC_CLASS_SKINNY ? OP_SKINNY : OP_GEMM, members[0], 1, 0});
     }

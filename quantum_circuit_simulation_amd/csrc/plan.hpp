@@ -69,34 +69,38 @@ struct Node {
   int32_t is_root = 0;
   // device run table location (entries into the blob's run array)
   int32_t runs_index = 0;
-  // fused pairs (see FusedPair): the first step's product is never stored;
-  // both steps run in the launch of the second
+  // fused chains (see FusedChain): only the last step's product is stored;
+  // every step of the chain runs in the launch of the last
   int32_t fuse_next = -1;    // the next step of its fused chain
   int32_t fuse_prev = -1;    // the previous step of its fused chain
   int32_t fused_index = -1;  // a chain's last step: index into PlanImpl::fused
 };
 
-// Two chained complex64 steps run as one pass over the first step's long
-// operand (k_fused2): a long tensor absorbs a small one (K1 = S1 = 4, 8, 16
-// or 32 entries) and the product is reduced at once against another small
-// tensor (K2 = S2, the same choices).  Built when every index is a power of two and a pass of
-// kFusePassEntries entries of the long operand holds whole rows of the
-// second step; the tables give, per index bit, the place of an entry (see
-// Fused2Args in kernels.hpp).
+// A chain of 2 .. kFuseMaxSteps complex64 steps run as one pass over the
+// first step's long operand (k_fused2): each step's product is at once the
+// next step's long operand, and each step absorbs a small tensor with K = S
+// (4, 8, 16 or 32 entries; in chains of three or more every K is 4 or 8 and
+// the steps between the first and the last share one K).  Built when every
+// index is a power of two and a pass of kFusePassEntries entries of the long
+// operand holds whole rows of every step; the tables give, per index bit, the
+// place of an entry (see Fused2Args in kernels.hpp).
 constexpr int64_t kFusePassEntries = 1024;
 constexpr int32_t kFuseOuterMax = 48;
-constexpr int64_t kFuseMinRows = int64_t(1) << 16;  // smaller steps are not worth a pair
-struct FusedPair {
-  int32_t first = -1, second = -1, third = -1;  // third: a three-step chain (all K <= 8), else -1
-  int32_t long1 = 0, long2 = 0, long3 = 0;  // 0: the step's lhs is its long operand, 1: its rhs
+constexpr int32_t kFuseMaxSteps = 6;
+constexpr int64_t kFuseMinRows = int64_t(1) << 16;  // smaller steps are not worth a pass
+struct FusedChain {
+  int32_t nsteps = 0;
+  int32_t step[kFuseMaxSteps] = {};
+  int32_t longop[kFuseMaxSteps] = {};  // 0: the step's lhs is its long operand, 1: its rhs
+  int32_t k[kFuseMaxSteps] = {};       // each step's K (= its short side S)
   int64_t rows = 0;          // rows of the first step's long operand
-  int32_t k1 = 0, k2 = 0, k3 = 0, nouter = 0;
+  int32_t nouter = 0;
   int32_t lrow[8] = {};      // the pass's local row bits of the long operand, ascending
   int32_t wbit[2] = {};      // row bits set by bits 0, 1 of the pass index (a workgroup's four passes)
   int32_t hole[10] = {};     // lrow and wbit, ascending: the rest count the workgroup's rounds
-  int32_t pos_row[8] = {}, pos_col[8] = {};
-  int32_t pos2_row[8] = {}, pos2_col[8] = {};  // the second step's products in the third's block
-  int64_t out_row[8] = {}, out_col[8] = {};
+  // [q]: the places of step q's products in step q + 1's block
+  int32_t pos_row[kFuseMaxSteps - 1][8] = {}, pos_col[kFuseMaxSteps - 1][8] = {};
+  int64_t out_row[8] = {}, out_col[8] = {};  // the last product's offsets
   int64_t out_pass[kFuseOuterMax] = {};
 };
 
@@ -130,7 +134,7 @@ struct PlanImpl {
   std::vector<std::vector<int32_t>> order;     // planned order per SSA tensor
   std::vector<std::vector<int32_t>> gemm_a, gemm_b;
   std::vector<Node> nodes;
-  std::vector<FusedPair> fused;
+  std::vector<FusedChain> fused;
   std::vector<std::vector<int32_t>> groups;
   std::vector<uint64_t> tensor_off;
   std::vector<int32_t> staged_leaf;

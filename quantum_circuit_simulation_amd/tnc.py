@@ -26,6 +26,7 @@ PREC_EXACT, PREC_BF16X3 = 0, 1
 ORDER_LIFETIME, ORDER_NAIVE = 0, 1
 CLASS_TINY, CLASS_SKINNY, CLASS_GEMM = 0, 1, 2
 NONE = (1 << 64) - 1
+FUSE_MAX_STEPS = 6  # TNC_FUSE_MAX_STEPS: the longest fused chain
 
 P = ctypes.POINTER
 
@@ -85,17 +86,24 @@ class NodeInfo(ctypes.Structure):
 
 
 class FusedInfo(ctypes.Structure):
-    _fields_ = [("first", ctypes.c_int32), ("second", ctypes.c_int32), ("third", ctypes.c_int32),
-                ("long1", ctypes.c_int32), ("long2", ctypes.c_int32), ("long3", ctypes.c_int32),
-                ("rows", ctypes.c_int64), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32), ("k3", ctypes.c_int32),
-                ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 8), ("hole", ctypes.c_int32 * 10),
-                ("wbit", ctypes.c_int32 * 2), ("pos_row", ctypes.c_int32 * 8), ("pos_col", ctypes.c_int32 * 8),
-                ("pos2_row", ctypes.c_int32 * 8), ("pos2_col", ctypes.c_int32 * 8),
+    _fields_ = [("nsteps", ctypes.c_int32), ("step", ctypes.c_int32 * FUSE_MAX_STEPS),
+                ("longop", ctypes.c_int32 * FUSE_MAX_STEPS), ("k", ctypes.c_int32 * FUSE_MAX_STEPS),
+                ("rows", ctypes.c_int64), ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 8),
+                ("hole", ctypes.c_int32 * 10), ("wbit", ctypes.c_int32 * 2),
+                ("pos_row", (ctypes.c_int32 * 8) * (FUSE_MAX_STEPS - 1)),
+                ("pos_col", (ctypes.c_int32 * 8) * (FUSE_MAX_STEPS - 1)),
                 ("out_row", ctypes.c_int64 * 8), ("out_col", ctypes.c_int64 * 8), ("out_pass", ctypes.c_int64 * 48)]
 
     def as_dict(self):
-        return {name: (list(getattr(self, name)) if isinstance(getattr(self, name), ctypes.Array)
-                       else getattr(self, name)) for name, _ in self._fields_}
+        def plain(v):
+            return [plain(x) for x in v] if isinstance(v, ctypes.Array) else v
+        d = {name: plain(getattr(self, name)) for name, _ in self._fields_}
+        n = d["nsteps"]   # the chain's own entries only
+        for name in ("step", "longop", "k"):
+            d[name] = d[name][:n]
+        for name in ("pos_row", "pos_col"):
+            d[name] = d[name][:n - 1]
+        return d
 
 
 class DistOptions(ctypes.Structure):
@@ -298,7 +306,9 @@ class Plan:
         return n.as_dict()
 
     def fused(self, index: int) -> dict:
-        """Pass tables of fused pair `index` (tnc_plan_fused)."""
+        """Pass tables of fused chain `index` (tnc_plan_fused); the per-step
+        lists (step, longop, k, and pos_row / pos_col per transition) hold the
+        chain's own entries only."""
         f = FusedInfo()
         _check(self._lib.tnc_plan_fused(self._h, index, ctypes.byref(f)), "tnc_plan_fused")
         return f.as_dict()

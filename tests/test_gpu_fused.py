@@ -1,13 +1,13 @@
 """Fused chains of steps (k_fused2): a long tensor T absorbs a small W1 (4,
 8, 16 or 32 entries of K, as many outputs) and the product is reduced at
-once against another small W2 (and, all K <= 8, a third W3), in one pass
-over T.  Every output entry of the
-whole contraction against the oracle, for (K1, K2) in {4, 8, 16, 32}^2 (the
-vector-ALU and matrix-core phases and their mixes), with
-the second step reducing 0 .. all of the first step's new modes, random
-declared orders and output orders (so the pair's product lands in many
+once against another small W2 (and, all K <= 8, up to four more), in one
+pass over T.  Every output entry of the whole contraction against the
+oracle, for (K1, K2) in {4, 8, 16, 32}^2 (the vector-ALU and matrix-core
+phases and their mixes) and chains of three to six steps, with each later
+step reducing 0 .. all of the modes the earlier steps brought in, random
+declared orders and output orders (so the chain's product lands in many
 layouts), the innermost output mode local to a pass (16-byte pair stores)
-or not (single stores), a sliced run, and the same plans with fusion off.
+or not (single stores), sliced runs, and the same plans with fusion off.
 |g - r| <= 1e-4 * max(|r|, rms(r))."""
 
 import numpy as np
@@ -94,6 +94,48 @@ def chain3_network(k1, k2, k3, v2, v3a, v3b, log_rows, last, seed, permuted=True
     return net, Tree([0, 5, 6, 7], [1, 2, 3, 4])
 
 
+def chain_n_network(ks, vs, log_rows, last, seed, permuted=True, with_data=True):
+    """A chain of n = len(ks) absorbs: T (outer modes O, then A_2 .. A_n, then
+    K_1) takes W_1 (K_1 -> S_1, 2^ks[0] x 2^ks[0]); step q = 2 .. n reduces
+    the product against W_q over K_q = vs[q - 1] modes drawn (seeded) from the
+    modes the earlier W's brought in and still open, plus ks[q - 1] -
+    vs[q - 1] further modes A_q of T (K_q -> S_q).  A last step contracts one
+    mode of the chain's product with a vector (an outer mode for last = "o", a
+    mode of S_n for "s").  All extents 2; T has 2^log_rows rows of 2^ks[0]
+    entries."""
+    rng = np.random.default_rng(seed)
+    n = len(ks)
+    na = [ks[q] - vs[q] for q in range(1, n)]
+    assert min(na) >= 0
+    n_outer = log_rows - sum(na)
+    assert n_outer >= 2
+    labels = iter(range(1000))
+    take = lambda c: [next(labels) for _ in range(c)]
+    O, K1 = take(n_outer), take(ks[0])
+    S = [take(k) for k in ks]
+    A = [take(c) for c in na]
+    pool = list(S[0])
+    ws = [S[0] + K1]
+    for q in range(1, n):
+        assert vs[q] <= len(pool)
+        pick = [pool[i] for i in sorted(rng.choice(len(pool), size=vs[q], replace=False))]
+        pool = [x for x in pool if x not in pick] + S[q]
+        ws.append(S[q] + pick + A[q - 1])
+    vmode = O[0] if last == "o" else S[-1][0]
+    leaves = [O + sum(A, []) + K1] + ws
+    out = [x for x in O + pool if x != vmode]
+    if permuted:
+        leaves = [list(rng.permutation(m)) for m in leaves]
+        out = list(rng.permutation(out))
+    leaves.append([vmode])
+    nl = len(leaves)
+    ext = np.full(next(labels), 2, dtype=np.int64)
+    data = [_cn(rng, [2] * len(l)) for l in leaves] if with_data else None
+    name = "chain{}_k{}_v{}_r{}_{}".format(n, "".join(map(str, ks)), "".join(map(str, vs[1:])), log_rows, last)
+    net = Network(ext, [list(map(int, l)) for l in leaves], [int(x) for x in out], data, name=name)
+    return net, Tree([0] + [nl + q for q in range(n)], list(range(1, n + 2)))
+
+
 # (log2 K1, log2 K2, shared modes v, log2 rows of T, last-step mode); a
 # phase with K <= 8 runs on the vector ALU, K >= 16 on the matrix cores
 CASES = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "s"), (4, 4, 4, 16, "o"), (4, 5, 2, 17, "s"), (5, 4, 1, 16, "s"),
@@ -127,6 +169,42 @@ def test_fused_chain_of_three_matches_oracle(case):
     net, tree = chain3_network(*case, seed=800 + sum(case[:7]))
     ks = _check(net, tree, expect_kernel="k_fused2", kind="fused")
     assert len(ks) == 1 and ks[0].count(",") == 2, ks   # one k_fused2<K1,K2,K3> launch
+
+
+# longer chains (every K <= 8, the steps between the first and the last with
+# one K, two of the pass's row bits left free): (log2 K of each step, shared
+# modes of each later step, log2 rows, last)
+CHAINN = [((2, 2, 2, 2), (0, 1, 1, 0), 16, "s"), ((2, 2, 2, 2, 2), (0, 0, 0, 1, 1), 16, "o"),
+          ((2, 2, 2, 2, 2, 2), (0, 2, 1, 2, 1, 2), 17, "s"), ((3, 3, 3, 3), (0, 1, 2, 1), 16, "o"),
+          ((2, 3, 3, 2), (0, 1, 2, 1), 17, "s"), ((3, 2, 2, 2, 3), (0, 1, 1, 1, 2), 16, "s"),
+          ((2, 2, 2, 2, 2), (0, 1, 0, 1, 0), 18, "s"), ((3, 3, 3, 3, 3), (0, 2, 2, 2, 2), 16, "o")]
+
+
+@pytest.mark.parametrize("case", CHAINN, ids=lambda c: "k{}_v{}_r{}_{}".format(
+    "".join(map(str, c[0])), "".join(map(str, c[1][1:])), c[2], c[3]))
+def test_fused_longer_chain_matches_oracle(case):
+    import quantum_circuit_simulation_amd as qa
+    ks, vs, log_rows, last = case
+    net, tree = chain_n_network(ks, vs, log_rows, last, seed=900 + sum(ks) + sum(vs) + log_rows)
+    plan = qa.Plan.from_network(net, tree)
+    assert plan.stats()["fused_pairs"] == 1 and plan.fused(0)["nsteps"] == len(ks)
+    kern = _check(net, tree, expect_kernel="k_fused2", kind="fused")
+    assert len(kern) == 1 and kern[0].count(",") == 2, kern
+
+
+def test_chain_stops_at_the_longest_chain():
+    # seven steps that could each follow the last: the first six form one
+    # chain, the seventh runs alone
+    import quantum_circuit_simulation_amd as qa
+    net, tree = chain_n_network((2,) * 7, (0, 2, 2, 2, 2, 2, 2), 16, "o", seed=95)
+    plan = qa.Plan.from_network(net, tree)
+    assert plan.stats()["fused_pairs"] == 1 and plan.fused(0)["step"] == list(range(6))
+    _check(net, tree, expect_kernel="k_fused2", kind="fused")
+
+
+def test_sliced_longer_chain():
+    net, tree = chain_n_network((2, 2, 2, 2, 2), (0, 1, 0, 1, 0), 18, "o", seed=97)
+    _check(net, tree, expect_kernel="k_fused2", kind="fused", sliced=[net.leaves[-1][0]])
 
 
 def test_sliced_chain_of_three():

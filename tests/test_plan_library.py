@@ -133,11 +133,57 @@ def test_fused_chain_plans_match_oracle(case, permuted):
         lib, ref = _check(net, tree, sliced=[net.leaves[4][0]])
 
 
+# (log2 K of each step, shared modes of each later step, log2 rows, last)
+LONGER = [((2, 2, 2, 2), (0, 1, 1, 0), 16, "s"), ((2, 2, 2, 2, 2), (0, 0, 0, 0, 0), 16, "o"),
+          ((2, 2, 2, 2, 2, 2), (0, 2, 1, 2, 1, 2), 17, "s"), ((3, 3, 3, 3), (0, 1, 2, 1), 16, "o"),
+          ((2, 3, 3, 2), (0, 1, 2, 1), 17, "s"), ((3, 2, 2, 2, 3), (0, 1, 1, 1, 2), 16, "s"),
+          # gates on new qubits (2 bits of T each): a fifth would leave no row
+          # bit of a pass of 256 rows free, so the chain has four steps
+          ((2, 2, 2, 2, 2), (0, 0, 0, 0, 0), 16, "o"), ((2, 2, 2, 2, 2), (0, 0, 0, 0, 1), 16, "o"),
+          ((2, 2, 2, 2, 2), (0, 0, 0, 1, 1), 17, "s"),
+          # the fourth step would need 8 bits of T in a pass of 128 rows: a chain of three
+          ((3, 3, 3, 3), (0, 0, 0, 1), 16, "o"),
+          # the middle steps' K would differ (4, then 8): a chain of three
+          ((2, 2, 3, 2), (0, 1, 2, 1), 16, "s"),
+          # a step with K = 16 does not join a chain of K <= 8 steps
+          ((2, 2, 2, 4), (0, 1, 1, 2), 16, "o"),
+          # seven steps in a row: a chain of the first six
+          ((2,) * 7, (0, 2, 2, 2, 2, 2, 2), 16, "o")]
+
+
+@pytest.mark.parametrize("case", LONGER, ids=lambda c: "k{}_v{}_r{}_{}".format(
+    "".join(map(str, c[0])), "".join(map(str, c[1][1:])), c[2], c[3]))
+@pytest.mark.parametrize("permuted", [False, True], ids=["aligned", "permuted"])
+def test_longer_chain_plans_match_oracle(case, permuted):
+    from tests.test_gpu_fused import chain_n_network
+    ks, vs, log_rows, last = case
+    net, tree = chain_n_network(ks, vs, log_rows, last, seed=60 + sum(ks) + sum(vs), permuted=permuted,
+                                with_data=False)
+    lib, ref = _check(net, tree)
+    # the longest chain from step 0 that keeps the form: T's modes reduced by
+    # the later steps fit a pass (bits <= 10 - log2 K1, two fewer from four
+    # steps on), every K <= 8 beyond a pair, one K between the first and the
+    # last step, at most six steps
+    n = 1
+    while n < min(len(ks), 6):
+        bits = sum(ks[q] - vs[q] for q in range(1, n + 1))
+        kk = ks[:n + 1]
+        if bits > 10 - ks[0] - (2 if n >= 3 else 0) or (n >= 2 and (max(kk) > 3 or len(set(kk[1:-1])) > 1)):
+            break
+        n += 1
+    assert ref.fused == [tuple(range(n))], (ref.fused, n)
+    if last == "o":
+        lib, ref = _check(net, tree, sliced=[net.leaves[-1][0]])
+
+
 def test_state_vector_plan_with_fused_chains_matches_oracle():
     c = circuits.brickwork(30, 14, 303)
     net = c.to_network(open_qubits=range(6))
     lib, ref = _check(net, trees.state_vector_tree(net))
-    assert len(ref.fused) == 68 and sum(len(x) == 3 for x in ref.fused) == 67
+    # 203 gates in time order: each gate after a chain's first brings 2 bits
+    # of the state into a pass of 256 rows of four entries, and two of its 8
+    # row bits stay free, so chains have four gates
+    assert len(ref.fused) == 51 and sum(len(x) == 4 for x in ref.fused) == 50
 
 
 def test_grid_depth16_plan_with_fused_pairs_matches_oracle():
