@@ -3523,10 +3523,11 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   if (kred_ok(a)) return run_kred(a, stream);
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
-  // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
-  // straight into registers; shorter rows are read as one contiguous block
-  // per 256 rows through LDS (grid-stride); chunked K one tile per workgroup
-  if (a.R >= 4096 && a.splits == 1 && a.K >= 8 && a.K <= kRowsKC) {
+  // kernel choice measured on MI355X: rows of >= 8 entries, and the single
+  // entries of outer products (K = 1), stream fastest straight into
+  // registers; rows of 2 .. 7 entries are read as one contiguous block per
+  // 256 rows through LDS (grid-stride); chunked K one tile per workgroup
+  if (a.R >= 4096 && a.splits == 1 && (a.K == 1 || (a.K >= 8 && a.K <= kRowsKC))) {
     const int rows = a.K <= 8 ? 2 : 1;
     const int64_t blocks = (a.R + 256 * rows - 1) / (256 * rows);
     note_kernel("k_skinny_small<%d>", rows);

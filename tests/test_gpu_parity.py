@@ -219,9 +219,10 @@ def test_large_permuted_pairs(seed, order):
 
 # skinny steps: (mode counts of M, N, K, extent) chosen to hit the row-tile
 # kernel with whole-K blocks (odd and non-power-of-two K included), chunked K,
-# interleaved outputs, and the few-row kernel with split K
+# interleaved outputs, the few-row kernel with split K, and outer products
+# (no K mode) of a long operand with a short one
 SKINNY_CASES = [(13, 2, 2, 2), (8, 1, 1, 3), (9, 1, 2, 3), (12, 4, 4, 2), (12, 3, 5, 2), (6, 2, 3, 5),
-                (0, 0, 17, 2), (2, 1, 12, 3), (1, 1, 15, 2)]
+                (0, 0, 17, 2), (2, 1, 12, 3), (1, 1, 15, 2), (13, 1, 0, 2), (14, 3, 0, 2), (8, 1, 0, 3)]
 
 
 @pytest.mark.parametrize("case", SKINNY_CASES)
