@@ -612,6 +612,67 @@ __global__ __launch_bounds__(256) void k_skinny_rows(StepArgs a, int64_t kchunk)
   }
 }
 
+// Outer products (K = 1, at most kSkinnyMax outputs per row) of a long
+// operand: C at rowoff(i) + coloff(j) = X[i] Y[j], pure streaming.  When C's
+// innermost row run has stride 1 and an even size, rows 2p and 2p + 1 sit
+// side by side in C and every other stride is even, so each lane reads a
+// row pair with one 16-byte load and writes one 16-byte pair per output
+// column; otherwise it takes single rows.  Grid-stride over chunks of 256 U
+// row pairs (U loads in flight per lane), no LDS staging of X.
+constexpr int kOuterU = 4;
+__global__ __launch_bounds__(256) void k_outer(StepArgs a) {
+  __shared__ float2 ys[kSkinnyMax];
+  __shared__ int64_t coloff[kSkinnyMax];
+  const int tid = threadIdx.x, S = (int)a.S;
+  if (tid < S) {
+    ys[tid] = a.Y[tid];
+    coloff[tid] = run_offset(tid, a.runs + a.nrr, a.ncr);
+  }
+  __syncthreads();
+  const RunDev inner = a.runs[a.nrr - 1];
+  const bool pairs = a.nrr >= 1 && inner.stride == 1 && (inner.size % 2) == 0 && (a.R % 2) == 0 &&
+                     aligned16(a.X) && aligned16(a.C);
+  if (pairs) {
+    const int64_t np = a.R / 2;
+    const float4 *X4 = (const float4 *)a.X;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * kOuterU; base < np;
+         base += (int64_t)gridDim.x * 256 * kOuterU) {
+      float4 v[kOuterU];
+#pragma unroll
+      for (int u = 0; u < kOuterU; ++u) {
+        const int64_t p = base + u * 256 + tid;
+        if (p < np) v[u] = X4[p];
+      }
+#pragma unroll
+      for (int u = 0; u < kOuterU; ++u) {
+        const int64_t p = base + u * 256 + tid;
+        if (p >= np) continue;
+        const int64_t ro = run_offset(2 * p, a.runs, a.nrr);
+        for (int j = 0; j < S; ++j) {
+          const float2 y = ys[j];
+          float4 o = make_float4(v[u].x * y.x - v[u].y * y.y, v[u].x * y.y + v[u].y * y.x,
+                                 v[u].z * y.x - v[u].w * y.y, v[u].z * y.y + v[u].w * y.x);
+          float4 *dst = (float4 *)(a.C + ro + coloff[j]);
+          if (a.beta) {
+            const float4 c = *dst;
+            o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+          }
+          *dst = o;
+        }
+      }
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < a.R; i += (int64_t)gridDim.x * 256) {
+      const float2 x = a.X[i];
+      const int64_t ro = run_offset(i, a.runs, a.nrr);
+      for (int j = 0; j < S; ++j) {
+        const float2 y = ys[j];
+        store_c(a.C + ro + coloff[j], make_float2(x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x), a.beta);
+      }
+    }
+  }
+}
+
 // Many rows, whole K <= 16, no split: no LDS staging of X at all.  Each
 // thread streams ROWS rows (row r of the step is row
 // (blockIdx.x * ROWS + u) * 256 + tid, so every u is a coalesced group of
@@ -3523,11 +3584,19 @@ hipError_t launch_skinny(const StepArgs &a, hipStream_t stream) {
   if (kred_ok(a)) return run_kred(a, stream);
   int64_t kchunk = a.K;
   if (a.splits > 1) kchunk = (a.K + a.splits - 1) / a.splits;
-  // kernel choice measured on MI355X: rows of >= 8 entries, and the single
-  // entries of outer products (K = 1), stream fastest straight into
-  // registers; rows of 2 .. 7 entries are read as one contiguous block per
-  // 256 rows through LDS (grid-stride); chunked K one tile per workgroup
-  if (a.R >= 4096 && a.splits == 1 && (a.K == 1 || (a.K >= 8 && a.K <= kRowsKC))) {
+  // outer products of a long operand (K = 1): streamed by k_outer
+  if (a.R >= 4096 && a.splits == 1 && a.K == 1 && a.S <= kSkinnyMax && a.nrr >= 1) {
+    int64_t blocks = (a.R / 2 + 256 * kOuterU - 1) / (256 * kOuterU);
+    const int64_t cap = 8 * (int64_t)num_cus();
+    if (blocks > cap) blocks = cap;
+    note_kernel("k_outer");
+    hipLaunchKernelGGL(k_outer, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  // kernel choice measured on MI355X: rows of >= 8 entries stream fastest
+  // straight into registers; shorter rows are read as one contiguous block
+  // per 256 rows through LDS (grid-stride); chunked K one tile per workgroup
+  if (a.R >= 4096 && a.splits == 1 && a.K >= 8 && a.K <= kRowsKC) {
     const int rows = a.K <= 8 ? 2 : 1;
     const int64_t blocks = (a.R + 256 * rows - 1) / (256 * rows);
     note_kernel("k_skinny_small<%d>", rows);

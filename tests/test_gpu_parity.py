@@ -254,6 +254,26 @@ def test_sliced_skinny_step_accumulates(ext_sliced):
     _assert_close(got, ref)
 
 
+@pytest.mark.parametrize("col_outer", [False, True], ids=["col_inner", "col_outer"])
+def test_sliced_outer_product_accumulates(col_outer):
+    """A pairwise step whose only shared mode is sliced: each slice is an
+    outer product (K = 1) of 2^13 rows with 2 columns, added into `out`
+    after the first (16-byte row pairs when the column mode is outer in the
+    output, single entries when it is innermost)."""
+    rng = np.random.default_rng(43)
+    M, N, x = list(range(13)), [13], 14
+    extents = np.array([2] * 15, dtype=np.int64)
+    A, B = M + [x], [x] + N
+    data = [sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in A)),
+            sweep.complex_gaussian(rng, tuple(int(extents[m]) for m in B))]
+    net = Network(extents, [A, B], (N + M) if col_outer else (M + N), data, name="sliced-outer")
+    tree = Tree([0], [1])
+    ref = oracle.contract_network(net, tree)
+    got, plan = _gpu_run(net, tree, sliced=[x])
+    assert plan.stats()["num_slices"] == 2 and plan.node(0)["k"] == 1
+    _assert_close(got, ref)
+
+
 def test_skinny_on_misaligned_views():
     """Leaves handed over as views starting at an odd entry (8-byte, not
     16-byte aligned): the 16-byte load paths must fall back."""
