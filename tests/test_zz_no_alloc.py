@@ -53,3 +53,15 @@ def test_noalloc_matches_execute_twice_with_smaller_second_call_then_sliced():
     sl = [m for m in range(small.num_modes) if m not in small.out_modes][10:12]
     _both(small, tree, sliced=sl)
 
+
+
+def test_noalloc_runs_fused_chains():
+    """Plans whose steps run as fused chains (a pair with matrix-core phases
+    and a chain of four on the vector ALU) through the static workspace."""
+    from tests.test_gpu_fused import chain_n_network, chain_network
+    net, tree = chain_network(4, 5, 2, 16, "s", seed=11)
+    assert qa.Plan.from_network(net, tree).stats()["fused_pairs"] == 1
+    _both(net, tree)
+    net, tree = chain_n_network((2, 2, 2, 2), (0, 1, 1, 0), 16, "o", seed=12)
+    assert qa.Plan.from_network(net, tree).fused(0)["nsteps"] == 4
+    _both(net, tree)
