@@ -1,8 +1,9 @@
 """GPU parity on the second workload family: honeycomb-lattice networks
 (random sites against the oracle; all-ones sites at the full 16 x 16, D = 8
-bench size against their closed form) and Ising partition functions on
-random 3-regular graphs and rings.  Tolerance as for every complex64 path:
-|g - r| <= 1e-4 * |r| (scalars)."""
+bench size against their closed form), Ising partition functions on
+random 3-regular graphs and rings, and the coset weights of surface-code
+decoding.  Tolerance as for every complex64 path: |g - r| <= 1e-4 * |r|
+(scalars)."""
 
 import math
 
@@ -75,3 +76,27 @@ def test_ising_ring_closed_form():
     got, _ = _run(net, trees.greedy_tree(net))
     expect = (2 * math.cosh(beta)) ** n + (2 * math.sinh(beta)) ** n
     assert abs(got.reshape(-1)[0] - expect) <= TOL * expect
+
+
+@pytest.mark.parametrize("d,p,seed", [(5, 0.08, 21), (7, 0.05, 22), (9, 0.05, 23), (11, 0.04, 24)])
+def test_surface_code_coset_weights_match_oracle(d, p, seed):
+    """Maximum-likelihood decoding of a random bit-flip error on the planar
+    surface code: both coset weights, Z(E) and Z(E xor logical), on the GPU
+    against the oracle, and the same decision wherever the two weights are
+    more than 0.1% apart."""
+    from workloads import qec
+    E = qec.random_error(d, p, seed)
+    G = E.copy()
+    G[qec.planar_code(d)[2]] ^= 1
+    got, ref = [], []
+    for err in (E, G):
+        net = qec.coset_network(d, p, err)
+        tree = trees.greedy_tree(net)
+        r = oracle.contract_network(net, tree)
+        g, _ = _run(net, tree)
+        ok, e = rel_err_ok(g, r, TOL)
+        assert ok, e
+        got.append(float(np.asarray(g).reshape(-1)[0].real))
+        ref.append(float(np.asarray(r).reshape(-1)[0].real))
+    if abs(math.log(ref[0] / ref[1])) > 1e-3:
+        assert (got[0] > got[1]) == (ref[0] > ref[1])

@@ -14,6 +14,8 @@ GPUs", sections 2.1-2.3, whose definitions are not given there):
 * random 2-D grid circuits with fSim-form couplers,
 * an 8x8 square-lattice (PEPS-style) partition-function network,
 * isolated pairwise contractions (the GEMM sweep),
+* honeycomb-lattice and graph Ising partition functions (``hexagonal``),
+* surface-code decoding (coset-weight) networks (``qec``),
 * small random networks for property tests.
 """
 
