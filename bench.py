@@ -326,6 +326,17 @@ class TreeWorkload:
             tree = trees.state_vector_tree(net)
             self.config = {"workload": "brickwork-30q-d14-batch64-statevector", "seed": 303,
                            "tree": "state-vector order (kets, gates in time order, bras)"}
+        elif which == "qec":
+            from workloads import qec
+            d, p = 23, 0.05
+            net = qec.coset_network(d, p, qec.random_error(d, p, 707), relative=True)
+            tree = qec.sweep_tree(d)
+            self.config = {"workload": "surface-code-d23-coset-weight", "seed": 707, "p": p,
+                           "weights": "relative to the error's own probability",
+                           "tree": "column sweep (caterpillar in site order)"}
+            # 1518 steps over up to 2^24 entries each: the whole contraction
+            # is far beyond a bounded oracle run, so the oracle times sub-slices
+            self.cpu_subslice_log_width = 16
         elif which == "brickwork30":
             net = circuits.brickwork(30, 14, 303).to_network(open_qubits=range(6))
             tree = trees.greedy_tree(net)
@@ -636,11 +647,35 @@ class TreeWorkload:
             # far beyond a bounded CPU run: time exact complex128 entries of the
             # tree's largest step on gathered rows instead (same rate measure)
             return self._cpu_largest_step(budget_s, threads)
+        if getattr(self, "cpu_subslice_log_width", None):
+            return self._cpu_sub_slices(budget_s, threads, self.cpu_subslice_log_width)
         t0 = time.perf_counter()
         oracle.contract_network(self.net, self.tree, threads=threads)
         el = time.perf_counter() - t0
         return {"value": self.flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                 "sample": f"full contraction ({self.flops:.3g} flop in {el:.1f} s)"}
+
+    def _cpu_sub_slices(self, budget_s, threads, log_width):
+        """The oracle on sub-slices of the same tree: modes fixed greedily
+        (trees.more_slices) until every intermediate has at most
+        2^log_width entries; rate = the sub-slices' flops / their time."""
+        import oracle
+        from workloads import trees
+        fixed = trees.more_slices(self.net, self.tree, self.sliced, 0, max_log_width=log_width)
+        c = trees.tree_cost(self.net, self.tree, fixed)
+        fl = float(c["flops"])
+        t0 = time.perf_counter()
+        done = 0
+        while done < 64:
+            vals = {x: (done >> (len(fixed) - 1 - i)) & 1 for i, x in enumerate(fixed)}
+            oracle.contract_network(self.net, self.tree, fixed=vals, threads=threads)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+        return {"value": done * fl / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} sub-slices of the same tree ({len(fixed)} modes fixed, width "
+                          f"2^{int(np.log2(c['max_elems']))}, {fl:.3g} flop each, {el:.1f} s)"}
 
     def _cpu_largest_step(self, budget_s, threads):
         import oracle
@@ -1002,7 +1037,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="grid7x8d16",
                     choices=["sweep", "skinny", "peps", "brickwork12", "brickwork30", "grid", "hexagonal",
-                             "brickwork30sv", "grid7x8", "grid7x8d16", "peaks"])
+                             "brickwork30sv", "grid7x8", "grid7x8d16", "qec", "peaks"])
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-fuse", action="store_true",
                     help="plan every step as its own launch (no fused pairs of chained small-operand steps)")

@@ -100,3 +100,43 @@ def test_surface_code_coset_weights_match_oracle(d, p, seed):
         ref.append(float(np.asarray(r).reshape(-1)[0].real))
     if abs(math.log(ref[0] / ref[1])) > 1e-3:
         assert (got[0] > got[1]) == (ref[0] > ref[1])
+
+
+def test_surface_code_full_size_exact_values():
+    """d = 23 (the bench distance) along the column sweep at p = 0, where
+    the coset weight is exactly 1 for the identity's class and 0 for the
+    logical's: Z(0) = 1, Z(stabilizer) = 1, Z(logical) = 0."""
+    from workloads import qec
+    d = 23
+    _, support, logical = qec.planar_code(d)
+    nq = d * d + (d - 1) ** 2
+    tree = qec.sweep_tree(d)
+    for err, expect in ((None, 1.0), (support[len(support) // 2], 1.0), (logical, 0.0)):
+        E = np.zeros(nq, dtype=np.int64)
+        if err is not None:
+            E[err] = 1
+        got, plan = _run(qec.coset_network(d, 0.0, E), tree)
+        assert plan.stats()["max_intermediate"] == 1 << 24
+        assert abs(complex(np.asarray(got).reshape(-1)[0]) - expect) <= TOL
+
+
+def test_surface_code_full_size_relative_weights():
+    """The bench instance (d = 23, p = 0.05, seed 707, relative weights):
+    both column sweeps agree, and multiplying E by a stabilizer changes the
+    relative weight by exactly ((1 - p) / p)^(w(F) - w(E)) (the coset's
+    weight is unchanged, the representative's probability is not)."""
+    from workloads import qec
+    d, p = 23, 0.05
+    _, support, _ = qec.planar_code(d)
+    E = qec.random_error(d, p, 707)
+    z = []
+    for rev in (False, True):
+        got, _ = _run(qec.coset_network(d, p, E, relative=True), qec.sweep_tree(d, reverse=rev))
+        z.append(complex(np.asarray(got).reshape(-1)[0]))
+    assert abs(z[0] - z[1]) <= TOL * abs(z[1])
+    F = E.copy()
+    F[support[100]] ^= 1
+    got, _ = _run(qec.coset_network(d, p, F, relative=True), qec.sweep_tree(d))
+    r = float(np.float32(1 - p)) / float(np.float32(p))
+    expect = z[0] * r ** (int(F.sum()) - int(E.sum()))
+    assert abs(complex(np.asarray(got).reshape(-1)[0]) - expect) <= 2 * TOL * abs(expect)

@@ -105,3 +105,20 @@ def test_coset_weight_is_invariant_under_stabilizers(d):
     G = E.copy()
     G[logical] ^= 1
     assert abs(_z(qec.coset_network(d, 0.08, G)) - z) > 1e-6 * z
+
+
+@pytest.mark.parametrize("d,p,seed", [(3, 0.1, 5), (4, 0.2, 6)])
+def test_relative_weights_and_sweep_trees(d, p, seed):
+    """Z(E) / P(E) from the relative network, times P(E) in float64, is
+    the definition's sum; the column sweeps in both directions give the
+    same value as the greedy tree."""
+    E = qec.random_error(d, 0.2, seed)
+    net = qec.coset_network(d, p, E, relative=True)
+    zr = oracle.contract_network(net, trees.greedy_tree(net))
+    w1, w0 = float(np.float32(p)), float(np.float32(1.0 - p))
+    pe = float(np.prod(np.where(E == 1, w1, w0)))
+    ref = _brute(d, p, E)
+    assert abs(zr * pe - ref) <= 1e-6 * ref   # the leaves hold w(a) / w(E_q) rounded to float32
+    for rev in (False, True):
+        zs = oracle.contract_network(net, qec.sweep_tree(d, reverse=rev))
+        assert abs(zs - zr) <= 1e-12 * abs(zr)

@@ -63,9 +63,14 @@ def random_error(d: int, p: float, seed: int) -> np.ndarray:
     return (np.random.default_rng(seed).random(nq) < p).astype(np.int64)
 
 
-def coset_network(d: int, p: float, error: Optional[Sequence[int]] = None) -> Network:
+def coset_network(d: int, p: float, error: Optional[Sequence[int]] = None, relative: bool = False) -> Network:
     """The coset-weight network Z(E) of the module docstring (E = 0 when
-    ``error`` is None)."""
+    ``error`` is None).  relative: every qubit leaf divided by w(E_q), so
+    that the network gives Z(E) / P(E) with P(E) = prod_q w(E_q), the
+    probability of E itself (the s = 0 term becomes 1 and no term under- or
+    overflows single precision at large d; needs 0 < p < 1)."""
+    if relative and not 0.0 < p < 1.0:
+        raise ValueError("relative weights need 0 < p < 1")
     qubits, support, logical = planar_code(d)
     nq = len(qubits)
     E = np.zeros(nq, dtype=np.int64) if error is None else np.asarray(error, dtype=np.int64).reshape(-1)
@@ -93,7 +98,33 @@ def coset_network(d: int, p: float, error: Optional[Sequence[int]] = None) -> Ne
             t = w[E[q] ^ a[:, None] ^ a[None, :]]
         else:
             raise AssertionError("every qubit belongs to one or two X stabilizers")
+        if relative:
+            t = t / w[E[q]]
         leaves.append(qmodes[q])
         data.append(t.astype(np.complex64))
-    return Network(np.full(len(inc), 2, dtype=np.int64), leaves, [], data, name=f"surface_d{d}",
-                   meta={"d": d, "p": p, "error": E.tolist(), "support": support, "logical": logical})
+    return Network(np.full(len(inc), 2, dtype=np.int64), leaves, [], data,
+                   name=f"surface_d{d}" + ("_rel" if relative else ""),
+                   meta={"d": d, "p": p, "error": E.tolist(), "support": support, "logical": logical,
+                         "relative": relative})
+
+
+def sweep_tree(d: int, reverse: bool = False):
+    """A caterpillar over the leaves in column-major site order (x, then y;
+    at one site the stabilizer before the qubit; from the last column when
+    ``reverse``): the running tensor's open modes are the bonds across the
+    current column, about 2d of them."""
+    from .network import Tree
+    qubits, support, _ = planar_code(d)
+    n = 2 * d - 1
+    stabs = [(x, y) for y in range(0, n, 2) for x in range(1, n, 2)]
+    site = [(x, y) for (x, y) in stabs] + [(x, y) for (x, y) in qubits]
+    sgn = -1 if reverse else 1
+    order = sorted(range(len(site)), key=lambda i: (sgn * site[i][0], site[i][1], i >= len(stabs)))
+    L = len(site)
+    lhs, rhs = [], []
+    cur = order[0]
+    for s, leaf in enumerate(order[1:]):
+        lhs.append(cur)
+        rhs.append(leaf)
+        cur = L + s
+    return Tree(lhs, rhs)
