@@ -228,9 +228,9 @@ typedef struct {
   int32_t k[TNC_FUSE_MAX_STEPS];
   int64_t rows;
   int32_t nouter;
-  int32_t lrow[8], hole[10], wbit[2];
-  int32_t pos_row[TNC_FUSE_MAX_STEPS - 1][8], pos_col[TNC_FUSE_MAX_STEPS - 1][8];
-  int64_t out_row[8], out_col[8];
+  int32_t lrow[9], hole[11], wbit[2];
+  int32_t pos_row[TNC_FUSE_MAX_STEPS - 1][9], pos_col[TNC_FUSE_MAX_STEPS - 1][8];
+  int64_t out_row[9], out_col[8];
   int64_t out_pass[48];
 } tnc_fused_info;
 

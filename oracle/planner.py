@@ -349,15 +349,15 @@ def _log2(v: int) -> int:
 
 def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
     """Chains of steps run as one pass: a long tensor T absorbs a small one
-    (K = S = 4, 8, 16 or 32 entries) and the product T1 is at once the long
+    (K = S = 2, 4, 8, 16 or 32 entries) and the product T1 is at once the long
     operand of the next step, which reduces it against another small tensor
-    (K = S = 4, 8, 16 or 32), with every extent of the modes involved a power
+    (K = S = 2, 4, 8, 16 or 32; K = 2 only beside K <= 8), with every extent of the modes involved a power
     of two, T holding at least 2^16 rows, both steps outside the tiny class,
     neither split over K nor the root, T1 read in place, and the modes of the
     second step's K that T carries spanning at most 1024 / K1 index values (so
     that a pass over 1024 entries of T yields whole rows of the second step).
     A chain extends to the next step in the same way, one step at a time up to
-    FUSE_MAX_STEPS steps, while every K of the chain is 4 or 8, the steps
+    FUSE_MAX_STEPS steps, while every K of the chain is 2, 4 or 8, the steps
     between the first and the last share one K, and the modes of T reduced by
     all later steps together span at most 1024 / K1 values (256 / K1 for
     chains of four or more, which leaves two of a pass's row bits to give its
@@ -386,10 +386,10 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
         if t != L + prev or (c.copy_a if t == c.lhs else c.copy_b) or sw != c.k:
             return None
         if len(ks) == 1:
-            if c.k not in (4, 8, 16, 32):
-                return None
-        elif c.k not in (4, 8) or any(k not in (4, 8) for k in ks) or any(k != ks[1] for k in ks[1:]):
-            return None   # a chain of three or more: K 4 or 8, one K between the first and the last
+            if c.k not in (2, 4, 8, 16, 32) or (2 in (ks[0], c.k) and max(ks[0], c.k) > 8):
+                return None   # a pair: K = 2 only beside K <= 8
+        elif c.k not in (2, 4, 8) or any(k not in (2, 4, 8) for k in ks) or any(k != ks[1] for k in ks[1:]):
+            return None   # a chain of three or more: K 2, 4 or 8, one K between the first and the last
         small = c.rhs if t == c.lhs else c.lhs
         if not all(_is_pow2(ext[x]) for x in sets[small]):
             return None
@@ -400,7 +400,7 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
         if a.cls == CLASS_TINY or a.splits > 1 or s1 in taken or (L + s1) not in consumer:
             continue
         t, r1, s1w = long_short(a)
-        if a.k not in (4, 8, 16, 32) or s1w != a.k or not _is_pow2(r1) or r1 < FUSE_MIN_ROWS:
+        if a.k not in (2, 4, 8, 16, 32) or s1w != a.k or not _is_pow2(r1) or r1 < FUSE_MIN_ROWS:
             continue
         small1 = a.rhs if t == a.lhs else a.lhs
         if not all(_is_pow2(ext[x]) for u in (t, small1) for x in sets[u]):

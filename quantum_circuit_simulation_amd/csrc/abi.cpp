@@ -50,6 +50,13 @@ tnc_status check(hipError_t e, hipStream_t stream, const char *what) {
 static_assert(tnc::kFuseEntries == tnc::kFusePassEntries && tnc::kFuseMaxOuter == tnc::kFuseOuterMax &&
                   tnc::kFuseMaxChain == tnc::kFuseMaxSteps && TNC_FUSE_MAX_STEPS == tnc::kFuseMaxSteps,
               "fused-pair pass size and table length agree between planner and kernel");
+#define TNC_SAME_TABLE(f) \
+  (sizeof(tnc_fused_info::f) == sizeof(tnc::FusedChain::f) && sizeof(tnc::Fused2Args::f) == sizeof(tnc::FusedChain::f))
+static_assert(TNC_SAME_TABLE(lrow) && TNC_SAME_TABLE(hole) && TNC_SAME_TABLE(wbit) && TNC_SAME_TABLE(pos_row) &&
+                  TNC_SAME_TABLE(pos_col) && TNC_SAME_TABLE(out_row) && TNC_SAME_TABLE(out_col) &&
+                  TNC_SAME_TABLE(out_pass),
+              "the fused chain's per-bit tables have one layout in the planner, the ABI and the kernel arguments");
+#undef TNC_SAME_TABLE
 
 const char *op_name(int kind) {
   switch (kind) {
@@ -195,16 +202,12 @@ tnc_status tnc_plan_fused(tnc_plan_t plan, int32_t index, tnc_fused_info *info) 
   }
   info->rows = f.rows;
   info->nouter = f.nouter;
-  for (int i = 0; i < 10; ++i) info->hole[i] = f.hole[i];
-  for (int i = 0; i < 8; ++i) {
-    info->lrow[i] = f.lrow[i];
-    for (int q = 0; q + 1 < tnc::kFuseMaxSteps; ++q) {
-      info->pos_row[q][i] = f.pos_row[q][i];
-      info->pos_col[q][i] = f.pos_col[q][i];
-    }
-    info->out_row[i] = f.out_row[i];
-    info->out_col[i] = f.out_col[i];
-  }
+  std::memcpy(info->hole, f.hole, sizeof(f.hole));
+  std::memcpy(info->lrow, f.lrow, sizeof(f.lrow));
+  std::memcpy(info->pos_row, f.pos_row, sizeof(f.pos_row));
+  std::memcpy(info->pos_col, f.pos_col, sizeof(f.pos_col));
+  std::memcpy(info->out_row, f.out_row, sizeof(f.out_row));
+  std::memcpy(info->out_col, f.out_col, sizeof(f.out_col));
   info->wbit[0] = f.wbit[0];
   info->wbit[1] = f.wbit[1];
   static_assert(sizeof(info->out_pass) / sizeof(info->out_pass[0]) == tnc::kFuseOuterMax, "out_pass length");
@@ -423,16 +426,12 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           fa.nouter = f.nouter;
           fa.wbit[0] = f.wbit[0];
           fa.wbit[1] = f.wbit[1];
-          for (int i = 0; i < 10; ++i) fa.hole[i] = f.hole[i];
-          for (int i = 0; i < 8; ++i) {
-            fa.lrow[i] = f.lrow[i];
-            for (int q = 0; q + 1 < ns; ++q) {
-              fa.pos_row[q][i] = f.pos_row[q][i];
-              fa.pos_col[q][i] = f.pos_col[q][i];
-            }
-            fa.out_row[i] = f.out_row[i];
-            fa.out_col[i] = f.out_col[i];
-          }
+          std::memcpy(fa.hole, f.hole, sizeof(f.hole));
+          std::memcpy(fa.lrow, f.lrow, sizeof(f.lrow));
+          std::memcpy(fa.pos_row, f.pos_row, sizeof(f.pos_row));
+          std::memcpy(fa.pos_col, f.pos_col, sizeof(f.pos_col));
+          std::memcpy(fa.out_row, f.out_row, sizeof(f.out_row));
+          std::memcpy(fa.out_col, f.out_col, sizeof(f.out_col));
           for (int i = 0; i < tnc::kFuseMaxOuter && i < tnc::kFuseOuterMax; ++i) fa.out_pass[i] = f.out_pass[i];
           e = tnc::launch_fused2(fa, stream);
           break;

@@ -1297,8 +1297,9 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int WB12 = W1F > W2F ? W1F : W2F, WB34 = W3F > W4F ? W3F : W4F;
   constexpr int WB = WB12 > WB34 ? WB12 : WB34;
   constexpr int LPT = E / 2 / 64;  // 16-byte loads per lane per pass
-  constexpr int JB2 = KL == 32 ? 5 : KL == 16 ? 4 : KL == 8 ? 3 : 2, LB2 = 10 - JB2;  // the stored product's bits
-  constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : 1;  // log2(K1 / 2)
+  constexpr int JB2 = KL == 32 ? 5 : KL == 16 ? 4 : KL == 8 ? 3 : KL == 4 ? 2 : 1, LB2 = 10 - JB2;  // the stored product's bits
+  constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : K1 == 4 ? 1 : 0;  // log2(K1 / 2)
+  constexpr int LK2 = K2 == 8 ? 3 : K2 == 4 ? 2 : 1;  // log2(K2) for a vector-ALU middle phase
   constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
   constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
   // a phase with K <= 8 runs on the vector ALU, a lane per row (the 32-wide
@@ -1432,7 +1433,10 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
     return p;
   };
   // vector-ALU phases: lane l takes block rows l + 64 i; the lane's row bits
-  // (0 .. 5) place its products, bits 6, 7 come from i
+  // (0 .. 5) place its products, bits 6 .. 8 come from i
+  auto rowhi = [](const int32_t *prow, int i) {
+    return ((i & 1) ? prow[6] : 0) + ((i & 2) ? prow[7] : 0) + ((i & 4) ? prow[8] : 0);
+  };
   int lane_pos_v = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b)
@@ -1521,7 +1525,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.x += x[i][k].x * w[k].x - x[i][k].y * w[k].y;
               y.y += x[i][k].x * w[k].y + x[i][k].y * w[k].x;
             }
-            x2[lp + ((i & 1) ? prow0[6] : 0) + ((i & 2) ? prow0[7] : 0) + pc] = y;
+            x2[lp + rowhi(prow0, i) + pc] = y;
           }
         }
       }
@@ -1579,7 +1583,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           int pc = 0;
           if constexpr (K3 != 0) {
 #pragma unroll
-            for (int c = 0; c < (K2 == 8 ? 3 : 2); ++c)
+            for (int c = 0; c < LK2; ++c)
               if ((s2 >> c) & 1) pc += pcol[c];
           }
 #pragma unroll
@@ -1591,7 +1595,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
             }
             if constexpr (K3 != 0)  // to its place in the next step's block
-              x2[lp2 + ((i & 1) ? prow[6] : 0) + ((i & 2) ? prow[7] : 0) + pc] = y;
+              x2[lp2 + rowhi(prow, i) + pc] = y;
             else
               x2[(lane + 64 * i) * SP + s2 + wo] = y;
           }
@@ -3528,39 +3532,62 @@ static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
 
 hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
   // the planner emits only chains that meet these; anything else is refused
-  auto kok = [](int32_t k) { return k == 4 || k == 8 || k == 16 || k == 32; };
+  auto kok = [](int32_t k) { return k == 2 || k == 4 || k == 8 || k == 16 || k == 32; };
   if (!kok(a.K1) || !kok(a.K2) || a.nouter < 0 || a.nouter > kFuseMaxOuter) return hipErrorInvalidValue;
   if (a.nsteps < 2 || a.nsteps > kFuseMaxChain || (a.nsteps == 2) != (a.K3 == 0)) return hipErrorInvalidValue;
-  if (a.K3 != 0 && (a.K1 > 8 || a.K2 > 8 || (a.K3 != 4 && a.K3 != 8))) return hipErrorInvalidValue;
+  if (a.K3 != 0 && (a.K1 > 8 || a.K2 > 8 || (a.K3 != 2 && a.K3 != 4 && a.K3 != 8))) return hipErrorInvalidValue;
+  // K = 2 pairs only with vector-ALU partners
+  if ((a.K1 == 2 && a.K2 > 8) || (a.K2 == 2 && a.K1 > 8)) return hipErrorInvalidValue;
   for (int q = 0; q < a.nsteps; ++q)
     if (!a.W[q]) return hipErrorInvalidValue;
   if (a.nouter < 2 || a.R != ((int64_t)(kFuseEntries / a.K1) << a.nouter) || !a.X || !a.C ||
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
   if (a.K3 != 0) {
-    // chains of three or more: every K is 4 or 8
-    const int code = (a.K1 == 8) * 4 + (a.K2 == 8) * 2 + (a.K3 == 8);
-    switch (code) {
-      case 0: return run_fused2_k<4, 4, 4>(a, stream);
-      case 1: return run_fused2_k<4, 4, 8>(a, stream);
-      case 2: return run_fused2_k<4, 8, 4>(a, stream);
-      case 3: return run_fused2_k<4, 8, 8>(a, stream);
-      case 4: return run_fused2_k<8, 4, 4>(a, stream);
-      case 5: return run_fused2_k<8, 4, 8>(a, stream);
-      case 6: return run_fused2_k<8, 8, 4>(a, stream);
-      default: return run_fused2_k<8, 8, 8>(a, stream);
+    // chains of three or more: every K is 2, 4 or 8
+    auto last = [&](auto k1c, auto k2c) {
+      constexpr int k1 = decltype(k1c)::value, k2 = decltype(k2c)::value;
+      switch (a.K3) {
+        case 2: return run_fused2_k<k1, k2, 2>(a, stream);
+        case 4: return run_fused2_k<k1, k2, 4>(a, stream);
+        default: return run_fused2_k<k1, k2, 8>(a, stream);
+      }
+    };
+    auto middle = [&](auto k1c) {
+      switch (a.K2) {
+        case 2: return last(k1c, std::integral_constant<int, 2>{});
+        case 4: return last(k1c, std::integral_constant<int, 4>{});
+        default: return last(k1c, std::integral_constant<int, 8>{});
+      }
+    };
+    switch (a.K1) {
+      case 2: return middle(std::integral_constant<int, 2>{});
+      case 4: return middle(std::integral_constant<int, 4>{});
+      default: return middle(std::integral_constant<int, 8>{});
     }
   }
   auto second = [&](auto k1c) {
     constexpr int k1 = decltype(k1c)::value;
-    switch (a.K2) {
-      case 4: return run_fused2_k<k1, 4>(a, stream);
-      case 8: return run_fused2_k<k1, 8>(a, stream);
-      case 16: return run_fused2_k<k1, 16>(a, stream);
-      default: return run_fused2_k<k1, 32>(a, stream);
+    if constexpr (k1 == 2) {
+      switch (a.K2) {
+        case 2: return run_fused2_k<2, 2>(a, stream);
+        case 4: return run_fused2_k<2, 4>(a, stream);
+        default: return run_fused2_k<2, 8>(a, stream);
+      }
+    } else {
+      switch (a.K2) {
+        case 2:
+          if constexpr (k1 <= 8) return run_fused2_k<k1, 2>(a, stream);
+          else return hipErrorInvalidValue;
+        case 4: return run_fused2_k<k1, 4>(a, stream);
+        case 8: return run_fused2_k<k1, 8>(a, stream);
+        case 16: return run_fused2_k<k1, 16>(a, stream);
+        default: return run_fused2_k<k1, 32>(a, stream);
+      }
     }
   };
   switch (a.K1) {
+    case 2: return second(std::integral_constant<int, 2>{});
     case 4: return second(std::integral_constant<int, 4>{});
     case 8: return second(std::integral_constant<int, 8>{});
     case 16: return second(std::integral_constant<int, 16>{});

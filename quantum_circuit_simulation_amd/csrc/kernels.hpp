@@ -68,9 +68,9 @@ struct Fused2Args {
                      // steps whose every K is 4 or 8 and whose middle steps all have K2
   int32_t nsteps;
   int32_t nouter;
-  int32_t lrow[8], hole[10], wbit[2];
-  int32_t pos_row[kFuseMaxChain - 1][8], pos_col[kFuseMaxChain - 1][8];
-  int64_t out_row[8], out_col[8];
+  int32_t lrow[9], hole[11], wbit[2];
+  int32_t pos_row[kFuseMaxChain - 1][9], pos_col[kFuseMaxChain - 1][8];
+  int64_t out_row[9], out_col[8];
   int64_t out_pass[kFuseMaxOuter];
 };
 

@@ -257,7 +257,7 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedChain *f
   } ph[kFuseMaxSteps];
   if (n < 2 || n > kFuseMaxSteps) return false;
   // longer chains run every step on the vector ALU, the middle ones with one K
-  auto kok = [n](int64_t k) { return k == 4 || k == 8 || (n == 2 && (k == 16 || k == 32)); };
+  auto kok = [n](int64_t k) { return k == 2 || k == 4 || k == 8 || (n == 2 && (k == 16 || k == 32)); };
   for (int q = 0; q < n; ++q) {
     const Node &nd = p.nodes[st[q]];
     Phase &h = ph[q];
@@ -290,6 +290,8 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedChain *f
       (i < h.lr ? h.tr[i] : h.tc[i - h.lr]) = t;
     }
   }
+  // K = 2 steps run only beside vector-ALU steps (K <= 8)
+  if ((ph[0].K == 2 || ph[1].K == 2) && (ph[0].K > 8 || ph[1].K > 8)) return false;
   const Phase &first = ph[0], &last = ph[n - 1];
   if (first.R < kFuseMinRows || first.lr - first.lb > kFuseOuterMax) return false;
   // A row bit of the first long operand passes through the chain: at each

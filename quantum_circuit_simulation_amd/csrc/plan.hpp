@@ -79,8 +79,9 @@ struct Node {
 // A chain of 2 .. kFuseMaxSteps complex64 steps run as one pass over the
 // first step's long operand (k_fused2): each step's product is at once the
 // next step's long operand, and each step absorbs a small tensor with K = S
-// (4, 8, 16 or 32 entries; in chains of three or more every K is 4 or 8 and
-// the steps between the first and the last share one K).  Built when every
+// (2, 4, 8, 16 or 32 entries, K = 2 only beside K <= 8; in chains of three
+// or more every K is 2, 4 or 8 and the steps between the first and the last
+// share one K).  Built when every
 // index is a power of two and a pass of kFusePassEntries entries of the long
 // operand holds whole rows of every step; the tables give, per index bit, the
 // place of an entry (see Fused2Args in kernels.hpp).
@@ -95,12 +96,12 @@ struct FusedChain {
   int32_t k[kFuseMaxSteps] = {};       // each step's K (= its short side S)
   int64_t rows = 0;          // rows of the first step's long operand
   int32_t nouter = 0;
-  int32_t lrow[8] = {};      // the pass's local row bits of the long operand, ascending
+  int32_t lrow[9] = {};      // the pass's local row bits of the long operand, ascending
   int32_t wbit[2] = {};      // row bits set by bits 0, 1 of the pass index (a workgroup's four passes)
-  int32_t hole[10] = {};     // lrow and wbit, ascending: the rest count the workgroup's rounds
+  int32_t hole[11] = {};     // lrow and wbit, ascending: the rest count the workgroup's rounds
   // [q]: the places of step q's products in step q + 1's block
-  int32_t pos_row[kFuseMaxSteps - 1][8] = {}, pos_col[kFuseMaxSteps - 1][8] = {};
-  int64_t out_row[8] = {}, out_col[8] = {};  // the last product's offsets
+  int32_t pos_row[kFuseMaxSteps - 1][9] = {}, pos_col[kFuseMaxSteps - 1][8] = {};
+  int64_t out_row[9] = {}, out_col[8] = {};  // the last product's offsets
   int64_t out_pass[kFuseOuterMax] = {};
 };
 

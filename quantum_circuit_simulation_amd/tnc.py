@@ -88,11 +88,11 @@ class NodeInfo(ctypes.Structure):
 class FusedInfo(ctypes.Structure):
     _fields_ = [("nsteps", ctypes.c_int32), ("step", ctypes.c_int32 * FUSE_MAX_STEPS),
                 ("longop", ctypes.c_int32 * FUSE_MAX_STEPS), ("k", ctypes.c_int32 * FUSE_MAX_STEPS),
-                ("rows", ctypes.c_int64), ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 8),
-                ("hole", ctypes.c_int32 * 10), ("wbit", ctypes.c_int32 * 2),
-                ("pos_row", (ctypes.c_int32 * 8) * (FUSE_MAX_STEPS - 1)),
+                ("rows", ctypes.c_int64), ("nouter", ctypes.c_int32), ("lrow", ctypes.c_int32 * 9),
+                ("hole", ctypes.c_int32 * 11), ("wbit", ctypes.c_int32 * 2),
+                ("pos_row", (ctypes.c_int32 * 9) * (FUSE_MAX_STEPS - 1)),
                 ("pos_col", (ctypes.c_int32 * 8) * (FUSE_MAX_STEPS - 1)),
-                ("out_row", ctypes.c_int64 * 8), ("out_col", ctypes.c_int64 * 8), ("out_pass", ctypes.c_int64 * 48)]
+                ("out_row", ctypes.c_int64 * 9), ("out_col", ctypes.c_int64 * 8), ("out_pass", ctypes.c_int64 * 48)]
 
     def as_dict(self):
         def plain(v):

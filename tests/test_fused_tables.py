@@ -17,7 +17,8 @@ from workloads.network import Network, Tree
 
 CASES = [(4, 4, 0, 16, "s"), (4, 4, 2, 16, "o"), (4, 5, 2, 16, "s"), (5, 4, 1, 16, "s"), (5, 5, 3, 16, "o"),
          (4, 4, 4, 16, "s"), (5, 4, 4, 16, "o"), (4, 5, 0, 16, "o"), (2, 2, 0, 16, "s"), (2, 3, 2, 16, "o"),
-         (3, 2, 1, 16, "s"), (3, 3, 3, 16, "o"), (3, 4, 1, 16, "s"), (5, 2, 2, 16, "o")]
+         (3, 2, 1, 16, "s"), (3, 3, 3, 16, "o"), (3, 4, 1, 16, "s"), (5, 2, 2, 16, "o"),
+         (1, 1, 0, 16, "s"), (1, 2, 1, 16, "o"), (3, 1, 1, 16, "s"), (1, 3, 0, 16, "o")]
 
 
 def _bits_sum(idx, table, nbits):

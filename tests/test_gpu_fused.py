@@ -1,9 +1,10 @@
-"""Fused chains of steps (k_fused2): a long tensor T absorbs a small W1 (4,
-8, 16 or 32 entries of K, as many outputs) and the product is reduced at
+"""Fused chains of steps (k_fused2): a long tensor T absorbs a small W1 (2,
+4, 8, 16 or 32 entries of K, as many outputs) and the product is reduced at
 once against another small W2 (and, all K <= 8, up to four more), in one
 pass over T.  Every output entry of the whole contraction against the
 oracle, for (K1, K2) in {4, 8, 16, 32}^2 (the vector-ALU and matrix-core
-phases and their mixes) and chains of three to six steps, with each later
+phases and their mixes), pairs with K = 2, and chains of three to six
+steps (K = 2, 4 and 8 mixed), with each later
 step reducing 0 .. all of the modes the earlier steps brought in, random
 declared orders and output orders (so the chain's product lands in many
 layouts), the innermost output mode local to a pass (16-byte pair stores)
@@ -142,7 +143,8 @@ CASES = [(4, 4, 0, 16, "s"), (4, 4, 2, 17, "s"), (4, 4, 4, 16, "o"), (4, 5, 2, 1
          (5, 5, 3, 17, "o"), (4, 5, 0, 16, "o"), (5, 5, 0, 18, "s"), (5, 4, 4, 17, "o"), (4, 4, 1, 19, "s"),
          (2, 2, 0, 16, "s"), (2, 2, 2, 17, "o"), (2, 3, 1, 16, "s"), (3, 2, 2, 17, "o"), (3, 3, 1, 16, "s"),
          (3, 3, 3, 18, "o"), (2, 2, 1, 19, "s"), (3, 4, 1, 17, "s"), (2, 5, 2, 16, "o"), (5, 3, 2, 17, "s"),
-         (4, 2, 1, 16, "s"), (5, 2, 0, 16, "o"), (2, 4, 2, 17, "s")]
+         (4, 2, 1, 16, "s"), (5, 2, 0, 16, "o"), (2, 4, 2, 17, "s"),
+         (1, 1, 0, 16, "s"), (1, 2, 1, 17, "o"), (3, 1, 1, 16, "s"), (1, 3, 0, 16, "o")]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "k{}_{}_v{}_r{}_{}".format(*c))
@@ -177,7 +179,10 @@ def test_fused_chain_of_three_matches_oracle(case):
 CHAINN = [((2, 2, 2, 2), (0, 1, 1, 0), 16, "s"), ((2, 2, 2, 2, 2), (0, 0, 0, 1, 1), 16, "o"),
           ((2, 2, 2, 2, 2, 2), (0, 2, 1, 2, 1, 2), 17, "s"), ((3, 3, 3, 3), (0, 1, 2, 1), 16, "o"),
           ((2, 3, 3, 2), (0, 1, 2, 1), 17, "s"), ((3, 2, 2, 2, 3), (0, 1, 1, 1, 2), 16, "s"),
-          ((2, 2, 2, 2, 2), (0, 1, 0, 1, 0), 18, "s"), ((3, 3, 3, 3, 3), (0, 2, 2, 2, 2), 16, "o")]
+          ((2, 2, 2, 2, 2), (0, 1, 0, 1, 0), 18, "s"), ((3, 3, 3, 3, 3), (0, 2, 2, 2, 2), 16, "o"),
+          ((1, 1, 1, 1), (0, 1, 0, 1), 17, "s"), ((2, 1, 1, 2), (0, 1, 1, 1), 16, "o"),
+          ((1, 2, 2, 1), (0, 1, 1, 0), 16, "s"), ((1,) * 6, (0, 1, 1, 0, 1, 1), 17, "o"),
+          ((3, 1, 1, 1, 3), (0, 1, 0, 1, 2), 16, "s")]
 
 
 @pytest.mark.parametrize("case", CHAINN, ids=lambda c: "k{}_v{}_r{}_{}".format(
