@@ -111,9 +111,10 @@ typedef struct {
   int64_t slice_end;          /*   slice_begin <= sigma < slice_end (0 <= begin < end <= number of
                                    slices) and leaves their sum in `out`: partial sums that add up to
                                    the whole result, e.g. one range per process or per call */
-  int32_t fuse;               /* 1: where a long tensor absorbs a small one (4, 8, 16 or 32
-                                 entries of K, as many outputs) and the product is reduced at once
-                                 against another such small tensor (and, all K 4 or 8, up to
+  int32_t fuse;               /* 1: where a long tensor absorbs a small one (2, 4, 8, 16 or 32
+                                 entries of K, as many outputs; 2 only beside K <= 8) and the product
+                                 is reduced at once against another such small tensor (and, all K
+                                 2, 4 or 8, up to
                                  TNC_FUSE_MAX_STEPS steps in a row), the chain runs in one pass
                                  over the long operand and only its last product is stored
                                  (complex64, exact, lifetime order, every extent a power of two,
@@ -205,7 +206,8 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  * nsteps - 1] (2 .. TNC_FUSE_MAX_STEPS; unused entries -1): each step's long
  * operand is the previous step's product (the first step's: its lhs for
  * longop = 0, else its rhs) and its small operand has k[q] x k[q] entries
- * (4, 8, 16 or 32; in chains of three or more every k is 4 or 8, and the
+ * (2, 4, 8, 16 or 32, 2 only beside k <= 8; in chains of three or more
+ * every k is 2, 4 or 8, and the
  * steps between the first and the last share one k).  Every index is a sum
  * of one offset per set bit.  A pass takes 1024 entries of the first long
  * operand X (row-major [rows, k[0]]): its local row rho (0 .. 1024/k[0] - 1)

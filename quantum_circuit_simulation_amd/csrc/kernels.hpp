@@ -63,9 +63,10 @@ struct Fused2Args {
   const float2 *W[kFuseMaxChain];    // step q's small operand, row-major [K, K] (S rows)
   float2 *C;
   int64_t R;         // a multiple of 1024 / K1; R / (1024 / K1) = 2^nouter passes
-  int32_t K1, K2;    // the first and second step's K: 4, 8, 16 or 32 (K <= 8: vector-ALU phase)
-  int32_t K3;        // 0 (a pair), or the last step's K (4 or 8) in a chain of nsteps >= 3
-                     // steps whose every K is 4 or 8 and whose middle steps all have K2
+  int32_t K1, K2;    // the first and second step's K: 2, 4, 8, 16 or 32 (K <= 8: vector-ALU
+                     // phase; 2 only beside K <= 8)
+  int32_t K3;        // 0 (a pair), or the last step's K (2, 4 or 8) in a chain of nsteps >= 3
+                     // steps whose every K is 2, 4 or 8 and whose middle steps all have K2
   int32_t nsteps;
   int32_t nouter;
   int32_t lrow[9], hole[11], wbit[2];
