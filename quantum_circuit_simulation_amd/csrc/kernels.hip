@@ -1495,8 +1495,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
       asm volatile("" : "+v"(wo));
       [[maybe_unused]] const float2 *w1 = (const float2 *)bt1 + wo, *w2 = (const float2 *)bt2 + wo;
       [[maybe_unused]] const float2 *w3 = (const float2 *)bt3 + wo;
-      if constexpr (V1)
-      {
+      if constexpr (V1) {
         // every read of the block comes before the first write (in place)
         float2 x[RPL1][K1];
 #pragma unroll
@@ -1528,100 +1527,95 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
             x2[lp + rowhi(prow0, i) + pc] = y;
           }
         }
-      }
-      else
-    {
-      f32x16 acc[NB1], acw[NB1];
-      fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
-      // the lane's base place, opaque per pass so that its 16 NB1 sums with
-      // the (uniform) row parts are formed here rather than held in registers
-      int lp = lane_pos;
-      asm volatile("" : "+v"(lp));
-      if constexpr (K1 == 32) {
-#pragma unroll
-        for (int nb = 0; nb < NB1; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            *(float2 *)&xf[2 * (lp + rpos(nb, r))] = make_float2(acc[nb][r], acw[nb][r]);
       } else {
-        const int part = l32 >> 4;
+        f32x16 acc[NB1], acw[NB1];
+        fused_phase<K1, NB1>(xb, bt1, lane, acc, acw);
+        // the lane's base place, opaque per pass so that its 16 NB1 sums with
+        // the (uniform) row parts are formed here rather than held in registers
+        int lp = lane_pos;
+        asm volatile("" : "+v"(lp));
+        if constexpr (K1 == 32) {
 #pragma unroll
-        for (int nb = 0; nb < NB1; ++nb)
+          for (int nb = 0; nb < NB1; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
+            for (int r = 0; r < 16; ++r)
+              *(float2 *)&xf[2 * (lp + rpos(nb, r))] = make_float2(acc[nb][r], acw[nb][r]);
+        } else {
+          const int part = l32 >> 4;
+#pragma unroll
+          for (int nb = 0; nb < NB1; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
+        }
       }
-    }
-      if constexpr (V2)
-      {
+      if constexpr (V2) {
         // the second step, and in a chain every step up to the last, each
         // with its own table and places in the next step's block
         const int nmid = K3 ? a.nsteps - 2 : 1;
 #pragma unroll
         for (int m = 0; m < NMID; ++m) {
-        if (m >= nmid) break;
-        float2 z[RPL2][K2];
+          if (m >= nmid) break;
+          float2 z[RPL2][K2];
 #pragma unroll
-        for (int i = 0; i < RPL2; ++i)
+          for (int i = 0; i < RPL2; ++i)
 #pragma unroll
-          for (int q = 0; q < K2 / 2; ++q) {
-            const float4 f = xb[(lane + 64 * i) * RS2 + q];
-            z[i][2 * q] = make_float2(f.x, f.y);
-            z[i][2 * q + 1] = make_float2(f.z, f.w);
-          }
-        [[maybe_unused]] const int32_t *prow = a.pos_row[1 + m], *pcol = a.pos_col[1 + m];
-        [[maybe_unused]] int lp2 = wo;
-        if constexpr (K3 != 0) {
-#pragma unroll
-          for (int b = 0; b < 6; ++b)
-            if ((lane >> b) & 1) lp2 += prow[b];
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < K2; ++s2) {
-          float2 w[K2];
-#pragma unroll
-          for (int k = 0; k < K2; ++k) w[k] = w2[(m * K2 + s2) * K2 + k];
-          int pc = 0;
+            for (int q = 0; q < K2 / 2; ++q) {
+              const float4 f = xb[(lane + 64 * i) * RS2 + q];
+              z[i][2 * q] = make_float2(f.x, f.y);
+              z[i][2 * q + 1] = make_float2(f.z, f.w);
+            }
+          [[maybe_unused]] const int32_t *prow = a.pos_row[1 + m], *pcol = a.pos_col[1 + m];
+          [[maybe_unused]] int lp2 = wo;
           if constexpr (K3 != 0) {
 #pragma unroll
-            for (int c = 0; c < LK2; ++c)
-              if ((s2 >> c) & 1) pc += pcol[c];
+            for (int b = 0; b < 6; ++b)
+              if ((lane >> b) & 1) lp2 += prow[b];
           }
 #pragma unroll
-          for (int i = 0; i < RPL2; ++i) {
-            float2 y = make_float2(0.f, 0.f);
+          for (int s2 = 0; s2 < K2; ++s2) {
+            float2 w[K2];
 #pragma unroll
-            for (int k = 0; k < K2; ++k) {
-              y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
-              y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
+            for (int k = 0; k < K2; ++k) w[k] = w2[(m * K2 + s2) * K2 + k];
+            int pc = 0;
+            if constexpr (K3 != 0) {
+#pragma unroll
+              for (int c = 0; c < LK2; ++c)
+                if ((s2 >> c) & 1) pc += pcol[c];
             }
-            if constexpr (K3 != 0)  // to its place in the next step's block
-              x2[lp2 + rowhi(prow, i) + pc] = y;
-            else
-              x2[(lane + 64 * i) * SP + s2 + wo] = y;
+#pragma unroll
+            for (int i = 0; i < RPL2; ++i) {
+              float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+              for (int k = 0; k < K2; ++k) {
+                y.x += z[i][k].x * w[k].x - z[i][k].y * w[k].y;
+                y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
+              }
+              if constexpr (K3 != 0)  // to its place in the next step's block
+                x2[lp2 + rowhi(prow, i) + pc] = y;
+              else
+                x2[(lane + 64 * i) * SP + s2 + wo] = y;
+            }
           }
         }
+      } else {
+        f32x16 acc[NB2], acw[NB2];
+        fused_phase<K2, NB2>(xb, bt2, lane, acc, acw);
+        if constexpr (K2 == 32) {
+#pragma unroll
+          for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              *(float2 *)&xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + l32) * 2] =
+                  make_float2(acc[nb][r], acw[nb][r]);
+        } else {
+          const int j = l32 & 15, part = l32 >> 4;
+#pragma unroll
+          for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
         }
       }
-      else
-    {
-      f32x16 acc[NB2], acw[NB2];
-      fused_phase<K2, NB2>(xb, bt2, lane, acc, acw);
-      if constexpr (K2 == 32) {
-#pragma unroll
-        for (int nb = 0; nb < NB2; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            *(float2 *)&xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + l32) * 2] =
-                make_float2(acc[nb][r], acw[nb][r]);
-      } else {
-        const int j = l32 & 15, part = l32 >> 4;
-#pragma unroll
-        for (int nb = 0; nb < NB2; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            xf[((nb * 32 + (r / 4) * 8 + h * 4 + (r % 4)) * SP + j) * 2 + part] = acc[nb][r];
-      }
-    }
       if constexpr (K3 != 0) {
         // third phase: the block's rows times W3, staged
         constexpr int RPL3 = ROWS3 / 64;
