@@ -207,8 +207,7 @@ tnc_status tnc_plan_node(tnc_plan_t plan, int32_t step, tnc_node_info *info);
  * operand is the previous step's product (the first step's: its lhs for
  * longop = 0, else its rhs) and its small operand has k[q] x k[q] entries
  * (2, 4, 8, 16 or 32, 2 only beside k <= 8; in chains of three or more
- * every k is 2, 4 or 8, and the
- * steps between the first and the last share one k).  Every index is a sum
+ * every k is 2, 4 or 8).  Every index is a sum
  * of one offset per set bit.  A pass takes 1024 entries of the first long
  * operand X (row-major [rows, k[0]]): its local row rho (0 .. 1024/k[0] - 1)
  * is X row spread(rho) + round part + wave part, where spread puts bit j of

@@ -357,8 +357,7 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
     second step's K that T carries spanning at most 1024 / K1 index values (so
     that a pass over 1024 entries of T yields whole rows of the second step).
     A chain extends to the next step in the same way, one step at a time up to
-    FUSE_MAX_STEPS steps, while every K of the chain is 2, 4 or 8, the steps
-    between the first and the last share one K, and the modes of T reduced by
+    FUSE_MAX_STEPS steps, while every K of the chain is 2, 4 or 8 and the modes of T reduced by
     all later steps together span at most 1024 / K1 values (256 / K1 for
     chains of four or more, which leaves two of a pass's row bits to give its
     stores contiguous pieces).  Chains are taken in step order and do not
@@ -388,8 +387,8 @@ def fused_pairs(nodes, sets, ext, L, eb, policy, fuse=True):
         if len(ks) == 1:
             if c.k not in (2, 4, 8, 16, 32) or (2 in (ks[0], c.k) and max(ks[0], c.k) > 8):
                 return None   # a pair: K = 2 only beside K <= 8
-        elif c.k not in (2, 4, 8) or any(k not in (2, 4, 8) for k in ks) or any(k != ks[1] for k in ks[1:]):
-            return None   # a chain of three or more: K 2, 4 or 8, one K between the first and the last
+        elif c.k not in (2, 4, 8) or any(k not in (2, 4, 8) for k in ks):
+            return None   # a chain of three or more: every K 2, 4 or 8
         small = c.rhs if t == c.lhs else c.lhs
         if not all(_is_pow2(ext[x]) for x in sets[small]):
             return None

@@ -423,6 +423,7 @@ tnc_status run_plan(tnc_plan_t plan, const void *const *leaves, void *out, void 
           fa.K2 = f.k[1];
           fa.K3 = ns > 2 ? f.k[ns - 1] : 0;
           fa.nsteps = ns;
+          for (int q = 1; q + 1 < ns; ++q) fa.kmid[q - 1] = f.k[q];
           fa.nouter = f.nouter;
           fa.wbit[0] = f.wbit[0];
           fa.wbit[1] = f.wbit[1];

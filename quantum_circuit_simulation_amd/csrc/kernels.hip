@@ -1285,13 +1285,70 @@ __device__ __forceinline__ void fused_phase(const float4 *xb, const float *bt, i
   }
 }
 
+// The part of a vector-ALU phase's product place set by the bits of i (a
+// lane takes block rows lane + 64 i; the lane's own bits 0 .. 5 are added
+// separately): row bits 6 .. 8 of the block.
+__device__ __forceinline__ int fused_rowhi(const int32_t *prow, int i) {
+  return ((i & 1) ? prow[6] : 0) + ((i & 2) ? prow[7] : 0) + ((i & 4) ? prow[8] : 0);
+}
+
+// A middle step of a fused chain on the vector ALU: lane l takes block rows
+// l + 64 i of the step's block xb ([1024 / K rows][K / 2 + 1 entry pairs]),
+// multiplies them by the step's table w ([K][K] complex, output rows) and
+// writes each product to its place in the next step's block x2: the block
+// row's bits through prow, the column's through pcol.  All of the lane's
+// reads of xb come before its first write.  wo is an opaque zero that keeps
+// the table reads inside the pass loop.
+template <int K>
+__device__ __forceinline__ void fused_mid_step(const float4 *xb, float2 *x2, const float2 *w, int lane, int wo,
+                                               const int32_t *prow, const int32_t *pcol) {
+  constexpr int RPL = kFuseEntries / K / 64, RS = K / 2 + 1, LK = K == 8 ? 3 : K == 4 ? 2 : 1;
+  float2 z[RPL][K];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int q = 0; q < K / 2; ++q) {
+      const float4 f = xb[(lane + 64 * i) * RS + q];
+      z[i][2 * q] = make_float2(f.x, f.y);
+      z[i][2 * q + 1] = make_float2(f.z, f.w);
+    }
+  int lp = wo;
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((lane >> b) & 1) lp += prow[b];
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    float2 wr[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wr[k] = w[s * K + k];
+    int pc = 0;
+#pragma unroll
+    for (int c = 0; c < LK; ++c)
+      if ((s >> c) & 1) pc += pcol[c];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      float2 y = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        y.x += z[i][k].x * wr[k].x - z[i][k].y * wr[k].y;
+        y.y += z[i][k].x * wr[k].y + z[i][k].y * wr[k].x;
+      }
+      x2[lp + fused_rowhi(prow, i) + pc] = y;
+    }
+  }
+}
+
+// K3 != 0: a chain of three or more steps; its middle steps all have K2,
+// or with K2 = 0 take their K (2, 4 or 8) from a.kmid at run time.
 template <int K1, int K2, int K3>
 __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int E = kFuseEntries;
   constexpr int KL = K3 ? K3 : K2;  // the last phase's K (K3 = 0: a pair)
-  constexpr int ROWS1 = E / K1, ROWS2 = E / K2, ROWS3 = K3 ? E / K3 : 1, ROWSL = E / KL;
+  static_assert(K2 != 0 || K3 != 0, "K2 = 0: a chain whose middle steps take their K at run time");
+  constexpr int K2E = K2 ? K2 : 2;  // a chain's middle blocks are at most those of K = 2
+  constexpr int ROWS1 = E / K1, ROWS2 = E / K2E, ROWS3 = K3 ? E / K3 : 1, ROWSL = E / KL;
   constexpr int NB1 = ROWS1 / 32, NB2 = ROWS2 / 32;
-  constexpr int RS1 = K1 / 2 + 1, RS2 = K2 / 2 + 1, RS3 = K3 / 2 + 1;  // 16-byte units per LDS row, one pad
+  constexpr int RS1 = K1 / 2 + 1, RS2 = K2E / 2 + 1, RS3 = K3 / 2 + 1;  // 16-byte units per LDS row, one pad
   constexpr int SP = KL + 1;                         // staged products: complex entries per row
   constexpr int W1F = ROWS1 * RS1, W2F = ROWS2 * RS2, W3F = (ROWSL * SP + 1) / 2, W4F = K3 ? ROWS3 * RS3 : 0;
   constexpr int WB12 = W1F > W2F ? W1F : W2F, WB34 = W3F > W4F ? W3F : W4F;
@@ -1299,16 +1356,17 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   constexpr int LPT = E / 2 / 64;  // 16-byte loads per lane per pass
   constexpr int JB2 = KL == 32 ? 5 : KL == 16 ? 4 : KL == 8 ? 3 : KL == 4 ? 2 : 1, LB2 = 10 - JB2;  // the stored product's bits
   constexpr int LKH = K1 == 32 ? 4 : K1 == 16 ? 3 : K1 == 8 ? 2 : K1 == 4 ? 1 : 0;  // log2(K1 / 2)
-  constexpr int LK2 = K2 == 8 ? 3 : K2 == 4 ? 2 : 1;  // log2(K2) for a vector-ALU middle phase
   constexpr int LB1 = 9 - LKH;            // log2(ROWS1): the pass's local row bits
   constexpr int NPT = 4 * E / 2 / 256;    // store pairs per thread in a workgroup round
   // a phase with K <= 8 runs on the vector ALU, a lane per row (the 32-wide
   // MFMA tile would need all 1024 / K rows' accumulators at once); its table
   // holds W itself
-  constexpr bool V1 = K1 <= 8, V2 = K2 <= 8;
+  constexpr bool V1 = K1 <= 8, V2 = K2E <= 8;
+  constexpr int LK2 = K2E == 8 ? 3 : K2E == 4 ? 2 : 1;  // log2(K2) for a vector-ALU middle phase
+  constexpr int NMID = K3 ? kFuseMaxChain - 2 : 1;      // the most middle steps
   constexpr int BT1 = V1 ? 2 * K1 * K1 : (K1 == 32 ? 2 : 1) * K1 * 64;
-  constexpr int NMID = K3 ? kFuseMaxChain - 2 : 1;  // the most steps with K2 (all but the first and last)
-  constexpr int BT2 = V2 ? NMID * 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
+  // a chain's middle tables sit 64 complex entries apart (K <= 8)
+  constexpr int BT2 = K3 ? (kFuseMaxChain - 2) * 128 : V2 ? 2 * K2 * K2 : (K2 == 32 ? 2 : 1) * K2 * 64;
   constexpr int BT3 = K3 ? 2 * K3 * K3 : 2;
   // chains of three or more run every phase on the vector ALU
   static_assert(K3 == 0 || (V1 && V2 && K3 <= 8), "chains of three or more have K <= 8");
@@ -1328,10 +1386,15 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
     fused_btable<K1>(a.W[0], bt1, tid);
   }
   if constexpr (V2) {
-    // a chain's middle steps' tables one after another
-    const int nmid = K3 ? a.nsteps - 2 : 1;
-    for (int e = tid; e < nmid * K2 * K2; e += 256)
-      *(float2 *)&bt2[2 * e] = a.W[1 + e / (K2 * K2)][e % (K2 * K2)];
+    if constexpr (K3 != 0) {
+      // the chain's middle steps' tables, 64 complex entries apart (each K <= 8)
+      for (int e = tid; e < (a.nsteps - 2) * 64; e += 256) {
+        const int m = e >> 6, j = e & 63;
+        if (j < a.kmid[m] * a.kmid[m]) *(float2 *)&bt2[2 * e] = a.W[1 + m][j];
+      }
+    } else {
+      for (int e = tid; e < K2 * K2; e += 256) *(float2 *)&bt2[2 * e] = a.W[1][e];
+    }
   } else {
     fused_btable<K2>(a.W[1], bt2, tid);
   }
@@ -1434,9 +1497,6 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
   };
   // vector-ALU phases: lane l takes block rows l + 64 i; the lane's row bits
   // (0 .. 5) place its products, bits 6 .. 8 come from i
-  auto rowhi = [](const int32_t *prow, int i) {
-    return ((i & 1) ? prow[6] : 0) + ((i & 2) ? prow[7] : 0) + ((i & 4) ? prow[8] : 0);
-  };
   int lane_pos_v = 0;
 #pragma unroll
   for (int b = 0; b < 6; ++b)
@@ -1524,7 +1584,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
               y.x += x[i][k].x * w[k].x - x[i][k].y * w[k].y;
               y.y += x[i][k].x * w[k].y + x[i][k].y * w[k].x;
             }
-            x2[lp + rowhi(prow0, i) + pc] = y;
+            x2[lp + fused_rowhi(prow0, i) + pc] = y;
           }
         }
       } else {
@@ -1548,9 +1608,22 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
             for (int r = 0; r < 16; ++r) xf[2 * (lp + rpos(nb, r)) + part] = acc[nb][r];
         }
       }
-      if constexpr (V2) {
-        // the second step, and in a chain every step up to the last, each
-        // with its own table and places in the next step's block
+      if constexpr (K3 != 0 && K2 == 0) {
+        // the chain's middle steps, each with its own K, table and places
+        // in the next step's block
+#pragma unroll
+        for (int m = 0; m < kFuseMaxChain - 2; ++m) {
+          if (m >= a.nsteps - 2) break;
+          const float2 *wm = w2 + m * 64;
+          const int32_t *prow = a.pos_row[1 + m], *pcol = a.pos_col[1 + m];
+          if (a.kmid[m] == 2) fused_mid_step<2>(xb, x2, wm, lane, wo, prow, pcol);
+          else if (a.kmid[m] == 4) fused_mid_step<4>(xb, x2, wm, lane, wo, prow, pcol);
+          else fused_mid_step<8>(xb, x2, wm, lane, wo, prow, pcol);
+        }
+      } else if constexpr (V2) {
+        // the second step, and in a chain whose middle steps share K2 every
+        // step up to the last, each with its own table and places in the
+        // next step's block
         const int nmid = K3 ? a.nsteps - 2 : 1;
 #pragma unroll
         for (int m = 0; m < NMID; ++m) {
@@ -1575,7 +1648,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
           for (int s2 = 0; s2 < K2; ++s2) {
             float2 w[K2];
 #pragma unroll
-            for (int k = 0; k < K2; ++k) w[k] = w2[(m * K2 + s2) * K2 + k];
+            for (int k = 0; k < K2; ++k) w[k] = w2[m * 64 + s2 * K2 + k];
             int pc = 0;
             if constexpr (K3 != 0) {
 #pragma unroll
@@ -1591,7 +1664,7 @@ __global__ __launch_bounds__(256) void k_fused2(Fused2Args a) {
                 y.y += z[i][k].x * w[k].y + z[i][k].y * w[k].x;
               }
               if constexpr (K3 != 0)  // to its place in the next step's block
-                x2[lp2 + rowhi(prow, i) + pc] = y;
+                x2[lp2 + fused_rowhi(prow, i) + pc] = y;
               else
                 x2[(lane + 64 * i) * SP + s2 + wo] = y;
             }
@@ -3538,17 +3611,24 @@ hipError_t launch_fused2(const Fused2Args &a, hipStream_t stream) {
       ((uintptr_t)a.X & 15) != 0)
     return hipErrorInvalidValue;
   if (a.K3 != 0) {
-    // chains of three or more: every K is 2, 4 or 8
+    // chains of three or more: every K is 2, 4 or 8, the middle ones at run time
+    for (int m = 0; m < a.nsteps - 2; ++m)
+      if (a.kmid[m] != 2 && a.kmid[m] != 4 && a.kmid[m] != 8) return hipErrorInvalidValue;
+    // middle steps that share one K run the instance compiled for it
+    bool same = true;
+    for (int m = 1; m < a.nsteps - 2; ++m) same = same && a.kmid[m] == a.kmid[0];
+    const int k2 = same ? a.kmid[0] : 0;
     auto last = [&](auto k1c, auto k2c) {
-      constexpr int k1 = decltype(k1c)::value, k2 = decltype(k2c)::value;
+      constexpr int k1 = decltype(k1c)::value, kk2 = decltype(k2c)::value;
       switch (a.K3) {
-        case 2: return run_fused2_k<k1, k2, 2>(a, stream);
-        case 4: return run_fused2_k<k1, k2, 4>(a, stream);
-        default: return run_fused2_k<k1, k2, 8>(a, stream);
+        case 2: return run_fused2_k<k1, kk2, 2>(a, stream);
+        case 4: return run_fused2_k<k1, kk2, 4>(a, stream);
+        default: return run_fused2_k<k1, kk2, 8>(a, stream);
       }
     };
     auto middle = [&](auto k1c) {
-      switch (a.K2) {
+      switch (k2) {
+        case 0: return last(k1c, std::integral_constant<int, 0>{});
         case 2: return last(k1c, std::integral_constant<int, 2>{});
         case 4: return last(k1c, std::integral_constant<int, 4>{});
         default: return last(k1c, std::integral_constant<int, 8>{});

@@ -66,8 +66,9 @@ struct Fused2Args {
   int32_t K1, K2;    // the first and second step's K: 2, 4, 8, 16 or 32 (K <= 8: vector-ALU
                      // phase; 2 only beside K <= 8)
   int32_t K3;        // 0 (a pair), or the last step's K (2, 4 or 8) in a chain of nsteps >= 3
-                     // steps whose every K is 2, 4 or 8 and whose middle steps all have K2
+                     // steps whose every K is 2, 4 or 8
   int32_t nsteps;
+  int32_t kmid[kFuseMaxChain - 2];  // a chain's middle steps' K (steps 1 .. nsteps - 2)
   int32_t nouter;
   int32_t lrow[9], hole[11], wbit[2];
   int32_t pos_row[kFuseMaxChain - 1][9], pos_col[kFuseMaxChain - 1][8];

@@ -267,7 +267,7 @@ bool make_fused_chain(const PlanImpl &p, const int32_t *st, int n, FusedChain *f
     h.R = h.lng == 0 ? nd.m : nd.n;
     const int64_t S = h.lng == 0 ? nd.n : nd.m;
     h.K = nd.k;
-    if (!kok(h.K) || S != h.K || (q > 1 && q < n - 1 && h.K != ph[1].K)) return false;
+    if (!kok(h.K) || S != h.K) return false;
     if (q > 0 && ((h.lng == 0 ? nd.lhs : nd.rhs) != p.L + st[q - 1] || (h.lng == 0 ? nd.copy_a : nd.copy_b) != 0))
       return false;
     // the oriented rows of a node are its N side when swapped, else its M side

@@ -80,8 +80,7 @@ struct Node {
 // first step's long operand (k_fused2): each step's product is at once the
 // next step's long operand, and each step absorbs a small tensor with K = S
 // (2, 4, 8, 16 or 32 entries, K = 2 only beside K <= 8; in chains of three
-// or more every K is 2, 4 or 8 and the steps between the first and the last
-// share one K).  Built when every
+// or more every K is 2, 4 or 8).  Built when every
 // index is a power of two and a pass of kFusePassEntries entries of the long
 // operand holds whole rows of every step; the tables give, per index bit, the
 // place of an entry (see Fused2Args in kernels.hpp).

@@ -173,16 +173,18 @@ def test_fused_chain_of_three_matches_oracle(case):
     assert len(ks) == 1 and ks[0].count(",") == 2, ks   # one k_fused2<K1,K2,K3> launch
 
 
-# longer chains (every K <= 8, the steps between the first and the last with
-# one K, two of the pass's row bits left free): (log2 K of each step, shared
-# modes of each later step, log2 rows, last)
+# longer chains (every K <= 8, two of the pass's row bits left free): (log2 K
+# of each step, shared modes of each later step, log2 rows, last)
 CHAINN = [((2, 2, 2, 2), (0, 1, 1, 0), 16, "s"), ((2, 2, 2, 2, 2), (0, 0, 0, 1, 1), 16, "o"),
           ((2, 2, 2, 2, 2, 2), (0, 2, 1, 2, 1, 2), 17, "s"), ((3, 3, 3, 3), (0, 1, 2, 1), 16, "o"),
           ((2, 3, 3, 2), (0, 1, 2, 1), 17, "s"), ((3, 2, 2, 2, 3), (0, 1, 1, 1, 2), 16, "s"),
           ((2, 2, 2, 2, 2), (0, 1, 0, 1, 0), 18, "s"), ((3, 3, 3, 3, 3), (0, 2, 2, 2, 2), 16, "o"),
           ((1, 1, 1, 1), (0, 1, 0, 1), 17, "s"), ((2, 1, 1, 2), (0, 1, 1, 1), 16, "o"),
           ((1, 2, 2, 1), (0, 1, 1, 0), 16, "s"), ((1,) * 6, (0, 1, 1, 0, 1, 1), 17, "o"),
-          ((3, 1, 1, 1, 3), (0, 1, 0, 1, 2), 16, "s")]
+          ((3, 1, 1, 1, 3), (0, 1, 0, 1, 2), 16, "s"),
+          # middle steps with different K
+          ((2, 1, 2, 1, 2, 1), (0, 1, 1, 1, 1, 1), 16, "s"), ((3, 2, 1, 3, 2), (0, 1, 1, 1, 1), 16, "o"),
+          ((2, 2, 3, 2), (0, 1, 2, 1), 17, "o")]
 
 
 @pytest.mark.parametrize("case", CHAINN, ids=lambda c: "k{}_v{}_r{}_{}".format(

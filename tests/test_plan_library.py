@@ -143,7 +143,7 @@ LONGER = [((2, 2, 2, 2), (0, 1, 1, 0), 16, "s"), ((2, 2, 2, 2, 2), (0, 0, 0, 0, 
           ((2, 2, 2, 2, 2), (0, 0, 0, 1, 1), 17, "s"),
           # the fourth step would need 8 bits of T in a pass of 128 rows: a chain of three
           ((3, 3, 3, 3), (0, 0, 0, 1), 16, "o"),
-          # the middle steps' K would differ (4, then 8): a chain of three
+          # middle steps with different K (4, then 8)
           ((2, 2, 3, 2), (0, 1, 2, 1), 16, "s"),
           # a step with K = 16 does not join a chain of K <= 8 steps
           ((2, 2, 2, 4), (0, 1, 1, 2), 16, "o"),
@@ -165,13 +165,12 @@ def test_longer_chain_plans_match_oracle(case, permuted):
     lib, ref = _check(net, tree)
     # the longest chain from step 0 that keeps the form: T's modes reduced by
     # the later steps fit a pass (bits <= 10 - log2 K1, two fewer from four
-    # steps on), every K <= 8 beyond a pair, one K between the first and the
-    # last step, at most six steps
+    # steps on), every K <= 8 beyond a pair, at most six steps
     n = 1
     while n < min(len(ks), 6):
         bits = sum(ks[q] - vs[q] for q in range(1, n + 1))
         kk = ks[:n + 1]
-        if bits > 10 - ks[0] - (2 if n >= 3 else 0) or (n >= 2 and (max(kk) > 3 or len(set(kk[1:-1])) > 1)):
+        if bits > 10 - ks[0] - (2 if n >= 3 else 0) or (n >= 2 and max(kk) > 3):
             break
         if n == 1 and 1 in kk and max(kk) > 3:   # K = 2 only beside K <= 8
             break
