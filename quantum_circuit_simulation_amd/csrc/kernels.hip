@@ -3589,7 +3589,12 @@ template <int K1, int K2, int K3 = 0>
 static hipError_t run_fused2_k(const Fused2Args &a, hipStream_t stream) {
   const int64_t nround = (a.R / (kFuseEntries / K1)) / 4;  // four passes per workgroup round
   int64_t blocks = nround;
-  const int64_t cap = 8 * (int64_t)num_cus();
+  // up to 8 workgroups per CU; a short launch, whose workgroups would get
+  // fewer than 16 rounds each, only those resident at once (two per CU by
+  // registers and LDS), so that each amortizes its table set-up over more
+  // rounds
+  const int64_t cus = num_cus();
+  const int64_t cap = nround < 16 * 8 * cus ? 2 * cus : 8 * cus;
   if (blocks > cap) blocks = cap;
   if (K3) note_kernel("k_fused2<%d,%d,%d>", K1, K2, K3);
   else note_kernel("k_fused2<%d,%d>", K1, K2);
